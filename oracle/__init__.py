@@ -1,0 +1,154 @@
+"""fp64 CPU oracle for the delta-rule / Kalman-Delta scans and the HOLA cache.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke``
+and by the CPU-baseline leg of ``bench.py``; never by the product package.
+It shares no code with the HIP library. The arithmetic lives in
+``kdn_oracle.c`` (plain sequential C in double precision, built with gcc).
+
+Sources are cited per function in ``kdn_oracle.c``:
+"A Hippocampus for Linear Attention" (part 2/3, secs. 3.2-3.5, eqs. 4-7),
+"Kalman Delta Networks: Uncertainty-aware Associative Memory" (abstract),
+"Memory by Design: Probabilistic Sequence Layers" (abstract),
+"DeltaNet-PC: Test-Time Memory Without Backpropagation Through Time" (eqs. 6-7).
+
+Parity unpinned: the diagonal-covariance write with stationary process noise
+and general keys (no closed form exists; pinned only through its special
+cases k = 0, one-hot keys, covariance reset and the Moebius fixed point).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kdn_oracle.c")
+_LIB = os.path.join(_HERE, "libkdn_oracle.so")
+
+MODES = {"delta": 0, "diag": 1, "full": 2}
+RESIDS = {"gated": 0, "plain": 1}
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i = ctypes.c_int
+        d = ctypes.c_double
+        lib.oracle_scan.argtypes = [i, i, i, i, i, P, P, P, P, P, P, P, d, P, i, i, P, P]
+        lib.oracle_scan.restype = i
+        lib.oracle_hola_step.argtypes = [i, i, i, i, i, P, P, P, P, i, P, P, P, P, P, P, d, P]
+        lib.oracle_hola_step.restype = i
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = i
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def _f32(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _ptr(x):
+    return None if x is None else x.ctypes.data_as(ctypes.c_void_p)
+
+
+def scan(q, k, v, alpha=None, beta=None, r=None, cov0=None, q_noise_var: float = 0.0,
+         S0=None, mode: str = "delta", resid: str = "gated", want_m: bool = True) -> dict:
+    """Sequential fp64 scan. q, k: [B,H,L,dk]; v: [B,H,L,dv]; alpha/beta/r: [B,H,L].
+    cov0: [B,H,dk] (diag) or [B,H,dk,dk] (full). S0: [B,H,dk,dv] (default zeros).
+    Returns dict(o [B,H,L,dv], S [B,H,dk,dv], cov, m [B,H,L]) in float64."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == (B, H, L, dk) and v.shape == (B, H, L, dv)
+    alpha, beta, r = _f32(alpha), _f32(beta), _f32(r)
+    for x in (alpha, beta, r):
+        assert x is None or x.shape == (B, H, L)
+    S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64, order="C")
+    assert S.shape == (B, H, dk, dv)
+    cov = None
+    if mode == "diag":
+        cov = np.array(cov0, dtype=np.float64, order="C").reshape(B, H, dk)
+    elif mode == "full":
+        cov = np.array(cov0, dtype=np.float64, order="C").reshape(B, H, dk, dk)
+    o = np.zeros((B, H, L, dv))
+    m = np.zeros((B, H, L)) if want_m else None
+    rc = _load().oracle_scan(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                             _ptr(beta), _ptr(r), _ptr(cov), float(q_noise_var), _ptr(S),
+                             MODES[mode], RESIDS[resid], _ptr(o), _ptr(m))
+    if rc != 0:
+        raise ValueError(f"oracle_scan rejected the arguments (status {rc})")
+    return dict(o=o, S=S, cov=cov, m=m)
+
+
+class HolaCache:
+    """Oracle-side HOLA cache state for [B, H] heads with capacity w."""
+
+    def __init__(self, B: int, H: int, dk: int, dv: int, w: int):
+        self.B, self.H, self.dk, self.dv, self.w = B, H, dk, dv, w
+        self.k = np.zeros((B, H, w, dk), np.float32)
+        self.v = np.zeros((B, H, w, dv), np.float32)
+        self.m = np.zeros((B, H, w), np.float32)
+        self.pos = np.full((B, H, w), -1, np.int32)
+        self.count = np.zeros((B, H), np.int32)
+
+    def step(self, q, k, v, m, t: int, sink_logit=None, rms_eps: float = 1e-6):
+        """Read over cache + current token (+ sink), then insert token t with score m.
+        Returns o_cache [B,H,dv] float64."""
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        m = np.ascontiguousarray(m, dtype=np.float64)
+        sink = _f32(sink_logit)
+        o = np.zeros((self.B, self.H, self.dv))
+        _load().oracle_hola_step(self.B, self.H, self.dk, self.dv, self.w, _ptr(q), _ptr(k),
+                                 _ptr(v), _ptr(m), int(t), _ptr(self.k), _ptr(self.v),
+                                 _ptr(self.m), _ptr(self.pos), _ptr(self.count), _ptr(sink),
+                                 float(rms_eps), _ptr(o))
+        return o
+
+
+def decode_run(steps_inputs, B: int, H: int, dk: int, dv: int, w: int, mode: str = "delta",
+               resid: str = "gated", S0=None, cov0=None, r_steps=None, q_noise_var: float = 0.0,
+               sink_logit=None, rms_eps: float = 1e-6, t0: int = 0, cache: HolaCache = None):
+    """Decode a sequence of single tokens: per step, the recurrence (one token of
+    ``scan``) then the HOLA cache read/insert with that token's score.
+    ``steps_inputs`` yields dicts with q, k, v ([B,H,d]) and alpha, beta ([B,H]).
+    Returns (list of o, list of o_cache, list of m, final S, final cov, cache)."""
+    S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    cov = None if cov0 is None else np.array(cov0, dtype=np.float64)
+    cache = cache or HolaCache(B, H, dk, dv, w)
+    outs, couts, ms = [], [], []
+    for i, inp in enumerate(steps_inputs):
+        rr = None if r_steps is None else r_steps[i][..., None]
+        res = scan(inp["q"][:, :, None], inp["k"][:, :, None], inp["v"][:, :, None],
+                   alpha=inp["alpha"][..., None], beta=inp["beta"][..., None], r=rr,
+                   cov0=cov, q_noise_var=q_noise_var, S0=S, mode=mode, resid=resid)
+        S, cov = res["S"], res["cov"]
+        m = res["m"][..., 0]
+        oc = cache.step(inp["q"], inp["k"], inp["v"], m, t0 + i, sink_logit, rms_eps)
+        outs.append(res["o"][:, :, 0])
+        couts.append(oc)
+        ms.append(m)
+    return outs, couts, ms, S, cov, cache

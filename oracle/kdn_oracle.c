@@ -1,0 +1,331 @@
+/*
+ * kdn_oracle.c -- plain, slow, sequential float64 reference for the delta-rule
+ * family of associative-memory recurrences and the HOLA exact cache.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product library links, loads or
+ * calls this file; it is used by the tests, by the package's smoke check and
+ * by the benchmark's CPU-baseline leg. It shares no code with the HIP path.
+ *
+ * Everything is strictly sequential in the token index t, one (batch, head)
+ * pair at a time (OpenMP only spreads independent pairs over host threads).
+ * Inputs arrive as float32 (the exact values the GPU sees; bf16 inputs are
+ * exactly representable in float32) and every operation is done in double.
+ *
+ * Notation: state S is d_k x d_v, S[i][j] at S[i*dv + j]; the prediction for
+ * key k is S^T k (a d_v vector); the read-out is o_t = S_t^T q_t.
+ *
+ * Sources (page title, then section / equation):
+ *  [HOLA]  "A Hippocampus for Linear Attention: An Exact Memory for What the
+ *          Recurrent State Forgets", part 2/3: sec. 3.2 eq. (4), sec. 3.3
+ *          eqs. (5)-(6), sec. 3.4 eq. (7), sec. 3.5.
+ *  [KDN]   "Kalman Delta Networks: Uncertainty-aware Associative Memory",
+ *          abstract.
+ *  [MBD]   "Memory by Design: Probabilistic Sequence Layers", abstract.
+ *  [PC]    "DeltaNet-PC: Test-Time Memory Without Backpropagation Through
+ *          Time", summary ("How it works"), eqs. (6)-(7).
+ *
+ * Readings where the pages leave a step open are listed where they are used
+ * (R-numbers match the design notes).
+ *
+ * Parity pins: every function here is checked in the CPU test-suite against
+ * closed forms, brute force and special cases that do not use this file's
+ * arithmetic (ridge regression, weighted ridge, exact recall, no-op write,
+ * covariance-reset reduction, one-hot keys, softmax attention, sorting).
+ * The diagonal-covariance write under stationary process noise with general
+ * keys has no closed form: there it is pinned only through its special cases
+ * (k = 0, one-hot keys, covariance reset, fixed point), see the tests.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_DELTA 0
+#define ORC_DIAG 1
+#define ORC_FULL 2
+#define ORC_GATED 0
+#define ORC_PLAIN 1
+
+/*
+ * One (batch, head) sequence of the write/read recurrence.
+ *
+ * Delta write (mode DELTA), gated form [HOLA sec. 3.5, eq. (5)]:
+ *     e_t = v_t - alpha_t S_{t-1}^T k_t
+ *     S_t = alpha_t S_{t-1} + beta_t k_t e_t^T
+ * Plain form (resid PLAIN; no decay inside the residual, as the delta rule is
+ * usually written): e_t = v_t - S_{t-1}^T k_t, same update.
+ *
+ * Kalman write (modes DIAG and FULL) [KDN abstract; MBD abstract]: memory is a
+ * linear-Gaussian state-space model. Reading R2: v_t = S_t^T k_t + n_t with
+ * n_t ~ N(0, r_t I), transition S_t = alpha_t S_{t-1} + w_t. All d_v value
+ * columns see the same key and noise, so one d_k x d_k covariance P is shared
+ * by every column. Process noise (reading S3): Q_t = (1 - alpha_t^2) sigma^2,
+ * a stationary AR(1) prior that pulls uncertainty back to sigma^2 as memory
+ * decays (sigma^2 = q_noise_var; 0 gives Q = 0).
+ *     predict : S- = alpha S,   P- = alpha^2 P + Q_t I
+ *     residual: e  = v - S-^T k                      (the gated residual)
+ *     gain    : u = P- k,  s = k^T u + r_t,  b = u / s
+ *     update  : S = S- + b e^T,   P = P- - u u^T / s
+ * FULL keeps the whole P (the exact Riccati recursion). DIAG keeps only the
+ * diagonal p (reading R3/S5, online mean-field projection): the gain uses the
+ * exact one-step posterior mean, b = (p- * k) / (sum_i p-_i k_i^2 + r), and the
+ * projected posterior keeps the diagonal of the posterior precision,
+ * 1/p_i = 1/p-_i + k_i^2 / r, i.e. p_i = p-_i r / (r + p-_i k_i^2).
+ * With alpha = 1, r = 1, Q = 0 and P_0 = eps^-1 I the FULL write is the
+ * recursive-least-squares update of [PC eq. (7)].
+ *
+ * Read-out o_t = S_t^T q_t, after the write (reading S2; the layer output is
+ * the predictive mean [MBD abstract]).
+ *
+ * Score m_t = ||Delta_t||_F with Delta_t = b e^T the token's rank-1 write
+ * [HOLA sec. 3.3, eq. (6)]: ||b|| ||e||. In DELTA mode the score is
+ * beta_t ||e_t|| exactly as eq. (6) states it (equal to ||b|| ||e|| for unit
+ * keys).
+ */
+static void scan_one(int L, int dk, int dv,
+                     const float *q, const float *k, const float *v,
+                     const float *alpha, const float *beta, const float *r,
+                     double *cov, double qvar, double *S,
+                     int mode, int resid, double *o, double *m,
+                     double *work)
+{
+    double *e = work;              /* dv */
+    double *b = e + dv;            /* dk */
+    double *pm = b + dk;           /* dk  (DIAG p-) */
+    double *u = pm + dk;           /* dk  (FULL P- k) */
+    double *Pm = u + dk;           /* dk*dk (FULL P-) */
+
+    for (int t = 0; t < L; ++t) {
+        const float *kt = k + (size_t)t * dk;
+        const float *qt = q + (size_t)t * dk;
+        const float *vt = v + (size_t)t * dv;
+        const double a = alpha ? (double)alpha[t] : 1.0;
+        const double rt = r ? (double)r[t] : 1.0;
+        const double Qt = (1.0 - a * a) * qvar;
+
+        /* predict the covariance */
+        if (mode == ORC_DIAG) {
+            for (int i = 0; i < dk; ++i) pm[i] = a * a * cov[i] + Qt;
+        } else if (mode == ORC_FULL) {
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dk; ++j)
+                    Pm[i * dk + j] = a * a * cov[i * dk + j] + (i == j ? Qt : 0.0);
+        }
+
+        /* residual */
+        const double scale = (resid == ORC_PLAIN) ? 1.0 : a;
+        for (int j = 0; j < dv; ++j) {
+            double pred = 0.0;
+            for (int i = 0; i < dk; ++i) pred += S[(size_t)i * dv + j] * (double)kt[i];
+            e[j] = (double)vt[j] - scale * pred;
+        }
+
+        /* write vector */
+        double s = 0.0;
+        if (mode == ORC_DELTA) {
+            const double bt = (double)beta[t];
+            for (int i = 0; i < dk; ++i) b[i] = bt * (double)kt[i];
+        } else if (mode == ORC_DIAG) {
+            s = rt;
+            for (int i = 0; i < dk; ++i) s += pm[i] * (double)kt[i] * (double)kt[i];
+            for (int i = 0; i < dk; ++i) b[i] = pm[i] * (double)kt[i] / s;
+        } else {
+            for (int i = 0; i < dk; ++i) {
+                double acc = 0.0;
+                for (int j = 0; j < dk; ++j) acc += Pm[i * dk + j] * (double)kt[j];
+                u[i] = acc;
+            }
+            s = rt;
+            for (int i = 0; i < dk; ++i) s += (double)kt[i] * u[i];
+            for (int i = 0; i < dk; ++i) b[i] = u[i] / s;
+        }
+
+        /* state update */
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] = a * S[(size_t)i * dv + j] + b[i] * e[j];
+
+        /* covariance update */
+        if (mode == ORC_DIAG) {
+            for (int i = 0; i < dk; ++i) {
+                const double k2 = (double)kt[i] * (double)kt[i];
+                cov[i] = pm[i] * rt / (rt + pm[i] * k2);
+            }
+        } else if (mode == ORC_FULL) {
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dk; ++j)
+                    cov[i * dk + j] = Pm[i * dk + j] - u[i] * u[j] / s;
+        }
+
+        /* read-out */
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += S[(size_t)i * dv + j] * (double)qt[i];
+            o[(size_t)t * dv + j] = acc;
+        }
+
+        /* write-magnitude score */
+        if (m) {
+            double ee = 0.0;
+            for (int j = 0; j < dv; ++j) ee += e[j] * e[j];
+            if (mode == ORC_DELTA) {
+                m[t] = (double)beta[t] * sqrt(ee);
+            } else {
+                double bb = 0.0;
+                for (int i = 0; i < dk; ++i) bb += b[i] * b[i];
+                m[t] = sqrt(bb) * sqrt(ee);
+            }
+        }
+    }
+}
+
+/*
+ * Full scan over [B, H, L, d] inputs.
+ *   q, k: [B,H,L,dk] float32; v: [B,H,L,dv] float32.
+ *   alpha, beta, r: [B,H,L] float32. alpha NULL => 1; r NULL => 1;
+ *   beta is required in DELTA mode and ignored otherwise.
+ *   cov: DIAG [B,H,dk] / FULL [B,H,dk,dk] float64, in = prior, out = final.
+ *   S:   [B,H,dk,dv] float64, in = S_0, out = S_L.
+ *   o:   [B,H,L,dv] float64 out;  m: [B,H,L] float64 out (may be NULL).
+ * Returns 0, or -1 for an unsupported combination.
+ */
+int oracle_scan(int B, int H, int L, int dk, int dv,
+                const float *q, const float *k, const float *v,
+                const float *alpha, const float *beta, const float *r,
+                double *cov, double q_noise_var, double *S,
+                int mode, int resid, double *o, double *m)
+{
+    if (mode != ORC_DELTA && mode != ORC_DIAG && mode != ORC_FULL) return -1;
+    if (resid == ORC_PLAIN && mode != ORC_DELTA) return -1;
+    if (mode == ORC_DELTA && !beta) return -1;
+    if (mode != ORC_DELTA && !cov) return -1;
+    const int BH = B * H;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < BH; ++bh) {
+        double *work = (double *)malloc(sizeof(double) * (size_t)(dv + 3 * dk + dk * dk));
+        if (!work) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        const size_t tok = (size_t)bh * L;
+        double *covp = NULL;
+        if (mode == ORC_DIAG) covp = cov + (size_t)bh * dk;
+        if (mode == ORC_FULL) covp = cov + (size_t)bh * dk * dk;
+        scan_one(L, dk, dv, q + tok * dk, k + tok * dk, v + tok * dv,
+                 alpha ? alpha + tok : NULL, beta ? beta + tok : NULL, r ? r + tok : NULL,
+                 covp, q_noise_var, S + (size_t)bh * dk * dv, mode, resid,
+                 o + tok * dv, m ? m + tok : NULL, work);
+        free(work);
+    }
+    return bad ? -2 : 0;
+}
+
+/*
+ * HOLA exact cache, one decode token for every (batch, head)
+ * [HOLA sec. 3.3 (top-w cache), sec. 3.4 eq. (7) (read), sec. 3.2 eq. (4)].
+ *
+ * Read first, over the visible set V_t = cache (as it stood before token t)
+ * plus the current token itself (the "current block" is one token when
+ * decoding), plus one null sink when sink_logit is given (a slot with value 0
+ * and logit sink_logit[h]):
+ *     qn = q / sqrt(mean(q^2) + eps),  kn_j likewise (RMSNorm with unit gain)
+ *     l_j = qn . kn_j / sqrt(dk)
+ *     o_cache = sum_j softmax(l)_j v_j
+ * Then insert token t with its score m_t. The decision is taken on the score
+ * rounded to float32 (reading S10: scores are float32 and ties go to the
+ * earlier token). The cache keeps the w tokens with the largest score, ties
+ * broken by the smaller position: while it has free slots the token is
+ * appended; otherwise it replaces the slot with the smallest (score, then
+ * largest position) if and only if its score is strictly larger.
+ *
+ *   q, k: [B,H,dk] float32; v: [B,H,dv] float32; m: [B,H] float64.
+ *   cache_k [B,H,w,dk], cache_v [B,H,w,dv] float32 (exact copies);
+ *   cache_m [B,H,w] float32; cache_pos [B,H,w] int32; count [B,H] int32.
+ *   sink_logit: [H] float32 or NULL.   o_cache: [B,H,dv] float64 out.
+ */
+int oracle_hola_step(int B, int H, int dk, int dv, int w,
+                     const float *q, const float *k, const float *v, const double *m,
+                     int t, float *cache_k, float *cache_v, float *cache_m,
+                     int32_t *cache_pos, int32_t *count, const float *sink_logit,
+                     double rms_eps, double *o_cache)
+{
+    const int BH = B * H;
+#pragma omp parallel for schedule(static)
+    for (int bh = 0; bh < BH; ++bh) {
+        const float *qt = q + (size_t)bh * dk;
+        const float *kt = k + (size_t)bh * dk;
+        const float *vt = v + (size_t)bh * dv;
+        float *ck = cache_k + (size_t)bh * w * dk;
+        float *cv = cache_v + (size_t)bh * w * dv;
+        float *cm = cache_m + (size_t)bh * w;
+        int32_t *cp = cache_pos + (size_t)bh * w;
+        const int n = count[bh];
+        double *oc = o_cache + (size_t)bh * dv;
+
+        /* RMS-normalised query */
+        double qq = 0.0;
+        for (int i = 0; i < dk; ++i) qq += (double)qt[i] * qt[i];
+        const double qs = 1.0 / sqrt(qq / dk + rms_eps);
+        const double inv_sqrt_d = 1.0 / sqrt((double)dk);
+
+        /* logits over the cache slots, then the current token, then the sink */
+        double *lg = (double *)malloc(sizeof(double) * (size_t)(n + 2));
+        for (int j = 0; j <= n; ++j) {
+            const float *kj = (j < n) ? ck + (size_t)j * dk : kt;
+            double kk = 0.0, qk = 0.0;
+            for (int i = 0; i < dk; ++i) {
+                kk += (double)kj[i] * kj[i];
+                qk += (double)qt[i] * kj[i];
+            }
+            const double ks = 1.0 / sqrt(kk / dk + rms_eps);
+            lg[j] = qk * qs * ks * inv_sqrt_d;
+        }
+        int nl = n + 1;
+        if (sink_logit) lg[nl++] = (double)sink_logit[bh % H];
+        double mx = lg[0];
+        for (int j = 1; j < nl; ++j) mx = lg[j] > mx ? lg[j] : mx;
+        double den = 0.0;
+        for (int j = 0; j < nl; ++j) den += exp(lg[j] - mx);
+        for (int c = 0; c < dv; ++c) oc[c] = 0.0;
+        for (int j = 0; j <= n; ++j) {   /* the sink's value is 0 */
+            const float *vj = (j < n) ? cv + (size_t)j * dv : vt;
+            const double p = exp(lg[j] - mx) / den;
+            for (int c = 0; c < dv; ++c) oc[c] += p * (double)vj[c];
+        }
+        free(lg);
+
+        /* top-w insert, decided on the float32 score */
+        const float mt = (float)m[bh];
+        int slot = -1;
+        if (n < w) {
+            slot = n;
+            count[bh] = n + 1;
+        } else {
+            int worst = 0;
+            for (int j = 1; j < w; ++j) {
+                if (cm[j] < cm[worst] || (cm[j] == cm[worst] && cp[j] > cp[worst])) worst = j;
+            }
+            if (mt > cm[worst]) slot = worst;
+        }
+        if (slot >= 0) {
+            memcpy(ck + (size_t)slot * dk, kt, sizeof(float) * (size_t)dk);
+            memcpy(cv + (size_t)slot * dv, vt, sizeof(float) * (size_t)dv);
+            cm[slot] = mt;
+            cp[slot] = t;
+        }
+    }
+    return 0;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
