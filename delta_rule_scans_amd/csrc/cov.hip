@@ -1,0 +1,224 @@
+// cov.hip -- covariance recursions of the Kalman writes and their per-token gains.
+//
+// "Kalman Delta Networks: Uncertainty-aware Associative Memory", abstract: the
+// transition propagates the memory and its uncertainty; the Kalman gain
+// weights each residual write. The covariance recursion never reads the
+// state S, so the gains are computed here, before the state scan, and the scan
+// consumes them as write vectors.
+//
+// Per token (process noise Q_t = (1 - alpha_t^2) sigma^2):
+//   P-  = alpha^2 P + Q I,   u = P- k,   s = k^T u + r,   g = u / s,   P = P- - u u^T / s
+// DIAG keeps p = diag(P) and projects after every step onto diagonal
+// covariances by keeping the diagonal of the precision (mean-field):
+//   p-_i = alpha^2 p_i + Q,  g_i = p-_i k_i / (sum_j p-_j k_j^2 + r),  p_i = p-_i r / (r + p-_i k_i^2).
+// Each coordinate's map p -> p_new is a linear-fractional (Moebius) map, so a
+// run of tokens composes into one 2x2 matrix (the abstract's "uncertainty
+// recurrences are Mobius maps"). The DIAG path uses that: one pass composes the
+// maps of every chunk in parallel, a second pass starts each chunk from the
+// composition of the chunks before it and recomputes the per-token values.
+#include "kdn_internal.h"
+
+namespace kdn {
+namespace {
+
+// Map of one token on (p, 1), projectively: p_new = (m00 p + m01) / (m10 p + m11).
+// From p- = a^2 p + Q and p_new = r p- / (k^2 p- + r). All entries are >= 0,
+// so products never cancel.
+__device__ __forceinline__ void token_map(float a, float qvar, float r, float kv, float& t00,
+                                          float& t01, float& t10, float& t11) {
+  const float a2 = a * a;
+  const float Q = (1.f - a) * (1.f + a) * qvar;
+  const float k2 = kv * kv;
+  t00 = r * a2;
+  t01 = r * Q;
+  t10 = k2 * a2;
+  t11 = fmaf(k2, Q, r);
+}
+
+template <typename Tk>
+__global__ __launch_bounds__(128) void diag_maps_kernel(const Tk* k, const float* alpha,
+                                                        const float* r, float qvar, float4* maps,
+                                                        int L, int dk, int C, int nchunks) {
+  const int bh = blockIdx.x, c = blockIdx.y, i = threadIdx.x;
+  if (i >= dk) return;
+  const int t0 = c * C, n = min(C, L - t0);
+  float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f;
+  for (int t = 0; t < n; ++t) {
+    const size_t g = (size_t)bh * L + t0 + t;
+    float t00, t01, t10, t11;
+    token_map(alpha ? alpha[g] : 1.f, qvar, r ? r[g] : 1.f, Elem<Tk>::load(k, g * dk + i), t00,
+              t01, t10, t11);
+    const float n00 = fmaf(t00, m00, t01 * m10), n01 = fmaf(t00, m01, t01 * m11);
+    const float n10 = fmaf(t10, m00, t11 * m10), n11 = fmaf(t10, m01, t11 * m11);
+    const float sc = 1.f / fmaxf(fmaxf(n00, n01), fmaxf(n10, n11));
+    m00 = n00 * sc;
+    m01 = n01 * sc;
+    m10 = n10 * sc;
+    m11 = n11 * sc;
+  }
+  maps[((size_t)bh * nchunks + c) * dk + i] = make_float4(m00, m01, m10, m11);
+}
+
+// One workgroup per (head, chunk), one thread per coordinate.
+template <typename Tk, typename Tg>
+__global__ __launch_bounds__(128) void diag_gains_kernel(const Tk* k, const float* alpha,
+                                                         const float* r, const float* cov_in,
+                                                         float* cov_out, float qvar,
+                                                         const float4* maps, Tg* gains, int L,
+                                                         int dk, int C, int nchunks) {
+  extern __shared__ float lds[];
+  const int bh = blockIdx.x, c = blockIdx.y, i = threadIdx.x;
+  const int KP = dk + 1;
+  float* sPK = lds;              // [C][KP] p-_i k_i
+  float* sPK2 = sPK + C * KP;    // [C][KP] p-_i k_i^2
+  float* sInv = sPK2 + C * KP;   // [C] 1 / s_t
+  const int t0 = c * C, n = min(C, L - t0);
+  if (i < dk) {
+    float p = cov_in[(size_t)bh * dk + i];
+    for (int cc = 0; cc < c; ++cc) {
+      const float4 M = maps[((size_t)bh * nchunks + cc) * dk + i];
+      p = fmaf(M.x, p, M.y) / fmaf(M.z, p, M.w);
+    }
+    for (int t = 0; t < n; ++t) {
+      const size_t g = (size_t)bh * L + t0 + t;
+      const float a = alpha ? alpha[g] : 1.f;
+      const float rt = r ? r[g] : 1.f;
+      const float kv = Elem<Tk>::load(k, g * dk + i);
+      const float pm = fmaf(a * a, p, (1.f - a) * (1.f + a) * qvar);
+      const float pk = pm * kv;
+      sPK[t * KP + i] = pk;
+      sPK2[t * KP + i] = pk * kv;
+      p = pm * rt / fmaf(pk, kv, rt);
+    }
+    if (c == nchunks - 1 && cov_out) cov_out[(size_t)bh * dk + i] = p;
+  }
+  __syncthreads();
+  if (i < n) {
+    const size_t g = (size_t)bh * L + t0 + i;
+    float s = r ? r[g] : 1.f;
+    for (int j = 0; j < dk; ++j) s += sPK2[i * KP + j];
+    sInv[i] = 1.f / s;
+  }
+  __syncthreads();
+  if (i < dk) {
+    for (int t = 0; t < n; ++t) {
+      const size_t g = ((size_t)bh * L + t0 + t) * dk + i;
+      Elem<Tg>::store(gains, g, sPK[t * KP + i] * sInv[t]);
+    }
+  }
+}
+
+// Full covariance, one workgroup per head, sequential over tokens (d_k <= 64).
+template <typename Tk, typename Tg>
+__global__ __launch_bounds__(256) void full_gains_kernel(const Tk* k, const float* alpha,
+                                                         const float* r, const float* cov_in,
+                                                         float* cov_out, float qvar, Tg* gains,
+                                                         int L, int dk) {
+  __shared__ float sP[64 * 65];
+  __shared__ float sU[64];
+  __shared__ float sKv[64];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int PP = dk + 1;
+  for (int idx = tid; idx < dk * dk; idx += 256) {
+    const int i = idx / dk, j = idx - i * dk;
+    sP[i * PP + j] = cov_in[(size_t)bh * dk * dk + idx];
+  }
+  for (int t = 0; t < L; ++t) {
+    const size_t g = (size_t)bh * L + t;
+    const float a = alpha ? alpha[g] : 1.f;
+    const float rt = r ? r[g] : 1.f;
+    const float Q = (1.f - a) * (1.f + a) * qvar;
+    if (tid < dk) sKv[tid] = Elem<Tk>::load(k, g * dk + tid);
+    __syncthreads();
+    for (int idx = tid; idx < dk * dk; idx += 256) {
+      const int i = idx / dk, j = idx - i * dk;
+      sP[i * PP + j] = fmaf(a * a, sP[i * PP + j], i == j ? Q : 0.f);
+    }
+    __syncthreads();
+    if (tid < dk) {
+      float u = 0.f;
+      for (int j = 0; j < dk; ++j) u = fmaf(sP[tid * PP + j], sKv[j], u);
+      sU[tid] = u;
+    }
+    __syncthreads();
+    float s = rt;
+    for (int j = 0; j < dk; ++j) s = fmaf(sKv[j], sU[j], s);
+    const float inv = 1.f / s;
+    if (tid < dk) Elem<Tg>::store(gains, g * dk + tid, sU[tid] * inv);
+    for (int idx = tid; idx < dk * dk; idx += 256) {
+      const int i = idx / dk, j = idx - i * dk;
+      sP[i * PP + j] -= sU[i] * sU[j] * inv;
+    }
+    __syncthreads();
+  }
+  if (cov_out) {
+    for (int idx = tid; idx < dk * dk; idx += 256) {
+      const int i = idx / dk, j = idx - i * dk;
+      cov_out[(size_t)bh * dk * dk + idx] = sP[i * PP + j];
+    }
+  }
+}
+
+template <typename Tk, typename Tg>
+hipError_t diag_typed(const void* k, const float* alpha, const float* r, const float* cov_in,
+                      float* cov_out, float qvar, void* gains, float* maps, int BH, int L, int dk,
+                      int C, hipStream_t s) {
+  const int nchunks = (L + C - 1) / C;
+  hipLaunchKernelGGL(diag_maps_kernel<Tk>, dim3(BH, nchunks), dim3(128), 0, s,
+                     static_cast<const Tk*>(k), alpha, r, qvar, reinterpret_cast<float4*>(maps), L,
+                     dk, C, nchunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = ((size_t)2 * C * (dk + 1) + C) * sizeof(float);
+  auto kern = diag_gains_kernel<Tk, Tg>;
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(BH, nchunks), dim3(128), lds, s, static_cast<const Tk*>(k), alpha,
+                     r, cov_in, cov_out, qvar, reinterpret_cast<const float4*>(maps),
+                     static_cast<Tg*>(gains), L, dk, C, nchunks);
+  return hipGetLastError();
+}
+
+template <typename Tk, typename Tg>
+hipError_t full_typed(const void* k, const float* alpha, const float* r, const float* cov_in,
+                      float* cov_out, float qvar, void* gains, int BH, int L, int dk,
+                      hipStream_t s) {
+  hipLaunchKernelGGL((full_gains_kernel<Tk, Tg>), dim3(BH), dim3(256), 0, s,
+                     static_cast<const Tk*>(k), alpha, r, cov_in, cov_out, qvar,
+                     static_cast<Tg*>(gains), L, dk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_diag_gains(const void* k, bool k_bf16, const float* alpha, const float* r,
+                             const float* cov_in, float* cov_out, float q_noise_var, void* gains,
+                             bool gains_f16, float* maps, int BH, int L, int dk, int chunk,
+                             hipStream_t s) {
+  if (k_bf16)
+    return gains_f16 ? diag_typed<uint16_t, _Float16>(k, alpha, r, cov_in, cov_out, q_noise_var,
+                                                       gains, maps, BH, L, dk, chunk, s)
+                      : diag_typed<uint16_t, float>(k, alpha, r, cov_in, cov_out, q_noise_var,
+                                                    gains, maps, BH, L, dk, chunk, s);
+  return gains_f16 ? diag_typed<float, _Float16>(k, alpha, r, cov_in, cov_out, q_noise_var, gains,
+                                                  maps, BH, L, dk, chunk, s)
+                    : diag_typed<float, float>(k, alpha, r, cov_in, cov_out, q_noise_var, gains,
+                                               maps, BH, L, dk, chunk, s);
+}
+
+hipError_t launch_full_gains(const void* k, bool k_bf16, const float* alpha, const float* r,
+                             const float* cov_in, float* cov_out, float q_noise_var, void* gains,
+                             bool gains_f16, int BH, int L, int dk, hipStream_t s) {
+  if (k_bf16)
+    return gains_f16 ? full_typed<uint16_t, _Float16>(k, alpha, r, cov_in, cov_out, q_noise_var,
+                                                       gains, BH, L, dk, s)
+                      : full_typed<uint16_t, float>(k, alpha, r, cov_in, cov_out, q_noise_var,
+                                                    gains, BH, L, dk, s);
+  return gains_f16 ? full_typed<float, _Float16>(k, alpha, r, cov_in, cov_out, q_noise_var, gains,
+                                                  BH, L, dk, s)
+                    : full_typed<float, float>(k, alpha, r, cov_in, cov_out, q_noise_var, gains,
+                                               BH, L, dk, s);
+}
+
+}  // namespace kdn

@@ -1,0 +1,234 @@
+// kdn_api.cpp -- the exported C ABI: argument checks, workspace sizing and
+// dispatch to the HIP kernels. Every check runs before anything is enqueued,
+// so a rejected call touches no device state.
+#include "../../include/kdn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kdn_internal.h"
+
+#define KDN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kMaxDim = 128;
+constexpr int kMaxFullDk = 64;
+constexpr int kMaxCapacity = 256;
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace layout, 256-byte aligned parts:
+//   [maps (DIAG) | gains (Kalman modes) | per-chunk (I + A)^-1 (matrix-core path)].
+// Gains are fp16 for bf16 inputs and float32 otherwise.
+struct WsLayout {
+  size_t maps_off, maps_bytes, gains_off, gains_bytes, t_off, t_bytes, total;
+};
+
+bool use_mfma_path(int in_dtype, int d_k, int d_v, int chunk) {
+  return in_dtype == KDN_BF16 && kdn::scan_mfma_supported(d_k, d_v, chunk);
+}
+
+WsLayout ws_layout(int B, int H, int L, int dk, int dv, int chunk, int mode, int in_dtype) {
+  WsLayout w{0, 0, 0, 0, 0, 0, 0};
+  if (L <= 0) return w;
+  const size_t BH = (size_t)B * H;
+  const size_t nchunks = ((size_t)L + chunk - 1) / chunk;
+  if (mode == KDN_GAIN_DIAG) w.maps_bytes = BH * nchunks * dk * 4 * sizeof(float);
+  if (mode != KDN_GAIN_DELTA) w.gains_bytes = BH * (size_t)L * dk * (in_dtype == KDN_BF16 ? 2 : 4);
+  if (use_mfma_path(in_dtype, dk, dv, chunk)) w.t_bytes = kdn::scan_mfma_workspace_bytes((int)BH, L);
+  w.maps_off = 0;
+  w.gains_off = round_up(w.maps_bytes, 256);
+  w.t_off = w.gains_off + round_up(w.gains_bytes, 256);
+  w.total = w.t_off + round_up(w.t_bytes, 256);
+  return w;
+}
+
+int map_hip(hipError_t e) { return e == hipSuccess ? KDN_OK : static_cast<int>(e); }
+
+}  // namespace
+
+KDN_EXPORT const char* kdn_status_string(int status) {
+  switch (status) {
+    case KDN_OK: return "ok";
+    case KDN_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case KDN_ERR_BAD_SHAPE: return "a size argument is out of range";
+    case KDN_ERR_BAD_CHUNK: return "chunk must be 16, 32 or 64";
+    case KDN_ERR_BAD_MODE: return "unknown write mode or residual form, or plain residual with a Kalman gain";
+    case KDN_ERR_BAD_DTYPE: return "unknown element type";
+    case KDN_ERR_UNSUPPORTED: return "valid arguments that this build does not implement (e.g. full covariance with d_k > 64)";
+    case KDN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than kdn_scan_workspace_size";
+    case KDN_ERR_BAD_CAPACITY: return "cache capacity w must be in [1, 256]";
+    case KDN_ERR_BAD_ALIGNMENT: return "a pointer is not 16-byte aligned";
+    default: break;
+  }
+  if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));
+  return "unknown status";
+}
+
+KDN_EXPORT int kdn_version(void) { return 100; }
+
+KDN_EXPORT size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
+                                          int mode, int in_dtype) {
+  if (B < 1 || H < 1 || L < 0 || d_k < 1 || d_v < 1 || !valid_chunk(chunk)) return 0;
+  return ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype).total;
+}
+
+KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const void* v,
+                                  int in_dtype, const float* alpha, const float* beta,
+                                  const float* r, const float* cov_in, float* cov_out,
+                                  float q_noise_var, const float* state_in, float* state_out,
+                                  void* o, int out_dtype, int B, int H, int L, int d_k, int d_v,
+                                  int chunk, int mode, int resid, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (phase != KDN_PHASE_ALL && phase != KDN_PHASE_PREPARE && phase != KDN_PHASE_STATE)
+    return KDN_ERR_BAD_MODE;
+  const bool do_prep = phase != KDN_PHASE_STATE, do_state = phase != KDN_PHASE_PREPARE;
+  if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_ERR_BAD_DTYPE;
+  if (out_dtype != KDN_F32 && out_dtype != KDN_BF16) return KDN_ERR_BAD_DTYPE;
+  if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_FULL)
+    return KDN_ERR_BAD_MODE;
+  if (resid != KDN_RESID_GATED && resid != KDN_RESID_PLAIN) return KDN_ERR_BAD_MODE;
+  if (resid == KDN_RESID_PLAIN && mode != KDN_GAIN_DELTA) return KDN_ERR_BAD_MODE;
+  if (B < 1 || H < 1 || L < 0 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
+    return KDN_ERR_BAD_SHAPE;
+  if ((long long)B * H > (1LL << 24)) return KDN_ERR_BAD_SHAPE;
+  if (!valid_chunk(chunk)) return KDN_ERR_BAD_CHUNK;
+  if ((long long)(L + chunk - 1) / chunk > kMaxGridYZ) return KDN_ERR_BAD_SHAPE;
+  if (mode == KDN_GAIN_FULL && d_k > kMaxFullDk) return KDN_ERR_UNSUPPORTED;
+  if (mode != KDN_GAIN_DELTA && cov_in == nullptr) return KDN_ERR_NULL_POINTER;
+  if (!std::isfinite(q_noise_var) || q_noise_var < 0.f) return KDN_ERR_BAD_SHAPE;
+  if (L > 0) {
+    if (!q || !k || !v || !o) return KDN_ERR_NULL_POINTER;
+    if (mode == KDN_GAIN_DELTA && beta == nullptr) return KDN_ERR_NULL_POINTER;
+  }
+  const WsLayout ws = ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype);
+  if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total || !aligned16(workspace)))
+    return KDN_ERR_WORKSPACE;
+  if (kdn::scan_f32_lds_bytes(d_k, chunk) == 0 &&
+      !(in_dtype == KDN_BF16 && kdn::scan_mfma_supported(d_k, d_v, chunk)))
+    return KDN_ERR_UNSUPPORTED;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  const size_t cov_elems = mode == KDN_GAIN_DIAG   ? (size_t)BH * d_k
+                           : mode == KDN_GAIN_FULL ? (size_t)BH * d_k * d_k
+                                                   : 0;
+  if (L == 0) {
+    hipError_t e = hipSuccess;
+    if (do_state && state_out)
+      e = kdn::launch_copy_f32(state_in, state_out, (size_t)BH * d_k * d_v, s);
+    if (do_prep && e == hipSuccess && cov_out && cov_elems)
+      e = kdn::launch_copy_f32(cov_in, cov_out, cov_elems, s);
+    return map_hip(e);
+  }
+
+  const bool in_bf16 = in_dtype == KDN_BF16;
+  const void* gains = nullptr;
+  if (mode != KDN_GAIN_DELTA) {
+    char* base = static_cast<char*>(workspace);
+    void* g = base + ws.gains_off;
+    gains = g;
+  }
+  if (do_prep && mode != KDN_GAIN_DELTA) {
+    char* base = static_cast<char*>(workspace);
+    void* g = base + ws.gains_off;
+    hipError_t e;
+    if (mode == KDN_GAIN_DIAG)
+      e = kdn::launch_diag_gains(k, in_bf16, alpha, r, cov_in, cov_out, q_noise_var, g, in_bf16,
+                                 reinterpret_cast<float*>(base + ws.maps_off), BH, L, d_k, chunk,
+                                 s);
+    else
+      e = kdn::launch_full_gains(k, in_bf16, alpha, r, cov_in, cov_out, q_noise_var, g, in_bf16,
+                                 BH, L, d_k, s);
+    if (e != hipSuccess) return map_hip(e);
+  }
+
+  kdn::ScanArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = mode == KDN_GAIN_DELTA ? beta : nullptr;
+  a.gain = gains;
+  a.state_in = state_in;
+  a.state_out = state_out;
+  a.o = o;
+  a.BH = BH;
+  a.L = L;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.chunk = chunk;
+  a.plain = resid == KDN_RESID_PLAIN ? 1 : 0;
+
+  const bool out_bf16 = out_dtype == KDN_BF16;
+  const bool mfma_ok = use_mfma_path(in_dtype, d_k, d_v, chunk) && aligned16(q) && aligned16(k) &&
+                       aligned16(v) && aligned16(o) && (gains == nullptr || aligned16(gains));
+  if (mfma_ok) {
+    void* tbuf = static_cast<char*>(workspace) + ws.t_off;
+    if (do_prep) {
+      const hipError_t e = kdn::launch_tinv_mfma(a, tbuf, s);
+      if (e != hipSuccess) return map_hip(e);
+    }
+    return do_state ? map_hip(kdn::launch_state_mfma(a, out_bf16, tbuf, s)) : KDN_OK;
+  }
+  return do_state ? map_hip(kdn::launch_scan_f32(a, in_bf16, out_bf16, in_bf16, s)) : KDN_OK;
+}
+
+KDN_EXPORT int kdn_scan_fwd(const void* q, const void* k, const void* v, int in_dtype,
+                            const float* alpha, const float* beta, const float* r,
+                            const float* cov_in, float* cov_out, float q_noise_var,
+                            const float* state_in, float* state_out, void* o, int out_dtype,
+                            int B, int H, int L, int d_k, int d_v, int chunk, int mode, int resid,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return kdn_scan_fwd_phase(KDN_PHASE_ALL, q, k, v, in_dtype, alpha, beta, r, cov_in, cov_out,
+                            q_noise_var, state_in, state_out, o, out_dtype, B, H, L, d_k, d_v,
+                            chunk, mode, resid, workspace, workspace_bytes, stream);
+}
+
+KDN_EXPORT int kdn_step_decode(const float* q, const float* k, const float* v, const float* alpha,
+                               const float* beta, const float* r, float* cov, float q_noise_var,
+                               float* state, float* o, float* m, int B, int H, int d_k, int d_v,
+                               int mode, int resid, void* stream) {
+  if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_FULL)
+    return KDN_ERR_BAD_MODE;
+  if (resid != KDN_RESID_GATED && resid != KDN_RESID_PLAIN) return KDN_ERR_BAD_MODE;
+  if (resid == KDN_RESID_PLAIN && mode != KDN_GAIN_DELTA) return KDN_ERR_BAD_MODE;
+  if (B < 1 || H < 1 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
+    return KDN_ERR_BAD_SHAPE;
+  if ((long long)B * H > (1LL << 30)) return KDN_ERR_BAD_SHAPE;
+  if (mode == KDN_GAIN_FULL) return KDN_ERR_UNSUPPORTED;
+  if (!std::isfinite(q_noise_var) || q_noise_var < 0.f) return KDN_ERR_BAD_SHAPE;
+  if (!q || !k || !v || !state || !o) return KDN_ERR_NULL_POINTER;
+  if (mode == KDN_GAIN_DELTA && beta == nullptr) return KDN_ERR_NULL_POINTER;
+  if (mode == KDN_GAIN_DIAG && cov == nullptr) return KDN_ERR_NULL_POINTER;
+  return map_hip(kdn::launch_decode(q, k, v, alpha, beta, r, cov, q_noise_var, state, o, m, B * H,
+                                    d_k, d_v, mode == KDN_GAIN_DIAG ? 1 : 0,
+                                    resid == KDN_RESID_PLAIN ? 1 : 0,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+KDN_EXPORT int hola_cache_update(const float* q, const float* k, const float* v, const float* m,
+                                 int32_t t, float* cache_k, float* cache_v, float* cache_m,
+                                 int32_t* cache_pos, int32_t* cache_count,
+                                 const float* sink_logit, float* o_cache, float rms_eps, int B,
+                                 int H, int d_k, int d_v, int w, void* stream) {
+  if (w < 1 || w > kMaxCapacity) return KDN_ERR_BAD_CAPACITY;
+  if (B < 1 || H < 1 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
+    return KDN_ERR_BAD_SHAPE;
+  if ((long long)B * H > (1LL << 30)) return KDN_ERR_BAD_SHAPE;
+  if (!(rms_eps >= 0.f) || !std::isfinite(rms_eps)) return KDN_ERR_BAD_SHAPE;
+  if (!q || !k || !v || !m || !cache_k || !cache_v || !cache_m || !cache_pos || !cache_count ||
+      !o_cache)
+    return KDN_ERR_NULL_POINTER;
+  return map_hip(kdn::launch_hola(q, k, v, m, t, cache_k, cache_v, cache_m, cache_pos, cache_count,
+                                  sink_logit, o_cache, rms_eps, B, H, d_k, d_v, w,
+                                  static_cast<hipStream_t>(stream)));
+}

@@ -1,0 +1,103 @@
+// kdn_internal.h -- declarations shared by the HIP translation units of the
+// library (device helpers and the host-side launchers the C ABI calls).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kdn {
+
+// ---------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static __forceinline__ float load(const float* p, size_t i) { return p[i]; }
+  __device__ static __forceinline__ void store(float* p, size_t i, float x) { p[i] = x; }
+};
+template <> struct Elem<_Float16> {
+  __device__ static __forceinline__ float load(const _Float16* p, size_t i) { return (float)p[i]; }
+  __device__ static __forceinline__ void store(_Float16* p, size_t i, float x) { p[i] = (_Float16)x; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static __forceinline__ float load(const uint16_t* p, size_t i) {
+    return bf16_to_f32(p[i]);
+  }
+  __device__ static __forceinline__ void store(uint16_t* p, size_t i, float x) {
+    p[i] = f32_to_bf16(x);
+  }
+};
+
+// ------------------------------------------------------------- scan arguments
+// Everything a scan kernel needs; device pointers, element counts in elements.
+struct ScanArgs {
+  const void* q;       // [BH, L, dk]
+  const void* k;       // [BH, L, dk]
+  const void* v;       // [BH, L, dv]
+  const float* alpha;  // [BH, L] or null (= 1)
+  const float* beta;   // [BH, L] (delta) or null
+  const void* gain;    // [BH, L, dk] precomputed write vectors (Kalman modes) or null
+  const float* state_in;  // [BH, dk, dv] or null (= 0)
+  float* state_out;       // [BH, dk, dv] or null
+  void* o;                // [BH, L, dv]
+  int BH, L, dk, dv, chunk;
+  int plain;  // 1: plain residual (delta only): b = (beta/alpha) k, v' = alpha v
+};
+
+// ------------------------------------------------------------------ launchers
+// Each returns a hipError_t (hipSuccess when the launch was enqueued).
+
+// Float32 vector-path chunk scan; in/out element types chosen at run time.
+// Gains (Kalman modes) are fp16 when gain_f16, else float32.
+hipError_t launch_scan_f32(const ScanArgs& a, bool in_bf16, bool out_bf16, bool gain_f16,
+                           hipStream_t s);
+// LDS bytes the float32 path needs for (dk, chunk), or 0 when it cannot run them.
+size_t scan_f32_lds_bytes(int dk, int chunk);
+
+// Matrix-core chunk scan for bf16 inputs (dk == 128, dv % 32 == 0, chunk == 64);
+// gains (if any) are fp16. `tbuf` holds scan_mfma_workspace_bytes(BH, L) bytes
+// for the per-chunk (I + A)^-1 matrices.
+hipError_t launch_tinv_mfma(const ScanArgs& a, void* tbuf, hipStream_t s);
+hipError_t launch_state_mfma(const ScanArgs& a, bool out_bf16, const void* tbuf, hipStream_t s);
+bool scan_mfma_supported(int dk, int dv, int chunk);
+size_t scan_mfma_workspace_bytes(int BH, int L);
+
+// Diagonal-covariance Kalman gains: writes gains [BH, L, dk] (fp16 or f32) and
+// the final covariance. `maps` is scratch of BH * nchunks * dk * 4 floats.
+hipError_t launch_diag_gains(const void* k, bool k_bf16, const float* alpha, const float* r,
+                             const float* cov_in, float* cov_out, float q_noise_var,
+                             void* gains, bool gains_f16, float* maps, int BH, int L, int dk,
+                             int chunk, hipStream_t s);
+
+// Full-covariance Kalman gains (dk <= 64): gains [BH, L, dk] and the final covariance.
+hipError_t launch_full_gains(const void* k, bool k_bf16, const float* alpha, const float* r,
+                             const float* cov_in, float* cov_out, float q_noise_var,
+                             void* gains, bool gains_f16, int BH, int L, int dk, hipStream_t s);
+
+// Copy the covariance / state through unchanged (L == 0).
+hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s);
+
+// One decode token per head.
+hipError_t launch_decode(const float* q, const float* k, const float* v, const float* alpha,
+                         const float* beta, const float* r, float* cov, float q_noise_var,
+                         float* state, float* o, float* m, int BH, int dk, int dv, int diag,
+                         int plain, hipStream_t s);
+
+// HOLA cache read + insert for one decode token per head.
+hipError_t launch_hola(const float* q, const float* k, const float* v, const float* m, int32_t t,
+                       float* cache_k, float* cache_v, float* cache_m, int32_t* cache_pos,
+                       int32_t* cache_count, const float* sink_logit, float* o_cache,
+                       float rms_eps, int B, int H, int dk, int dv, int w, hipStream_t s);
+
+}  // namespace kdn

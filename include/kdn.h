@@ -1,0 +1,215 @@
+/*
+ * kdn.h -- C ABI of the MI355X (gfx950) delta-rule / Kalman-Delta scan library.
+ *
+ * The library computes the recurrent associative-memory write of delta-rule
+ * linear attention and the uncertainty-aware (Kalman) writes derived from it,
+ * plus the HOLA write-magnitude score and its exact top-w key/value cache:
+ *
+ *   state S (d_k x d_v, float32), prediction S^T k, read-out o_t = S_t^T q_t.
+ *
+ *   delta write, gated residual  ("A Hippocampus for Linear Attention",
+ *   sec. 3.3 eq. (5) and sec. 3.5):
+ *       e_t = v_t - alpha_t S_{t-1}^T k_t,   S_t = alpha_t S_{t-1} + beta_t k_t e_t^T
+ *   delta write, plain residual: e_t = v_t - S_{t-1}^T k_t, same update.
+ *   Kalman write ("Kalman Delta Networks: Uncertainty-aware Associative
+ *   Memory", abstract; "Memory by Design: Probabilistic Sequence Layers",
+ *   abstract): the delta write with beta_t k_t replaced by the Kalman gain
+ *   g_t = P-_t k_t / (k_t^T P-_t k_t + r_t), where P-_t = alpha_t^2 P_{t-1} + Q_t I,
+ *   Q_t = (1 - alpha_t^2) sigma^2, and P_t = P-_t - P-_t k_t k_t^T P-_t / s_t.
+ *   FULL keeps the whole d_k x d_k covariance (the recursive-least-squares
+ *   update of "DeltaNet-PC", eq. (7), when alpha = 1, r = 1, sigma^2 = 0);
+ *   DIAG keeps a diagonal covariance, projected after every token by
+ *   mean-field inference: 1/p_i = 1/p-_i + k_i^2 / r_t.
+ *   score ("A Hippocampus for Linear Attention", sec. 3.3 eq. (6)):
+ *       m_t = ||write_t||_F = beta_t ||e_t|| (delta), ||g_t|| ||e_t|| (Kalman).
+ *
+ * Conventions for every entry point
+ *  - Every array argument is a DEVICE pointer owned by the caller; the library
+ *    keeps no pointer after the call returns. Layouts are row-major and
+ *    contiguous: sequences [B, H, L, d], per-token scalars [B, H, L], state
+ *    [B, H, d_k, d_v] (S[i][j] at i*d_v + j), covariance [B, H, d_k] (DIAG) or
+ *    [B, H, d_k, d_k] (FULL).
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream). Work is only
+ *    enqueued; the call never synchronises. The library never allocates device
+ *    memory: scratch space comes from the caller's `workspace`.
+ *  - Return value: KDN_OK (0); a negative KDN_ERR_* code when the arguments are
+ *    rejected, in which case nothing was enqueued and no device memory was
+ *    touched; or a positive hipError_t value when a launch failed.
+ *  - NaN or Inf inputs are not checked: they propagate into the outputs.
+ *  - Calls that share output or state buffers must be ordered on one stream.
+ */
+#ifndef KDN_H
+#define KDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types of q, k, v, o */
+#define KDN_F32 0
+#define KDN_BF16 1
+
+/* write modes */
+#define KDN_GAIN_DELTA 0 /* b_t = beta_t k_t                                   */
+#define KDN_GAIN_DIAG 1  /* diagonal-covariance Kalman gain, cov [B,H,d_k]       */
+#define KDN_GAIN_FULL 2  /* full-covariance Kalman gain, cov [B,H,d_k,d_k], d_k <= 64 */
+
+/* residual forms (delta mode only; the Kalman modes always use the gated form) */
+#define KDN_RESID_GATED 0 /* e = v - alpha S^T k */
+#define KDN_RESID_PLAIN 1 /* e = v - S^T k       */
+
+/* status codes */
+#define KDN_OK 0
+#define KDN_ERR_NULL_POINTER (-1)  /* a required pointer is NULL                   */
+#define KDN_ERR_BAD_SHAPE (-2)     /* a size is < 1 (L may be 0) or out of range   */
+#define KDN_ERR_BAD_CHUNK (-3)     /* chunk not in {16, 32, 64}                     */
+#define KDN_ERR_BAD_MODE (-4)      /* unknown mode / residual, or PLAIN with a gain */
+#define KDN_ERR_BAD_DTYPE (-5)     /* unknown element type                          */
+#define KDN_ERR_UNSUPPORTED (-6)   /* valid but not implemented for these sizes    */
+#define KDN_ERR_WORKSPACE (-7)     /* workspace missing or smaller than required   */
+#define KDN_ERR_BAD_CAPACITY (-8)  /* cache capacity w not in [1, 256]              */
+#define KDN_ERR_BAD_ALIGNMENT (-9) /* a pointer is not 16-byte aligned              */
+
+/* Static, human-readable message for a status code (never NULL). */
+const char *kdn_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int kdn_version(void);
+
+/*
+ * Bytes of device workspace kdn_scan_fwd needs for these arguments: the
+ * per-token Kalman gains and per-chunk covariance maps (Kalman modes) and, on
+ * the matrix-core path, the per-chunk (I + A)^-1 matrices of the chunk form
+ * (chunk * chunk fp16 values per chunk and head). 0 for the delta write on the
+ * float32 path. Pure host computation; 0 for invalid sizes.
+ */
+size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
+                               int mode, int in_dtype);
+
+/*
+ * Chunkwise-parallel forward scan over a whole sequence (all L tokens of all
+ * B*H heads), writing o_t = S_t^T q_t for every token.
+ *
+ *  q, k      [B,H,L,d_k] in_dtype. The state path assumes unit-norm keys
+ *            ("A Hippocampus for Linear Attention", sec. 3.4); the library
+ *            does not normalise them.
+ *  v         [B,H,L,d_v] in_dtype.
+ *  alpha     [B,H,L] float32 decay in (0, 1]; NULL means alpha = 1.
+ *  beta      [B,H,L] float32 write strength; required in DELTA mode, ignored
+ *            otherwise (the Kalman gain replaces it).
+ *  r         [B,H,L] float32 observation-noise variance > 0 (Kalman modes);
+ *            NULL means r = 1. Ignored in DELTA mode.
+ *  cov_in    prior covariance: [B,H,d_k] (DIAG, entries > 0) or
+ *            [B,H,d_k,d_k] (FULL, symmetric positive definite). Required in
+ *            the Kalman modes, ignored in DELTA mode.
+ *  cov_out   final covariance, same shape as cov_in; NULL = not written. May
+ *            alias cov_in.
+ *  q_noise_var  sigma^2 of the process noise Q_t = (1 - alpha_t^2) sigma^2 (>= 0).
+ *  state_in  [B,H,d_k,d_v] float32 initial state; NULL means S_0 = 0.
+ *  state_out [B,H,d_k,d_v] float32 final state; NULL = not written. May alias
+ *            state_in.
+ *  o         [B,H,L,d_v] out_dtype output (bf16 outputs are the float32 result
+ *            rounded to nearest even; that rounding alone is up to 2^-9 |o|,
+ *            so use float32 output when the error bar is relative to RMS(o)).
+ *  chunk     chunk length in tokens: 16, 32 or 64. The result does not depend on
+ *            it beyond rounding; L need not be a multiple of it.
+ *  mode      KDN_GAIN_*;  resid  KDN_RESID_* (PLAIN only with DELTA).
+ *  workspace device scratch of at least kdn_scan_workspace_size(...) bytes,
+ *            16-byte aligned (may be NULL when that size is 0).
+ * Sizes: B, H >= 1; L >= 0 (L = 0 copies state_in to state_out and cov_in to
+ * cov_out); 1 <= d_k, d_v <= 128; FULL mode needs d_k <= 64.
+ * Paths: bf16 inputs with d_k = 128, d_v a multiple of 32, chunk = 64 and
+ * 16-byte-aligned q, k, v, o run on the matrix cores: products in fp16 with
+ * float32 accumulation, float32 state; bf16 inputs are converted to fp16, so
+ * their magnitudes must stay below 65504 (values below 2^-14 lose precision as
+ * fp16 subnormals). Every other combination runs the float32 vector path.
+ */
+int kdn_scan_fwd(const void *q, const void *k, const void *v, int in_dtype,
+                 const float *alpha, const float *beta, const float *r,
+                 const float *cov_in, float *cov_out, float q_noise_var,
+                 const float *state_in, float *state_out,
+                 void *o, int out_dtype,
+                 int B, int H, int L, int d_k, int d_v, int chunk, int mode, int resid,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* phases of kdn_scan_fwd_phase */
+#define KDN_PHASE_ALL 0     /* everything: the same as kdn_scan_fwd                     */
+#define KDN_PHASE_PREPARE 1 /* the state-independent part, into the workspace          */
+#define KDN_PHASE_STATE 2   /* the sequential state scan that consumes the workspace   */
+
+/*
+ * kdn_scan_fwd split in two enqueued parts. PREPARE does everything that does
+ * not depend on the state: the covariance recursion and Kalman gains (it
+ * writes cov_out) and, on the matrix-core path, the per-chunk inverses
+ * (I + A)^-1 of the chunk form; it writes only the workspace and cov_out.
+ * STATE then runs the chunk-by-chunk state scan and writes o and state_out.
+ * A STATE call must see the workspace of a PREPARE call made with the same
+ * arguments and inputs (same stream, or ordered by the caller); PREPARE may
+ * run ahead on another stream, e.g. for the next batch. Arguments, checks and
+ * status codes are those of kdn_scan_fwd; an unknown phase is KDN_ERR_BAD_MODE.
+ */
+int kdn_scan_fwd_phase(int phase, const void *q, const void *k, const void *v, int in_dtype,
+                       const float *alpha, const float *beta, const float *r,
+                       const float *cov_in, float *cov_out, float q_noise_var,
+                       const float *state_in, float *state_out,
+                       void *o, int out_dtype,
+                       int B, int H, int L, int d_k, int d_v, int chunk, int mode, int resid,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step: the same write and read as kdn_scan_fwd for a single token
+ * per head, updating the state (and, in DIAG mode, the covariance) in place.
+ * Float32 throughout ("A Hippocampus for Linear Attention", secs. 3.3, 3.5).
+ *
+ *  q, k      [B,H,d_k] float32;  v [B,H,d_v] float32.
+ *  alpha     [B,H] float32 (NULL = 1);  beta [B,H] float32 (DELTA mode).
+ *  r         [B,H] float32 (DIAG mode, NULL = 1).
+ *  cov       [B,H,d_k] float32, in/out (DIAG mode only, else ignored).
+ *  state     [B,H,d_k,d_v] float32, in/out.
+ *  o         [B,H,d_v] float32 out: S_t^T q_t after the write.
+ *  m         [B,H] float32 out: the write score; NULL = not written.
+ * Sizes: B, H >= 1; 1 <= d_k, d_v <= 128. Modes DELTA and DIAG.
+ */
+int kdn_step_decode(const float *q, const float *k, const float *v,
+                    const float *alpha, const float *beta, const float *r,
+                    float *cov, float q_noise_var, float *state,
+                    float *o, float *m,
+                    int B, int H, int d_k, int d_v, int mode, int resid, void *stream);
+
+/*
+ * HOLA exact cache for one decoding token per head ("A Hippocampus for Linear
+ * Attention", sec. 3.3 (top-w cache by write score), sec. 3.4 eq. (7) (read),
+ * sec. 3.2 eq. (4) (softmax read)).
+ *
+ * First the read over the visible set: the cached tokens, the current token
+ * and, if sink_logit is given, one null sink (value 0, logit sink_logit[h]):
+ *     qn = q / sqrt(mean(q^2) + rms_eps), kn likewise,  l_j = qn . kn_j / sqrt(d_k),
+ *     o_cache = sum_j softmax(l)_j v_j.
+ * Then the insert: the cache keeps the w tokens with the largest score m
+ * (ties: the earlier token). While count < w the token goes to slot `count`;
+ * afterwards it replaces the slot with the smallest (m, then largest pos) when
+ * its m is strictly larger. Comparisons are on the float32 scores.
+ *
+ *  q, k      [B,H,d_k] float32;  v [B,H,d_v] float32;  m [B,H] float32 score.
+ *  t         absolute token position (stored in cache_pos; tie-break).
+ *  cache_k   [B,H,w,d_k] float32, cache_v [B,H,w,d_v] float32 (exact copies),
+ *  cache_m   [B,H,w] float32, cache_pos [B,H,w] int32, cache_count [B,H] int32:
+ *            in/out. Start from cache_count = 0.
+ *  sink_logit [H] float32 or NULL (no sink).
+ *  o_cache   [B,H,d_v] float32 out.
+ * Sizes: B, H >= 1; 1 <= d_k, d_v <= 128; 1 <= w <= 256; rms_eps >= 0.
+ */
+int hola_cache_update(const float *q, const float *k, const float *v, const float *m,
+                      int32_t t, float *cache_k, float *cache_v, float *cache_m,
+                      int32_t *cache_pos, int32_t *cache_count, const float *sink_logit,
+                      float *o_cache, float rms_eps, int B, int H, int d_k, int d_v, int w,
+                      void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDN_H */

@@ -1,0 +1,169 @@
+"""The C-ABI library loads, exports exactly what include/kdn.h declares, and
+rejects bad arguments with the documented status codes before touching a
+device (these calls run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kdn.h")
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([a-z_][a-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+def _header_constants():
+    vals = {}
+    for name, val in re.findall(r"#define\s+(KDN_[A-Z0-9_]+)\s+\(?(-?\d+)\)?", open(HEADER).read()):
+        vals[name] = int(val)
+    return vals
+
+
+@pytest.fixture(scope="module")
+def kdn():
+    import delta_rule_scans_amd as k
+    return k
+
+
+def test_exports_match_header(kdn):
+    declared = _header_functions()
+    assert declared == sorted(["hola_cache_update", "kdn_scan_fwd", "kdn_scan_fwd_phase",
+                               "kdn_scan_workspace_size", "kdn_status_string", "kdn_step_decode",
+                               "kdn_version"])
+    out = subprocess.run(["nm", "-D", "--defined-only", kdn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines()
+                      if " T " in line and not line.split()[-1].startswith("_"))
+    assert exported == declared
+    for name in declared:
+        assert hasattr(kdn.lib, name)
+
+
+def test_status_strings_and_constants(kdn):
+    c = _header_constants()
+    assert c["KDN_OK"] == 0
+    codes = [v for k, v in c.items() if k.startswith("KDN_ERR_")]
+    assert len(codes) == len(set(codes)) and all(v < 0 for v in codes)
+    for v in codes:
+        s = kdn.kdn_status_string(v)
+        assert s and s != "unknown status"
+    assert kdn.kdn_status_string(0) == "ok"
+    assert kdn.lib.kdn_version() >= 100
+    assert (c["KDN_GAIN_DELTA"], c["KDN_GAIN_DIAG"], c["KDN_GAIN_FULL"]) == (0, 1, 2)
+    assert (kdn.MODES["delta"], kdn.MODES["diag"], kdn.MODES["full"]) == (0, 1, 2)
+
+
+def test_workspace_size(kdn):
+    assert kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 64, "delta", kdn.F32) == 0
+    assert kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 32, "delta", kdn.BF16) == 0
+    tinv = 4 * 16 * 64 * 64 * 64 * 2          # per-chunk (I + A)^-1 in fp16 (matrix-core path)
+    assert kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 64, "delta", kdn.BF16) == tinv
+    ws = kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 64, "diag", kdn.BF16)
+    gains = 4 * 16 * 4096 * 128 * 2
+    maps = 4 * 16 * 64 * 128 * 16
+    assert ws >= gains + maps + tinv
+    assert kdn.kdn_scan_workspace_size(1, 1, 64, 16, 16, 16, "full", kdn.F32) >= 64 * 16 * 4
+    assert kdn.kdn_scan_workspace_size(1, 1, 64, 16, 16, 17, "full", kdn.F32) == 0
+
+
+# Fake (never dereferenced) device addresses: every call below must be rejected
+# by the host-side checks before any launch.
+P = 0x10000
+
+
+def _scan(kdn, **kw):
+    a = dict(q=P, k=P, v=P, in_dtype=1, alpha=P, beta=P, r=None, cov_in=None, cov_out=None,
+             qvar=0.0, state_in=None, state_out=None, o=P, out_dtype=1, B=1, H=1, L=64, dk=128,
+             dv=128, chunk=64, mode=0, resid=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return kdn.lib.kdn_scan_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["alpha"], a["beta"],
+                                a["r"], a["cov_in"], a["cov_out"], a["qvar"], a["state_in"],
+                                a["state_out"], a["o"], a["out_dtype"], a["B"], a["H"], a["L"],
+                                a["dk"], a["dv"], a["chunk"], a["mode"], a["resid"], a["ws"],
+                                a["wsb"], a["stream"])
+
+
+def test_scan_rejections(kdn):
+    c = _header_constants()
+    assert _scan(kdn, q=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _scan(kdn, o=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _scan(kdn, beta=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _scan(kdn, mode=1) == c["KDN_ERR_NULL_POINTER"]            # DIAG without cov_in
+    assert _scan(kdn, in_dtype=7) == c["KDN_ERR_BAD_DTYPE"]
+    assert _scan(kdn, out_dtype=-1) == c["KDN_ERR_BAD_DTYPE"]
+    assert _scan(kdn, mode=3) == c["KDN_ERR_BAD_MODE"]
+    assert _scan(kdn, resid=2) == c["KDN_ERR_BAD_MODE"]
+    assert _scan(kdn, mode=1, resid=1, cov_in=P) == c["KDN_ERR_BAD_MODE"]
+    for bad in (dict(B=0), dict(H=-1), dict(L=-1), dict(dk=0), dict(dv=129), dict(dk=256)):
+        assert _scan(kdn, **bad) == c["KDN_ERR_BAD_SHAPE"], bad
+    assert _scan(kdn, qvar=-1.0) == c["KDN_ERR_BAD_SHAPE"]
+    assert _scan(kdn, qvar=float("nan")) == c["KDN_ERR_BAD_SHAPE"]
+    for ch in (0, 8, 17, 128, 256):
+        assert _scan(kdn, chunk=ch) == c["KDN_ERR_BAD_CHUNK"], ch
+    assert _scan(kdn, mode=2, cov_in=P, dk=128) == c["KDN_ERR_UNSUPPORTED"]
+    assert _scan(kdn, mode=2, cov_in=P, dk=64) == c["KDN_ERR_WORKSPACE"]
+    # an unknown phase is rejected like an unknown mode
+    assert kdn.lib.kdn_scan_fwd_phase(3, P, P, P, 1, P, P, None, None, None, 0.0, None, None, P, 1,
+                                      1, 1, 64, 128, 128, 64, 0, 0, None, 0, None) == c["KDN_ERR_BAD_MODE"]
+    need = kdn.kdn_scan_workspace_size(1, 1, 64, 128, 128, 64, "diag", kdn.BF16)
+    assert _scan(kdn, mode=1, cov_in=P, ws=P, wsb=need - 1) == c["KDN_ERR_WORKSPACE"]
+    assert _scan(kdn, mode=1, cov_in=P, ws=P + 4, wsb=need) == c["KDN_ERR_WORKSPACE"]
+
+
+def _decode(kdn, **kw):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, r=None, cov=None, qvar=0.0, state=P, o=P, m=P, B=2,
+             H=2, dk=128, dv=128, mode=0, resid=0, stream=None)
+    a.update(kw)
+    return kdn.lib.kdn_step_decode(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["r"],
+                                   a["cov"], a["qvar"], a["state"], a["o"], a["m"], a["B"],
+                                   a["H"], a["dk"], a["dv"], a["mode"], a["resid"], a["stream"])
+
+
+def test_decode_rejections(kdn):
+    c = _header_constants()
+    assert _decode(kdn, state=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _decode(kdn, beta=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _decode(kdn, mode=1) == c["KDN_ERR_NULL_POINTER"]
+    assert _decode(kdn, mode=2) == c["KDN_ERR_UNSUPPORTED"]
+    assert _decode(kdn, mode=5) == c["KDN_ERR_BAD_MODE"]
+    assert _decode(kdn, mode=1, resid=1, cov=P) == c["KDN_ERR_BAD_MODE"]
+    assert _decode(kdn, dk=0) == c["KDN_ERR_BAD_SHAPE"]
+    assert _decode(kdn, dv=200) == c["KDN_ERR_BAD_SHAPE"]
+    assert _decode(kdn, B=0) == c["KDN_ERR_BAD_SHAPE"]
+
+
+def _hola(kdn, **kw):
+    a = dict(q=P, k=P, v=P, m=P, t=0, ck=P, cv=P, cm=P, cp=P, cc=P, sink=None, oc=P, eps=1e-6,
+             B=1, H=1, dk=128, dv=128, w=64, stream=None)
+    a.update(kw)
+    return kdn.lib.hola_cache_update(a["q"], a["k"], a["v"], a["m"], a["t"], a["ck"], a["cv"],
+                                     a["cm"], a["cp"], a["cc"], a["sink"], a["oc"], a["eps"],
+                                     a["B"], a["H"], a["dk"], a["dv"], a["w"], a["stream"])
+
+
+def test_hola_rejections(kdn):
+    c = _header_constants()
+    for w in (0, -3, 257, 1024):
+        assert _hola(kdn, w=w) == c["KDN_ERR_BAD_CAPACITY"]
+    assert _hola(kdn, cc=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _hola(kdn, m=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _hola(kdn, dk=129) == c["KDN_ERR_BAD_SHAPE"]
+    assert _hola(kdn, eps=-1.0) == c["KDN_ERR_BAD_SHAPE"]
+    assert _hola(kdn, eps=float("nan")) == c["KDN_ERR_BAD_SHAPE"]
+
+
+def test_product_package_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "delta_rule_scans_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f
