@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Benchmark of the delta-rule / Kalman-Delta scan library on one MI355X.
+
+Prints ONE JSON line. The headline value is the forward-scan throughput of the
+gated delta workload (B=4, H=16, L=4096, d_k=d_v=128, chunk 64, bf16 q/k/v,
+float32 alpha/beta, float32 output and state), in tokens/s (a token is one
+position of one batch row, all H heads). One step = one kdn_scan_fwd call:
+the parallel (I + A)^-1 kernel plus the sequential state kernel. Inputs are
+resident in HBM before timing starts.
+
+Extra fields: the roofline of the dominant (state) kernel, timed on its own
+stream with events around its phase; the fp64 oracle timed on a bounded
+sample on the host cores; and (unless --quick) the decode + HOLA cache step,
+the diagonal Kalman scan and the long-context scan.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "scan tokens/sec (fwd, H=16, d=128) + % MFMA peak; decode % HBM BW"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak, published
+
+
+def scan_flops_per_token_head(C, dk, dv):
+    """Algorithmic flops of the chunk form per token and head (lower triangles
+    counted once): Grams K B^T and Q B^T, T = (I + A)^-1, T X, P U and the three
+    state products K S, Q S and the state update."""
+    return C * (3 * dk + 2 * dv) + C * C / 3 + 6 * dk * dv
+
+
+def scan_bytes(B, H, L, dk, dv, in_bytes=2, out_bytes=4, extra_per_token=0, state_out=True):
+    """Algorithmic HBM bytes of one scan: q, k, v read once, alpha/beta (+extra)
+    read once, o written once, the final state written once."""
+    per_tok = (2 * dk + dv) * in_bytes + 8 + extra_per_token + dv * out_bytes
+    return B * H * L * per_tok + (B * H * dk * dv * 4 if state_out else 0)
+
+
+DECODE_BYTES_PER_HEAD = (
+    2 * 128 * 128 * 4      # state read + write
+    + 2 * 64 * 128 * 4     # cache keys and values read
+    + 64 * 8               # cache scores and positions read
+    + 3 * 128 * 4 + 8      # q, k, v, alpha, beta
+    + 2 * 128 * 4 + 4 + 4  # o, o_cache, m written; m read back
+    + 2 * 128 * 4 + 8 + 8  # inserted key/value, score/position, count read + write
+)
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True):
+    import workloads
+    cfg = workloads.WORKLOADS[name]
+    B, H, L, dk, dv, C = cfg["B"], cfg["H"], cfg["L"], cfg["dk"], cfg["dv"], cfg["chunk"]
+    inp = workloads.named_scan_inputs(name)
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("q", "k", "v")}
+    for n in t:
+        t[n] = t[n].to(torch.bfloat16)
+    alpha = torch.from_numpy(inp["alpha"]).to(dev)
+    beta = torch.from_numpy(inp["beta"]).to(dev)
+    r = torch.from_numpy(inp["r"]).to(dev) if inp["r"] is not None else None
+    del inp
+    cov_in = cov_out = None
+    if mode == "diag":
+        cov_in = torch.full((B, H, dk), cfg["cov_init"], device=dev)
+        cov_out = torch.empty_like(cov_in)
+    o = torch.empty((B, H, L, dv), dtype=torch.float32, device=dev)
+    s_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    need = kdn.kdn_scan_workspace_size(B, H, L, dk, dv, C, mode, kdn.BF16)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    qvar = cfg.get("q_noise_var", 0.0)
+
+    def step(phase="all"):
+        kdn.kdn_scan_fwd(t["q"], t["k"], t["v"], alpha=alpha, beta=beta, r=r, cov_in=cov_in,
+                         cov_out=cov_out, q_noise_var=qvar, state_out=s_out, o=o, chunk=C,
+                         mode=mode, workspace=ws, phase=phase)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    res = dict(ms_per_step=ms, tokens_per_s=B * L / (ms * 1e-3), B=B, H=H, L=L, dk=dk, dv=dv, C=C)
+    if per_phase:
+        ev = _events(torch, 3 * steps)
+        for i in range(steps):
+            ev[3 * i].record()
+            step("prepare")
+            ev[3 * i + 1].record()
+            step("state")
+            ev[3 * i + 2].record()
+        torch.cuda.synchronize()
+        res["prepare_ms"] = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)) / steps
+        res["state_ms"] = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)) / steps
+    return res
+
+
+def bench_decode(kdn, torch, steps, warmup):
+    """Decode + HOLA cache at B=256, H=32, d=128, w=64, timed after the cache is full."""
+    import workloads
+    cfg = workloads.WORKLOADS["decode"]
+    B, H, d, w = cfg["B"], cfg["H"], cfg["dk"], cfg["w"]
+    dev = torch.device("cuda:0")
+    warmup = max(warmup, w)          # steady state: every step reads a full cache
+    total = warmup + steps
+    inputs = []
+    for s in range(total):
+        st = workloads.decode_step_inputs(s, B, H, d, d)
+        inputs.append({n: torch.from_numpy(x).to(dev) for n, x in st.items()})
+    state = torch.zeros((B, H, d, d), device=dev)
+    cache = kdn.HolaCache(B, H, d, d, w, device=dev)
+    o = torch.empty((B, H, d), device=dev)
+    oc = torch.empty((B, H, d), device=dev)
+    m = torch.empty((B, H), device=dev)
+
+    def step(i):
+        x = inputs[i]
+        kdn.kdn_step_decode(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, o=o, m=m)
+        kdn.hola_cache_update(x["q"], x["k"], x["v"], m, i, cache, o_cache=oc)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for i in range(warmup, total):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    gbs = B * H * DECODE_BYTES_PER_HEAD / (ms * 1e-3) / 1e9
+    return dict(ms_per_step=round(ms, 5), tokens_per_s=round(B / (ms * 1e-3), 1),
+                bytes_per_step=B * H * DECODE_BYTES_PER_HEAD, achieved_gbs=round(gbs, 1),
+                hbm_frac=round(gbs / HBM_PEAK_GBS, 4), steps=steps, warmup=warmup,
+                config="decode + HOLA cache, B=256 H=32 d=128 fp32, w=64, cache full")
+
+
+def cpu_baseline(name="gated", seconds_target=15.0):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    the first n (batch, head) sequences at full length, on all host threads."""
+    import oracle
+    import workloads
+    cfg = workloads.WORKLOADS[name]
+    B, H, L = cfg["B"], cfg["H"], cfg["L"]
+    inp = workloads.named_scan_inputs(name)
+    q, k, v = (inp[n].reshape(B * H, L, -1) for n in ("q", "k", "v"))
+    a, b = inp["alpha"].reshape(B * H, L), inp["beta"].reshape(B * H, L)
+    threads = oracle.num_threads()
+    # calibrate with one sequence per thread, then size the sample
+    n = min(B * H, threads)
+    t0 = time.perf_counter()
+    oracle.scan(q[None, :n], k[None, :n], v[None, :n], alpha=a[None, :n], beta=b[None, :n],
+                want_m=False)
+    t1 = time.perf_counter() - t0
+    rounds = max(1, min(B * H // n, int(seconds_target / max(t1, 1e-3))))
+    n2 = min(B * H, n * rounds)
+    t0 = time.perf_counter()
+    oracle.scan(q[None, :n2], k[None, :n2], v[None, :n2], alpha=a[None, :n2], beta=b[None, :n2],
+                want_m=False)
+    dt = time.perf_counter() - t0
+    token_heads_per_s = n2 * L / dt
+    return dict(value=round(token_heads_per_s / H, 1), unit="tokens/s", cores=threads,
+                kind="oracle",
+                sample=f"{n2} of {B * H} (batch, head) sequences of the gated workload at full "
+                       f"length {L}, fp64 sequential recurrence, {dt:.1f} s; tokens/s = "
+                       f"token-heads/s / H")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the scan shards over heads with no communication, see the design notes",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import delta_rule_scans_amd as kdn
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        x = torch.ones(n, device="cuda")
+        y = torch.empty_like(x)
+        y.copy_(x)
+        torch.cuda.synchronize()
+        del x, y
+
+    main_res = bench_scan(kdn, torch, "gated", args.steps, args.warmup)
+    B, H, L, dk, dv, C = (main_res[k] for k in ("B", "H", "L", "dk", "dv", "C"))
+    nbytes = scan_bytes(B, H, L, dk, dv)
+    flops = B * H * L * scan_flops_per_token_head(C, dk, dv)
+    state_s = main_res["state_ms"] * 1e-3
+    achieved = nbytes / state_s / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(main_res["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 matrix products, f32 accumulation and state",
+        "data": "synthetic",
+        "config": {"workload": "gated delta scan B=4 H=16 L=4096 d_k=d_v=128 chunk 64, "
+                               "bf16 q/k/v, f32 alpha/beta/o/state",
+                   "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "scan_kernel (sequential state scan)",
+                     "kernel_ms": round(main_res["state_ms"], 5),
+                     "algorithmic_bytes": nbytes},
+        "mfma": {"algorithmic_tflops_per_step": round(flops / 1e12, 3),
+                 "frac_of_peak_step": round(flops / (main_res["ms_per_step"] * 1e-3) / 1e12
+                                            / MFMA_F16_PEAK_TFLOPS, 4),
+                 "frac_of_peak_state_kernel": round(flops / state_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                 "peak_tflops": MFMA_F16_PEAK_TFLOPS},
+        "phases_ms": {"prepare": round(main_res["prepare_ms"], 5),
+                      "state": round(main_res["state_ms"], 5)},
+    }
+    if not args.quick:
+        extra = {}
+        extra["decode"] = bench_decode(kdn, torch, steps=max(8, args.steps), warmup=args.warmup)
+        for name, mode in (("kdn_diag", "diag"), ("long", "delta")):
+            r = bench_scan(kdn, torch, name, max(2, args.steps // 4), 1, mode=mode, per_phase=True)
+            nb = scan_bytes(r["B"], r["H"], r["L"], r["dk"], r["dv"],
+                            extra_per_token=4 if mode == "diag" else 0)
+            extra[name] = dict(ms_per_step=round(r["ms_per_step"], 5),
+                               tokens_per_s=round(r["tokens_per_s"], 1),
+                               prepare_ms=round(r["prepare_ms"], 5),
+                               state_ms=round(r["state_ms"], 5),
+                               hbm_frac_step=round(nb / (r["ms_per_step"] * 1e-3) / 1e9
+                                                   / HBM_PEAK_GBS, 4))
+            torch.cuda.empty_cache()
+        line["extra"] = extra
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
