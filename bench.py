@@ -54,6 +54,20 @@ DECODE_BYTES_PER_HEAD = (
 )
 
 
+def measured_traffic(kernel_ms):
+    """HBM bytes per launch of the state kernel from the committed counter runs
+    (profiles/*_traffic.json), or None when the kernel source changed since."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "scan_gated_B4H16L4096_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, rec["source"])
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["hbm_read_bytes"] + rec["hbm_write_bytes"]
+
+
 def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
@@ -153,33 +167,34 @@ def bench_decode(kdn, torch, steps, warmup):
 
 def cpu_baseline(name="gated", seconds_target=15.0):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
-    the first n (batch, head) sequences at full length, on all host threads."""
+    all (batch, head) sequences at full length, repeated until about
+    `seconds_target` seconds of host time, on all host threads."""
     import oracle
     import workloads
     cfg = workloads.WORKLOADS[name]
     B, H, L = cfg["B"], cfg["H"], cfg["L"]
     inp = workloads.named_scan_inputs(name)
-    q, k, v = (inp[n].reshape(B * H, L, -1) for n in ("q", "k", "v"))
-    a, b = inp["alpha"].reshape(B * H, L), inp["beta"].reshape(B * H, L)
+    q, k, v = (inp[n].reshape(1, B * H, L, -1) for n in ("q", "k", "v"))
+    a, b = inp["alpha"].reshape(1, B * H, L), inp["beta"].reshape(1, B * H, L)
     threads = oracle.num_threads()
-    # calibrate with one sequence per thread, then size the sample
-    n = min(B * H, threads)
+
+    def run():
+        oracle.scan(q, k, v, alpha=a, beta=b, want_m=False)
+
     t0 = time.perf_counter()
-    oracle.scan(q[None, :n], k[None, :n], v[None, :n], alpha=a[None, :n], beta=b[None, :n],
-                want_m=False)
+    run()
     t1 = time.perf_counter() - t0
-    rounds = max(1, min(B * H // n, int(seconds_target / max(t1, 1e-3))))
-    n2 = min(B * H, n * rounds)
+    reps = max(1, int(round(seconds_target / max(t1, 1e-3))) - 1)
     t0 = time.perf_counter()
-    oracle.scan(q[None, :n2], k[None, :n2], v[None, :n2], alpha=a[None, :n2], beta=b[None, :n2],
-                want_m=False)
-    dt = time.perf_counter() - t0
-    token_heads_per_s = n2 * L / dt
+    for _ in range(reps):
+        run()
+    dt = time.perf_counter() - t0 + t1
+    token_heads_per_s = (reps + 1) * B * H * L / dt
     return dict(value=round(token_heads_per_s / H, 1), unit="tokens/s", cores=threads,
                 kind="oracle",
-                sample=f"{n2} of {B * H} (batch, head) sequences of the gated workload at full "
-                       f"length {L}, fp64 sequential recurrence, {dt:.1f} s; tokens/s = "
-                       f"token-heads/s / H")
+                sample=f"the whole gated workload ({B * H} (batch, head) sequences of length {L}) "
+                       f"{reps + 1} times, fp64 sequential recurrence, {dt:.1f} s; "
+                       f"tokens/s = token-heads/s / H")
 
 
 def main():
@@ -234,7 +249,8 @@ def main():
                                "bf16 q/k/v, f32 alpha/beta/o/state",
                    "global_batch": B, "seq_len": L, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(main_res["state_ms"]),
                      "kernel": "scan_kernel (sequential state scan)",
                      "kernel_ms": round(main_res["state_ms"], 5),
                      "algorithmic_bytes": nbytes},
