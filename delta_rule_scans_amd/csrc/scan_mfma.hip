@@ -354,16 +354,84 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
 
 // =====================================================================  state kernel
 //
-// Warp-specialised: wavefronts 0-7 compute, wavefronts 8-15 move data.
-//  * The compute wavefronts never load from global memory (they only store
-//    o), so nothing in their chunk loop waits on the memory counters.
-//    Wavefront w owns token block rb = w % 4 and value block cb = w / 4 of
-//    the 64 x 32 chunk outputs, and the state tiles (d_k blocks 2 rb, 2 rb + 1;
-//    value block cb), 128 x 32 in all, in float32 accumulators.
-//  * The producer wavefronts load chunk c + 3 while chunk c is computed
-//    (two register buffers), and convert chunk c + 1 into the LDS buffer
-//    (c + 1) % 2 that chunk c - 1 has released. The two roles run separate
-//    loops with the same barriers, so their registers never overlap.
+// One workgroup per (head, 32-column slice of d_v), four wavefronts with
+// fixed roles and one workgroup barrier per step. Step c:
+//  * wavefront 0 carries the sequential chain of chunk c:
+//      K S (16 products), X = v_scale V - g K S, U = T X (6), and the state
+//      update S = g_n S + (diag(w) B)^T U (16).
+//    The float32 state slice (128 x 32) lives in its 32x32 accumulators for
+//    the whole sequence, and every intermediate (S, X, U in fp16) goes from
+//    one product's accumulator straight into the next product's operand
+//    registers (see "operand k order" below). The transposed write vectors
+//    come from the staged [token][d_k] tile by ds_read_b64_tr_b16. Chunk c's
+//    incoming state and its residuals U go to an exchange buffer.
+//  * wavefront 1 writes the outputs of chunk c - 1 from the exchange buffer:
+//    O = diag(g) Q S + P U (22 products).
+//  * wavefronts 2-3 stage into LDS what wavefront 0 reads for chunk c + 1 (K
+//    and, for the Kalman writes, the gains; V; T; scalars) and what wavefront
+//    1 reads for chunk c (Q unless the write is a Kalman one, P, g), from
+//    registers loaded two steps earlier with fully coalesced 1 KB loads.
+// The chain never touches global memory. Loads of rows past the end of the
+// sequence go through buffer descriptors sized to the head, which return
+// zeros; output stores past it are dropped the same way.
+//
+// Operand k order: the 32x32x16 accumulator gives lane (h = lane / 32, col)
+// the rows 8 j + 4 h + r (j, r = 0..3) of a 32-row block. Registers 8 i ..
+// 8 i + 7 of such a block are used as the operand of k step i + 2 (block),
+// so within a 16-wide k step, operand slot e of half h stands for index
+// 8 (e / 4) + 4 h + e % 4. Operands read from memory follow the same order:
+// two 8-byte reads at columns 4 h and 8 + 4 h of the k step.
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+__device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ half8 cat(half4 a, half4 b) {
+  return half8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+__device__ __forceinline__ half4 ld4(const _Float16* p) {
+  return *reinterpret_cast<const half4*>(p);
+}
+// operand of one 16-wide k step from a row whose k step starts at p
+__device__ __forceinline__ half8 ld_op(const _Float16* p, int h) {
+  return cat(ld4(p + 4 * h), ld4(p + 8 + 4 * h));
+}
+
+// Transposing LDS read: within each group of 16 lanes, lane i receives element
+// i % 4 of the 8-byte blocks addressed by lanes i / 4, i / 4 + 4, i / 4 + 8,
+// i / 4 + 12. A group whose lanes address 4 rows x 4 column quads
+// (lane 4 r + q: row r, quad q) returns one column per lane, 4 rows deep.
+__device__ __forceinline__ half4 ld_tr(const _Float16* p) {
+  const short4v v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v*)(p));
+  return __builtin_bit_cast(half4, v);
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  // raw buffer: stride 0, accesses at offsets >= `bytes` read 0 / are dropped
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes > 0x7fffffffu ? 0x7fffffffu : bytes),
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// 4 bf16 values (8 bytes) -> 4 fp16 values.
+__device__ __forceinline__ half4 bf16x4_to_f16x4(uint2 u) {
+  half4 r;
+  r[0] = (_Float16)__uint_as_float(u.x << 16);
+  r[1] = (_Float16)__uint_as_float(u.x & 0xffff0000u);
+  r[2] = (_Float16)__uint_as_float(u.y << 16);
+  r[3] = (_Float16)__uint_as_float(u.y & 0xffff0000u);
+  return r;
+}
 
 struct StateArgs {
   const uint16_t* q;     // bf16 [BH, L, DK]
@@ -374,156 +442,177 @@ struct StateArgs {
   const float* state_in;
   float* state_out;
   void* o;
-  int out_bf16;
   int BH, L, dv, nchunks, ntiles;
 };
 
-constexpr int NW_COMPUTE = 8;
-constexpr int NW_PROD = 8;
-constexpr int NT_STATE = 64 * (NW_COMPUTE + NW_PROD);
-constexpr int NT_PROD = 64 * NW_PROD;
+constexpr int NT_STATE = 256;
+constexpr int VP = DV + 8;  // fp16 pitch of the staged V rows
 
-// One LDS buffer of chunk inputs.
-struct StageBuf {
-  _Float16* q;     // [C][KP] fp16
-  _Float16* k;     // [C][KP] fp16
-  _Float16* t;     // [C][CP] T
-  _Float16* p;     // [C][CP] P
-  _Float16* vt;    // [DV][CP] V^T
-  float* gam;      // [C] g
-  float* w;        // [C] w
-  float* vs;       // [C] value scale
-};
-
-constexpr size_t kStageBytes = (size_t)2 * C * KP * 2 + (size_t)2 * C * CP * 2 +
-                               (size_t)DV * CP * 2 + (size_t)3 * C * 4;
-
+// LDS: chain stages [2] {K [C][KP]; gains [C][KP] (Kalman writes); T [C][CP];
+// V [C][VP]; g, w, value scale [C]}, output stages [2] {Q [C][KP] (delta
+// write); P [C][CP]; g [C]}, exchange buffers [2] {S (8 k steps), U (4 k
+// steps)}, 16 bytes per lane and k step in wavefront-0 register order.
+constexpr size_t kStK = (size_t)C * KP * 2;
+constexpr size_t kStT = (size_t)C * CP * 2;
+constexpr size_t kStV = (size_t)C * VP * 2;
+constexpr size_t kExBytes = (size_t)12 * 64 * 16;
+__host__ __device__ constexpr size_t chain_stage_bytes(bool gain) {
+  return kStK * (gain ? 2 : 1) + kStT + kStV + (size_t)3 * C * 4;
+}
+__host__ __device__ constexpr size_t out_stage_bytes(bool gain) {
+  return (gain ? 0 : kStK) + kStT + (size_t)C * 4;
+}
 size_t state_lds_bytes(bool gain) {
-  return 2 * kStageBytes + (gain ? (size_t)C * KP * 2 : 0)  // stage buffers, gains
-         + (size_t)DV * KP * 2                              // S^T
-         + (size_t)3 * DV * CP * 2;                         // X^T, U^T, (w U)^T
+  return 2 * chain_stage_bytes(gain) + 2 * out_stage_bytes(gain) + 2 * kExBytes;
 }
 
-__device__ __forceinline__ StageBuf carve_stage(unsigned char* p) {
-  StageBuf b;
-  b.q = reinterpret_cast<_Float16*>(p); p += C * KP * 2;
-  b.k = reinterpret_cast<_Float16*>(p); p += C * KP * 2;
-  b.t = reinterpret_cast<_Float16*>(p); p += C * CP * 2;
-  b.p = reinterpret_cast<_Float16*>(p); p += C * CP * 2;
-  b.vt = reinterpret_cast<_Float16*>(p); p += DV * CP * 2;
-  b.gam = reinterpret_cast<float*>(p); p += C * 4;
-  b.w = reinterpret_cast<float*>(p); p += C * 4;
-  b.vs = reinterpret_cast<float*>(p);
-  return b;
+struct ChainStage {
+  _Float16* k;   // K
+  _Float16* b;   // write vectors: K (delta) or the gains
+  _Float16* t;
+  _Float16* v;
+  float* g;
+  float* w;
+  float* vs;
+};
+struct OutStage {
+  _Float16* q;   // delta write only
+  _Float16* p;
+  float* g;
+};
+template <bool GAIN>
+__device__ __forceinline__ ChainStage chain_stage(unsigned char* lds, int buf) {
+  unsigned char* p = lds + (size_t)buf * chain_stage_bytes(GAIN);
+  ChainStage s;
+  s.k = reinterpret_cast<_Float16*>(p); p += kStK;
+  s.b = s.k;
+  if (GAIN) { s.b = reinterpret_cast<_Float16*>(p); p += kStK; }
+  s.t = reinterpret_cast<_Float16*>(p); p += kStT;
+  s.v = reinterpret_cast<_Float16*>(p); p += kStV;
+  s.g = reinterpret_cast<float*>(p); p += C * 4;
+  s.w = reinterpret_cast<float*>(p); p += C * 4;
+  s.vs = reinterpret_cast<float*>(p);
+  return s;
+}
+template <bool GAIN>
+__device__ __forceinline__ OutStage out_stage(unsigned char* lds, int buf) {
+  unsigned char* p = lds + 2 * chain_stage_bytes(GAIN) + (size_t)buf * out_stage_bytes(GAIN);
+  OutStage s;
+  s.q = reinterpret_cast<_Float16*>(p);
+  if (!GAIN) p += kStK;
+  s.p = reinterpret_cast<_Float16*>(p); p += kStT;
+  s.g = reinterpret_cast<float*>(p);
+  return s;
+}
+template <bool GAIN>
+__device__ __forceinline__ half8* exch_at(unsigned char* lds, int buf) {
+  return reinterpret_cast<half8*>(lds + 2 * chain_stage_bytes(GAIN) + 2 * out_stage_bytes(GAIN) +
+                                  (size_t)buf * kExBytes);
 }
 
-// Raw inputs of one chunk in a producer's registers. Loads are unconditional
-// (rows past the chunk's end are clamped to its last row) and nothing is
-// computed from them until the chunk is staged.
-template <bool GAIN> struct BufGain {};
-template <> struct BufGain<true> {
-  uint4 g0, g1;            // gains of the q/k rows
+// ---- wavefronts 2-3 (pw = 0, 1). Every load instruction of a wavefront
+// reads 1 KB of consecutive bytes: for a tile with R-byte rows, lane l of
+// instruction i reads 16 bytes of row (rows per instruction) * (8 pw + i) + ...
+// Chain fields belong to one chunk, output fields to the one before it.
+template <bool GAIN> struct ProdX { uint4 gn[8]; };            // gains (chain chunk)
+template <> struct ProdX<false> { uint4 q[8]; };               // Q (output chunk)
+template <bool GAIN>
+struct ProdBuf : ProdX<GAIN> {
+  uint4 k[8];   // K: rows 32 pw + 4 i + l / 16, 16-byte piece l % 16
+  uint4 t[4];   // T: rows 32 pw + 8 i + l / 8, piece l % 8
+  uint4 v[2];   // V slice: rows 32 pw + 16 i + l / 4, piece l % 4
+  uint4 p[4];   // P (output chunk), as T
+  float4 sc;    // scalars of token l: chain chunk (pw 0) or output chunk (pw 1)
+};
+
+struct ProdCtx {
+  __amdgpu_buffer_rsrc_t rk, rx, rv;
+  const unsigned char* rec;   // records of this head
+  int pw, lane;
 };
 
 template <bool GAIN>
-struct Buf : BufGain<GAIN> {
-  uint4 q0, q1, k0, k1;    // rows p / 16 and p / 16 + 32, columns 8 (p % 16) ..
-  uint4 t, pm;             // T and P: row p / 8, columns 8 (p % 8) ..
-  uint2 v;                 // value row p / 8, columns j0 + 4 (p % 8) ..
-  float4 sc;               // scalars of token p % 64
-};
-
-template <bool GAIN>
-__device__ __forceinline__ void load_buf(const StateArgs& a, Buf<GAIN>& b, int bh, int j0, int c,
-                                         int p) {
-  const int c0 = c * C, n = min(C, a.L - c0);
-  const size_t tok = (size_t)bh * a.L + c0;
-  const unsigned char* rec = a.rec + ((size_t)bh * a.nchunks + c) * kRecBytes;
-  const float4* sc = reinterpret_cast<const float4*>(rec + kRecS);
-  const size_t off0 = (tok + min(p >> 4, n - 1)) * DK + (p & 15) * 8;
-  const size_t off1 = (tok + min((p >> 4) + 32, n - 1)) * DK + (p & 15) * 8;
-  b.q0 = *reinterpret_cast<const uint4*>(a.q + off0);
-  b.q1 = *reinterpret_cast<const uint4*>(a.q + off1);
-  b.k0 = *reinterpret_cast<const uint4*>(a.k + off0);
-  b.k1 = *reinterpret_cast<const uint4*>(a.k + off1);
-  if constexpr (GAIN) {
-    b.g0 = *reinterpret_cast<const uint4*>(a.gain + off0);
-    b.g1 = *reinterpret_cast<const uint4*>(a.gain + off1);
-  }
-  b.t = reinterpret_cast<const uint4*>(rec + kRecT)[p];
-  b.pm = reinterpret_cast<const uint4*>(rec + kRecP)[p];
-  const int vrow = min(p >> 3, n - 1);
-  b.v = *reinterpret_cast<const uint2*>(a.v + (tok + vrow) * a.dv + j0 + (p & 7) * 4);
-  b.sc = sc[p & 63];
-}
-
-// Convert a chunk into LDS (everything but the gains). Every thread consumes
-// everything it loaded, on every path: a load consumed only on some paths
-// makes the compiler wait for all outstanding loads before reusing its
-// registers, which would serialise the prefetch.
-template <bool GAIN>
-__device__ __forceinline__ void stage_buf(const StateArgs& a, const Buf<GAIN>& b, const StageBuf& s,
-                                          int c, int p) {
-  const int n = min(C, a.L - c * C);
-  {
-    const int row = p >> 4, c8 = p & 15;
-    const float keep0 = row < n ? 1.f : 0.f, keep1 = row + 32 < n ? 1.f : 0.f;
-    *reinterpret_cast<uint4*>(s.q + row * KP + c8 * 8) = bf16x8_to_f16x8(b.q0, keep0);
-    *reinterpret_cast<uint4*>(s.k + row * KP + c8 * 8) = bf16x8_to_f16x8(b.k0, keep0);
-    *reinterpret_cast<uint4*>(s.q + (row + 32) * KP + c8 * 8) = bf16x8_to_f16x8(b.q1, keep1);
-    *reinterpret_cast<uint4*>(s.k + (row + 32) * KP + c8 * 8) = bf16x8_to_f16x8(b.k1, keep1);
-  }
-  {
-    const int row = p >> 3, c8 = p & 7;
-    *reinterpret_cast<uint4*>(s.t + row * CP + c8 * 8) = b.t;
-    *reinterpret_cast<uint4*>(s.p + row * CP + c8 * 8) = b.pm;
-  }
-  {
-    const int row = p >> 3, c4 = (p & 7) * 4;
-    const float keep = row < n ? 1.f : 0.f;
-    const uint32_t w[2] = {b.v.x, b.v.y};
+__device__ __forceinline__ void prod_load(const ProdCtx& x, ProdBuf<GAIN>& b, int cc, int co, int dv) {
+  const int l = x.lane, r0 = 32 * x.pw;
+  const unsigned char* rc = x.rec + (size_t)cc * kRecBytes;
+  const unsigned char* ro = x.rec + (size_t)co * kRecBytes;
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      s.vt[(c4 + 2 * e) * CP + row] = (_Float16)(__uint_as_float(w[e] << 16) * keep);
-      s.vt[(c4 + 2 * e + 1) * CP + row] = (_Float16)(__uint_as_float(w[e] & 0xffff0000u) * keep);
+  for (int i = 0; i < 8; ++i) {
+    const int off_c = (cc * C + r0 + 4 * i) * (DK * 2) + l * 16;
+    b.k[i] = bload16(x.rk, off_c);
+    if constexpr (GAIN) b.gn[i] = bload16(x.rx, off_c);
+    else b.q[i] = bload16(x.rx, (co * C + r0 + 4 * i) * (DK * 2) + l * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    b.t[i] = reinterpret_cast<const uint4*>(rc + kRecT)[(r0 + 8 * i) * 8 + l];
+    b.p[i] = reinterpret_cast<const uint4*>(ro + kRecP)[(r0 + 8 * i) * 8 + l];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    b.v[i] = bload16(x.rv, (cc * C + r0 + 16 * i + (l >> 2)) * dv * 2 + (l & 3) * 16);
+  b.sc = reinterpret_cast<const float4*>((x.pw ? ro : rc) + kRecS)[l];
+}
+
+template <bool GAIN>
+__device__ __forceinline__ void prod_stage(const ProdCtx& x, const ProdBuf<GAIN>& b,
+                                           const ChainStage& cs, const OutStage& os) {
+  const int l = x.lane, r0 = 32 * x.pw;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int off = (r0 + 4 * i + (l >> 4)) * KP + (l & 15) * 8;
+    *reinterpret_cast<uint4*>(cs.k + off) = bf16x8_to_f16x8(b.k[i], 1.f);
+    if constexpr (GAIN) *reinterpret_cast<uint4*>(cs.b + off) = b.gn[i];
+    else *reinterpret_cast<uint4*>(os.q + off) = bf16x8_to_f16x8(b.q[i], 1.f);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int off = (r0 + 8 * i + (l >> 3)) * CP + (l & 7) * 8;
+    *reinterpret_cast<uint4*>(cs.t + off) = b.t[i];
+    *reinterpret_cast<uint4*>(os.p + off) = b.p[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    *reinterpret_cast<uint4*>(cs.v + (r0 + 16 * i + (l >> 2)) * VP + (l & 3) * 8) =
+        bf16x8_to_f16x8(b.v[i], 1.f);
+  if (x.pw == 0) {
+    cs.g[l] = b.sc.x;
+    cs.w[l] = b.sc.y;
+    cs.vs[l] = b.sc.z;
+  } else {
+    os.g[l] = b.sc.x;
+  }
+}
+
+// ---- wavefront 1 (Kalman writes): Q rows of one chunk straight from global
+// memory, in operand k order.
+struct QBuf {
+  uint2 q[2][8][2];  // [token block][k step][low/high quad]
+};
+__device__ __forceinline__ void q_load(__amdgpu_buffer_rsrc_t rq, QBuf& b, int c, int lane) {
+  const int m = lane & 31, h4 = (lane >> 5) * 4;
+#pragma unroll
+  for (int tb = 0; tb < 2; ++tb) {
+    const int off = (c * C + 32 * tb + m) * (DK * 2) + h4 * 2;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      b.q[tb][s][0] = bload8(rq, off + 32 * s);
+      b.q[tb][s][1] = bload8(rq, off + 32 * s + 16);
     }
   }
-  // eight threads write each token's scalars (the same values)
-  s.gam[p & 63] = b.sc.x;
-  s.w[p & 63] = b.sc.y;
-  s.vs[p & 63] = b.sc.z;
 }
 
-__device__ __forceinline__ void stage_gain(const Buf<true>& b, _Float16* sG, int n, int p) {
-  const int row = p >> 4, c8 = p & 15;
-  const uint4 z = make_uint4(0, 0, 0, 0);
-  *reinterpret_cast<uint4*>(sG + row * KP + c8 * 8) = row < n ? b.g0 : z;
-  *reinterpret_cast<uint4*>(sG + (row + 32) * KP + c8 * 8) = row + 32 < n ? b.g1 : z;
-}
-
-template <bool GAIN>
+template <bool GAIN, bool OBF16>
 __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  unsigned char* lp = lds_raw + 2 * kStageBytes;  // two stage buffers first
-  _Float16* sG = nullptr;
-  if (GAIN) { sG = reinterpret_cast<_Float16*>(lp); lp += C * KP * 2; }
-  _Float16* sST = reinterpret_cast<_Float16*>(lp); lp += DV * KP * 2;  // S^T (fp16)
-  _Float16* sXT = reinterpret_cast<_Float16*>(lp); lp += DV * CP * 2;  // X^T
-  _Float16* sUT = reinterpret_cast<_Float16*>(lp); lp += DV * CP * 2;  // U^T
-  _Float16* sUW = reinterpret_cast<_Float16*>(lp);                     // (w U)^T
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, c32 = lane & 31;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r16 = lane & 15, kq = lane >> 4, k8 = kq * 8;
-  const bool producer = wave >= NW_COMPUTE;
-  const int p = tid - 64 * NW_COMPUTE;          // producer thread index
-  const int rb = wave & 3, cb = (wave >> 2) & 1; // compute wavefront's blocks
-  const int t0 = 16 * rb + kq * 4;               // this lane's 4 token rows
-  const int col = 16 * cb + r16;                 // this lane's value column (in the slice)
-
-  // (head, d_v slice): the slices of one head land on one XCD (blocks are
-  // dealt to the 8 XCDs round-robin), so they share that XCD's L2.
   int bh, tile;
   {
+    // the d_v slices of one head land on one XCD (blocks are dealt to the 8
+    // XCDs round-robin), so they share that XCD's L2
     const int id = blockIdx.x;
     if ((a.BH & 7) == 0) {
       const int xcd = id & 7, slot = id >> 3;
@@ -535,152 +624,248 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
     }
   }
   const int j0 = tile * DV;
-
-  // Both loops run an even number of chunk steps (an odd count gets one
-  // idle step), three barriers per step, so the barrier counts match.
-  const int nsteps = (a.nchunks + 1) & ~1;
   const int last = a.nchunks - 1;
+  const int nsteps = (a.nchunks + 2) & ~1;  // chunks + 1 (output lag), even
+  const unsigned char* rec_head = a.rec + (size_t)bh * a.nchunks * kRecBytes;
+  const size_t head_tok = (size_t)bh * a.L;
 
-  if (producer) {
-    // ---------------------------------------------------------- producers
-    // Step c: stage chunk c + 1 from the register buffer that holds it into
-    // LDS buffer (c + 1) % 2, then reload that register buffer with chunk
-    // c + 3. Every load and stage is unconditional (chunk indices are clamped
-    // to the last chunk; restaging it into the idle buffer is harmless), so
-    // no path leaves a load pending and the compiler waits only for the
-    // buffer being consumed, never for the one still in flight.
-    Buf<GAIN> r0, r1;
-    load_buf<GAIN>(a, r0, bh, j0, 0, p);
-    load_buf<GAIN>(a, r1, bh, j0, min(1, last), p);
-    stage_buf<GAIN>(a, r0, carve_stage(lds_raw), 0, p);
-    if constexpr (GAIN) stage_gain(r0, sG, min(C, a.L), p);
-    load_buf<GAIN>(a, r0, bh, j0, min(2, last), p);
+  if (wv >= 2) {
+    // ------------------------------------------------------------ producers
+    ProdCtx x;
+    x.rk = make_rsrc(a.k + head_tok * DK, (size_t)a.L * DK * 2);
+    x.rx = GAIN ? make_rsrc(a.gain + head_tok * DK, (size_t)a.L * DK * 2)
+                : make_rsrc(a.q + head_tok * DK, (size_t)a.L * DK * 2);
+    x.rv = make_rsrc(a.v + head_tok * a.dv + j0, ((size_t)a.L * a.dv - j0) * 2);
+    x.rec = rec_head;
+    x.pw = wv - 2;
+    x.lane = lane;
+    // step c stages the chain inputs of chunk c + 1 and the output inputs of
+    // chunk c from the register buffer that holds them, then reloads it with
+    // chunks c + 3 and c + 2. Chunk indices are clamped to the last chunk;
+    // restaging it into an idle buffer is harmless.
+    ProdBuf<GAIN> r0, r1;
+    prod_load<GAIN>(x, r0, 0, 0, a.dv);
+    prod_load<GAIN>(x, r1, min(1, last), 0, a.dv);
+    prod_stage<GAIN>(x, r0, chain_stage<GAIN>(lds_raw, 0), out_stage<GAIN>(lds_raw, 1));
+    prod_load<GAIN>(x, r0, min(2, last), min(1, last), a.dv);
     __syncthreads();
-    // The scheduling barriers keep the compiler from hoisting the next
-    // step's conversions (and so its waits for loads still in flight) into
-    // this step.
-    auto pbody = [&](int c, Buf<GAIN>& rn) {
-      const int cn = min(c + 1, last);
+    auto body = [&](int c, ProdBuf<GAIN>& r) {
       __builtin_amdgcn_sched_barrier(0);
-      stage_buf<GAIN>(a, rn, carve_stage(lds_raw + ((c + 1) & 1) * kStageBytes), cn, p);
-      if constexpr (!GAIN) load_buf<GAIN>(a, rn, bh, j0, min(c + 3, last), p);
-      __syncthreads();
-      if constexpr (GAIN) {
-        // the gains of chunk c + 1 (the compute side read chunk c's before the barrier)
-        stage_gain(rn, sG, min(C, a.L - cn * C), p);
-        load_buf<GAIN>(a, rn, bh, j0, min(c + 3, last), p);
-      }
-      __syncthreads();
+      prod_stage<GAIN>(x, r, chain_stage<GAIN>(lds_raw, (c + 1) & 1), out_stage<GAIN>(lds_raw, c & 1));
+      prod_load<GAIN>(x, r, min(c + 3, last), min(c + 2, last), a.dv);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     };
     for (int c = 0; c < nsteps; c += 2) {
-      pbody(c, r1);
-      pbody(c + 1, r0);
+      body(c, r1);
+      body(c + 1, r0);
     }
     return;
   }
 
-  // ------------------------------------------------------------ compute
-  floatx4 S[2];  // state tiles (d_k blocks 2 rb, 2 rb + 1; value block cb)
-#pragma unroll
-  for (int db = 0; db < 2; ++db) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int d = 32 * rb + 16 * db + kq * 4 + jj;
-      S[db][jj] = a.state_in ? a.state_in[((size_t)bh * DK + d) * a.dv + j0 + col] : 0.f;
+  if (wv == 1) {
+    // ------------------------------------------------------------ outputs
+    constexpr int esz = OBF16 ? 2 : 4;
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(static_cast<unsigned char*>(a.o) + (head_tok * a.dv + j0) * esz,
+                  ((size_t)a.L * a.dv - j0) * esz);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + head_tok * DK, (size_t)a.L * DK * 2);
+    QBuf b0, b1;
+    if constexpr (GAIN) {
+      q_load(rq, b0, 0, lane);
+      q_load(rq, b1, min(1, last), lane);
     }
-    st4(sST + col * KP + 32 * rb + 16 * db + kq * 4, S[db]);
+    __syncthreads();
+    // step c (1 <= c <= nchunks) writes the outputs of chunk c - 1
+    auto body = [&](int c, QBuf& b) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int cc = c - 1;
+      if (cc >= 0 && cc <= last) {
+        const half8* ex = exch_at<GAIN>(lds_raw, cc & 1);
+        const OutStage st = out_stage<GAIN>(lds_raw, cc & 1);
+        half8 sv[8], uv[4], pa[6];
+#pragma unroll
+        for (int s = 0; s < 8; ++s) sv[s] = ex[s * 64 + lane];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) uv[s] = ex[(8 + s) * 64 + lane];
+        pa[0] = ld_op(st.p + c32 * CP, h);
+        pa[1] = ld_op(st.p + c32 * CP + 16, h);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) pa[2 + s] = ld_op(st.p + (32 + c32) * CP + 16 * s, h);
+        floatx16 o[2];
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb) {
+          half8 qa[8];
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            if constexpr (GAIN)
+              qa[s] = cat(bf16x4_to_f16x4(b.q[tb][s][0]), bf16x4_to_f16x4(b.q[tb][s][1]));
+            else
+              qa[s] = ld_op(st.q + (32 * tb + c32) * KP + 16 * s, h);
+          }
+          floatx16 acc = {};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) acc = mfma32(qa[s], sv[s], acc);
+          // rows are tokens: scale by g
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const float4 gg = *reinterpret_cast<const float4*>(st.g + 32 * tb + 8 * g4 + 4 * h);
+            acc[4 * g4 + 0] *= gg.x;
+            acc[4 * g4 + 1] *= gg.y;
+            acc[4 * g4 + 2] *= gg.z;
+            acc[4 * g4 + 3] *= gg.w;
+          }
+          o[tb] = acc;
+        }
+        o[0] = mfma32(pa[0], uv[0], o[0]);
+        o[0] = mfma32(pa[1], uv[1], o[0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) o[1] = mfma32(pa[2 + s], uv[s], o[1]);
+        // o[tb] register j: token 32 tb + 8 (j / 4) + 4 h + j % 4, column c32
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int tok = cc * C + 32 * tb + 8 * (j >> 2) + 4 * h + (j & 3);
+            const int off = (tok * a.dv + c32) * esz;
+            if constexpr (OBF16)
+              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(o[tb][j]), ro, off, 0, 0);
+            else
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[tb][j]), ro, off, 0, 0);
+          }
+        if constexpr (GAIN) q_load(rq, b, min(cc + 2, last), lane);
+      }
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int c = 0; c < nsteps; c += 2) {
+      body(c, b1);
+      body(c + 1, b0);
+    }
+    return;
   }
+
+  // -------------------------------------------------------------- chain
+  floatx16 S[4];  // S[b] register j: d_k row 32 b + 8 (j / 4) + 4 h + j % 4, column c32
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int d = 32 * b + 8 * (j >> 2) + 4 * h + (j & 3);
+      S[b][j] = a.state_in ? a.state_in[((size_t)bh * DK + d) * a.dv + j0 + c32] : 0.f;
+    }
   __syncthreads();
 
-  const int nks = rb >= 2 ? 2 : 1;
+  // transposed reads: group G = lane / 16 covers columns 16 (G % 2) .. + 16 and
+  // rows 4 (G / 2) .. + 4 of an 8-row half step; lane jj of the group
+  // addresses row jj / 4 and column quad jj % 4
+  const int G = lane >> 4, jj = lane & 15;
+  const int tr_row = 4 * (G >> 1) + (jj >> 2);
+  const int tr_col = 16 * (G & 1) + 4 * (jj & 3);
+
   for (int c = 0; c < nsteps; ++c) {
-    if (c > last) {  // the idle step of an odd chunk count
-      __syncthreads();
-      __syncthreads();
-      __syncthreads();
-      break;
-    }
-    const StageBuf cur = carve_stage(lds_raw + (c & 1) * kStageBytes);
-    const int n = min(C, a.L - c * C);
-    // state-update operand B^T for this wavefront's d_k blocks, gathered early
-    half8 bt[2][2];
-    const _Float16* srcB = GAIN ? sG : cur.k;
+    if (c <= last) {
+      const ChainStage st = chain_stage<GAIN>(lds_raw, c & 1);
+      half8* ex = exch_at<GAIN>(lds_raw, c & 1);
+      const int n = min(C, a.L - c * C);
+      // operands that do not depend on this chunk's results, issued first
+      half8 ka[2][8];
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+      for (int s = 0; s < 8; ++s)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
+        for (int blk = 0; blk < 2; ++blk) ka[blk][s] = ld_op(st.k + (32 * blk + c32) * KP + 16 * s, h);
+      // S in fp16, as the k = d_k operand
+      half8 s16[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          bt[db][ks][e] = srcB[(32 * ks + k8 + e) * KP + 32 * rb + 16 * db + r16];
-    // phase A: K S and Q S for (rb, cb); X = v_scale V - g K S; O part g Q S
-    floatx4 opart;
-    {
-      floatx4 ks_acc = {0.f, 0.f, 0.f, 0.f}, qs_acc = ks_acc;
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int kd = 0; kd < DK / 32; ++kd) {
-        const half8 sv = ld8(sST + col * KP + 32 * kd + k8);
-        ks_acc = mfma(ld8(cur.k + (16 * rb + r16) * KP + 32 * kd + k8), sv, ks_acc);
-        qs_acc = mfma(ld8(cur.q + (16 * rb + r16) * KP + 32 * kd + k8), sv, qs_acc);
-      }
-      const float4 g4 = *reinterpret_cast<const float4*>(cur.gam + t0);
-      const float4 s4 = *reinterpret_cast<const float4*>(cur.vs + t0);
-      const half4 v4 = *reinterpret_cast<const half4*>(cur.vt + col * CP + t0);
-      const float gv[4] = {g4.x, g4.y, g4.z, g4.w};
-      const float sv4[4] = {s4.x, s4.y, s4.z, s4.w};
-      floatx4 x;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        x[jj] = sv4[jj] * (float)v4[jj] - gv[jj] * ks_acc[jj];
-        opart[jj] = gv[jj] * qs_acc[jj];
-      }
-      st4(sXT + col * CP + t0, x);
-    }
-    __syncthreads();
-
-    // phase B: U = T X for (rb, cb)
-    {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int ks = 0; ks < nks; ++ks)
-        acc = mfma(ld8(cur.t + (16 * rb + r16) * CP + 32 * ks + k8),
-                   ld8(sXT + col * CP + 32 * ks + k8), acc);
-      st4(sUT + col * CP + t0, acc);
-      const float4 w4 = *reinterpret_cast<const float4*>(cur.w + t0);
-      floatx4 wu;
-      wu[0] = acc[0] * w4.x;
-      wu[1] = acc[1] * w4.y;
-      wu[2] = acc[2] * w4.z;
-      wu[3] = acc[3] * w4.w;
-      st4(sUW + col * CP + t0, wu);
-    }
-    __syncthreads();
-
-    // phase C: O = g Q S + P U;  S = g_n S + B^T (w U)
-    {
-      floatx4 acc = opart;
-      for (int ks = 0; ks < nks; ++ks)
-        acc = mfma(ld8(cur.p + (16 * rb + r16) * CP + 32 * ks + k8),
-                   ld8(sUT + col * CP + 32 * ks + k8), acc);
-      const size_t tok = (size_t)bh * a.L + (size_t)c * C;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        if (t0 + jj < n) {
-          const size_t off = (tok + t0 + jj) * a.dv + j0 + col;
-          if (a.out_bf16)
-            static_cast<uint16_t*>(a.o)[off] = f32_to_bf16(acc[jj]);
-          else
-            static_cast<float*>(a.o)[off] = acc[jj];
+        for (int i = 0; i < 8; ++i) {
+          s16[2 * b][i] = (_Float16)S[b][i];
+          s16[2 * b + 1][i] = (_Float16)S[b][8 + i];
         }
-      }
-      const float gn = cur.gam[n - 1];
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        floatx4 st = S[db] * gn;
+      for (int s = 0; s < 8; ++s) ex[s * 64 + lane] = s16[s];
+      half4 vv[2][4];
+      float4 gg[2][4], sc[2][4];
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) st = mfma(bt[db][ks], ld8(sUW + col * CP + 32 * ks + k8), st);
-        S[db] = st;
-        st4(sST + col * KP + 32 * rb + 16 * db + kq * 4, st);
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          vv[blk][g4] = ld_tr(st.v + (32 * blk + 8 * g4 + tr_row) * VP + tr_col);
+          gg[blk][g4] = *reinterpret_cast<const float4*>(st.g + 32 * blk + 8 * g4 + 4 * h);
+          sc[blk][g4] = *reinterpret_cast<const float4*>(st.vs + 32 * blk + 8 * g4 + 4 * h);
+        }
+      half8 ta[6];
+      ta[0] = ld_op(st.t + c32 * CP, h);
+      ta[1] = ld_op(st.t + c32 * CP + 16, h);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ta[2 + s] = ld_op(st.t + (32 + c32) * CP + 16 * s, h);
+      // K S for the two token blocks
+      floatx16 ks[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) ks[blk] = mfma32(ka[blk][s], s16[s], ks[blk]);
+      // transposed write vectors for the state update (independent of U)
+      half8 bt[4][4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const _Float16* base = st.b + 32 * b + tr_col;
+          bt[b][s] = cat(ld_tr(base + (16 * s + tr_row) * KP), ld_tr(base + (16 * s + 8 + tr_row) * KP));
+        }
+      float4 ww[2][4];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          ww[blk][g4] = *reinterpret_cast<const float4*>(st.w + 32 * blk + 8 * g4 + 4 * h);
+      const float gn = st.g[n - 1];
+      // X = v_scale V - g K S, as the k = token operand
+      half8 x16[4];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float gv[4] = {gg[blk][g4].x, gg[blk][g4].y, gg[blk][g4].z, gg[blk][g4].w};
+          const float sv[4] = {sc[blk][g4].x, sc[blk][g4].y, sc[blk][g4].z, sc[blk][g4].w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            x16[2 * blk + (g4 >> 1)][4 * (g4 & 1) + r] =
+                (_Float16)(sv[r] * (float)vv[blk][g4][r] - gv[r] * ks[blk][4 * g4 + r]);
+        }
+      // U = T X (T is lower triangular by 32-blocks)
+      floatx16 u[2] = {floatx16{}, floatx16{}};
+      u[0] = mfma32(ta[0], x16[0], u[0]);
+      u[1] = mfma32(ta[2], x16[0], u[1]);
+      u[0] = mfma32(ta[1], x16[1], u[0]);
+      u[1] = mfma32(ta[3], x16[1], u[1]);
+      u[1] = mfma32(ta[4], x16[2], u[1]);
+      u[1] = mfma32(ta[5], x16[3], u[1]);
+      // U (for the outputs) and w U (for the state update), k = token
+      half8 u16[4], uw16[4];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float wv4[4] = {ww[blk][g4].x, ww[blk][g4].y, ww[blk][g4].z, ww[blk][g4].w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float uv = u[blk][4 * g4 + r];
+            u16[2 * blk + (g4 >> 1)][4 * (g4 & 1) + r] = (_Float16)uv;
+            uw16[2 * blk + (g4 >> 1)][4 * (g4 & 1) + r] = (_Float16)(uv * wv4[r]);
+          }
+        }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ex[(8 + s) * 64 + lane] = u16[s];
+      // S = g_n S + (diag(w) B)^T U
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        floatx16 acc = S[b] * gn;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) acc = mfma32(bt[b][s], uw16[s], acc);
+        S[b] = acc;
       }
     }
     __syncthreads();
@@ -688,11 +873,11 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
 
   if (a.state_out) {
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d = 32 * rb + 16 * db + kq * 4 + jj;
-        a.state_out[((size_t)bh * DK + d) * a.dv + j0 + col] = S[db][jj];
+      for (int j = 0; j < 16; ++j) {
+        const int d = 32 * b + 8 * (j >> 2) + 4 * h + (j & 3);
+        a.state_out[((size_t)bh * DK + d) * a.dv + j0 + c32] = S[b][j];
       }
   }
 }
@@ -729,10 +914,10 @@ hipError_t launch_tinv_mfma(const ScanArgs& s, void* tbuf, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool GAIN>
+template <bool GAIN, bool OBF16>
 hipError_t launch_state_typed(const StateArgs& sa, hipStream_t st) {
   const size_t lds = state_lds_bytes(GAIN);
-  auto kern = state_kernel<GAIN>;
+  auto kern = state_kernel<GAIN, OBF16>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -750,13 +935,14 @@ hipError_t launch_state_mfma(const ScanArgs& s, bool out_bf16, const void* tbuf,
   sa.state_in = s.state_in;
   sa.state_out = s.state_out;
   sa.o = s.o;
-  sa.out_bf16 = out_bf16 ? 1 : 0;
   sa.BH = s.BH;
   sa.L = s.L;
   sa.dv = s.dv;
   sa.nchunks = (s.L + C - 1) / C;
   sa.ntiles = s.dv / DV;
-  return s.gain ? launch_state_typed<true>(sa, st) : launch_state_typed<false>(sa, st);
+  if (s.gain)
+    return out_bf16 ? launch_state_typed<true, true>(sa, st) : launch_state_typed<true, false>(sa, st);
+  return out_bf16 ? launch_state_typed<false, true>(sa, st) : launch_state_typed<false, false>(sa, st);
 }
 
 }  // namespace kdn
