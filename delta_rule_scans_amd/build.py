@@ -26,6 +26,12 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch=
           "-Wall", "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]
 
 
+# Per-file extras. The matrix-core scan keeps its accumulators in ordinary
+# VGPRs (no copies between accumulation and vector registers around the vector
+# work done on the state between products).
+EXTRA = {"scan_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith(".hip") or f.endswith(".cpp"))
@@ -34,7 +40,7 @@ def sources():
 def _compile(src):
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", src, "-o", obj]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(os.path.basename(src), []), *lang, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stderr}")

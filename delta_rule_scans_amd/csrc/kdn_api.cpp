@@ -43,7 +43,7 @@ WsLayout ws_layout(int B, int H, int L, int dk, int dv, int chunk, int mode, int
   const size_t nchunks = ((size_t)L + chunk - 1) / chunk;
   if (mode == KDN_GAIN_DIAG) w.maps_bytes = BH * nchunks * dk * 4 * sizeof(float);
   if (mode != KDN_GAIN_DELTA) w.gains_bytes = BH * (size_t)L * dk * (in_dtype == KDN_BF16 ? 2 : 4);
-  if (use_mfma_path(in_dtype, dk, dv, chunk)) w.t_bytes = kdn::scan_mfma_workspace_bytes((int)BH, L);
+  if (use_mfma_path(in_dtype, dk, dv, chunk)) w.t_bytes = kdn::scan_mfma_workspace_bytes((int)BH, L, mode != KDN_GAIN_DELTA);
   w.maps_off = 0;
   w.gains_off = round_up(w.maps_bytes, 256);
   w.t_off = w.gains_off + round_up(w.gains_bytes, 256);

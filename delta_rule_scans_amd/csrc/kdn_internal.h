@@ -66,12 +66,13 @@ hipError_t launch_scan_f32(const ScanArgs& a, bool in_bf16, bool out_bf16, bool 
 size_t scan_f32_lds_bytes(int dk, int chunk);
 
 // Matrix-core chunk scan for bf16 inputs (dk == 128, dv % 32 == 0, chunk == 64);
-// gains (if any) are fp16. `tbuf` holds scan_mfma_workspace_bytes(BH, L) bytes
-// for the per-chunk (I + A)^-1 matrices.
+// gains (if any) are fp16. `tbuf` holds scan_mfma_workspace_bytes(BH, L, gain)
+// bytes: per chunk (I + A)^-1, the masked query-key product for the Kalman
+// writes, and the token scalars.
 hipError_t launch_tinv_mfma(const ScanArgs& a, void* tbuf, hipStream_t s);
 hipError_t launch_state_mfma(const ScanArgs& a, bool out_bf16, const void* tbuf, hipStream_t s);
 bool scan_mfma_supported(int dk, int dv, int chunk);
-size_t scan_mfma_workspace_bytes(int BH, int L);
+size_t scan_mfma_workspace_bytes(int BH, int L, bool gain);
 
 // Diagonal-covariance Kalman gains: writes gains [BH, L, dk] (fp16 or f32) and
 // the final covariance. `maps` is scratch of BH * nchunks * dk * 4 floats.

@@ -38,6 +38,8 @@
 // (16-byte LDS reads); its result gives each lane 4 consecutive rows of one
 // column, which is written either as [n][m] (one 8-byte write) or [m][n]
 // (four 2-byte writes). Every buffer below is laid out for its reader.
+#include <utility>
+
 #include "kdn_internal.h"
 
 namespace kdn {
@@ -54,11 +56,29 @@ constexpr int DV = 32;         // value columns per workgroup
 constexpr int KP = DK + 8;     // fp16 pitch of [token][d_k] tiles (272 B: conflict-free rows)
 constexpr int CP = C + 8;      // fp16 pitch of [.][token] tiles (144 B)
 
-// Per (head, chunk) record written by prep_kernel and read by state_kernel.
-constexpr size_t kRecT = 0;                       // T, fp16 [C][C]
-constexpr size_t kRecP = C * C * 2;               // P, fp16 [C][C]
-constexpr size_t kRecS = 2 * C * C * 2;           // scalars, float4 [C]: g, w, value scale, 0
-constexpr size_t kRecBytes = kRecS + C * 16;      // 17408
+// Per (head, chunk) record written by prep_kernel and read by state_kernel:
+//   T  = (I + A)^-1 as its three nonzero 32 x 32 blocks (rows/cols 0-31,
+//        rows 32-63 x cols 0-31, rows/cols 32-63), fp16, row-major per block;
+//   P  (Kalman writes only) in the same three-block form;
+//   scalars, three float4 per token: (g, w, log2 g, write scale),
+//        (R, Cf, f0, f1), (value scale, extreme, 0, 0). They factor the decay
+//        ratio of the masked query-key product bs_l g_i / g_l (l <= i):
+//        across the two 32-token halves as f0_l f1_i with
+//        f0_l = bs_l g_31 / g_l (l < 32), f1_i = g_i / g_31 (i >= 32), both
+//        <= bs_l resp. 1; inside a half b as R_l Cf_i with
+//        R_l = bs_l g_r / g_l, Cf_i = g_i / g_r, r = 32 b + 15. Those can
+//        overflow only for decay faster than 2^-100 over 16 tokens; the chunk's
+//        `extreme` flag (1.0) then selects exp2 of log2 g differences instead.
+// The delta write's P is formed by the state kernel from the staged Q and K.
+constexpr size_t kTriBytes = 3 * 32 * 32 * 2;     // 6144
+constexpr size_t kRecT = 0;
+__host__ __device__ constexpr size_t rec_p_off(bool gain) { return gain ? kTriBytes : 0; }
+__host__ __device__ constexpr size_t rec_s_off(bool gain) { return gain ? 2 * kTriBytes : kTriBytes; }
+__host__ __device__ constexpr size_t rec_bytes(bool gain) { return rec_s_off(gain) + (size_t)C * 48; }
+// element (row, col) of a lower-triangular 64 x 64 matrix in three-block form (col <= row block)
+__host__ __device__ constexpr int tri_index(int row, int col) {
+  return row < 32 ? row * 32 + col : (col < 32 ? 1024 + (row - 32) * 32 + col : 2048 + (row - 32) * 32 + col - 32);
+}
 
 __device__ __forceinline__ floatx4 mfma(half8 a, half8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -128,7 +148,7 @@ struct PrepArgs {
   const _Float16* gain;   // fp16 [BH, L, DK] or null (delta write)
   const float* alpha;     // [BH, L] or null
   const float* beta;      // [BH, L]
-  unsigned char* rec;     // [BH, nchunks] records of kRecBytes
+  unsigned char* rec;     // [BH, nchunks] records of rec_bytes(gain)
   int L, nchunks, plain;
 };
 
@@ -171,22 +191,27 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   const int r16 = lane & 15, kq = lane >> 4, k8 = kq * 8;
   const int c0 = c * C, n = min(C, a.L - c0);
   const size_t tok = (size_t)bh * a.L + c0;
-  unsigned char* rec = a.rec + ((size_t)bh * a.nchunks + c) * kRecBytes;
+  unsigned char* rec = a.rec + ((size_t)bh * a.nchunks + c) * rec_bytes(gain);
 
-  // phase 1: stage Q, K (and the gains) as fp16; per-token scalars
+  // phase 1: stage K (and for the Kalman writes Q and the gains) as fp16;
+  // per-token scalars
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int seg = tid + NT * i, row = seg >> 4, c8 = seg & 15;
     uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, gv = qv;
     if (row < n) {
       const size_t off = (tok + row) * DK + c8 * 8;
-      qv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.q + off), 1.f);
       kv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.k + off), 1.f);
-      if (gain) gv = *reinterpret_cast<const uint4*>(a.gain + off);
+      if (gain) {
+        qv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.q + off), 1.f);
+        gv = *reinterpret_cast<const uint4*>(a.gain + off);
+      }
     }
-    *reinterpret_cast<uint4*>(sQ + row * KP + c8 * 8) = qv;
     *reinterpret_cast<uint4*>(sK + row * KP + c8 * 8) = kv;
-    if (gain) *reinterpret_cast<uint4*>(sB + row * KP + c8 * 8) = gv;
+    if (gain) {
+      *reinterpret_cast<uint4*>(sQ + row * KP + c8 * 8) = qv;
+      *reinterpret_cast<uint4*>(sB + row * KP + c8 * 8) = gv;
+    }
   }
   if (wave == 0) {
     float la = 0.f, bs = 0.f, vs = 1.f;
@@ -201,10 +226,20 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
     }
     const float lg = wave_prefix(la, lane);
     const float lgn = __shfl(lg, n - 1, 64);
+    const float lg31 = __shfl(lg, 31, 64);
+    const float lgr = __shfl(lg, (lane & 32) + 15, 64);   // reference of this half
     sLg[lane] = lg;
     sBs[lane] = bs;
     const float w = lane < n ? exp2f(lgn - lg) * bs : 0.f;
-    *reinterpret_cast<float4*>(rec + kRecS + lane * 16) = make_float4(exp2f(lg), w, vs, 0.f);
+    // exponents of R and Cf stay in [-100, 100] unless the decay is extreme
+    const float span = fabsf(lgr - lg);
+    const bool extreme = __ballot(span > 100.f) != 0;
+    float4* sc = reinterpret_cast<float4*>(rec + rec_s_off(gain));
+    sc[3 * lane] = make_float4(exp2f(lg), w, lg, bs);
+    sc[3 * lane + 1] = make_float4(extreme ? 0.f : bs * exp2f(lgr - lg), extreme ? 0.f : exp2f(lg - lgr),
+                                   lane < 32 ? bs * exp2f(lg31 - lg) : 0.f,
+                                   lane >= 32 ? exp2f(lg - lg31) : 0.f);
+    sc[3 * lane + 2] = make_float4(vs, extreme ? 1.f : 0.f, 0.f, 0.f);
   }
   __syncthreads();
 
@@ -222,6 +257,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   for (int j = 0; j < 5; ++j) {
     const int tl = wave + 4 * j;
     const bool isP = tl >= 10;
+    if (isP && !gain) continue;
     int ti, tj;
     tile_ij(isP ? tl - 10 : tl, ti, tj);
     const _Float16* srcA = isP ? sQ : sK;
@@ -335,20 +371,24 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
     }
   }
 
-  // phase 5: T and P (row-major, zero above the diagonal blocks) to the record
+  // phase 5: T (and P) to the record in three-block form
   _Float16* tdst = reinterpret_cast<_Float16*>(rec + kRecT);
-  _Float16* pdst = reinterpret_cast<_Float16*>(rec + kRecP);
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int seg = tid + NT * i, row = seg >> 3, c8 = seg & 7;
-    const bool lower = (c8 >> 1) <= (row >> 4);
-    uint4 tv = make_uint4(0, 0, 0, 0), pv = tv;
-    if (lower) {
-      tv = *reinterpret_cast<const uint4*>(sT + row * CP + c8 * 8);
-      pv = *reinterpret_cast<const uint4*>(sP + row * CP + c8 * 8);
+  _Float16* pdst = reinterpret_cast<_Float16*>(rec + rec_p_off(gain));
+  {
+    // each block is 32 rows x 64 bytes = 128 pieces of 16 bytes; 3 blocks = 384 pieces
+    for (int seg = tid; seg < 384; seg += NT) {
+      const int blk = seg >> 7, brow = (seg >> 2) & 31, piece = seg & 3;
+      const int row = (blk == 0 ? 0 : 32) + brow, col = (blk == 2 ? 32 : 0) + 8 * piece;
+      // 16 x 16 blocks above the diagonal were never written: zeros
+      const bool lower = (col >> 4) <= (row >> 4);
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      const uint4 tv = lower ? *reinterpret_cast<const uint4*>(sT + row * CP + col) : z;
+      *reinterpret_cast<uint4*>(tdst + blk * 1024 + brow * 32 + 8 * piece) = tv;
+      if (gain) {
+        const uint4 pv = lower ? *reinterpret_cast<const uint4*>(sP + row * CP + col) : z;
+        *reinterpret_cast<uint4*>(pdst + blk * 1024 + brow * 32 + 8 * piece) = pv;
+      }
     }
-    *reinterpret_cast<uint4*>(tdst + row * C + c8 * 8) = tv;
-    *reinterpret_cast<uint4*>(pdst + row * C + c8 * 8) = pv;
   }
 }
 
@@ -366,12 +406,21 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
 //    come from the staged [token][d_k] tile by ds_read_b64_tr_b16. Chunk c's
 //    incoming state and its residuals U go to an exchange buffer.
 //  * wavefront 1 writes the outputs of chunk c - 1 from the exchange buffer:
-//    O = diag(g) Q S + P U (22 products).
-//  * wavefronts 2-3 stage into LDS what wavefront 0 reads for chunk c + 1 (K
-//    and, for the Kalman writes, the gains; V; T; scalars) and what wavefront
-//    1 reads for chunk c (Q unless the write is a Kalman one, P, g), from
-//    registers loaded two steps earlier with fully coalesced 1 KB loads.
-// The chain never touches global memory. Loads of rows past the end of the
+//    O = diag(g) Q S + P U. For the delta write it also forms P from the
+//    staged Q and K as P^T = K Q^T (masked, scaled by the decay ratios), whose
+//    accumulator layout is directly the operand layout of P U; for the Kalman
+//    writes P comes with the prepare record.
+//  * wavefronts 2-3 stage into LDS what wavefront 0 reads for chunk c + 1 (K,
+//    the gains for the Kalman writes, V scaled by the value scale, T, token
+//    scalars) and what wavefront 1 reads for chunk c (Q, or P for the Kalman
+//    writes), from registers loaded two steps earlier with 1 KB loads of
+//    consecutive bytes. Wavefronts 0 and 1 never wait on global memory.
+//    Chain stages are triple-buffered for the delta write (wavefront 1 reads
+//    chunk c - 1's K and scalars while chunk c + 1 is staged).
+// Each wavefront's products are software-pipelined by hand: operand reads are
+// issued a few products ahead and scheduling fences keep the compiler from
+// regrouping them (the LDS counter tracks at most 15 reads, so issuing
+// everything up front would serialise). Loads of rows past the end of the
 // sequence go through buffer descriptors sized to the head, which return
 // zeros; output stores past it are dropped the same way.
 //
@@ -383,6 +432,16 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
 // two 8-byte reads at columns 4 h and 8 + 4 h of the k step.
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// Compile-time loop: f(std::integral_constant<int, 0>) ... f(<N - 1>).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
@@ -448,22 +507,27 @@ struct StateArgs {
 constexpr int NT_STATE = 256;
 constexpr int VP = DV + 8;  // fp16 pitch of the staged V rows
 
-// LDS: chain stages [2] {K [C][KP]; gains [C][KP] (Kalman writes); T [C][CP];
-// V [C][VP]; g, w, value scale [C]}, output stages [2] {Q [C][KP] (delta
-// write); P [C][CP]; g [C]}, exchange buffers [2] {S (8 k steps), U (4 k
-// steps)}, 16 bytes per lane and k step in wavefront-0 register order.
+// LDS, per chain stage (3 for the delta write, 2 for the Kalman writes):
+//   K [C][KP]; gains [C][KP] (Kalman); T [C][CP] (lower blocks only);
+//   V times the value scale [C][VP]; eight token scalars [8][C] (g, w, log2 g,
+//   write scale, R, Cf, f0, f1) and the chunk's extreme-decay flag;
+// per output stage (2): Q [C][KP] (delta) or P [C][CP] and g [C] (Kalman);
+// per exchange buffer (2): S (8 k steps) and U (4 k steps), 16 bytes per lane
+// and k step in wavefront-0 register order.
 constexpr size_t kStK = (size_t)C * KP * 2;
 constexpr size_t kStT = (size_t)C * CP * 2;
 constexpr size_t kStV = (size_t)C * VP * 2;
+constexpr size_t kStSc = (size_t)8 * C * 4 + 16;
 constexpr size_t kExBytes = (size_t)12 * 64 * 16;
+__host__ __device__ constexpr int n_chain_stages(bool gain) { return gain ? 2 : 3; }
 __host__ __device__ constexpr size_t chain_stage_bytes(bool gain) {
-  return kStK * (gain ? 2 : 1) + kStT + kStV + (size_t)3 * C * 4;
+  return kStK * (gain ? 2 : 1) + kStT + kStV + kStSc;
 }
 __host__ __device__ constexpr size_t out_stage_bytes(bool gain) {
-  return (gain ? 0 : kStK) + kStT + (size_t)C * 4;
+  return gain ? kStT + (size_t)C * 4 : kStK;
 }
 size_t state_lds_bytes(bool gain) {
-  return 2 * chain_stage_bytes(gain) + 2 * out_stage_bytes(gain) + 2 * kExBytes;
+  return n_chain_stages(gain) * chain_stage_bytes(gain) + 2 * out_stage_bytes(gain) + 2 * kExBytes;
 }
 
 struct ChainStage {
@@ -471,14 +535,20 @@ struct ChainStage {
   _Float16* b;   // write vectors: K (delta) or the gains
   _Float16* t;
   _Float16* v;
-  float* g;
+  float* g;      // token scalars
   float* w;
-  float* vs;
+  float* lg;
+  float* bs;
+  float* f0;
+  float* f1;
+  float* rr;
+  float* cf;
+  float* extreme;
 };
 struct OutStage {
-  _Float16* q;   // delta write only
-  _Float16* p;
-  float* g;
+  _Float16* q;   // delta write
+  _Float16* p;   // Kalman writes
+  float* g;      // Kalman writes
 };
 template <bool GAIN>
 __device__ __forceinline__ ChainStage chain_stage(unsigned char* lds, int buf) {
@@ -489,40 +559,46 @@ __device__ __forceinline__ ChainStage chain_stage(unsigned char* lds, int buf) {
   if (GAIN) { s.b = reinterpret_cast<_Float16*>(p); p += kStK; }
   s.t = reinterpret_cast<_Float16*>(p); p += kStT;
   s.v = reinterpret_cast<_Float16*>(p); p += kStV;
-  s.g = reinterpret_cast<float*>(p); p += C * 4;
-  s.w = reinterpret_cast<float*>(p); p += C * 4;
-  s.vs = reinterpret_cast<float*>(p);
+  float* f = reinterpret_cast<float*>(p);
+  s.g = f; s.w = f + C; s.lg = f + 2 * C; s.bs = f + 3 * C; s.f0 = f + 4 * C; s.f1 = f + 5 * C;
+  s.rr = f + 6 * C; s.cf = f + 7 * C; s.extreme = f + 8 * C;
   return s;
 }
 template <bool GAIN>
 __device__ __forceinline__ OutStage out_stage(unsigned char* lds, int buf) {
-  unsigned char* p = lds + 2 * chain_stage_bytes(GAIN) + (size_t)buf * out_stage_bytes(GAIN);
+  unsigned char* p = lds + n_chain_stages(GAIN) * chain_stage_bytes(GAIN) +
+                     (size_t)buf * out_stage_bytes(GAIN);
   OutStage s;
   s.q = reinterpret_cast<_Float16*>(p);
-  if (!GAIN) p += kStK;
-  s.p = reinterpret_cast<_Float16*>(p); p += kStT;
-  s.g = reinterpret_cast<float*>(p);
+  s.p = reinterpret_cast<_Float16*>(p);
+  s.g = reinterpret_cast<float*>(p + kStT);
   return s;
 }
 template <bool GAIN>
 __device__ __forceinline__ half8* exch_at(unsigned char* lds, int buf) {
-  return reinterpret_cast<half8*>(lds + 2 * chain_stage_bytes(GAIN) + 2 * out_stage_bytes(GAIN) +
-                                  (size_t)buf * kExBytes);
+  return reinterpret_cast<half8*>(lds + n_chain_stages(GAIN) * chain_stage_bytes(GAIN) +
+                                  2 * out_stage_bytes(GAIN) + (size_t)buf * kExBytes);
 }
 
-// ---- wavefronts 2-3 (pw = 0, 1). Every load instruction of a wavefront
-// reads 1 KB of consecutive bytes: for a tile with R-byte rows, lane l of
-// instruction i reads 16 bytes of row (rows per instruction) * (8 pw + i) + ...
-// Chain fields belong to one chunk, output fields to the one before it.
-template <bool GAIN> struct ProdX { uint4 gn[8]; };            // gains (chain chunk)
-template <> struct ProdX<false> { uint4 q[8]; };               // Q (output chunk)
+// ---- wavefronts 2-3 (pw = 0, 1). Each load instruction of a wavefront reads
+// 1 KB of consecutive bytes. Chain fields belong to one chunk, output fields
+// to the one before it.
+template <bool GAIN> struct ProdX {
+  uint4 gn[8];  // gains: rows 32 pw + 4 i + l / 16, piece l % 16 (chain chunk)
+  uint4 p[3];   // P, three-block form: 1 KB pieces 3 pw + i (output chunk)
+  float go;     // g of token l (output chunk)
+};
+template <> struct ProdX<false> {
+  uint4 q[8];   // Q: rows 32 pw + 4 i + l / 16, piece l % 16 (output chunk)
+};
 template <bool GAIN>
 struct ProdBuf : ProdX<GAIN> {
-  uint4 k[8];   // K: rows 32 pw + 4 i + l / 16, 16-byte piece l % 16
-  uint4 t[4];   // T: rows 32 pw + 8 i + l / 8, piece l % 8
-  uint4 v[2];   // V slice: rows 32 pw + 16 i + l / 4, piece l % 4
-  uint4 p[4];   // P (output chunk), as T
-  float4 sc;    // scalars of token l: chain chunk (pw 0) or output chunk (pw 1)
+  uint4 k[8];    // K: rows 32 pw + 4 i + l / 16, 16-byte piece l % 16
+  uint4 t[3];    // T, three-block form: 1 KB pieces 3 pw + i
+  uint4 v[2];    // V slice: rows 32 pw + 16 i + l / 4, piece l % 4
+  float4 sc0;    // scalars of token l (chain chunk): g, w, log2 g, write scale
+  float4 sc1;    //   R, Cf, f0, f1
+  float2 sc2;    //   value scale, extreme
 };
 
 struct ProdCtx {
@@ -531,11 +607,19 @@ struct ProdCtx {
   int pw, lane;
 };
 
+// T / P piece j (0..5) of the three-block form: block j / 2, block rows
+// 16 (j % 2) + l / 4, columns 8 (l % 4) .. + 8 -> matrix (row, col)
+__device__ __forceinline__ void tri_piece(int j, int l, int& row, int& col) {
+  const int blk = j >> 1, brow = 16 * (j & 1) + (l >> 2);
+  row = (blk == 0 ? 0 : 32) + brow;
+  col = (blk == 2 ? 32 : 0) + 8 * (l & 3);
+}
+
 template <bool GAIN>
 __device__ __forceinline__ void prod_load(const ProdCtx& x, ProdBuf<GAIN>& b, int cc, int co, int dv) {
   const int l = x.lane, r0 = 32 * x.pw;
-  const unsigned char* rc = x.rec + (size_t)cc * kRecBytes;
-  const unsigned char* ro = x.rec + (size_t)co * kRecBytes;
+  const unsigned char* rc = x.rec + (size_t)cc * rec_bytes(GAIN);
+  const unsigned char* ro = x.rec + (size_t)co * rec_bytes(GAIN);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int off_c = (cc * C + r0 + 4 * i) * (DK * 2) + l * 16;
@@ -544,14 +628,18 @@ __device__ __forceinline__ void prod_load(const ProdCtx& x, ProdBuf<GAIN>& b, in
     else b.q[i] = bload16(x.rx, (co * C + r0 + 4 * i) * (DK * 2) + l * 16);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    b.t[i] = reinterpret_cast<const uint4*>(rc + kRecT)[(r0 + 8 * i) * 8 + l];
-    b.p[i] = reinterpret_cast<const uint4*>(ro + kRecP)[(r0 + 8 * i) * 8 + l];
+  for (int i = 0; i < 3; ++i) {
+    b.t[i] = reinterpret_cast<const uint4*>(rc + kRecT)[(3 * x.pw + i) * 64 + l];
+    if constexpr (GAIN) b.p[i] = reinterpret_cast<const uint4*>(ro + rec_p_off(true))[(3 * x.pw + i) * 64 + l];
   }
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     b.v[i] = bload16(x.rv, (cc * C + r0 + 16 * i + (l >> 2)) * dv * 2 + (l & 3) * 16);
-  b.sc = reinterpret_cast<const float4*>((x.pw ? ro : rc) + kRecS)[l];
+  const float4* sc = reinterpret_cast<const float4*>(rc + rec_s_off(GAIN));
+  b.sc0 = sc[3 * l];
+  b.sc1 = sc[3 * l + 1];
+  b.sc2 = *reinterpret_cast<const float2*>(sc + 3 * l + 2);
+  if constexpr (GAIN) b.go = reinterpret_cast<const float4*>(ro + rec_s_off(true))[3 * l].x;
 }
 
 template <bool GAIN>
@@ -566,21 +654,31 @@ __device__ __forceinline__ void prod_stage(const ProdCtx& x, const ProdBuf<GAIN>
     else *reinterpret_cast<uint4*>(os.q + off) = bf16x8_to_f16x8(b.q[i], 1.f);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int off = (r0 + 8 * i + (l >> 3)) * CP + (l & 7) * 8;
-    *reinterpret_cast<uint4*>(cs.t + off) = b.t[i];
-    *reinterpret_cast<uint4*>(os.p + off) = b.p[i];
+  for (int i = 0; i < 3; ++i) {
+    int row, col;
+    tri_piece(3 * x.pw + i, l, row, col);
+    *reinterpret_cast<uint4*>(cs.t + row * CP + col) = b.t[i];
+    if constexpr (GAIN) *reinterpret_cast<uint4*>(os.p + row * CP + col) = b.p[i];
   }
+  // V times the value scale of its row (lane t holds token t's scalars)
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 2; ++i) {
+    const float vsr = __shfl(b.sc2.x, r0 + 16 * i + (l >> 2), 64);
     *reinterpret_cast<uint4*>(cs.v + (r0 + 16 * i + (l >> 2)) * VP + (l & 3) * 8) =
-        bf16x8_to_f16x8(b.v[i], 1.f);
+        bf16x8_to_f16x8(b.v[i], vsr);
+  }
   if (x.pw == 0) {
-    cs.g[l] = b.sc.x;
-    cs.w[l] = b.sc.y;
-    cs.vs[l] = b.sc.z;
+    cs.g[l] = b.sc0.x;
+    cs.w[l] = b.sc0.y;
+    cs.lg[l] = b.sc0.z;
+    cs.bs[l] = b.sc0.w;
+    if (l == 0) cs.extreme[0] = b.sc2.y;
   } else {
-    os.g[l] = b.sc.x;
+    cs.rr[l] = b.sc1.x;
+    cs.cf[l] = b.sc1.y;
+    cs.f0[l] = b.sc1.z;
+    cs.f1[l] = b.sc1.w;
+    if constexpr (GAIN) os.g[l] = b.go;
   }
 }
 
@@ -605,6 +703,7 @@ __device__ __forceinline__ void q_load(__amdgpu_buffer_rsrc_t rq, QBuf& b, int c
 template <bool GAIN, bool OBF16>
 __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
+  constexpr int NCH = n_chain_stages(GAIN);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 5, c32 = lane & 31;
@@ -626,8 +725,15 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
   const int j0 = tile * DV;
   const int last = a.nchunks - 1;
   const int nsteps = (a.nchunks + 2) & ~1;  // chunks + 1 (output lag), even
-  const unsigned char* rec_head = a.rec + (size_t)bh * a.nchunks * kRecBytes;
+  const unsigned char* rec_head = a.rec + (size_t)bh * a.nchunks * rec_bytes(GAIN);
   const size_t head_tok = (size_t)bh * a.L;
+
+  // transposed reads: group G = lane / 16 covers columns 16 (G % 2) .. + 16 and
+  // rows 4 (G / 2) .. + 4 of an 8-row half step; lane jj of the group
+  // addresses row jj / 4 and column quad jj % 4
+  const int G = lane >> 4, jj = lane & 15;
+  const int tr_row = 4 * (G >> 1) + (jj >> 2);
+  const int tr_col = 16 * (G & 1) + 4 * (jj & 3);
 
   if (wv >= 2) {
     // ------------------------------------------------------------ producers
@@ -642,17 +748,19 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
     // step c stages the chain inputs of chunk c + 1 and the output inputs of
     // chunk c from the register buffer that holds them, then reloads it with
     // chunks c + 3 and c + 2. Chunk indices are clamped to the last chunk;
-    // restaging it into an idle buffer is harmless.
+    // restaging it into a buffer no one reads this step is harmless.
     ProdBuf<GAIN> r0, r1;
     prod_load<GAIN>(x, r0, 0, 0, a.dv);
     prod_load<GAIN>(x, r1, min(1, last), 0, a.dv);
     prod_stage<GAIN>(x, r0, chain_stage<GAIN>(lds_raw, 0), out_stage<GAIN>(lds_raw, 1));
     prod_load<GAIN>(x, r0, min(2, last), min(1, last), a.dv);
     __syncthreads();
+    int cs_next = 1 % NCH;  // chain stage of chunk c + 1
     auto body = [&](int c, ProdBuf<GAIN>& r) {
       __builtin_amdgcn_sched_barrier(0);
-      prod_stage<GAIN>(x, r, chain_stage<GAIN>(lds_raw, (c + 1) & 1), out_stage<GAIN>(lds_raw, c & 1));
+      prod_stage<GAIN>(x, r, chain_stage<GAIN>(lds_raw, cs_next), out_stage<GAIN>(lds_raw, c & 1));
       prod_load<GAIN>(x, r, min(c + 3, last), min(c + 2, last), a.dv);
+      cs_next = cs_next + 1 == NCH ? 0 : cs_next + 1;
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -676,51 +784,163 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
       q_load(rq, b1, min(1, last), lane);
     }
     __syncthreads();
+    int cs_prev = NCH - 1;  // chain stage of chunk c - 1
     // step c (1 <= c <= nchunks) writes the outputs of chunk c - 1
     auto body = [&](int c, QBuf& b) {
       __builtin_amdgcn_sched_barrier(0);
       const int cc = c - 1;
       if (cc >= 0 && cc <= last) {
         const half8* ex = exch_at<GAIN>(lds_raw, cc & 1);
-        const OutStage st = out_stage<GAIN>(lds_raw, cc & 1);
-        half8 sv[8], uv[4], pa[6];
+        const OutStage os = out_stage<GAIN>(lds_raw, cc & 1);
+        const ChainStage cs = chain_stage<GAIN>(lds_raw, cs_prev);
+        // Q operands: product i = token block i / 8, k step i % 8
+        auto q_op = [&](int i) -> half8 {
+          const int tb = i >> 3, s = i & 7;
+          if constexpr (GAIN)
+            return cat(bf16x4_to_f16x4(b.q[tb][s][0]), bf16x4_to_f16x4(b.q[tb][s][1]));
+          else
+            return ld_op(os.q + (32 * tb + c32) * KP + 16 * s, h);
+        };
+        half8 sv[8], uv[4], qa[16], pa[6];
+        floatx16 o[2] = {floatx16{}, floatx16{}};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qa[i] = q_op(i);
 #pragma unroll
         for (int s = 0; s < 8; ++s) sv[s] = ex[s * 64 + lane];
+        if constexpr (!GAIN) {
+          // P^T = K Q^T on blocks (token block of K, of Q) = (0,0), (0,1), (1,1),
+          // k step outer so that every Q operand is read once, in order
+          floatx16 pt[3] = {floatx16{}, floatx16{}, floatx16{}};
+          half8 kb[2][8];
+          float4 fac[3][4];   // row factors: R (diagonal blocks 0, 2), f0 (block 1)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) uv[s] = ex[(8 + s) * 64 + lane];
-        pa[0] = ld_op(st.p + c32 * CP, h);
-        pa[1] = ld_op(st.p + c32 * CP + 16, h);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) pa[2 + s] = ld_op(st.p + (32 + c32) * CP + 16 * s, h);
-        floatx16 o[2];
-#pragma unroll
-        for (int tb = 0; tb < 2; ++tb) {
-          half8 qa[8];
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            if constexpr (GAIN)
-              qa[s] = cat(bf16x4_to_f16x4(b.q[tb][s][0]), bf16x4_to_f16x4(b.q[tb][s][1]));
-            else
-              qa[s] = ld_op(st.q + (32 * tb + c32) * KP + 16 * s, h);
+          for (int s = 0; s < 2; ++s) {
+            kb[0][s] = ld_op(cs.k + c32 * KP + 16 * s, h);
+            kb[1][s] = ld_op(cs.k + (32 + c32) * KP + 16 * s, h);
           }
-          floatx16 acc = {};
 #pragma unroll
-          for (int s = 0; s < 8; ++s) acc = mfma32(qa[s], sv[s], acc);
-          // rows are tokens: scale by g
+          for (int i = 8; i < 12; ++i) qa[i] = q_op(i);
+          __builtin_amdgcn_sched_barrier(0);
+          static_for<24>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            constexpr int s = i / 3, blk = i % 3;          // 0: (0,0) 1: (0,1) 2: (1,1)
+            constexpr int lb = blk == 2 ? 1 : 0, qb = blk == 0 ? 0 : 1;
+            pt[blk] = mfma32(kb[lb][s], qa[8 * qb + s], pt[blk]);
+            if constexpr (blk == 2 && s + 2 < 8) {
+              kb[0][s + 2] = ld_op(cs.k + c32 * KP + 16 * (s + 2), h);
+              kb[1][s + 2] = ld_op(cs.k + (32 + c32) * KP + 16 * (s + 2), h);
+            }
+            // Q operands: token block 0 k step s + 2 and block 1 k step s + 2
+            if constexpr (blk == 0 && s + 4 < 8) qa[s + 4] = q_op(s + 4);
+            if constexpr (blk == 1 && s + 4 < 8) qa[8 + s + 4] = q_op(8 + s + 4);
+            if constexpr (i >= 12) {
+              constexpr int q = i - 12, fb = q / 4, fj = q % 4;
+              const float* src = fb == 1 ? cs.f0 : cs.rr;
+              fac[fb][fj] = *reinterpret_cast<const float4*>(src + 32 * (fb == 2 ? 1 : 0) + 8 * fj + 4 * h);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          });
+          // P_il = (q_i . k_l) bs_l g_i / g_l for l <= i. Lane (h, c32) holds
+          // column i = 32 qb + c32 and rows l = 32 lb + 8 j + 4 h + r. The
+          // off-diagonal block multiplies f0_l f1_i; the diagonal blocks
+          // R_l Cf_i, or exp2 of log2 g differences in an extreme chunk.
+          const bool extreme =
+              __builtin_amdgcn_readfirstlane(__float_as_int(cs.extreme[0])) != 0;
+          const float f1i = cs.f1[32 + c32];
+          const float cfi[2] = {cs.cf[c32], cs.cf[32 + c32]};
+          const float lgi[2] = {cs.lg[c32], cs.lg[32 + c32]};
+          auto scale_quad = [&](int blk, int j, auto exact_c) {
+            constexpr bool exact = decltype(exact_c)::value;
+            const int lb = blk == 2 ? 1 : 0;
+            const int l0 = 32 * lb + 8 * j + 4 * h;
+            if (blk == 1) {
+              const float4 f0l = fac[1][j];
+              pt[1][4 * j + 0] *= f0l.x * f1i;
+              pt[1][4 * j + 1] *= f0l.y * f1i;
+              pt[1][4 * j + 2] *= f0l.z * f1i;
+              pt[1][4 * j + 3] *= f0l.w * f1i;
+            } else {
+              const int di = c32 - (8 * j + 4 * h);   // i - l for r = 0
+              if constexpr (!exact) {
+                const float4 rl = fac[blk][j];
+                const float rv[4] = {rl.x, rl.y, rl.z, rl.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  pt[blk][4 * j + r] = di >= r ? pt[blk][4 * j + r] * (rv[r] * cfi[lb]) : 0.f;
+              } else {
+                const float4 lgl = *reinterpret_cast<const float4*>(cs.lg + l0);
+                const float4 bsl = *reinterpret_cast<const float4*>(cs.bs + l0);
+                const float lgv[4] = {lgl.x, lgl.y, lgl.z, lgl.w};
+                const float bsv[4] = {bsl.x, bsl.y, bsl.z, bsl.w};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const float e = __builtin_amdgcn_exp2f(lgi[lb] - lgv[r]) * bsv[r];
+                  pt[blk][4 * j + r] = di >= r ? pt[blk][4 * j + r] * e : 0.f;
+                }
+              }
+            }
+          };
+          // Q S (16 products) with the scaling of P^T under it
+          auto qs_scaled = [&](auto exact_c) {
+            static_for<16>([&](auto ic) {
+              constexpr int i = decltype(ic)::value;
+              o[i & 1] = mfma32(qa[8 * (i & 1) + (i >> 1)], sv[i >> 1], o[i & 1]);
+              if constexpr (i < 12) scale_quad(i / 4, i % 4, exact_c);
+              if constexpr (i == 12) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) uv[s] = ex[(8 + s) * 64 + lane];
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            });
+          };
+          if (!extreme) qs_scaled(std::false_type{});
+          else qs_scaled(std::true_type{});
+          // operands of P U: output token block ib, k step s over l
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pa[0][e] = (_Float16)pt[0][e];
+            pa[1][e] = (_Float16)pt[0][8 + e];
+            pa[2][e] = (_Float16)pt[1][e];
+            pa[3][e] = (_Float16)pt[1][8 + e];
+            pa[4][e] = (_Float16)pt[2][e];
+            pa[5][e] = (_Float16)pt[2][8 + e];
+          }
+        } else {
+#pragma unroll
+          for (int i = 4; i < 16; ++i) qa[i] = q_op(i);
+          __builtin_amdgcn_sched_barrier(0);
+          static_for<16>([&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            o[i & 1] = mfma32(qa[8 * (i & 1) + (i >> 1)], sv[i >> 1], o[i & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          });
+#pragma unroll
+          for (int s = 0; s < 4; ++s) uv[s] = ex[(8 + s) * 64 + lane];
+          pa[0] = ld_op(os.p + c32 * CP, h);
+          pa[1] = ld_op(os.p + c32 * CP + 16, h);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) pa[2 + s] = ld_op(os.p + (32 + c32) * CP + 16 * s, h);
+        }
+        // rows of Q S are tokens: O = diag(g) Q S + P U
+        const float* gsrc = GAIN ? os.g : cs.g;
+#pragma unroll
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
-            const float4 gg = *reinterpret_cast<const float4*>(st.g + 32 * tb + 8 * g4 + 4 * h);
-            acc[4 * g4 + 0] *= gg.x;
-            acc[4 * g4 + 1] *= gg.y;
-            acc[4 * g4 + 2] *= gg.z;
-            acc[4 * g4 + 3] *= gg.w;
+            const float4 gg = *reinterpret_cast<const float4*>(gsrc + 32 * tb + 8 * g4 + 4 * h);
+            o[tb][4 * g4 + 0] *= gg.x;
+            o[tb][4 * g4 + 1] *= gg.y;
+            o[tb][4 * g4 + 2] *= gg.z;
+            o[tb][4 * g4 + 3] *= gg.w;
           }
-          o[tb] = acc;
-        }
         o[0] = mfma32(pa[0], uv[0], o[0]);
+        o[1] = mfma32(pa[2], uv[0], o[1]);
         o[0] = mfma32(pa[1], uv[1], o[0]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) o[1] = mfma32(pa[2 + s], uv[s], o[1]);
+        o[1] = mfma32(pa[3], uv[1], o[1]);
+        o[1] = mfma32(pa[4], uv[2], o[1]);
+        o[1] = mfma32(pa[5], uv[3], o[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (GAIN) q_load(rq, b, min(cc + 2, last), lane);
         // o[tb] register j: token 32 tb + 8 (j / 4) + 4 h + j % 4, column c32
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
@@ -733,8 +953,8 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
             else
               __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[tb][j]), ro, off, 0, 0);
           }
-        if constexpr (GAIN) q_load(rq, b, min(cc + 2, last), lane);
       }
+      cs_prev = cs_prev + 1 == NCH ? 0 : cs_prev + 1;
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -756,118 +976,132 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
     }
   __syncthreads();
 
-  // transposed reads: group G = lane / 16 covers columns 16 (G % 2) .. + 16 and
-  // rows 4 (G / 2) .. + 4 of an 8-row half step; lane jj of the group
-  // addresses row jj / 4 and column quad jj % 4
-  const int G = lane >> 4, jj = lane & 15;
-  const int tr_row = 4 * (G >> 1) + (jj >> 2);
-  const int tr_col = 16 * (G & 1) + 4 * (jj & 3);
-
+  // One step is 38 products issued back to back, one per "slot"; the
+  // conversions between them and all LDS reads are placed in the slots of
+  // earlier products so that they run under the matrix core instead of
+  // between its products:
+  //   slots  0- 7  K S, token block 0        S -> fp16 (blocks 1-3), V, g reads
+  //   slots  8-15  K S, token block 1        S *= g_n, X of block 0, w, T reads
+  //   slots 16-17  U0  = T00 X0              B^T reads (transposed)
+  //   slots 18-19  U1  = T10 X0              X of block 1
+  //   slots 20-21  U1 += T11 X1              U0 -> fp16, w U0 -> fp16
+  //   slots 22-29  S  += B^T w U, tokens 0-31    U1 -> fp16, w U1 -> fp16
+  //   slots 30-37  S  += B^T w U, tokens 32-63
+  int cs_cur = 0;  // chain stage of chunk c
   for (int c = 0; c < nsteps; ++c) {
+    __builtin_amdgcn_sched_barrier(0);
     if (c <= last) {
-      const ChainStage st = chain_stage<GAIN>(lds_raw, c & 1);
+      const ChainStage st = chain_stage<GAIN>(lds_raw, cs_cur);
       half8* ex = exch_at<GAIN>(lds_raw, c & 1);
       const int n = min(C, a.L - c * C);
-      // operands that do not depend on this chunk's results, issued first
-      half8 ka[2][8];
+      half8 s16[8], ka[16], x16[4], u16[4], uw16[4], ta[6];
+      half4 vv[2][4], btr[32];
+      float4 gg[2][4], ww[2][4];
+      floatx16 ks[2] = {floatx16{}, floatx16{}}, u[2] = {floatx16{}, floatx16{}};
+      // product i of K S: token block i / 8, k step i % 8
+      auto k_op = [&](int i) -> half8 {
+        return ld_op(st.k + (32 * (i >> 3) + c32) * KP + 16 * (i & 7), h);
+      };
+      auto s_to_f16 = [&](int b) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) ka[blk][s] = ld_op(st.k + (32 * blk + c32) * KP + 16 * s, h);
-      // S in fp16, as the k = d_k operand
-      half8 s16[8];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          s16[2 * b][i] = (_Float16)S[b][i];
-          s16[2 * b + 1][i] = (_Float16)S[b][8 + i];
+        for (int e = 0; e < 8; ++e) {
+          s16[2 * b][e] = (_Float16)S[b][e];
+          s16[2 * b + 1][e] = (_Float16)S[b][8 + e];
         }
+        ex[(2 * b) * 64 + lane] = s16[2 * b];
+        ex[(2 * b + 1) * 64 + lane] = s16[2 * b + 1];
+      };
+      // X = V' - g K S for token block blk, column quads g4 (k = token operand)
+      auto x_quad = [&](int blk, int g4) {
 #pragma unroll
-      for (int s = 0; s < 8; ++s) ex[s * 64 + lane] = s16[s];
-      half4 vv[2][4];
-      float4 gg[2][4], sc[2][4];
+        for (int r = 0; r < 4; ++r) {
+          const float gv = r == 0 ? gg[blk][g4].x : r == 1 ? gg[blk][g4].y : r == 2 ? gg[blk][g4].z : gg[blk][g4].w;
+          x16[2 * blk + (g4 >> 1)][4 * (g4 & 1) + r] =
+              (_Float16)((float)vv[blk][g4][r] - gv * ks[blk][4 * g4 + r]);
+        }
+      };
+      // U (outputs) and w U (state update) in fp16 for token block blk, quad g4
+      auto u_quad = [&](int blk, int g4) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+        for (int r = 0; r < 4; ++r) {
+          const float wv = r == 0 ? ww[blk][g4].x : r == 1 ? ww[blk][g4].y : r == 2 ? ww[blk][g4].z : ww[blk][g4].w;
+          const float uv = u[blk][4 * g4 + r];
+          u16[2 * blk + (g4 >> 1)][4 * (g4 & 1) + r] = (_Float16)uv;
+          uw16[2 * blk + (g4 >> 1)][4 * (g4 & 1) + r] = (_Float16)(uv * wv);
+        }
+      };
+      // transposed write vectors, in the order the state update uses them:
+      // q = 0..31 -> (k step s, d_k block b) = tokens 0-31 first, b outer
+      auto bt_read = [&](int q) {
+        const int part = q >> 4, b = (q >> 2) & 3, s = 2 * part + ((q >> 1) & 1), hi = q & 1;
+        btr[q] = ld_tr(st.b + (16 * s + 8 * hi + tr_row) * KP + 32 * b + tr_col);
+      };
+      const int tr_[6] = {0, 0, 32, 32, 32, 32}, tk_[6] = {0, 16, 0, 16, 32, 48};
+
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
+      for (int i = 0; i < 4; ++i) ka[i] = k_op(i);
+      s_to_f16(0);
+      const float gn = st.g[n - 1];
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<38>([&](auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
+        // ---- the product
+        if constexpr (slot < 16) {
+          ks[slot >> 3] = mfma32(ka[slot], s16[slot & 7], ks[slot >> 3]);
+        } else if constexpr (slot < 22) {
+          const int j = slot - 16;  // 0,1: U0 <- T00 ; 2,3: U1 <- T10 ; 4,5: U1 <- T11
+          const int acc = j < 2 ? 0 : 1, xs = j < 4 ? (j & 1) : 2 + (j & 1);
+          u[acc] = mfma32(ta[j], x16[xs], u[acc]);
+        } else {
+          const int q = slot - 22, part = q >> 3, b = (q >> 1) & 3, s = 2 * part + (q & 1);
+          const int bi = 16 * part + 4 * b + 2 * (q & 1);
+          S[b] = mfma32(cat(btr[bi], btr[bi + 1]), uw16[s], S[b]);
+        }
+        // ---- work placed under it
+        if constexpr (slot < 12) ka[slot + 4] = k_op(slot + 4);
+        if constexpr (slot == 0) s_to_f16(1);
+        if constexpr (slot == 2) s_to_f16(2);
+        if constexpr (slot == 4) s_to_f16(3);
+        if constexpr (slot >= 1 && slot <= 8) {
+          const int q = slot - 1, blk = q >> 2, g4 = q & 3;
           vv[blk][g4] = ld_tr(st.v + (32 * blk + 8 * g4 + tr_row) * VP + tr_col);
           gg[blk][g4] = *reinterpret_cast<const float4*>(st.g + 32 * blk + 8 * g4 + 4 * h);
-          sc[blk][g4] = *reinterpret_cast<const float4*>(st.vs + 32 * blk + 8 * g4 + 4 * h);
         }
-      half8 ta[6];
-      ta[0] = ld_op(st.t + c32 * CP, h);
-      ta[1] = ld_op(st.t + c32 * CP + 16, h);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) ta[2 + s] = ld_op(st.t + (32 + c32) * CP + 16 * s, h);
-      // K S for the two token blocks
-      floatx16 ks[2] = {floatx16{}, floatx16{}};
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) ks[blk] = mfma32(ka[blk][s], s16[s], ks[blk]);
-      // transposed write vectors for the state update (independent of U)
-      half8 bt[4][4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const _Float16* base = st.b + 32 * b + tr_col;
-          bt[b][s] = cat(ld_tr(base + (16 * s + tr_row) * KP), ld_tr(base + (16 * s + 8 + tr_row) * KP));
+        if constexpr (slot >= 8 && slot <= 11) S[slot - 8] = S[slot - 8] * gn;
+        if constexpr (slot >= 9 && slot <= 12) {
+          const int q = slot - 9;
+          ww[q >> 1][2 * (q & 1)] = *reinterpret_cast<const float4*>(st.w + 32 * (q >> 1) + 16 * (q & 1) + 4 * h);
+          ww[q >> 1][2 * (q & 1) + 1] = *reinterpret_cast<const float4*>(st.w + 32 * (q >> 1) + 16 * (q & 1) + 8 + 4 * h);
         }
-      float4 ww[2][4];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4)
-          ww[blk][g4] = *reinterpret_cast<const float4*>(st.w + 32 * blk + 8 * g4 + 4 * h);
-      const float gn = st.g[n - 1];
-      // X = v_scale V - g K S, as the k = token operand
-      half8 x16[4];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float gv[4] = {gg[blk][g4].x, gg[blk][g4].y, gg[blk][g4].z, gg[blk][g4].w};
-          const float sv[4] = {sc[blk][g4].x, sc[blk][g4].y, sc[blk][g4].z, sc[blk][g4].w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            x16[2 * blk + (g4 >> 1)][4 * (g4 & 1) + r] =
-                (_Float16)(sv[r] * (float)vv[blk][g4][r] - gv[r] * ks[blk][4 * g4 + r]);
+        if constexpr (slot >= 12 && slot <= 14) {
+          const int j = 2 * (slot - 12);
+          ta[j] = ld_op(st.t + (tr_[j] + c32) * CP + tk_[j], h);
+          ta[j + 1] = ld_op(st.t + (tr_[j + 1] + c32) * CP + tk_[j + 1], h);
         }
-      // U = T X (T is lower triangular by 32-blocks)
-      floatx16 u[2] = {floatx16{}, floatx16{}};
-      u[0] = mfma32(ta[0], x16[0], u[0]);
-      u[1] = mfma32(ta[2], x16[0], u[1]);
-      u[0] = mfma32(ta[1], x16[1], u[0]);
-      u[1] = mfma32(ta[3], x16[1], u[1]);
-      u[1] = mfma32(ta[4], x16[2], u[1]);
-      u[1] = mfma32(ta[5], x16[3], u[1]);
-      // U (for the outputs) and w U (for the state update), k = token
-      half8 u16[4], uw16[4];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float wv4[4] = {ww[blk][g4].x, ww[blk][g4].y, ww[blk][g4].z, ww[blk][g4].w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float uv = u[blk][4 * g4 + r];
-            u16[2 * blk + (g4 >> 1)][4 * (g4 & 1) + r] = (_Float16)uv;
-            uw16[2 * blk + (g4 >> 1)][4 * (g4 & 1) + r] = (_Float16)(uv * wv4[r]);
-          }
+        if constexpr (slot >= 10 && slot <= 13) x_quad(0, slot - 10);
+        if constexpr (slot >= 15 && slot <= 22) {
+          const int q0 = 4 * (slot - 15);
+          bt_read(q0); bt_read(q0 + 1); bt_read(q0 + 2); bt_read(q0 + 3);
         }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) ex[(8 + s) * 64 + lane] = u16[s];
-      // S = g_n S + (diag(w) B)^T U
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        floatx16 acc = S[b] * gn;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) acc = mfma32(bt[b][s], uw16[s], acc);
-        S[b] = acc;
-      }
+        if constexpr (slot == 17 || slot == 18) {
+          x_quad(1, 2 * (slot - 17));
+          x_quad(1, 2 * (slot - 17) + 1);
+        }
+        if constexpr (slot == 20) { u_quad(0, 0); u_quad(0, 1); }
+        if constexpr (slot == 21) {
+          u_quad(0, 2); u_quad(0, 3);
+          ex[8 * 64 + lane] = u16[0];
+          ex[9 * 64 + lane] = u16[1];
+        }
+        if constexpr (slot >= 24 && slot <= 27) u_quad(1, slot - 24);
+        if constexpr (slot == 28) {
+          ex[10 * 64 + lane] = u16[2];
+          ex[11 * 64 + lane] = u16[3];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
+    cs_cur = cs_cur + 1 == NCH ? 0 : cs_cur + 1;
     __syncthreads();
   }
 
@@ -888,9 +1122,9 @@ bool scan_mfma_supported(int dk, int dv, int chunk) {
   return dk == DK && chunk == C && dv % DV == 0 && dv >= DV;
 }
 
-size_t scan_mfma_workspace_bytes(int BH, int L) {
+size_t scan_mfma_workspace_bytes(int BH, int L, bool gain) {
   const size_t nchunks = ((size_t)L + C - 1) / C;
-  return (size_t)BH * nchunks * kRecBytes;
+  return (size_t)BH * nchunks * rec_bytes(gain);
 }
 
 hipError_t launch_tinv_mfma(const ScanArgs& s, void* tbuf, hipStream_t st) {

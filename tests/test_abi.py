@@ -64,9 +64,9 @@ def test_status_strings_and_constants(kdn):
 def test_workspace_size(kdn):
     assert kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 64, "delta", kdn.F32) == 0
     assert kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 32, "delta", kdn.BF16) == 0
-    # matrix-core path, one record per (head, chunk): (I + A)^-1 and the masked
-    # decayed query-key product, both fp16 [64][64], then 64 float4 token scalars
-    tinv = 4 * 16 * 64 * (2 * 64 * 64 * 2 + 64 * 16)
+    # matrix-core path, one record per (head, chunk): the three nonzero 32 x 32
+    # fp16 blocks of (I + A)^-1 and three float4 scalars per token
+    tinv = 4 * 16 * 64 * (3 * 32 * 32 * 2 + 64 * 48)
     assert kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 64, "delta", kdn.BF16) == tinv
     ws = kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 64, "diag", kdn.BF16)
     gains = 4 * 16 * 4096 * 128 * 2
