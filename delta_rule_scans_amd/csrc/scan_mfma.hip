@@ -443,6 +443,8 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 typedef short short4v __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
 __device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
@@ -884,7 +886,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
           auto qs_scaled = [&](auto exact_c) {
             static_for<16>([&](auto ic) {
               constexpr int i = decltype(ic)::value;
-              o[i & 1] = mfma32(qa[8 * (i & 1) + (i >> 1)], sv[i >> 1], o[i & 1]);
+              o[i & 1] = mfma32(sv[i >> 1], qa[8 * (i & 1) + (i >> 1)], o[i & 1]);
               if constexpr (i < 12) scale_quad(i / 4, i % 4, exact_c);
               if constexpr (i == 12) {
 #pragma unroll
@@ -911,7 +913,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
           __builtin_amdgcn_sched_barrier(0);
           static_for<16>([&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            o[i & 1] = mfma32(qa[8 * (i & 1) + (i >> 1)], sv[i >> 1], o[i & 1]);
+            o[i & 1] = mfma32(sv[i >> 1], qa[8 * (i & 1) + (i >> 1)], o[i & 1]);
             __builtin_amdgcn_sched_barrier(0);
           });
 #pragma unroll
@@ -921,37 +923,42 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
 #pragma unroll
           for (int s = 0; s < 4; ++s) pa[2 + s] = ld_op(os.p + (32 + c32) * CP + 16 * s, h);
         }
-        // rows of Q S are tokens: O = diag(g) Q S + P U
+        // The products run transposed, O^T = S^T Q^T + U^T P^T (the operand
+        // registers are the same, A and B swap), so that each lane ends with 4
+        // consecutive value columns of one token: 16-byte stores. Columns of
+        // O^T are tokens: O^T = (S^T Q^T) diag(g) + U^T P^T.
         const float* gsrc = GAIN ? os.g : cs.g;
+        const float gt[2] = {gsrc[c32], gsrc[32 + c32]};
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const float4 gg = *reinterpret_cast<const float4*>(gsrc + 32 * tb + 8 * g4 + 4 * h);
-            o[tb][4 * g4 + 0] *= gg.x;
-            o[tb][4 * g4 + 1] *= gg.y;
-            o[tb][4 * g4 + 2] *= gg.z;
-            o[tb][4 * g4 + 3] *= gg.w;
-          }
-        o[0] = mfma32(pa[0], uv[0], o[0]);
-        o[1] = mfma32(pa[2], uv[0], o[1]);
-        o[0] = mfma32(pa[1], uv[1], o[0]);
-        o[1] = mfma32(pa[3], uv[1], o[1]);
-        o[1] = mfma32(pa[4], uv[2], o[1]);
-        o[1] = mfma32(pa[5], uv[3], o[1]);
+          for (int e = 0; e < 16; ++e) o[tb][e] *= gt[tb];
+        o[0] = mfma32(uv[0], pa[0], o[0]);
+        o[1] = mfma32(uv[0], pa[2], o[1]);
+        o[0] = mfma32(uv[1], pa[1], o[0]);
+        o[1] = mfma32(uv[1], pa[3], o[1]);
+        o[1] = mfma32(uv[2], pa[4], o[1]);
+        o[1] = mfma32(uv[3], pa[5], o[1]);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (GAIN) q_load(rq, b, min(cc + 2, last), lane);
-        // o[tb] register j: token 32 tb + 8 (j / 4) + 4 h + j % 4, column c32
+        // o[tb] registers 4 q .. 4 q + 3: token 32 tb + c32, columns 8 q + 4 h .. + 4
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int tok = cc * C + 32 * tb + 8 * (j >> 2) + 4 * h + (j & 3);
-            const int off = (tok * a.dv + c32) * esz;
-            if constexpr (OBF16)
-              __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(o[tb][j]), ro, off, 0, 0);
-            else
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(o[tb][j]), ro, off, 0, 0);
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int tok = cc * C + 32 * tb + c32;
+            const int off = (tok * a.dv + 8 * q4 + 4 * h) * esz;
+            if constexpr (OBF16) {
+              const uint32_t lo = (uint32_t)f32_to_bf16(o[tb][4 * q4]) |
+                                  ((uint32_t)f32_to_bf16(o[tb][4 * q4 + 1]) << 16);
+              const uint32_t hi = (uint32_t)f32_to_bf16(o[tb][4 * q4 + 2]) |
+                                  ((uint32_t)f32_to_bf16(o[tb][4 * q4 + 3]) << 16);
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, make_uint2(lo, hi)), ro, off, 0, 0);
+            } else {
+              const uint4 w4 = make_uint4(__float_as_uint(o[tb][4 * q4]), __float_as_uint(o[tb][4 * q4 + 1]),
+                                          __float_as_uint(o[tb][4 * q4 + 2]), __float_as_uint(o[tb][4 * q4 + 3]));
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w4), ro, off, 0, 0);
+            }
           }
       }
       cs_prev = cs_prev + 1 == NCH ? 0 : cs_prev + 1;
