@@ -54,16 +54,23 @@ DECODE_BYTES_PER_HEAD = (
 )
 
 
+def code_digest(path):
+    """sha256 of a C/HIP source with its // comments and all whitespace removed,
+    so that edits to comments alone keep a counter record valid."""
+    import hashlib
+    import re
+    code = "".join(re.sub(r"//.*", "", line) for line in open(path, encoding="utf-8"))
+    return hashlib.sha256(re.sub(r"\s+", "", code).encode()).hexdigest()
+
+
 def measured_traffic(kernel_ms):
     """HBM bytes per launch of the state kernel from the committed counter runs
-    (profiles/*_traffic.json), or None when the kernel source changed since."""
-    import hashlib
+    (profiles/*_traffic.json), or None when the kernel code changed since."""
     path = os.path.join(ROOT, "profiles", "scan_gated_B4H16L4096_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = os.path.join(ROOT, rec["source"])
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec["source_sha256"]:
+    if code_digest(os.path.join(ROOT, rec["source"])) != rec["code_sha256"]:
         return None
     return rec["hbm_read_bytes"] + rec["hbm_write_bytes"]
 

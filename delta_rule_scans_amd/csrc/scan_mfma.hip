@@ -19,20 +19,21 @@
 //    reductions through DPP), the six off-diagonal blocks follow by block
 //    products on the matrix cores, diagonal by diagonal:
 //    T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj.
-//    Output per (head, chunk): T and P (fp16, 64 x 64 each) and the scalars.
+//    Output per (head, chunk): T (and P for the Kalman writes) in fp16, and
+//    the token scalars.
 //  * state_kernel: one workgroup per (head, 32-column slice of d_v); the loop
-//    over chunks is sequential. The float32 state slice (128 x 32) stays in
-//    the matrix-core accumulators for the whole sequence; its fp16 copy in LDS
-//    feeds the products K S and Q S. Per chunk: K S and Q S, U = T X, P U and
-//    the state update, three workgroup barriers; the next chunk's inputs are
-//    prefetched two chunks ahead into registers.
+//    over chunks is sequential. One wavefront carries the chain (K S, U = T X,
+//    state update) with the float32 state slice (128 x 32) in its matrix-core
+//    accumulators for the whole sequence, one writes the outputs of the chunk
+//    before, two stage the inputs; details at the kernel.
 //
-// All matrix products are v_mfma_f32_16x16x32_f16: fp16 operands, fp32
-// accumulation. bf16 inputs are converted to fp16 when staged in LDS (exact
-// for bf16 values of magnitude in [2^-14, 65504]). fp16 rather than bf16
-// operands because the intermediate operands (S, X, U, P, T) need the 3 extra
-// significand bits: with bf16 operands the output error at the gated-delta
-// workload is ~3.7e-2 RMS(o), with fp16 ~5e-3.
+// Matrix products are fp16 x fp16 -> fp32: v_mfma_f32_16x16x32_f16 in the
+// prepare kernel, v_mfma_f32_32x32x16_f16 in the state kernel. bf16 inputs are
+// converted to fp16 when staged (exact for bf16 values of magnitude in
+// [2^-14, 65504]). fp16 rather than bf16 operands because the intermediate
+// operands (S, X, U, P, T) need the 3 extra significand bits: with bf16
+// operands the output error at the gated-delta workload is ~3.7e-2 RMS(o),
+// with fp16 ~5e-3.
 //
 // Operand layouts: an MFMA reads A as [m][k] and B as [n][k] with k contiguous
 // (16-byte LDS reads); its result gives each lane 4 consecutive rows of one
