@@ -156,8 +156,9 @@ struct PrepArgs {
 constexpr int kAdP = 17;  // fp32 pitch of the diagonal blocks of A
 constexpr int kPrepR1 = (C * KP > 2 * C * CP ? C * KP : 2 * C * CP) * 2;  // sQ, later sT + sTt
 
+// The delta write stages only K, which then shares the first region with T.
 size_t prep_lds_bytes(bool gain) {
-  return (size_t)kPrepR1 + (size_t)C * KP * 2 + (gain ? (size_t)C * KP * 2 : 0) +
+  return (size_t)kPrepR1 + (gain ? (size_t)2 * C * KP * 2 : 0) +
          (size_t)C * CP * 2 + (size_t)4 * 16 * kAdP * 4 + (size_t)4 * 16 * 24 * 2 +
          (size_t)2 * C * 4;
 }
@@ -170,14 +171,15 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   _Float16* sT = reinterpret_cast<_Float16*>(p);   // [C][CP] (phases 3-5, reuses sQ)
   _Float16* sTt = sT + C * CP;                     // [C][CP] T transposed
   p += kPrepR1;
-  _Float16* sK = reinterpret_cast<_Float16*>(p);   // [C][KP] (phases 1-2)
-  _Float16* sP = sK;                               // [C][CP] (phases 3-5, reuses sK)
-  p += C * KP * 2;
-  _Float16* sB = sK;
+  _Float16* sK = sQ;                               // [C][KP] (phases 1-2)
+  _Float16* sB = sK;                               // [C][KP] write vectors
   if (gain) {
+    sK = reinterpret_cast<_Float16*>(p);
+    p += C * KP * 2;
     sB = reinterpret_cast<_Float16*>(p);
     p += C * KP * 2;
   }
+  _Float16* sP = sK;                               // [C][CP] (phases 3-5, Kalman writes)
   _Float16* sAh = reinterpret_cast<_Float16*>(p);  // [C][CP] A in fp16
   p += C * CP * 2;
   float* sAd = reinterpret_cast<float*>(p);        // [4][16][kAdP] diagonal blocks of A
@@ -382,11 +384,12 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
       const int row = (blk == 0 ? 0 : 32) + brow, col = (blk == 2 ? 32 : 0) + 8 * piece;
       // 16 x 16 blocks above the diagonal were never written: zeros
       const bool lower = (col >> 4) <= (row >> 4);
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      const uint4 tv = lower ? *reinterpret_cast<const uint4*>(sT + row * CP + col) : z;
+      uint4 tv = *reinterpret_cast<const uint4*>(sT + row * CP + col);
+      if (!lower) tv = make_uint4(0, 0, 0, 0);
       *reinterpret_cast<uint4*>(tdst + blk * 1024 + brow * 32 + 8 * piece) = tv;
       if (gain) {
-        const uint4 pv = lower ? *reinterpret_cast<const uint4*>(sP + row * CP + col) : z;
+        uint4 pv = *reinterpret_cast<const uint4*>(sP + row * CP + col);
+        if (!lower) pv = make_uint4(0, 0, 0, 0);
         *reinterpret_cast<uint4*>(pdst + blk * 1024 + brow * 32 + 8 * piece) = pv;
       }
     }
