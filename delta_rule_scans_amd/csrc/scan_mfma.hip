@@ -96,17 +96,30 @@ __device__ __forceinline__ void st4(_Float16* p, floatx4 x) {
   *reinterpret_cast<half4*>(p) = h;
 }
 
+typedef float float2v __attribute__((ext_vector_type(2)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+
+// Two floats -> two fp16 in one dword (one v_cvt_pk_f16_f32).
+__device__ __forceinline__ uint32_t pk_f16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(float2v{lo, hi}, half2v));
+}
+
 // 8 bf16 values (one 16-byte load), each times `scale`, -> 8 fp16 values.
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u, float scale) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
   uint32_t r[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const _Float16 lo = (_Float16)(__uint_as_float(w[i] << 16) * scale);
-    const _Float16 hi = (_Float16)(__uint_as_float(w[i] & 0xffff0000u) * scale);
-    r[i] = (uint32_t)__builtin_bit_cast(uint16_t, lo) |
-           ((uint32_t)__builtin_bit_cast(uint16_t, hi) << 16);
-  }
+  for (int i = 0; i < 4; ++i)
+    r[i] = pk_f16(__uint_as_float(w[i] << 16) * scale, __uint_as_float(w[i] & 0xffff0000u) * scale);
+  return make_uint4(r[0], r[1], r[2], r[3]);
+}
+// The same without a scale.
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 u) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  uint32_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = pk_f16(__uint_as_float(w[i] << 16), __uint_as_float(w[i] & 0xffff0000u));
   return make_uint4(r[0], r[1], r[2], r[3]);
 }
 
@@ -204,9 +217,9 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
     uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, gv = qv;
     if (row < n) {
       const size_t off = (tok + row) * DK + c8 * 8;
-      kv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.k + off), 1.f);
+      kv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.k + off));
       if (gain) {
-        qv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.q + off), 1.f);
+        qv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.q + off));
         gv = *reinterpret_cast<const uint4*>(a.gain + off);
       }
     }
@@ -490,12 +503,8 @@ __device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, int off) {
 
 // 4 bf16 values (8 bytes) -> 4 fp16 values.
 __device__ __forceinline__ half4 bf16x4_to_f16x4(uint2 u) {
-  half4 r;
-  r[0] = (_Float16)__uint_as_float(u.x << 16);
-  r[1] = (_Float16)__uint_as_float(u.x & 0xffff0000u);
-  r[2] = (_Float16)__uint_as_float(u.y << 16);
-  r[3] = (_Float16)__uint_as_float(u.y & 0xffff0000u);
-  return r;
+  return __builtin_bit_cast(half4, make_uint2(pk_f16(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u)),
+                                              pk_f16(__uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u))));
 }
 
 struct StateArgs {
@@ -655,9 +664,9 @@ __device__ __forceinline__ void prod_stage(const ProdCtx& x, const ProdBuf<GAIN>
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int off = (r0 + 4 * i + (l >> 4)) * KP + (l & 15) * 8;
-    *reinterpret_cast<uint4*>(cs.k + off) = bf16x8_to_f16x8(b.k[i], 1.f);
+    *reinterpret_cast<uint4*>(cs.k + off) = bf16x8_to_f16x8(b.k[i]);
     if constexpr (GAIN) *reinterpret_cast<uint4*>(cs.b + off) = b.gn[i];
-    else *reinterpret_cast<uint4*>(os.q + off) = bf16x8_to_f16x8(b.q[i], 1.f);
+    else *reinterpret_cast<uint4*>(os.q + off) = bf16x8_to_f16x8(b.q[i]);
   }
 #pragma unroll
   for (int i = 0; i < 3; ++i) {
