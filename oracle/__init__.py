@@ -27,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kdn_oracle.c")
 _LIB = os.path.join(_HERE, "libkdn_oracle.so")
 
-MODES = {"delta": 0, "diag": 1, "full": 2}
+MODES = {"delta": 0, "diag": 1, "full": 2, "iso": 3}
 RESIDS = {"gated": 0, "plain": 1}
 
 
@@ -78,7 +78,7 @@ def _ptr(x):
 def scan(q, k, v, alpha=None, beta=None, r=None, cov0=None, q_noise_var: float = 0.0,
          S0=None, mode: str = "delta", resid: str = "gated", want_m: bool = True) -> dict:
     """Sequential fp64 scan. q, k: [B,H,L,dk]; v: [B,H,L,dv]; alpha/beta/r: [B,H,L].
-    cov0: [B,H,dk] (diag) or [B,H,dk,dk] (full). S0: [B,H,dk,dv] (default zeros).
+    cov0: [B,H,dk] (diag), [B,H,dk,dk] (full) or [B,H] (iso). S0: [B,H,dk,dv] (default zeros).
     Returns dict(o [B,H,L,dv], S [B,H,dk,dv], cov, m [B,H,L]) in float64."""
     q, k, v = _f32(q), _f32(k), _f32(v)
     B, H, L, dk = q.shape
@@ -94,6 +94,8 @@ def scan(q, k, v, alpha=None, beta=None, r=None, cov0=None, q_noise_var: float =
         cov = np.array(cov0, dtype=np.float64, order="C").reshape(B, H, dk)
     elif mode == "full":
         cov = np.array(cov0, dtype=np.float64, order="C").reshape(B, H, dk, dk)
+    elif mode == "iso":
+        cov = np.array(cov0, dtype=np.float64, order="C").reshape(B, H)
     o = np.zeros((B, H, L, dv))
     m = np.zeros((B, H, L)) if want_m else None
     rc = _load().oracle_scan(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),

@@ -44,6 +44,7 @@
 #define ORC_DELTA 0
 #define ORC_DIAG 1
 #define ORC_FULL 2
+#define ORC_ISO 3
 #define ORC_GATED 0
 #define ORC_PLAIN 1
 
@@ -74,6 +75,12 @@
  * 1/p_i = 1/p-_i + k_i^2 / r, i.e. p_i = p-_i r / (r + p-_i k_i^2).
  * With alpha = 1, r = 1, Q = 0 and P_0 = eps^-1 I the FULL write is the
  * recursive-least-squares update of [PC eq. (7)].
+ * ISO keeps one variance p per (batch, head), the isotropic variant that
+ * [KDN abstract] lists beside the diagonal one (reading R4): the covariance is
+ * p I, the gain is the exact one-step posterior mean under that prior,
+ * b = p- k / (p- ||k||^2 + r), and the posterior precision (1/p-) I + k k^T / r
+ * is projected back onto multiples of the identity by KL(q||p), which keeps
+ * its mean diagonal: 1/p = 1/p- + ||k||^2 / (d_k r).
  *
  * Read-out o_t = S_t^T q_t, after the write (reading S2; the layer output is
  * the predictive mean [MBD abstract]).
@@ -95,6 +102,7 @@ static void scan_one(int L, int dk, int dv,
     double *pm = b + dk;           /* dk  (DIAG p-) */
     double *u = pm + dk;           /* dk  (FULL P- k) */
     double *Pm = u + dk;           /* dk*dk (FULL P-) */
+    double pm_iso = 0.0, kk_iso = 0.0; /* ISO p- and ||k||^2 */
 
     for (int t = 0; t < L; ++t) {
         const float *kt = k + (size_t)t * dk;
@@ -107,6 +115,8 @@ static void scan_one(int L, int dk, int dv,
         /* predict the covariance */
         if (mode == ORC_DIAG) {
             for (int i = 0; i < dk; ++i) pm[i] = a * a * cov[i] + Qt;
+        } else if (mode == ORC_ISO) {
+            pm_iso = a * a * cov[0] + Qt;
         } else if (mode == ORC_FULL) {
             for (int i = 0; i < dk; ++i)
                 for (int j = 0; j < dk; ++j)
@@ -130,6 +140,11 @@ static void scan_one(int L, int dk, int dv,
             s = rt;
             for (int i = 0; i < dk; ++i) s += pm[i] * (double)kt[i] * (double)kt[i];
             for (int i = 0; i < dk; ++i) b[i] = pm[i] * (double)kt[i] / s;
+        } else if (mode == ORC_ISO) {
+            kk_iso = 0.0;
+            for (int i = 0; i < dk; ++i) kk_iso += (double)kt[i] * (double)kt[i];
+            s = pm_iso * kk_iso + rt;
+            for (int i = 0; i < dk; ++i) b[i] = pm_iso * (double)kt[i] / s;
         } else {
             for (int i = 0; i < dk; ++i) {
                 double acc = 0.0;
@@ -152,6 +167,8 @@ static void scan_one(int L, int dk, int dv,
                 const double k2 = (double)kt[i] * (double)kt[i];
                 cov[i] = pm[i] * rt / (rt + pm[i] * k2);
             }
+        } else if (mode == ORC_ISO) {
+            cov[0] = pm_iso * dk * rt / (dk * rt + pm_iso * kk_iso);
         } else if (mode == ORC_FULL) {
             for (int i = 0; i < dk; ++i)
                 for (int j = 0; j < dk; ++j)
@@ -185,7 +202,8 @@ static void scan_one(int L, int dk, int dv,
  *   q, k: [B,H,L,dk] float32; v: [B,H,L,dv] float32.
  *   alpha, beta, r: [B,H,L] float32. alpha NULL => 1; r NULL => 1;
  *   beta is required in DELTA mode and ignored otherwise.
- *   cov: DIAG [B,H,dk] / FULL [B,H,dk,dk] float64, in = prior, out = final.
+ *   cov: DIAG [B,H,dk] / FULL [B,H,dk,dk] / ISO [B,H] float64, in = prior,
+ *        out = final.
  *   S:   [B,H,dk,dv] float64, in = S_0, out = S_L.
  *   o:   [B,H,L,dv] float64 out;  m: [B,H,L] float64 out (may be NULL).
  * Returns 0, or -1 for an unsupported combination.
@@ -196,7 +214,7 @@ int oracle_scan(int B, int H, int L, int dk, int dv,
                 double *cov, double q_noise_var, double *S,
                 int mode, int resid, double *o, double *m)
 {
-    if (mode != ORC_DELTA && mode != ORC_DIAG && mode != ORC_FULL) return -1;
+    if (mode != ORC_DELTA && mode != ORC_DIAG && mode != ORC_FULL && mode != ORC_ISO) return -1;
     if (resid == ORC_PLAIN && mode != ORC_DELTA) return -1;
     if (mode == ORC_DELTA && !beta) return -1;
     if (mode != ORC_DELTA && !cov) return -1;
@@ -214,6 +232,7 @@ int oracle_scan(int B, int H, int L, int dk, int dv,
         double *covp = NULL;
         if (mode == ORC_DIAG) covp = cov + (size_t)bh * dk;
         if (mode == ORC_FULL) covp = cov + (size_t)bh * dk * dk;
+        if (mode == ORC_ISO) covp = cov + bh;
         scan_one(L, dk, dv, q + tok * dk, k + tok * dk, v + tok * dv,
                  alpha ? alpha + tok : NULL, beta ? beta + tok : NULL, r ? r + tok : NULL,
                  covp, q_noise_var, S + (size_t)bh * dk * dv, mode, resid,

@@ -306,6 +306,104 @@ def test_delta_is_covariance_reset_kalman(orc):
 
 
 # ---------------------------------------------------------------------------
+# Isotropic-covariance write (one variance per head)
+# ---------------------------------------------------------------------------
+
+def test_iso_one_step_is_isotropic_projection_of_exact_posterior(orc):
+    """Kalman Delta Networks, abstract (the isotropic variant keeps a single
+    uncertainty scalar per head): from the prior p I one exact step (FULL
+    branch, pinned above) gives the posterior mean and a dense posterior
+    precision (1/p-) I + k k^T / r. The KL(q||p) projection onto covariances
+    c I keeps the mean and sets 1/c to the average diagonal entry of that
+    precision, trace / d_k. The ISO branch must agree for general keys (not
+    unit-norm), decays, noises and process noise."""
+    rng = _rng(31)
+    B, H, dk, dv = 2, 3, 8, 5
+    for trial in range(3):
+        q = rng.standard_normal((B, H, 1, dk)).astype(np.float32)
+        k = rng.standard_normal((B, H, 1, dk)).astype(np.float32)
+        v = rng.standard_normal((B, H, 1, dv)).astype(np.float32)
+        a = rng.uniform(0.5, 1.0, (B, H, 1)).astype(np.float32)
+        r = rng.uniform(0.1, 2.0, (B, H, 1)).astype(np.float32)
+        p0 = rng.uniform(0.2, 3.0, (B, H))
+        S0 = rng.standard_normal((B, H, dk, dv))
+        sig2 = [0.0, 1.0, 0.3][trial]
+        full = orc.scan(q, k, v, alpha=a, r=r, cov0=p0[..., None, None] * np.eye(dk),
+                        q_noise_var=sig2, S0=S0, mode="full")
+        iso = orc.scan(q, k, v, alpha=a, r=r, cov0=p0, q_noise_var=sig2, S0=S0, mode="iso")
+        np.testing.assert_allclose(iso["S"], full["S"], atol=1e-12)
+        np.testing.assert_allclose(iso["o"], full["o"], atol=1e-12)
+        np.testing.assert_allclose(iso["m"], full["m"], rtol=1e-12)
+        prec_mean = np.einsum("bhii->bh", np.linalg.inv(full["cov"])) / dk
+        np.testing.assert_allclose(1.0 / iso["cov"], prec_mean, rtol=1e-11)
+
+
+def test_iso_precision_affine_without_process_noise(orc):
+    """Kalman Delta Networks, abstract (Moebius uncertainty maps): with no
+    process noise the isotropic precision is affine in time,
+    1/p_t = (1/p_0)/G_t^2 + sum_j (G_j/G_t)^2 ||k_j||^2 / (d_k r_j)."""
+    inp = workloads.scan_inputs(2, 2, 50, 8, 4, seed=32, dtype="f32", with_r=True)
+    k = inp["k"] * _rng(32).uniform(0.5, 2.0, (2, 2, 50, 1)).astype(np.float32)
+    p0 = _rng(33).uniform(0.5, 2.0, (2, 2))
+    res = orc.scan(inp["q"], k, inp["v"], alpha=inp["alpha"], r=inp["r"], cov0=p0,
+                   q_noise_var=0.0, mode="iso")
+    G = np.cumprod(inp["alpha"].astype(np.float64), axis=-1)
+    Gt = G[..., -1]
+    kk = np.sum(k.astype(np.float64) ** 2, axis=-1)
+    prec = (1.0 / p0) / Gt ** 2 + np.sum((G / Gt[..., None]) ** 2 * kk / (8 * inp["r"]), axis=-1)
+    np.testing.assert_allclose(1.0 / res["cov"], prec, rtol=1e-11)
+
+
+def test_iso_zero_keys_and_fixed_point(orc):
+    """Kalman Delta Networks, abstract (Moebius maps). k = 0: p_t = sigma^2 +
+    G_t^2 (p_0 - sigma^2) and S_t = G_t S_0. Constant (alpha, ||k||^2, r): with
+    c = ||k||^2 / (d_k r), p converges to the positive root of
+    c a^2 p^2 + (1 + c Q - a^2) p - Q = 0."""
+    rng = _rng(34)
+    L, dk, dv, sig2 = 30, 4, 3, 0.8
+    a = rng.uniform(0.7, 1.0, (1, 1, L)).astype(np.float32)
+    z = np.zeros((1, 1, L, dk), np.float32)
+    v = rng.standard_normal((1, 1, L, dv)).astype(np.float32)
+    S0 = rng.standard_normal((1, 1, dk, dv))
+    p0 = np.array([[3.0]])
+    res = orc.scan(z, z, v, alpha=a, r=np.ones((1, 1, L), np.float32), cov0=p0,
+                   q_noise_var=sig2, S0=S0, mode="iso")
+    G = np.prod(a.astype(np.float64))
+    np.testing.assert_allclose(res["cov"], sig2 + G ** 2 * (p0 - sig2), rtol=1e-12)
+    np.testing.assert_allclose(res["S"][0, 0], G * S0[0, 0], rtol=1e-12)
+
+    L = 4000
+    al, rr = np.float32(0.9), np.float32(0.5)
+    kk = np.full((1, 1, L, dk), np.float32(0.75))
+    res = orc.scan(kk, kk, np.zeros((1, 1, L, 1), np.float32), alpha=np.full((1, 1, L), al),
+                   r=np.full((1, 1, L), rr), cov0=np.ones((1, 1)), q_noise_var=sig2, mode="iso")
+    a2, Q = float(al) ** 2, (1 - float(al) ** 2) * sig2
+    c = dk * 0.75 ** 2 / (dk * float(rr))
+    root = max(np.roots([c * a2, 1 + c * Q - a2, -Q]).real)
+    np.testing.assert_allclose(res["cov"][0, 0], root, rtol=1e-12)
+
+
+def test_iso_equals_diag_for_one_dimensional_keys(orc):
+    """With d_k = 1 a single variance per head and a diagonal covariance are the
+    same family, so the isotropic and the diagonal writes must agree exactly
+    over a whole sequence (any decay, noise and process noise)."""
+    rng = _rng(35)
+    B, H, L, dv = 2, 2, 70, 5
+    q = rng.standard_normal((B, H, L, 1)).astype(np.float32)
+    k = rng.standard_normal((B, H, L, 1)).astype(np.float32)
+    v = rng.standard_normal((B, H, L, dv)).astype(np.float32)
+    a = rng.uniform(0.7, 1.0, (B, H, L)).astype(np.float32)
+    r = rng.uniform(0.2, 2.0, (B, H, L)).astype(np.float32)
+    p0 = rng.uniform(0.5, 2.0, (B, H))
+    for sig2 in (0.0, 1.0):
+        iso = orc.scan(q, k, v, alpha=a, r=r, cov0=p0, q_noise_var=sig2, mode="iso")
+        diag = orc.scan(q, k, v, alpha=a, r=r, cov0=p0[..., None], q_noise_var=sig2, mode="diag")
+        np.testing.assert_allclose(iso["o"], diag["o"], rtol=0, atol=1e-13 * np.abs(diag["o"]).max())
+        np.testing.assert_allclose(iso["cov"], diag["cov"][..., 0], rtol=1e-13)
+        np.testing.assert_allclose(iso["m"], diag["m"], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # Delta write (gated and plain forms)
 # ---------------------------------------------------------------------------
 
