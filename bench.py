@@ -11,7 +11,7 @@ resident in HBM before timing starts.
 Extra fields: the roofline of the dominant (state) kernel, timed on its own
 stream with events around its phase; the fp64 oracle timed on a bounded
 sample on the host cores; and (unless --quick) the decode + HOLA cache step,
-the diagonal Kalman scan and the long-context scan.
+the diagonal and isotropic Kalman scans and the long-context scan.
 """
 from __future__ import annotations
 
@@ -93,8 +93,8 @@ def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True):
     r = torch.from_numpy(inp["r"]).to(dev) if inp["r"] is not None else None
     del inp
     cov_in = cov_out = None
-    if mode == "diag":
-        cov_in = torch.full((B, H, dk), cfg["cov_init"], device=dev)
+    if mode in ("diag", "iso"):
+        cov_in = torch.full((B, H, dk) if mode == "diag" else (B, H), cfg["cov_init"], device=dev)
         cov_out = torch.empty_like(cov_in)
     o = torch.empty((B, H, L, dv), dtype=torch.float32, device=dev)
     s_out = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
@@ -258,7 +258,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(main_res["state_ms"]),
-                     "kernel": "scan_kernel (sequential state scan)",
+                     "kernel": "state_kernel (sequential chunk-state scan)",
                      "kernel_ms": round(main_res["state_ms"], 5),
                      "algorithmic_bytes": nbytes},
         "mfma": {"algorithmic_tflops_per_step": round(flops / 1e12, 3),
@@ -272,11 +272,12 @@ def main():
     if not args.quick:
         extra = {}
         extra["decode"] = bench_decode(kdn, torch, steps=max(8, args.steps), warmup=args.warmup)
-        for name, mode in (("kdn_diag", "diag"), ("long", "delta")):
+        for key, name, mode in (("kdn_diag", "kdn_diag", "diag"), ("kdn_iso", "kdn_diag", "iso"),
+                                ("long", "long", "delta")):
             r = bench_scan(kdn, torch, name, max(2, args.steps // 4), 1, mode=mode, per_phase=True)
             nb = scan_bytes(r["B"], r["H"], r["L"], r["dk"], r["dv"],
-                            extra_per_token=4 if mode == "diag" else 0)
-            extra[name] = dict(ms_per_step=round(r["ms_per_step"], 5),
+                            extra_per_token=4 if mode in ("diag", "iso") else 0)
+            extra[key] = dict(ms_per_step=round(r["ms_per_step"], 5),
                                tokens_per_s=round(r["tokens_per_s"], 1),
                                prepare_ms=round(r["prepare_ms"], 5),
                                state_ms=round(r["state_ms"], 5),

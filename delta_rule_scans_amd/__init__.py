@@ -27,7 +27,7 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdn.so")
 
 F32, BF16 = 0, 1
-MODES = {"delta": 0, "diag": 1, "full": 2}
+MODES = {"delta": 0, "diag": 1, "full": 2, "iso": 3}
 RESIDS = {"gated": 0, "plain": 1}
 PHASES = {"all": 0, "prepare": 1, "state": 2}
 
@@ -128,8 +128,8 @@ def kdn_scan_fwd(q, k, v, alpha=None, beta=None, r=None, cov_in=None, cov_out=No
                  chunk: int = 64, mode: str = "delta", resid: str = "gated", workspace=None,
                  stream=None, phase: str = "all"):
     """Chunkwise scan. q, k: [B,H,L,d_k]; v: [B,H,L,d_v] (bf16 or float32, same dtype);
-    alpha/beta/r: [B,H,L] float32; cov_in/cov_out: [B,H,d_k] (diag) or [B,H,d_k,d_k]
-    (full) float32; state_in/state_out: [B,H,d_k,d_v] float32. Returns o [B,H,L,d_v]
+    alpha/beta/r: [B,H,L] float32; cov_in/cov_out: [B,H,d_k] (diag), [B,H,d_k,d_k]
+    (full) or [B,H] (iso) float32; state_in/state_out: [B,H,d_k,d_v] float32. Returns o [B,H,L,d_v]
     (float32 unless ``out_dtype`` or ``o`` says otherwise). ``phase`` "prepare" /
     "state" runs one half of the call (kdn_scan_fwd_phase); both halves must see
     the same ``workspace`` tensor."""
@@ -142,7 +142,7 @@ def kdn_scan_fwd(q, k, v, alpha=None, beta=None, r=None, cov_in=None, cov_out=No
     _check(v, "v", q.dtype, (B, H, L, dv), dev)
     for name, t in (("alpha", alpha), ("beta", beta), ("r", r)):
         _check(t, name, torch.float32, (B, H, L), dev)
-    cshape = (B, H, dk) if mode == "diag" else (B, H, dk, dk)
+    cshape = {"diag": (B, H, dk), "iso": (B, H)}.get(mode, (B, H, dk, dk))
     _check(cov_in, "cov_in", torch.float32, cshape, dev)
     _check(cov_out, "cov_out", torch.float32, cshape, dev)
     _check(state_in, "state_in", torch.float32, (B, H, dk, dv), dev)
@@ -174,7 +174,7 @@ def kdn_step_decode(q, k, v, alpha, beta, state, o=None, m=None, r=None, cov=Non
                     q_noise_var: float = 0.0, mode: str = "delta", resid: str = "gated",
                     stream=None):
     """One token per head. q, k: [B,H,d_k]; v: [B,H,d_v]; alpha, beta, r: [B,H];
-    state [B,H,d_k,d_v] and cov [B,H,d_k] (diag) are updated in place.
+    state [B,H,d_k,d_v] and cov [B,H,d_k] (diag) or [B,H] (iso) are updated in place.
     Returns (o [B,H,d_v], m [B,H])."""
     torch = _torch()
     B, H, dk = q.shape
@@ -187,7 +187,7 @@ def kdn_step_decode(q, k, v, alpha, beta, state, o=None, m=None, r=None, cov=Non
     _check(alpha, "alpha", f, (B, H), dev)
     _check(beta, "beta", f, (B, H), dev)
     _check(r, "r", f, (B, H), dev)
-    _check(cov, "cov", f, (B, H, dk), dev)
+    _check(cov, "cov", f, (B, H) if mode == "iso" else (B, H, dk), dev)
     _check(state, "state", f, (B, H, dk, dv), dev)
     if o is None:
         o = torch.empty((B, H, dv), dtype=f, device=dev)

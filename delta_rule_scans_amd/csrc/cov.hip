@@ -159,6 +159,89 @@ __global__ __launch_bounds__(256) void full_gains_kernel(const Tk* k, const floa
   }
 }
 
+// ---------------------------------------------------------------- isotropic
+// One variance p per head ("Kalman Delta Networks", abstract: the isotropic
+// variant): p- = alpha^2 p + Q, gain p- k / (p- ||k||^2 + r) = beta_t k with
+// beta_t = p- / (p- ||k||^2 + r), and the precision projected onto multiples
+// of the identity, 1/p = 1/p- + ||k||^2 / (d_k r). The write is then the delta
+// write with that beta. In p, one token is the Moebius map
+// p -> (a^2 p + Q) / (c a^2 p + c Q + 1) with c = ||k||^2 / (d_k r).
+
+// Per (head, chunk): ||k_t||^2 of the chunk's tokens (16 lanes per token) and
+// the composition of the chunk's token maps.
+template <typename Tk>
+__global__ __launch_bounds__(256) void iso_maps_kernel(const Tk* k, const float* alpha,
+                                                       const float* r, float qvar, float* kk,
+                                                       float4* maps, int L, int dk, int C,
+                                                       int nchunks) {
+  __shared__ float s_kk[128];
+  const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int grp = tid >> 4, j = tid & 15;
+  const int t0 = c * C, n = min(C, L - t0);
+  const size_t tok = (size_t)bh * L + t0;
+  for (int t = grp; t < n; t += 16) {
+    float acc = 0.f;
+    for (int i = j; i < dk; i += 16) {
+      const float x = Elem<Tk>::load(k, (tok + t) * dk + i);
+      acc = fmaf(x, x, acc);
+    }
+    acc += __shfl_xor(acc, 8, 16);
+    acc += __shfl_xor(acc, 4, 16);
+    acc += __shfl_xor(acc, 2, 16);
+    acc += __shfl_xor(acc, 1, 16);
+    if (j == 0) s_kk[t] = acc;
+  }
+  __syncthreads();
+  if (tid < n) kk[tok + tid] = s_kk[tid];
+  if (tid == 0) {
+    float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f;
+    for (int t = 0; t < n; ++t) {
+      const float a = alpha ? alpha[tok + t] : 1.f, rt = r ? r[tok + t] : 1.f;
+      const float a2 = a * a, Q = (1.f - a) * (1.f + a) * qvar;
+      const float cc = s_kk[t] / (dk * rt);
+      const float t00 = a2, t01 = Q, t10 = cc * a2, t11 = fmaf(cc, Q, 1.f);
+      const float n00 = fmaf(t00, m00, t01 * m10), n01 = fmaf(t00, m01, t01 * m11);
+      const float n10 = fmaf(t10, m00, t11 * m10), n11 = fmaf(t10, m01, t11 * m11);
+      const float sc = 1.f / fmaxf(fmaxf(n00, n01), fmaxf(n10, n11));
+      m00 = n00 * sc;
+      m01 = n01 * sc;
+      m10 = n10 * sc;
+      m11 = n11 * sc;
+    }
+    maps[(size_t)bh * nchunks + c] = make_float4(m00, m01, m10, m11);
+  }
+}
+
+// Per (head, chunk): p at the chunk start from the maps of the chunks before
+// it, then the chunk's tokens in order: the write strengths beta_t and p.
+__global__ __launch_bounds__(64) void iso_beta_kernel(const float* alpha, const float* r,
+                                                      const float* kk, const float* cov_in,
+                                                      float* cov_out, float qvar,
+                                                      const float4* maps, float* beta, int L,
+                                                      int dk, int C, int nchunks) {
+  __shared__ float s_b[128];
+  const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+  const int t0 = c * C, n = min(C, L - t0);
+  const size_t tok = (size_t)bh * L + t0;
+  if (tid == 0) {
+    float p = cov_in[bh];
+    for (int cc = 0; cc < c; ++cc) {
+      const float4 M = maps[(size_t)bh * nchunks + cc];
+      p = fmaf(M.x, p, M.y) / fmaf(M.z, p, M.w);
+    }
+    for (int t = 0; t < n; ++t) {
+      const float a = alpha ? alpha[tok + t] : 1.f, rt = r ? r[tok + t] : 1.f;
+      const float pm = fmaf(a * a, p, (1.f - a) * (1.f + a) * qvar);
+      const float kt = kk[tok + t];
+      s_b[t] = pm / fmaf(pm, kt, rt);
+      p = pm * (dk * rt) / fmaf(pm, kt, dk * rt);
+    }
+    if (c == nchunks - 1 && cov_out) cov_out[bh] = p;
+  }
+  __syncthreads();
+  for (int t = tid; t < n; t += 64) beta[tok + t] = s_b[t];
+}
+
 template <typename Tk, typename Tg>
 hipError_t diag_typed(const void* k, const float* alpha, const float* r, const float* cov_in,
                       float* cov_out, float qvar, void* gains, float* maps, int BH, int L, int dk,
@@ -205,6 +288,27 @@ hipError_t launch_diag_gains(const void* k, bool k_bf16, const float* alpha, con
                                                   maps, BH, L, dk, chunk, s)
                     : diag_typed<float, float>(k, alpha, r, cov_in, cov_out, q_noise_var, gains,
                                                maps, BH, L, dk, chunk, s);
+}
+
+hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const float* r,
+                          const float* cov_in, float* cov_out, float q_noise_var, float* beta,
+                          float* kk, float* maps, int BH, int L, int dk, int chunk,
+                          hipStream_t s) {
+  const int nchunks = (L + chunk - 1) / chunk;
+  if (k_bf16)
+    hipLaunchKernelGGL(iso_maps_kernel<uint16_t>, dim3(BH, nchunks), dim3(256), 0, s,
+                       static_cast<const uint16_t*>(k), alpha, r, q_noise_var, kk,
+                       reinterpret_cast<float4*>(maps), L, dk, chunk, nchunks);
+  else
+    hipLaunchKernelGGL(iso_maps_kernel<float>, dim3(BH, nchunks), dim3(256), 0, s,
+                       static_cast<const float*>(k), alpha, r, q_noise_var, kk,
+                       reinterpret_cast<float4*>(maps), L, dk, chunk, nchunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(iso_beta_kernel, dim3(BH, nchunks), dim3(64), 0, s, alpha, r, kk, cov_in,
+                     cov_out, q_noise_var, reinterpret_cast<const float4*>(maps), beta, L, dk,
+                     chunk, nchunks);
+  return hipGetLastError();
 }
 
 hipError_t launch_full_gains(const void* k, bool k_bf16, const float* alpha, const float* r,

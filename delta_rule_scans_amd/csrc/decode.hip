@@ -3,9 +3,11 @@
 // "A Hippocampus for Linear Attention", sec. 3.3 eqs. (5)-(6) and sec. 3.5:
 //   e = v - alpha S^T k,  S <- alpha S + b e^T,  o = S^T q (after the write),
 //   m = ||b e^T||_F  (= beta ||e|| for the delta write with unit keys).
-// b = beta k (delta) or the diagonal Kalman gain ("Kalman Delta Networks",
-// abstract). The read-out is computed in the same pass over S as
-// o = alpha S_old^T q + (b . q) e, so S is read once and written once.
+// b = beta k (delta), the diagonal Kalman gain or the isotropic one ("Kalman
+// Delta Networks", abstract; the isotropic gain is p- k / (p- ||k||^2 + r) with
+// one variance per head, 1/p = 1/p- + ||k||^2 / (d_k r)). The read-out is
+// computed in the same pass over S as o = alpha S_old^T q + (b . q) e, so S is
+// read once and written once.
 //
 // One workgroup (256 lanes) per head. Lane (rg, cg): column group cg (4
 // columns), rows rg, rg + 8, ... The state row is read with 16-byte loads, so a
@@ -42,16 +44,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
                                                     float* __restrict__ cov, float qvar,
                                                     float* __restrict__ state,
                                                     float* __restrict__ o, float* __restrict__ m,
-                                                    int dk, int dv, int diag, int plain) {
+                                                    int dk, int dv, int gmode, int plain) {
   __shared__ float sk[128], sq[128], sv[128], sb[128], se[128];
   __shared__ float red1[8][128], red2[8][128];
   __shared__ float scratch[4];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int cg = tid & 31, rg = tid >> 5;
 
+  const bool diag = gmode == 1, iso = gmode == 2;
   const float a = alpha ? alpha[bh] : 1.f;
   float bscale = 1.f, vscale = 1.f;
-  if (!diag) {
+  if (gmode == 0) {
     bscale = beta[bh];
     if (plain) {  // plain residual = gated form with (beta / alpha, alpha v)
       bscale /= a;
@@ -78,6 +81,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
       sb[tid] = pm * kv / s;
       cov[(size_t)bh * dk + tid] = pm * rt / fmaf(pm * kv, kv, rt);
     }
+  } else if (iso) {
+    const float rt = r ? r[bh] : 1.f;
+    const float pm = fmaf(a * a, cov[bh], (1.f - a) * (1.f + a) * qvar);
+    const float kv = tid < dk ? sk[tid] : 0.f;
+    const float kk = block_sum(kv * kv, scratch);
+    bscale = pm / fmaf(pm, kk, rt);
+    if (tid < dk) sb[tid] = bscale * kv;
+    if (tid == 0) cov[bh] = pm * (dk * rt) / fmaf(pm, kk, dk * rt);
   } else if (tid < dk) {
     sb[tid] = bscale * sk[tid];
   }
@@ -139,9 +150,9 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
   }
   const float bq = block_sum(tid < dk ? sb[tid] * sq[tid] : 0.f, scratch);
   const float ee = block_sum(e * e, scratch);
-  const float bb = diag ? block_sum(tid < dk ? sb[tid] * sb[tid] : 0.f, scratch) : 0.f;
+  const float bb = gmode ? block_sum(tid < dk ? sb[tid] * sb[tid] : 0.f, scratch) : 0.f;
   if (tid < dv) o[(size_t)bh * dv + tid] = fmaf(bq, e, oq);
-  if (m && tid == 0) m[bh] = diag ? sqrtf(bb) * sqrtf(ee) : bscale * sqrtf(ee);
+  if (m && tid == 0) m[bh] = gmode ? sqrtf(bb) * sqrtf(ee) : bscale * sqrtf(ee);
 
   // S <- alpha S + b e^T
 #pragma unroll
@@ -173,15 +184,15 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
 
 hipError_t launch_decode(const float* q, const float* k, const float* v, const float* alpha,
                          const float* beta, const float* r, float* cov, float q_noise_var,
-                         float* state, float* o, float* m, int BH, int dk, int dv, int diag,
+                         float* state, float* o, float* m, int BH, int dk, int dv, int gmode,
                          int plain, hipStream_t s) {
   const bool vec = (dv % 4 == 0) && ((reinterpret_cast<uintptr_t>(state) & 15) == 0);
   if (vec)
     hipLaunchKernelGGL(decode_kernel<true>, dim3(BH), dim3(NT), 0, s, q, k, v, alpha, beta, r, cov,
-                       q_noise_var, state, o, m, dk, dv, diag, plain);
+                       q_noise_var, state, o, m, dk, dv, gmode, plain);
   else
     hipLaunchKernelGGL(decode_kernel<false>, dim3(BH), dim3(NT), 0, s, q, k, v, alpha, beta, r,
-                       cov, q_noise_var, state, o, m, dk, dv, diag, plain);
+                       cov, q_noise_var, state, o, m, dk, dv, gmode, plain);
   return hipGetLastError();
 }
 

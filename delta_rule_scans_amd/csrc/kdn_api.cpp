@@ -26,7 +26,8 @@ bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace layout, 256-byte aligned parts:
-//   [maps (DIAG) | gains (Kalman modes) | per-chunk (I + A)^-1 (matrix-core path)].
+//   [maps (DIAG, ISO) | gains (DIAG, FULL) or write strengths and key norms (ISO)
+//    | per-chunk records of the matrix-core path].
 // Gains are fp16 for bf16 inputs and float32 otherwise.
 struct WsLayout {
   size_t maps_off, maps_bytes, gains_off, gains_bytes, t_off, t_bytes, total;
@@ -42,8 +43,12 @@ WsLayout ws_layout(int B, int H, int L, int dk, int dv, int chunk, int mode, int
   const size_t BH = (size_t)B * H;
   const size_t nchunks = ((size_t)L + chunk - 1) / chunk;
   if (mode == KDN_GAIN_DIAG) w.maps_bytes = BH * nchunks * dk * 4 * sizeof(float);
-  if (mode != KDN_GAIN_DELTA) w.gains_bytes = BH * (size_t)L * dk * (in_dtype == KDN_BF16 ? 2 : 4);
-  if (use_mfma_path(in_dtype, dk, dv, chunk)) w.t_bytes = kdn::scan_mfma_workspace_bytes((int)BH, L, mode != KDN_GAIN_DELTA);
+  if (mode == KDN_GAIN_ISO) w.maps_bytes = BH * nchunks * 4 * sizeof(float);
+  if (mode == KDN_GAIN_DIAG || mode == KDN_GAIN_FULL)
+    w.gains_bytes = BH * (size_t)L * dk * (in_dtype == KDN_BF16 ? 2 : 4);
+  if (mode == KDN_GAIN_ISO) w.gains_bytes = 2 * BH * (size_t)L * sizeof(float);
+  const bool gain = mode == KDN_GAIN_DIAG || mode == KDN_GAIN_FULL;
+  if (use_mfma_path(in_dtype, dk, dv, chunk)) w.t_bytes = kdn::scan_mfma_workspace_bytes((int)BH, L, gain);
   w.maps_off = 0;
   w.gains_off = round_up(w.maps_bytes, 256);
   w.t_off = w.gains_off + round_up(w.gains_bytes, 256);
@@ -93,7 +98,8 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   const bool do_prep = phase != KDN_PHASE_STATE, do_state = phase != KDN_PHASE_PREPARE;
   if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_ERR_BAD_DTYPE;
   if (out_dtype != KDN_F32 && out_dtype != KDN_BF16) return KDN_ERR_BAD_DTYPE;
-  if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_FULL)
+  if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_FULL &&
+      mode != KDN_GAIN_ISO)
     return KDN_ERR_BAD_MODE;
   if (resid != KDN_RESID_GATED && resid != KDN_RESID_PLAIN) return KDN_ERR_BAD_MODE;
   if (resid == KDN_RESID_PLAIN && mode != KDN_GAIN_DELTA) return KDN_ERR_BAD_MODE;
@@ -120,6 +126,7 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   const int BH = B * H;
   const size_t cov_elems = mode == KDN_GAIN_DIAG   ? (size_t)BH * d_k
                            : mode == KDN_GAIN_FULL ? (size_t)BH * d_k * d_k
+                           : mode == KDN_GAIN_ISO  ? (size_t)BH
                                                    : 0;
   if (L == 0) {
     hipError_t e = hipSuccess;
@@ -131,13 +138,25 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   }
 
   const bool in_bf16 = in_dtype == KDN_BF16;
+  const bool has_gain = mode == KDN_GAIN_DIAG || mode == KDN_GAIN_FULL;
   const void* gains = nullptr;
-  if (mode != KDN_GAIN_DELTA) {
+  if (has_gain) {
     char* base = static_cast<char*>(workspace);
     void* g = base + ws.gains_off;
     gains = g;
   }
-  if (do_prep && mode != KDN_GAIN_DELTA) {
+  // the isotropic write runs as the delta write with the beta it computes here
+  float* iso_beta = mode == KDN_GAIN_ISO
+                        ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.gains_off)
+                        : nullptr;
+  if (do_prep && mode == KDN_GAIN_ISO) {
+    char* base = static_cast<char*>(workspace);
+    const hipError_t e = kdn::launch_iso_beta(
+        k, in_bf16, alpha, r, cov_in, cov_out, q_noise_var, iso_beta, iso_beta + (size_t)BH * L,
+        reinterpret_cast<float*>(base + ws.maps_off), BH, L, d_k, chunk, s);
+    if (e != hipSuccess) return map_hip(e);
+  }
+  if (do_prep && has_gain) {
     char* base = static_cast<char*>(workspace);
     void* g = base + ws.gains_off;
     hipError_t e;
@@ -156,7 +175,7 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   a.k = k;
   a.v = v;
   a.alpha = alpha;
-  a.beta = mode == KDN_GAIN_DELTA ? beta : nullptr;
+  a.beta = mode == KDN_GAIN_DELTA ? beta : iso_beta;
   a.gain = gains;
   a.state_in = state_in;
   a.state_out = state_out;
@@ -197,7 +216,8 @@ KDN_EXPORT int kdn_step_decode(const float* q, const float* k, const float* v, c
                                const float* beta, const float* r, float* cov, float q_noise_var,
                                float* state, float* o, float* m, int B, int H, int d_k, int d_v,
                                int mode, int resid, void* stream) {
-  if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_FULL)
+  if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_FULL &&
+      mode != KDN_GAIN_ISO)
     return KDN_ERR_BAD_MODE;
   if (resid != KDN_RESID_GATED && resid != KDN_RESID_PLAIN) return KDN_ERR_BAD_MODE;
   if (resid == KDN_RESID_PLAIN && mode != KDN_GAIN_DELTA) return KDN_ERR_BAD_MODE;
@@ -208,9 +228,13 @@ KDN_EXPORT int kdn_step_decode(const float* q, const float* k, const float* v, c
   if (!std::isfinite(q_noise_var) || q_noise_var < 0.f) return KDN_ERR_BAD_SHAPE;
   if (!q || !k || !v || !state || !o) return KDN_ERR_NULL_POINTER;
   if (mode == KDN_GAIN_DELTA && beta == nullptr) return KDN_ERR_NULL_POINTER;
-  if (mode == KDN_GAIN_DIAG && cov == nullptr) return KDN_ERR_NULL_POINTER;
+  if ((mode == KDN_GAIN_DIAG || mode == KDN_GAIN_ISO) && cov == nullptr)
+    return KDN_ERR_NULL_POINTER;
   return map_hip(kdn::launch_decode(q, k, v, alpha, beta, r, cov, q_noise_var, state, o, m, B * H,
-                                    d_k, d_v, mode == KDN_GAIN_DIAG ? 1 : 0,
+                                    d_k, d_v,
+                                    mode == KDN_GAIN_DIAG  ? 1
+                                    : mode == KDN_GAIN_ISO ? 2
+                                                           : 0,
                                     resid == KDN_RESID_PLAIN ? 1 : 0,
                                     static_cast<hipStream_t>(stream)));
 }

@@ -81,6 +81,14 @@ hipError_t launch_diag_gains(const void* k, bool k_bf16, const float* alpha, con
                              void* gains, bool gains_f16, float* maps, int BH, int L, int dk,
                              int chunk, hipStream_t s);
 
+// Isotropic Kalman write: the per-token write strengths beta [BH, L] (the gain
+// is beta_t k_t) and the final variance [BH]. `kk` is scratch of BH * L floats,
+// `maps` of BH * nchunks * 4 floats (16-byte aligned). chunk <= 128.
+hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const float* r,
+                          const float* cov_in, float* cov_out, float q_noise_var, float* beta,
+                          float* kk, float* maps, int BH, int L, int dk, int chunk,
+                          hipStream_t s);
+
 // Full-covariance Kalman gains (dk <= 64): gains [BH, L, dk] and the final covariance.
 hipError_t launch_full_gains(const void* k, bool k_bf16, const float* alpha, const float* r,
                              const float* cov_in, float* cov_out, float q_noise_var,
@@ -89,10 +97,10 @@ hipError_t launch_full_gains(const void* k, bool k_bf16, const float* alpha, con
 // Copy the covariance / state through unchanged (L == 0).
 hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s);
 
-// One decode token per head.
+// One decode token per head; gmode 0 = delta, 1 = diagonal, 2 = isotropic gain.
 hipError_t launch_decode(const float* q, const float* k, const float* v, const float* alpha,
                          const float* beta, const float* r, float* cov, float q_noise_var,
-                         float* state, float* o, float* m, int BH, int dk, int dv, int diag,
+                         float* state, float* o, float* m, int BH, int dk, int dv, int gmode,
                          int plain, hipStream_t s);
 
 // HOLA cache read + insert for one decode token per head.

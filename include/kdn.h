@@ -19,7 +19,10 @@
  *   FULL keeps the whole d_k x d_k covariance (the recursive-least-squares
  *   update of "DeltaNet-PC", eq. (7), when alpha = 1, r = 1, sigma^2 = 0);
  *   DIAG keeps a diagonal covariance, projected after every token by
- *   mean-field inference: 1/p_i = 1/p-_i + k_i^2 / r_t.
+ *   mean-field inference: 1/p_i = 1/p-_i + k_i^2 / r_t. ISO keeps one variance
+ *   p per head (the covariance is p I), projected onto multiples of the
+ *   identity: 1/p = 1/p- + ||k_t||^2 / (d_k r_t); its gain is beta_t k_t with
+ *   beta_t = p- / (p- ||k_t||^2 + r_t).
  *   score ("A Hippocampus for Linear Attention", sec. 3.3 eq. (6)):
  *       m_t = ||write_t||_F = beta_t ||e_t|| (delta), ||g_t|| ||e_t|| (Kalman).
  *
@@ -27,8 +30,8 @@
  *  - Every array argument is a DEVICE pointer owned by the caller; the library
  *    keeps no pointer after the call returns. Layouts are row-major and
  *    contiguous: sequences [B, H, L, d], per-token scalars [B, H, L], state
- *    [B, H, d_k, d_v] (S[i][j] at i*d_v + j), covariance [B, H, d_k] (DIAG) or
- *    [B, H, d_k, d_k] (FULL).
+ *    [B, H, d_k, d_v] (S[i][j] at i*d_v + j), covariance [B, H, d_k] (DIAG),
+ *    [B, H, d_k, d_k] (FULL) or [B, H] (ISO).
  *  - `stream` is a hipStream_t (NULL = the legacy default stream). Work is only
  *    enqueued; the call never synchronises. The library never allocates device
  *    memory: scratch space comes from the caller's `workspace`.
@@ -56,6 +59,7 @@ extern "C" {
 #define KDN_GAIN_DELTA 0 /* b_t = beta_t k_t                                   */
 #define KDN_GAIN_DIAG 1  /* diagonal-covariance Kalman gain, cov [B,H,d_k]       */
 #define KDN_GAIN_FULL 2  /* full-covariance Kalman gain, cov [B,H,d_k,d_k], d_k <= 64 */
+#define KDN_GAIN_ISO 3   /* isotropic Kalman gain: one variance per head, cov [B,H]   */
 
 /* residual forms (delta mode only; the Kalman modes always use the gated form) */
 #define KDN_RESID_GATED 0 /* e = v - alpha S^T k */
@@ -102,9 +106,9 @@ size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
  *            otherwise (the Kalman gain replaces it).
  *  r         [B,H,L] float32 observation-noise variance > 0 (Kalman modes);
  *            NULL means r = 1. Ignored in DELTA mode.
- *  cov_in    prior covariance: [B,H,d_k] (DIAG, entries > 0) or
- *            [B,H,d_k,d_k] (FULL, symmetric positive definite). Required in
- *            the Kalman modes, ignored in DELTA mode.
+ *  cov_in    prior covariance: [B,H,d_k] (DIAG, entries > 0),
+ *            [B,H,d_k,d_k] (FULL, symmetric positive definite) or [B,H] (ISO,
+ *            > 0). Required in the Kalman modes, ignored in DELTA mode.
  *  cov_out   final covariance, same shape as cov_in; NULL = not written. May
  *            alias cov_in.
  *  q_noise_var  sigma^2 of the process noise Q_t = (1 - alpha_t^2) sigma^2 (>= 0).
@@ -166,12 +170,12 @@ int kdn_scan_fwd_phase(int phase, const void *q, const void *k, const void *v, i
  *
  *  q, k      [B,H,d_k] float32;  v [B,H,d_v] float32.
  *  alpha     [B,H] float32 (NULL = 1);  beta [B,H] float32 (DELTA mode).
- *  r         [B,H] float32 (DIAG mode, NULL = 1).
- *  cov       [B,H,d_k] float32, in/out (DIAG mode only, else ignored).
+ *  r         [B,H] float32 (DIAG and ISO modes, NULL = 1).
+ *  cov       [B,H,d_k] (DIAG) or [B,H] (ISO) float32, in/out; ignored in DELTA mode.
  *  state     [B,H,d_k,d_v] float32, in/out.
  *  o         [B,H,d_v] float32 out: S_t^T q_t after the write.
  *  m         [B,H] float32 out: the write score; NULL = not written.
- * Sizes: B, H >= 1; 1 <= d_k, d_v <= 128. Modes DELTA and DIAG.
+ * Sizes: B, H >= 1; 1 <= d_k, d_v <= 128. Modes DELTA, DIAG and ISO (cov [B,H]).
  */
 int kdn_step_decode(const float *q, const float *k, const float *v,
                     const float *alpha, const float *beta, const float *r,

@@ -57,8 +57,8 @@ def test_status_strings_and_constants(kdn):
         assert s and s != "unknown status"
     assert kdn.kdn_status_string(0) == "ok"
     assert kdn.lib.kdn_version() >= 100
-    assert (c["KDN_GAIN_DELTA"], c["KDN_GAIN_DIAG"], c["KDN_GAIN_FULL"]) == (0, 1, 2)
-    assert (kdn.MODES["delta"], kdn.MODES["diag"], kdn.MODES["full"]) == (0, 1, 2)
+    assert (c["KDN_GAIN_DELTA"], c["KDN_GAIN_DIAG"], c["KDN_GAIN_FULL"], c["KDN_GAIN_ISO"]) == (0, 1, 2, 3)
+    assert [kdn.MODES[m] for m in ("delta", "diag", "full", "iso")] == [0, 1, 2, 3]
 
 
 def test_workspace_size(kdn):
@@ -72,6 +72,9 @@ def test_workspace_size(kdn):
     gains = 4 * 16 * 4096 * 128 * 2
     maps = 4 * 16 * 64 * 128 * 16
     assert ws >= gains + maps + tinv
+    # isotropic write: per-token write strengths and key norms, one map per chunk
+    iso = kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 64, "iso", kdn.BF16)
+    assert iso == 4 * 16 * 64 * 16 + 2 * 4 * 16 * 4096 * 4 + tinv
     assert kdn.kdn_scan_workspace_size(1, 1, 64, 16, 16, 16, "full", kdn.F32) >= 64 * 16 * 4
     assert kdn.kdn_scan_workspace_size(1, 1, 64, 16, 16, 17, "full", kdn.F32) == 0
 
@@ -101,7 +104,10 @@ def test_scan_rejections(kdn):
     assert _scan(kdn, mode=1) == c["KDN_ERR_NULL_POINTER"]            # DIAG without cov_in
     assert _scan(kdn, in_dtype=7) == c["KDN_ERR_BAD_DTYPE"]
     assert _scan(kdn, out_dtype=-1) == c["KDN_ERR_BAD_DTYPE"]
-    assert _scan(kdn, mode=3) == c["KDN_ERR_BAD_MODE"]
+    assert _scan(kdn, mode=3) == c["KDN_ERR_NULL_POINTER"]            # ISO without cov_in
+    assert _scan(kdn, mode=4) == c["KDN_ERR_BAD_MODE"]
+    assert _scan(kdn, mode=3, resid=1, cov_in=P) == c["KDN_ERR_BAD_MODE"]
+    assert _scan(kdn, mode=3, cov_in=P) == c["KDN_ERR_WORKSPACE"]
     assert _scan(kdn, resid=2) == c["KDN_ERR_BAD_MODE"]
     assert _scan(kdn, mode=1, resid=1, cov_in=P) == c["KDN_ERR_BAD_MODE"]
     for bad in (dict(B=0), dict(H=-1), dict(L=-1), dict(dk=0), dict(dv=129), dict(dk=256)):
@@ -135,6 +141,8 @@ def test_decode_rejections(kdn):
     assert _decode(kdn, beta=None) == c["KDN_ERR_NULL_POINTER"]
     assert _decode(kdn, mode=1) == c["KDN_ERR_NULL_POINTER"]
     assert _decode(kdn, mode=2) == c["KDN_ERR_UNSUPPORTED"]
+    assert _decode(kdn, mode=3) == c["KDN_ERR_NULL_POINTER"]
+    assert _decode(kdn, mode=3, resid=1, cov=P) == c["KDN_ERR_BAD_MODE"]
     assert _decode(kdn, mode=5) == c["KDN_ERR_BAD_MODE"]
     assert _decode(kdn, mode=1, resid=1, cov=P) == c["KDN_ERR_BAD_MODE"]
     assert _decode(kdn, dk=0) == c["KDN_ERR_BAD_SHAPE"]

@@ -48,9 +48,11 @@ def _membership(hist, w):
 def _run_decode(kdn, orc, B, H, dk, dv, w, steps, seed, mode="delta", resid="gated",
                 sink=False, qvar=0.0, sample=None):
     import torch
-    inputs = _steps(steps, B, H, dk, dv, seed, diag=(mode == "diag"))
+    kalman = mode in ("diag", "iso")
+    inputs = _steps(steps, B, H, dk, dv, seed, diag=kalman)
     state = torch.zeros((B, H, dk, dv), device="cuda")
-    cov = torch.ones((B, H, dk), device="cuda") if mode == "diag" else None
+    cshape = {"diag": (B, H, dk), "iso": (B, H)}.get(mode)
+    cov = torch.ones(cshape, device="cuda") if kalman else None
     cache = kdn.HolaCache(B, H, dk, dv, w)
     rng = np.random.Generator(np.random.PCG64([seed, 99]))
     sink_np = rng.standard_normal(H).astype(np.float32) if sink else None
@@ -70,10 +72,11 @@ def _run_decode(kdn, orc, B, H, dk, dv, w, steps, seed, mode="delta", resid="gat
     torch.cuda.synchronize()
     # oracle on the sampled heads only (B' = 1, H' = len(sample))
     sub_inputs = [{n: x[bs, hs][None] for n, x in inp.items()} for inp in inputs]
-    r_steps = [s["r"] for s in sub_inputs] if mode == "diag" else None
+    r_steps = [s["r"] for s in sub_inputs] if kalman else None
     o_ref, oc_ref, m_ref, S_ref, cov_ref, ocache = orc.decode_run(
         sub_inputs, 1, len(sel), dk, dv, w, mode=mode, resid=resid,
-        cov0=np.ones((1, len(sel), dk)) if mode == "diag" else None, r_steps=r_steps,
+        cov0=np.ones((1, len(sel)) + ((dk,) if mode == "diag" else ())) if kalman else None,
+        r_steps=r_steps,
         q_noise_var=qvar, sink_logit=None if sink_np is None else sink_np[hs],
         rms_eps=1e-6)
     got = dict(o=np.stack(outs), oc=np.stack(couts), m=np.stack(ms), S=host(state)[bs, hs],
@@ -117,11 +120,11 @@ def _compare(got, ref, w, what):
 
 
 @pytest.mark.parametrize("mode,resid,sink", [("delta", "gated", False), ("delta", "plain", True),
-                                             ("diag", "gated", False)])
+                                             ("diag", "gated", False), ("iso", "gated", True)])
 def test_decode_hola_small(kdn, orc, mode, resid, sink):
     log(f"decode {mode} {resid} sink={sink}")
     got, ref = _run_decode(kdn, orc, 3, 4, 128, 128, 16, 60, seed=201, mode=mode, resid=resid,
-                           sink=sink, qvar=1.0 if mode == "diag" else 0.0)
+                           sink=sink, qvar=1.0 if mode in ("diag", "iso") else 0.0)
     _compare(got, ref, 16, f"decode {mode}/{resid}")
 
 

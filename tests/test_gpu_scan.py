@@ -175,6 +175,26 @@ def test_diag_kalman_small(kdn, orc, dtype):
         assert_close(got["cov"], ref["cov"], TOL_F32, "diag p")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_iso_kalman_small(kdn, orc, dtype):
+    """Isotropic Kalman write (one variance per head), keys of varying norm."""
+    inp = workloads.scan_inputs(2, 2, 260, 128, 128, seed=109, dtype=dtype, with_r=True)
+    scale = np.random.Generator(np.random.PCG64(109)).uniform(0.5, 1.5, (2, 2, 260, 1))
+    inp["k"] = inp["k"] * scale.astype(np.float32)
+    if dtype == "bf16":
+        inp["k"] = workloads.bf16_round(inp["k"])
+    p0 = np.array([[0.5, 1.0], [2.0, 1.0]], np.float32)
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"], cov0=p0,
+                   q_noise_var=1.0, mode="iso")
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    for chunk in (16, 64):
+        log(f"iso {dtype} chunk {chunk}")
+        got = _scan_gpu(kdn, inp, dtype, chunk, mode="iso", cov0=p0, qvar=1.0)
+        assert_close(got["o"], ref["o"], tol, "iso o")
+        assert_close(got["S"], ref["S"], tol, "iso S")
+        assert_close(got["cov"], ref["cov"], TOL_F32, "iso p")
+
+
 def test_full_kalman_small(kdn, orc):
     inp = workloads.scan_inputs(1, 2, 150, 32, 48, seed=108, dtype="f32", with_r=True)
     rng = np.random.Generator(np.random.PCG64(108))
@@ -194,8 +214,8 @@ def _sampled_check(kdn, orc, name, heads, mode="delta", check_state=True):
     cfg = workloads.WORKLOADS[name]
     inp = workloads.named_scan_inputs(name)
     log(f"{name}: full-size GPU run")
-    cov0 = np.full((cfg["B"], cfg["H"], cfg["dk"]), cfg.get("cov_init", 1.0), np.float32) \
-        if mode == "diag" else None
+    cshape = {"diag": (cfg["B"], cfg["H"], cfg["dk"]), "iso": (cfg["B"], cfg["H"])}.get(mode)
+    cov0 = np.full(cshape, cfg.get("cov_init", 1.0), np.float32) if cshape else None
     got = _scan_gpu(kdn, inp, cfg["dtype"], cfg["chunk"], mode=mode, cov0=cov0,
                     qvar=cfg.get("q_noise_var", 0.0))
     assert np.all(np.isfinite(got["o"]))
@@ -208,7 +228,7 @@ def _sampled_check(kdn, orc, name, heads, mode="delta", check_state=True):
         assert_close(got["o"][b:b + 1, h:h + 1], ref["o"], TOL_BF16, f"{name} o head {(b, h)}")
         if check_state:
             assert_close(got["S"][b:b + 1, h:h + 1], ref["S"], TOL_BF16, f"{name} S head {(b, h)}")
-        if mode == "diag":
+        if cov0 is not None:
             assert_close(got["cov"][b:b + 1, h:h + 1], ref["cov"], TOL_F32, f"{name} p head {(b, h)}")
 
 
@@ -218,6 +238,11 @@ def test_full_size_gated(kdn, orc):
 
 def test_full_size_kdn_diag(kdn, orc):
     _sampled_check(kdn, orc, "kdn_diag", [(0, 3), (2, 9), (3, 15)], mode="diag")
+
+
+def test_full_size_kdn_iso(kdn, orc):
+    """The Kalman workload's inputs with one variance per head instead of a diagonal."""
+    _sampled_check(kdn, orc, "kdn_diag", [(0, 3), (3, 15)], mode="iso")
 
 
 def test_full_size_long(kdn, orc):
