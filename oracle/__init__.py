@@ -57,6 +57,9 @@ def _load():
         lib.oracle_scan.restype = i
         lib.oracle_hola_step.argtypes = [i, i, i, i, i, P, P, P, P, i, P, P, P, P, P, P, d, P]
         lib.oracle_hola_step.restype = i
+        lib.oracle_hola_prefill.argtypes = [i, i, i, i, i, i, i, P, P, P, P, i, P, P, P, P, P, P,
+                                            d, P]
+        lib.oracle_hola_prefill.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
         _lib = lib
@@ -128,6 +131,27 @@ class HolaCache:
                                  _ptr(v), _ptr(m), int(t), _ptr(self.k), _ptr(self.v),
                                  _ptr(self.m), _ptr(self.pos), _ptr(self.count), _ptr(sink),
                                  float(rms_eps), _ptr(o))
+        return o
+
+
+    def prefill(self, q, k, v, m, t0: int, block: int, sink_logit=None, rms_eps: float = 1e-6):
+        """A whole prompt of L tokens (q, k: [B,H,L,dk]; v: [B,H,L,dv]; m: [B,H,L]) in
+        blocks of ``block``: each token reads the cache as it stood before its block
+        plus the block's tokens up to itself (+ sink); then the block is inserted.
+        Returns o_cache [B,H,L,dv] float64; the cache ends sorted by (m desc, pos asc)."""
+        q, k, v = _f32(q), _f32(k), _f32(v)
+        B, H, L, dk = q.shape
+        assert (B, H, dk) == (self.B, self.H, self.dk) and v.shape == (B, H, L, self.dv)
+        m = np.ascontiguousarray(m, dtype=np.float64)
+        assert m.shape == (B, H, L)
+        sink = _f32(sink_logit)
+        o = np.zeros((B, H, L, self.dv))
+        rc = _load().oracle_hola_prefill(B, H, L, dk, self.dv, self.w, int(block), _ptr(q), _ptr(k),
+                                         _ptr(v), _ptr(m), int(t0), _ptr(self.k), _ptr(self.v),
+                                         _ptr(self.m), _ptr(self.pos), _ptr(self.count), _ptr(sink),
+                                         float(rms_eps), _ptr(o))
+        if rc != 0:
+            raise ValueError(f"oracle_hola_prefill rejected the arguments (status {rc})")
         return o
 
 

@@ -348,3 +348,140 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * HOLA exact cache over a whole prompt, block by block [HOLA sec. 3.3 (top-w
+ * cache by write score, order-independent), sec. 3.4 eq. (7) (the visible set:
+ * the cache, the causal tokens of the current block and an optional null sink),
+ * sec. 3.2 eq. (4) (softmax read)].
+ *
+ * The L tokens (positions t0 .. t0 + L - 1) are taken in blocks of `block`.
+ * For token i of block j the visible set is the cache as it stood before block
+ * j, the tokens of block j up to and including i, and the sink. After the
+ * whole block has been read, its tokens are inserted: the cache becomes the
+ * w best of (cache, block) by score descending, then position ascending, on
+ * float32 scores (reading S10). With block = 1 this is the decode step's
+ * read-then-insert. On return slots 0 .. count-1 hold the cache in that order.
+ *
+ *   q, k: [B,H,L,dk] float32; v: [B,H,L,dv] float32; m: [B,H,L] float64.
+ *   cache_*: as oracle_hola_step, in = the cache before the prompt, out = after.
+ *   o_cache: [B,H,L,dv] float64 out.
+ */
+typedef struct { float m; int32_t pos; int src; } orc_entry; /* src >= 0: token, < 0: slot -1-src */
+
+static int orc_entry_before(const orc_entry *a, const orc_entry *b)
+{
+    return a->m > b->m || (a->m == b->m && a->pos < b->pos);
+}
+
+int oracle_hola_prefill(int B, int H, int L, int dk, int dv, int w, int block,
+                        const float *q, const float *k, const float *v, const double *m,
+                        int t0, float *cache_k, float *cache_v, float *cache_m,
+                        int32_t *cache_pos, int32_t *count, const float *sink_logit,
+                        double rms_eps, double *o_cache)
+{
+    if (block < 1 || w < 1) return -1;
+    const int BH = B * H;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < BH; ++bh) {
+        const float *qh = q + (size_t)bh * L * dk, *kh = k + (size_t)bh * L * dk;
+        const float *vh = v + (size_t)bh * L * dv;
+        float *ck = cache_k + (size_t)bh * w * dk, *cv = cache_v + (size_t)bh * w * dv;
+        float *cm = cache_m + (size_t)bh * w;
+        int32_t *cp = cache_pos + (size_t)bh * w;
+        const int n0 = count[bh];
+        orc_entry *cur = (orc_entry *)malloc(sizeof(orc_entry) * (size_t)(w + block));
+        orc_entry *cand = (orc_entry *)malloc(sizeof(orc_entry) * (size_t)(w + block));
+        double *lg = (double *)malloc(sizeof(double) * (size_t)(w + block + 1));
+        float *ok = (float *)malloc(sizeof(float) * (size_t)w * (dk + dv));
+        if (!cur || !cand || !lg || !ok) {
+#pragma omp atomic write
+            bad = 1;
+            free(cur); free(cand); free(lg); free(ok);
+            continue;
+        }
+        int n = n0;
+        for (int s = 0; s < n0; ++s) {
+            cur[s].m = cm[s];
+            cur[s].pos = cp[s];
+            cur[s].src = -1 - s;
+        }
+        const double inv_sqrt_d = 1.0 / sqrt((double)dk);
+        for (int j0 = 0; j0 < L; j0 += block) {
+            const int j1 = (j0 + block < L) ? j0 + block : L;
+            /* read: every token of the block against cache + causal block tokens */
+            for (int i = j0; i < j1; ++i) {
+                const float *qt = qh + (size_t)i * dk;
+                double qq = 0.0;
+                for (int a = 0; a < dk; ++a) qq += (double)qt[a] * qt[a];
+                const double qs = 1.0 / sqrt(qq / dk + rms_eps);
+                int nl = 0;
+                for (int e = 0; e < n + (i - j0 + 1); ++e) {
+                    const float *kj;
+                    if (e < n) kj = cur[e].src >= 0 ? kh + (size_t)cur[e].src * dk
+                                                   : ck + (size_t)(-1 - cur[e].src) * dk;
+                    else kj = kh + (size_t)(j0 + e - n) * dk;
+                    double kk = 0.0, qk = 0.0;
+                    for (int a = 0; a < dk; ++a) {
+                        kk += (double)kj[a] * kj[a];
+                        qk += (double)qt[a] * kj[a];
+                    }
+                    lg[nl++] = qk * qs * inv_sqrt_d / sqrt(kk / dk + rms_eps);
+                }
+                const int nv = nl;
+                if (sink_logit) lg[nl++] = (double)sink_logit[bh % H];
+                double mx = lg[0];
+                for (int e = 1; e < nl; ++e) mx = lg[e] > mx ? lg[e] : mx;
+                double den = 0.0;
+                for (int e = 0; e < nl; ++e) den += exp(lg[e] - mx);
+                double *oc = o_cache + ((size_t)bh * L + i) * dv;
+                for (int c = 0; c < dv; ++c) oc[c] = 0.0;
+                for (int e = 0; e < nv; ++e) {
+                    const float *vj;
+                    if (e < n) vj = cur[e].src >= 0 ? vh + (size_t)cur[e].src * dv
+                                                   : cv + (size_t)(-1 - cur[e].src) * dv;
+                    else vj = vh + (size_t)(j0 + e - n) * dv;
+                    const double p = exp(lg[e] - mx) / den;
+                    for (int c = 0; c < dv; ++c) oc[c] += p * (double)vj[c];
+                }
+            }
+            /* insert the block: keep the w best of cache + block */
+            int nc = 0;
+            for (int e = 0; e < n; ++e) cand[nc++] = cur[e];
+            for (int i = j0; i < j1; ++i) {
+                cand[nc].m = (float)m[(size_t)bh * L + i];
+                cand[nc].pos = t0 + i;
+                cand[nc].src = i;
+                ++nc;
+            }
+            for (int a = 1; a < nc; ++a) {   /* insertion sort, (m desc, pos asc) */
+                orc_entry x = cand[a];
+                int b = a - 1;
+                while (b >= 0 && orc_entry_before(&x, &cand[b])) {
+                    cand[b + 1] = cand[b];
+                    --b;
+                }
+                cand[b + 1] = x;
+            }
+            n = nc < w ? nc : w;
+            for (int e = 0; e < n; ++e) cur[e] = cand[e];
+        }
+        /* write the final cache back (old slots are read before any is written) */
+        for (int e = 0; e < n; ++e) {
+            const float *ks = cur[e].src >= 0 ? kh + (size_t)cur[e].src * dk : ck + (size_t)(-1 - cur[e].src) * dk;
+            const float *vs = cur[e].src >= 0 ? vh + (size_t)cur[e].src * dv : cv + (size_t)(-1 - cur[e].src) * dv;
+            memcpy(ok + (size_t)e * (dk + dv), ks, sizeof(float) * (size_t)dk);
+            memcpy(ok + (size_t)e * (dk + dv) + dk, vs, sizeof(float) * (size_t)dv);
+        }
+        for (int e = 0; e < n; ++e) {
+            memcpy(ck + (size_t)e * dk, ok + (size_t)e * (dk + dv), sizeof(float) * (size_t)dk);
+            memcpy(cv + (size_t)e * dv, ok + (size_t)e * (dk + dv) + dk, sizeof(float) * (size_t)dv);
+            cm[e] = cur[e].m;
+            cp[e] = cur[e].pos;
+        }
+        count[bh] = n;
+        free(cur); free(cand); free(lg); free(ok);
+    }
+    return bad ? -2 : 0;
+}

@@ -652,3 +652,102 @@ def test_cache_read_sharpness_numbers_from_the_page(orc):
             assert abs(mass - expect) <= tol
         else:
             assert mass > g["sharp_mass_min"]
+
+
+# ---------------------------------------------------------------------------
+# HOLA cache over a whole prompt (block by block)
+# ---------------------------------------------------------------------------
+
+def test_prefill_with_unit_blocks_is_the_decode_step(orc):
+    """A Hippocampus for Linear Attention, sec. 3.4 eq. (7): the visible set of
+    a token is the cache, the causal tokens of its block and the sink. With
+    blocks of one token that is the decode step's read-then-insert, so the
+    prompt routine must reproduce a sequence of decode steps exactly, starting
+    from a non-empty cache."""
+    rng = _rng(40)
+    B, H, dk, dv, w, L = 2, 2, 8, 5, 6, 40
+    q = rng.standard_normal((B, H, L, dk)).astype(np.float32)
+    k = rng.standard_normal((B, H, L, dk)).astype(np.float32)
+    v = rng.standard_normal((B, H, L, dv)).astype(np.float32)
+    m = np.round(rng.uniform(0, 3, (B, H, L)) * 4) / 4   # many exact ties
+    sink = rng.standard_normal(H).astype(np.float32)
+    a = orc.HolaCache(B, H, dk, dv, w)
+    for t in range(4):                                    # a cache from earlier tokens
+        a.step(q[:, :, t], k[:, :, t], v[:, :, t], m[:, :, t] + 1.0, t - 10)
+    b = orc.HolaCache(B, H, dk, dv, w)
+    for f in ("k", "v", "m", "pos", "count"):
+        setattr(b, f, getattr(a, f).copy())
+    steps = np.stack([a.step(q[:, :, t], k[:, :, t], v[:, :, t], m[:, :, t], t + 100, sink)
+                      for t in range(L)], 2)
+    pre = b.prefill(q, k, v, m, 100, 1, sink)
+    np.testing.assert_allclose(pre, steps, rtol=0, atol=1e-13)
+    np.testing.assert_array_equal(b.count, a.count)
+    for bb in range(B):
+        for h in range(H):
+            n = a.count[bb, h]
+            sa = sorted(zip(a.pos[bb, h, :n], a.m[bb, h, :n]))
+            sb = sorted(zip(b.pos[bb, h, :n], b.m[bb, h, :n]))
+            assert sa == sb
+            ia, ib = np.argsort(a.pos[bb, h, :n]), np.argsort(b.pos[bb, h, :n])
+            np.testing.assert_array_equal(a.k[bb, h, ia], b.k[bb, h, ib])
+            np.testing.assert_array_equal(a.v[bb, h, ia], b.v[bb, h, ib])
+
+
+def test_prefill_without_eviction_is_causal_attention(orc):
+    """A Hippocampus for Linear Attention, sec. 3.2 eq. (4), sec. 3.4 eq. (7):
+    when nothing is evicted (w >= cached + L) every token sees every earlier
+    token (from the cache or from its own block) and itself, for any block
+    size: exact causal softmax attention on RMS-normalised q, k at 1/sqrt(d),
+    here against torch's rms_norm and scaled_dot_product_attention in float64,
+    with the cached tokens as an always-visible prefix and the sink as an extra
+    key through the additive mask."""
+    import torch
+    rng = _rng(41)
+    B, H, dk, dv, L, P, eps = 1, 2, 16, 8, 45, 3, 1e-6
+    q = rng.standard_normal((B, H, L, dk)).astype(np.float32)
+    k = rng.standard_normal((B, H, P + L, dk)).astype(np.float32)
+    v = rng.standard_normal((B, H, P + L, dv)).astype(np.float32)
+    sink = rng.standard_normal(H).astype(np.float32)
+    qt = _rmsnorm(torch.from_numpy(q).double(), eps)
+    kt = _rmsnorm(torch.from_numpy(k).double(), eps)
+    vt = torch.from_numpy(v).double()
+    kz = torch.cat([kt, torch.zeros(B, H, 1, dk, dtype=torch.float64)], 2)
+    vz = torch.cat([vt, torch.zeros(B, H, 1, dv, dtype=torch.float64)], 2)
+    for use_sink in (False, True):
+        mask = torch.full((L, P + L + 1), float("-inf"), dtype=torch.float64)
+        mask[:, :P] = 0.0
+        mask[:, P:P + L] = torch.triu(torch.full((L, L), float("-inf"), dtype=torch.float64), 1)
+        mask = mask.expand(B, H, L, P + L + 1).clone()
+        if use_sink:
+            mask[..., P + L] = torch.from_numpy(sink.astype(np.float64))[None, :, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qt, kz, vz, attn_mask=mask).numpy()
+        for block in (1, 7, 16, 64):
+            c = orc.HolaCache(B, H, dk, dv, P + L)
+            for t in range(P):
+                c.step(q[:, :, 0], k[:, :, t], v[:, :, t], np.ones((B, H)), t - P)
+            got = c.prefill(q, k[:, :, P:], v[:, :, P:], rng.uniform(0, 1, (B, H, L)), 0, block,
+                            sink if use_sink else None, eps)
+            np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_prefill_final_cache_is_sorted_topw(orc):
+    """A Hippocampus for Linear Attention, sec. 3.3: the cache is the top-w of
+    the whole history by score (ties: the earlier token), whatever the block
+    size; the prompt routine leaves it in that order. Brute force by sorting."""
+    rng = _rng(42)
+    B, H, dk, dv, w, L = 1, 3, 4, 3, 10, 77
+    q = rng.standard_normal((B, H, L, dk)).astype(np.float32)
+    k = rng.standard_normal((B, H, L, dk)).astype(np.float32)
+    v = rng.standard_normal((B, H, L, dv)).astype(np.float32)
+    m = np.round(rng.uniform(0, 3, (B, H, L)) * 3) / 3
+    m32 = m.astype(np.float32)
+    for block in (1, 5, 32, 200):
+        c = orc.HolaCache(B, H, dk, dv, w)
+        c.prefill(q, k, v, m, 1000, block)
+        for h in range(H):
+            order = sorted(range(L), key=lambda j: (-m32[0, h, j], j))[:w]
+            assert c.count[0, h] == w
+            np.testing.assert_array_equal(c.pos[0, h], np.array(order) + 1000)
+            np.testing.assert_array_equal(c.m[0, h], m32[0, h, order])
+            np.testing.assert_array_equal(c.k[0, h], k[0, h, order])
+            np.testing.assert_array_equal(c.v[0, h], v[0, h, order])
