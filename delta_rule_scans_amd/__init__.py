@@ -21,6 +21,7 @@ import os
 __all__ = [
     "lib", "KdnError", "kdn_scan_fwd", "kdn_step_decode", "hola_cache_update",
     "kdn_scan_workspace_size", "kdn_status_string", "HolaCache", "LIB_PATH",
+    "hola_prefill", "hola_prefill_workspace_size",
     "F32", "BF16", "MODES", "RESIDS", "PHASES",
 ]
 
@@ -49,9 +50,9 @@ def _load():
     L.kdn_status_string.restype = ctypes.c_char_p
     L.kdn_version.argtypes = []
     L.kdn_version.restype = I
-    L.kdn_scan_workspace_size.argtypes = [I, I, I, I, I, I, I, I]
+    L.kdn_scan_workspace_size.argtypes = [I, I, I, I, I, I, I, I, I]
     L.kdn_scan_workspace_size.restype = SZ
-    L.kdn_scan_fwd.argtypes = [P, P, P, I, P, P, P, P, P, F, P, P, P, I,
+    L.kdn_scan_fwd.argtypes = [P, P, P, I, P, P, P, P, P, F, P, P, P, I, P,
                                I, I, I, I, I, I, I, I, P, SZ, P]
     L.kdn_scan_fwd.restype = I
     L.kdn_scan_fwd_phase.argtypes = [I] + L.kdn_scan_fwd.argtypes
@@ -61,6 +62,11 @@ def _load():
     L.hola_cache_update.argtypes = [P, P, P, P, ctypes.c_int32, P, P, P, P, P, P, P, F,
                                     I, I, I, I, I, P]
     L.hola_cache_update.restype = I
+    L.hola_prefill_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    L.hola_prefill_workspace_size.restype = SZ
+    L.hola_prefill.argtypes = [P, P, P, I, P, ctypes.c_int32, I, P, P, P, P, P, P, P, F,
+                               I, I, I, I, I, I, P, SZ, P]
+    L.hola_prefill.restype = I
     return L
 
 
@@ -71,9 +77,11 @@ def kdn_status_string(status: int) -> str:
     return lib.kdn_status_string(int(status)).decode()
 
 
-def kdn_scan_workspace_size(B, H, L, d_k, d_v, chunk, mode="delta", in_dtype=BF16) -> int:
+def kdn_scan_workspace_size(B, H, L, d_k, d_v, chunk, mode="delta", in_dtype=BF16,
+                            with_scores: bool = False) -> int:
     m = MODES[mode] if isinstance(mode, str) else int(mode)
-    return int(lib.kdn_scan_workspace_size(B, H, L, d_k, d_v, chunk, m, in_dtype))
+    return int(lib.kdn_scan_workspace_size(B, H, L, d_k, d_v, chunk, m, in_dtype,
+                                           1 if with_scores else 0))
 
 
 # ----------------------------------------------------------------- helpers
@@ -126,13 +134,14 @@ def _dtype_code(dt):
 def kdn_scan_fwd(q, k, v, alpha=None, beta=None, r=None, cov_in=None, cov_out=None,
                  q_noise_var: float = 0.0, state_in=None, state_out=None, o=None, out_dtype=None,
                  chunk: int = 64, mode: str = "delta", resid: str = "gated", workspace=None,
-                 stream=None, phase: str = "all"):
+                 stream=None, phase: str = "all", m=None):
     """Chunkwise scan. q, k: [B,H,L,d_k]; v: [B,H,L,d_v] (bf16 or float32, same dtype);
     alpha/beta/r: [B,H,L] float32; cov_in/cov_out: [B,H,d_k] (diag), [B,H,d_k,d_k]
     (full) or [B,H] (iso) float32; state_in/state_out: [B,H,d_k,d_v] float32. Returns o [B,H,L,d_v]
     (float32 unless ``out_dtype`` or ``o`` says otherwise). ``phase`` "prepare" /
     "state" runs one half of the call (kdn_scan_fwd_phase); both halves must see
-    the same ``workspace`` tensor."""
+    the same ``workspace`` tensor. ``m`` ([B,H,L] float32 tensor, or True to
+    allocate one) receives the write scores; the call then returns (o, m)."""
     torch = _torch()
     _check(q, "q", (torch.bfloat16, torch.float32))
     B, H, L, dk = q.shape
@@ -152,7 +161,13 @@ def kdn_scan_fwd(q, k, v, alpha=None, beta=None, r=None, cov_in=None, cov_out=No
     _check(o, "o", (torch.bfloat16, torch.float32), (B, H, L, dv), dev)
     in_code = _dtype_code(q.dtype)
     mcode, rcode = MODES[mode], RESIDS[resid]
-    need = int(lib.kdn_scan_workspace_size(B, H, L, dk, dv, chunk, mcode, in_code))
+    want_m = m is not None and m is not False
+    if m is True:
+        m = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    if want_m:
+        _check(m, "m", torch.float32, (B, H, L), dev)
+    need = int(lib.kdn_scan_workspace_size(B, H, L, dk, dv, chunk, mcode, in_code,
+                                           1 if want_m else 0))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -161,11 +176,12 @@ def kdn_scan_fwd(q, k, v, alpha=None, beta=None, r=None, cov_in=None, cov_out=No
     st = lib.kdn_scan_fwd_phase(PHASES[phase], _ptr(q), _ptr(k), _ptr(v), in_code, _ptr(alpha),
                                 _ptr(beta), _ptr(r), _ptr(cov_in), _ptr(cov_out),
                                 float(q_noise_var), _ptr(state_in), _ptr(state_out), _ptr(o),
-                                _dtype_code(o.dtype), B, H, L, dk, dv, int(chunk), mcode, rcode,
-                                _ptr(workspace), wbytes, _stream(stream))
+                                _dtype_code(o.dtype), _ptr(m) if want_m else None, B, H, L, dk,
+                                dv, int(chunk), mcode, rcode, _ptr(workspace), wbytes,
+                                _stream(stream))
     if st != 0:
         raise KdnError(st, "kdn_scan_fwd")
-    return o
+    return (o, m) if want_m else o
 
 
 # ----------------------------------------------------------------- decode
@@ -242,3 +258,40 @@ def hola_cache_update(q, k, v, m, t: int, cache: HolaCache, sink_logit=None, o_c
     if st != 0:
         raise KdnError(st, "hola_cache_update")
     return o_cache
+
+
+def hola_prefill(q, k, v, m, t0: int, cache: HolaCache, block: int = 256, sink_logit=None,
+                 o_cache=None, rms_eps: float = 1e-6, workspace=None, stream=None):
+    """The HOLA cache over a whole prompt in blocks of ``block`` tokens: each
+    token reads the cache as it stood before its block, its block's tokens up to
+    itself and the sink; then the block is inserted. q, k: [B,H,L,d_k]; v:
+    [B,H,L,d_v] (bf16 or float32); m: [B,H,L] float32 scores; t0: position of
+    token 0. Updates ``cache`` in place; returns o_cache [B,H,L,d_v] float32."""
+    torch = _torch()
+    B, H, dk, dv, w = cache.B, cache.H, cache.d_k, cache.d_v, cache.w
+    dev = cache.k.device
+    _check(q, "q", (torch.bfloat16, torch.float32))
+    L = q.shape[2]
+    _check(q, "q", q.dtype, (B, H, L, dk), dev)
+    _check(k, "k", q.dtype, (B, H, L, dk), dev)
+    _check(v, "v", q.dtype, (B, H, L, dv), dev)
+    _check(m, "m", torch.float32, (B, H, L), dev)
+    _check(sink_logit, "sink_logit", torch.float32, (H,), dev)
+    if o_cache is None:
+        o_cache = torch.empty((B, H, L, dv), dtype=torch.float32, device=dev)
+    _check(o_cache, "o_cache", torch.float32, (B, H, L, dv), dev)
+    need = int(lib.hola_prefill_workspace_size(B, H, max(L, 1), dk, dv, w, int(block)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.hola_prefill(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(m), int(t0),
+                          int(block), _ptr(cache.k), _ptr(cache.v), _ptr(cache.m),
+                          _ptr(cache.pos), _ptr(cache.count), _ptr(sink_logit), _ptr(o_cache),
+                          float(rms_eps), B, H, L, dk, dv, w, _ptr(workspace),
+                          workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise KdnError(st, "hola_prefill")
+    return o_cache
+
+
+def hola_prefill_workspace_size(B, H, L, d_k, d_v, w, block) -> int:
+    return int(lib.hola_prefill_workspace_size(B, H, L, d_k, d_v, w, block))

@@ -18,6 +18,7 @@ constexpr int kMaxDim = 128;
 constexpr int kMaxFullDk = 64;
 constexpr int kMaxCapacity = 256;
 constexpr int kMaxGridYZ = 65535;
+constexpr int kMaxPrefillBlock = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -27,18 +28,21 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace layout, 256-byte aligned parts:
 //   [maps (DIAG, ISO) | gains (DIAG, FULL) or write strengths and key norms (ISO)
-//    | per-chunk records of the matrix-core path].
-// Gains are fp16 for bf16 inputs and float32 otherwise.
+//    | per-chunk records of the matrix-core path | residuals for the scores].
+// Gains are fp16 for bf16 inputs and float32 otherwise. The residual part holds
+// fp16 residuals (matrix-core path) or per-tile squared norms (float32 path),
+// sized for the larger of the two since the path is chosen at call time.
 struct WsLayout {
-  size_t maps_off, maps_bytes, gains_off, gains_bytes, t_off, t_bytes, total;
+  size_t maps_off, maps_bytes, gains_off, gains_bytes, t_off, t_bytes, s_off, s_bytes, total;
 };
 
 bool use_mfma_path(int in_dtype, int d_k, int d_v, int chunk) {
   return in_dtype == KDN_BF16 && kdn::scan_mfma_supported(d_k, d_v, chunk);
 }
 
-WsLayout ws_layout(int B, int H, int L, int dk, int dv, int chunk, int mode, int in_dtype) {
-  WsLayout w{0, 0, 0, 0, 0, 0, 0};
+WsLayout ws_layout(int B, int H, int L, int dk, int dv, int chunk, int mode, int in_dtype,
+                   bool scores) {
+  WsLayout w{0, 0, 0, 0, 0, 0, 0, 0, 0};
   if (L <= 0) return w;
   const size_t BH = (size_t)B * H;
   const size_t nchunks = ((size_t)L + chunk - 1) / chunk;
@@ -49,10 +53,20 @@ WsLayout ws_layout(int B, int H, int L, int dk, int dv, int chunk, int mode, int
   if (mode == KDN_GAIN_ISO) w.gains_bytes = 2 * BH * (size_t)L * sizeof(float);
   const bool gain = mode == KDN_GAIN_DIAG || mode == KDN_GAIN_FULL;
   if (use_mfma_path(in_dtype, dk, dv, chunk)) w.t_bytes = kdn::scan_mfma_workspace_bytes((int)BH, L, gain);
+  if (scores) {
+    const int cols = kdn::scan_f32_tile_cols(dk, chunk);
+    const size_t ntiles = cols > 0 ? (size_t)(dv + cols - 1) / cols : 0;
+    w.s_bytes = BH * ntiles * (size_t)L * sizeof(float);
+    if (use_mfma_path(in_dtype, dk, dv, chunk)) {
+      const size_t u = kdn::scan_mfma_ubuf_bytes((int)BH, L, dv);
+      if (u > w.s_bytes) w.s_bytes = u;
+    }
+  }
   w.maps_off = 0;
   w.gains_off = round_up(w.maps_bytes, 256);
   w.t_off = w.gains_off + round_up(w.gains_bytes, 256);
-  w.total = w.t_off + round_up(w.t_bytes, 256);
+  w.s_off = w.t_off + round_up(w.t_bytes, 256);
+  w.total = w.s_off + round_up(w.s_bytes, 256);
   return w;
 }
 
@@ -81,17 +95,17 @@ KDN_EXPORT const char* kdn_status_string(int status) {
 KDN_EXPORT int kdn_version(void) { return 100; }
 
 KDN_EXPORT size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
-                                          int mode, int in_dtype) {
+                                          int mode, int in_dtype, int with_scores) {
   if (B < 1 || H < 1 || L < 0 || d_k < 1 || d_v < 1 || !valid_chunk(chunk)) return 0;
-  return ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype).total;
+  return ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype, with_scores != 0).total;
 }
 
 KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const void* v,
                                   int in_dtype, const float* alpha, const float* beta,
                                   const float* r, const float* cov_in, float* cov_out,
                                   float q_noise_var, const float* state_in, float* state_out,
-                                  void* o, int out_dtype, int B, int H, int L, int d_k, int d_v,
-                                  int chunk, int mode, int resid, void* workspace,
+                                  void* o, int out_dtype, float* m, int B, int H, int L, int d_k,
+                                  int d_v, int chunk, int mode, int resid, void* workspace,
                                   size_t workspace_bytes, void* stream) {
   if (phase != KDN_PHASE_ALL && phase != KDN_PHASE_PREPARE && phase != KDN_PHASE_STATE)
     return KDN_ERR_BAD_MODE;
@@ -115,7 +129,7 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
     if (!q || !k || !v || !o) return KDN_ERR_NULL_POINTER;
     if (mode == KDN_GAIN_DELTA && beta == nullptr) return KDN_ERR_NULL_POINTER;
   }
-  const WsLayout ws = ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype);
+  const WsLayout ws = ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype, m != nullptr);
   if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total || !aligned16(workspace)))
     return KDN_ERR_WORKSPACE;
   if (kdn::scan_f32_lds_bytes(d_k, chunk) == 0 &&
@@ -190,25 +204,51 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   const bool out_bf16 = out_dtype == KDN_BF16;
   const bool mfma_ok = use_mfma_path(in_dtype, d_k, d_v, chunk) && aligned16(q) && aligned16(k) &&
                        aligned16(v) && aligned16(o) && (gains == nullptr || aligned16(gains));
+  kdn::ScoreArgs sc{};
+  if (m) {
+    void* sbuf = static_cast<char*>(workspace) + ws.s_off;
+    if (mfma_ok) a.ubuf = sbuf;
+    else a.esq = static_cast<float*>(sbuf);
+    const int cols = kdn::scan_f32_tile_cols(d_k, chunk);
+    sc.esq = a.esq;
+    sc.ubuf = a.ubuf;
+    sc.ntiles = mfma_ok ? d_v / 32 : (d_v + cols - 1) / cols;
+    sc.beta = a.beta;
+    sc.alpha = alpha;
+    sc.plain = a.plain;
+    sc.iso_beta = iso_beta;
+    sc.iso_kk = iso_beta ? iso_beta + (size_t)BH * L : nullptr;
+    sc.gains = gains;
+    sc.gains_f16 = in_bf16 ? 1 : 0;
+    sc.m = m;
+    sc.BH = BH;
+    sc.L = L;
+    sc.dk = d_k;
+    sc.dv = d_v;
+  }
+  hipError_t e = hipSuccess;
   if (mfma_ok) {
     void* tbuf = static_cast<char*>(workspace) + ws.t_off;
     if (do_prep) {
-      const hipError_t e = kdn::launch_tinv_mfma(a, tbuf, s);
+      e = kdn::launch_tinv_mfma(a, tbuf, s);
       if (e != hipSuccess) return map_hip(e);
     }
-    return do_state ? map_hip(kdn::launch_state_mfma(a, out_bf16, tbuf, s)) : KDN_OK;
+    if (do_state) e = kdn::launch_state_mfma(a, out_bf16, tbuf, s);
+  } else if (do_state) {
+    e = kdn::launch_scan_f32(a, in_bf16, out_bf16, in_bf16, s);
   }
-  return do_state ? map_hip(kdn::launch_scan_f32(a, in_bf16, out_bf16, in_bf16, s)) : KDN_OK;
+  if (e == hipSuccess && do_state && m) e = kdn::launch_scores(sc, s);
+  return map_hip(e);
 }
 
 KDN_EXPORT int kdn_scan_fwd(const void* q, const void* k, const void* v, int in_dtype,
                             const float* alpha, const float* beta, const float* r,
                             const float* cov_in, float* cov_out, float q_noise_var,
                             const float* state_in, float* state_out, void* o, int out_dtype,
-                            int B, int H, int L, int d_k, int d_v, int chunk, int mode, int resid,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            float* m, int B, int H, int L, int d_k, int d_v, int chunk, int mode,
+                            int resid, void* workspace, size_t workspace_bytes, void* stream) {
   return kdn_scan_fwd_phase(KDN_PHASE_ALL, q, k, v, in_dtype, alpha, beta, r, cov_in, cov_out,
-                            q_noise_var, state_in, state_out, o, out_dtype, B, H, L, d_k, d_v,
+                            q_noise_var, state_in, state_out, o, out_dtype, m, B, H, L, d_k, d_v,
                             chunk, mode, resid, workspace, workspace_bytes, stream);
 }
 
@@ -255,4 +295,56 @@ KDN_EXPORT int hola_cache_update(const float* q, const float* k, const float* v,
   return map_hip(kdn::launch_hola(q, k, v, m, t, cache_k, cache_v, cache_m, cache_pos, cache_count,
                                   sink_logit, o_cache, rms_eps, B, H, d_k, d_v, w,
                                   static_cast<hipStream_t>(stream)));
+}
+
+KDN_EXPORT size_t hola_prefill_workspace_size(int B, int H, int L, int d_k, int d_v, int w,
+                                              int block) {
+  if (B < 1 || H < 1 || L < 1 || d_k < 1 || d_v < 1 || w < 1 || block < 1) return 0;
+  return kdn::prefill_workspace_bytes(B * H, L, d_k, d_v, w, block);
+}
+
+KDN_EXPORT int hola_prefill(const void* q, const void* k, const void* v, int in_dtype,
+                            const float* m, int32_t t0, int block, float* cache_k, float* cache_v,
+                            float* cache_m, int32_t* cache_pos, int32_t* cache_count,
+                            const float* sink_logit, float* o_cache, float rms_eps, int B, int H,
+                            int L, int d_k, int d_v, int w, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_ERR_BAD_DTYPE;
+  if (w < 1 || w > kMaxCapacity) return KDN_ERR_BAD_CAPACITY;
+  if (B < 1 || H < 1 || L < 0 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
+    return KDN_ERR_BAD_SHAPE;
+  if (block < 1 || block > kMaxPrefillBlock) return KDN_ERR_BAD_SHAPE;
+  if ((long long)B * H > (1LL << 24)) return KDN_ERR_BAD_SHAPE;
+  if ((long long)(L + block - 1) / block > kMaxGridYZ) return KDN_ERR_BAD_SHAPE;
+  if ((long long)t0 + L > INT32_MAX) return KDN_ERR_BAD_SHAPE;
+  if (!(rms_eps >= 0.f) || !std::isfinite(rms_eps)) return KDN_ERR_BAD_SHAPE;
+  if (!cache_k || !cache_v || !cache_m || !cache_pos || !cache_count) return KDN_ERR_NULL_POINTER;
+  if (L == 0) return KDN_OK;
+  if (!q || !k || !v || !m || !o_cache) return KDN_ERR_NULL_POINTER;
+  const size_t need = kdn::prefill_workspace_bytes(B * H, L, d_k, d_v, w, block);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+    return KDN_ERR_WORKSPACE;
+  kdn::PrefillArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.m = m;
+  a.t0 = t0;
+  a.block = block;
+  a.cache_k = cache_k;
+  a.cache_v = cache_v;
+  a.cache_m = cache_m;
+  a.cache_pos = cache_pos;
+  a.cache_count = cache_count;
+  a.sink_logit = sink_logit;
+  a.o_cache = o_cache;
+  a.rms_eps = rms_eps;
+  a.BH = B * H;
+  a.H = H;
+  a.L = L;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.w = w;
+  kdn::prefill_bind_workspace(a, workspace);
+  return map_hip(kdn::launch_prefill(a, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream)));
 }

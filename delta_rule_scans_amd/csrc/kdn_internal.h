@@ -53,6 +53,11 @@ struct ScanArgs {
   void* o;                // [BH, L, dv]
   int BH, L, dk, dv, chunk;
   int plain;  // 1: plain residual (delta only): b = (beta/alpha) k, v' = alpha v
+  // Residuals for the write scores, or null: the float32 path writes per-tile
+  // sums of e_t^2 to esq [BH, d_v tiles, L]; the matrix-core path writes the
+  // residuals themselves (fp16) to ubuf, see scan_mfma_ubuf_bytes.
+  float* esq = nullptr;
+  void* ubuf = nullptr;
 };
 
 // ------------------------------------------------------------------ launchers
@@ -64,6 +69,8 @@ hipError_t launch_scan_f32(const ScanArgs& a, bool in_bf16, bool out_bf16, bool 
                            hipStream_t s);
 // LDS bytes the float32 path needs for (dk, chunk), or 0 when it cannot run them.
 size_t scan_f32_lds_bytes(int dk, int chunk);
+// Value columns per workgroup of the float32 path (its d_v tile).
+int scan_f32_tile_cols(int dk, int chunk);
 
 // Matrix-core chunk scan for bf16 inputs (dk == 128, dv % 32 == 0, chunk == 64);
 // gains (if any) are fp16. `tbuf` holds scan_mfma_workspace_bytes(BH, L, gain)
@@ -73,6 +80,31 @@ hipError_t launch_tinv_mfma(const ScanArgs& a, void* tbuf, hipStream_t s);
 hipError_t launch_state_mfma(const ScanArgs& a, bool out_bf16, const void* tbuf, hipStream_t s);
 bool scan_mfma_supported(int dk, int dv, int chunk);
 size_t scan_mfma_workspace_bytes(int BH, int L, bool gain);
+// Bytes of the residual buffer of the matrix-core path (fp16 residuals of
+// every token and value column).
+size_t scan_mfma_ubuf_bytes(int BH, int L, int dv);
+
+// Write scores m_t = s_t ||e_t|| ("A Hippocampus for Linear Attention", sec.
+// 3.3 eq. (6)) from the residuals a scan left in esq (float32 path, `ntiles`
+// d_v tiles) or ubuf (matrix-core path, dv / 32 tiles). The write scale s_t is
+// beta_t (divided by alpha_t for the plain residual) for the delta write,
+// beta_t ||k_t|| for the isotropic gain (iso_beta, iso_kk = ||k||^2), and
+// ||g_t|| for the diagonal / full gains (gains [BH, L, dk], fp16 or f32).
+struct ScoreArgs {
+  const float* esq;
+  const void* ubuf;
+  int ntiles;
+  const float* beta;
+  const float* alpha;
+  int plain;
+  const float* iso_beta;
+  const float* iso_kk;
+  const void* gains;
+  int gains_f16;
+  float* m;
+  int BH, L, dk, dv;
+};
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t s);
 
 // Diagonal-covariance Kalman gains: writes gains [BH, L, dk] (fp16 or f32) and
 // the final covariance. `maps` is scratch of BH * nchunks * dk * 4 floats.
@@ -108,5 +140,34 @@ hipError_t launch_hola(const float* q, const float* k, const float* v, const flo
                        float* cache_k, float* cache_v, float* cache_m, int32_t* cache_pos,
                        int32_t* cache_count, const float* sink_logit, float* o_cache,
                        float rms_eps, int B, int H, int dk, int dv, int w, hipStream_t s);
+
+// HOLA cache over a whole prompt in blocks; see hola_prefill.hip.
+struct PrefillArgs {
+  const void* q;   // [BH, L, dk] (bf16 or float32)
+  const void* k;   // [BH, L, dk]
+  const void* v;   // [BH, L, dv]
+  const float* m;  // [BH, L] scores
+  int t0, block;
+  float* cache_k;  // [BH, w, dk]
+  float* cache_v;  // [BH, w, dv]
+  float* cache_m;  // [BH, w]
+  int32_t* cache_pos;
+  int32_t* cache_count;
+  const float* sink_logit;  // [H] or null
+  float* o_cache;           // [BH, L, dv]
+  float rms_eps;
+  int BH, H, L, dk, dv, w;
+  // workspace parts (prefill_bind_workspace)
+  int* members;       // [BH, blocks, w] cache members each block reads
+  int* member_count;  // [BH, blocks]
+  int* final_src;     // [BH, w]
+  float* final_m;     // [BH, w]
+  int* final_pos;     // [BH, w]
+  int* final_count;   // [BH]
+  float* stage;       // [BH, w, dk + dv]
+};
+size_t prefill_workspace_bytes(int BH, int L, int dk, int dv, int w, int block);
+void prefill_bind_workspace(PrefillArgs& a, void* ws);
+hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, hipStream_t s);
 
 }  // namespace kdn

@@ -177,6 +177,12 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
         __syncthreads();
       }
     }
+    // per-tile squared residual norms for the write scores
+    if (a.esq && tid < n) {
+      float ss = 0.f;
+      for (int j = 0; j < nj; ++j) ss = fmaf(sX[tid * dvt + j], sX[tid * dvt + j], ss);
+      a.esq[((size_t)bh * gridDim.y + blockIdx.y) * L + c0 + tid] = ss;
+    }
     // O = diag(g) Q S0 + P U
     for (int idx = tid; idx < n * dvt; idx += NT) {
       const int i = idx / dvt, j = idx - i * dvt;
@@ -229,6 +235,7 @@ __global__ void copy_f32_kernel(const float* src, float* dst, size_t n) {
 }  // namespace
 
 size_t scan_f32_lds_bytes(int dk, int chunk) { return plan_f32(dk, chunk).lds; }
+int scan_f32_tile_cols(int dk, int chunk) { return plan_f32(dk, chunk).dvt; }
 
 hipError_t launch_scan_f32(const ScanArgs& a, bool in_bf16, bool out_bf16, bool gain_f16,
                            hipStream_t s) {

@@ -516,6 +516,7 @@ struct StateArgs {
   const float* state_in;
   float* state_out;
   void* o;
+  half8* ubuf;           // residuals for the write scores, or null
   int BH, L, dv, nchunks, ntiles;
 };
 
@@ -953,6 +954,12 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         o[1] = mfma32(uv[2], pa[4], o[1]);
         o[1] = mfma32(uv[3], pa[5], o[1]);
         __builtin_amdgcn_sched_barrier(0);
+        if (a.ubuf) {
+          // residuals U of this chunk and d_v slice, in wavefront-0 register order
+          half8* ub = a.ubuf + ((size_t)(bh * a.ntiles + tile) * a.nchunks + cc) * 256;
+#pragma unroll
+          for (int s = 0; s < 4; ++s) ub[s * 64 + lane] = uv[s];
+        }
         if constexpr (GAIN) q_load(rq, b, min(cc + 2, last), lane);
         // o[tb] registers 4 q .. 4 q + 3: token 32 tb + c32, columns 8 q + 4 h .. + 4
 #pragma unroll
@@ -1142,6 +1149,11 @@ bool scan_mfma_supported(int dk, int dv, int chunk) {
   return dk == DK && chunk == C && dv % DV == 0 && dv >= DV;
 }
 
+size_t scan_mfma_ubuf_bytes(int BH, int L, int dv) {
+  const size_t nchunks = ((size_t)L + C - 1) / C;
+  return (size_t)BH * (dv / DV) * nchunks * 256 * sizeof(half8);
+}
+
 size_t scan_mfma_workspace_bytes(int BH, int L, bool gain) {
   const size_t nchunks = ((size_t)L + C - 1) / C;
   return (size_t)BH * nchunks * rec_bytes(gain);
@@ -1194,6 +1206,7 @@ hipError_t launch_state_mfma(const ScanArgs& s, bool out_bf16, const void* tbuf,
   sa.dv = s.dv;
   sa.nchunks = (s.L + C - 1) / C;
   sa.ntiles = s.dv / DV;
+  sa.ubuf = static_cast<half8*>(s.ubuf);
   if (s.gain)
     return out_bf16 ? launch_state_typed<true, true>(sa, st) : launch_state_typed<true, false>(sa, st);
   return out_bf16 ? launch_state_typed<false, true>(sa, st) : launch_state_typed<false, false>(sa, st);

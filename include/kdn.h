@@ -85,13 +85,15 @@ int kdn_version(void);
 
 /*
  * Bytes of device workspace kdn_scan_fwd needs for these arguments: the
- * per-token Kalman gains and per-chunk covariance maps (Kalman modes) and, on
- * the matrix-core path, the per-chunk (I + A)^-1 matrices of the chunk form
- * (chunk * chunk fp16 values per chunk and head). 0 for the delta write on the
- * float32 path. Pure host computation; 0 for invalid sizes.
+ * per-token Kalman gains and per-chunk covariance maps (Kalman modes), on the
+ * matrix-core path the per-chunk records of the chunk form ((I + A)^-1 and
+ * token scalars), and with with_scores != 0 room for the residuals the write
+ * scores are formed from (needed when kdn_scan_fwd is given an `m` output).
+ * 0 for the delta write on the float32 path without scores. Pure host
+ * computation; 0 for invalid sizes.
  */
 size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
-                               int mode, int in_dtype);
+                               int mode, int in_dtype, int with_scores);
 
 /*
  * Chunkwise-parallel forward scan over a whole sequence (all L tokens of all
@@ -118,6 +120,13 @@ size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
  *  o         [B,H,L,d_v] out_dtype output (bf16 outputs are the float32 result
  *            rounded to nearest even; that rounding alone is up to 2^-9 |o|,
  *            so use float32 output when the error bar is relative to RMS(o)).
+ *  m         [B,H,L] float32 write scores, or NULL (not computed): the norm
+ *            of each token's rank-one write ("A Hippocampus for Linear
+ *            Attention", sec. 3.3 eq. (6)): beta_t ||e_t|| for the delta write
+ *            (e_t the residual of the form in use), ||g_t|| ||e_t|| for the
+ *            Kalman gains. On the matrix-core path e_t is taken from its fp16
+ *            copy (relative error ~2^-11). Needs the workspace sized with
+ *            with_scores = 1.
  *  chunk     chunk length in tokens: 16, 32 or 64. The result does not depend on
  *            it beyond rounding; L need not be a multiple of it.
  *  mode      KDN_GAIN_*;  resid  KDN_RESID_* (PLAIN only with DELTA).
@@ -135,7 +144,7 @@ int kdn_scan_fwd(const void *q, const void *k, const void *v, int in_dtype,
                  const float *alpha, const float *beta, const float *r,
                  const float *cov_in, float *cov_out, float q_noise_var,
                  const float *state_in, float *state_out,
-                 void *o, int out_dtype,
+                 void *o, int out_dtype, float *m,
                  int B, int H, int L, int d_k, int d_v, int chunk, int mode, int resid,
                  void *workspace, size_t workspace_bytes, void *stream);
 
@@ -149,7 +158,7 @@ int kdn_scan_fwd(const void *q, const void *k, const void *v, int in_dtype,
  * not depend on the state: the covariance recursion and Kalman gains (it
  * writes cov_out) and, on the matrix-core path, the per-chunk inverses
  * (I + A)^-1 of the chunk form; it writes only the workspace and cov_out.
- * STATE then runs the chunk-by-chunk state scan and writes o and state_out.
+ * STATE then runs the chunk-by-chunk state scan and writes o, m and state_out.
  * A STATE call must see the workspace of a PREPARE call made with the same
  * arguments and inputs (same stream, or ordered by the caller); PREPARE may
  * run ahead on another stream, e.g. for the next batch. Arguments, checks and
@@ -159,7 +168,7 @@ int kdn_scan_fwd_phase(int phase, const void *q, const void *k, const void *v, i
                        const float *alpha, const float *beta, const float *r,
                        const float *cov_in, float *cov_out, float q_noise_var,
                        const float *state_in, float *state_out,
-                       void *o, int out_dtype,
+                       void *o, int out_dtype, float *m,
                        int B, int H, int L, int d_k, int d_v, int chunk, int mode, int resid,
                        void *workspace, size_t workspace_bytes, void *stream);
 
@@ -211,6 +220,39 @@ int hola_cache_update(const float *q, const float *k, const float *v, const floa
                       int32_t *cache_pos, int32_t *cache_count, const float *sink_logit,
                       float *o_cache, float rms_eps, int B, int H, int d_k, int d_v, int w,
                       void *stream);
+
+/*
+ * The HOLA cache over a whole prompt ("A Hippocampus for Linear Attention",
+ * sec. 3.3 (top-w cache by write score), sec. 3.4 eq. (7) (visible set: the
+ * cache, the causal tokens of the current block and an optional null sink),
+ * sec. 3.2 eq. (4)). The L prompt tokens (positions t0 .. t0 + L - 1) are taken
+ * in blocks of `block` tokens. Every token of block j reads over the cache as
+ * it stood before block j, the tokens of block j up to and including itself,
+ * and the sink, with the read of hola_cache_update (RMS-normalised query and
+ * keys, 1/sqrt(d_k), softmax). After block j the cache keeps the w best of
+ * (cache, block j) by float32 score descending, then position ascending. With
+ * block = 1 this is hola_cache_update applied token by token.
+ *
+ *  q, k      [B,H,L,d_k] in_dtype (KDN_F32 or KDN_BF16); v [B,H,L,d_v] in_dtype.
+ *  m         [B,H,L] float32 write scores of the prompt tokens (e.g. the `m`
+ *            output of kdn_scan_fwd). NaN scores rank below every other score.
+ *  cache_*   as hola_cache_update: in = the cache before the prompt (count
+ *            may be 0), out = after it, slots 0 .. count-1 in rank order.
+ *            Cached entries must have positions below t0.
+ *  sink_logit [H] float32 or NULL;  o_cache [B,H,L,d_v] float32 out.
+ *  workspace device scratch of hola_prefill_workspace_size(...) bytes, 16-byte
+ *            aligned.
+ * Sizes: B, H >= 1; L >= 0 (L = 0 leaves the cache as it is); 1 <= d_k, d_v
+ * <= 128; 1 <= w <= 256; 1 <= block <= 1024; t0 + L <= 2^31 - 1; rms_eps >= 0.
+ * The read runs in float32 on the vector units.
+ */
+size_t hola_prefill_workspace_size(int B, int H, int L, int d_k, int d_v, int w, int block);
+
+int hola_prefill(const void *q, const void *k, const void *v, int in_dtype, const float *m,
+                 int32_t t0, int block, float *cache_k, float *cache_v, float *cache_m,
+                 int32_t *cache_pos, int32_t *cache_count, const float *sink_logit,
+                 float *o_cache, float rms_eps, int B, int H, int L, int d_k, int d_v, int w,
+                 void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

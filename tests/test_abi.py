@@ -35,9 +35,9 @@ def kdn():
 
 def test_exports_match_header(kdn):
     declared = _header_functions()
-    assert declared == sorted(["hola_cache_update", "kdn_scan_fwd", "kdn_scan_fwd_phase",
-                               "kdn_scan_workspace_size", "kdn_status_string", "kdn_step_decode",
-                               "kdn_version"])
+    assert declared == sorted(["hola_cache_update", "hola_prefill", "hola_prefill_workspace_size",
+                               "kdn_scan_fwd", "kdn_scan_fwd_phase", "kdn_scan_workspace_size",
+                               "kdn_status_string", "kdn_step_decode", "kdn_version"])
     out = subprocess.run(["nm", "-D", "--defined-only", kdn.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = sorted(line.split()[-1] for line in out.splitlines()
@@ -86,12 +86,12 @@ P = 0x10000
 
 def _scan(kdn, **kw):
     a = dict(q=P, k=P, v=P, in_dtype=1, alpha=P, beta=P, r=None, cov_in=None, cov_out=None,
-             qvar=0.0, state_in=None, state_out=None, o=P, out_dtype=1, B=1, H=1, L=64, dk=128,
+             qvar=0.0, state_in=None, state_out=None, o=P, out_dtype=1, m=None, B=1, H=1, L=64, dk=128,
              dv=128, chunk=64, mode=0, resid=0, ws=None, wsb=0, stream=None)
     a.update(kw)
     return kdn.lib.kdn_scan_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["alpha"], a["beta"],
                                 a["r"], a["cov_in"], a["cov_out"], a["qvar"], a["state_in"],
-                                a["state_out"], a["o"], a["out_dtype"], a["B"], a["H"], a["L"],
+                                a["state_out"], a["o"], a["out_dtype"], a["m"], a["B"], a["H"], a["L"],
                                 a["dk"], a["dv"], a["chunk"], a["mode"], a["resid"], a["ws"],
                                 a["wsb"], a["stream"])
 
@@ -120,7 +120,12 @@ def test_scan_rejections(kdn):
     assert _scan(kdn, mode=2, cov_in=P, dk=64) == c["KDN_ERR_WORKSPACE"]
     # an unknown phase is rejected like an unknown mode
     assert kdn.lib.kdn_scan_fwd_phase(3, P, P, P, 1, P, P, None, None, None, 0.0, None, None, P, 1,
-                                      1, 1, 64, 128, 128, 64, 0, 0, None, 0, None) == c["KDN_ERR_BAD_MODE"]
+                                      None, 1, 1, 64, 128, 128, 64, 0, 0, None, 0, None) == c["KDN_ERR_BAD_MODE"]
+    # scores need the larger workspace
+    base = kdn.kdn_scan_workspace_size(1, 1, 64, 128, 128, 64, "delta", kdn.BF16)
+    big = kdn.kdn_scan_workspace_size(1, 1, 64, 128, 128, 64, "delta", kdn.BF16, with_scores=True)
+    assert big >= base + 64 * 128 * 2
+    assert _scan(kdn, m=P, ws=P, wsb=base) == c["KDN_ERR_WORKSPACE"]
     need = kdn.kdn_scan_workspace_size(1, 1, 64, 128, 128, 64, "diag", kdn.BF16)
     assert _scan(kdn, mode=1, cov_in=P, ws=P, wsb=need - 1) == c["KDN_ERR_WORKSPACE"]
     assert _scan(kdn, mode=1, cov_in=P, ws=P + 4, wsb=need) == c["KDN_ERR_WORKSPACE"]
@@ -177,3 +182,33 @@ def test_product_package_does_not_touch_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def _prefill(kdn, **kw):
+    a = dict(q=P, k=P, v=P, dt=1, m=P, t0=0, block=256, ck=P, cv=P, cm=P, cp=P, cc=P, sink=None,
+             oc=P, eps=1e-6, B=1, H=1, L=512, dk=128, dv=128, w=64, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return kdn.lib.hola_prefill(a["q"], a["k"], a["v"], a["dt"], a["m"], a["t0"], a["block"],
+                                a["ck"], a["cv"], a["cm"], a["cp"], a["cc"], a["sink"], a["oc"],
+                                a["eps"], a["B"], a["H"], a["L"], a["dk"], a["dv"], a["w"],
+                                a["ws"], a["wsb"], a["stream"])
+
+
+def test_prefill_rejections(kdn):
+    c = _header_constants()
+    need = kdn.hola_prefill_workspace_size(1, 1, 512, 128, 128, 64, 256)
+    # members per block, final cache and a staging copy of the final rows
+    assert need >= 2 * 64 * 4 + 64 * 256 * 4
+    assert kdn.hola_prefill_workspace_size(1, 1, 512, 128, 128, 0, 256) == 0
+    assert _prefill(kdn, dt=3) == c["KDN_ERR_BAD_DTYPE"]
+    for w in (0, 257):
+        assert _prefill(kdn, w=w) == c["KDN_ERR_BAD_CAPACITY"]
+    for bad in (dict(block=0), dict(block=1025), dict(L=-1), dict(dk=129), dict(B=0),
+                dict(eps=-1.0), dict(t0=2 ** 31 - 100)):
+        assert _prefill(kdn, **bad) == c["KDN_ERR_BAD_SHAPE"], bad
+    assert _prefill(kdn, cc=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _prefill(kdn, m=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _prefill(kdn, L=0, m=None) == c["KDN_OK"]          # nothing to do, nothing touched
+    assert _prefill(kdn) == c["KDN_ERR_WORKSPACE"]
+    assert _prefill(kdn, ws=P, wsb=need - 1) == c["KDN_ERR_WORKSPACE"]
+    assert _prefill(kdn, ws=P + 8, wsb=need) == c["KDN_ERR_WORKSPACE"]

@@ -208,6 +208,38 @@ def test_full_kalman_small(kdn, orc):
     assert_close(got["cov"], ref["cov"], TOL_F32, "full P")
 
 
+@pytest.mark.parametrize("mode,resid,dtype,dk", [("delta", "gated", "bf16", 128),
+                                                 ("delta", "gated", "f32", 128),
+                                                 ("delta", "plain", "bf16", 128),
+                                                 ("diag", "gated", "bf16", 128),
+                                                 ("iso", "gated", "f32", 64),
+                                                 ("full", "gated", "f32", 32)])
+def test_write_scores(kdn, orc, mode, resid, dtype, dk):
+    """Per-token write scores m_t = ||b_t e_t^T||_F (A Hippocampus for Linear
+    Attention, sec. 3.3 eq. (6)) emitted by the scan, against the oracle's."""
+    import torch
+    inp = workloads.scan_inputs(2, 2, 200, dk, 64, seed=110, dtype=dtype, with_r=True)
+    cov0 = {"diag": np.ones((2, 2, dk), np.float32), "iso": np.ones((2, 2), np.float32),
+            "full": np.broadcast_to(np.eye(dk, dtype=np.float32), (2, 2, dk, dk)).copy()}.get(mode)
+    qvar = 0.5 if mode != "delta" else 0.0
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"],
+                   r=inp["r"] if mode != "delta" else None, cov0=cov0, q_noise_var=qvar,
+                   mode=mode, resid=resid)
+    q, k, v = (dev_tensor(inp[n], dtype) for n in ("q", "k", "v"))
+    cin = dev_tensor(cov0) if cov0 is not None else None
+    cout = torch.empty_like(cin) if cin is not None else None
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    for chunk in ((64,) if dtype == "bf16" else (32, 64)):
+        log(f"scores {mode}/{resid} {dtype} chunk {chunk}")
+        o, m = kdn.kdn_scan_fwd(q, k, v, alpha=dev_tensor(inp["alpha"]), beta=dev_tensor(inp["beta"]),
+                                r=dev_tensor(inp["r"]) if mode != "delta" else None, cov_in=cin,
+                                cov_out=cout, q_noise_var=qvar, chunk=chunk, mode=mode,
+                                resid=resid, m=True)
+        torch.cuda.synchronize()
+        assert_close(host(m), ref["m"], tol, f"m {mode}")
+        assert_close(host(o), ref["o"], tol, f"o {mode}")
+
+
 # --------------------------------------------------------------- full-size workloads
 
 def _sampled_check(kdn, orc, name, heads, mode="delta", check_state=True):
