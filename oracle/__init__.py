@@ -28,7 +28,9 @@ _SRC = os.path.join(_HERE, "kdn_oracle.c")
 _LIB = os.path.join(_HERE, "libkdn_oracle.so")
 
 MODES = {"delta": 0, "diag": 1, "full": 2, "iso": 3}
-RESIDS = {"gated": 0, "plain": 1}
+RESIDS = {"gated": 0, "plain": 1, "noerase": 2}
+SCORES = {"write": 0, "resid": 1, "value": 2}
+POLICIES = {"score": 0, "recency": 1}
 
 
 def build(force: bool = True) -> str:
@@ -53,12 +55,12 @@ def _load():
         P = ctypes.c_void_p
         i = ctypes.c_int
         d = ctypes.c_double
-        lib.oracle_scan.argtypes = [i, i, i, i, i, P, P, P, P, P, P, P, d, P, i, i, P, P]
+        lib.oracle_scan.argtypes = [i, i, i, i, i, P, P, P, P, P, P, P, d, P, i, i, i, P, P]
         lib.oracle_scan.restype = i
-        lib.oracle_hola_step.argtypes = [i, i, i, i, i, P, P, P, P, i, P, P, P, P, P, P, d, P]
+        lib.oracle_hola_step.argtypes = [i, i, i, i, i, P, P, P, P, i, P, P, P, P, P, P, d, i, P]
         lib.oracle_hola_step.restype = i
         lib.oracle_hola_prefill.argtypes = [i, i, i, i, i, i, i, P, P, P, P, i, P, P, P, P, P, P,
-                                            d, P]
+                                            d, i, P]
         lib.oracle_hola_prefill.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
@@ -79,7 +81,8 @@ def _ptr(x):
 
 
 def scan(q, k, v, alpha=None, beta=None, r=None, cov0=None, q_noise_var: float = 0.0,
-         S0=None, mode: str = "delta", resid: str = "gated", want_m: bool = True) -> dict:
+         S0=None, mode: str = "delta", resid: str = "gated", want_m: bool = True,
+         score: str = "write") -> dict:
     """Sequential fp64 scan. q, k: [B,H,L,dk]; v: [B,H,L,dv]; alpha/beta/r: [B,H,L].
     cov0: [B,H,dk] (diag), [B,H,dk,dk] (full) or [B,H] (iso). S0: [B,H,dk,dv] (default zeros).
     Returns dict(o [B,H,L,dv], S [B,H,dk,dv], cov, m [B,H,L]) in float64."""
@@ -103,7 +106,7 @@ def scan(q, k, v, alpha=None, beta=None, r=None, cov0=None, q_noise_var: float =
     m = np.zeros((B, H, L)) if want_m else None
     rc = _load().oracle_scan(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                              _ptr(beta), _ptr(r), _ptr(cov), float(q_noise_var), _ptr(S),
-                             MODES[mode], RESIDS[resid], _ptr(o), _ptr(m))
+                             MODES[mode], RESIDS[resid], SCORES[score], _ptr(o), _ptr(m))
     if rc != 0:
         raise ValueError(f"oracle_scan rejected the arguments (status {rc})")
     return dict(o=o, S=S, cov=cov, m=m)
@@ -112,8 +115,9 @@ def scan(q, k, v, alpha=None, beta=None, r=None, cov0=None, q_noise_var: float =
 class HolaCache:
     """Oracle-side HOLA cache state for [B, H] heads with capacity w."""
 
-    def __init__(self, B: int, H: int, dk: int, dv: int, w: int):
+    def __init__(self, B: int, H: int, dk: int, dv: int, w: int, policy: str = "score"):
         self.B, self.H, self.dk, self.dv, self.w = B, H, dk, dv, w
+        self.policy = POLICIES[policy]
         self.k = np.zeros((B, H, w, dk), np.float32)
         self.v = np.zeros((B, H, w, dv), np.float32)
         self.m = np.zeros((B, H, w), np.float32)
@@ -130,7 +134,7 @@ class HolaCache:
         _load().oracle_hola_step(self.B, self.H, self.dk, self.dv, self.w, _ptr(q), _ptr(k),
                                  _ptr(v), _ptr(m), int(t), _ptr(self.k), _ptr(self.v),
                                  _ptr(self.m), _ptr(self.pos), _ptr(self.count), _ptr(sink),
-                                 float(rms_eps), _ptr(o))
+                                 float(rms_eps), self.policy, _ptr(o))
         return o
 
 
@@ -149,7 +153,7 @@ class HolaCache:
         rc = _load().oracle_hola_prefill(B, H, L, dk, self.dv, self.w, int(block), _ptr(q), _ptr(k),
                                          _ptr(v), _ptr(m), int(t0), _ptr(self.k), _ptr(self.v),
                                          _ptr(self.m), _ptr(self.pos), _ptr(self.count), _ptr(sink),
-                                         float(rms_eps), _ptr(o))
+                                         float(rms_eps), self.policy, _ptr(o))
         if rc != 0:
             raise ValueError(f"oracle_hola_prefill rejected the arguments (status {rc})")
         return o
@@ -157,20 +161,21 @@ class HolaCache:
 
 def decode_run(steps_inputs, B: int, H: int, dk: int, dv: int, w: int, mode: str = "delta",
                resid: str = "gated", S0=None, cov0=None, r_steps=None, q_noise_var: float = 0.0,
-               sink_logit=None, rms_eps: float = 1e-6, t0: int = 0, cache: HolaCache = None):
+               sink_logit=None, rms_eps: float = 1e-6, t0: int = 0, cache: HolaCache = None,
+               score: str = "write", policy: str = "score"):
     """Decode a sequence of single tokens: per step, the recurrence (one token of
     ``scan``) then the HOLA cache read/insert with that token's score.
     ``steps_inputs`` yields dicts with q, k, v ([B,H,d]) and alpha, beta ([B,H]).
     Returns (list of o, list of o_cache, list of m, final S, final cov, cache)."""
     S = np.zeros((B, H, dk, dv)) if S0 is None else np.array(S0, dtype=np.float64)
     cov = None if cov0 is None else np.array(cov0, dtype=np.float64)
-    cache = cache or HolaCache(B, H, dk, dv, w)
+    cache = cache or HolaCache(B, H, dk, dv, w, policy)
     outs, couts, ms = [], [], []
     for i, inp in enumerate(steps_inputs):
         rr = None if r_steps is None else r_steps[i][..., None]
         res = scan(inp["q"][:, :, None], inp["k"][:, :, None], inp["v"][:, :, None],
                    alpha=inp["alpha"][..., None], beta=inp["beta"][..., None], r=rr,
-                   cov0=cov, q_noise_var=q_noise_var, S0=S, mode=mode, resid=resid)
+                   cov0=cov, q_noise_var=q_noise_var, S0=S, mode=mode, resid=resid, score=score)
         S, cov = res["S"], res["cov"]
         m = res["m"][..., 0]
         oc = cache.step(inp["q"], inp["k"], inp["v"], m, t0 + i, sink_logit, rms_eps)

@@ -47,6 +47,12 @@
 #define ORC_ISO 3
 #define ORC_GATED 0
 #define ORC_PLAIN 1
+#define ORC_NOERASE 2
+#define ORC_SCORE_WRITE 0
+#define ORC_SCORE_RESID 1
+#define ORC_SCORE_VALUE 2
+#define ORC_EVICT_SCORE 0
+#define ORC_EVICT_RECENCY 1
 
 /*
  * One (batch, head) sequence of the write/read recurrence.
@@ -56,6 +62,10 @@
  *     S_t = alpha_t S_{t-1} + beta_t k_t e_t^T
  * Plain form (resid PLAIN; no decay inside the residual, as the delta rule is
  * usually written): e_t = v_t - S_{t-1}^T k_t, same update.
+ * No-erase form (resid NOERASE): e_t = v_t, i.e. S_t = alpha_t S_{t-1} +
+ * beta_t k_t v_t^T, the decayed linear-attention write that the delta rule
+ * extends with its erase term [HOLA sec. 3.5; the filter family of MBD
+ * abstract].
  *
  * Kalman write (modes DIAG and FULL) [KDN abstract; MBD abstract]: memory is a
  * linear-Gaussian state-space model. Reading R2: v_t = S_t^T k_t + n_t with
@@ -88,13 +98,16 @@
  * Score m_t = ||Delta_t||_F with Delta_t = b e^T the token's rank-1 write
  * [HOLA sec. 3.3, eq. (6)]: ||b|| ||e||. In DELTA mode the score is
  * beta_t ||e_t|| exactly as eq. (6) states it (equal to ||b|| ||e|| for unit
- * keys).
+ * keys). The page's ablation of the score [HOLA sec. 3.3, "versus recency";
+ * sec. 4.5] replaces it by the residual alone (score RESID: ||e_t||) or the
+ * write strength alone (score VALUE: beta_t ||v_t||, ||b_t|| ||v_t|| for a
+ * Kalman gain).
  */
 static void scan_one(int L, int dk, int dv,
                      const float *q, const float *k, const float *v,
                      const float *alpha, const float *beta, const float *r,
                      double *cov, double qvar, double *S,
-                     int mode, int resid, double *o, double *m,
+                     int mode, int resid, int score, double *o, double *m,
                      double *work)
 {
     double *e = work;              /* dv */
@@ -124,7 +137,7 @@ static void scan_one(int L, int dk, int dv,
         }
 
         /* residual */
-        const double scale = (resid == ORC_PLAIN) ? 1.0 : a;
+        const double scale = (resid == ORC_PLAIN) ? 1.0 : (resid == ORC_NOERASE ? 0.0 : a);
         for (int j = 0; j < dv; ++j) {
             double pred = 0.0;
             for (int i = 0; i < dk; ++i) pred += S[(size_t)i * dv + j] * (double)kt[i];
@@ -184,15 +197,22 @@ static void scan_one(int L, int dk, int dv,
 
         /* write-magnitude score */
         if (m) {
-            double ee = 0.0;
-            for (int j = 0; j < dv; ++j) ee += e[j] * e[j];
+            double ee = 0.0, vv = 0.0;
+            for (int j = 0; j < dv; ++j) {
+                ee += e[j] * e[j];
+                vv += (double)vt[j] * (double)vt[j];
+            }
+            double ws;  /* the write strength */
             if (mode == ORC_DELTA) {
-                m[t] = (double)beta[t] * sqrt(ee);
+                ws = (double)beta[t];
             } else {
                 double bb = 0.0;
                 for (int i = 0; i < dk; ++i) bb += b[i] * b[i];
-                m[t] = sqrt(bb) * sqrt(ee);
+                ws = sqrt(bb);
             }
+            m[t] = score == ORC_SCORE_RESID ? sqrt(ee)
+                 : score == ORC_SCORE_VALUE ? ws * sqrt(vv)
+                                            : ws * sqrt(ee);
         }
     }
 }
@@ -212,10 +232,12 @@ int oracle_scan(int B, int H, int L, int dk, int dv,
                 const float *q, const float *k, const float *v,
                 const float *alpha, const float *beta, const float *r,
                 double *cov, double q_noise_var, double *S,
-                int mode, int resid, double *o, double *m)
+                int mode, int resid, int score, double *o, double *m)
 {
     if (mode != ORC_DELTA && mode != ORC_DIAG && mode != ORC_FULL && mode != ORC_ISO) return -1;
+    if (resid != ORC_GATED && resid != ORC_PLAIN && resid != ORC_NOERASE) return -1;
     if (resid == ORC_PLAIN && mode != ORC_DELTA) return -1;
+    if (score < ORC_SCORE_WRITE || score > ORC_SCORE_VALUE) return -1;
     if (mode == ORC_DELTA && !beta) return -1;
     if (mode != ORC_DELTA && !cov) return -1;
     const int BH = B * H;
@@ -235,7 +257,7 @@ int oracle_scan(int B, int H, int L, int dk, int dv,
         if (mode == ORC_ISO) covp = cov + bh;
         scan_one(L, dk, dv, q + tok * dk, k + tok * dk, v + tok * dv,
                  alpha ? alpha + tok : NULL, beta ? beta + tok : NULL, r ? r + tok : NULL,
-                 covp, q_noise_var, S + (size_t)bh * dk * dv, mode, resid,
+                 covp, q_noise_var, S + (size_t)bh * dk * dv, mode, resid, score,
                  o + tok * dv, m ? m + tok : NULL, work);
         free(work);
     }
@@ -259,6 +281,9 @@ int oracle_scan(int B, int H, int L, int dk, int dv,
  * broken by the smaller position: while it has free slots the token is
  * appended; otherwise it replaces the slot with the smallest (score, then
  * largest position) if and only if its score is strictly larger.
+ * Policy RECENCY is the page's matched control [HOLA sec. 4.5]: the cache
+ * keeps the w most recent tokens, so a full cache always replaces the slot
+ * with the smallest position.
  *
  *   q, k: [B,H,dk] float32; v: [B,H,dv] float32; m: [B,H] float64.
  *   cache_k [B,H,w,dk], cache_v [B,H,w,dv] float32 (exact copies);
@@ -269,7 +294,7 @@ int oracle_hola_step(int B, int H, int dk, int dv, int w,
                      const float *q, const float *k, const float *v, const double *m,
                      int t, float *cache_k, float *cache_v, float *cache_m,
                      int32_t *cache_pos, int32_t *count, const float *sink_logit,
-                     double rms_eps, double *o_cache)
+                     double rms_eps, int policy, double *o_cache)
 {
     const int BH = B * H;
 #pragma omp parallel for schedule(static)
@@ -322,6 +347,10 @@ int oracle_hola_step(int B, int H, int dk, int dv, int w,
         if (n < w) {
             slot = n;
             count[bh] = n + 1;
+        } else if (policy == ORC_EVICT_RECENCY) {
+            int oldest = 0;
+            for (int j = 1; j < w; ++j) oldest = cp[j] < cp[oldest] ? j : oldest;
+            slot = oldest;
         } else {
             int worst = 0;
             for (int j = 1; j < w; ++j) {
@@ -362,6 +391,7 @@ int oracle_num_threads(void)
  * w best of (cache, block) by score descending, then position ascending, on
  * float32 scores (reading S10). With block = 1 this is the decode step's
  * read-then-insert. On return slots 0 .. count-1 hold the cache in that order.
+ * Policy RECENCY keeps the w most recent tokens instead (most recent first).
  *
  *   q, k: [B,H,L,dk] float32; v: [B,H,L,dv] float32; m: [B,H,L] float64.
  *   cache_*: as oracle_hola_step, in = the cache before the prompt, out = after.
@@ -369,8 +399,9 @@ int oracle_num_threads(void)
  */
 typedef struct { float m; int32_t pos; int src; } orc_entry; /* src >= 0: token, < 0: slot -1-src */
 
-static int orc_entry_before(const orc_entry *a, const orc_entry *b)
+static int orc_entry_before(const orc_entry *a, const orc_entry *b, int policy)
 {
+    if (policy == ORC_EVICT_RECENCY) return a->pos > b->pos;
     return a->m > b->m || (a->m == b->m && a->pos < b->pos);
 }
 
@@ -378,7 +409,7 @@ int oracle_hola_prefill(int B, int H, int L, int dk, int dv, int w, int block,
                         const float *q, const float *k, const float *v, const double *m,
                         int t0, float *cache_k, float *cache_v, float *cache_m,
                         int32_t *cache_pos, int32_t *count, const float *sink_logit,
-                        double rms_eps, double *o_cache)
+                        double rms_eps, int policy, double *o_cache)
 {
     if (block < 1 || w < 1) return -1;
     const int BH = B * H;
@@ -458,7 +489,7 @@ int oracle_hola_prefill(int B, int H, int L, int dk, int dv, int w, int block,
             for (int a = 1; a < nc; ++a) {   /* insertion sort, (m desc, pos asc) */
                 orc_entry x = cand[a];
                 int b = a - 1;
-                while (b >= 0 && orc_entry_before(&x, &cand[b])) {
+                while (b >= 0 && orc_entry_before(&x, &cand[b], policy)) {
                     cand[b + 1] = cand[b];
                     --b;
                 }

@@ -751,3 +751,80 @@ def test_prefill_final_cache_is_sorted_topw(orc):
             np.testing.assert_array_equal(c.m[0, h], m32[0, h, order])
             np.testing.assert_array_equal(c.k[0, h], k[0, h, order])
             np.testing.assert_array_equal(c.v[0, h], v[0, h, order])
+
+
+# ---------------------------------------------------------------------------
+# Ablation switches: no-erase write, score variants, recency eviction
+# ---------------------------------------------------------------------------
+
+def test_noerase_is_decayed_linear_attention(orc):
+    """A Hippocampus for Linear Attention, sec. 3.5 (the gated delta rule adds an
+    erase term to the decayed outer-product write): without it,
+    S_t = sum_{j<=t} (prod_{j<i<=t} alpha_i) beta_j k_j v_j^T and o_t = S_t^T q_t,
+    written out here directly."""
+    inp = workloads.scan_inputs(2, 2, 60, 8, 5, seed=50, dtype="f32")
+    res = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"],
+                   resid="noerase")
+    a, b = inp["alpha"].astype(np.float64), inp["beta"].astype(np.float64)
+    K, V, Q = (inp[n].astype(np.float64) for n in ("k", "v", "q"))
+    L = a.shape[-1]
+    for t in (0, 17, L - 1):
+        w = np.array([np.prod(a[..., j + 1:t + 1], axis=-1) for j in range(t + 1)])  # [t+1,B,H]
+        S = np.einsum("jbh,bhj,bhjd,bhje->bhde", w, b[..., :t + 1], K[:, :, :t + 1], V[:, :, :t + 1])
+        np.testing.assert_allclose(res["o"][:, :, t], np.einsum("bhde,bhd->bhe", S, Q[:, :, t]),
+                                   rtol=0, atol=1e-12)
+        if t == L - 1:
+            np.testing.assert_allclose(res["S"], S, rtol=0, atol=1e-12)
+    # its write score is beta ||v||
+    np.testing.assert_allclose(res["m"], b * np.linalg.norm(V, axis=-1), rtol=1e-12)
+
+
+def test_score_variants(orc):
+    """A Hippocampus for Linear Attention, sec. 3.3 ("versus recency") and sec.
+    4.5: the ablation scores are the residual alone, ||e_t||, and the write
+    strength alone, beta_t ||v_t||. ||e_t|| is recomputed from the states of
+    the prefix scans (brute force); beta ||v|| from the inputs."""
+    inp = workloads.scan_inputs(1, 2, 25, 8, 6, seed=51, dtype="f32")
+    q, k, v, a, b = (inp[n] for n in ("q", "k", "v", "alpha", "beta"))
+    resid = orc.scan(q, k, v, alpha=a, beta=b, score="resid")["m"]
+    value = orc.scan(q, k, v, alpha=a, beta=b, score="value")["m"]
+    np.testing.assert_allclose(value, b.astype(np.float64) * np.linalg.norm(v.astype(np.float64), axis=-1),
+                               rtol=1e-12)
+    prev = np.zeros((1, 2, 8, 6))
+    for t in range(25):
+        e = v[:, :, t].astype(np.float64) - a[:, :, t, None] * np.einsum("bhde,bhd->bhe", prev, k[:, :, t])
+        np.testing.assert_allclose(resid[:, :, t], np.linalg.norm(e, axis=-1), rtol=1e-11)
+        prev = orc.scan(q[:, :, :t + 1], k[:, :, :t + 1], v[:, :, :t + 1], alpha=a[..., :t + 1],
+                        beta=b[..., :t + 1])["S"]
+    # Kalman writes: the write strength is the gain's norm
+    r = np.ones_like(a)
+    p0 = np.ones((1, 2, 8))
+    wr = orc.scan(q, k, v, alpha=a, r=r, cov0=p0, mode="diag", score="write")["m"]
+    rs = orc.scan(q, k, v, alpha=a, r=r, cov0=p0, mode="diag", score="resid")["m"]
+    va = orc.scan(q, k, v, alpha=a, r=r, cov0=p0, mode="diag", score="value")["m"]
+    np.testing.assert_allclose(va, wr / rs * np.linalg.norm(v.astype(np.float64), axis=-1), rtol=1e-11)
+
+
+def test_recency_eviction_keeps_the_last_w(orc):
+    """A Hippocampus for Linear Attention, sec. 4.5 (the matched control keeps the
+    most recent w tokens): decode-step and prompt versions, against brute force,
+    and the prompt version with unit blocks against the decode steps."""
+    rng = _rng(52)
+    B, H, dk, dv, w, L = 1, 2, 4, 3, 7, 40
+    q = rng.standard_normal((B, H, L, dk)).astype(np.float32)
+    k = rng.standard_normal((B, H, L, dk)).astype(np.float32)
+    v = rng.standard_normal((B, H, L, dv)).astype(np.float32)
+    m = rng.uniform(0, 1, (B, H, L))
+    a = orc.HolaCache(B, H, dk, dv, w, policy="recency")
+    outs = []
+    for t in range(L):
+        outs.append(a.step(q[:, :, t], k[:, :, t], v[:, :, t], m[:, :, t], t))
+        n = a.count[0, 0]
+        assert sorted(a.pos[0, 0, :n].tolist()) == list(range(max(0, t + 1 - w), t + 1))
+    for block in (1, 6, 64):
+        c = orc.HolaCache(B, H, dk, dv, w, policy="recency")
+        o = c.prefill(q, k, v, m, 0, block)
+        np.testing.assert_array_equal(c.pos[0, 0], np.arange(L - 1, L - 1 - w, -1))
+        np.testing.assert_array_equal(c.k[0, 1], k[0, 1, L - 1:L - 1 - w:-1])
+        if block == 1:
+            np.testing.assert_allclose(o, np.stack(outs, 2), rtol=0, atol=1e-13)
