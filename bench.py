@@ -11,7 +11,8 @@ resident in HBM before timing starts.
 Extra fields: the roofline of the dominant (state) kernel, timed on its own
 stream with events around its phase; the fp64 oracle timed on a bounded
 sample on the host cores; and (unless --quick) the decode + HOLA cache step,
-the diagonal and isotropic Kalman scans and the long-context scan.
+the HOLA prompt cache after a scan with write scores, the diagonal and
+isotropic Kalman scans and the long-context scan.
 """
 from __future__ import annotations
 
@@ -130,6 +131,62 @@ def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True):
         res["prepare_ms"] = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)) / steps
         res["state_ms"] = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)) / steps
     return res
+
+
+def bench_prefill(kdn, torch, steps, warmup, block=256, w=64):
+    """The gated workload as a prompt with the HOLA cache: the scan with write
+    scores, then the block-by-block cache (blocks of 256, w = 64)."""
+    import workloads
+    cfg = workloads.WORKLOADS["gated"]
+    B, H, L, dk, dv, C = cfg["B"], cfg["H"], cfg["L"], cfg["dk"], cfg["dv"], cfg["chunk"]
+    inp = workloads.named_scan_inputs("gated")
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(inp[n]).to(dev).to(torch.bfloat16) for n in ("q", "k", "v")}
+    alpha = torch.from_numpy(inp["alpha"]).to(dev)
+    beta = torch.from_numpy(inp["beta"]).to(dev)
+    del inp
+    o = torch.empty((B, H, L, dv), dtype=torch.float32, device=dev)
+    m = torch.empty((B, H, L), dtype=torch.float32, device=dev)
+    oc = torch.empty_like(o)
+    ws = torch.empty(kdn.kdn_scan_workspace_size(B, H, L, dk, dv, C, "delta", kdn.BF16, True),
+                     dtype=torch.uint8, device=dev)
+    pws = torch.empty(kdn.hola_prefill_workspace_size(B, H, L, dk, dv, w, block), dtype=torch.uint8,
+                      device=dev)
+    cache = kdn.HolaCache(B, H, dk, dv, w)
+
+    def scan():
+        kdn.kdn_scan_fwd(t["q"], t["k"], t["v"], alpha=alpha, beta=beta, o=o, chunk=C,
+                         workspace=ws, m=m)
+
+    def prefill():
+        cache.count.zero_()
+        kdn.hola_prefill(t["q"], t["k"], t["v"], m, 0, cache, block=block, o_cache=oc,
+                         workspace=pws)
+
+    for _ in range(warmup):
+        scan()
+        prefill()
+    torch.cuda.synchronize()
+    ev = _events(torch, 3 * steps)
+    for i in range(steps):
+        ev[3 * i].record()
+        scan()
+        ev[3 * i + 1].record()
+        prefill()
+        ev[3 * i + 2].record()
+    torch.cuda.synchronize()
+    s_ms = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)) / steps
+    p_ms = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)) / steps
+    # the read's algorithmic work: each query against w cached keys plus the causal
+    # part of its block, 2 (d_k + d_v) flops per key
+    keys = L * w + sum(min(block, L - j) * (min(block, L - j) + 1) // 2 for j in range(0, L, block))
+    flops = B * H * keys * 2 * (dk + dv)
+    return dict(scan_with_scores_ms=round(s_ms, 5), prefill_ms=round(p_ms, 5),
+                tokens_per_s=round(B * L / ((s_ms + p_ms) * 1e-3), 1), block=block, w=w,
+                read_gflop=round(flops / 1e9, 2),
+                read_tflops=round(flops / (p_ms * 1e-3) / 1e12, 2),
+                config="gated delta scan with write scores, then the HOLA prompt cache "
+                       f"(blocks of {block}, w = {w}), B=4 H=16 L=4096 d=128")
 
 
 def bench_decode(kdn, torch, steps, warmup):
@@ -272,6 +329,8 @@ def main():
     if not args.quick:
         extra = {}
         extra["decode"] = bench_decode(kdn, torch, steps=max(8, args.steps), warmup=args.warmup)
+        extra["prompt_cache"] = bench_prefill(kdn, torch, steps=max(2, args.steps // 4), warmup=1)
+        torch.cuda.empty_cache()
         for key, name, mode in (("kdn_diag", "kdn_diag", "diag"), ("kdn_iso", "kdn_diag", "iso"),
                                 ("long", "long", "delta")):
             r = bench_scan(kdn, torch, name, max(2, args.steps // 4), 1, mode=mode, per_phase=True)

@@ -29,7 +29,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdn.so")
 
 F32, BF16 = 0, 1
 MODES = {"delta": 0, "diag": 1, "full": 2, "iso": 3}
-RESIDS = {"gated": 0, "plain": 1}
+RESIDS = {"gated": 0, "plain": 1, "noerase": 2}
+SCORES = {"write": 0, "resid": 1, "value": 2}
+POLICIES = {"score": 0, "recency": 1}
 PHASES = {"all": 0, "prepare": 1, "state": 2}
 
 
@@ -52,20 +54,20 @@ def _load():
     L.kdn_version.restype = I
     L.kdn_scan_workspace_size.argtypes = [I, I, I, I, I, I, I, I, I]
     L.kdn_scan_workspace_size.restype = SZ
-    L.kdn_scan_fwd.argtypes = [P, P, P, I, P, P, P, P, P, F, P, P, P, I, P,
+    L.kdn_scan_fwd.argtypes = [P, P, P, I, P, P, P, P, P, F, P, P, P, I, P, I,
                                I, I, I, I, I, I, I, I, P, SZ, P]
     L.kdn_scan_fwd.restype = I
     L.kdn_scan_fwd_phase.argtypes = [I] + L.kdn_scan_fwd.argtypes
     L.kdn_scan_fwd_phase.restype = I
-    L.kdn_step_decode.argtypes = [P, P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, P]
+    L.kdn_step_decode.argtypes = [P, P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P]
     L.kdn_step_decode.restype = I
     L.hola_cache_update.argtypes = [P, P, P, P, ctypes.c_int32, P, P, P, P, P, P, P, F,
-                                    I, I, I, I, I, P]
+                                    I, I, I, I, I, I, P]
     L.hola_cache_update.restype = I
     L.hola_prefill_workspace_size.argtypes = [I, I, I, I, I, I, I]
     L.hola_prefill_workspace_size.restype = SZ
     L.hola_prefill.argtypes = [P, P, P, I, P, ctypes.c_int32, I, P, P, P, P, P, P, P, F,
-                               I, I, I, I, I, I, P, SZ, P]
+                               I, I, I, I, I, I, I, P, SZ, P]
     L.hola_prefill.restype = I
     return L
 
@@ -134,14 +136,15 @@ def _dtype_code(dt):
 def kdn_scan_fwd(q, k, v, alpha=None, beta=None, r=None, cov_in=None, cov_out=None,
                  q_noise_var: float = 0.0, state_in=None, state_out=None, o=None, out_dtype=None,
                  chunk: int = 64, mode: str = "delta", resid: str = "gated", workspace=None,
-                 stream=None, phase: str = "all", m=None):
+                 stream=None, phase: str = "all", m=None, score: str = "write"):
     """Chunkwise scan. q, k: [B,H,L,d_k]; v: [B,H,L,d_v] (bf16 or float32, same dtype);
     alpha/beta/r: [B,H,L] float32; cov_in/cov_out: [B,H,d_k] (diag), [B,H,d_k,d_k]
     (full) or [B,H] (iso) float32; state_in/state_out: [B,H,d_k,d_v] float32. Returns o [B,H,L,d_v]
     (float32 unless ``out_dtype`` or ``o`` says otherwise). ``phase`` "prepare" /
     "state" runs one half of the call (kdn_scan_fwd_phase); both halves must see
     the same ``workspace`` tensor. ``m`` ([B,H,L] float32 tensor, or True to
-    allocate one) receives the write scores; the call then returns (o, m)."""
+    allocate one) receives the write scores of kind ``score`` ("write", "resid",
+    "value"); the call then returns (o, m)."""
     torch = _torch()
     _check(q, "q", (torch.bfloat16, torch.float32))
     B, H, L, dk = q.shape
@@ -176,8 +179,8 @@ def kdn_scan_fwd(q, k, v, alpha=None, beta=None, r=None, cov_in=None, cov_out=No
     st = lib.kdn_scan_fwd_phase(PHASES[phase], _ptr(q), _ptr(k), _ptr(v), in_code, _ptr(alpha),
                                 _ptr(beta), _ptr(r), _ptr(cov_in), _ptr(cov_out),
                                 float(q_noise_var), _ptr(state_in), _ptr(state_out), _ptr(o),
-                                _dtype_code(o.dtype), _ptr(m) if want_m else None, B, H, L, dk,
-                                dv, int(chunk), mcode, rcode, _ptr(workspace), wbytes,
+                                _dtype_code(o.dtype), _ptr(m) if want_m else None, SCORES[score],
+                                B, H, L, dk, dv, int(chunk), mcode, rcode, _ptr(workspace), wbytes,
                                 _stream(stream))
     if st != 0:
         raise KdnError(st, "kdn_scan_fwd")
@@ -188,7 +191,7 @@ def kdn_scan_fwd(q, k, v, alpha=None, beta=None, r=None, cov_in=None, cov_out=No
 
 def kdn_step_decode(q, k, v, alpha, beta, state, o=None, m=None, r=None, cov=None,
                     q_noise_var: float = 0.0, mode: str = "delta", resid: str = "gated",
-                    stream=None):
+                    stream=None, score: str = "write"):
     """One token per head. q, k: [B,H,d_k]; v: [B,H,d_v]; alpha, beta, r: [B,H];
     state [B,H,d_k,d_v] and cov [B,H,d_k] (diag) or [B,H] (iso) are updated in place.
     Returns (o [B,H,d_v], m [B,H])."""
@@ -213,7 +216,8 @@ def kdn_step_decode(q, k, v, alpha, beta, state, o=None, m=None, r=None, cov=Non
     _check(m, "m", f, (B, H), dev)
     st = lib.kdn_step_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(r),
                              _ptr(cov), float(q_noise_var), _ptr(state), _ptr(o), _ptr(m),
-                             B, H, dk, dv, MODES[mode], RESIDS[resid], _stream(stream))
+                             SCORES[score], B, H, dk, dv, MODES[mode], RESIDS[resid],
+                             _stream(stream))
     if st != 0:
         raise KdnError(st, "kdn_step_decode")
     return o, m
@@ -224,9 +228,11 @@ def kdn_step_decode(q, k, v, alpha, beta, state, o=None, m=None, r=None, cov=Non
 class HolaCache:
     """Device tensors of a HOLA exact cache for [B, H] heads with capacity w."""
 
-    def __init__(self, B: int, H: int, d_k: int, d_v: int, w: int = 64, device="cuda"):
+    def __init__(self, B: int, H: int, d_k: int, d_v: int, w: int = 64, device="cuda",
+                 policy: str = "score"):
         torch = _torch()
         self.B, self.H, self.d_k, self.d_v, self.w = B, H, d_k, d_v, w
+        self.policy = POLICIES[policy]
         self.k = torch.zeros((B, H, w, d_k), dtype=torch.float32, device=device)
         self.v = torch.zeros((B, H, w, d_v), dtype=torch.float32, device=device)
         self.m = torch.zeros((B, H, w), dtype=torch.float32, device=device)
@@ -254,7 +260,7 @@ def hola_cache_update(q, k, v, m, t: int, cache: HolaCache, sink_logit=None, o_c
     st = lib.hola_cache_update(_ptr(q), _ptr(k), _ptr(v), _ptr(m), int(t), _ptr(cache.k),
                                _ptr(cache.v), _ptr(cache.m), _ptr(cache.pos), _ptr(cache.count),
                                _ptr(sink_logit), _ptr(o_cache), float(rms_eps), B, H, dk, dv, w,
-                               _stream(stream))
+                               cache.policy, _stream(stream))
     if st != 0:
         raise KdnError(st, "hola_cache_update")
     return o_cache
@@ -286,7 +292,7 @@ def hola_prefill(q, k, v, m, t0: int, cache: HolaCache, block: int = 256, sink_l
     st = lib.hola_prefill(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(m), int(t0),
                           int(block), _ptr(cache.k), _ptr(cache.v), _ptr(cache.m),
                           _ptr(cache.pos), _ptr(cache.count), _ptr(sink_logit), _ptr(o_cache),
-                          float(rms_eps), B, H, L, dk, dv, w, _ptr(workspace),
+                          float(rms_eps), B, H, L, dk, dv, w, cache.policy, _ptr(workspace),
                           workspace.numel() * workspace.element_size(), _stream(stream))
     if st != 0:
         raise KdnError(st, "hola_prefill")

@@ -44,7 +44,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
                                                     float* __restrict__ cov, float qvar,
                                                     float* __restrict__ state,
                                                     float* __restrict__ o, float* __restrict__ m,
-                                                    int dk, int dv, int gmode, int plain) {
+                                                    int dk, int dv, int gmode, int resid,
+                                                    int score_kind) {
   __shared__ float sk[128], sq[128], sv[128], sb[128], se[128];
   __shared__ float red1[8][128], red2[8][128];
   __shared__ float scratch[4];
@@ -52,6 +53,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
   const int cg = tid & 31, rg = tid >> 5;
 
   const bool diag = gmode == 1, iso = gmode == 2;
+  const bool plain = resid == 1, noerase = resid == 2;
   const float a = alpha ? alpha[bh] : 1.f;
   float bscale = 1.f, vscale = 1.f;
   if (gmode == 0) {
@@ -144,15 +146,21 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
       pred += red1[g][tid];
       qp += red2[g][tid];
     }
-    e = sv[tid] - a * pred;
+    e = noerase ? sv[tid] : sv[tid] - a * pred;
     oq = a * qp;
     se[tid] = e;
   }
   const float bq = block_sum(tid < dk ? sb[tid] * sq[tid] : 0.f, scratch);
   const float ee = block_sum(e * e, scratch);
   const float bb = gmode ? block_sum(tid < dk ? sb[tid] * sb[tid] : 0.f, scratch) : 0.f;
+  const float vv = score_kind == 2 ? block_sum(tid < dv ? sv[tid] * sv[tid] : 0.f, scratch) : 0.f;
   if (tid < dv) o[(size_t)bh * dv + tid] = fmaf(bq, e, oq);
-  if (m && tid == 0) m[bh] = gmode ? sqrtf(bb) * sqrtf(ee) : bscale * sqrtf(ee);
+  if (m && tid == 0) {
+    // the plain form runs as the gated one with (beta / alpha, alpha v): its
+    // residual and value are alpha times the plain ones, its beta 1 / alpha times
+    const float ws = gmode ? sqrtf(bb) : bscale;
+    m[bh] = score_kind == 1 ? sqrtf(ee) / vscale : (score_kind == 2 ? ws * sqrtf(vv) : ws * sqrtf(ee));
+  }
 
   // S <- alpha S + b e^T
 #pragma unroll
@@ -185,14 +193,14 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
 hipError_t launch_decode(const float* q, const float* k, const float* v, const float* alpha,
                          const float* beta, const float* r, float* cov, float q_noise_var,
                          float* state, float* o, float* m, int BH, int dk, int dv, int gmode,
-                         int plain, hipStream_t s) {
+                         int resid, int score_kind, hipStream_t s) {
   const bool vec = (dv % 4 == 0) && ((reinterpret_cast<uintptr_t>(state) & 15) == 0);
   if (vec)
     hipLaunchKernelGGL(decode_kernel<true>, dim3(BH), dim3(NT), 0, s, q, k, v, alpha, beta, r, cov,
-                       q_noise_var, state, o, m, dk, dv, gmode, plain);
+                       q_noise_var, state, o, m, dk, dv, gmode, resid, score_kind);
   else
     hipLaunchKernelGGL(decode_kernel<false>, dim3(BH), dim3(NT), 0, s, q, k, v, alpha, beta, r,
-                       cov, q_noise_var, state, o, m, dk, dv, gmode, plain);
+                       cov, q_noise_var, state, o, m, dk, dv, gmode, resid, score_kind);
   return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@
 // per pass), 16-byte loads. Weighted value sum: lane (rg, cg) accumulates
 // columns of group cg over rows rg, rg + 8, ...; partial sums meet in LDS.
 // Eviction: one wavefront takes the lexicographic minimum of (m, -pos) with
-// shuffles, so the choice is deterministic and uses no atomics.
+// shuffles, so the choice is deterministic and uses no atomics. The recency
+// control of sec. 4.5 evicts the smallest position instead.
 #include "kdn_internal.h"
 
 namespace kdn {
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
                                                   int32_t* __restrict__ cache_count,
                                                   const float* __restrict__ sink_logit,
                                                   float* __restrict__ o_cache, float rms_eps,
-                                                  int H, int dk, int dv, int w) {
+                                                  int H, int dk, int dv, int w, int recency) {
   __shared__ float sq[128], sk[128], sv[128];
   __shared__ float sl[WMAX + 2];
   __shared__ float red[8][128];
@@ -148,8 +149,9 @@ __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
       float bm = INFINITY;
       int bp = -1, bs = -1;
       for (int j = lane; j < w; j += 64) {
-        const float mj = cache_m[(size_t)bh * w + j];
-        const int pj = cache_pos[(size_t)bh * w + j];
+        // recency: rank by position alone
+        const float mj = recency ? 0.f : cache_m[(size_t)bh * w + j];
+        const int pj = recency ? -cache_pos[(size_t)bh * w + j] : cache_pos[(size_t)bh * w + j];
         if (bs < 0 || mj < bm || (mj == bm && pj > bp)) {
           bm = mj;
           bp = pj;
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
           bs = os;
         }
       }
-      if (mt > bm) slot = bs;
+      if (recency || mt > bm) slot = bs;
     }
     if (lane == 0) sslot = slot;
   }
@@ -194,18 +196,18 @@ __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
 hipError_t launch_hola(const float* q, const float* k, const float* v, const float* m, int32_t t,
                        float* cache_k, float* cache_v, float* cache_m, int32_t* cache_pos,
                        int32_t* cache_count, const float* sink_logit, float* o_cache, float rms_eps,
-                       int B, int H, int dk, int dv, int w, hipStream_t s) {
+                       int B, int H, int dk, int dv, int w, int policy, hipStream_t s) {
   const bool vec = dk % 4 == 0 && dv % 4 == 0 &&
                    ((reinterpret_cast<uintptr_t>(cache_k) | reinterpret_cast<uintptr_t>(cache_v)) &
                     15) == 0;
   if (vec)
     hipLaunchKernelGGL(hola_kernel<true>, dim3(B * H), dim3(NT), 0, s, q, k, v, m, t, cache_k,
                        cache_v, cache_m, cache_pos, cache_count, sink_logit, o_cache, rms_eps, H, dk,
-                       dv, w);
+                       dv, w, policy);
   else
     hipLaunchKernelGGL(hola_kernel<false>, dim3(B * H), dim3(NT), 0, s, q, k, v, m, t, cache_k,
                        cache_v, cache_m, cache_pos, cache_count, sink_logit, o_cache, rms_eps, H,
-                       dk, dv, w);
+                       dk, dv, w, policy);
   return hipGetLastError();
 }
 

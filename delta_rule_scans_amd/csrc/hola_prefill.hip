@@ -31,8 +31,10 @@ constexpr int MAXD = 128;
 
 // Score order: larger score first, then smaller position, then smaller
 // candidate index (only reached when a caller repeats a position). NaN scores
-// rank below every other score.
-__device__ __forceinline__ bool before(float ma, int pa, int ia, float mb, int pb, int ib) {
+// rank below every other score. Recency order: larger position first.
+__device__ __forceinline__ bool before(float ma, int pa, int ia, float mb, int pb, int ib,
+                                       bool recency) {
+  if (recency) return pa != pb ? pa > pb : ia < ib;
   ma = ma == ma ? ma : -INFINITY;
   mb = mb == mb ? mb : -INFINITY;
   if (ma != mb) return ma > mb;
@@ -84,7 +86,7 @@ __global__ __launch_bounds__(NT) void select_kernel(PrefillArgs a) {
       const float mx = cm[x];
       const int px = cp[x];
       int rank = 0;
-      for (int y = 0; y < nc; ++y) rank += before(cm[y], cp[y], y, mx, px, x) ? 1 : 0;
+      for (int y = 0; y < nc; ++y) rank += before(cm[y], cp[y], y, mx, px, x, a.policy == 1) ? 1 : 0;
       if (rank < a.w) {
         nm[rank] = mx;
         np_[rank] = px;

@@ -104,9 +104,9 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
                                   int in_dtype, const float* alpha, const float* beta,
                                   const float* r, const float* cov_in, float* cov_out,
                                   float q_noise_var, const float* state_in, float* state_out,
-                                  void* o, int out_dtype, float* m, int B, int H, int L, int d_k,
-                                  int d_v, int chunk, int mode, int resid, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
+                                  void* o, int out_dtype, float* m, int score_kind, int B, int H,
+                                  int L, int d_k, int d_v, int chunk, int mode, int resid,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
   if (phase != KDN_PHASE_ALL && phase != KDN_PHASE_PREPARE && phase != KDN_PHASE_STATE)
     return KDN_ERR_BAD_MODE;
   const bool do_prep = phase != KDN_PHASE_STATE, do_state = phase != KDN_PHASE_PREPARE;
@@ -115,8 +115,10 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_FULL &&
       mode != KDN_GAIN_ISO)
     return KDN_ERR_BAD_MODE;
-  if (resid != KDN_RESID_GATED && resid != KDN_RESID_PLAIN) return KDN_ERR_BAD_MODE;
-  if (resid == KDN_RESID_PLAIN && mode != KDN_GAIN_DELTA) return KDN_ERR_BAD_MODE;
+  if (resid != KDN_RESID_GATED && resid != KDN_RESID_PLAIN && resid != KDN_RESID_NOERASE)
+    return KDN_ERR_BAD_MODE;
+  if (resid != KDN_RESID_GATED && mode != KDN_GAIN_DELTA) return KDN_ERR_BAD_MODE;
+  if (m && (score_kind < KDN_SCORE_WRITE || score_kind > KDN_SCORE_VALUE)) return KDN_ERR_BAD_MODE;
   if (B < 1 || H < 1 || L < 0 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
     return KDN_ERR_BAD_SHAPE;
   if ((long long)B * H > (1LL << 24)) return KDN_ERR_BAD_SHAPE;
@@ -200,16 +202,23 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   a.dv = d_v;
   a.chunk = chunk;
   a.plain = resid == KDN_RESID_PLAIN ? 1 : 0;
+  a.noerase = resid == KDN_RESID_NOERASE ? 1 : 0;
 
   const bool out_bf16 = out_dtype == KDN_BF16;
-  const bool mfma_ok = use_mfma_path(in_dtype, d_k, d_v, chunk) && aligned16(q) && aligned16(k) &&
-                       aligned16(v) && aligned16(o) && (gains == nullptr || aligned16(gains));
+  // the matrix-core kernels carry the erase term; the no-erase write runs on the
+  // float32 path
+  const bool mfma_ok = use_mfma_path(in_dtype, d_k, d_v, chunk) && !a.noerase && aligned16(q) &&
+                       aligned16(k) && aligned16(v) && aligned16(o) &&
+                       (gains == nullptr || aligned16(gains));
   kdn::ScoreArgs sc{};
   if (m) {
     void* sbuf = static_cast<char*>(workspace) + ws.s_off;
     if (mfma_ok) a.ubuf = sbuf;
     else a.esq = static_cast<float*>(sbuf);
     const int cols = kdn::scan_f32_tile_cols(d_k, chunk);
+    sc.kind = score_kind;
+    sc.v = v;
+    sc.v_bf16 = in_bf16 ? 1 : 0;
     sc.esq = a.esq;
     sc.ubuf = a.ubuf;
     sc.ntiles = mfma_ok ? d_v / 32 : (d_v + cols - 1) / cols;
@@ -245,22 +254,25 @@ KDN_EXPORT int kdn_scan_fwd(const void* q, const void* k, const void* v, int in_
                             const float* alpha, const float* beta, const float* r,
                             const float* cov_in, float* cov_out, float q_noise_var,
                             const float* state_in, float* state_out, void* o, int out_dtype,
-                            float* m, int B, int H, int L, int d_k, int d_v, int chunk, int mode,
-                            int resid, void* workspace, size_t workspace_bytes, void* stream) {
+                            float* m, int score_kind, int B, int H, int L, int d_k, int d_v,
+                            int chunk, int mode, int resid, void* workspace,
+                            size_t workspace_bytes, void* stream) {
   return kdn_scan_fwd_phase(KDN_PHASE_ALL, q, k, v, in_dtype, alpha, beta, r, cov_in, cov_out,
-                            q_noise_var, state_in, state_out, o, out_dtype, m, B, H, L, d_k, d_v,
-                            chunk, mode, resid, workspace, workspace_bytes, stream);
+                            q_noise_var, state_in, state_out, o, out_dtype, m, score_kind, B, H, L,
+                            d_k, d_v, chunk, mode, resid, workspace, workspace_bytes, stream);
 }
 
 KDN_EXPORT int kdn_step_decode(const float* q, const float* k, const float* v, const float* alpha,
                                const float* beta, const float* r, float* cov, float q_noise_var,
-                               float* state, float* o, float* m, int B, int H, int d_k, int d_v,
-                               int mode, int resid, void* stream) {
+                               float* state, float* o, float* m, int score_kind, int B, int H,
+                               int d_k, int d_v, int mode, int resid, void* stream) {
   if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_FULL &&
       mode != KDN_GAIN_ISO)
     return KDN_ERR_BAD_MODE;
-  if (resid != KDN_RESID_GATED && resid != KDN_RESID_PLAIN) return KDN_ERR_BAD_MODE;
-  if (resid == KDN_RESID_PLAIN && mode != KDN_GAIN_DELTA) return KDN_ERR_BAD_MODE;
+  if (resid != KDN_RESID_GATED && resid != KDN_RESID_PLAIN && resid != KDN_RESID_NOERASE)
+    return KDN_ERR_BAD_MODE;
+  if (resid != KDN_RESID_GATED && mode != KDN_GAIN_DELTA) return KDN_ERR_BAD_MODE;
+  if (m && (score_kind < KDN_SCORE_WRITE || score_kind > KDN_SCORE_VALUE)) return KDN_ERR_BAD_MODE;
   if (B < 1 || H < 1 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
     return KDN_ERR_BAD_SHAPE;
   if ((long long)B * H > (1LL << 30)) return KDN_ERR_BAD_SHAPE;
@@ -275,16 +287,16 @@ KDN_EXPORT int kdn_step_decode(const float* q, const float* k, const float* v, c
                                     mode == KDN_GAIN_DIAG  ? 1
                                     : mode == KDN_GAIN_ISO ? 2
                                                            : 0,
-                                    resid == KDN_RESID_PLAIN ? 1 : 0,
-                                    static_cast<hipStream_t>(stream)));
+                                    resid, m ? score_kind : 0, static_cast<hipStream_t>(stream)));
 }
 
 KDN_EXPORT int hola_cache_update(const float* q, const float* k, const float* v, const float* m,
                                  int32_t t, float* cache_k, float* cache_v, float* cache_m,
                                  int32_t* cache_pos, int32_t* cache_count,
                                  const float* sink_logit, float* o_cache, float rms_eps, int B,
-                                 int H, int d_k, int d_v, int w, void* stream) {
+                                 int H, int d_k, int d_v, int w, int policy, void* stream) {
   if (w < 1 || w > kMaxCapacity) return KDN_ERR_BAD_CAPACITY;
+  if (policy != KDN_EVICT_SCORE && policy != KDN_EVICT_RECENCY) return KDN_ERR_BAD_MODE;
   if (B < 1 || H < 1 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
     return KDN_ERR_BAD_SHAPE;
   if ((long long)B * H > (1LL << 30)) return KDN_ERR_BAD_SHAPE;
@@ -293,7 +305,7 @@ KDN_EXPORT int hola_cache_update(const float* q, const float* k, const float* v,
       !o_cache)
     return KDN_ERR_NULL_POINTER;
   return map_hip(kdn::launch_hola(q, k, v, m, t, cache_k, cache_v, cache_m, cache_pos, cache_count,
-                                  sink_logit, o_cache, rms_eps, B, H, d_k, d_v, w,
+                                  sink_logit, o_cache, rms_eps, B, H, d_k, d_v, w, policy,
                                   static_cast<hipStream_t>(stream)));
 }
 
@@ -307,10 +319,11 @@ KDN_EXPORT int hola_prefill(const void* q, const void* k, const void* v, int in_
                             const float* m, int32_t t0, int block, float* cache_k, float* cache_v,
                             float* cache_m, int32_t* cache_pos, int32_t* cache_count,
                             const float* sink_logit, float* o_cache, float rms_eps, int B, int H,
-                            int L, int d_k, int d_v, int w, void* workspace,
+                            int L, int d_k, int d_v, int w, int policy, void* workspace,
                             size_t workspace_bytes, void* stream) {
   if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_ERR_BAD_DTYPE;
   if (w < 1 || w > kMaxCapacity) return KDN_ERR_BAD_CAPACITY;
+  if (policy != KDN_EVICT_SCORE && policy != KDN_EVICT_RECENCY) return KDN_ERR_BAD_MODE;
   if (B < 1 || H < 1 || L < 0 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
     return KDN_ERR_BAD_SHAPE;
   if (block < 1 || block > kMaxPrefillBlock) return KDN_ERR_BAD_SHAPE;
@@ -345,6 +358,7 @@ KDN_EXPORT int hola_prefill(const void* q, const void* k, const void* v, int in_
   a.dk = d_k;
   a.dv = d_v;
   a.w = w;
+  a.policy = policy;
   kdn::prefill_bind_workspace(a, workspace);
   return map_hip(kdn::launch_prefill(a, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream)));
 }

@@ -53,6 +53,7 @@ struct ScanArgs {
   void* o;                // [BH, L, dv]
   int BH, L, dk, dv, chunk;
   int plain;  // 1: plain residual (delta only): b = (beta/alpha) k, v' = alpha v
+  int noerase = 0;  // 1: e = v (no prediction subtracted; float32 path only)
   // Residuals for the write scores, or null: the float32 path writes per-tile
   // sums of e_t^2 to esq [BH, d_v tiles, L]; the matrix-core path writes the
   // residuals themselves (fp16) to ubuf, see scan_mfma_ubuf_bytes.
@@ -91,6 +92,9 @@ size_t scan_mfma_ubuf_bytes(int BH, int L, int dv);
 // beta_t ||k_t|| for the isotropic gain (iso_beta, iso_kk = ||k||^2), and
 // ||g_t|| for the diagonal / full gains (gains [BH, L, dk], fp16 or f32).
 struct ScoreArgs {
+  int kind;  // 0: s ||e||, 1: ||e||, 2: s ||v|| (s: the write scale below)
+  const void* v;  // [BH, L, dv] input values (kind 2)
+  int v_bf16;
   const float* esq;
   const void* ubuf;
   int ntiles;
@@ -129,17 +133,19 @@ hipError_t launch_full_gains(const void* k, bool k_bf16, const float* alpha, con
 // Copy the covariance / state through unchanged (L == 0).
 hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s);
 
-// One decode token per head; gmode 0 = delta, 1 = diagonal, 2 = isotropic gain.
+// One decode token per head; gmode 0 = delta, 1 = diagonal, 2 = isotropic gain;
+// resid 0 gated, 1 plain, 2 no erase; score kind as ScoreArgs::kind.
 hipError_t launch_decode(const float* q, const float* k, const float* v, const float* alpha,
                          const float* beta, const float* r, float* cov, float q_noise_var,
                          float* state, float* o, float* m, int BH, int dk, int dv, int gmode,
-                         int plain, hipStream_t s);
+                         int resid, int score_kind, hipStream_t s);
 
 // HOLA cache read + insert for one decode token per head.
 hipError_t launch_hola(const float* q, const float* k, const float* v, const float* m, int32_t t,
                        float* cache_k, float* cache_v, float* cache_m, int32_t* cache_pos,
                        int32_t* cache_count, const float* sink_logit, float* o_cache,
-                       float rms_eps, int B, int H, int dk, int dv, int w, hipStream_t s);
+                       float rms_eps, int B, int H, int dk, int dv, int w, int policy,
+                       hipStream_t s);
 
 // HOLA cache over a whole prompt in blocks; see hola_prefill.hip.
 struct PrefillArgs {
@@ -157,6 +163,7 @@ struct PrefillArgs {
   float* o_cache;           // [BH, L, dv]
   float rms_eps;
   int BH, H, L, dk, dv, w;
+  int policy;  // 0: top-w by score, 1: the w most recent
   // workspace parts (prefill_bind_workspace)
   int* members;       // [BH, blocks, w] cache members each block reads
   int* member_count;  // [BH, blocks]

@@ -10,7 +10,8 @@
 // incoming state S0 and chunk-local decay g_i = prod_{l<=i} alpha_l):
 //   A = strict_lower((K B^T) * G), G_il = g_i / g_l;   (I + A) U = V - diag(g) K S0
 //   O = diag(g) Q S0 + lower_incl((Q B^T) * G) U;      S = g_n S0 + (diag(g_n / g) B)^T U
-// U are exactly the per-token residuals e_t.
+// U are exactly the per-token residuals e_t. Without the erase term (e_t = v_t)
+// A = 0 and the K S0 term drops: U = V.
 //
 // One workgroup per (head, d_v tile): grid (heads, d_v tiles). The state tile lives in LDS; the loop
 // over chunks is sequential inside the workgroup.
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
         qs = fmaf(sQ[i * KP + r], s, qs);
       }
       const float g = expf(sLg[i]);
-      sX[idx] -= g * ks;
+      if (!a.noerase) sX[idx] -= g * ks;
       sO[idx] = g * qs;
     }
     __syncthreads();
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
       const int j = tid % dvt;
       const int part = tid / dvt;
       const int nparts = NT / dvt;
-      for (int i = 1; i < n; ++i) {
+      for (int i = 1; i < (a.noerase ? 0 : n); ++i) {
         float acc = 0.f;
         for (int l = part; l < i; l += nparts) acc = fmaf(sA[i * CP + l], sX[l * dvt + j], acc);
         sRed[tid] = acc;

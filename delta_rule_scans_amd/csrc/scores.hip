@@ -7,6 +7,9 @@
 // scan kernels leave them (or their per-tile squared norms) behind and this
 // kernel combines the d_v tiles in a fixed order and applies the scale.
 //
+// The ablation scores of the same section replace the product by the residual
+// alone (||e_t||) or by the write strength alone (s_t ||v_t||).
+//
 // One thread per token, one workgroup per (head, 64 tokens).
 #include "kdn_internal.h"
 
@@ -46,6 +49,12 @@ __global__ __launch_bounds__(64) void scores_kernel(ScoreArgs a) {
   } else {
     for (int tile = 0; tile < a.ntiles; ++tile) ss += a.esq[((size_t)bh * a.ntiles + tile) * a.L + tok];
   }
+  if (a.kind == 1) {  // ||e||; the plain form's residual is alpha e, see ScanArgs
+    float e = sqrtf(ss);
+    if (a.plain && a.alpha) e /= a.alpha[g];
+    a.m[g] = e;
+    return;
+  }
   float scale;
   if (a.gains) {
     float gg = 0.f;
@@ -59,7 +68,17 @@ __global__ __launch_bounds__(64) void scores_kernel(ScoreArgs a) {
     scale = a.iso_beta[g] * sqrtf(a.iso_kk[g]);
   } else {
     scale = a.beta[g];
-    if (a.plain) scale /= a.alpha ? a.alpha[g] : 1.f;
+    if (a.plain && a.kind == 0) scale /= a.alpha ? a.alpha[g] : 1.f;
+  }
+  if (a.kind == 2) {  // write strength times ||v|| of the input value
+    float vv = 0.f;
+    for (int c = 0; c < a.dv; ++c) {
+      const float x = a.v_bf16 ? bf16_to_f32(static_cast<const uint16_t*>(a.v)[g * a.dv + c])
+                               : static_cast<const float*>(a.v)[g * a.dv + c];
+      vv = fmaf(x, x, vv);
+    }
+    a.m[g] = scale * sqrtf(vv);
+    return;
   }
   a.m[g] = scale * sqrtf(ss);
 }

@@ -61,16 +61,30 @@ extern "C" {
 #define KDN_GAIN_FULL 2  /* full-covariance Kalman gain, cov [B,H,d_k,d_k], d_k <= 64 */
 #define KDN_GAIN_ISO 3   /* isotropic Kalman gain: one variance per head, cov [B,H]   */
 
-/* residual forms (delta mode only; the Kalman modes always use the gated form) */
-#define KDN_RESID_GATED 0 /* e = v - alpha S^T k */
-#define KDN_RESID_PLAIN 1 /* e = v - S^T k       */
+/* residual forms (PLAIN and NOERASE with the delta write only; the Kalman
+ * modes always use the gated form) */
+#define KDN_RESID_GATED 0   /* e = v - alpha S^T k                                  */
+#define KDN_RESID_PLAIN 1   /* e = v - S^T k                                        */
+#define KDN_RESID_NOERASE 2 /* e = v: S = alpha S + beta k v^T (decayed linear attention) */
+
+/* write scores ("A Hippocampus for Linear Attention", sec. 3.3 eq. (6); the
+ * two ablation variants of sec. 3.3 "versus recency" and sec. 4.5) */
+#define KDN_SCORE_WRITE 0 /* ||b e^T||_F: beta ||e|| (delta), ||g|| ||e|| (Kalman)  */
+#define KDN_SCORE_RESID 1 /* ||e|| (the residual alone)                             */
+#define KDN_SCORE_VALUE 2 /* beta ||v|| (delta), ||g|| ||v|| (the write strength alone) */
+
+/* cache eviction ("A Hippocampus for Linear Attention", sec. 3.3; sec. 4.5's
+ * matched control) */
+#define KDN_EVICT_SCORE 0   /* keep the w largest scores (ties: earlier token) */
+#define KDN_EVICT_RECENCY 1 /* keep the w most recent tokens                   */
 
 /* status codes */
 #define KDN_OK 0
 #define KDN_ERR_NULL_POINTER (-1)  /* a required pointer is NULL                   */
 #define KDN_ERR_BAD_SHAPE (-2)     /* a size is < 1 (L may be 0) or out of range   */
 #define KDN_ERR_BAD_CHUNK (-3)     /* chunk not in {16, 32, 64}                     */
-#define KDN_ERR_BAD_MODE (-4)      /* unknown mode / residual, or PLAIN with a gain */
+#define KDN_ERR_BAD_MODE (-4)      /* unknown mode / residual / score / policy, or a
+                                      residual form the write mode does not take   */
 #define KDN_ERR_BAD_DTYPE (-5)     /* unknown element type                          */
 #define KDN_ERR_UNSUPPORTED (-6)   /* valid but not implemented for these sizes    */
 #define KDN_ERR_WORKSPACE (-7)     /* workspace missing or smaller than required   */
@@ -120,16 +134,19 @@ size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
  *  o         [B,H,L,d_v] out_dtype output (bf16 outputs are the float32 result
  *            rounded to nearest even; that rounding alone is up to 2^-9 |o|,
  *            so use float32 output when the error bar is relative to RMS(o)).
- *  m         [B,H,L] float32 write scores, or NULL (not computed): the norm
- *            of each token's rank-one write ("A Hippocampus for Linear
- *            Attention", sec. 3.3 eq. (6)): beta_t ||e_t|| for the delta write
- *            (e_t the residual of the form in use), ||g_t|| ||e_t|| for the
- *            Kalman gains. On the matrix-core path e_t is taken from its fp16
- *            copy (relative error ~2^-11). Needs the workspace sized with
- *            with_scores = 1.
+ *  m         [B,H,L] float32 write scores, or NULL (not computed): with
+ *            score_kind KDN_SCORE_WRITE the norm of each token's rank-one write
+ *            ("A Hippocampus for Linear Attention", sec. 3.3 eq. (6)):
+ *            beta_t ||e_t|| for the delta write (e_t the residual of the form in
+ *            use), ||g_t|| ||e_t|| for the Kalman gains; KDN_SCORE_RESID gives
+ *            ||e_t||, KDN_SCORE_VALUE the write strength times ||v_t||. On the
+ *            matrix-core path e_t is taken from its fp16 copy (relative error
+ *            ~2^-11). Needs the workspace sized with with_scores = 1.
+ *  score_kind KDN_SCORE_* (ignored when m is NULL).
  *  chunk     chunk length in tokens: 16, 32 or 64. The result does not depend on
  *            it beyond rounding; L need not be a multiple of it.
- *  mode      KDN_GAIN_*;  resid  KDN_RESID_* (PLAIN only with DELTA).
+ *  mode      KDN_GAIN_*;  resid  KDN_RESID_* (PLAIN and NOERASE only with
+ *            DELTA; NOERASE runs on the float32 path).
  *  workspace device scratch of at least kdn_scan_workspace_size(...) bytes,
  *            16-byte aligned (may be NULL when that size is 0).
  * Sizes: B, H >= 1; L >= 0 (L = 0 copies state_in to state_out and cov_in to
@@ -144,7 +161,7 @@ int kdn_scan_fwd(const void *q, const void *k, const void *v, int in_dtype,
                  const float *alpha, const float *beta, const float *r,
                  const float *cov_in, float *cov_out, float q_noise_var,
                  const float *state_in, float *state_out,
-                 void *o, int out_dtype, float *m,
+                 void *o, int out_dtype, float *m, int score_kind,
                  int B, int H, int L, int d_k, int d_v, int chunk, int mode, int resid,
                  void *workspace, size_t workspace_bytes, void *stream);
 
@@ -168,7 +185,7 @@ int kdn_scan_fwd_phase(int phase, const void *q, const void *k, const void *v, i
                        const float *alpha, const float *beta, const float *r,
                        const float *cov_in, float *cov_out, float q_noise_var,
                        const float *state_in, float *state_out,
-                       void *o, int out_dtype, float *m,
+                       void *o, int out_dtype, float *m, int score_kind,
                        int B, int H, int L, int d_k, int d_v, int chunk, int mode, int resid,
                        void *workspace, size_t workspace_bytes, void *stream);
 
@@ -183,13 +200,14 @@ int kdn_scan_fwd_phase(int phase, const void *q, const void *k, const void *v, i
  *  cov       [B,H,d_k] (DIAG) or [B,H] (ISO) float32, in/out; ignored in DELTA mode.
  *  state     [B,H,d_k,d_v] float32, in/out.
  *  o         [B,H,d_v] float32 out: S_t^T q_t after the write.
- *  m         [B,H] float32 out: the write score; NULL = not written.
+ *  m         [B,H] float32 out: the write score of kind score_kind
+ *            (KDN_SCORE_*); NULL = not written.
  * Sizes: B, H >= 1; 1 <= d_k, d_v <= 128. Modes DELTA, DIAG and ISO (cov [B,H]).
  */
 int kdn_step_decode(const float *q, const float *k, const float *v,
                     const float *alpha, const float *beta, const float *r,
                     float *cov, float q_noise_var, float *state,
-                    float *o, float *m,
+                    float *o, float *m, int score_kind,
                     int B, int H, int d_k, int d_v, int mode, int resid, void *stream);
 
 /*
@@ -204,7 +222,9 @@ int kdn_step_decode(const float *q, const float *k, const float *v,
  * Then the insert: the cache keeps the w tokens with the largest score m
  * (ties: the earlier token). While count < w the token goes to slot `count`;
  * afterwards it replaces the slot with the smallest (m, then largest pos) when
- * its m is strictly larger. Comparisons are on the float32 scores.
+ * its m is strictly larger. Comparisons are on the float32 scores. With
+ * policy KDN_EVICT_RECENCY the cache keeps the w most recent tokens instead
+ * (a full cache replaces the slot with the smallest pos).
  *
  *  q, k      [B,H,d_k] float32;  v [B,H,d_v] float32;  m [B,H] float32 score.
  *  t         absolute token position (stored in cache_pos; tie-break).
@@ -219,7 +239,7 @@ int hola_cache_update(const float *q, const float *k, const float *v, const floa
                       int32_t t, float *cache_k, float *cache_v, float *cache_m,
                       int32_t *cache_pos, int32_t *cache_count, const float *sink_logit,
                       float *o_cache, float rms_eps, int B, int H, int d_k, int d_v, int w,
-                      void *stream);
+                      int policy, void *stream);
 
 /*
  * The HOLA cache over a whole prompt ("A Hippocampus for Linear Attention",
@@ -231,7 +251,9 @@ int hola_cache_update(const float *q, const float *k, const float *v, const floa
  * and the sink, with the read of hola_cache_update (RMS-normalised query and
  * keys, 1/sqrt(d_k), softmax). After block j the cache keeps the w best of
  * (cache, block j) by float32 score descending, then position ascending. With
- * block = 1 this is hola_cache_update applied token by token.
+ * block = 1 this is hola_cache_update applied token by token. With policy
+ * KDN_EVICT_RECENCY the cache keeps the w most recent tokens (most recent
+ * first).
  *
  *  q, k      [B,H,L,d_k] in_dtype (KDN_F32 or KDN_BF16); v [B,H,L,d_v] in_dtype.
  *  m         [B,H,L] float32 write scores of the prompt tokens (e.g. the `m`
@@ -252,7 +274,7 @@ int hola_prefill(const void *q, const void *k, const void *v, int in_dtype, cons
                  int32_t t0, int block, float *cache_k, float *cache_v, float *cache_m,
                  int32_t *cache_pos, int32_t *cache_count, const float *sink_logit,
                  float *o_cache, float rms_eps, int B, int H, int L, int d_k, int d_v, int w,
-                 void *workspace, size_t workspace_bytes, void *stream);
+                 int policy, void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -86,12 +86,12 @@ P = 0x10000
 
 def _scan(kdn, **kw):
     a = dict(q=P, k=P, v=P, in_dtype=1, alpha=P, beta=P, r=None, cov_in=None, cov_out=None,
-             qvar=0.0, state_in=None, state_out=None, o=P, out_dtype=1, m=None, B=1, H=1, L=64, dk=128,
+             qvar=0.0, state_in=None, state_out=None, o=P, out_dtype=1, m=None, sk=0, B=1, H=1, L=64, dk=128,
              dv=128, chunk=64, mode=0, resid=0, ws=None, wsb=0, stream=None)
     a.update(kw)
     return kdn.lib.kdn_scan_fwd(a["q"], a["k"], a["v"], a["in_dtype"], a["alpha"], a["beta"],
                                 a["r"], a["cov_in"], a["cov_out"], a["qvar"], a["state_in"],
-                                a["state_out"], a["o"], a["out_dtype"], a["m"], a["B"], a["H"], a["L"],
+                                a["state_out"], a["o"], a["out_dtype"], a["m"], a["sk"], a["B"], a["H"], a["L"],
                                 a["dk"], a["dv"], a["chunk"], a["mode"], a["resid"], a["ws"],
                                 a["wsb"], a["stream"])
 
@@ -108,7 +108,6 @@ def test_scan_rejections(kdn):
     assert _scan(kdn, mode=4) == c["KDN_ERR_BAD_MODE"]
     assert _scan(kdn, mode=3, resid=1, cov_in=P) == c["KDN_ERR_BAD_MODE"]
     assert _scan(kdn, mode=3, cov_in=P) == c["KDN_ERR_WORKSPACE"]
-    assert _scan(kdn, resid=2) == c["KDN_ERR_BAD_MODE"]
     assert _scan(kdn, mode=1, resid=1, cov_in=P) == c["KDN_ERR_BAD_MODE"]
     for bad in (dict(B=0), dict(H=-1), dict(L=-1), dict(dk=0), dict(dv=129), dict(dk=256)):
         assert _scan(kdn, **bad) == c["KDN_ERR_BAD_SHAPE"], bad
@@ -120,7 +119,11 @@ def test_scan_rejections(kdn):
     assert _scan(kdn, mode=2, cov_in=P, dk=64) == c["KDN_ERR_WORKSPACE"]
     # an unknown phase is rejected like an unknown mode
     assert kdn.lib.kdn_scan_fwd_phase(3, P, P, P, 1, P, P, None, None, None, 0.0, None, None, P, 1,
-                                      None, 1, 1, 64, 128, 128, 64, 0, 0, None, 0, None) == c["KDN_ERR_BAD_MODE"]
+                                      None, 0, 1, 1, 64, 128, 128, 64, 0, 0, None, 0, None) == c["KDN_ERR_BAD_MODE"]
+    # residual forms other than the gated one take the delta write only; scores 0..2
+    assert _scan(kdn, resid=3) == c["KDN_ERR_BAD_MODE"]
+    assert _scan(kdn, resid=2, mode=1, cov_in=P) == c["KDN_ERR_BAD_MODE"]
+    assert _scan(kdn, m=P, sk=3) == c["KDN_ERR_BAD_MODE"]
     # scores need the larger workspace
     base = kdn.kdn_scan_workspace_size(1, 1, 64, 128, 128, 64, "delta", kdn.BF16)
     big = kdn.kdn_scan_workspace_size(1, 1, 64, 128, 128, 64, "delta", kdn.BF16, with_scores=True)
@@ -132,12 +135,13 @@ def test_scan_rejections(kdn):
 
 
 def _decode(kdn, **kw):
-    a = dict(q=P, k=P, v=P, alpha=P, beta=P, r=None, cov=None, qvar=0.0, state=P, o=P, m=P, B=2,
-             H=2, dk=128, dv=128, mode=0, resid=0, stream=None)
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, r=None, cov=None, qvar=0.0, state=P, o=P, m=P, sk=0,
+             B=2, H=2, dk=128, dv=128, mode=0, resid=0, stream=None)
     a.update(kw)
     return kdn.lib.kdn_step_decode(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["r"],
-                                   a["cov"], a["qvar"], a["state"], a["o"], a["m"], a["B"],
-                                   a["H"], a["dk"], a["dv"], a["mode"], a["resid"], a["stream"])
+                                   a["cov"], a["qvar"], a["state"], a["o"], a["m"], a["sk"],
+                                   a["B"], a["H"], a["dk"], a["dv"], a["mode"], a["resid"],
+                                   a["stream"])
 
 
 def test_decode_rejections(kdn):
@@ -149,6 +153,8 @@ def test_decode_rejections(kdn):
     assert _decode(kdn, mode=3) == c["KDN_ERR_NULL_POINTER"]
     assert _decode(kdn, mode=3, resid=1, cov=P) == c["KDN_ERR_BAD_MODE"]
     assert _decode(kdn, mode=5) == c["KDN_ERR_BAD_MODE"]
+    assert _decode(kdn, sk=5) == c["KDN_ERR_BAD_MODE"]
+    assert _decode(kdn, resid=2, mode=3, cov=P) == c["KDN_ERR_BAD_MODE"]
     assert _decode(kdn, mode=1, resid=1, cov=P) == c["KDN_ERR_BAD_MODE"]
     assert _decode(kdn, dk=0) == c["KDN_ERR_BAD_SHAPE"]
     assert _decode(kdn, dv=200) == c["KDN_ERR_BAD_SHAPE"]
@@ -157,11 +163,12 @@ def test_decode_rejections(kdn):
 
 def _hola(kdn, **kw):
     a = dict(q=P, k=P, v=P, m=P, t=0, ck=P, cv=P, cm=P, cp=P, cc=P, sink=None, oc=P, eps=1e-6,
-             B=1, H=1, dk=128, dv=128, w=64, stream=None)
+             B=1, H=1, dk=128, dv=128, w=64, policy=0, stream=None)
     a.update(kw)
     return kdn.lib.hola_cache_update(a["q"], a["k"], a["v"], a["m"], a["t"], a["ck"], a["cv"],
                                      a["cm"], a["cp"], a["cc"], a["sink"], a["oc"], a["eps"],
-                                     a["B"], a["H"], a["dk"], a["dv"], a["w"], a["stream"])
+                                     a["B"], a["H"], a["dk"], a["dv"], a["w"], a["policy"],
+                                     a["stream"])
 
 
 def test_hola_rejections(kdn):
@@ -173,6 +180,7 @@ def test_hola_rejections(kdn):
     assert _hola(kdn, dk=129) == c["KDN_ERR_BAD_SHAPE"]
     assert _hola(kdn, eps=-1.0) == c["KDN_ERR_BAD_SHAPE"]
     assert _hola(kdn, eps=float("nan")) == c["KDN_ERR_BAD_SHAPE"]
+    assert _hola(kdn, policy=2) == c["KDN_ERR_BAD_MODE"]
 
 
 def test_product_package_does_not_touch_the_oracle():
@@ -186,12 +194,13 @@ def test_product_package_does_not_touch_the_oracle():
 
 def _prefill(kdn, **kw):
     a = dict(q=P, k=P, v=P, dt=1, m=P, t0=0, block=256, ck=P, cv=P, cm=P, cp=P, cc=P, sink=None,
-             oc=P, eps=1e-6, B=1, H=1, L=512, dk=128, dv=128, w=64, ws=None, wsb=0, stream=None)
+             oc=P, eps=1e-6, B=1, H=1, L=512, dk=128, dv=128, w=64, policy=0, ws=None, wsb=0,
+             stream=None)
     a.update(kw)
     return kdn.lib.hola_prefill(a["q"], a["k"], a["v"], a["dt"], a["m"], a["t0"], a["block"],
                                 a["ck"], a["cv"], a["cm"], a["cp"], a["cc"], a["sink"], a["oc"],
                                 a["eps"], a["B"], a["H"], a["L"], a["dk"], a["dv"], a["w"],
-                                a["ws"], a["wsb"], a["stream"])
+                                a["policy"], a["ws"], a["wsb"], a["stream"])
 
 
 def test_prefill_rejections(kdn):
@@ -206,6 +215,7 @@ def test_prefill_rejections(kdn):
     for bad in (dict(block=0), dict(block=1025), dict(L=-1), dict(dk=129), dict(B=0),
                 dict(eps=-1.0), dict(t0=2 ** 31 - 100)):
         assert _prefill(kdn, **bad) == c["KDN_ERR_BAD_SHAPE"], bad
+    assert _prefill(kdn, policy=-1) == c["KDN_ERR_BAD_MODE"]
     assert _prefill(kdn, cc=None) == c["KDN_ERR_NULL_POINTER"]
     assert _prefill(kdn, m=None) == c["KDN_ERR_NULL_POINTER"]
     assert _prefill(kdn, L=0, m=None) == c["KDN_OK"]          # nothing to do, nothing touched

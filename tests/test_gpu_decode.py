@@ -188,3 +188,45 @@ def test_full_size_decode_hola(kdn, orc):
     got, ref = _run_decode(kdn, orc, cfg["B"], cfg["H"], cfg["dk"], cfg["dv"], cfg["w"],
                            cfg["steps"], seed=workloads.DECODE_SEED, sample=sample)
     _compare(got, ref, cfg["w"], "decode full size")
+
+
+@pytest.mark.parametrize("resid,score", [("noerase", "write"), ("gated", "resid"),
+                                         ("plain", "resid"), ("plain", "value")])
+def test_decode_switches(kdn, orc, resid, score):
+    """No-erase write and the ablation scores in the decode step."""
+    import torch
+    B, H, d, T = 2, 3, 64, 30
+    inputs = _steps(T, B, H, d, d, seed=205)
+    state = torch.zeros((B, H, d, d), device="cuda")
+    ms, outs = [], []
+    for inp in inputs:
+        g = {n: dev_tensor(x) for n, x in inp.items()}
+        o, m = kdn.kdn_step_decode(g["q"], g["k"], g["v"], g["alpha"], g["beta"], state,
+                                   resid=resid, score=score)
+        outs.append(host(o))
+        ms.append(host(m))
+    torch.cuda.synchronize()
+    o_ref, _, m_ref, S_ref, _, _ = orc.decode_run(inputs, B, H, d, d, 4, resid=resid, score=score)
+    assert_close(np.stack(outs), np.stack(o_ref), TOL_F32, f"{resid} o")
+    assert_close(np.stack(ms), np.stack(m_ref), TOL_F32, f"{score} m")
+    assert_close(host(state), S_ref, TOL_F32, f"{resid} S")
+
+
+def test_recency_cache(kdn, orc):
+    """The recency control (A Hippocampus for Linear Attention, sec. 4.5): the
+    cache keeps the w most recent tokens; reads against the oracle."""
+    import torch
+    B, H, d, w, T = 2, 2, 128, 8, 40
+    inputs = _steps(T, B, H, d, d, seed=206)
+    cache = kdn.HolaCache(B, H, d, d, w, policy="recency")
+    ocache = orc.HolaCache(B, H, d, d, w, policy="recency")
+    for t, inp in enumerate(inputs):
+        g = {n: dev_tensor(x) for n, x in inp.items()}
+        m = torch.rand((B, H), device="cuda")
+        oc = kdn.hola_cache_update(g["q"], g["k"], g["v"], m, t, cache)
+        ref = ocache.step(inp["q"], inp["k"], inp["v"], host(m), t)
+        assert_close(host(oc), ref, TOL_F32, f"recency o_cache t={t}")
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            assert sorted(host(cache.pos)[b, h].astype(int).tolist()) == list(range(T - w, T))

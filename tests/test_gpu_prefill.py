@@ -24,13 +24,14 @@ def kdn():
     return k
 
 
-def _prefill_case(kdn, orc, q, k, v, m, t0, block, w, dtype, sink=None, init=None, heads=None):
+def _prefill_case(kdn, orc, q, k, v, m, t0, block, w, dtype, sink=None, init=None, heads=None,
+                  policy="score"):
     """Run hola_prefill on the GPU and the oracle (on `heads`, default all) and compare."""
     import torch
     B, H, L, dk = q.shape
     dv = v.shape[-1]
-    cache = kdn.HolaCache(B, H, dk, dv, w)
-    ocache = orc.HolaCache(B, H, dk, dv, w)
+    cache = kdn.HolaCache(B, H, dk, dv, w, policy=policy)
+    ocache = orc.HolaCache(B, H, dk, dv, w, policy=policy)
     if init is not None:
         n0, rng = init
         for f, shape in (("k", (B, H, w, dk)), ("v", (B, H, w, dv))):
@@ -53,7 +54,7 @@ def _prefill_case(kdn, orc, q, k, v, m, t0, block, w, dtype, sink=None, init=Non
     sel = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     bs = np.array([s[0] for s in sel])
     hs = np.array([s[1] for s in sel])
-    sub = orc.HolaCache(1, len(sel), dk, dv, w)
+    sub = orc.HolaCache(1, len(sel), dk, dv, w, policy=policy)
     for f in ("k", "v", "m", "pos"):
         setattr(sub, f, np.ascontiguousarray(getattr(ocache, f)[bs, hs][None]))
     sub.count = np.ascontiguousarray(ocache.count[bs, hs][None])
@@ -87,6 +88,18 @@ def test_prefill_small(kdn, orc, dtype):
         log(f"prefill {dtype} block {block} sink {use_sink} init {init}")
         _prefill_case(kdn, orc, q, k, v, m, 40, block, w, dtype, sink if use_sink else None,
                       None if init is None else (init, rng))
+
+
+def test_prefill_recency(kdn, orc):
+    """The recency control (A Hippocampus for Linear Attention, sec. 4.5) over a prompt."""
+    rng = np.random.Generator(np.random.PCG64(304))
+    B, H, L, d, w = 1, 3, 200, 64, 12
+    q, k, v = (rng.standard_normal((B, H, L, d)).astype(np.float32) for _ in range(3))
+    m = rng.uniform(0, 1, (B, H, L)).astype(np.float32)
+    for block, init in ((1, None), (32, 6), (128, None)):
+        got = _prefill_case(kdn, orc, q, k, v, m, 50, block, w, "f32",
+                            init=None if init is None else (init, rng), policy="recency")
+        np.testing.assert_array_equal(got["pos"][0, 0], np.arange(50 + L - 1, 50 + L - 1 - w, -1))
 
 
 def test_prefill_odd_shapes(kdn, orc):

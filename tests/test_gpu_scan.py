@@ -240,6 +240,50 @@ def test_write_scores(kdn, orc, mode, resid, dtype, dk):
         assert_close(host(o), ref["o"], tol, f"o {mode}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_noerase_write(kdn, orc, dtype):
+    """Decayed linear attention (the write without its erase term), with scores."""
+    import torch
+    inp = workloads.scan_inputs(2, 2, 230, 128, 64, seed=111, dtype=dtype)
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"],
+                   resid="noerase")
+    tol = TOL_BF16 if dtype == "bf16" else TOL_F32
+    for chunk in (16, 64):
+        got = _scan_gpu(kdn, inp, dtype, chunk, resid="noerase")
+        assert_close(got["o"], ref["o"], tol, f"noerase o chunk {chunk}")
+        assert_close(got["S"], ref["S"], tol, f"noerase S chunk {chunk}")
+    q, k, v = (dev_tensor(inp[n], dtype) for n in ("q", "k", "v"))
+    _, m = kdn.kdn_scan_fwd(q, k, v, alpha=dev_tensor(inp["alpha"]), beta=dev_tensor(inp["beta"]),
+                            resid="noerase", m=True)
+    torch.cuda.synchronize()
+    assert_close(host(m), ref["m"], tol, "noerase m")
+
+
+@pytest.mark.parametrize("score,mode,resid,dtype", [("resid", "delta", "gated", "bf16"),
+                                                    ("value", "delta", "gated", "bf16"),
+                                                    ("resid", "delta", "plain", "f32"),
+                                                    ("value", "delta", "plain", "bf16"),
+                                                    ("value", "diag", "gated", "f32"),
+                                                    ("resid", "iso", "gated", "bf16")])
+def test_score_variants(kdn, orc, score, mode, resid, dtype):
+    """The ablation scores (A Hippocampus for Linear Attention, sec. 3.3 "versus
+    recency", sec. 4.5): the residual alone and the write strength alone."""
+    import torch
+    inp = workloads.scan_inputs(1, 2, 150, 128, 64, seed=112, dtype=dtype, with_r=True)
+    cov0 = {"diag": np.ones((1, 2, 128), np.float32), "iso": np.ones((1, 2), np.float32)}.get(mode)
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"],
+                   r=inp["r"] if mode != "delta" else None, cov0=cov0, q_noise_var=0.5,
+                   mode=mode, resid=resid, score=score)
+    q, k, v = (dev_tensor(inp[n], dtype) for n in ("q", "k", "v"))
+    cin = dev_tensor(cov0) if cov0 is not None else None
+    _, m = kdn.kdn_scan_fwd(q, k, v, alpha=dev_tensor(inp["alpha"]), beta=dev_tensor(inp["beta"]),
+                            r=dev_tensor(inp["r"]) if mode != "delta" else None, cov_in=cin,
+                            cov_out=torch.empty_like(cin) if cin is not None else None,
+                            q_noise_var=0.5, mode=mode, resid=resid, m=True, score=score)
+    torch.cuda.synchronize()
+    assert_close(host(m), ref["m"], TOL_BF16 if dtype == "bf16" else TOL_F32, f"m {score}")
+
+
 # --------------------------------------------------------------- full-size workloads
 
 def _sampled_check(kdn, orc, name, heads, mode="delta", check_state=True):
