@@ -62,6 +62,8 @@ def _load():
         lib.oracle_hola_prefill.argtypes = [i, i, i, i, i, i, i, P, P, P, P, i, P, P, P, P, P, P,
                                             d, i, P]
         lib.oracle_hola_prefill.restype = i
+        lib.oracle_scan_bwd.argtypes = [i, i, i, i, i, P, P, P, P, P, P, P, P, i, P, P, P, P, P, P]
+        lib.oracle_scan_bwd.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
         _lib = lib
@@ -110,6 +112,29 @@ def scan(q, k, v, alpha=None, beta=None, r=None, cov0=None, q_noise_var: float =
     if rc != 0:
         raise ValueError(f"oracle_scan rejected the arguments (status {rc})")
     return dict(o=o, S=S, cov=cov, m=m)
+
+
+def scan_bwd(q, k, v, alpha=None, beta=None, S0=None, d_o=None, dS=None,
+             resid: str = "gated") -> dict:
+    """Gradients of the delta-write scan (fp64 adjoint, see kdn_oracle.c) for the
+    loss sum(d_o * o) + sum(dS * S_L). Returns dict(dq, dk, dv, dalpha, dbeta, dS0)."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    alpha, beta = _f32(alpha), _f32(beta)
+    S0 = None if S0 is None else np.ascontiguousarray(S0, dtype=np.float64)
+    d_o = np.ascontiguousarray(d_o, dtype=np.float64)
+    assert d_o.shape == (B, H, L, dv)
+    dS = None if dS is None else np.ascontiguousarray(dS, dtype=np.float64)
+    out = dict(dq=np.zeros((B, H, L, dk)), dk=np.zeros((B, H, L, dk)), dv=np.zeros((B, H, L, dv)),
+               dalpha=np.zeros((B, H, L)), dbeta=np.zeros((B, H, L)), dS0=np.zeros((B, H, dk, dv)))
+    rc = _load().oracle_scan_bwd(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                 _ptr(beta), _ptr(S0), _ptr(d_o), _ptr(dS), RESIDS[resid],
+                                 _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                 _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dS0"]))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_bwd rejected the arguments (status {rc})")
+    return out
 
 
 class HolaCache:

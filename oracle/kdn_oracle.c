@@ -516,3 +516,148 @@ int oracle_hola_prefill(int B, int H, int L, int dk, int dv, int w, int block,
     }
     return bad ? -2 : 0;
 }
+
+/*
+ * Gradients of the delta-write scan (reverse mode), one (batch, head) at a
+ * time. The pages give no backward formulas; this is the adjoint of the
+ * token recurrence written above, derived by hand and pinned in the tests by
+ * finite differences of oracle_scan:
+ *
+ *   S_t = M_t S_{t-1} + beta_t k_t v_t^T,  M_t = alpha_t I - c_t beta_t k_t k_t^T,
+ *   o_t = S_t^T q_t,   e_t = v_t - c_t S_{t-1}^T k_t,
+ *   c_t = alpha_t (gated residual), 1 (plain), 0 (no erase).
+ *
+ * Given dL/do_t and dL/dS_L, with G_t = dL/dS_t accumulated backwards:
+ *   G_t += q_t do_t^T;   dq_t = S_t do_t;   y_t = G_t^T k_t;
+ *   dv_t = beta_t y_t;   dbeta_t = y_t . e_t;
+ *   dk_t = beta_t G_t e_t - c_t beta_t S_{t-1} y_t;
+ *   dalpha_t = <G_t, S_{t-1}> - [gated] beta_t y_t . (S_{t-1}^T k_t);
+ *   G_{t-1} = alpha_t G_t - c_t beta_t k_t y_t^T;   dS_0 = G_0.
+ * States are recomputed from checkpoints every 64 tokens.
+ *
+ *   inputs as oracle_scan (DELTA mode); d_o [B,H,L,dv]; dS_L [B,H,dk,dv] or NULL;
+ *   S0 [B,H,dk,dv] float64 or NULL (= 0).
+ *   outputs float64: dq, dk [B,H,L,dk]; dv [B,H,L,dv]; dalpha, dbeta [B,H,L];
+ *   dS0 [B,H,dk,dv] (may be NULL).
+ */
+int oracle_scan_bwd(int B, int H, int L, int dk, int dv,
+                    const float *q, const float *k, const float *v,
+                    const float *alpha, const float *beta, const double *S0,
+                    const double *d_o, const double *dSL, int resid,
+                    double *dq, double *dkk, double *dvv, double *dalpha, double *dbeta,
+                    double *dS0)
+{
+    if (resid != ORC_GATED && resid != ORC_PLAIN && resid != ORC_NOERASE) return -1;
+    const int CK = 64;
+    const int nck = (L + CK - 1) / CK;
+    const int BH = B * H;
+    const size_t SS = (size_t)dk * dv;
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < BH; ++bh) {
+        double *ckpt = (double *)malloc(sizeof(double) * SS * (size_t)(nck + 1));
+        double *hist = (double *)malloc(sizeof(double) * SS * (size_t)(CK + 1));
+        double *G = (double *)malloc(sizeof(double) * SS);
+        double *y = (double *)malloc(sizeof(double) * (size_t)(dv + dv + dk));
+        if (!ckpt || !hist || !G || !y) {
+#pragma omp atomic write
+            bad = 1;
+            free(ckpt); free(hist); free(G); free(y);
+            continue;
+        }
+        double *e = y + dv, *p = e + dv;
+        const float *qh = q + (size_t)bh * L * dk, *kh = k + (size_t)bh * L * dk;
+        const float *vh = v + (size_t)bh * L * dv;
+        const float *ah = alpha ? alpha + (size_t)bh * L : NULL, *bt = beta + (size_t)bh * L;
+        const double *doh = d_o + (size_t)bh * L * dv;
+        /* forward: checkpoints at t = 0, 64, 128, ... (the state before token t) */
+        double *S = hist;  /* scratch */
+        for (size_t i = 0; i < SS; ++i) S[i] = S0 ? S0[(size_t)bh * SS + i] : 0.0;
+        for (int t = 0; t < L; ++t) {
+            if (t % CK == 0) memcpy(ckpt + SS * (size_t)(t / CK), S, sizeof(double) * SS);
+            const double a = ah ? (double)ah[t] : 1.0, b = (double)bt[t];
+            const double c = resid == ORC_GATED ? a : (resid == ORC_PLAIN ? 1.0 : 0.0);
+            const float *kt = kh + (size_t)t * dk, *vt = vh + (size_t)t * dv;
+            for (int j = 0; j < dv; ++j) {
+                double pr = 0.0;
+                for (int i = 0; i < dk; ++i) pr += S[(size_t)i * dv + j] * (double)kt[i];
+                e[j] = (double)vt[j] - c * pr;
+            }
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j)
+                    S[(size_t)i * dv + j] = a * S[(size_t)i * dv + j] + b * (double)kt[i] * e[j];
+        }
+        for (size_t i = 0; i < SS; ++i) G[i] = dSL ? dSL[(size_t)bh * SS + i] : 0.0;
+        /* backward, chunk by chunk from the end */
+        for (int ck = nck - 1; ck >= 0; --ck) {
+            const int t0 = ck * CK, t1 = (t0 + CK < L) ? t0 + CK : L;
+            /* hist[s] = state before token t0 + s, s = 0 .. t1 - t0 */
+            memcpy(hist, ckpt + SS * (size_t)ck, sizeof(double) * SS);
+            for (int t = t0; t < t1; ++t) {
+                const double *Sp = hist + SS * (size_t)(t - t0);
+                double *Sn = hist + SS * (size_t)(t - t0 + 1);
+                const double a = ah ? (double)ah[t] : 1.0, b = (double)bt[t];
+                const double c = resid == ORC_GATED ? a : (resid == ORC_PLAIN ? 1.0 : 0.0);
+                const float *kt = kh + (size_t)t * dk, *vt = vh + (size_t)t * dv;
+                for (int j = 0; j < dv; ++j) {
+                    double pr = 0.0;
+                    for (int i = 0; i < dk; ++i) pr += Sp[(size_t)i * dv + j] * (double)kt[i];
+                    e[j] = (double)vt[j] - c * pr;
+                }
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j)
+                        Sn[(size_t)i * dv + j] = a * Sp[(size_t)i * dv + j] + b * (double)kt[i] * e[j];
+            }
+            for (int t = t1 - 1; t >= t0; --t) {
+                const double *Sp = hist + SS * (size_t)(t - t0);      /* S_{t-1} */
+                const double *Sn = hist + SS * (size_t)(t - t0 + 1);  /* S_t */
+                const double a = ah ? (double)ah[t] : 1.0, b = (double)bt[t];
+                const double c = resid == ORC_GATED ? a : (resid == ORC_PLAIN ? 1.0 : 0.0);
+                const float *kt = kh + (size_t)t * dk, *vt = vh + (size_t)t * dv;
+                const float *qt = qh + (size_t)t * dk;
+                const double *dot = doh + (size_t)t * dv;
+                const size_t tok = (size_t)bh * L + t;
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j) G[(size_t)i * dv + j] += (double)qt[i] * dot[j];
+                for (int i = 0; i < dk; ++i) {
+                    double s = 0.0;
+                    for (int j = 0; j < dv; ++j) s += Sn[(size_t)i * dv + j] * dot[j];
+                    dq[tok * dk + i] = s;
+                }
+                for (int j = 0; j < dv; ++j) {
+                    double yy = 0.0, pr = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        yy += G[(size_t)i * dv + j] * (double)kt[i];
+                        pr += Sp[(size_t)i * dv + j] * (double)kt[i];
+                    }
+                    y[j] = yy;
+                    p[j] = pr;
+                    e[j] = (double)vt[j] - c * pr;
+                }
+                double db = 0.0, yp = 0.0, gs = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    dvv[tok * dv + j] = b * y[j];
+                    db += y[j] * e[j];
+                    yp += y[j] * p[j];
+                }
+                for (size_t i = 0; i < SS; ++i) gs += G[i] * Sp[i];
+                dbeta[tok] = db;
+                dalpha[tok] = gs - (resid == ORC_GATED ? b * yp : 0.0);
+                for (int i = 0; i < dk; ++i) {
+                    double ge = 0.0, sy = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        ge += G[(size_t)i * dv + j] * e[j];
+                        sy += Sp[(size_t)i * dv + j] * y[j];
+                    }
+                    dkk[tok * dk + i] = b * ge - c * b * sy;
+                }
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j)
+                        G[(size_t)i * dv + j] = a * G[(size_t)i * dv + j] - c * b * (double)kt[i] * y[j];
+            }
+        }
+        if (dS0) memcpy(dS0 + (size_t)bh * SS, G, sizeof(double) * SS);
+        free(ckpt); free(hist); free(G); free(y);
+    }
+    return bad ? -2 : 0;
+}

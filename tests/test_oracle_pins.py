@@ -828,3 +828,51 @@ def test_recency_eviction_keeps_the_last_w(orc):
         np.testing.assert_array_equal(c.k[0, 1], k[0, 1, L - 1:L - 1 - w:-1])
         if block == 1:
             np.testing.assert_allclose(o, np.stack(outs, 2), rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass of the delta-write scan
+# ---------------------------------------------------------------------------
+
+def _fd_loss(orc, inp, S0, d_o, dS, resid):
+    r = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"], S0=S0,
+                 resid=resid, want_m=False)
+    return float(np.sum(r["o"] * d_o) + np.sum(r["S"] * dS))
+
+
+@pytest.mark.parametrize("resid,L", [("gated", 9), ("plain", 9), ("noerase", 9), ("gated", 150)])
+def test_backward_matches_finite_differences(orc, resid, L):
+    """The gradients of the scan (the pages give none; the adjoint recurrence is
+    derived for this library) against central finite differences of the forward
+    oracle, for every input including the initial state, on a loss
+    sum(d_o * o) + sum(dS * S_L). Inputs are float32, so the steps are powers
+    of two that keep the perturbed inputs exact; L = 150 crosses the backward's
+    64-token recomputation checkpoints (sampled elements)."""
+    rng = _rng(60 + L)
+    B, H, dk, dv = 1, 2, 4, 3
+    inp = workloads.scan_inputs(B, H, L, dk, dv, seed=61, dtype="f32")
+    S0 = rng.standard_normal((B, H, dk, dv)) * 0.5
+    d_o = rng.standard_normal((B, H, L, dv))
+    dS = rng.standard_normal((B, H, dk, dv))
+    g = orc.scan_bwd(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"], S0=S0,
+                     d_o=d_o, dS=dS, resid=resid)
+    h = 2.0 ** -12
+    names = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "beta": "dbeta"}
+    for name, gname in names.items():
+        x = inp[name]
+        idx = list(np.ndindex(x.shape))
+        if L > 20:
+            idx = [idx[i] for i in rng.choice(len(idx), 25, replace=False)]
+        for ix in idx:
+            xp = {**inp, name: x.copy()}
+            xm = {**inp, name: x.copy()}
+            xp[name][ix] += np.float32(h)
+            xm[name][ix] -= np.float32(h)
+            fd = (_fd_loss(orc, xp, S0, d_o, dS, resid) - _fd_loss(orc, xm, S0, d_o, dS, resid)) / (2 * h)
+            assert abs(fd - g[gname][ix]) <= 1e-6 * (1 + abs(fd)), (name, ix, fd, g[gname][ix])
+    for ix in np.ndindex(S0.shape):
+        sp, sm = S0.copy(), S0.copy()
+        sp[ix] += h
+        sm[ix] -= h
+        fd = (_fd_loss(orc, inp, sp, d_o, dS, resid) - _fd_loss(orc, inp, sm, d_o, dS, resid)) / (2 * h)
+        assert abs(fd - g["dS0"][ix]) <= 1e-6 * (1 + abs(fd)), ("S0", ix, fd, g["dS0"][ix])
