@@ -11,8 +11,8 @@ resident in HBM before timing starts.
 Extra fields: the roofline of the dominant (state) kernel, timed on its own
 stream with events around its phase; the fp64 oracle timed on a bounded
 sample on the host cores; and (unless --quick) the decode + HOLA cache step,
-the HOLA prompt cache after a scan with write scores, the diagonal and
-isotropic Kalman scans and the long-context scan.
+the HOLA prompt cache after a scan with write scores, the backward pass, the
+diagonal and isotropic Kalman scans and the long-context scan.
 """
 from __future__ import annotations
 
@@ -189,6 +189,37 @@ def bench_prefill(kdn, torch, steps, warmup, block=256, w=64):
                        f"(blocks of {block}, w = {w}), B=4 H=16 L=4096 d=128")
 
 
+def bench_backward(kdn, torch, steps, warmup):
+    """Gradients of the gated delta scan at the headline shape (float32 inputs)."""
+    import workloads
+    cfg = workloads.WORKLOADS["gated"]
+    B, H, L, dk, dv = cfg["B"], cfg["H"], cfg["L"], cfg["dk"], cfg["dv"]
+    inp = workloads.named_scan_inputs("gated")
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("q", "k", "v", "alpha", "beta")}
+    del inp
+    d_o = torch.randn((B, H, L, dv), device=dev)
+    ws = torch.empty(int(kdn.lib.kdn_scan_bwd_workspace_size(B, H, L, dk, dv)), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        kdn.kdn_scan_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], d_o, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    return dict(ms_per_step=round(ms, 5), tokens_per_s=round(B * L / (ms * 1e-3), 1),
+                config="gradients of the gated delta scan, B=4 H=16 L=4096 d=128, float32, "
+                       "token-sequential reference kernel")
+
+
 def bench_decode(kdn, torch, steps, warmup):
     """Decode + HOLA cache at B=256, H=32, d=128, w=64, timed after the cache is full."""
     import workloads
@@ -330,6 +361,8 @@ def main():
         extra = {}
         extra["decode"] = bench_decode(kdn, torch, steps=max(8, args.steps), warmup=args.warmup)
         extra["prompt_cache"] = bench_prefill(kdn, torch, steps=max(2, args.steps // 4), warmup=1)
+        torch.cuda.empty_cache()
+        extra["backward"] = bench_backward(kdn, torch, steps=2, warmup=1)
         torch.cuda.empty_cache()
         for key, name, mode in (("kdn_diag", "kdn_diag", "diag"), ("kdn_iso", "kdn_diag", "iso"),
                                 ("long", "long", "delta")):

@@ -21,7 +21,7 @@ import os
 __all__ = [
     "lib", "KdnError", "kdn_scan_fwd", "kdn_step_decode", "hola_cache_update",
     "kdn_scan_workspace_size", "kdn_status_string", "HolaCache", "LIB_PATH",
-    "hola_prefill", "hola_prefill_workspace_size",
+    "hola_prefill", "hola_prefill_workspace_size", "kdn_scan_bwd",
     "F32", "BF16", "MODES", "RESIDS", "PHASES",
 ]
 
@@ -64,6 +64,10 @@ def _load():
     L.hola_cache_update.argtypes = [P, P, P, P, ctypes.c_int32, P, P, P, P, P, P, P, F,
                                     I, I, I, I, I, I, P]
     L.hola_cache_update.restype = I
+    L.kdn_scan_bwd_workspace_size.argtypes = [I, I, I, I, I]
+    L.kdn_scan_bwd_workspace_size.restype = SZ
+    L.kdn_scan_bwd.argtypes = [P] * 14 + [I] * 6 + [P, SZ, P]
+    L.kdn_scan_bwd.restype = I
     L.hola_prefill_workspace_size.argtypes = [I, I, I, I, I, I, I]
     L.hola_prefill_workspace_size.restype = SZ
     L.hola_prefill.argtypes = [P, P, P, I, P, ctypes.c_int32, I, P, P, P, P, P, P, P, F,
@@ -301,3 +305,39 @@ def hola_prefill(q, k, v, m, t0: int, cache: HolaCache, block: int = 256, sink_l
 
 def hola_prefill_workspace_size(B, H, L, d_k, d_v, w, block) -> int:
     return int(lib.hola_prefill_workspace_size(B, H, L, d_k, d_v, w, block))
+
+
+def kdn_scan_bwd(q, k, v, alpha, beta, d_o, state_in=None, dstate_out=None, resid: str = "gated",
+                 workspace=None, stream=None, want_dstate: bool = True) -> dict:
+    """Gradients of the delta-write scan for dL/do = d_o and dL/dS_L = dstate_out
+    (float32 tensors, shapes as kdn_scan_fwd). Returns dict(dq, dk, dv, dalpha,
+    dbeta, dstate_in)."""
+    torch = _torch()
+    f = torch.float32
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _check(q, "q", f, (B, H, L, dk), dev)
+    _check(k, "k", f, (B, H, L, dk), dev)
+    _check(v, "v", f, (B, H, L, dv), dev)
+    _check(alpha, "alpha", f, (B, H, L), dev)
+    _check(beta, "beta", f, (B, H, L), dev)
+    _check(d_o, "d_o", f, (B, H, L, dv), dev)
+    _check(state_in, "state_in", f, (B, H, dk, dv), dev)
+    _check(dstate_out, "dstate_out", f, (B, H, dk, dv), dev)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dalpha=torch.empty((B, H, L), dtype=f, device=dev) if alpha is not None else None,
+               dbeta=torch.empty((B, H, L), dtype=f, device=dev),
+               dstate_in=torch.empty((B, H, dk, dv), dtype=f, device=dev) if want_dstate else None)
+    need = int(lib.kdn_scan_bwd_workspace_size(B, H, max(L, 1), dk, dv))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.kdn_scan_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(state_in),
+                          _ptr(d_o), _ptr(dstate_out), _ptr(out["dq"]), _ptr(out["dk"]),
+                          _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["dbeta"]),
+                          _ptr(out["dstate_in"]), B, H, L, dk, dv, RESIDS[resid],
+                          _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          _stream(stream))
+    if st != 0:
+        raise KdnError(st, "kdn_scan_bwd")
+    return out

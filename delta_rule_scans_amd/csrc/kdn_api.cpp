@@ -362,3 +362,56 @@ KDN_EXPORT int hola_prefill(const void* q, const void* k, const void* v, int in_
   kdn::prefill_bind_workspace(a, workspace);
   return map_hip(kdn::launch_prefill(a, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream)));
 }
+
+KDN_EXPORT size_t kdn_scan_bwd_workspace_size(int B, int H, int L, int d_k, int d_v) {
+  if (B < 1 || H < 1 || L < 1 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim) return 0;
+  return kdn::scan_bwd_workspace_bytes(B * H, L, d_k, d_v);
+}
+
+KDN_EXPORT int kdn_scan_bwd(const float* q, const float* k, const float* v, const float* alpha,
+                            const float* beta, const float* state_in, const float* d_o,
+                            const float* dstate_out, float* dq, float* dk, float* dv,
+                            float* dalpha, float* dbeta, float* dstate_in, int B, int H, int L,
+                            int d_k, int d_v, int resid, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (resid != KDN_RESID_GATED && resid != KDN_RESID_PLAIN && resid != KDN_RESID_NOERASE)
+    return KDN_ERR_BAD_MODE;
+  if (B < 1 || H < 1 || L < 0 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
+    return KDN_ERR_BAD_SHAPE;
+  if ((long long)B * H > (1LL << 24) || (long long)(d_v + 31) / 32 > kMaxGridYZ)
+    return KDN_ERR_BAD_SHAPE;
+  if (L == 0) {
+    // no tokens: the initial state's gradient is the final state's
+    hipError_t e = hipSuccess;
+    if (dstate_in)
+      e = kdn::launch_copy_f32(dstate_out, dstate_in, (size_t)B * H * d_k * d_v,
+                               static_cast<hipStream_t>(stream));
+    return map_hip(e);
+  }
+  if (!q || !k || !v || !beta || !d_o || !dq || !dk || !dv || !dbeta) return KDN_ERR_NULL_POINTER;
+  if (alpha && !dalpha) return KDN_ERR_NULL_POINTER;
+  const size_t need = kdn::scan_bwd_workspace_bytes(B * H, L, d_k, d_v);
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+    return KDN_ERR_WORKSPACE;
+  kdn::BwdArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.state_in = state_in;
+  a.d_o = d_o;
+  a.dstate_out = dstate_out;
+  a.dq = dq;
+  a.dk_out = dk;
+  a.dv_out = dv;
+  a.dalpha = alpha ? dalpha : nullptr;
+  a.dbeta = dbeta;
+  a.dstate_in = dstate_in;
+  a.BH = B * H;
+  a.L = L;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.resid = resid;
+  return map_hip(kdn::launch_scan_bwd(a, workspace, static_cast<hipStream_t>(stream)));
+}

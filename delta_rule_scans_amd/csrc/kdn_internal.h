@@ -147,6 +147,35 @@ hipError_t launch_hola(const float* q, const float* k, const float* v, const flo
                        float rms_eps, int B, int H, int dk, int dv, int w, int policy,
                        hipStream_t s);
 
+// Gradients of the delta-write scan (float32); see scan_bwd.hip.
+struct BwdArgs {
+  const float* q;           // [BH, L, dk]
+  const float* k;           // [BH, L, dk]
+  const float* v;           // [BH, L, dv]
+  const float* alpha;       // [BH, L] or null (= 1)
+  const float* beta;        // [BH, L]
+  const float* state_in;    // [BH, dk, dv] or null (= 0)
+  const float* d_o;         // [BH, L, dv]
+  const float* dstate_out;  // [BH, dk, dv] or null (= 0)
+  float* dq;                // [BH, L, dk]
+  float* dk_out;            // [BH, L, dk]
+  float* dv_out;            // [BH, L, dv]
+  float* dalpha;            // [BH, L] or null
+  float* dbeta;             // [BH, L]
+  float* dstate_in;         // [BH, dk, dv] or null
+  int BH, L, dk, dv;
+  int resid;                // 0 gated, 1 plain, 2 no erase
+  // workspace parts (set by launch_scan_bwd)
+  float* ckpt = nullptr;
+  float* hist = nullptr;
+  float* dq_part = nullptr;
+  float* dk_part = nullptr;
+  float* da_part = nullptr;
+  float* db_part = nullptr;
+};
+size_t scan_bwd_workspace_bytes(int BH, int L, int dk, int dv);
+hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s);
+
 // HOLA cache over a whole prompt in blocks; see hola_prefill.hip.
 struct PrefillArgs {
   const void* q;   // [BH, L, dk] (bf16 or float32)

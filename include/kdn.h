@@ -242,6 +242,39 @@ int hola_cache_update(const float *q, const float *k, const float *v, const floa
                       int policy, void *stream);
 
 /*
+ * Gradients of the delta-write scan (reverse mode) for a loss L with given
+ * dL/do (d_o) and dL/dS_L (dstate_out). The pages give no backward pass; the
+ * library uses the adjoint of the token recurrence (c = alpha for the gated
+ * residual, 1 for the plain one, 0 without erase):
+ *   S_t = (alpha_t I - c_t beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,  o_t = S_t^T q_t,
+ *   G_t = dL/dS_t:  G_t += q_t do_t^T,  dq_t = S_t do_t,  y_t = G_t^T k_t,
+ *   dv_t = beta_t y_t,  dbeta_t = y_t . e_t,  dk_t = beta_t G_t e_t - c_t beta_t S_{t-1} y_t,
+ *   dalpha_t = <G_t, S_{t-1}> - [gated] beta_t y_t . (S_{t-1}^T k_t),
+ *   G_{t-1} = alpha_t G_t - c_t beta_t k_t y_t^T,  dS_0 = G_0.
+ * Float32 inputs and outputs, layouts as kdn_scan_fwd; the delta write only.
+ *
+ *  q, k [B,H,L,d_k], v [B,H,L,d_v], alpha (NULL = 1), beta [B,H,L], state_in
+ *            (NULL = 0): the forward call's inputs.
+ *  d_o       [B,H,L,d_v];  dstate_out [B,H,d_k,d_v] or NULL (= 0).
+ *  dq, dk    [B,H,L,d_k] out;  dv [B,H,L,d_v] out;  dalpha [B,H,L] out
+ *            (required when alpha is given, else ignored);  dbeta [B,H,L] out;
+ *            dstate_in [B,H,d_k,d_v] out or NULL.
+ *  resid     KDN_RESID_GATED, _PLAIN or _NOERASE.
+ *  workspace kdn_scan_bwd_workspace_size(...) bytes, 16-byte aligned: the
+ *            states at every 64-token chunk start, one chunk's recomputed
+ *            states per (head, 32 value columns), and per-tile partial sums.
+ * Sizes: B, H >= 1; L >= 0; 1 <= d_k, d_v <= 128. The kernel walks the
+ * tokens one by one (a reference-quality path, not a tuned one).
+ */
+size_t kdn_scan_bwd_workspace_size(int B, int H, int L, int d_k, int d_v);
+
+int kdn_scan_bwd(const float *q, const float *k, const float *v, const float *alpha,
+                 const float *beta, const float *state_in, const float *d_o,
+                 const float *dstate_out, float *dq, float *dk, float *dv, float *dalpha,
+                 float *dbeta, float *dstate_in, int B, int H, int L, int d_k, int d_v,
+                 int resid, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * The HOLA cache over a whole prompt ("A Hippocampus for Linear Attention",
  * sec. 3.3 (top-w cache by write score), sec. 3.4 eq. (7) (visible set: the
  * cache, the causal tokens of the current block and an optional null sink),

@@ -36,7 +36,8 @@ def kdn():
 def test_exports_match_header(kdn):
     declared = _header_functions()
     assert declared == sorted(["hola_cache_update", "hola_prefill", "hola_prefill_workspace_size",
-                               "kdn_scan_fwd", "kdn_scan_fwd_phase", "kdn_scan_workspace_size",
+                               "kdn_scan_bwd", "kdn_scan_bwd_workspace_size", "kdn_scan_fwd",
+                               "kdn_scan_fwd_phase", "kdn_scan_workspace_size",
                                "kdn_status_string", "kdn_step_decode", "kdn_version"])
     out = subprocess.run(["nm", "-D", "--defined-only", kdn.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -222,3 +223,27 @@ def test_prefill_rejections(kdn):
     assert _prefill(kdn) == c["KDN_ERR_WORKSPACE"]
     assert _prefill(kdn, ws=P, wsb=need - 1) == c["KDN_ERR_WORKSPACE"]
     assert _prefill(kdn, ws=P + 8, wsb=need) == c["KDN_ERR_WORKSPACE"]
+
+
+def _bwd(kdn, **kw):
+    a = dict(q=P, k=P, v=P, alpha=P, beta=P, s0=None, do=P, dso=None, dq=P, dk=P, dv=P, da=P, db=P,
+             ds0=None, B=1, H=1, L=64, dk_=128, dv_=128, resid=0, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return kdn.lib.kdn_scan_bwd(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["s0"], a["do"],
+                                a["dso"], a["dq"], a["dk"], a["dv"], a["da"], a["db"], a["ds0"],
+                                a["B"], a["H"], a["L"], a["dk_"], a["dv_"], a["resid"], a["ws"],
+                                a["wsb"], a["stream"])
+
+
+def test_backward_rejections(kdn):
+    c = _header_constants()
+    need = kdn.lib.kdn_scan_bwd_workspace_size(1, 1, 64, 128, 128)
+    # one 64-token checkpoint and 65 recomputed states per 32-column tile, partials
+    assert need >= 4 * (1 + 65) * 128 * 32 * 4
+    assert _bwd(kdn, resid=3) == c["KDN_ERR_BAD_MODE"]
+    assert _bwd(kdn, dk_=129) == c["KDN_ERR_BAD_SHAPE"]
+    assert _bwd(kdn, L=-1) == c["KDN_ERR_BAD_SHAPE"]
+    assert _bwd(kdn, do=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _bwd(kdn, da=None) == c["KDN_ERR_NULL_POINTER"]
+    assert _bwd(kdn) == c["KDN_ERR_WORKSPACE"]
+    assert _bwd(kdn, ws=P, wsb=need - 1) == c["KDN_ERR_WORKSPACE"]
