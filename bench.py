@@ -76,6 +76,24 @@ def measured_traffic(kernel_ms):
     return rec["hbm_read_bytes"] + rec["hbm_write_bytes"]
 
 
+# The GPU runs at its idle clock until it has been busy for a few tens of
+# milliseconds (measured: the gated step takes 0.176 ms after 3 warm-up steps
+# and 0.154 ms from 300 on), so warm-up always lasts at least this long on top
+# of the requested steps. It is untimed.
+MIN_WARMUP_S = 0.25
+
+
+def _warm(torch, step, warmup):
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.time()
+    while time.time() - t0 < MIN_WARMUP_S:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+
+
 def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
@@ -108,9 +126,7 @@ def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True):
                          cov_out=cov_out, q_noise_var=qvar, state_out=s_out, o=o, chunk=C,
                          mode=mode, workspace=ws, phase=phase)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    _warm(torch, step, warmup)
     e0, e1 = _events(torch, 2)
     e0.record()
     for _ in range(steps):
@@ -163,10 +179,7 @@ def bench_prefill(kdn, torch, steps, warmup, block=256, w=64):
         kdn.hola_prefill(t["q"], t["k"], t["v"], m, 0, cache, block=block, o_cache=oc,
                          workspace=pws)
 
-    for _ in range(warmup):
-        scan()
-        prefill()
-    torch.cuda.synchronize()
+    _warm(torch, lambda: (scan(), prefill()), warmup)
     ev = _events(torch, 3 * steps)
     for i in range(steps):
         ev[3 * i].record()
@@ -205,9 +218,7 @@ def bench_backward(kdn, torch, steps, warmup):
     def step():
         kdn.kdn_scan_bwd(t["q"], t["k"], t["v"], t["alpha"], t["beta"], d_o, workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    _warm(torch, step, warmup)
     e0, e1 = _events(torch, 2)
     e0.record()
     for _ in range(steps):
@@ -295,7 +306,7 @@ def cpu_baseline(name="gated", seconds_target=15.0):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -334,6 +345,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_s": MIN_WARMUP_S,
         "ms_per_step": round(main_res["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
