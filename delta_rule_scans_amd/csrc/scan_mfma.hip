@@ -494,6 +494,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, si
                                            (int)(bytes > 0x7fffffffu ? 0x7fffffffu : bytes),
                                            0x00020000);
 }
+// Cache policy of the output stores: sc0 nt, a streaming write that does not
+// allocate in L2. The outputs are never read back by the kernel, and keeping
+// them out of L2 leaves it to the keys, queries and records that the four d_v
+// slices of a head share (measured: the state kernel 18% faster than with
+// default stores; non-temporal loads are much slower and are not used).
+constexpr int kStreamStore = 3;
+
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
@@ -973,11 +980,13 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
                                   ((uint32_t)f32_to_bf16(o[tb][4 * q4 + 1]) << 16);
               const uint32_t hi = (uint32_t)f32_to_bf16(o[tb][4 * q4 + 2]) |
                                   ((uint32_t)f32_to_bf16(o[tb][4 * q4 + 3]) << 16);
-              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, make_uint2(lo, hi)), ro, off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, make_uint2(lo, hi)), ro, off, 0,
+                                                    kStreamStore);
             } else {
               const uint4 w4 = make_uint4(__float_as_uint(o[tb][4 * q4]), __float_as_uint(o[tb][4 * q4 + 1]),
                                           __float_as_uint(o[tb][4 * q4 + 2]), __float_as_uint(o[tb][4 * q4 + 3]));
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w4), ro, off, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w4), ro, off, 0,
+                                                     kStreamStore);
             }
           }
       }
