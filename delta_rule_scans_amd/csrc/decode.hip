@@ -162,7 +162,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
     m[bh] = score_kind == 1 ? sqrtf(ee) / vscale : (score_kind == 2 ? ws * sqrtf(vv) : ws * sqrtf(ee));
   }
 
-  // S <- alpha S + b e^T
+  // S <- alpha S + b e^T, streamed back (the state is not read again here)
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(S, (size_t)dk * dv * sizeof(float));
 #pragma unroll
   for (int s = 0; s < 16; ++s) {
     const int i = rg + 8 * s;
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
           x.y = fmaf(a, reg[s][1], bi * se[4 * cg + 1]);
           x.z = fmaf(a, reg[s][2], bi * se[4 * cg + 2]);
           x.w = fmaf(a, reg[s][3], bi * se[4 * cg + 3]);
-          *reinterpret_cast<float4*>(S + (size_t)i * dv + 4 * cg) = x;
+          stream_store16(rS, (i * dv + 4 * cg) * (int)sizeof(float), x);
         }
       } else {
 #pragma unroll

@@ -21,6 +21,27 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end read 0,
+// stores past it are dropped. The base must be uniform across the wavefront.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(bytes > 0x7fffffffu ? 0x7fffffffu : bytes),
+                                           0x00020000);
+}
+
+// Streaming store (cache policy sc0 nt): written once and not read back by the
+// kernel, so it does not allocate in L2.
+constexpr int kStreamStore = 3;
+__device__ __forceinline__ void stream_store16(__amdgpu_buffer_rsrc_t r, int off, float4 x) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  __builtin_amdgcn_raw_buffer_store_b128(
+      u4{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)}, r,
+      off, 0, kStreamStore);
+}
+__device__ __forceinline__ void stream_store4(__amdgpu_buffer_rsrc_t r, int off, float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, kStreamStore);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   __device__ static __forceinline__ float load(const float* p, size_t i) { return p[i]; }

@@ -250,6 +250,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
     // exponents of R and Cf stay in [-100, 100] unless the decay is extreme
     const float span = fabsf(lgr - lg);
     const bool extreme = __ballot(span > 100.f) != 0;
+    // default (write-back) stores: the state kernel reads the records soon after
     float4* sc = reinterpret_cast<float4*>(rec + rec_s_off(gain));
     sc[3 * lane] = make_float4(exp2f(lg), w, lg, bs);
     sc[3 * lane + 1] = make_float4(extreme ? 0.f : bs * exp2f(lgr - lg), extreme ? 0.f : exp2f(lg - lgr),
@@ -488,18 +489,11 @@ __device__ __forceinline__ half4 ld_tr(const _Float16* p) {
   return __builtin_bit_cast(half4, v);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, size_t bytes) {
-  // raw buffer: stride 0, accesses at offsets >= `bytes` read 0 / are dropped
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)(bytes > 0x7fffffffu ? 0x7fffffffu : bytes),
-                                           0x00020000);
-}
-// Cache policy of the output stores: sc0 nt, a streaming write that does not
-// allocate in L2. The outputs are never read back by the kernel, and keeping
-// them out of L2 leaves it to the keys, queries and records that the four d_v
-// slices of a head share (measured: the state kernel 18% faster than with
-// default stores; non-temporal loads are much slower and are not used).
-constexpr int kStreamStore = 3;
+// The output stores stream (kStreamStore, kdn_internal.h): the outputs are
+// never read back by the kernel, and keeping them out of L2 leaves it to the
+// keys, queries and records that the four d_v slices of a head share
+// (measured: the state kernel 18% faster than with default stores;
+// non-temporal loads are much slower and are not used).
 
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
