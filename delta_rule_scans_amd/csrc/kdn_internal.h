@@ -38,6 +38,14 @@ __device__ __forceinline__ void stream_store16(__amdgpu_buffer_rsrc_t r, int off
       u4{__float_as_uint(x.x), __float_as_uint(x.y), __float_as_uint(x.z), __float_as_uint(x.w)}, r,
       off, 0, kStreamStore);
 }
+// Streaming load (sc0 nt) for data read exactly once by the whole grid. Data
+// that other workgroups read again must use ordinary loads.
+__device__ __forceinline__ float4 stream_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+  const u4 x = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kStreamStore);
+  return make_float4(__uint_as_float(x[0]), __uint_as_float(x[1]), __uint_as_float(x[2]),
+                     __uint_as_float(x[3]));
+}
 __device__ __forceinline__ void stream_store4(__amdgpu_buffer_rsrc_t r, int off, float x) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, kStreamStore);
 }
