@@ -14,8 +14,9 @@
 // Each coordinate's map p -> p_new is a linear-fractional (Moebius) map, so a
 // run of tokens composes into one 2x2 matrix (the abstract's "uncertainty
 // recurrences are Mobius maps"). The DIAG path uses that: one pass composes the
-// maps of every chunk in parallel, a second pass starts each chunk from the
-// composition of the chunks before it and recomputes the per-token values.
+// maps of every chunk in parallel, a short sequential pass over chunks applies
+// them to get every chunk's starting variances, and a third pass recomputes the
+// per-token values of every chunk in parallel.
 #include "kdn_internal.h"
 
 namespace kdn {
@@ -39,24 +40,47 @@ template <typename Tk>
 __global__ __launch_bounds__(128) void diag_maps_kernel(const Tk* k, const float* alpha,
                                                         const float* r, float qvar, float4* maps,
                                                         int L, int dk, int C, int nchunks) {
+  __shared__ float sa[64], sr[64];
   const int bh = blockIdx.x, c = blockIdx.y, i = threadIdx.x;
-  if (i >= dk) return;
   const int t0 = c * C, n = min(C, L - t0);
+  if (i < n) {
+    const size_t g = (size_t)bh * L + t0 + i;
+    sa[i] = alpha ? alpha[g] : 1.f;
+    sr[i] = r ? r[g] : 1.f;
+  }
+  __syncthreads();
+  if (i >= dk) return;
   float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f;
   for (int t = 0; t < n; ++t) {
     const size_t g = (size_t)bh * L + t0 + t;
     float t00, t01, t10, t11;
-    token_map(alpha ? alpha[g] : 1.f, qvar, r ? r[g] : 1.f, Elem<Tk>::load(k, g * dk + i), t00,
-              t01, t10, t11);
+    token_map(sa[t], qvar, sr[t], Elem<Tk>::load(k, g * dk + i), t00, t01, t10, t11);
     const float n00 = fmaf(t00, m00, t01 * m10), n01 = fmaf(t00, m01, t01 * m11);
     const float n10 = fmaf(t10, m00, t11 * m10), n11 = fmaf(t10, m01, t11 * m11);
-    const float sc = 1.f / fmaxf(fmaxf(n00, n01), fmaxf(n10, n11));
+    // projective scale: any positive factor will do, so an approximate reciprocal
+    const float sc = __builtin_amdgcn_rcpf(fmaxf(fmaxf(n00, n01), fmaxf(n10, n11)));
     m00 = n00 * sc;
     m01 = n01 * sc;
     m10 = n10 * sc;
     m11 = n11 * sc;
   }
   maps[((size_t)bh * nchunks + c) * dk + i] = make_float4(m00, m01, m10, m11);
+}
+
+// One thread per (head, coordinate): the variance at every chunk start, by
+// applying the chunk maps in order; stored over the map's first entry.
+__global__ __launch_bounds__(128) void diag_prefix_kernel(const float* cov_in, float4* maps,
+                                                          int BH, int dk, int nchunks) {
+  const int idx = blockIdx.x * 128 + threadIdx.x;
+  if (idx >= BH * dk) return;
+  const int bh = idx / dk, i = idx - bh * dk;
+  float p = cov_in[idx];
+  float4* m = maps + (size_t)bh * nchunks * dk + i;
+  for (int c = 0; c < nchunks; ++c) {
+    const float4 M = m[(size_t)c * dk];
+    m[(size_t)c * dk].x = p;
+    p = fmaf(M.x, p, M.y) / fmaf(M.z, p, M.w);
+  }
 }
 
 // One workgroup per (head, chunk), one thread per coordinate.
@@ -74,11 +98,7 @@ __global__ __launch_bounds__(128) void diag_gains_kernel(const Tk* k, const floa
   float* sInv = sPK2 + C * KP;   // [C] 1 / s_t
   const int t0 = c * C, n = min(C, L - t0);
   if (i < dk) {
-    float p = cov_in[(size_t)bh * dk + i];
-    for (int cc = 0; cc < c; ++cc) {
-      const float4 M = maps[((size_t)bh * nchunks + cc) * dk + i];
-      p = fmaf(M.x, p, M.y) / fmaf(M.z, p, M.w);
-    }
+    float p = maps[((size_t)bh * nchunks + c) * dk + i].x;  // the chunk's starting variance
     for (int t = 0; t < n; ++t) {
       const size_t g = (size_t)bh * L + t0 + t;
       const float a = alpha ? alpha[g] : 1.f;
@@ -202,7 +222,7 @@ __global__ __launch_bounds__(256) void iso_maps_kernel(const Tk* k, const float*
       const float t00 = a2, t01 = Q, t10 = cc * a2, t11 = fmaf(cc, Q, 1.f);
       const float n00 = fmaf(t00, m00, t01 * m10), n01 = fmaf(t00, m01, t01 * m11);
       const float n10 = fmaf(t10, m00, t11 * m10), n11 = fmaf(t10, m01, t11 * m11);
-      const float sc = 1.f / fmaxf(fmaxf(n00, n01), fmaxf(n10, n11));
+      const float sc = __builtin_amdgcn_rcpf(fmaxf(fmaxf(n00, n01), fmaxf(n10, n11)));
       m00 = n00 * sc;
       m01 = n01 * sc;
       m10 = n10 * sc;
@@ -212,8 +232,23 @@ __global__ __launch_bounds__(256) void iso_maps_kernel(const Tk* k, const float*
   }
 }
 
-// Per (head, chunk): p at the chunk start from the maps of the chunks before
-// it, then the chunk's tokens in order: the write strengths beta_t and p.
+// One thread per head: the variance at every chunk start (over the map's
+// first entry).
+__global__ __launch_bounds__(64) void iso_prefix_kernel(const float* cov_in, float4* maps, int BH,
+                                                        int nchunks) {
+  const int bh = blockIdx.x * 64 + threadIdx.x;
+  if (bh >= BH) return;
+  float p = cov_in[bh];
+  float4* m = maps + (size_t)bh * nchunks;
+  for (int c = 0; c < nchunks; ++c) {
+    const float4 M = m[c];
+    m[c].x = p;
+    p = fmaf(M.x, p, M.y) / fmaf(M.z, p, M.w);
+  }
+}
+
+// Per (head, chunk): from the chunk's starting p (iso_prefix_kernel), the
+// chunk's tokens in order: the write strengths beta_t and p.
 __global__ __launch_bounds__(64) void iso_beta_kernel(const float* alpha, const float* r,
                                                       const float* kk, const float* cov_in,
                                                       float* cov_out, float qvar,
@@ -224,11 +259,7 @@ __global__ __launch_bounds__(64) void iso_beta_kernel(const float* alpha, const 
   const int t0 = c * C, n = min(C, L - t0);
   const size_t tok = (size_t)bh * L + t0;
   if (tid == 0) {
-    float p = cov_in[bh];
-    for (int cc = 0; cc < c; ++cc) {
-      const float4 M = maps[(size_t)bh * nchunks + cc];
-      p = fmaf(M.x, p, M.y) / fmaf(M.z, p, M.w);
-    }
+    float p = maps[(size_t)bh * nchunks + c].x;  // the chunk's starting variance
     for (int t = 0; t < n; ++t) {
       const float a = alpha ? alpha[tok + t] : 1.f, rt = r ? r[tok + t] : 1.f;
       const float pm = fmaf(a * a, p, (1.f - a) * (1.f + a) * qvar);
@@ -251,6 +282,10 @@ hipError_t diag_typed(const void* k, const float* alpha, const float* r, const f
                      static_cast<const Tk*>(k), alpha, r, qvar, reinterpret_cast<float4*>(maps), L,
                      dk, C, nchunks);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(diag_prefix_kernel, dim3((BH * dk + 127) / 128), dim3(128), 0, s, cov_in,
+                     reinterpret_cast<float4*>(maps), BH, dk, nchunks);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t lds = ((size_t)2 * C * (dk + 1) + C) * sizeof(float);
   auto kern = diag_gains_kernel<Tk, Tg>;
@@ -304,6 +339,10 @@ hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const
                        static_cast<const float*>(k), alpha, r, q_noise_var, kk,
                        reinterpret_cast<float4*>(maps), L, dk, chunk, nchunks);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(iso_prefix_kernel, dim3((BH + 63) / 64), dim3(64), 0, s, cov_in,
+                     reinterpret_cast<float4*>(maps), BH, nchunks);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(iso_beta_kernel, dim3(BH, nchunks), dim3(64), 0, s, alpha, r, kk, cov_in,
                      cov_out, q_noise_var, reinterpret_cast<const float4*>(maps), beta, L, dk,
