@@ -76,55 +76,62 @@ __global__ __launch_bounds__(128) void diag_prefix_kernel(const float* cov_in, f
   const int bh = idx / dk, i = idx - bh * dk;
   float p = cov_in[idx];
   float4* m = maps + (size_t)bh * nchunks * dk + i;
-  for (int c = 0; c < nchunks; ++c) {
-    const float4 M = m[(size_t)c * dk];
-    m[(size_t)c * dk].x = p;
-    p = fmaf(M.x, p, M.y) / fmaf(M.z, p, M.w);
+  for (int c0 = 0; c0 < nchunks; c0 += 8) {  // eight maps in flight at a time
+    float4 M[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < nchunks) M[j] = m[(size_t)(c0 + j) * dk];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < nchunks) {
+        m[(size_t)(c0 + j) * dk].x = p;
+        p = fmaf(M[j].x, p, M[j].y) / fmaf(M[j].z, p, M[j].w);
+      }
   }
 }
 
-// One workgroup per (head, chunk), one thread per coordinate.
+// One wavefront per (head, chunk): lane l carries coordinates l and l + 64
+// through the chunk's tokens in order; the sum over coordinates in
+// s_t = r_t + sum_i p-_i k_i^2 is a wavefront reduction, so the gains of token
+// t are written as soon as it is done. No LDS and no barriers, so many
+// wavefronts per SIMD hide the memory latency.
+__device__ __forceinline__ float wave_sum64(float x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
 template <typename Tk, typename Tg>
-__global__ __launch_bounds__(128) void diag_gains_kernel(const Tk* k, const float* alpha,
-                                                         const float* r, const float* cov_in,
-                                                         float* cov_out, float qvar,
-                                                         const float4* maps, Tg* gains, int L,
-                                                         int dk, int C, int nchunks) {
-  extern __shared__ float lds[];
-  const int bh = blockIdx.x, c = blockIdx.y, i = threadIdx.x;
-  const int KP = dk + 1;
-  float* sPK = lds;              // [C][KP] p-_i k_i
-  float* sPK2 = sPK + C * KP;    // [C][KP] p-_i k_i^2
-  float* sInv = sPK2 + C * KP;   // [C] 1 / s_t
+__global__ __launch_bounds__(256) void diag_gains_kernel(const Tk* k, const float* alpha,
+                                                         const float* r, float* cov_out,
+                                                         float qvar, const float4* maps,
+                                                         Tg* gains, int BH, int L, int dk,
+                                                         int C, int nchunks) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave >= BH * nchunks) return;
+  const int bh = wave / nchunks, c = wave - bh * nchunks;
   const int t0 = c * C, n = min(C, L - t0);
-  if (i < dk) {
-    float p = maps[((size_t)bh * nchunks + c) * dk + i].x;  // the chunk's starting variance
-    for (int t = 0; t < n; ++t) {
-      const size_t g = (size_t)bh * L + t0 + t;
-      const float a = alpha ? alpha[g] : 1.f;
-      const float rt = r ? r[g] : 1.f;
-      const float kv = Elem<Tk>::load(k, g * dk + i);
-      const float pm = fmaf(a * a, p, (1.f - a) * (1.f + a) * qvar);
-      const float pk = pm * kv;
-      sPK[t * KP + i] = pk;
-      sPK2[t * KP + i] = pk * kv;
-      p = pm * rt / fmaf(pk, kv, rt);
-    }
-    if (c == nchunks - 1 && cov_out) cov_out[(size_t)bh * dk + i] = p;
+  const size_t tok = (size_t)bh * L + t0;
+  const int i0 = lane, i1 = lane + 64;
+  const bool ok0 = i0 < dk, ok1 = i1 < dk;
+  const float4* mp = maps + ((size_t)bh * nchunks + c) * dk;
+  float p0 = ok0 ? mp[i0].x : 0.f, p1 = ok1 ? mp[i1].x : 0.f;  // chunk-start variances
+  for (int t = 0; t < n; ++t) {
+    const size_t g = tok + t;
+    const float a = alpha ? alpha[g] : 1.f, rt = r ? r[g] : 1.f;
+    const float a2 = a * a, Q = (1.f - a) * (1.f + a) * qvar;
+    const float k0 = ok0 ? Elem<Tk>::load(k, g * dk + i0) : 0.f;
+    const float k1 = ok1 ? Elem<Tk>::load(k, g * dk + i1) : 0.f;
+    const float pm0 = fmaf(a2, p0, Q), pm1 = fmaf(a2, p1, Q);
+    const float pk0 = pm0 * k0, pk1 = pm1 * k1;
+    const float inv = 1.f / (rt + wave_sum64(fmaf(pk0, k0, pk1 * k1)));
+    if (ok0) Elem<Tg>::store(gains, g * dk + i0, pk0 * inv);
+    if (ok1) Elem<Tg>::store(gains, g * dk + i1, pk1 * inv);
+    p0 = pm0 * rt / fmaf(pk0, k0, rt);
+    p1 = pm1 * rt / fmaf(pk1, k1, rt);
   }
-  __syncthreads();
-  if (i < n) {
-    const size_t g = (size_t)bh * L + t0 + i;
-    float s = r ? r[g] : 1.f;
-    for (int j = 0; j < dk; ++j) s += sPK2[i * KP + j];
-    sInv[i] = 1.f / s;
-  }
-  __syncthreads();
-  if (i < dk) {
-    for (int t = 0; t < n; ++t) {
-      const size_t g = ((size_t)bh * L + t0 + t) * dk + i;
-      Elem<Tg>::store(gains, g, sPK[t * KP + i] * sInv[t]);
-    }
+  if (c == nchunks - 1 && cov_out) {
+    if (ok0) cov_out[(size_t)bh * dk + i0] = p0;
+    if (ok1) cov_out[(size_t)bh * dk + i1] = p1;
   }
 }
 
@@ -194,11 +201,15 @@ __global__ __launch_bounds__(256) void iso_maps_kernel(const Tk* k, const float*
                                                        const float* r, float qvar, float* kk,
                                                        float4* maps, int L, int dk, int C,
                                                        int nchunks) {
-  __shared__ float s_kk[128];
+  __shared__ float s_kk[128], s_a[128], s_r[128];
   const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int grp = tid >> 4, j = tid & 15;
   const int t0 = c * C, n = min(C, L - t0);
   const size_t tok = (size_t)bh * L + t0;
+  if (tid < n) {
+    s_a[tid] = alpha ? alpha[tok + tid] : 1.f;
+    s_r[tid] = r ? r[tok + tid] : 1.f;
+  }
   for (int t = grp; t < n; t += 16) {
     float acc = 0.f;
     for (int i = j; i < dk; i += 16) {
@@ -216,7 +227,7 @@ __global__ __launch_bounds__(256) void iso_maps_kernel(const Tk* k, const float*
   if (tid == 0) {
     float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f;
     for (int t = 0; t < n; ++t) {
-      const float a = alpha ? alpha[tok + t] : 1.f, rt = r ? r[tok + t] : 1.f;
+      const float a = s_a[t], rt = s_r[t];
       const float a2 = a * a, Q = (1.f - a) * (1.f + a) * qvar;
       const float cc = s_kk[t] / (dk * rt);
       const float t00 = a2, t01 = Q, t10 = cc * a2, t11 = fmaf(cc, Q, 1.f);
@@ -240,10 +251,17 @@ __global__ __launch_bounds__(64) void iso_prefix_kernel(const float* cov_in, flo
   if (bh >= BH) return;
   float p = cov_in[bh];
   float4* m = maps + (size_t)bh * nchunks;
-  for (int c = 0; c < nchunks; ++c) {
-    const float4 M = m[c];
-    m[c].x = p;
-    p = fmaf(M.x, p, M.y) / fmaf(M.z, p, M.w);
+  for (int c0 = 0; c0 < nchunks; c0 += 8) {  // eight maps in flight at a time
+    float4 M[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < nchunks) M[j] = m[c0 + j];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < nchunks) {
+        m[c0 + j].x = p;
+        p = fmaf(M[j].x, p, M[j].y) / fmaf(M[j].z, p, M[j].w);
+      }
   }
 }
 
@@ -254,16 +272,22 @@ __global__ __launch_bounds__(64) void iso_beta_kernel(const float* alpha, const 
                                                       float* cov_out, float qvar,
                                                       const float4* maps, float* beta, int L,
                                                       int dk, int C, int nchunks) {
-  __shared__ float s_b[128];
+  __shared__ float s_b[128], s_a[128], s_r[128], s_k[128];
   const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
   const int t0 = c * C, n = min(C, L - t0);
   const size_t tok = (size_t)bh * L + t0;
+  for (int t = tid; t < n; t += 64) {
+    s_a[t] = alpha ? alpha[tok + t] : 1.f;
+    s_r[t] = r ? r[tok + t] : 1.f;
+    s_k[t] = kk[tok + t];
+  }
+  __syncthreads();
   if (tid == 0) {
     float p = maps[(size_t)bh * nchunks + c].x;  // the chunk's starting variance
     for (int t = 0; t < n; ++t) {
-      const float a = alpha ? alpha[tok + t] : 1.f, rt = r ? r[tok + t] : 1.f;
+      const float a = s_a[t], rt = s_r[t];
       const float pm = fmaf(a * a, p, (1.f - a) * (1.f + a) * qvar);
-      const float kt = kk[tok + t];
+      const float kt = s_k[t];
       s_b[t] = pm / fmaf(pm, kt, rt);
       p = pm * (dk * rt) / fmaf(pm, kt, dk * rt);
     }
@@ -287,14 +311,11 @@ hipError_t diag_typed(const void* k, const float* alpha, const float* r, const f
                      reinterpret_cast<float4*>(maps), BH, dk, nchunks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t lds = ((size_t)2 * C * (dk + 1) + C) * sizeof(float);
-  auto kern = diag_gains_kernel<Tk, Tg>;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(BH, nchunks), dim3(128), lds, s, static_cast<const Tk*>(k), alpha,
-                     r, cov_in, cov_out, qvar, reinterpret_cast<const float4*>(maps),
-                     static_cast<Tg*>(gains), L, dk, C, nchunks);
+  const int waves = BH * nchunks;
+  hipLaunchKernelGGL((diag_gains_kernel<Tk, Tg>), dim3((waves + 3) / 4), dim3(256), 0, s,
+                     static_cast<const Tk*>(k), alpha, r, cov_out, qvar,
+                     reinterpret_cast<const float4*>(maps), static_cast<Tg*>(gains), BH, L, dk, C,
+                     nchunks);
   return hipGetLastError();
 }
 
