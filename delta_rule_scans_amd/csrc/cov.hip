@@ -17,6 +17,8 @@
 // maps of every chunk in parallel, a short sequential pass over chunks applies
 // them to get every chunk's starting variances, and a third pass recomputes the
 // per-token values of every chunk in parallel.
+#include <type_traits>
+
 #include "kdn_internal.h"
 
 namespace kdn {
@@ -194,53 +196,99 @@ __global__ __launch_bounds__(256) void full_gains_kernel(const Tk* k, const floa
 // write with that beta. In p, one token is the Moebius map
 // p -> (a^2 p + Q) / (c a^2 p + c Q + 1) with c = ||k||^2 / (d_k r).
 
-// Per (head, chunk): ||k_t||^2 of the chunk's tokens (16 lanes per token) and
-// the composition of the chunk's token maps.
+// A token's map on p, projectively: p -> (a^2 p + Q) / (c a^2 p + c Q + 1), c =
+// ||k||^2 / (d_k r), as the matrix [[a^2, Q], [c a^2, c Q + 1]].
+struct Mob {
+  float a, b, c, d;
+};
+__device__ __forceinline__ Mob mob_token(float al, float rt, float kk, float qvar, int dk) {
+  const float a2 = al * al, Q = (1.f - al) * (1.f + al) * qvar, cc = kk / (dk * rt);
+  return Mob{a2, Q, cc * a2, fmaf(cc, Q, 1.f)};
+}
+// x after y (x y), scaled so that the largest entry is 1 (any positive scale
+// is the same map).
+__device__ __forceinline__ Mob mob_mul(Mob x, Mob y) {
+  Mob z{fmaf(x.a, y.a, x.b * y.c), fmaf(x.a, y.b, x.b * y.d), fmaf(x.c, y.a, x.d * y.c),
+        fmaf(x.c, y.b, x.d * y.d)};
+  const float sc = __builtin_amdgcn_rcpf(fmaxf(fmaxf(z.a, z.b), fmaxf(z.c, z.d)));
+  return Mob{z.a * sc, z.b * sc, z.c * sc, z.d * sc};
+}
+__device__ __forceinline__ Mob mob_shfl_up(Mob x, int off, int lane) {
+  Mob y{__shfl_up(x.a, off, 64), __shfl_up(x.b, off, 64), __shfl_up(x.c, off, 64),
+        __shfl_up(x.d, off, 64)};
+  return lane >= off ? y : Mob{1.f, 0.f, 0.f, 1.f};
+}
+// Inclusive scan over the wavefront in token order: lane t gets M_t ... M_0.
+__device__ __forceinline__ Mob mob_scan(Mob m, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) m = mob_mul(m, mob_shfl_up(m, off, lane));
+  return m;
+}
+
+// One wavefront per (head, chunk), lane t = token t: ||k_t||^2 (the wavefront
+// reads each key row together, coalesced, and reduces it) and the chunk's map,
+// the product of its token maps by a wavefront scan.
 template <typename Tk>
 __global__ __launch_bounds__(256) void iso_maps_kernel(const Tk* k, const float* alpha,
                                                        const float* r, float qvar, float* kk,
-                                                       float4* maps, int L, int dk, int C,
+                                                       float4* maps, int BH, int L, int dk, int C,
                                                        int nchunks) {
-  __shared__ float s_kk[128], s_a[128], s_r[128];
-  const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
-  const int grp = tid >> 4, j = tid & 15;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave >= BH * nchunks) return;
+  const int bh = wave / nchunks, c = wave - bh * nchunks;
   const int t0 = c * C, n = min(C, L - t0);
-  const size_t tok = (size_t)bh * L + t0;
-  if (tid < n) {
-    s_a[tid] = alpha ? alpha[tok + tid] : 1.f;
-    s_r[tid] = r ? r[tok + tid] : 1.f;
-  }
-  for (int t = grp; t < n; t += 16) {
-    float acc = 0.f;
-    for (int i = j; i < dk; i += 16) {
-      const float x = Elem<Tk>::load(k, (tok + t) * dk + i);
-      acc = fmaf(x, x, acc);
+  const size_t g = (size_t)bh * L + t0 + lane;
+  const size_t row0 = (size_t)bh * L + t0;
+  float mine = 0.f;
+  if constexpr (std::is_same<Tk, uint16_t>::value) {
+    if (dk == 128) {
+      // 16 lanes per row, 16-byte loads: rows 4 j + lane / 16 in pass j, all
+      // 16 passes in flight; lane t then picks its row's sum
+      const int q = lane >> 4, e = lane & 15;
+      float part[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int t = 4 * j + q;
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (t < n) u = *reinterpret_cast<const uint4*>(k + (row0 + t) * 128 + 8 * e);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        float acc = 0.f;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const float lo = __uint_as_float(w[h] << 16), hi = __uint_as_float(w[h] & 0xffff0000u);
+          acc = fmaf(lo, lo, fmaf(hi, hi, acc));
+        }
+        part[j] = acc;
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        float x = part[j];
+        x += __shfl_xor(x, 8, 16);
+        x += __shfl_xor(x, 4, 16);
+        x += __shfl_xor(x, 2, 16);
+        x += __shfl_xor(x, 1, 16);
+        const float v = __shfl(x, 16 * (lane & 3), 64);  // row 4 j + lane % 4
+        if ((lane >> 2) == j) mine = v;
+      }
+      goto have_norms;
     }
-    acc += __shfl_xor(acc, 8, 16);
-    acc += __shfl_xor(acc, 4, 16);
-    acc += __shfl_xor(acc, 2, 16);
-    acc += __shfl_xor(acc, 1, 16);
-    if (j == 0) s_kk[t] = acc;
   }
-  __syncthreads();
-  if (tid < n) kk[tok + tid] = s_kk[tid];
-  if (tid == 0) {
-    float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f;
-    for (int t = 0; t < n; ++t) {
-      const float a = s_a[t], rt = s_r[t];
-      const float a2 = a * a, Q = (1.f - a) * (1.f + a) * qvar;
-      const float cc = s_kk[t] / (dk * rt);
-      const float t00 = a2, t01 = Q, t10 = cc * a2, t11 = fmaf(cc, Q, 1.f);
-      const float n00 = fmaf(t00, m00, t01 * m10), n01 = fmaf(t00, m01, t01 * m11);
-      const float n10 = fmaf(t10, m00, t11 * m10), n11 = fmaf(t10, m01, t11 * m11);
-      const float sc = __builtin_amdgcn_rcpf(fmaxf(fmaxf(n00, n01), fmaxf(n10, n11)));
-      m00 = n00 * sc;
-      m01 = n01 * sc;
-      m10 = n10 * sc;
-      m11 = n11 * sc;
-    }
-    maps[(size_t)bh * nchunks + c] = make_float4(m00, m01, m10, m11);
+  for (int t = 0; t < n; ++t) {
+    const float x0 = lane < dk ? Elem<Tk>::load(k, (row0 + t) * dk + lane) : 0.f;
+    const float x1 = lane + 64 < dk ? Elem<Tk>::load(k, (row0 + t) * dk + lane + 64) : 0.f;
+    const float sq = wave_sum64(fmaf(x0, x0, x1 * x1));
+    if (lane == t) mine = sq;
   }
+have_norms:
+  Mob m{1.f, 0.f, 0.f, 1.f};
+  if (lane < n) {
+    kk[g] = mine;
+    m = mob_token(alpha ? alpha[g] : 1.f, r ? r[g] : 1.f, mine, qvar, dk);
+  }
+  m = mob_scan(m, lane);
+  const Mob tot{__shfl(m.a, n - 1, 64), __shfl(m.b, n - 1, 64), __shfl(m.c, n - 1, 64),
+                __shfl(m.d, n - 1, 64)};
+  if (lane == 0) maps[(size_t)bh * nchunks + c] = make_float4(tot.a, tot.b, tot.c, tot.d);
 }
 
 // One thread per head: the variance at every chunk start (over the map's
@@ -265,36 +313,33 @@ __global__ __launch_bounds__(64) void iso_prefix_kernel(const float* cov_in, flo
   }
 }
 
-// Per (head, chunk): from the chunk's starting p (iso_prefix_kernel), the
-// chunk's tokens in order: the write strengths beta_t and p.
-__global__ __launch_bounds__(64) void iso_beta_kernel(const float* alpha, const float* r,
-                                                      const float* kk, const float* cov_in,
-                                                      float* cov_out, float qvar,
-                                                      const float4* maps, float* beta, int L,
-                                                      int dk, int C, int nchunks) {
-  __shared__ float s_b[128], s_a[128], s_r[128], s_k[128];
-  const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x;
+// One wavefront per (head, chunk), lane t = token t: the variance before the
+// token from the chunk's starting p (iso_prefix_kernel) and an exclusive scan
+// of the token maps, then the write strength beta_t.
+__global__ __launch_bounds__(256) void iso_beta_kernel(const float* alpha, const float* r,
+                                                       const float* kk, float* cov_out, float qvar,
+                                                       const float4* maps, float* beta, int BH,
+                                                       int L, int dk, int C, int nchunks) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave >= BH * nchunks) return;
+  const int bh = wave / nchunks, c = wave - bh * nchunks;
   const int t0 = c * C, n = min(C, L - t0);
-  const size_t tok = (size_t)bh * L + t0;
-  for (int t = tid; t < n; t += 64) {
-    s_a[t] = alpha ? alpha[tok + t] : 1.f;
-    s_r[t] = r ? r[tok + t] : 1.f;
-    s_k[t] = kk[tok + t];
+  const size_t g = (size_t)bh * L + t0 + lane;
+  const float p0 = maps[(size_t)bh * nchunks + c].x;  // the chunk's starting variance
+  float al = 1.f, rt = 1.f, kt = 0.f;
+  Mob m{1.f, 0.f, 0.f, 1.f};
+  if (lane < n) {
+    al = alpha ? alpha[g] : 1.f;
+    rt = r ? r[g] : 1.f;
+    kt = kk[g];
+    m = mob_token(al, rt, kt, qvar, dk);
   }
-  __syncthreads();
-  if (tid == 0) {
-    float p = maps[(size_t)bh * nchunks + c].x;  // the chunk's starting variance
-    for (int t = 0; t < n; ++t) {
-      const float a = s_a[t], rt = s_r[t];
-      const float pm = fmaf(a * a, p, (1.f - a) * (1.f + a) * qvar);
-      const float kt = s_k[t];
-      s_b[t] = pm / fmaf(pm, kt, rt);
-      p = pm * (dk * rt) / fmaf(pm, kt, dk * rt);
-    }
-    if (c == nchunks - 1 && cov_out) cov_out[bh] = p;
-  }
-  __syncthreads();
-  for (int t = tid; t < n; t += 64) beta[tok + t] = s_b[t];
+  const Mob e = mob_shfl_up(mob_scan(m, lane), 1, lane);  // M_{t-1} ... M_0
+  const float p = fmaf(e.a, p0, e.b) / fmaf(e.c, p0, e.d);   // variance after token t - 1
+  const float pm = fmaf(al * al, p, (1.f - al) * (1.f + al) * qvar);
+  if (lane < n) beta[g] = pm / fmaf(pm, kt, rt);
+  if (c == nchunks - 1 && cov_out && lane == n - 1)
+    cov_out[bh] = pm * (dk * rt) / fmaf(pm, kt, dk * rt);
 }
 
 template <typename Tk, typename Tg>
@@ -351,23 +396,24 @@ hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const
                           float* kk, float* maps, int BH, int L, int dk, int chunk,
                           hipStream_t s) {
   const int nchunks = (L + chunk - 1) / chunk;
+  const int blocks = (BH * nchunks + 3) / 4;  // four wavefronts per workgroup
   if (k_bf16)
-    hipLaunchKernelGGL(iso_maps_kernel<uint16_t>, dim3(BH, nchunks), dim3(256), 0, s,
+    hipLaunchKernelGGL(iso_maps_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const uint16_t*>(k), alpha, r, q_noise_var, kk,
-                       reinterpret_cast<float4*>(maps), L, dk, chunk, nchunks);
+                       reinterpret_cast<float4*>(maps), BH, L, dk, chunk, nchunks);
   else
-    hipLaunchKernelGGL(iso_maps_kernel<float>, dim3(BH, nchunks), dim3(256), 0, s,
+    hipLaunchKernelGGL(iso_maps_kernel<float>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const float*>(k), alpha, r, q_noise_var, kk,
-                       reinterpret_cast<float4*>(maps), L, dk, chunk, nchunks);
+                       reinterpret_cast<float4*>(maps), BH, L, dk, chunk, nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(iso_prefix_kernel, dim3((BH + 63) / 64), dim3(64), 0, s, cov_in,
                      reinterpret_cast<float4*>(maps), BH, nchunks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(iso_beta_kernel, dim3(BH, nchunks), dim3(64), 0, s, alpha, r, kk, cov_in,
-                     cov_out, q_noise_var, reinterpret_cast<const float4*>(maps), beta, L, dk,
-                     chunk, nchunks);
+  hipLaunchKernelGGL(iso_beta_kernel, dim3(blocks), dim3(256), 0, s, alpha, r, kk, cov_out,
+                     q_noise_var, reinterpret_cast<const float4*>(maps), beta, BH, L, dk, chunk,
+                     nchunks);
   return hipGetLastError();
 }
 

@@ -148,7 +148,7 @@ hipError_t launch_diag_gains(const void* k, bool k_bf16, const float* alpha, con
 
 // Isotropic Kalman write: the per-token write strengths beta [BH, L] (the gain
 // is beta_t k_t) and the final variance [BH]. `kk` is scratch of BH * L floats,
-// `maps` of BH * nchunks * 4 floats (16-byte aligned). chunk <= 128.
+// `maps` of BH * nchunks * 4 floats (16-byte aligned). chunk <= 64.
 hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const float* r,
                           const float* cov_in, float* cov_out, float q_noise_var, float* beta,
                           float* kk, float* maps, int BH, int L, int dk, int chunk,
