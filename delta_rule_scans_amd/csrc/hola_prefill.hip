@@ -8,13 +8,15 @@
 //
 // Block j's tokens read the cache as it stood before block j; then the block
 // is inserted. Three kernels:
-//  * select: one workgroup per head walks the blocks in order and records, for
-//    every block, which tokens the cache holds when the block reads it, then
-//    merges the block in: every candidate's rank among (cache, block) by score
-//    descending, position ascending is counted directly, and the first w stay.
+//  * block top: one workgroup per (head, block), every block in parallel,
+//    ranks the block's tokens by score descending, position ascending (or by
+//    position descending for the recency control) and keeps the first w.
+//  * merge: one workgroup per head walks the blocks in order, records for
+//    every block which tokens the cache holds when the block reads it, then
+//    merges the block's top list in.
 //  * read: one workgroup per (head, block, 64 queries), every block in
 //    parallel: streaming softmax over 32-key tiles of (cache members, causal
-//    block tokens) in float32.
+//    block tokens) in float32, register-tiled.
 //  * commit: one workgroup per head gathers the final members' keys and values
 //    (from the old cache or the prompt), then writes the cache in rank order.
 #include <math.h>
@@ -28,89 +30,178 @@ constexpr int NT = 256;
 constexpr int QT = 64;   // queries per read workgroup
 constexpr int KT = 32;   // keys per tile
 constexpr int MAXD = 128;
+constexpr int kMaxW = 256;       // largest cache capacity
+constexpr int kMaxBlock = 1024;  // largest prompt block
 
-// Score order: larger score first, then smaller position, then smaller
-// candidate index (only reached when a caller repeats a position). NaN scores
-// rank below every other score. Recency order: larger position first.
-__device__ __forceinline__ bool before(float ma, int pa, int ia, float mb, int pb, int ib,
-                                       bool recency) {
-  if (recency) return pa != pb ? pa > pb : ia < ib;
-  ma = ma == ma ? ma : -INFINITY;
-  mb = mb == mb ? mb : -INFINITY;
-  if (ma != mb) return ma > mb;
-  if (pa != pb) return pa < pb;
-  return ia < ib;
+// NaN scores rank below every other score.
+__device__ __forceinline__ float score_key(float m) { return m == m ? m : -INFINITY; }
+
+// Block tops: the w best tokens of each block on its own, every block in
+// parallel. Positions rise with the index inside a block, so the score order
+// ties break on the index and the recency order is the reverse index order.
+// Each token's rank is counted against the whole block.
+__global__ __launch_bounds__(NT) void block_top_kernel(PrefillArgs a) {
+  __shared__ __align__(16) float sm[kMaxBlock];
+  const int bh = blockIdx.x, j = blockIdx.y, tid = threadIdx.x;
+  const int nblk = (a.L + a.block - 1) / a.block;
+  const int j0 = j * a.block, nb = min(a.block, a.L - j0);
+  const float* mh = a.m + (size_t)bh * a.L + j0;
+  for (int i = tid; i < nb; i += NT) sm[i] = score_key(mh[i]);
+  for (int i = nb + tid; i < ((nb + 3) & ~3); i += NT) sm[i] = -INFINITY;
+  __syncthreads();
+  const size_t base = ((size_t)bh * nblk + j) * a.w;
+  for (int x = tid; x < nb; x += NT) {
+    int rank;
+    if (a.policy == 1) {
+      rank = nb - 1 - x;
+    } else {
+      const float mx = sm[x];
+      rank = 0;
+      // padding slots hold -inf and sit after x, so they never count
+      for (int y = 0; y < nb; y += 4) {
+        const float4 m4 = *reinterpret_cast<const float4*>(&sm[y]);
+        rank += (m4.x > mx) | ((m4.x == mx) & (y < x));
+        rank += (m4.y > mx) | ((m4.y == mx) & (y + 1 < x));
+        rank += (m4.z > mx) | ((m4.z == mx) & (y + 2 < x));
+        rank += (m4.w > mx) | ((m4.w == mx) & (y + 3 < x));
+      }
+    }
+    if (rank < a.w) {
+      a.top_m[base + rank] = mh[x];
+      a.top_pos[base + rank] = a.t0 + j0 + x;
+      a.top_src[base + rank] = j0 + x;
+    }
+  }
 }
 
 // Cache members are coded as src >= 0: prompt token src; src < 0: old slot -1 - src.
-__global__ __launch_bounds__(NT) void select_kernel(PrefillArgs a) {
-  extern __shared__ __align__(16) unsigned char lds_raw[];
-  const int cap = a.w + a.block;
-  float* cm = reinterpret_cast<float*>(lds_raw);  // candidates [cap]
-  int* cp = reinterpret_cast<int*>(cm + cap);
-  int* cs = cp + cap;
-  float* nm = reinterpret_cast<float*>(cs + cap);  // next cache [w]
-  int* np_ = reinterpret_cast<int*>(nm + a.w);
-  int* ns = np_ + a.w;
+//
+// The cache a block reads is the top-w of the old cache and every earlier
+// block, and the top-w of a union is the top-w of the union of the parts'
+// top-w lists, so one workgroup per head merges the block tops in order: two
+// sorted lists, each entry's new rank is its own index plus the number of
+// entries of the other list ahead of it (a binary search). On a full tie the
+// cache entry goes first, as the earlier candidate.
+__global__ __launch_bounds__(NT) void merge_kernel(PrefillArgs a) {
+  __shared__ float cm[2][kMaxW];
+  __shared__ int cp[2][kMaxW], cs[2][kMaxW];
+  __shared__ float tm[kMaxW];
+  __shared__ int tp[kMaxW];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int nblk = (a.L + a.block - 1) / a.block;
-  int n = min(a.cache_count[bh], a.w);
-  n = max(n, 0);
-  for (int e = tid; e < n; e += NT) {
-    nm[e] = a.cache_m[(size_t)bh * a.w + e];
-    np_[e] = a.cache_pos[(size_t)bh * a.w + e];
-    ns[e] = -1 - e;
+  const bool rec = a.policy == 1;
+  int n = min(max(a.cache_count[bh], 0), a.w);
+  // the old cache need not be in rank order: rank it by counting, ties by slot
+  if (tid < n) {
+    cm[1][tid] = a.cache_m[(size_t)bh * a.w + tid];
+    cp[1][tid] = a.cache_pos[(size_t)bh * a.w + tid];
+  }
+  __syncthreads();
+  if (tid < n) {
+    const float mx = score_key(cm[1][tid]);
+    const int px = cp[1][tid];
+    int r = 0;
+    for (int y = 0; y < n; ++y) {
+      const float my = score_key(cm[1][y]);
+      const int py = cp[1][y];
+      const bool tie_first = y < tid;
+      r += rec ? (py > px || (py == px && tie_first))
+               : (my > mx || (my == mx && (py < px || (py == px && tie_first))));
+    }
+    cm[0][r] = cm[1][tid];
+    cp[0][r] = px;
+    cs[0][r] = -1 - tid;
+  }
+  int cur = 0;
+  // the next block top, loaded a step ahead
+  const size_t tbase = (size_t)bh * nblk * a.w;
+  float nm = 0.f;
+  int npos = 0, nsrc = 0;
+  if (tid < min(a.block, a.L) && tid < a.w) {
+    nm = a.top_m[tbase + tid];
+    npos = a.top_pos[tbase + tid];
+    nsrc = a.top_src[tbase + tid];
   }
   __syncthreads();
   for (int j = 0; j < nblk; ++j) {
-    const int j0 = j * a.block, nb = min(a.block, a.L - j0);
-    // the cache this block reads
+    const int nt = min(min(a.block, a.L - j * a.block), a.w);
     int* mem = a.members + ((size_t)bh * nblk + j) * a.w;
-    for (int e = tid; e < n; e += NT) mem[e] = ns[e];
+    if (tid < n) mem[tid] = cs[cur][tid];
     if (tid == 0) a.member_count[(size_t)bh * nblk + j] = n;
-    const int nc = n + nb;
-    for (int e = tid; e < nc; e += NT) {
-      if (e < n) {
-        cm[e] = nm[e];
-        cp[e] = np_[e];
-        cs[e] = ns[e];
-      } else {
-        const int i = j0 + e - n;
-        cm[e] = a.m[(size_t)bh * a.L + i];
-        cp[e] = a.t0 + i;
-        cs[e] = i;
-      }
+    const float fm = nm;
+    const int fp = npos, fs = nsrc;
+    if (tid < nt) {
+      tm[tid] = score_key(fm);
+      tp[tid] = fp;
+    }
+    if (j + 1 < nblk && tid < min(min(a.block, a.L - (j + 1) * a.block), a.w)) {
+      const size_t o = tbase + (size_t)(j + 1) * a.w + tid;
+      nm = a.top_m[o];
+      npos = a.top_pos[o];
+      nsrc = a.top_src[o];
     }
     __syncthreads();
-    for (int x = tid; x < nc; x += NT) {
-      const float mx = cm[x];
-      const int px = cp[x];
-      int rank = 0;
-      for (int y = 0; y < nc; ++y) rank += before(cm[y], cp[y], y, mx, px, x, a.policy == 1) ? 1 : 0;
-      if (rank < a.w) {
-        nm[rank] = mx;
-        np_[rank] = px;
-        ns[rank] = cs[x];
+    const int nx = cur ^ 1;
+    if (tid < n) {  // cache entry: block-top entries strictly ahead of it
+      const float mx = score_key(cm[cur][tid]);
+      const int px = cp[cur][tid];
+      int lo = 0, hi = nt;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const bool ahead = rec ? tp[mid] > px : (tm[mid] > mx || (tm[mid] == mx && tp[mid] < px));
+        if (ahead) lo = mid + 1;
+        else hi = mid;
+      }
+      const int r = tid + lo;
+      if (r < a.w) {
+        cm[nx][r] = cm[cur][tid];
+        cp[nx][r] = px;
+        cs[nx][r] = cs[cur][tid];
       }
     }
-    n = min(nc, a.w);
+    if (tid < nt) {  // block-top entry: cache entries ahead of it or tied with it
+      const float mx = tm[tid];
+      const int px = fp;
+      int lo = 0, hi = n;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        const float cmid = score_key(cm[cur][mid]);
+        const int pmid = cp[cur][mid];
+        const bool ahead = rec ? pmid >= px : (cmid > mx || (cmid == mx && pmid <= px));
+        if (ahead) lo = mid + 1;
+        else hi = mid;
+      }
+      const int r = tid + lo;
+      if (r < a.w) {
+        cm[nx][r] = fm;
+        cp[nx][r] = fp;
+        cs[nx][r] = fs;
+      }
+    }
+    n = min(n + nt, a.w);
+    cur = nx;
     __syncthreads();
   }
-  int* fin = a.final_src + (size_t)bh * a.w;
-  for (int e = tid; e < n; e += NT) {
-    fin[e] = ns[e];
-    a.final_m[(size_t)bh * a.w + e] = nm[e];
-    a.final_pos[(size_t)bh * a.w + e] = np_[e];
+  if (tid < n) {
+    a.final_src[(size_t)bh * a.w + tid] = cs[cur][tid];
+    a.final_m[(size_t)bh * a.w + tid] = cm[cur][tid];
+    a.final_pos[(size_t)bh * a.w + tid] = cp[cur][tid];
   }
   if (tid == 0) a.final_count[bh] = n;
 }
 
+// Read: 64 queries per workgroup against 32-key tiles, register-tiled so that
+// every LDS read feeds several FMAs. Thread (qg, j) = (tid / 16, tid % 16)
+// owns queries 4 qg .. 4 qg + 3; in the logits it takes keys 2 j, 2 j + 1 of
+// the tile, in the weighted sum value columns 8 j .. 8 j + 7. Queries and
+// keys are stored transposed ([d][query], [d][key]) and scaled by their RMS
+// norm (the queries also by 1/sqrt(d_k)), so a logit is a plain dot product.
 template <typename Tin>
 __global__ __launch_bounds__(NT) void read_kernel(PrefillArgs a) {
-  __shared__ float sQ[QT][MAXD + 1];
-  __shared__ float sK[KT][MAXD + 1];
-  __shared__ float sV[KT][MAXD];
-  __shared__ float sP[QT][KT + 1];
+  __shared__ float sQt[MAXD][QT + 4];
+  __shared__ float sKt[MAXD][KT + 4];
+  __shared__ float sV[KT][MAXD + 4];
+  __shared__ float sPt[KT][QT + 4];
   __shared__ int sSrc[KT];
   const int bh = blockIdx.x, j = blockIdx.y, qt = blockIdx.z, tid = threadIdx.x;
   const int dk = a.dk, dv = a.dv;
@@ -130,33 +221,31 @@ __global__ __launch_bounds__(NT) void read_kernel(PrefillArgs a) {
   const int nkeys = ncache + q0 + nq;
   const float inv_sqrt_d = 1.f / sqrtf((float)dk);
 
-  // queries, RMS-normalised (4 lanes per row)
-  for (int idx = tid; idx < QT * dk; idx += NT) {
-    const int r = idx / dk, c = idx - r * dk;
-    sQ[r][c] = r < nq ? Elem<Tin>::load(qh, (size_t)(j0 + q0 + r) * dk + c) : 0.f;
-  }
-  __syncthreads();
-  const int qi = tid >> 2, part = tid & 3;
-  {
+  {  // queries: 4 lanes per row, RMS-normalised, times 1/sqrt(d_k), transposed
+    const int r = tid >> 2, part = tid & 3;
+    float x[MAXD / 4];
     float ss = 0.f;
-    for (int c = part; c < dk; c += 4) ss = fmaf(sQ[qi][c], sQ[qi][c], ss);
+#pragma unroll
+    for (int u = 0; u < MAXD / 4; ++u) {
+      const int c = part + 4 * u;
+      x[u] = (r < nq && c < dk) ? Elem<Tin>::load(qh, (size_t)(j0 + q0 + r) * dk + c) : 0.f;
+      ss = fmaf(x[u], x[u], ss);
+    }
     ss += __shfl_xor(ss, 1, 4);
     ss += __shfl_xor(ss, 2, 4);
-    const float sc = inv_sqrt_d / sqrtf(ss / dk + a.rms_eps);  // folds the 1/sqrt(d_k)
-    for (int c = part; c < dk; c += 4) sQ[qi][c] *= sc;
-  }
-  const int qtok = q0 + qi;  // this row's token, relative to the block
-  float M, Z;
-  if (a.sink_logit) {
-    M = a.sink_logit[bh % a.H];
-    Z = 1.f;
-  } else {
-    M = -INFINITY;
-    Z = 0.f;
-  }
-  float acc[MAXD / 4];
+    const float sc = inv_sqrt_d / sqrtf(ss / dk + a.rms_eps);
 #pragma unroll
-  for (int u = 0; u < MAXD / 4; ++u) acc[u] = 0.f;
+    for (int u = 0; u < MAXD / 4; ++u) sQt[part + 4 * u][r] = x[u] * sc;
+  }
+  const int qg = tid >> 4, jj = tid & 15;
+  float M[4], Z[4], acc[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    M[i] = a.sink_logit ? a.sink_logit[bh % a.H] : -INFINITY;
+    Z[i] = a.sink_logit ? 1.f : 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
+  }
 
   for (int e0 = 0; e0 < nkeys; e0 += KT) {
     __syncthreads();
@@ -165,13 +254,26 @@ __global__ __launch_bounds__(NT) void read_kernel(PrefillArgs a) {
       sSrc[tid] = e < nkeys ? (e < ncache ? mem[e] : j0 + e - ncache) : 0x7fffffff;
     }
     __syncthreads();
-    for (int idx = tid; idx < KT * dk; idx += NT) {
-      const int r = idx / dk, c = idx - r * dk;
-      const int src = sSrc[r];
-      float x = 0.f;
-      if (src != 0x7fffffff)
-        x = src >= 0 ? Elem<Tin>::load(kh, (size_t)src * dk + c) : ck[(size_t)(-1 - src) * dk + c];
-      sK[r][c] = x;
+    {  // keys: 8 lanes per key, RMS-normalised, transposed
+      const int kr = tid >> 3, part = tid & 7;
+      const int src = sSrc[kr];
+      float x[MAXD / 8];
+      float ss = 0.f;
+#pragma unroll
+      for (int u = 0; u < MAXD / 8; ++u) {
+        const int c = part + 8 * u;
+        float v = 0.f;
+        if (src != 0x7fffffff && c < dk)
+          v = src >= 0 ? Elem<Tin>::load(kh, (size_t)src * dk + c) : ck[(size_t)(-1 - src) * dk + c];
+        x[u] = v;
+        ss = fmaf(v, v, ss);
+      }
+      ss += __shfl_xor(ss, 1, 8);
+      ss += __shfl_xor(ss, 2, 8);
+      ss += __shfl_xor(ss, 4, 8);
+      const float sc = 1.f / sqrtf(ss / dk + a.rms_eps);
+#pragma unroll
+      for (int u = 0; u < MAXD / 8; ++u) sKt[part + 8 * u][kr] = x[u] * sc;
     }
     for (int idx = tid; idx < KT * dv; idx += NT) {
       const int r = idx / dv, c = idx - r * dv;
@@ -182,70 +284,81 @@ __global__ __launch_bounds__(NT) void read_kernel(PrefillArgs a) {
       sV[r][c] = x;
     }
     __syncthreads();
-    {  // key norms, 8 lanes per key
-      const int kr = tid >> 3, sub = tid & 7;
-      float ss = 0.f;
-      for (int c = sub; c < dk; c += 8) ss = fmaf(sK[kr][c], sK[kr][c], ss);
-      ss += __shfl_xor(ss, 1, 8);
-      ss += __shfl_xor(ss, 2, 8);
-      ss += __shfl_xor(ss, 4, 8);
-      const float sc = 1.f / sqrtf(ss / dk + a.rms_eps);
-      for (int c = sub; c < dk; c += 8) sK[kr][c] *= sc;
-    }
-    __syncthreads();
-    // logits of this row against keys 8 part .. 8 part + 7 of the tile
-    float l[8];
+    // logits: 4 queries x 2 keys per thread
+    float l[4][2];
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) l[jj] = 0.f;
-    for (int c = 0; c < dk; ++c) {
-      const float qv = sQ[qi][c];
+    for (int i = 0; i < 4; ++i) l[i][0] = l[i][1] = 0.f;
+    for (int d = 0; d < dk; ++d) {
+      const float4 qv = *reinterpret_cast<const float4*>(&sQt[d][4 * qg]);
+      const float2 kv = *reinterpret_cast<const float2*>(&sKt[d][2 * jj]);
+      const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) l[jj] = fmaf(qv, sK[8 * part + jj][c], l[jj]);
-    }
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const int e = e0 + 8 * part + jj;
-      // cache members are always visible; block tokens up to the query itself
-      const bool vis = qi < nq && e < nkeys && (e < ncache || e - ncache <= qtok);
-      l[jj] = vis ? l[jj] : -INFINITY;
-      tmax = fmaxf(tmax, l[jj]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 4));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 4));
-    const float Mn = fmaxf(M, tmax);
-    // rows with nothing visible yet keep M = -inf; their weights stay 0
-    const float scale = Mn == -INFINITY ? 1.f : __expf(M - Mn);
-    float psum = 0.f;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const float p = l[jj] == -INFINITY ? 0.f : __expf(l[jj] - Mn);
-      sP[qi][8 * part + jj] = p;
-      psum += p;
-    }
-    psum += __shfl_xor(psum, 1, 4);
-    psum += __shfl_xor(psum, 2, 4);
-    Z = fmaf(Z, scale, psum);
-    M = Mn;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < MAXD / 4; ++u) acc[u] *= scale;
-    for (int e = 0; e < KT; ++e) {
-      const float p = sP[qi][e];
-#pragma unroll
-      for (int u = 0; u < MAXD / 4; ++u) {
-        const int c = part + 4 * u;
-        if (c < dv) acc[u] = fmaf(p, sV[e][c], acc[u]);
+      for (int i = 0; i < 4; ++i) {
+        l[i][0] = fmaf(qa[i], kv.x, l[i][0]);
+        l[i][1] = fmaf(qa[i], kv.y, l[i][1]);
       }
     }
-  }
-  if (qi < nq) {
-    float* o = a.o_cache + ((size_t)bh * a.L + j0 + qtok) * dv;
-    const float inv = 1.f / Z;
+    float p[4][2];
 #pragma unroll
-    for (int u = 0; u < MAXD / 4; ++u) {
-      const int c = part + 4 * u;
-      if (c < dv) o[c] = acc[u] * inv;
+    for (int i = 0; i < 4; ++i) {
+      const int qtok = q0 + 4 * qg + i;  // relative to the block
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int e = e0 + 2 * jj + h;
+        // cache members are always visible; block tokens up to the query itself
+        const bool vis = 4 * qg + i < nq && e < nkeys && (e < ncache || e - ncache <= qtok);
+        l[i][h] = vis ? l[i][h] : -INFINITY;
+        tmax = fmaxf(tmax, l[i][h]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 4, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 8, 16));
+      const float Mn = fmaxf(M[i], tmax);
+      // rows with nothing visible yet keep M = -inf; their weights stay 0
+      const float scale = Mn == -INFINITY ? 1.f : __expf(M[i] - Mn);
+      float ps = 0.f;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        p[i][h] = l[i][h] == -INFINITY ? 0.f : __expf(l[i][h] - Mn);
+        ps += p[i][h];
+      }
+      ps += __shfl_xor(ps, 1, 16);
+      ps += __shfl_xor(ps, 2, 16);
+      ps += __shfl_xor(ps, 4, 16);
+      ps += __shfl_xor(ps, 8, 16);
+      Z[i] = fmaf(Z[i], scale, ps);
+      M[i] = Mn;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[i][c] *= scale;
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      *reinterpret_cast<float4*>(&sPt[2 * jj + h][4 * qg]) = make_float4(p[0][h], p[1][h], p[2][h], p[3][h]);
+    __syncthreads();
+    // weighted values: 4 queries x 8 value columns per thread
+    for (int e = 0; e < KT; ++e) {
+      const float4 pv = *reinterpret_cast<const float4*>(&sPt[e][4 * qg]);
+      const float4 v0 = *reinterpret_cast<const float4*>(&sV[e][8 * jj]);
+      const float4 v1 = *reinterpret_cast<const float4*>(&sV[e][8 * jj + 4]);
+      const float pa[4] = {pv.x, pv.y, pv.z, pv.w};
+      const float va[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[i][c] = fmaf(pa[i], va[c], acc[i][c]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int qi = 4 * qg + i;
+    if (qi < nq) {
+      float* o = a.o_cache + ((size_t)bh * a.L + j0 + q0 + qi) * dv;
+      const float inv = 1.f / Z[i];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (8 * jj + c < dv) o[8 * jj + c] = acc[i][c] * inv;
     }
   }
 }
@@ -289,9 +402,12 @@ __global__ __launch_bounds__(NT) void commit_kernel(PrefillArgs a) {
 template <typename Tin>
 hipError_t prefill_typed(const PrefillArgs& a, hipStream_t s) {
   const int nblk = (a.L + a.block - 1) / a.block;
-  const size_t sel_lds = (size_t)3 * (a.w + a.block) * 4 + (size_t)3 * a.w * 4;
-  hipLaunchKernelGGL(select_kernel, dim3(a.BH), dim3(NT), sel_lds, s, a);
+  if (a.w > kMaxW || a.block > kMaxBlock || a.w > NT) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(block_top_kernel, dim3(a.BH, nblk), dim3(NT), 0, s, a);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_kernel, dim3(a.BH), dim3(NT), 0, s, a);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(read_kernel<Tin>, dim3(a.BH, nblk, (a.block + QT - 1) / QT), dim3(NT), 0, s,
                      a);
@@ -306,8 +422,8 @@ hipError_t prefill_typed(const PrefillArgs& a, hipStream_t s) {
 size_t prefill_workspace_bytes(int BH, int L, int dk, int dv, int w, int block) {
   const size_t nblk = ((size_t)L + block - 1) / block;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  return up((size_t)BH * nblk * w * 4) + up((size_t)BH * nblk * 4) + 3 * up((size_t)BH * w * 4) +
-         up((size_t)BH * 4) + up((size_t)BH * w * (dk + dv) * 4);
+  return 4 * up((size_t)BH * nblk * w * 4) + up((size_t)BH * nblk * 4) +
+         3 * up((size_t)BH * w * 4) + up((size_t)BH * 4) + up((size_t)BH * w * (dk + dv) * 4);
 }
 
 void prefill_bind_workspace(PrefillArgs& a, void* ws) {
@@ -327,13 +443,15 @@ void prefill_bind_workspace(PrefillArgs& a, void* ws) {
   a.final_count = reinterpret_cast<int*>(p);
   p += up((size_t)a.BH * 4);
   a.stage = reinterpret_cast<float*>(p);
+  p += up((size_t)a.BH * a.w * (a.dk + a.dv) * 4);
+  a.top_m = reinterpret_cast<float*>(p);
+  p += up((size_t)a.BH * nblk * a.w * 4);
+  a.top_pos = reinterpret_cast<int*>(p);
+  p += up((size_t)a.BH * nblk * a.w * 4);
+  a.top_src = reinterpret_cast<int*>(p);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, bool in_bf16, hipStream_t s) {
-  const size_t sel_lds = (size_t)3 * (a.w + a.block) * 4 + (size_t)3 * a.w * 4;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(select_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)sel_lds);
-  if (e != hipSuccess) return e;
   return in_bf16 ? prefill_typed<uint16_t>(a, s) : prefill_typed<float>(a, s);
 }
 

@@ -230,6 +230,9 @@ struct PrefillArgs {
   int* final_pos;     // [BH, w]
   int* final_count;   // [BH]
   float* stage;       // [BH, w, dk + dv]
+  float* top_m;       // [BH, blocks, w] each block's own top-w, in rank order
+  int* top_pos;       // [BH, blocks, w]
+  int* top_src;       // [BH, blocks, w]
 };
 size_t prefill_workspace_bytes(int BH, int L, int dk, int dv, int w, int block);
 void prefill_bind_workspace(PrefillArgs& a, void* ws);
