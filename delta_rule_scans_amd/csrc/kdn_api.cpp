@@ -378,7 +378,8 @@ KDN_EXPORT int kdn_scan_bwd(const float* q, const float* k, const float* v, cons
     return KDN_ERR_BAD_MODE;
   if (B < 1 || H < 1 || L < 0 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
     return KDN_ERR_BAD_SHAPE;
-  if ((long long)B * H > (1LL << 24) || (long long)(d_v + 31) / 32 > kMaxGridYZ)
+  if ((long long)B * H > (1LL << 24) || (long long)(d_v + 31) / 32 > kMaxGridYZ ||
+      ((long long)L + 63) / 64 > kMaxGridYZ)
     return KDN_ERR_BAD_SHAPE;
   if (L == 0) {
     // no tokens: the initial state's gradient is the final state's

@@ -195,12 +195,19 @@ struct BwdArgs {
   int BH, L, dk, dv;
   int resid;                // 0 gated, 1 plain, 2 no erase
   // workspace parts (set by launch_scan_bwd)
-  float* ckpt = nullptr;
-  float* hist = nullptr;
-  float* dq_part = nullptr;
-  float* dk_part = nullptr;
-  float* da_part = nullptr;
-  float* db_part = nullptr;
+  float* S0s = nullptr;  // [BH, chunks, dk, dv] state at each chunk start
+  float* Gs = nullptr;   // [BH, chunks, dk, dv] state gradient at each chunk end
+  float* E = nullptr;    // [BH, chunks * 64, dv] residuals
+  float* dR = nullptr;   // [BH, chunks * 64, dv] residual-input gradients
+  float* Am = nullptr;   // [BH, chunks, 64, 64]
+  float* Tm = nullptr;   // [BH, chunks, 64, 64]
+  float* Pm = nullptr;   // [BH, chunks, 64, 64]
+  float* M1 = nullptr;   // [BH, chunks * 64, dk] dO S0^T
+  float* M2 = nullptr;   // [BH, chunks * 64, dk] dR S0^T
+  float* M3 = nullptr;   // [BH, chunks * 64, dk] E G^T
+  float* dPm = nullptr;  // [BH, chunks, 64, 64] dO E^T
+  float* dA = nullptr;   // [BH, chunks, 64, 64] dR E^T
+  float* gs0 = nullptr;  // [BH, chunks] <G, S0>
 };
 size_t scan_bwd_workspace_bytes(int BH, int L, int dk, int dv);
 hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s);

@@ -1,288 +1,740 @@
-// scan_bwd.hip -- gradients of the delta-write scan (reverse mode).
+// scan_bwd.hip -- gradients of the delta-write scan (reverse mode), chunkwise.
 //
 // Forward ("A Hippocampus for Linear Attention", sec. 3.3 eq. (5), sec. 3.5):
-//   S_t = M_t S_{t-1} + beta_t k_t v_t^T,  M_t = alpha_t I - c_t beta_t k_t k_t^T,
-//   o_t = S_t^T q_t,  e_t = v_t - c_t S_{t-1}^T k_t,
-//   c_t = alpha_t (gated residual), 1 (plain), 0 (no erase).
-// The pages give no backward pass; its adjoint, with G_t = dL/dS_t:
-//   G_t += q_t do_t^T;  dq_t = S_t do_t;  y_t = G_t^T k_t;  dv_t = beta_t y_t;
-//   dbeta_t = y_t . e_t;  dk_t = beta_t G_t e_t - c_t beta_t S_{t-1} y_t;
-//   dalpha_t = <G_t, S_{t-1}> - [gated] beta_t y_t . (S_{t-1}^T k_t);
-//   G_{t-1} = alpha_t G_t - c_t beta_t k_t y_t^T;  dS_0 = G_0.
+//   S_t = alpha_t S_{t-1} + b_t k_t e_t^T,  e_t = v_t - c_t S_{t-1}^T k_t,  o_t = S_t^T q_t,
+// c_t = alpha_t (gated residual) or 0 (no erase). The plain residual (c_t = 1)
+// is the gated one with b_t = beta_t / alpha_t and values alpha_t v_t, so it is
+// run in that form and its gradients are mapped back at the end.
 //
-// Every value column is independent, so one workgroup takes one head and 32
-// value columns: thread (c, rg) owns column c and rows rg, rg + 8, ... of S
-// and G in registers. A first forward pass stores the state at every 64-token
-// chunk start; the reverse pass recomputes each chunk's states (kept in a
-// per-workgroup history buffer) and walks it backwards. Sums over rows meet in
-// LDS (one barrier per forward token, two per backward token); the per-tile
-// partial sums of dq, dk, dalpha, dbeta are added over tiles in a fixed order
-// by a second kernel. Float32 throughout.
+// Over a chunk of C tokens with incoming state S0, local decays
+// g_t = prod_{l<=t} alpha_l, D_tl = g_t / g_l, Lambda_t = g_C / g_t and B = diag(b) K:
+//   A = strict_lower((K B^T) * D),  Pm = lower_incl((Q B^T) * D),  T = (I + A)^-1,
+//   E = T (V - diag(g) K S0),  O = diag(g) Q S0 + Pm E,  S_C = g_C S0 + (diag(Lambda) B)^T E.
+// The pages give no backward pass. Differentiating the chunk form, with
+// G = dL/dS_C and dO = dL/dO:
+//   dE = Pm^T dO + diag(Lambda) B G,   dR = T^T dE (= dV),   dA = -strict_lower(dR E^T),
+//   dS0 = g_C G + Q^T diag(g) dO - K^T diag(g) dR          (the chain to the previous chunk),
+//   Xp = lower_incl(dO E^T) * D,  Xa = dA * D,
+//   dQ = diag(g) dO S0^T + Xp B,
+//   dB = Xp^T Q + Xa^T K + diag(Lambda) E G^T,
+//   dK = Xa B - diag(g) dR S0^T + diag(b) dB,   db_t = dB_t . k_t,
+// and the decays enter through log g: the row minus column sums of dPm * Pm and
+// dA * A (the D factors), g_t q_t . (dO S0^T)_t, -g_t k_t . (dR S0^T)_t, and the
+// state terms Lambda_t b_t k_t . (G e_t) (minus at t, plus at the chunk end) and
+// g_C <G, S0>. Then d log alpha_t = sum_{t' >= t} d log g_t' within the chunk and
+// dalpha_t = d log alpha_t / alpha_t (alpha must be positive). Without the erase
+// term A = 0, T = I and the K S0 terms drop.
+//
+// Kernels (C = 64, float32 throughout, d_k, d_v <= 128):
+//  * prep (head, chunk): A, Pm and T by blocked inversion (16 -> 32 -> 64).
+//  * forward chain (head, 32 value columns): chunk-start states S0 and residuals E.
+//  * reverse chain (head, 32 value columns): G at every chunk end, dR, dV, dS0.
+//  * contractions over d_v (head, chunk, part): dO S0^T and dO E^T; dR S0^T and
+//    dR E^T; E G^T and <G, S0>.
+//  * gradients (head, chunk): dQ, dK, dbeta, dalpha.
+// Products run on register tiles of each thread over LDS operands.
 #include "kdn_internal.h"
 
 namespace kdn {
 namespace {
 
 constexpr int NT = 256;
-constexpr int CW = 32;   // value columns per workgroup
-constexpr int CH = 64;   // tokens per recomputation chunk
-constexpr int RPT = 16;  // rows per thread (d_k <= 128)
+constexpr int C = 64;       // tokens per chunk (one wavefront of scalars)
+constexpr int TW = 32;      // value columns per chain workgroup
+constexpr int DP = 128;     // d_k, padded
+constexpr int LK = DP + 4;  // row stride of [C][d_k] arrays
+constexpr int LC = C + 1;   // row stride of [C][C] arrays
+constexpr int LT = C + 4;   // row stride of transposed [d][C] arrays
 
-struct BwdLds {
-  float k[CH][128];
-  float q[CH][128];
-  float v[CH][CW];
-  float dout[CH][CW];
-  float a[CH], b[CH];
-  float red[2][8][CW];       // column sums over row groups
-  float red2[2][8][CW];
-  float red3[2][8][CW];
-  float row[2][128][CW + 1];   // row sums over columns (dk)
-  float row2[2][128][CW + 1];  // (dq)
-};
-
-__global__ __launch_bounds__(NT) void scan_bwd_kernel(BwdArgs a) {
-  extern __shared__ __align__(16) unsigned char lds_raw[];
-  BwdLds& L_ = *reinterpret_cast<BwdLds*>(lds_raw);
-  const int bh = blockIdx.x, tile = blockIdx.y, tid = threadIdx.x;
-  const int c = tid & 31, rg = tid >> 5;
-  const int dk = a.dk, dv = a.dv, L = a.L;
-  const int j0 = tile * CW, col = j0 + c;
-  const bool cok = col < dv;
-  const int nchunks = (L + CH - 1) / CH;
-  const size_t tile_id = (size_t)bh * gridDim.y + tile;
-  float* ckpt = a.ckpt + tile_id * (size_t)nchunks * dk * CW;
-  float* hist = a.hist + tile_id * (size_t)(CH + 1) * dk * CW;
-  const size_t tok0 = (size_t)bh * L;
-
-  float S[RPT], G[RPT];
+// acc[i][j] += sum_{k < K} A(m0 + i, k) B(k, n0 + j), A(m, k) = pa[m am + k ak],
+// B(k, n) = pb[k ldb + n] (rows 16-byte aligned, n0 a multiple of 4).
+template <int TM, int TN>
+__device__ __forceinline__ void mma(float (&acc)[TM][TN], const float* pa, int am, int ak,
+                                    const float* pb, int ldb, int m0, int n0, int K) {
+#pragma unroll 4
+  for (int k = 0; k < K; ++k) {
+    float av[TM], bv[TN];
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    const int r = rg + 8 * i;
-    const bool ok = r < dk && cok;
-    S[i] = ok && a.state_in ? a.state_in[((size_t)bh * dk + r) * dv + col] : 0.f;
-    G[i] = ok && a.dstate_out ? a.dstate_out[((size_t)bh * dk + r) * dv + col] : 0.f;
+    for (int i = 0; i < TM; ++i) av[i] = pa[(m0 + i) * am + k * ak];
+#pragma unroll
+    for (int j = 0; j < TN; j += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(pb + k * ldb + n0 + j);
+      bv[j] = x.x;
+      bv[j + 1] = x.y;
+      bv[j + 2] = x.z;
+      bv[j + 3] = x.w;
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
   }
+}
 
-  // chunk inputs into LDS (zero past the end and past d_v)
-  auto load_chunk = [&](int ck, bool with_q) {
-    const int t0 = ck * CH, n = min(CH, L - t0);
-    __syncthreads();
-    for (int idx = tid; idx < CH * dk; idx += NT) {
-      const int s = idx / dk, r = idx - s * dk;
-      const bool ok = s < n;
-      L_.k[s][r] = ok ? a.k[(tok0 + t0 + s) * dk + r] : 0.f;
-      if (with_q) L_.q[s][r] = ok ? a.q[(tok0 + t0 + s) * dk + r] : 0.f;
+// Chunk scalars (first wavefront): cumulative log decay, write scale b (beta,
+// or beta / alpha for the plain residual), decay. Tokens past the end get
+// alpha = 1 and b = 0, which leaves every product unchanged.
+__device__ void load_scalars(const BwdArgs& a, size_t tok, int n, float* sLg, float* sB,
+                             float* sAl) {
+  const int t = threadIdx.x;
+  if (t < C) {
+    float al = 1.f, b = 0.f;
+    if (t < n) {
+      al = a.alpha ? a.alpha[tok + t] : 1.f;
+      b = a.beta[tok + t];
+      if (a.resid == 1) b /= al;
     }
-    for (int idx = tid; idx < CH * CW; idx += NT) {
-      const int s = idx / CW, cc = idx - s * CW;
-      const bool ok = s < n && j0 + cc < dv;
-      L_.v[s][cc] = ok ? a.v[(tok0 + t0 + s) * dv + j0 + cc] : 0.f;
-      if (with_q) L_.dout[s][cc] = ok ? a.d_o[(tok0 + t0 + s) * dv + j0 + cc] : 0.f;
-    }
-    if (tid < CH) {
-      const bool ok = tid < n;
-      L_.a[tid] = ok ? (a.alpha ? a.alpha[tok0 + t0 + tid] : 1.f) : 1.f;
-      L_.b[tid] = ok ? a.beta[tok0 + t0 + tid] : 0.f;
-    }
-    __syncthreads();
-  };
-  auto coef = [&](float al) { return a.resid == 0 ? al : (a.resid == 1 ? 1.f : 0.f); };
-  // one forward token: S <- alpha S + beta k e^T, e = v - c S^T k
-  auto forward = [&](int s, int par) {
-    float pk = 0.f;
+    float lg = logf(al);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = rg + 8 * i;
-      if (r < dk) pk = fmaf(S[i], L_.k[s][r], pk);
+    for (int off = 1; off < C; off <<= 1) {
+      const float y = __shfl_up(lg, off, C);
+      if (t >= off) lg += y;
     }
-    L_.red[par][rg][c] = pk;
-    __syncthreads();
-    float p = 0.f;
-#pragma unroll
-    for (int g = 0; g < 8; ++g) p += L_.red[par][g][c];
-    const float al = L_.a[s], be = L_.b[s];
-    const float e = L_.v[s][c] - coef(al) * p;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = rg + 8 * i;
-      if (r < dk) S[i] = fmaf(al, S[i], be * L_.k[s][r] * e);
-    }
-  };
-  auto store_state = [&](float* dst) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = rg + 8 * i;
-      if (r < dk) dst[r * CW + c] = S[i];
-    }
-  };
-
-  // pass 1: states at the chunk starts
-  for (int ck = 0; ck < nchunks; ++ck) {
-    store_state(ckpt + (size_t)ck * dk * CW);
-    load_chunk(ck, false);
-    const int n = min(CH, L - ck * CH);
-    for (int s = 0; s < n; ++s) forward(s, s & 1);
+    sLg[t] = lg;
+    sB[t] = b;
+    sAl[t] = al;
   }
+}
 
-  // pass 2: chunks in reverse
-  for (int ck = nchunks - 1; ck >= 0; --ck) {
-    const int t0 = ck * CH, n = min(CH, L - t0);
-    load_chunk(ck, true);
+// [C][d] rows (n valid) into LDS [C][LK], zero padded.
+__device__ void load_rows(const float* src, int n, int d, float* dst) {
+  for (int idx = threadIdx.x; idx < C * DP; idx += NT) {
+    const int t = idx >> 7, i = idx & (DP - 1);
+    dst[t * LK + i] = (t < n && i < d) ? src[(size_t)t * d + i] : 0.f;
+  }
+}
+
+// A row-major [C][C] matrix into LDS [C][LC].
+__device__ void load_cc(const float* src, float* dst) {
+  for (int idx = threadIdx.x; idx < C * C; idx += NT) dst[(idx >> 6) * LC + (idx & 63)] = src[idx];
+}
+
+// Columns j0 .. j0 + TW - 1 of [C][dv] rows (n valid) into LDS [C][TW], zero
+// padded, rows scaled by rs[t] when given.
+__device__ void load_tile(const float* src, int n, int dv, int j0, float* dst, const float* rs) {
+  for (int idx = threadIdx.x; idx < C * TW; idx += NT) {
+    const int t = idx >> 5, j = idx & 31;
+    float x = 0.f;
+    if (t < n && j0 + j < dv) x = src[(size_t)t * dv + j0 + j];
+    dst[idx] = rs ? x * rs[t] : x;
+  }
+}
+
+__device__ __forceinline__ size_t cc_off(int bh, int nch, int c) {
+  return ((size_t)bh * nch + c) * C * C;
+}
+
+// ---------------------------------------------------------------------------
+// prep: A, Pm, T of one chunk
+__global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) float lds[];
+  float* sKt = lds;               // [DP][LT] keys, transposed
+  float* sQt = sKt + DP * LT;     // [DP][LT] queries, transposed
+  float* sA = sQt + DP * LT;      // [C][LC]
+  float* sT = sA + C * LC;        // [C][LC]
+  float* sY = sT + C * LC;        // [32][33]
+  float* sLg = sY + 32 * 33;
+  float* sB = sLg + C;
+  float* sAl = sB + C;
+  const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, nch = gridDim.y;
+  const int n = min(C, a.L - c * C), dk = a.dk;
+  const size_t tok = (size_t)bh * a.L + (size_t)c * C;
+  const bool erase = a.resid != 2;
+  for (int idx = tid; idx < C * DP; idx += NT) {
+    const int t = idx >> 7, i = idx & (DP - 1);
+    const bool ok = t < n && i < dk;
+    sKt[i * LT + t] = ok ? a.k[(tok + t) * dk + i] : 0.f;
+    sQt[i * LT + t] = ok ? a.q[(tok + t) * dk + i] : 0.f;
+  }
+  for (int idx = tid; idx < C * LC; idx += NT) sT[idx] = 0.f;
+  load_scalars(a, tok, n, sLg, sB, sAl);
+  __syncthreads();
+  const int tm = tid >> 4, tn = tid & 15;
+  float kk[4][4] = {}, qk[4][4] = {};
+  for (int d = 0; d < dk; ++d) {
+    const float4 b4 = *reinterpret_cast<const float4*>(sKt + d * LT + 4 * tn);
+    const float4 k4 = *reinterpret_cast<const float4*>(sKt + d * LT + 4 * tm);
+    const float4 q4 = *reinterpret_cast<const float4*>(sQt + d * LT + 4 * tm);
+    const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+    const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
+    const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = rg + 8 * i;
-      S[i] = r < dk ? ckpt[((size_t)ck * dk + r) * CW + c] : 0.f;
-    }
-    store_state(hist);
-    for (int s = 0; s < n; ++s) {
-      forward(s, s & 1);
-      store_state(hist + (size_t)(s + 1) * dk * CW);
-    }
-    __threadfence_block();
-    __syncthreads();
-    // S now holds S_{t0+n-1}, the state after the chunk's last token
-    for (int s = n - 1; s >= 0; --s) {
-      const int par = s & 1;
-      const size_t t = tok0 + t0 + s;
-      const float al = L_.a[s], be = L_.b[s], cf = coef(al);
-      const float dout = L_.dout[s][c];
-      float Sp[RPT];
-      float yp = 0.f, pp = 0.f, gs = 0.f;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int r = rg + 8 * i;
-        Sp[i] = r < dk ? hist[((size_t)s * dk + r) * CW + c] : 0.f;
-        if (r < dk) {
-          G[i] = fmaf(L_.q[s][r], dout, G[i]);
-          yp = fmaf(G[i], L_.k[s][r], yp);
-          pp = fmaf(Sp[i], L_.k[s][r], pp);
-          gs = fmaf(G[i], Sp[i], gs);
-          L_.row2[par][r][c] = S[i] * dout;  // dq: S_t do_t
-        }
+      for (int j = 0; j < 4; ++j) {
+        kk[i][j] = fmaf(kv[i], bv[j], kk[i][j]);
+        qk[i][j] = fmaf(qv[i], bv[j], qk[i][j]);
       }
-      L_.red[par][rg][c] = yp;
-      L_.red2[par][rg][c] = pp;
-      L_.red3[par][rg][c] = gs;
+  }
+  float* Ag = a.Am + cc_off(bh, nch, c);
+  float* Pg = a.Pm + cc_off(bh, nch, c);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = 4 * tm + i, l = 4 * tn + j;
+      const float f = l <= t ? sB[l] * expf(sLg[t] - sLg[l]) : 0.f;
+      const float av = (erase && l < t) ? kk[i][j] * f : 0.f;
+      sA[t * LC + l] = av;
+      Ag[t * C + l] = av;
+      Pg[t * C + l] = qk[i][j] * f;
+    }
+  __syncthreads();
+  // diagonal 16 x 16 blocks by substitution, one column per thread
+  if (tid < 64) {
+    const int o = 16 * (tid >> 4), col = tid & 15;
+    float x[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s = r == col ? 1.f : 0.f;
+#pragma unroll
+      for (int q = 0; q < r; ++q) s = fmaf(-sA[(o + r) * LC + o + q], x[q], s);
+      x[r] = s;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sT[(o + r) * LC + o + col] = x[r];
+  }
+  __syncthreads();
+  // [[T1, 0], [X, T2]] inverts [[I + A11, 0], [A21, I + A22]] with X = -T2 A21 T1
+  {
+    const int p = tid >> 7, r = (tid >> 3) & 15, c2 = (tid & 7) * 2, o = 32 * p;
+    float y0 = 0.f, y1 = 0.f;
+    for (int s = 0; s < 16; ++s) {
+      const float av = sA[(o + 16 + r) * LC + o + s];
+      y0 = fmaf(av, sT[(o + s) * LC + o + c2], y0);
+      y1 = fmaf(av, sT[(o + s) * LC + o + c2 + 1], y1);
+    }
+    sY[(16 * p + r) * 33 + c2] = y0;
+    sY[(16 * p + r) * 33 + c2 + 1] = y1;
+    __syncthreads();
+    float x0 = 0.f, x1 = 0.f;
+    for (int s = 0; s < 16; ++s) {
+      const float tv = sT[(o + 16 + r) * LC + o + 16 + s];
+      x0 = fmaf(-tv, sY[(16 * p + s) * 33 + c2], x0);
+      x1 = fmaf(-tv, sY[(16 * p + s) * 33 + c2 + 1], x1);
+    }
+    sT[(o + 16 + r) * LC + o + c2] = x0;
+    sT[(o + 16 + r) * LC + o + c2 + 1] = x1;
+  }
+  __syncthreads();
+  {
+    const int r = tid >> 3, c4 = (tid & 7) * 4;
+    float y[4] = {};
+    for (int s = 0; s < 32; ++s) {
+      const float av = sA[(32 + r) * LC + s];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) y[u] = fmaf(av, sT[s * LC + c4 + u], y[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sY[r * 33 + c4 + u] = y[u];
+    __syncthreads();
+    float x[4] = {};
+    for (int s = 0; s < 32; ++s) {
+      const float tv = sT[(32 + r) * LC + 32 + s];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = fmaf(-tv, sY[s * 33 + c4 + u], x[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sT[(32 + r) * LC + c4 + u] = x[u];
+  }
+  __syncthreads();
+  float* Tg = a.Tm + cc_off(bh, nch, c);
+  for (int idx = tid; idx < C * C; idx += NT) Tg[idx] = sT[(idx >> 6) * LC + (idx & 63)];
+}
+
+// ---------------------------------------------------------------------------
+// forward chain: chunk-start states and residuals for 32 value columns
+__global__ __launch_bounds__(NT) void bwd_fwd_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) float lds[];
+  float* sK = lds;             // [C][LK]
+  float* sT = sK + C * LK;     // [C][LC]
+  float* sS = sT + C * LC;     // [DP][TW] state tile
+  float* sR = sS + DP * TW;    // [C][TW] V - diag(g) K S0
+  float* sE = sR + C * TW;     // [C][TW] diag(Lambda b) E
+  float* sLg = sE + C * TW;
+  float* sB = sLg + C;
+  float* sAl = sB + C;
+  const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
+  const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C;
+  const bool erase = a.resid != 2;
+  for (int idx = tid; idx < DP * TW; idx += NT) {
+    const int d = idx >> 5, j = idx & 31;
+    sS[idx] = (a.state_in && d < dk && j0 + j < dv) ? a.state_in[((size_t)bh * dk + d) * dv + j0 + j]
+                                                     : 0.f;
+  }
+  const int tm = tid >> 3, tn = tid & 7;  // 64 x 32 outputs: rows 2 tm + i, columns 4 tn + j
+  for (int c = 0; c < nch; ++c) {
+    const int n = min(C, L - c * C);
+    const size_t tok = (size_t)bh * L + (size_t)c * C;
+    __syncthreads();
+    load_rows(a.k + tok * dk, n, dk, sK);
+    if (erase) load_cc(a.Tm + cc_off(bh, nch, c), sT);
+    load_scalars(a, tok, n, sLg, sB, sAl);
+    float* s0g = a.S0s + ((size_t)bh * nch + c) * dk * dv;
+    for (int idx = tid; idx < dk * TW; idx += NT) {
+      const int d = idx >> 5, j = idx & 31;
+      if (j0 + j < dv) s0g[(size_t)d * dv + j0 + j] = sS[idx];
+    }
+    __syncthreads();
+    load_tile(a.v + tok * dv, n, dv, j0, sR, a.resid == 1 ? sAl : nullptr);
+    __syncthreads();
+    float e[2][4] = {};
+    if (erase) {
+      float x[2][4] = {};
+      mma<2, 4>(x, sK, LK, 1, sS, TW, 2 * tm, 4 * tn, dk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const float g = expf(sLg[2 * tm + i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sR[(2 * tm + i) * TW + 4 * tn + j] -= g * x[i][j];
+      }
       __syncthreads();
-      float y = 0.f, p = 0.f, g = 0.f;
+      mma<2, 4>(e, sT, LC, 1, sR, TW, 2 * tm, 4 * tn, C);
+    } else {
 #pragma unroll
-      for (int gg = 0; gg < 8; ++gg) {
-        y += L_.red[par][gg][c];
-        p += L_.red2[par][gg][c];
-        g += L_.red3[par][gg][c];
-      }
-      const float e = L_.v[s][c] - cf * p;
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int r = rg + 8 * i;
-        if (r < dk) L_.row[par][r][c] = be * (G[i] * e - cf * Sp[i] * y);
-      }
-      if (rg == 0) {
-        if (cok) a.dv_out[t * dv + col] = be * y;
-        // over the 32 columns of this tile (one half-wavefront)
-        float da = g - (a.resid == 0 ? be * y * p : 0.f), db = y * e;
-        for (int off = 16; off > 0; off >>= 1) {
-          da += __shfl_xor(da, off, 32);
-          db += __shfl_xor(db, off, 32);
-        }
-        if (c == 0) {
-          a.da_part[tile_id * L + t0 + s] = da;
-          a.db_part[tile_id * L + t0 + s] = db;
-        }
-      }
-      __syncthreads();
-      if (tid < dk) {
-        float sk = 0.f, sq = 0.f;
-        for (int cc = 0; cc < CW; ++cc) {
-          sk += L_.row[par][tid][cc];
-          sq += L_.row2[par][tid][cc];
-        }
-        a.dk_part[(tile_id * L + t0 + s) * dk + tid] = sk;
-        a.dq_part[(tile_id * L + t0 + s) * dk + tid] = sq;
-      }
+        for (int j = 0; j < 4; ++j) e[i][j] = sR[(2 * tm + i) * TW + 4 * tn + j];
+    }
+    const float lgC = sLg[C - 1];
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int r = rg + 8 * i;
-        if (r < dk) {
-          G[i] = fmaf(-cf * be * L_.k[s][r], y, al * G[i]);
-          S[i] = Sp[i];
-        }
+    for (int i = 0; i < 2; ++i) {
+      const int t = 2 * tm + i;
+      const float w = sB[t] * expf(lgC - sLg[t]);
+      float* eg = a.E + ((size_t)bh * nch * C + (size_t)c * C + t) * dv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = j0 + 4 * tn + j;
+        if (t < n && col < dv) eg[col] = e[i][j];
+        sE[t * TW + 4 * tn + j] = e[i][j] * w;
       }
     }
-  }
-  if (a.dstate_in) {
+    __syncthreads();
+    {
+      const int um = tid >> 3, un = tid & 7;  // 128 x 32: rows 4 um + i, columns 4 un + j
+      float s[4][4] = {};
+      mma<4, 4>(s, sK, 1, LK, sE, TW, 4 * um, 4 * un, C);
+      const float gC = expf(lgC);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = rg + 8 * i;
-      if (r < dk && cok) a.dstate_in[((size_t)bh * dk + r) * dv + col] = G[i];
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int idx = (4 * um + i) * TW + 4 * un + j;
+          sS[idx] = fmaf(gC, sS[idx], s[i][j]);
+        }
     }
   }
 }
 
-// Sum the per-tile partials in tile order.
-__global__ void bwd_reduce_kernel(BwdArgs a, int ntiles) {
-  const size_t n = (size_t)a.BH * a.L;
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n * a.dk;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const size_t bh = i / ((size_t)a.L * a.dk), rem = i - bh * a.L * a.dk;
-    float sq = 0.f, sk = 0.f;
-    for (int tl = 0; tl < ntiles; ++tl) {
-      const size_t p = ((bh * ntiles + tl) * a.L) * a.dk + rem;
-      sq += a.dq_part[p];
-      sk += a.dk_part[p];
-    }
-    a.dq[i] = sq;
-    a.dk_out[i] = sk;
+// ---------------------------------------------------------------------------
+// reverse chain: state gradients at chunk ends, dR (= dV), dS0
+__global__ __launch_bounds__(NT) void bwd_rev_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) float lds[];
+  float* sK = lds;             // [C][LK]
+  float* sQ = sK + C * LK;     // [C][LK]
+  float* sT = sQ + C * LK;     // [C][LC]
+  float* sP = sT + C * LC;     // [C][LC]
+  float* sG = sP + C * LC;     // [DP][TW] state gradient tile
+  float* sO = sG + DP * TW;    // [C][TW] dO, then diag(g) dO
+  float* sD = sO + C * TW;     // [C][TW] dE
+  float* sX = sD + C * TW;     // [C][TW] diag(g) dR
+  float* sLg = sX + C * TW;
+  float* sB = sLg + C;
+  float* sAl = sB + C;
+  const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
+  const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C;
+  const bool erase = a.resid != 2;
+  for (int idx = tid; idx < DP * TW; idx += NT) {
+    const int d = idx >> 5, j = idx & 31;
+    sG[idx] = (a.dstate_out && d < dk && j0 + j < dv)
+                  ? a.dstate_out[((size_t)bh * dk + d) * dv + j0 + j]
+                  : 0.f;
   }
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
-       i += (size_t)gridDim.x * blockDim.x) {
-    const size_t bh = i / a.L, t = i - bh * a.L;
-    float da = 0.f, db = 0.f;
-    for (int tl = 0; tl < ntiles; ++tl) {
-      da += a.da_part[(bh * ntiles + tl) * a.L + t];
-      db += a.db_part[(bh * ntiles + tl) * a.L + t];
+  const int tm = tid >> 3, tn = tid & 7;
+  const int um = tid >> 3, un = tid & 7;
+  for (int c = nch - 1; c >= 0; --c) {
+    const int n = min(C, L - c * C);
+    const size_t tok = (size_t)bh * L + (size_t)c * C;
+    __syncthreads();
+    load_rows(a.k + tok * dk, n, dk, sK);
+    load_rows(a.q + tok * dk, n, dk, sQ);
+    load_cc(a.Pm + cc_off(bh, nch, c), sP);
+    if (erase) load_cc(a.Tm + cc_off(bh, nch, c), sT);
+    load_tile(a.d_o + tok * dv, n, dv, j0, sO, nullptr);
+    load_scalars(a, tok, n, sLg, sB, sAl);
+    float* gg = a.Gs + ((size_t)bh * nch + c) * dk * dv;
+    for (int idx = tid; idx < dk * TW; idx += NT) {
+      const int d = idx >> 5, j = idx & 31;
+      if (j0 + j < dv) gg[(size_t)d * dv + j0 + j] = sG[idx];
     }
-    if (a.dalpha) a.dalpha[i] = da;
-    a.dbeta[i] = db;
+    __syncthreads();
+    const float lgC = sLg[C - 1];
+    float r[2][4];
+    {
+      float x[2][4] = {}, y[2][4] = {};
+      mma<2, 4>(x, sP, 1, LC, sO, TW, 2 * tm, 4 * tn, C);
+      mma<2, 4>(y, sK, LK, 1, sG, TW, 2 * tm, 4 * tn, dk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int t = 2 * tm + i;
+        const float w = sB[t] * expf(lgC - sLg[t]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r[i][j] = fmaf(w, y[i][j], x[i][j]);
+          sD[t * TW + 4 * tn + j] = r[i][j];
+        }
+      }
+    }
+    __syncthreads();
+    if (erase) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[i][j] = 0.f;
+      mma<2, 4>(r, sT, 1, LC, sD, TW, 2 * tm, 4 * tn, C);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int t = 2 * tm + i;
+      const float g = expf(sLg[t]);
+      float* rg = a.dR + ((size_t)bh * nch * C + (size_t)c * C + t) * dv;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = j0 + 4 * tn + j;
+        if (t < n && col < dv) {
+          rg[col] = r[i][j];
+          a.dv_out[(tok + t) * dv + col] = a.resid == 1 ? sAl[t] * r[i][j] : r[i][j];
+        }
+        sX[t * TW + 4 * tn + j] = g * r[i][j];
+        sO[t * TW + 4 * tn + j] *= g;
+      }
+    }
+    __syncthreads();
+    {
+      float s1[4][4] = {};
+      mma<4, 4>(s1, sQ, 1, LK, sO, TW, 4 * um, 4 * un, C);
+      if (erase) {
+        float s2[4][4] = {};
+        mma<4, 4>(s2, sK, 1, LK, sX, TW, 4 * um, 4 * un, C);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s1[i][j] -= s2[i][j];
+      }
+      const float gC = expf(lgC);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int idx = (4 * um + i) * TW + 4 * un + j;
+          sG[idx] = fmaf(gC, sG[idx], s1[i][j]);
+        }
+    }
   }
+  __syncthreads();
+  if (a.dstate_in) {
+    for (int idx = tid; idx < dk * TW; idx += NT) {
+      const int d = idx >> 5, j = idx & 31;
+      if (j0 + j < dv) a.dstate_in[((size_t)bh * dk + d) * dv + j0 + j] = sG[idx];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// contractions over the value columns; part 0: dO S0^T, dO E^T; part 1:
+// dR S0^T, dR E^T; part 2: E G^T, <G, S0>
+__global__ __launch_bounds__(NT) void bwd_contract_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) float lds[];
+  constexpr int LA = TW + 1;
+  float* sA = lds;               // [C][LA] left operand block
+  float* sBt = sA + C * LA + 64; // [TW][LK] S0^T or G^T block (offset keeps 16-byte alignment)
+  float* sEt = sBt + TW * LK;    // [TW][LT] E^T block
+  float* sRed = sEt + TW * LT;   // [NT / 64]
+  const int bh = blockIdx.x, c = blockIdx.y, part = blockIdx.z, tid = threadIdx.x;
+  const int nch = gridDim.y, L = a.L, dk = a.dk, dv = a.dv;
+  const int n = min(C, L - c * C);
+  const size_t row0 = (size_t)bh * nch * C + (size_t)c * C;  // padded-row arrays
+  const float* left = part == 0 ? a.d_o + ((size_t)bh * L + (size_t)c * C) * dv
+                                : (part == 1 ? a.dR : a.E) + row0 * dv;
+  const float* S0c = a.S0s + ((size_t)bh * nch + c) * dk * dv;
+  const float* right = part == 2 ? a.Gs + ((size_t)bh * nch + c) * dk * dv : S0c;
+  const float* Ec = a.E + row0 * dv;
+  const int tm = tid >> 4, tn = tid & 15;
+  float m[4][8] = {};
+  float p[4][4] = {};
+  float gs = 0.f;
+  for (int jb = 0; jb < dv; jb += TW) {
+    __syncthreads();
+    for (int idx = tid; idx < C * TW; idx += NT) {
+      const int t = idx >> 5, j = idx & 31;
+      const bool ok = t < n && jb + j < dv;
+      sA[t * LA + j] = ok ? left[(size_t)t * dv + jb + j] : 0.f;
+      if (part < 2) sEt[j * LT + t] = ok ? Ec[(size_t)t * dv + jb + j] : 0.f;
+    }
+    for (int idx = tid; idx < DP * TW; idx += NT) {
+      const int d = idx >> 5, j = idx & 31;
+      float x = 0.f;
+      if (d < dk && jb + j < dv) {
+        x = right[(size_t)d * dv + jb + j];
+        if (part == 2) gs = fmaf(x, S0c[(size_t)d * dv + jb + j], gs);
+      }
+      sBt[j * LK + d] = x;
+    }
+    __syncthreads();
+    const int K = min(TW, dv - jb);
+    mma<4, 8>(m, sA, LA, 1, sBt, LK, 4 * tm, 8 * tn, K);
+    if (part < 2) mma<4, 4>(p, sA, LA, 1, sEt, LT, 4 * tm, 4 * tn, K);
+  }
+  float* M = (part == 0 ? a.M1 : part == 1 ? a.M2 : a.M3) + row0 * dk;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = 8 * tn + j;
+      if (d < dk) M[(size_t)(4 * tm + i) * dk + d] = m[i][j];
+    }
+  if (part < 2) {
+    float* P = (part == 0 ? a.dPm : a.dA) + cc_off(bh, nch, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) P[(4 * tm + i) * C + 4 * tn + j] = p[i][j];
+  } else {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) gs += __shfl_xor(gs, off, 64);
+    if ((tid & 63) == 0) sRed[tid >> 6] = gs;
+    __syncthreads();
+    if (tid == 0) a.gs0[(size_t)bh * nch + c] = (sRed[0] + sRed[1]) + (sRed[2] + sRed[3]);
+  }
+}
+
+__device__ __forceinline__ float sum16(float x) {
+  x += __shfl_xor(x, 1, 16);
+  x += __shfl_xor(x, 2, 16);
+  x += __shfl_xor(x, 4, 16);
+  x += __shfl_xor(x, 8, 16);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// per-token gradients of one chunk
+__global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) float lds[];
+  float* sQ = lds;               // [C][LK]
+  float* sK = sQ + C * LK;       // [C][LK]
+  float* sXp = sK + C * LK;      // [C][LC]
+  float* sXa = sXp + C * LC;     // [C][LC]
+  float* sXpb = sXa + C * LC;    // [C][LC] Xp diag(b)
+  float* sXab = sXpb + C * LC;   // [C][LC] Xa diag(b)
+  float* sW = sXab + C * LC;     // [C][LC] dPm * Pm + dA * A
+  float* sLg = sW + C * LC;
+  float* sB = sLg + C;
+  float* sAl = sB + C;
+  float* sRow = sAl + C;         // [5][C]
+  const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, nch = gridDim.y;
+  const int L = a.L, dk = a.dk, dv = a.dv;
+  const int n = min(C, L - c * C);
+  const size_t tok = (size_t)bh * L + (size_t)c * C;
+  const size_t row0 = (size_t)bh * nch * C + (size_t)c * C;
+  const bool erase = a.resid != 2, plain = a.resid == 1;
+  load_rows(a.q + tok * dk, n, dk, sQ);
+  load_rows(a.k + tok * dk, n, dk, sK);
+  load_scalars(a, tok, n, sLg, sB, sAl);
+  __syncthreads();
+  {
+    const size_t o = cc_off(bh, nch, c);
+    const float *Pg = a.Pm + o, *Ag = a.Am + o, *dPg = a.dPm + o, *dAg = a.dA + o;
+    for (int idx = tid; idx < C * C; idx += NT) {
+      const int t = idx >> 6, s = idx & 63;
+      const bool lo = s <= t, st = erase && s < t;
+      const float D = lo ? expf(sLg[t] - sLg[s]) : 0.f;
+      const float dp = lo ? dPg[idx] : 0.f;
+      const float da = st ? -dAg[idx] : 0.f;
+      const float xp = dp * D, xa = da * D;
+      sXp[t * LC + s] = xp;
+      sXa[t * LC + s] = xa;
+      sXpb[t * LC + s] = xp * sB[s];
+      sXab[t * LC + s] = xa * sB[s];
+      sW[t * LC + s] = dp * (lo ? Pg[idx] : 0.f) + da * (st ? Ag[idx] : 0.f);
+    }
+  }
+  __syncthreads();
+  const int tm = tid >> 4, tn = tid & 15;  // 64 x 128: rows 4 tm + i, columns 8 tn + j
+  const float lgC = sLg[C - 1];
+  float pq[4], kr[4], wv[4], dbv[4], vv[4];
+  {  // dQ = diag(g) dO S0^T + Xp B
+    float acc[4][8] = {};
+    mma<4, 8>(acc, sXpb, LC, 1, sK, LK, 4 * tm, 8 * tn, C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * tm + i;
+      const float g = expf(sLg[t]);
+      const float* m1 = a.M1 + (row0 + t) * dk;
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = 8 * tn + j;
+        const float x = d < dk ? m1[d] : 0.f;
+        s = fmaf(x, sQ[t * LK + d], s);
+        if (t < n && d < dk) a.dq[(tok + t) * dk + d] = fmaf(g, x, acc[i][j]);
+      }
+      pq[i] = g * s;
+    }
+  }
+  {  // dB = Xp^T Q + Xa^T K + diag(Lambda) E G^T;  dK = Xa B - diag(g) dR S0^T + diag(b) dB
+    float db[4][8] = {};
+    mma<4, 8>(db, sXp, 1, LC, sQ, LK, 4 * tm, 8 * tn, C);
+    if (erase) mma<4, 8>(db, sXa, 1, LC, sK, LK, 4 * tm, 8 * tn, C);
+    float dkk[4][8] = {};
+    if (erase) mma<4, 8>(dkk, sXab, LC, 1, sK, LK, 4 * tm, 8 * tn, C);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 4 * tm + i;
+      const float lam = expf(lgC - sLg[t]), g = expf(sLg[t]), b = sB[t];
+      const float* m3 = a.M3 + (row0 + t) * dk;
+      const float* m2 = a.M2 + (row0 + t) * dk;
+      float w = 0.f, sb = 0.f, sr = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = 8 * tn + j;
+        const float kv = sK[t * LK + d];
+        const float x3 = d < dk ? m3[d] : 0.f;
+        const float x2 = (erase && d < dk) ? m2[d] : 0.f;
+        w = fmaf(kv, x3, w);
+        const float dbb = fmaf(lam, x3, db[i][j]);
+        sb = fmaf(dbb, kv, sb);
+        const float dkr = -g * x2;
+        sr = fmaf(dkr, kv, sr);
+        if (t < n && d < dk) a.dk_out[(tok + t) * dk + d] = fmaf(b, dbb, dkk[i][j] + dkr);
+      }
+      wv[i] = lam * b * w;
+      dbv[i] = sb;
+      kr[i] = sr;
+      float s = 0.f;
+      if (plain && t < n) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = 8 * tn + j;
+          if (col < dv) s = fmaf(a.dR[(row0 + t) * dv + col], a.v[(tok + t) * dv + col], s);
+        }
+      }
+      vv[i] = s;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    pq[i] = sum16(pq[i]);
+    kr[i] = sum16(kr[i]);
+    wv[i] = sum16(wv[i]);
+    dbv[i] = sum16(dbv[i]);
+    vv[i] = sum16(vv[i]);
+    if (tn == 0) {
+      const int t = 4 * tm + i;
+      sRow[t] = pq[i];
+      sRow[C + t] = kr[i];
+      sRow[2 * C + t] = wv[i];
+      sRow[3 * C + t] = dbv[i];
+      sRow[4 * C + t] = vv[i];
+    }
+  }
+  __syncthreads();
+  if (tid < C) {
+    const int t = tid;
+    float rs = 0.f, cs = 0.f;
+    for (int s = 0; s < C; ++s) {
+      rs += sW[t * LC + s];
+      cs += sW[s * LC + t];
+    }
+    const float w = sRow[2 * C + t];
+    float dl = (rs - cs) + sRow[t] + sRow[C + t] - w;
+    float wsum = w;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off, 64);
+    if (t == n - 1) dl += expf(lgC) * a.gs0[(size_t)bh * nch + c] + wsum;
+    float suf = dl;  // sum over t' >= t (tokens past the end hold 0)
+#pragma unroll
+    for (int off = 1; off < C; off <<= 1) {
+      const float y = __shfl_down(suf, off, 64);
+      if (t + off < C) suf += y;
+    }
+    if (t < n) {
+      const float al = sAl[t], dbp = sRow[3 * C + t];
+      float dal = suf / al, dbe = dbp;
+      if (plain) {
+        dal += -dbp * sB[t] / al + sRow[4 * C + t];
+        dbe = dbp / al;
+      }
+      if (a.dalpha) a.dalpha[tok + t] = dal;
+      a.dbeta[tok + t] = dbe;
+    }
+  }
+}
+
+struct BwdPlan {
+  size_t off[14];
+  size_t total;
+};
+
+BwdPlan plan_bwd(int BH, int L, int dk, int dv) {
+  const size_t nch = ((size_t)L + C - 1) / C, Lp = nch * C;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t sz[14] = {
+      (size_t)BH * nch * dk * dv, (size_t)BH * nch * dk * dv,           // S0s, Gs
+      (size_t)BH * Lp * dv,       (size_t)BH * Lp * dv,                 // E, dR
+      (size_t)BH * nch * C * C,   (size_t)BH * nch * C * C,             // Am, Tm
+      (size_t)BH * nch * C * C,                                         // Pm
+      (size_t)BH * Lp * dk,       (size_t)BH * Lp * dk, (size_t)BH * Lp * dk,  // M1..M3
+      (size_t)BH * nch * C * C,   (size_t)BH * nch * C * C,             // dPm, dA
+      (size_t)BH * nch,           0};                                   // gs0
+  BwdPlan p{};
+  size_t o = 0;
+  for (int i = 0; i < 14; ++i) {
+    p.off[i] = o;
+    o += up(sz[i] * 4);
+  }
+  p.total = o;
+  return p;
+}
+
+template <typename K>
+hipError_t launch_lds(K kern, dim3 grid, size_t lds, const BwdArgs& a, hipStream_t s) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(NT), lds, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 size_t scan_bwd_workspace_bytes(int BH, int L, int dk, int dv) {
-  const size_t ntiles = (dv + CW - 1) / CW, nchunks = ((size_t)L + CH - 1) / CH;
-  const size_t tiles = (size_t)BH * ntiles;
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  return up(tiles * nchunks * dk * CW * 4) + up(tiles * (CH + 1) * dk * CW * 4) +
-         2 * up(tiles * L * dk * 4) + 2 * up(tiles * L * 4);
+  return plan_bwd(BH, L, dk, dv).total;
 }
 
 hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
-  const int ntiles = (a.dv + CW - 1) / CW, nchunks = (a.L + CH - 1) / CH;
-  const size_t tiles = (size_t)a.BH * ntiles;
-  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  char* p = static_cast<char*>(ws);
-  a.ckpt = reinterpret_cast<float*>(p);
-  p += up(tiles * nchunks * a.dk * CW * 4);
-  a.hist = reinterpret_cast<float*>(p);
-  p += up(tiles * (CH + 1) * a.dk * CW * 4);
-  a.dq_part = reinterpret_cast<float*>(p);
-  p += up(tiles * a.L * a.dk * 4);
-  a.dk_part = reinterpret_cast<float*>(p);
-  p += up(tiles * a.L * a.dk * 4);
-  a.da_part = reinterpret_cast<float*>(p);
-  p += up(tiles * a.L * 4);
-  a.db_part = reinterpret_cast<float*>(p);
-  const size_t lds = sizeof(BwdLds);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_bwd_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (a.dk > DP || a.dv > 128) return hipErrorInvalidValue;
+  const BwdPlan p = plan_bwd(a.BH, a.L, a.dk, a.dv);
+  char* b = static_cast<char*>(ws);
+  float** parts[13] = {&a.S0s, &a.Gs, &a.E, &a.dR, &a.Am, &a.Tm, &a.Pm,
+                       &a.M1,  &a.M2, &a.M3, &a.dPm, &a.dA, &a.gs0};
+  for (int i = 0; i < 13; ++i) *parts[i] = reinterpret_cast<float*>(b + p.off[i]);
+  const int nch = (a.L + C - 1) / C, ntw = (a.dv + TW - 1) / TW;
+  const size_t f = sizeof(float);
+  hipError_t e;
+  e = launch_lds(bwd_prep_kernel, dim3(a.BH, nch),
+                 (2 * DP * LT + 2 * C * LC + 32 * 33 + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(scan_bwd_kernel, dim3(a.BH, ntiles), dim3(NT), lds, s, a);
-  e = hipGetLastError();
+  e = launch_lds(bwd_fwd_kernel, dim3(a.BH, ntw),
+                 (C * LK + C * LC + DP * TW + 2 * C * TW + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_reduce_kernel, dim3(1024), dim3(256), 0, s, a, ntiles);
-  return hipGetLastError();
+  e = launch_lds(bwd_rev_kernel, dim3(a.BH, ntw),
+                 (2 * C * LK + 2 * C * LC + DP * TW + 3 * C * TW + 3 * C) * f, a, s);
+  if (e != hipSuccess) return e;
+  e = launch_lds(bwd_contract_kernel, dim3(a.BH, nch, 3),
+                 (C * (TW + 1) + 64 + TW * LK + TW * LT + NT / 64) * f, a, s);
+  if (e != hipSuccess) return e;
+  return launch_lds(bwd_grad_kernel, dim3(a.BH, nch),
+                    (2 * C * LK + 5 * C * LC + 3 * C + 5 * C) * f, a, s);
 }
 
 }  // namespace kdn

@@ -238,8 +238,9 @@ def _bwd(kdn, **kw):
 def test_backward_rejections(kdn):
     c = _header_constants()
     need = kdn.lib.kdn_scan_bwd_workspace_size(1, 1, 64, 128, 128)
-    # one 64-token checkpoint and 65 recomputed states per 32-column tile, partials
-    assert need >= 4 * (1 + 65) * 128 * 32 * 4
+    # one 64-token chunk: its start state and end-state gradient, residuals and
+    # their gradients, three [64, d_k] contractions, five 64 x 64 chunk matrices
+    assert need >= 4 * (2 * 128 * 128 + 2 * 64 * 128 + 3 * 64 * 128 + 5 * 64 * 64)
     assert _bwd(kdn, resid=3) == c["KDN_ERR_BAD_MODE"]
     assert _bwd(kdn, dk_=129) == c["KDN_ERR_BAD_SHAPE"]
     assert _bwd(kdn, L=-1) == c["KDN_ERR_BAD_SHAPE"]
