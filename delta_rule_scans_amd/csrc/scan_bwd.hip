@@ -71,20 +71,89 @@ __device__ __forceinline__ void mma(float (&acc)[TM][TN], const float* pa, int a
   }
 }
 
+// Loads are split in two: fetch into registers (every load of a chunk in
+// flight at once, or during the previous chunk's products), then put into LDS.
+template <int N>
+struct Frag {
+  float x[N];
+};
+constexpr int kRowsPer = C * DP / NT;  // [C][d_k] block
+constexpr int kCCPer = C * C / NT;     // [C][C] matrix
+constexpr int kTilePer = C * TW / NT;  // [C][TW] value tile
+
+// [C][d] rows (n valid), zero padded to [C][DP]
+__device__ __forceinline__ void fetch_rows(Frag<kRowsPer>& f, const float* src, int n, int d) {
+#pragma unroll
+  for (int u = 0; u < kRowsPer; ++u) {
+    const int idx = threadIdx.x + u * NT, t = idx >> 7, i = idx & (DP - 1);
+    f.x[u] = (t < n && i < d) ? src[(size_t)t * d + i] : 0.f;
+  }
+}
+__device__ __forceinline__ void put_rows(const Frag<kRowsPer>& f, float* dst) {
+#pragma unroll
+  for (int u = 0; u < kRowsPer; ++u) {
+    const int idx = threadIdx.x + u * NT;
+    dst[(idx >> 7) * LK + (idx & (DP - 1))] = f.x[u];
+  }
+}
+// transposed: dst[i][t] with row stride LT
+__device__ __forceinline__ void put_rows_t(const Frag<kRowsPer>& f, float* dst) {
+#pragma unroll
+  for (int u = 0; u < kRowsPer; ++u) {
+    const int idx = threadIdx.x + u * NT;
+    dst[(idx & (DP - 1)) * LT + (idx >> 7)] = f.x[u];
+  }
+}
+// a row-major [C][C] matrix
+__device__ __forceinline__ void fetch_cc(Frag<kCCPer>& f, const float* src) {
+#pragma unroll
+  for (int u = 0; u < kCCPer; ++u) f.x[u] = src[threadIdx.x + u * NT];
+}
+__device__ __forceinline__ void put_cc(const Frag<kCCPer>& f, float* dst) {
+#pragma unroll
+  for (int u = 0; u < kCCPer; ++u) {
+    const int idx = threadIdx.x + u * NT;
+    dst[(idx >> 6) * LC + (idx & 63)] = f.x[u];
+  }
+}
+// columns j0 .. j0 + TW - 1 of [C][dv] rows (n valid), zero padded
+__device__ __forceinline__ void fetch_tile(Frag<kTilePer>& f, const float* src, int n, int dv,
+                                           int j0) {
+#pragma unroll
+  for (int u = 0; u < kTilePer; ++u) {
+    const int idx = threadIdx.x + u * NT, t = idx >> 5, j = idx & 31;
+    f.x[u] = (t < n && j0 + j < dv) ? src[(size_t)t * dv + j0 + j] : 0.f;
+  }
+}
+// rows scaled by rs[t] when given
+__device__ __forceinline__ void put_tile(const Frag<kTilePer>& f, float* dst, const float* rs) {
+#pragma unroll
+  for (int u = 0; u < kTilePer; ++u) {
+    const int idx = threadIdx.x + u * NT;
+    dst[idx] = rs ? f.x[u] * rs[idx >> 5] : f.x[u];
+  }
+}
+
 // Chunk scalars (first wavefront): cumulative log decay, write scale b (beta,
 // or beta / alpha for the plain residual), decay. Tokens past the end get
 // alpha = 1 and b = 0, which leaves every product unchanged.
-__device__ void load_scalars(const BwdArgs& a, size_t tok, int n, float* sLg, float* sB,
-                             float* sAl) {
+struct Scal {
+  float al, be;
+};
+__device__ __forceinline__ Scal fetch_scalars(const BwdArgs& a, size_t tok, int n) {
+  const int t = threadIdx.x;
+  Scal r{1.f, 0.f};
+  if (t < n && t < C) {
+    r.al = a.alpha ? a.alpha[tok + t] : 1.f;
+    r.be = a.beta[tok + t];
+  }
+  return r;
+}
+__device__ void put_scalars(const BwdArgs& a, Scal f, float* sLg, float* sB, float* sAl) {
   const int t = threadIdx.x;
   if (t < C) {
-    float al = 1.f, b = 0.f;
-    if (t < n) {
-      al = a.alpha ? a.alpha[tok + t] : 1.f;
-      b = a.beta[tok + t];
-      if (a.resid == 1) b /= al;
-    }
-    float lg = logf(al);
+    const float b = a.resid == 1 ? f.be / f.al : f.be;
+    float lg = logf(f.al);
 #pragma unroll
     for (int off = 1; off < C; off <<= 1) {
       const float y = __shfl_up(lg, off, C);
@@ -92,33 +161,10 @@ __device__ void load_scalars(const BwdArgs& a, size_t tok, int n, float* sLg, fl
     }
     sLg[t] = lg;
     sB[t] = b;
-    sAl[t] = al;
+    sAl[t] = f.al;
   }
 }
 
-// [C][d] rows (n valid) into LDS [C][LK], zero padded.
-__device__ void load_rows(const float* src, int n, int d, float* dst) {
-  for (int idx = threadIdx.x; idx < C * DP; idx += NT) {
-    const int t = idx >> 7, i = idx & (DP - 1);
-    dst[t * LK + i] = (t < n && i < d) ? src[(size_t)t * d + i] : 0.f;
-  }
-}
-
-// A row-major [C][C] matrix into LDS [C][LC].
-__device__ void load_cc(const float* src, float* dst) {
-  for (int idx = threadIdx.x; idx < C * C; idx += NT) dst[(idx >> 6) * LC + (idx & 63)] = src[idx];
-}
-
-// Columns j0 .. j0 + TW - 1 of [C][dv] rows (n valid) into LDS [C][TW], zero
-// padded, rows scaled by rs[t] when given.
-__device__ void load_tile(const float* src, int n, int dv, int j0, float* dst, const float* rs) {
-  for (int idx = threadIdx.x; idx < C * TW; idx += NT) {
-    const int t = idx >> 5, j = idx & 31;
-    float x = 0.f;
-    if (t < n && j0 + j < dv) x = src[(size_t)t * dv + j0 + j];
-    dst[idx] = rs ? x * rs[t] : x;
-  }
-}
 
 __device__ __forceinline__ size_t cc_off(int bh, int nch, int c) {
   return ((size_t)bh * nch + c) * C * C;
@@ -140,14 +186,16 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   const int n = min(C, a.L - c * C), dk = a.dk;
   const size_t tok = (size_t)bh * a.L + (size_t)c * C;
   const bool erase = a.resid != 2;
-  for (int idx = tid; idx < C * DP; idx += NT) {
-    const int t = idx >> 7, i = idx & (DP - 1);
-    const bool ok = t < n && i < dk;
-    sKt[i * LT + t] = ok ? a.k[(tok + t) * dk + i] : 0.f;
-    sQt[i * LT + t] = ok ? a.q[(tok + t) * dk + i] : 0.f;
+  {
+    Frag<kRowsPer> fk, fq;
+    fetch_rows(fk, a.k + tok * dk, n, dk);
+    fetch_rows(fq, a.q + tok * dk, n, dk);
+    const Scal sc = fetch_scalars(a, tok, n);
+    for (int idx = tid; idx < C * LC; idx += NT) sT[idx] = 0.f;
+    put_rows_t(fk, sKt);
+    put_rows_t(fq, sQt);
+    put_scalars(a, sc, sLg, sB, sAl);
   }
-  for (int idx = tid; idx < C * LC; idx += NT) sT[idx] = 0.f;
-  load_scalars(a, tok, n, sLg, sB, sAl);
   __syncthreads();
   const int tm = tid >> 4, tn = tid & 15;
   float kk[4][4] = {}, qk[4][4] = {};
@@ -263,20 +311,34 @@ __global__ __launch_bounds__(NT) void bwd_fwd_kernel(BwdArgs a) {
                                                      : 0.f;
   }
   const int tm = tid >> 3, tn = tid & 7;  // 64 x 32 outputs: rows 2 tm + i, columns 4 tn + j
-  for (int c = 0; c < nch; ++c) {
+  // the next chunk's inputs, fetched while the current one is computed
+  Frag<kRowsPer> fk;
+  Frag<kCCPer> ft;
+  Frag<kTilePer> fv;
+  Scal fs;
+  auto fetch = [&](int c) {
     const int n = min(C, L - c * C);
     const size_t tok = (size_t)bh * L + (size_t)c * C;
+    fetch_rows(fk, a.k + tok * dk, n, dk);
+    if (erase) fetch_cc(ft, a.Tm + cc_off(bh, nch, c));
+    fetch_tile(fv, a.v + tok * dv, n, dv, j0);
+    fs = fetch_scalars(a, tok, n);
+  };
+  fetch(0);
+  for (int c = 0; c < nch; ++c) {
+    const int n = min(C, L - c * C);
     __syncthreads();
-    load_rows(a.k + tok * dk, n, dk, sK);
-    if (erase) load_cc(a.Tm + cc_off(bh, nch, c), sT);
-    load_scalars(a, tok, n, sLg, sB, sAl);
+    put_rows(fk, sK);
+    if (erase) put_cc(ft, sT);
+    put_scalars(a, fs, sLg, sB, sAl);
     float* s0g = a.S0s + ((size_t)bh * nch + c) * dk * dv;
     for (int idx = tid; idx < dk * TW; idx += NT) {
       const int d = idx >> 5, j = idx & 31;
       if (j0 + j < dv) s0g[(size_t)d * dv + j0 + j] = sS[idx];
     }
     __syncthreads();
-    load_tile(a.v + tok * dv, n, dv, j0, sR, a.resid == 1 ? sAl : nullptr);
+    put_tile(fv, sR, a.resid == 1 ? sAl : nullptr);
+    if (c + 1 < nch) fetch(c + 1);
     __syncthreads();
     float e[2][4] = {};
     if (erase) {
@@ -352,16 +414,32 @@ __global__ __launch_bounds__(NT) void bwd_rev_kernel(BwdArgs a) {
   }
   const int tm = tid >> 3, tn = tid & 7;
   const int um = tid >> 3, un = tid & 7;
+  Frag<kRowsPer> fk, fq;
+  Frag<kCCPer> fp, ft;
+  Frag<kTilePer> fo;
+  Scal fs;
+  auto fetch = [&](int c) {
+    const int n = min(C, L - c * C);
+    const size_t tok = (size_t)bh * L + (size_t)c * C;
+    fetch_rows(fk, a.k + tok * dk, n, dk);
+    fetch_rows(fq, a.q + tok * dk, n, dk);
+    fetch_cc(fp, a.Pm + cc_off(bh, nch, c));
+    if (erase) fetch_cc(ft, a.Tm + cc_off(bh, nch, c));
+    fetch_tile(fo, a.d_o + tok * dv, n, dv, j0);
+    fs = fetch_scalars(a, tok, n);
+  };
+  fetch(nch - 1);
   for (int c = nch - 1; c >= 0; --c) {
     const int n = min(C, L - c * C);
     const size_t tok = (size_t)bh * L + (size_t)c * C;
     __syncthreads();
-    load_rows(a.k + tok * dk, n, dk, sK);
-    load_rows(a.q + tok * dk, n, dk, sQ);
-    load_cc(a.Pm + cc_off(bh, nch, c), sP);
-    if (erase) load_cc(a.Tm + cc_off(bh, nch, c), sT);
-    load_tile(a.d_o + tok * dv, n, dv, j0, sO, nullptr);
-    load_scalars(a, tok, n, sLg, sB, sAl);
+    put_rows(fk, sK);
+    put_rows(fq, sQ);
+    put_cc(fp, sP);
+    if (erase) put_cc(ft, sT);
+    put_tile(fo, sO, nullptr);
+    put_scalars(a, fs, sLg, sB, sAl);
+    if (c > 0) fetch(c - 1);
     float* gg = a.Gs + ((size_t)bh * nch + c) * dk * dv;
     for (int idx = tid; idx < dk * TW; idx += NT) {
       const int d = idx >> 5, j = idx & 31;
@@ -464,21 +542,29 @@ __global__ __launch_bounds__(NT) void bwd_contract_kernel(BwdArgs a) {
   float p[4][4] = {};
   float gs = 0.f;
   for (int jb = 0; jb < dv; jb += TW) {
-    __syncthreads();
-    for (int idx = tid; idx < C * TW; idx += NT) {
-      const int t = idx >> 5, j = idx & 31;
-      const bool ok = t < n && jb + j < dv;
-      sA[t * LA + j] = ok ? left[(size_t)t * dv + jb + j] : 0.f;
-      if (part < 2) sEt[j * LT + t] = ok ? Ec[(size_t)t * dv + jb + j] : 0.f;
+    Frag<kTilePer> fl, fe;
+    Frag<DP * TW / NT> fr, fs0;
+    fetch_tile(fl, left, n, dv, jb);
+    if (part < 2) fetch_tile(fe, Ec, n, dv, jb);
+#pragma unroll
+    for (int u = 0; u < DP * TW / NT; ++u) {
+      const int idx = tid + u * NT, d = idx >> 5, j = idx & 31;
+      const bool ok = d < dk && jb + j < dv;
+      fr.x[u] = ok ? right[(size_t)d * dv + jb + j] : 0.f;
+      fs0.x[u] = (ok && part == 2) ? S0c[(size_t)d * dv + jb + j] : 0.f;
     }
-    for (int idx = tid; idx < DP * TW; idx += NT) {
-      const int d = idx >> 5, j = idx & 31;
-      float x = 0.f;
-      if (d < dk && jb + j < dv) {
-        x = right[(size_t)d * dv + jb + j];
-        if (part == 2) gs = fmaf(x, S0c[(size_t)d * dv + jb + j], gs);
-      }
-      sBt[j * LK + d] = x;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kTilePer; ++u) {
+      const int idx = tid + u * NT, t = idx >> 5, j = idx & 31;
+      sA[t * LA + j] = fl.x[u];
+      if (part < 2) sEt[j * LT + t] = fe.x[u];
+    }
+#pragma unroll
+    for (int u = 0; u < DP * TW / NT; ++u) {
+      const int idx = tid + u * NT, d = idx >> 5, j = idx & 31;
+      sBt[j * LK + d] = fr.x[u];
+      gs = fmaf(fr.x[u], fs0.x[u], gs);
     }
     __syncthreads();
     const int K = min(TW, dv - jb);
@@ -537,26 +623,37 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
   const size_t tok = (size_t)bh * L + (size_t)c * C;
   const size_t row0 = (size_t)bh * nch * C + (size_t)c * C;
   const bool erase = a.resid != 2, plain = a.resid == 1;
-  load_rows(a.q + tok * dk, n, dk, sQ);
-  load_rows(a.k + tok * dk, n, dk, sK);
-  load_scalars(a, tok, n, sLg, sB, sAl);
-  __syncthreads();
   {
-    const size_t o = cc_off(bh, nch, c);
-    const float *Pg = a.Pm + o, *Ag = a.Am + o, *dPg = a.dPm + o, *dAg = a.dA + o;
-    for (int idx = tid; idx < C * C; idx += NT) {
-      const int t = idx >> 6, s = idx & 63;
-      const bool lo = s <= t, st = erase && s < t;
-      const float D = lo ? expf(sLg[t] - sLg[s]) : 0.f;
-      const float dp = lo ? dPg[idx] : 0.f;
-      const float da = st ? -dAg[idx] : 0.f;
-      const float xp = dp * D, xa = da * D;
-      sXp[t * LC + s] = xp;
-      sXa[t * LC + s] = xa;
-      sXpb[t * LC + s] = xp * sB[s];
-      sXab[t * LC + s] = xa * sB[s];
-      sW[t * LC + s] = dp * (lo ? Pg[idx] : 0.f) + da * (st ? Ag[idx] : 0.f);
-    }
+    Frag<kRowsPer> fq, fk;
+    fetch_rows(fq, a.q + tok * dk, n, dk);
+    fetch_rows(fk, a.k + tok * dk, n, dk);
+    const Scal sc = fetch_scalars(a, tok, n);
+    put_rows(fq, sQ);
+    put_rows(fk, sK);
+    put_scalars(a, sc, sLg, sB, sAl);
+  }
+  const size_t o = cc_off(bh, nch, c);
+  Frag<kCCPer> fP, fA, fdP, fdA;
+  fetch_cc(fP, a.Pm + o);
+  fetch_cc(fdP, a.dPm + o);
+  if (erase) {
+    fetch_cc(fA, a.Am + o);
+    fetch_cc(fdA, a.dA + o);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kCCPer; ++u) {
+    const int idx = tid + u * NT, t = idx >> 6, s = idx & 63;
+    const bool lo = s <= t, st = erase && s < t;
+    const float D = lo ? expf(sLg[t] - sLg[s]) : 0.f;
+    const float dp = lo ? fdP.x[u] : 0.f;
+    const float da = st ? -fdA.x[u] : 0.f;
+    const float xp = dp * D, xa = da * D;
+    sXp[t * LC + s] = xp;
+    sXa[t * LC + s] = xa;
+    sXpb[t * LC + s] = xp * sB[s];
+    sXab[t * LC + s] = xa * sB[s];
+    sW[t * LC + s] = dp * (lo ? fP.x[u] : 0.f) + (st ? da * fA.x[u] : 0.f);
   }
   __syncthreads();
   const int tm = tid >> 4, tn = tid & 15;  // 64 x 128: rows 4 tm + i, columns 8 tn + j
