@@ -77,60 +77,64 @@ template <int N>
 struct Frag {
   float x[N];
 };
-constexpr int kRowsPer = C * DP / NT;  // [C][d_k] block
-constexpr int kCCPer = C * C / NT;     // [C][C] matrix
-constexpr int kTilePer = C * TW / NT;  // [C][TW] value tile
 
 // [C][d] rows (n valid), zero padded to [C][DP]
-__device__ __forceinline__ void fetch_rows(Frag<kRowsPer>& f, const float* src, int n, int d) {
+template <int NTH>
+__device__ __forceinline__ void fetch_rows(Frag<C * DP / NTH>& f, const float* src, int n, int d) {
 #pragma unroll
-  for (int u = 0; u < kRowsPer; ++u) {
-    const int idx = threadIdx.x + u * NT, t = idx >> 7, i = idx & (DP - 1);
+  for (int u = 0; u < C * DP / NTH; ++u) {
+    const int idx = threadIdx.x + u * NTH, t = idx >> 7, i = idx & (DP - 1);
     f.x[u] = (t < n && i < d) ? src[(size_t)t * d + i] : 0.f;
   }
 }
-__device__ __forceinline__ void put_rows(const Frag<kRowsPer>& f, float* dst) {
+template <int NTH, int LD>
+__device__ __forceinline__ void put_rows(const Frag<C * DP / NTH>& f, float* dst) {
 #pragma unroll
-  for (int u = 0; u < kRowsPer; ++u) {
-    const int idx = threadIdx.x + u * NT;
-    dst[(idx >> 7) * LK + (idx & (DP - 1))] = f.x[u];
+  for (int u = 0; u < C * DP / NTH; ++u) {
+    const int idx = threadIdx.x + u * NTH;
+    dst[(idx >> 7) * LD + (idx & (DP - 1))] = f.x[u];
   }
 }
 // transposed: dst[i][t] with row stride LT
-__device__ __forceinline__ void put_rows_t(const Frag<kRowsPer>& f, float* dst) {
+template <int NTH>
+__device__ __forceinline__ void put_rows_t(const Frag<C * DP / NTH>& f, float* dst) {
 #pragma unroll
-  for (int u = 0; u < kRowsPer; ++u) {
-    const int idx = threadIdx.x + u * NT;
+  for (int u = 0; u < C * DP / NTH; ++u) {
+    const int idx = threadIdx.x + u * NTH;
     dst[(idx & (DP - 1)) * LT + (idx >> 7)] = f.x[u];
   }
 }
 // a row-major [C][C] matrix
-__device__ __forceinline__ void fetch_cc(Frag<kCCPer>& f, const float* src) {
+template <int NTH>
+__device__ __forceinline__ void fetch_cc(Frag<C * C / NTH>& f, const float* src) {
 #pragma unroll
-  for (int u = 0; u < kCCPer; ++u) f.x[u] = src[threadIdx.x + u * NT];
+  for (int u = 0; u < C * C / NTH; ++u) f.x[u] = src[threadIdx.x + u * NTH];
 }
-__device__ __forceinline__ void put_cc(const Frag<kCCPer>& f, float* dst) {
+template <int NTH, int LD>
+__device__ __forceinline__ void put_cc(const Frag<C * C / NTH>& f, float* dst) {
 #pragma unroll
-  for (int u = 0; u < kCCPer; ++u) {
-    const int idx = threadIdx.x + u * NT;
-    dst[(idx >> 6) * LC + (idx & 63)] = f.x[u];
+  for (int u = 0; u < C * C / NTH; ++u) {
+    const int idx = threadIdx.x + u * NTH;
+    dst[(idx >> 6) * LD + (idx & 63)] = f.x[u];
   }
 }
 // columns j0 .. j0 + TW - 1 of [C][dv] rows (n valid), zero padded
-__device__ __forceinline__ void fetch_tile(Frag<kTilePer>& f, const float* src, int n, int dv,
+template <int NTH>
+__device__ __forceinline__ void fetch_tile(Frag<C * TW / NTH>& f, const float* src, int n, int dv,
                                            int j0) {
 #pragma unroll
-  for (int u = 0; u < kTilePer; ++u) {
-    const int idx = threadIdx.x + u * NT, t = idx >> 5, j = idx & 31;
+  for (int u = 0; u < C * TW / NTH; ++u) {
+    const int idx = threadIdx.x + u * NTH, t = idx >> 5, j = idx & 31;
     f.x[u] = (t < n && j0 + j < dv) ? src[(size_t)t * dv + j0 + j] : 0.f;
   }
 }
 // rows scaled by rs[t] when given
-__device__ __forceinline__ void put_tile(const Frag<kTilePer>& f, float* dst, const float* rs) {
+template <int NTH, int LD>
+__device__ __forceinline__ void put_tile(const Frag<C * TW / NTH>& f, float* dst, const float* rs) {
 #pragma unroll
-  for (int u = 0; u < kTilePer; ++u) {
-    const int idx = threadIdx.x + u * NT;
-    dst[idx] = rs ? f.x[u] * rs[idx >> 5] : f.x[u];
+  for (int u = 0; u < C * TW / NTH; ++u) {
+    const int idx = threadIdx.x + u * NTH, t = idx >> 5, j = idx & 31;
+    dst[t * LD + j] = rs ? f.x[u] * rs[t] : f.x[u];
   }
 }
 
@@ -187,13 +191,13 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   const size_t tok = (size_t)bh * a.L + (size_t)c * C;
   const bool erase = a.resid != 2;
   {
-    Frag<kRowsPer> fk, fq;
-    fetch_rows(fk, a.k + tok * dk, n, dk);
-    fetch_rows(fq, a.q + tok * dk, n, dk);
+    Frag<C * DP / NT> fk, fq;
+    fetch_rows<NT>(fk, a.k + tok * dk, n, dk);
+    fetch_rows<NT>(fq, a.q + tok * dk, n, dk);
     const Scal sc = fetch_scalars(a, tok, n);
     for (int idx = tid; idx < C * LC; idx += NT) sT[idx] = 0.f;
-    put_rows_t(fk, sKt);
-    put_rows_t(fq, sQt);
+    put_rows_t<NT>(fk, sKt);
+    put_rows_t<NT>(fq, sQt);
     put_scalars(a, sc, sLg, sB, sAl);
   }
   __syncthreads();
@@ -291,141 +295,171 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The two state chains run their products on the fp32 matrix cores: one
+// 16 x 16 block per v_mfma_f32_16x16x4f32 chain. Lane l holds A(m0 + l % 16,
+// k + l / 16) and B(k + l / 16, n0 + l % 16); the block's element
+// (4 (l / 16) + i, l % 16) is accumulator i. Eight wavefronts per workgroup;
+// the 128 x 32 state (or state-gradient) tile stays in registers, two blocks
+// per wavefront, and is mirrored into LDS as an operand. Row strides are 2
+// mod 32 words so that both the row and the column reads of an operand
+// spread over the LDS banks.
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int NTC = 512;      // threads of a chain workgroup
+constexpr int LKC = DP + 2;   // [C][d_k] rows
+constexpr int LCC = C + 2;    // [C][C] rows
+constexpr int LOC = TW + 2;   // [C][TW] and [DP][TW] rows
+
+// acc += sum_{k < K} A(m0 + i, k) B(k, n0 + j), A(m, k) = pa[m am + k ak],
+// B(k, n) = pb[k bk + n bn]; K a multiple of 4
+__device__ __forceinline__ void mfma16(floatx4& acc, const float* pa, int am, int ak,
+                                       const float* pb, int bk, int bn, int m0, int n0, int K) {
+  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+  const float* A = pa + (m0 + r) * am + q * ak;
+  const float* B = pb + q * bk + (n0 + r) * bn;
+#pragma unroll 4
+  for (int k = 0; k < K; k += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[k * ak], B[k * bk], acc, 0, 0, 0);
+}
+
 // forward chain: chunk-start states and residuals for 32 value columns
-__global__ __launch_bounds__(NT) void bwd_fwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float lds[];
-  float* sK = lds;             // [C][LK]
-  float* sT = sK + C * LK;     // [C][LC]
-  float* sS = sT + C * LC;     // [DP][TW] state tile
-  float* sR = sS + DP * TW;    // [C][TW] V - diag(g) K S0
-  float* sE = sR + C * TW;     // [C][TW] diag(Lambda b) E
-  float* sLg = sE + C * TW;
+  float* sK = lds;              // [C][LKC]
+  float* sT = sK + C * LKC;     // [C][LCC]
+  float* sS = sT + C * LCC;     // [DP][LOC] state tile (operand copy)
+  float* sR = sS + DP * LOC;    // [C][LOC] V - diag(g) K S0
+  float* sE = sR + C * LOC;     // [C][LOC] diag(Lambda b) E
+  float* sLg = sE + C * LOC;
   float* sB = sLg + C;
   float* sAl = sB + C;
   const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
-  const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C;
+  const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C, dk4 = (dk + 3) & ~3;
   const bool erase = a.resid != 2;
-  for (int idx = tid; idx < DP * TW; idx += NT) {
-    const int d = idx >> 5, j = idx & 31;
-    sS[idx] = (a.state_in && d < dk && j0 + j < dv) ? a.state_in[((size_t)bh * dk + d) * dv + j0 + j]
-                                                     : 0.f;
-  }
-  const int tm = tid >> 3, tn = tid & 7;  // 64 x 32 outputs: rows 2 tm + i, columns 4 tn + j
-  // the next chunk's inputs, fetched while the current one is computed
-  Frag<kRowsPer> fk;
-  Frag<kCCPer> ft;
-  Frag<kTilePer> fv;
+  const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
+  const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);  // this wavefront's [C][TW] block
+  // state rows 16 w + 4 q + i, columns 16 h + r (h = 0, 1)
+  floatx4 S[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * w + 4 * q + i, j = 16 * h + r;
+      S[h][i] = (a.state_in && d < dk && j0 + j < dv)
+                    ? a.state_in[((size_t)bh * dk + d) * dv + j0 + j]
+                    : 0.f;
+      sS[d * LOC + j] = S[h][i];
+    }
+  Frag<C * DP / NTC> fk;
+  Frag<C * C / NTC> ft;
+  Frag<C * TW / NTC> fv;
   Scal fs;
   auto fetch = [&](int c) {
     const int n = min(C, L - c * C);
     const size_t tok = (size_t)bh * L + (size_t)c * C;
-    fetch_rows(fk, a.k + tok * dk, n, dk);
-    if (erase) fetch_cc(ft, a.Tm + cc_off(bh, nch, c));
-    fetch_tile(fv, a.v + tok * dv, n, dv, j0);
+    fetch_rows<NTC>(fk, a.k + tok * dk, n, dk);
+    if (erase) fetch_cc<NTC>(ft, a.Tm + cc_off(bh, nch, c));
+    fetch_tile<NTC>(fv, a.v + tok * dv, n, dv, j0);
     fs = fetch_scalars(a, tok, n);
   };
   fetch(0);
   for (int c = 0; c < nch; ++c) {
     const int n = min(C, L - c * C);
     __syncthreads();
-    put_rows(fk, sK);
-    if (erase) put_cc(ft, sT);
+    put_rows<NTC, LKC>(fk, sK);
+    if (erase) put_cc<NTC, LCC>(ft, sT);
     put_scalars(a, fs, sLg, sB, sAl);
-    float* s0g = a.S0s + ((size_t)bh * nch + c) * dk * dv;
-    for (int idx = tid; idx < dk * TW; idx += NT) {
-      const int d = idx >> 5, j = idx & 31;
-      if (j0 + j < dv) s0g[(size_t)d * dv + j0 + j] = sS[idx];
+    {
+      float* s0g = a.S0s + ((size_t)bh * nch + c) * dk * dv;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 16 * w + 4 * q + i, col = j0 + 16 * h + r;
+          if (d < dk && col < dv) s0g[(size_t)d * dv + col] = S[h][i];
+        }
     }
     __syncthreads();
-    put_tile(fv, sR, a.resid == 1 ? sAl : nullptr);
+    put_tile<NTC, LOC>(fv, sR, a.resid == 1 ? sAl : nullptr);
     if (c + 1 < nch) fetch(c + 1);
     __syncthreads();
-    float e[2][4] = {};
+    floatx4 e = {0.f, 0.f, 0.f, 0.f};
     if (erase) {
-      float x[2][4] = {};
-      mma<2, 4>(x, sK, LK, 1, sS, TW, 2 * tm, 4 * tn, dk);
+      floatx4 x = {0.f, 0.f, 0.f, 0.f};
+      mfma16(x, sK, LKC, 1, sS, LOC, 1, m0, n0, dk4);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const float g = expf(sLg[2 * tm + i]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sR[(2 * tm + i) * TW + 4 * tn + j] -= g * x[i][j];
+      for (int i = 0; i < 4; ++i) {
+        const int t = m0 + 4 * q + i;
+        sR[t * LOC + n0 + r] -= expf(sLg[t]) * x[i];
       }
       __syncthreads();
-      mma<2, 4>(e, sT, LC, 1, sR, TW, 2 * tm, 4 * tn, C);
+      mfma16(e, sT, LCC, 1, sR, LOC, 1, m0, n0, C);
     } else {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) e[i][j] = sR[(2 * tm + i) * TW + 4 * tn + j];
+      for (int i = 0; i < 4; ++i) e[i] = sR[(m0 + 4 * q + i) * LOC + n0 + r];
     }
     const float lgC = sLg[C - 1];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = 2 * tm + i;
-      const float w = sB[t] * expf(lgC - sLg[t]);
-      float* eg = a.E + ((size_t)bh * nch * C + (size_t)c * C + t) * dv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = j0 + 4 * tn + j;
-        if (t < n && col < dv) eg[col] = e[i][j];
-        sE[t * TW + 4 * tn + j] = e[i][j] * w;
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int t = m0 + 4 * q + i, col = j0 + n0 + r;
+      if (t < n && col < dv) a.E[((size_t)bh * nch * C + (size_t)c * C + t) * dv + col] = e[i];
+      sE[t * LOC + n0 + r] = e[i] * sB[t] * expf(lgC - sLg[t]);
     }
     __syncthreads();
-    {
-      const int um = tid >> 3, un = tid & 7;  // 128 x 32: rows 4 um + i, columns 4 un + j
-      float s[4][4] = {};
-      mma<4, 4>(s, sK, 1, LK, sE, TW, 4 * um, 4 * un, C);
-      const float gC = expf(lgC);
+    const float gC = expf(lgC);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int h = 0; h < 2; ++h) {
+      floatx4 acc = S[h] * gC;
+      mfma16(acc, sK, 1, LKC, sE, LOC, 1, 16 * w, 16 * h, C);
+      S[h] = acc;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int idx = (4 * um + i) * TW + 4 * un + j;
-          sS[idx] = fmaf(gC, sS[idx], s[i][j]);
-        }
+      for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * q + i) * LOC + 16 * h + r] = acc[i];
     }
   }
 }
 
-// ---------------------------------------------------------------------------
 // reverse chain: state gradients at chunk ends, dR (= dV), dS0
-__global__ __launch_bounds__(NT) void bwd_rev_kernel(BwdArgs a) {
+__global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float lds[];
-  float* sK = lds;             // [C][LK]
-  float* sQ = sK + C * LK;     // [C][LK]
-  float* sT = sQ + C * LK;     // [C][LC]
-  float* sP = sT + C * LC;     // [C][LC]
-  float* sG = sP + C * LC;     // [DP][TW] state gradient tile
-  float* sO = sG + DP * TW;    // [C][TW] dO, then diag(g) dO
-  float* sD = sO + C * TW;     // [C][TW] dE
-  float* sX = sD + C * TW;     // [C][TW] diag(g) dR
-  float* sLg = sX + C * TW;
+  float* sK = lds;              // [C][LKC]
+  float* sQ = sK + C * LKC;     // [C][LKC]
+  float* sT = sQ + C * LKC;     // [C][LCC]
+  float* sP = sT + C * LCC;     // [C][LCC]
+  float* sG = sP + C * LCC;     // [DP][LOC] state gradient tile (operand copy)
+  float* sO = sG + DP * LOC;    // [C][LOC] dO, then diag(g) dO
+  float* sD = sO + C * LOC;     // [C][LOC] dE
+  float* sX = sD + C * LOC;     // [C][LOC] -diag(g) dR
+  float* sLg = sX + C * LOC;
   float* sB = sLg + C;
   float* sAl = sB + C;
   const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
-  const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C;
+  const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C, dk4 = (dk + 3) & ~3;
   const bool erase = a.resid != 2;
-  for (int idx = tid; idx < DP * TW; idx += NT) {
-    const int d = idx >> 5, j = idx & 31;
-    sG[idx] = (a.dstate_out && d < dk && j0 + j < dv)
-                  ? a.dstate_out[((size_t)bh * dk + d) * dv + j0 + j]
-                  : 0.f;
-  }
-  const int tm = tid >> 3, tn = tid & 7;
-  const int um = tid >> 3, un = tid & 7;
-  Frag<kRowsPer> fk, fq;
-  Frag<kCCPer> fp, ft;
-  Frag<kTilePer> fo;
+  const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
+  const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
+  floatx4 G[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * w + 4 * q + i, j = 16 * h + r;
+      G[h][i] = (a.dstate_out && d < dk && j0 + j < dv)
+                    ? a.dstate_out[((size_t)bh * dk + d) * dv + j0 + j]
+                    : 0.f;
+      sG[d * LOC + j] = G[h][i];
+    }
+  Frag<C * DP / NTC> fk, fq;
+  Frag<C * C / NTC> fp, ft;
+  Frag<C * TW / NTC> fo;
   Scal fs;
   auto fetch = [&](int c) {
     const int n = min(C, L - c * C);
     const size_t tok = (size_t)bh * L + (size_t)c * C;
-    fetch_rows(fk, a.k + tok * dk, n, dk);
-    fetch_rows(fq, a.q + tok * dk, n, dk);
-    fetch_cc(fp, a.Pm + cc_off(bh, nch, c));
-    if (erase) fetch_cc(ft, a.Tm + cc_off(bh, nch, c));
-    fetch_tile(fo, a.d_o + tok * dv, n, dv, j0);
+    fetch_rows<NTC>(fk, a.k + tok * dk, n, dk);
+    fetch_rows<NTC>(fq, a.q + tok * dk, n, dk);
+    fetch_cc<NTC>(fp, a.Pm + cc_off(bh, nch, c));
+    if (erase) fetch_cc<NTC>(ft, a.Tm + cc_off(bh, nch, c));
+    fetch_tile<NTC>(fo, a.d_o + tok * dv, n, dv, j0);
     fs = fetch_scalars(a, tok, n);
   };
   fetch(nch - 1);
@@ -433,88 +467,76 @@ __global__ __launch_bounds__(NT) void bwd_rev_kernel(BwdArgs a) {
     const int n = min(C, L - c * C);
     const size_t tok = (size_t)bh * L + (size_t)c * C;
     __syncthreads();
-    put_rows(fk, sK);
-    put_rows(fq, sQ);
-    put_cc(fp, sP);
-    if (erase) put_cc(ft, sT);
-    put_tile(fo, sO, nullptr);
+    put_rows<NTC, LKC>(fk, sK);
+    put_rows<NTC, LKC>(fq, sQ);
+    put_cc<NTC, LCC>(fp, sP);
+    if (erase) put_cc<NTC, LCC>(ft, sT);
+    put_tile<NTC, LOC>(fo, sO, nullptr);
     put_scalars(a, fs, sLg, sB, sAl);
     if (c > 0) fetch(c - 1);
-    float* gg = a.Gs + ((size_t)bh * nch + c) * dk * dv;
-    for (int idx = tid; idx < dk * TW; idx += NT) {
-      const int d = idx >> 5, j = idx & 31;
-      if (j0 + j < dv) gg[(size_t)d * dv + j0 + j] = sG[idx];
+    {
+      float* gg = a.Gs + ((size_t)bh * nch + c) * dk * dv;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = 16 * w + 4 * q + i, col = j0 + 16 * h + r;
+          if (d < dk && col < dv) gg[(size_t)d * dv + col] = G[h][i];
+        }
     }
     __syncthreads();
     const float lgC = sLg[C - 1];
-    float r[2][4];
+    // dE = Pm^T dO + diag(Lambda b) K G
+    floatx4 de;
     {
-      float x[2][4] = {}, y[2][4] = {};
-      mma<2, 4>(x, sP, 1, LC, sO, TW, 2 * tm, 4 * tn, C);
-      mma<2, 4>(y, sK, LK, 1, sG, TW, 2 * tm, 4 * tn, dk);
+      floatx4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
+      mfma16(x, sP, 1, LCC, sO, LOC, 1, m0, n0, C);
+      mfma16(y, sK, LKC, 1, sG, LOC, 1, m0, n0, dk4);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int t = 2 * tm + i;
-        const float w = sB[t] * expf(lgC - sLg[t]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          r[i][j] = fmaf(w, y[i][j], x[i][j]);
-          sD[t * TW + 4 * tn + j] = r[i][j];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int t = m0 + 4 * q + i;
+        de[i] = fmaf(sB[t] * expf(lgC - sLg[t]), y[i], x[i]);
+        sD[t * LOC + n0 + r] = de[i];
       }
     }
     __syncthreads();
+    floatx4 dr = de;
     if (erase) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) r[i][j] = 0.f;
-      mma<2, 4>(r, sT, 1, LC, sD, TW, 2 * tm, 4 * tn, C);
+      dr = floatx4{0.f, 0.f, 0.f, 0.f};
+      mfma16(dr, sT, 1, LCC, sD, LOC, 1, m0, n0, C);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int t = 2 * tm + i;
-      const float g = expf(sLg[t]);
-      float* rg = a.dR + ((size_t)bh * nch * C + (size_t)c * C + t) * dv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = j0 + 4 * tn + j;
-        if (t < n && col < dv) {
-          rg[col] = r[i][j];
-          a.dv_out[(tok + t) * dv + col] = a.resid == 1 ? sAl[t] * r[i][j] : r[i][j];
-        }
-        sX[t * TW + 4 * tn + j] = g * r[i][j];
-        sO[t * TW + 4 * tn + j] *= g;
+    for (int i = 0; i < 4; ++i) {
+      const int t = m0 + 4 * q + i, col = j0 + n0 + r;
+      if (t < n && col < dv) {
+        a.dR[((size_t)bh * nch * C + (size_t)c * C + t) * dv + col] = dr[i];
+        a.dv_out[(tok + t) * dv + col] = a.resid == 1 ? sAl[t] * dr[i] : dr[i];
       }
+      const float g = expf(sLg[t]);
+      sX[t * LOC + n0 + r] = -g * dr[i];
+      sO[t * LOC + n0 + r] *= g;
     }
     __syncthreads();
-    {
-      float s1[4][4] = {};
-      mma<4, 4>(s1, sQ, 1, LK, sO, TW, 4 * um, 4 * un, C);
-      if (erase) {
-        float s2[4][4] = {};
-        mma<4, 4>(s2, sK, 1, LK, sX, TW, 4 * um, 4 * un, C);
+    // G <- g_C G + Q^T diag(g) dO - K^T diag(g) dR
+    const float gC = expf(lgC);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+    for (int h = 0; h < 2; ++h) {
+      floatx4 acc = G[h] * gC;
+      mfma16(acc, sQ, 1, LKC, sO, LOC, 1, 16 * w, 16 * h, C);
+      if (erase) mfma16(acc, sK, 1, LKC, sX, LOC, 1, 16 * w, 16 * h, C);
+      G[h] = acc;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s1[i][j] -= s2[i][j];
-      }
-      const float gC = expf(lgC);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int idx = (4 * um + i) * TW + 4 * un + j;
-          sG[idx] = fmaf(gC, sG[idx], s1[i][j]);
-        }
+      for (int i = 0; i < 4; ++i) sG[(16 * w + 4 * q + i) * LOC + 16 * h + r] = acc[i];
     }
   }
-  __syncthreads();
   if (a.dstate_in) {
-    for (int idx = tid; idx < dk * TW; idx += NT) {
-      const int d = idx >> 5, j = idx & 31;
-      if (j0 + j < dv) a.dstate_in[((size_t)bh * dk + d) * dv + j0 + j] = sG[idx];
-    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = 16 * w + 4 * q + i, col = j0 + 16 * h + r;
+        if (d < dk && col < dv) a.dstate_in[((size_t)bh * dk + d) * dv + col] = G[h][i];
+      }
   }
 }
 
@@ -542,10 +564,10 @@ __global__ __launch_bounds__(NT) void bwd_contract_kernel(BwdArgs a) {
   float p[4][4] = {};
   float gs = 0.f;
   for (int jb = 0; jb < dv; jb += TW) {
-    Frag<kTilePer> fl, fe;
+    Frag<C * TW / NT> fl, fe;
     Frag<DP * TW / NT> fr, fs0;
-    fetch_tile(fl, left, n, dv, jb);
-    if (part < 2) fetch_tile(fe, Ec, n, dv, jb);
+    fetch_tile<NT>(fl, left, n, dv, jb);
+    if (part < 2) fetch_tile<NT>(fe, Ec, n, dv, jb);
 #pragma unroll
     for (int u = 0; u < DP * TW / NT; ++u) {
       const int idx = tid + u * NT, d = idx >> 5, j = idx & 31;
@@ -555,7 +577,7 @@ __global__ __launch_bounds__(NT) void bwd_contract_kernel(BwdArgs a) {
     }
     __syncthreads();
 #pragma unroll
-    for (int u = 0; u < kTilePer; ++u) {
+    for (int u = 0; u < C * TW / NT; ++u) {
       const int idx = tid + u * NT, t = idx >> 5, j = idx & 31;
       sA[t * LA + j] = fl.x[u];
       if (part < 2) sEt[j * LT + t] = fe.x[u];
@@ -624,25 +646,25 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
   const size_t row0 = (size_t)bh * nch * C + (size_t)c * C;
   const bool erase = a.resid != 2, plain = a.resid == 1;
   {
-    Frag<kRowsPer> fq, fk;
-    fetch_rows(fq, a.q + tok * dk, n, dk);
-    fetch_rows(fk, a.k + tok * dk, n, dk);
+    Frag<C * DP / NT> fq, fk;
+    fetch_rows<NT>(fq, a.q + tok * dk, n, dk);
+    fetch_rows<NT>(fk, a.k + tok * dk, n, dk);
     const Scal sc = fetch_scalars(a, tok, n);
-    put_rows(fq, sQ);
-    put_rows(fk, sK);
+    put_rows<NT, LK>(fq, sQ);
+    put_rows<NT, LK>(fk, sK);
     put_scalars(a, sc, sLg, sB, sAl);
   }
   const size_t o = cc_off(bh, nch, c);
-  Frag<kCCPer> fP, fA, fdP, fdA;
-  fetch_cc(fP, a.Pm + o);
-  fetch_cc(fdP, a.dPm + o);
+  Frag<C * C / NT> fP, fA, fdP, fdA;
+  fetch_cc<NT>(fP, a.Pm + o);
+  fetch_cc<NT>(fdP, a.dPm + o);
   if (erase) {
-    fetch_cc(fA, a.Am + o);
-    fetch_cc(fdA, a.dA + o);
+    fetch_cc<NT>(fA, a.Am + o);
+    fetch_cc<NT>(fdA, a.dA + o);
   }
   __syncthreads();
 #pragma unroll
-  for (int u = 0; u < kCCPer; ++u) {
+  for (int u = 0; u < C * C / NT; ++u) {
     const int idx = tid + u * NT, t = idx >> 6, s = idx & 63;
     const bool lo = s <= t, st = erase && s < t;
     const float D = lo ? expf(sLg[t] - sLg[s]) : 0.f;
@@ -794,11 +816,11 @@ BwdPlan plan_bwd(int BH, int L, int dk, int dv) {
 }
 
 template <typename K>
-hipError_t launch_lds(K kern, dim3 grid, size_t lds, const BwdArgs& a, hipStream_t s) {
+hipError_t launch_lds(K kern, dim3 grid, int threads, size_t lds, const BwdArgs& a, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(NT), lds, s, a);
+  hipLaunchKernelGGL(kern, grid, dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -818,19 +840,19 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
   const int nch = (a.L + C - 1) / C, ntw = (a.dv + TW - 1) / TW;
   const size_t f = sizeof(float);
   hipError_t e;
-  e = launch_lds(bwd_prep_kernel, dim3(a.BH, nch),
+  e = launch_lds(bwd_prep_kernel, dim3(a.BH, nch), NT,
                  (2 * DP * LT + 2 * C * LC + 32 * 33 + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
-  e = launch_lds(bwd_fwd_kernel, dim3(a.BH, ntw),
-                 (C * LK + C * LC + DP * TW + 2 * C * TW + 3 * C) * f, a, s);
+  e = launch_lds(bwd_fwd_kernel, dim3(a.BH, ntw), NTC,
+                 (C * LKC + C * LCC + DP * LOC + 2 * C * LOC + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
-  e = launch_lds(bwd_rev_kernel, dim3(a.BH, ntw),
-                 (2 * C * LK + 2 * C * LC + DP * TW + 3 * C * TW + 3 * C) * f, a, s);
+  e = launch_lds(bwd_rev_kernel, dim3(a.BH, ntw), NTC,
+                 (2 * C * LKC + 2 * C * LCC + DP * LOC + 3 * C * LOC + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
-  e = launch_lds(bwd_contract_kernel, dim3(a.BH, nch, 3),
+  e = launch_lds(bwd_contract_kernel, dim3(a.BH, nch, 3), NT,
                  (C * (TW + 1) + 64 + TW * LK + TW * LT + NT / 64) * f, a, s);
   if (e != hipSuccess) return e;
-  return launch_lds(bwd_grad_kernel, dim3(a.BH, nch),
+  return launch_lds(bwd_grad_kernel, dim3(a.BH, nch), NT,
                     (2 * C * LK + 5 * C * LC + 3 * C + 5 * C) * f, a, s);
 }
 
