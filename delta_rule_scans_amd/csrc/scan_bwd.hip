@@ -42,34 +42,8 @@ constexpr int NT = 256;
 constexpr int C = 64;       // tokens per chunk (one wavefront of scalars)
 constexpr int TW = 32;      // value columns per chain workgroup
 constexpr int DP = 128;     // d_k, padded
-constexpr int LK = DP + 4;  // row stride of [C][d_k] arrays
 constexpr int LC = C + 1;   // row stride of [C][C] arrays
-constexpr int LT = C + 4;   // row stride of transposed [d][C] arrays
 
-// acc[i][j] += sum_{k < K} A(m0 + i, k) B(k, n0 + j), A(m, k) = pa[m am + k ak],
-// B(k, n) = pb[k ldb + n] (rows 16-byte aligned, n0 a multiple of 4).
-template <int TM, int TN>
-__device__ __forceinline__ void mma(float (&acc)[TM][TN], const float* pa, int am, int ak,
-                                    const float* pb, int ldb, int m0, int n0, int K) {
-#pragma unroll 4
-  for (int k = 0; k < K; ++k) {
-    float av[TM], bv[TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) av[i] = pa[(m0 + i) * am + k * ak];
-#pragma unroll
-    for (int j = 0; j < TN; j += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(pb + k * ldb + n0 + j);
-      bv[j] = x.x;
-      bv[j + 1] = x.y;
-      bv[j + 2] = x.z;
-      bv[j + 3] = x.w;
-    }
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
-  }
-}
 
 // Loads are split in two: fetch into registers (every load of a chunk in
 // flight at once, or during the previous chunk's products), then put into LDS.
@@ -93,15 +67,6 @@ __device__ __forceinline__ void put_rows(const Frag<C * DP / NTH>& f, float* dst
   for (int u = 0; u < C * DP / NTH; ++u) {
     const int idx = threadIdx.x + u * NTH;
     dst[(idx >> 7) * LD + (idx & (DP - 1))] = f.x[u];
-  }
-}
-// transposed: dst[i][t] with row stride LT
-template <int NTH>
-__device__ __forceinline__ void put_rows_t(const Frag<C * DP / NTH>& f, float* dst) {
-#pragma unroll
-  for (int u = 0; u < C * DP / NTH; ++u) {
-    const int idx = threadIdx.x + u * NTH;
-    dst[(idx & (DP - 1)) * LT + (idx >> 7)] = f.x[u];
   }
 }
 // a row-major [C][C] matrix
@@ -170,6 +135,55 @@ __device__ void put_scalars(const BwdArgs& a, Scal f, float* sLg, float* sB, flo
 }
 
 
+// ---------------------------------------------------------------------------
+// Every product runs on the fp32 matrix cores in 16 x 16 blocks of
+// v_mfma_f32_16x16x4f32: lane l holds A(m0 + l % 16, k + l / 16) and
+// B(k + l / 16, n0 + l % 16); the block's element (4 (l / 16) + i, l % 16) is
+// accumulator i. LDS row strides are chosen per access pattern so that the 32
+// lanes of a read fall on distinct banks (2 mod 32 words for rows read along
+// the contraction, 16 for rows read across it, 18 for both).
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int NTC = 512;      // threads of a chain workgroup
+constexpr int LKC = DP + 2;   // [C][d_k] rows
+constexpr int LCC = C + 2;    // [C][C] rows
+constexpr int LOC = TW + 2;   // [C][TW] and [DP][TW] rows
+
+// acc += sum_{k < K} A(m0 + i, k) B(k, n0 + j), A(m, k) = pa[m am + k ak],
+// B(k, n) = pb[k bk + n bn]; K a multiple of 4
+__device__ __forceinline__ void mfma16(floatx4& acc, const float* pa, int am, int ak,
+                                       const float* pb, int bk, int bn, int m0, int n0, int K) {
+  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+  const float* A = pa + (m0 + r) * am + q * ak;
+  const float* B = pb + q * bk + (n0 + r) * bn;
+#pragma unroll 4
+  for (int k = 0; k < K; k += 4)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[k * ak], B[k * bk], acc, 0, 0, 0);
+}
+
+// A row of blocks (m0, 16 b), b < NB, sharing the A operand: acc[b] +=
+// sum_{k < K} A(m0 + i, k) B(k, 16 b + j), A(m, k) = pa[m am + k ak] (times
+// as[k] when given), B(k, n) = pb[k bk + n bn].
+template <int NB>
+__device__ __forceinline__ void mfma_row(floatx4 (&acc)[NB], const float* pa, int am, int ak,
+                                         const float* as, const float* pb, int bk, int bn, int m0,
+                                         int K) {
+  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+  const float* A = pa + (m0 + r) * am + q * ak;
+  const float* B = pb + q * bk + r * bn;
+#pragma unroll 2
+  for (int k = 0; k < K; k += 4) {
+    float av = A[k * ak];
+    if (as) av *= as[k + q];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, B[k * bk + 16 * b * bn], acc[b], 0, 0, 0);
+  }
+}
+
+// Chain kernels: eight wavefronts; the 128 x 32 state (or state-gradient) tile
+// stays in registers, two blocks per wavefront, mirrored into LDS as an operand.
+
 __device__ __forceinline__ size_t cc_off(int bh, int nch, int c) {
   return ((size_t)bh * nch + c) * C * C;
 }
@@ -178,16 +192,17 @@ __device__ __forceinline__ size_t cc_off(int bh, int nch, int c) {
 // prep: A, Pm, T of one chunk
 __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float lds[];
-  float* sKt = lds;               // [DP][LT] keys, transposed
-  float* sQt = sKt + DP * LT;     // [DP][LT] queries, transposed
-  float* sA = sQt + DP * LT;      // [C][LC]
+  constexpr int LP = DP + 2;
+  float* sK = lds;                // [C][LP]
+  float* sQ = sK + C * LP;        // [C][LP]
+  float* sA = sQ + C * LP;        // [C][LC]
   float* sT = sA + C * LC;        // [C][LC]
   float* sY = sT + C * LC;        // [32][33]
   float* sLg = sY + 32 * 33;
   float* sB = sLg + C;
   float* sAl = sB + C;
   const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, nch = gridDim.y;
-  const int n = min(C, a.L - c * C), dk = a.dk;
+  const int n = min(C, a.L - c * C), dk = a.dk, dk4 = (dk + 3) & ~3;
   const size_t tok = (size_t)bh * a.L + (size_t)c * C;
   const bool erase = a.resid != 2;
   {
@@ -196,40 +211,27 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
     fetch_rows<NT>(fq, a.q + tok * dk, n, dk);
     const Scal sc = fetch_scalars(a, tok, n);
     for (int idx = tid; idx < C * LC; idx += NT) sT[idx] = 0.f;
-    put_rows_t<NT>(fk, sKt);
-    put_rows_t<NT>(fq, sQt);
+    put_rows<NT, LP>(fk, sK);
+    put_rows<NT, LP>(fq, sQ);
     put_scalars(a, sc, sLg, sB, sAl);
   }
   __syncthreads();
-  const int tm = tid >> 4, tn = tid & 15;
-  float kk[4][4] = {}, qk[4][4] = {};
-  for (int d = 0; d < dk; ++d) {
-    const float4 b4 = *reinterpret_cast<const float4*>(sKt + d * LT + 4 * tn);
-    const float4 k4 = *reinterpret_cast<const float4*>(sKt + d * LT + 4 * tm);
-    const float4 q4 = *reinterpret_cast<const float4*>(sQt + d * LT + 4 * tm);
-    const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
-    const float kv[4] = {k4.x, k4.y, k4.z, k4.w};
-    const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kk[i][j] = fmaf(kv[i], bv[j], kk[i][j]);
-        qk[i][j] = fmaf(qv[i], bv[j], qk[i][j]);
-      }
-  }
+  const int w = tid >> 6, r = tid & 15, q = (tid & 63) >> 4;
+  floatx4 kk[4] = {}, qk[4] = {};
+  mfma_row<4>(kk, sK, LP, 1, nullptr, sK, 1, LP, 16 * w, dk4);
+  mfma_row<4>(qk, sQ, LP, 1, nullptr, sK, 1, LP, 16 * w, dk4);
   float* Ag = a.Am + cc_off(bh, nch, c);
   float* Pg = a.Pm + cc_off(bh, nch, c);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 4 * tm + i, l = 4 * tn + j;
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * w + 4 * q + i, l = 16 * b + r;
       const float f = l <= t ? sB[l] * expf(sLg[t] - sLg[l]) : 0.f;
-      const float av = (erase && l < t) ? kk[i][j] * f : 0.f;
+      const float av = (erase && l < t) ? kk[b][i] * f : 0.f;
       sA[t * LC + l] = av;
       Ag[t * C + l] = av;
-      Pg[t * C + l] = qk[i][j] * f;
+      Pg[t * C + l] = qk[b][i] * f;
     }
   __syncthreads();
   // diagonal 16 x 16 blocks by substitution, one column per thread
@@ -292,34 +294,6 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   __syncthreads();
   float* Tg = a.Tm + cc_off(bh, nch, c);
   for (int idx = tid; idx < C * C; idx += NT) Tg[idx] = sT[(idx >> 6) * LC + (idx & 63)];
-}
-
-// ---------------------------------------------------------------------------
-// The two state chains run their products on the fp32 matrix cores: one
-// 16 x 16 block per v_mfma_f32_16x16x4f32 chain. Lane l holds A(m0 + l % 16,
-// k + l / 16) and B(k + l / 16, n0 + l % 16); the block's element
-// (4 (l / 16) + i, l % 16) is accumulator i. Eight wavefronts per workgroup;
-// the 128 x 32 state (or state-gradient) tile stays in registers, two blocks
-// per wavefront, and is mirrored into LDS as an operand. Row strides are 2
-// mod 32 words so that both the row and the column reads of an operand
-// spread over the LDS banks.
-typedef float floatx4 __attribute__((ext_vector_type(4)));
-
-constexpr int NTC = 512;      // threads of a chain workgroup
-constexpr int LKC = DP + 2;   // [C][d_k] rows
-constexpr int LCC = C + 2;    // [C][C] rows
-constexpr int LOC = TW + 2;   // [C][TW] and [DP][TW] rows
-
-// acc += sum_{k < K} A(m0 + i, k) B(k, n0 + j), A(m, k) = pa[m am + k ak],
-// B(k, n) = pb[k bk + n bn]; K a multiple of 4
-__device__ __forceinline__ void mfma16(floatx4& acc, const float* pa, int am, int ak,
-                                       const float* pb, int bk, int bn, int m0, int n0, int K) {
-  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
-  const float* A = pa + (m0 + r) * am + q * ak;
-  const float* B = pb + q * bk + (n0 + r) * bn;
-#pragma unroll 4
-  for (int k = 0; k < K; k += 4)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[k * ak], B[k * bk], acc, 0, 0, 0);
 }
 
 // forward chain: chunk-start states and residuals for 32 value columns
@@ -542,14 +516,15 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // contractions over the value columns; part 0: dO S0^T, dO E^T; part 1:
-// dR S0^T, dR E^T; part 2: E G^T, <G, S0>
+// dR S0^T, dR E^T; part 2: E G^T, <G, S0>. Wavefront w takes rows 16 w ..
+// 16 w + 15 of both products; the value columns stream through LDS 32 at a time.
 __global__ __launch_bounds__(NT) void bwd_contract_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float lds[];
-  constexpr int LA = TW + 1;
-  float* sA = lds;               // [C][LA] left operand block
-  float* sBt = sA + C * LA + 64; // [TW][LK] S0^T or G^T block (offset keeps 16-byte alignment)
-  float* sEt = sBt + TW * LK;    // [TW][LT] E^T block
-  float* sRed = sEt + TW * LT;   // [NT / 64]
+  constexpr int LJ = TW + 2;
+  float* sL = lds;               // [C][LJ] left operand block
+  float* sR = sL + C * LJ;       // [DP][LJ] S0 or G block
+  float* sE = sR + DP * LJ;      // [C][LJ] E block
+  float* sRed = sE + C * LJ;     // [NT / 64]
   const int bh = blockIdx.x, c = blockIdx.y, part = blockIdx.z, tid = threadIdx.x;
   const int nch = gridDim.y, L = a.L, dk = a.dk, dv = a.dv;
   const int n = min(C, L - c * C);
@@ -559,9 +534,8 @@ __global__ __launch_bounds__(NT) void bwd_contract_kernel(BwdArgs a) {
   const float* S0c = a.S0s + ((size_t)bh * nch + c) * dk * dv;
   const float* right = part == 2 ? a.Gs + ((size_t)bh * nch + c) * dk * dv : S0c;
   const float* Ec = a.E + row0 * dv;
-  const int tm = tid >> 4, tn = tid & 15;
-  float m[4][8] = {};
-  float p[4][4] = {};
+  const int w = tid >> 6, r = tid & 15, q = (tid & 63) >> 4;
+  floatx4 m[8] = {}, p[4] = {};
   float gs = 0.f;
   for (int jb = 0; jb < dv; jb += TW) {
     Frag<C * TW / NT> fl, fe;
@@ -576,37 +550,33 @@ __global__ __launch_bounds__(NT) void bwd_contract_kernel(BwdArgs a) {
       fs0.x[u] = (ok && part == 2) ? S0c[(size_t)d * dv + jb + j] : 0.f;
     }
     __syncthreads();
-#pragma unroll
-    for (int u = 0; u < C * TW / NT; ++u) {
-      const int idx = tid + u * NT, t = idx >> 5, j = idx & 31;
-      sA[t * LA + j] = fl.x[u];
-      if (part < 2) sEt[j * LT + t] = fe.x[u];
-    }
+    put_tile<NT, LJ>(fl, sL, nullptr);
+    if (part < 2) put_tile<NT, LJ>(fe, sE, nullptr);
 #pragma unroll
     for (int u = 0; u < DP * TW / NT; ++u) {
       const int idx = tid + u * NT, d = idx >> 5, j = idx & 31;
-      sBt[j * LK + d] = fr.x[u];
+      sR[d * LJ + j] = fr.x[u];
       gs = fmaf(fr.x[u], fs0.x[u], gs);
     }
     __syncthreads();
-    const int K = min(TW, dv - jb);
-    mma<4, 8>(m, sA, LA, 1, sBt, LK, 4 * tm, 8 * tn, K);
-    if (part < 2) mma<4, 4>(p, sA, LA, 1, sEt, LT, 4 * tm, 4 * tn, K);
+    const int K4 = (min(TW, dv - jb) + 3) & ~3;
+    mfma_row<8>(m, sL, LJ, 1, nullptr, sR, 1, LJ, 16 * w, K4);
+    if (part < 2) mfma_row<4>(p, sL, LJ, 1, nullptr, sE, 1, LJ, 16 * w, K4);
   }
   float* M = (part == 0 ? a.M1 : part == 1 ? a.M2 : a.M3) + row0 * dk;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int b = 0; b < 8; ++b)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = 8 * tn + j;
-      if (d < dk) M[(size_t)(4 * tm + i) * dk + d] = m[i][j];
+    for (int i = 0; i < 4; ++i) {
+      const int d = 16 * b + r;
+      if (d < dk) M[(size_t)(16 * w + 4 * q + i) * dk + d] = m[b][i];
     }
   if (part < 2) {
     float* P = (part == 0 ? a.dPm : a.dA) + cc_off(bh, nch, c);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) P[(4 * tm + i) * C + 4 * tn + j] = p[i][j];
+      for (int i = 0; i < 4; ++i) P[(16 * w + 4 * q + i) * C + 16 * b + r] = p[b][i];
   } else {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) gs += __shfl_xor(gs, off, 64);
@@ -625,20 +595,21 @@ __device__ __forceinline__ float sum16(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// per-token gradients of one chunk
+// per-token gradients of one chunk; wavefront w takes tokens 16 w .. 16 w + 15
+// of the [C][d_k] products
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float lds[];
-  float* sQ = lds;               // [C][LK]
-  float* sK = sQ + C * LK;       // [C][LK]
-  float* sXp = sK + C * LK;      // [C][LC]
-  float* sXa = sXp + C * LC;     // [C][LC]
-  float* sXpb = sXa + C * LC;    // [C][LC] Xp diag(b)
-  float* sXab = sXpb + C * LC;   // [C][LC] Xa diag(b)
-  float* sW = sXab + C * LC;     // [C][LC] dPm * Pm + dA * A
-  float* sLg = sW + C * LC;
+  constexpr int LQ = DP + 16;  // read across rows only
+  constexpr int LX = C + 18;   // read along and across rows
+  float* sQ = lds;               // [C][LQ]
+  float* sK = sQ + C * LQ;       // [C][LQ]
+  float* sXp = sK + C * LQ;      // [C][LX] lower_incl(dO E^T) * D
+  float* sXa = sXp + C * LX;     // [C][LX] dA * D
+  float* sLg = sXa + C * LX;
   float* sB = sLg + C;
   float* sAl = sB + C;
-  float* sRow = sAl + C;         // [5][C]
+  float* sRow = sAl + C;         // [6][C] per-token sums
+  float* sCs = sRow + 6 * C;     // [NT / 64][C] partial column sums
   const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, nch = gridDim.y;
   const int L = a.L, dk = a.dk, dv = a.dv;
   const int n = min(C, L - c * C);
@@ -650,8 +621,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     fetch_rows<NT>(fq, a.q + tok * dk, n, dk);
     fetch_rows<NT>(fk, a.k + tok * dk, n, dk);
     const Scal sc = fetch_scalars(a, tok, n);
-    put_rows<NT, LK>(fq, sQ);
-    put_rows<NT, LK>(fk, sK);
+    put_rows<NT, LQ>(fq, sQ);
+    put_rows<NT, LQ>(fk, sK);
     put_scalars(a, sc, sLg, sB, sAl);
   }
   const size_t o = cc_off(bh, nch, c);
@@ -663,81 +634,84 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     fetch_cc<NT>(fdA, a.dA + o);
   }
   __syncthreads();
+  // Xp, Xa, and the row and column sums of W = dPm * Pm + dA * A (lane = s)
+  {
+    const int s = tid & 63;
+    float cs = 0.f;
 #pragma unroll
-  for (int u = 0; u < C * C / NT; ++u) {
-    const int idx = tid + u * NT, t = idx >> 6, s = idx & 63;
-    const bool lo = s <= t, st = erase && s < t;
-    const float D = lo ? expf(sLg[t] - sLg[s]) : 0.f;
-    const float dp = lo ? fdP.x[u] : 0.f;
-    const float da = st ? -fdA.x[u] : 0.f;
-    const float xp = dp * D, xa = da * D;
-    sXp[t * LC + s] = xp;
-    sXa[t * LC + s] = xa;
-    sXpb[t * LC + s] = xp * sB[s];
-    sXab[t * LC + s] = xa * sB[s];
-    sW[t * LC + s] = dp * (lo ? fP.x[u] : 0.f) + (st ? da * fA.x[u] : 0.f);
+    for (int u = 0; u < C * C / NT; ++u) {
+      const int t = (tid >> 6) + u * (NT / 64);
+      const bool lo = s <= t, st = erase && s < t;
+      const float D = lo ? expf(sLg[t] - sLg[s]) : 0.f;
+      const float dp = lo ? fdP.x[u] : 0.f;
+      const float da = st ? -fdA.x[u] : 0.f;
+      sXp[t * LX + s] = dp * D;
+      sXa[t * LX + s] = da * D;
+      const float wv = dp * (lo ? fP.x[u] : 0.f) + (st ? da * fA.x[u] : 0.f);
+      cs += wv;
+      float rs = wv;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) rs += __shfl_xor(rs, off, 64);
+      if (s == 0) sRow[5 * C + t] = rs;
+    }
+    sCs[(tid >> 6) * C + s] = cs;
   }
   __syncthreads();
-  const int tm = tid >> 4, tn = tid & 15;  // 64 x 128: rows 4 tm + i, columns 8 tn + j
+  const int w = tid >> 6, r = tid & 15, q = (tid & 63) >> 4;
   const float lgC = sLg[C - 1];
-  float pq[4], kr[4], wv[4], dbv[4], vv[4];
-  {  // dQ = diag(g) dO S0^T + Xp B
-    float acc[4][8] = {};
-    mma<4, 8>(acc, sXpb, LC, 1, sK, LK, 4 * tm, 8 * tn, C);
+  float pq[4] = {}, kr[4] = {}, wv[4] = {}, dbv[4] = {}, vv[4] = {};
+  {  // dQ = diag(g) dO S0^T + Xp diag(b) K
+    floatx4 acc[8] = {};
+    mfma_row<8>(acc, sXp, LX, 1, sB, sK, LQ, 1, 16 * w, C);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 4 * tm + i;
+      const int t = 16 * w + 4 * q + i;
       const float g = expf(sLg[t]);
       const float* m1 = a.M1 + (row0 + t) * dk;
-      float s = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = 8 * tn + j;
+      for (int b = 0; b < 8; ++b) {
+        const int d = 16 * b + r;
         const float x = d < dk ? m1[d] : 0.f;
-        s = fmaf(x, sQ[t * LK + d], s);
-        if (t < n && d < dk) a.dq[(tok + t) * dk + d] = fmaf(g, x, acc[i][j]);
+        pq[i] = fmaf(x, sQ[t * LQ + d], pq[i]);
+        if (t < n && d < dk) a.dq[(tok + t) * dk + d] = fmaf(g, x, acc[b][i]);
       }
-      pq[i] = g * s;
+      pq[i] *= g;
     }
   }
-  {  // dB = Xp^T Q + Xa^T K + diag(Lambda) E G^T;  dK = Xa B - diag(g) dR S0^T + diag(b) dB
-    float db[4][8] = {};
-    mma<4, 8>(db, sXp, 1, LC, sQ, LK, 4 * tm, 8 * tn, C);
-    if (erase) mma<4, 8>(db, sXa, 1, LC, sK, LK, 4 * tm, 8 * tn, C);
-    float dkk[4][8] = {};
-    if (erase) mma<4, 8>(dkk, sXab, LC, 1, sK, LK, 4 * tm, 8 * tn, C);
+  {  // dB = Xp^T Q + Xa^T K + diag(Lambda) E G^T;  dK = Xa diag(b) K - diag(g) dR S0^T + diag(b) dB
+    floatx4 db[8] = {}, dkk[8] = {};
+    mfma_row<8>(db, sXp, 1, LX, nullptr, sQ, LQ, 1, 16 * w, C);
+    if (erase) {
+      mfma_row<8>(db, sXa, 1, LX, nullptr, sK, LQ, 1, 16 * w, C);
+      mfma_row<8>(dkk, sXa, LX, 1, sB, sK, LQ, 1, 16 * w, C);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 4 * tm + i;
+      const int t = 16 * w + 4 * q + i;
       const float lam = expf(lgC - sLg[t]), g = expf(sLg[t]), b = sB[t];
       const float* m3 = a.M3 + (row0 + t) * dk;
       const float* m2 = a.M2 + (row0 + t) * dk;
-      float w = 0.f, sb = 0.f, sr = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = 8 * tn + j;
-        const float kv = sK[t * LK + d];
+      for (int bb = 0; bb < 8; ++bb) {
+        const int d = 16 * bb + r;
+        const float kv = sK[t * LQ + d];
         const float x3 = d < dk ? m3[d] : 0.f;
         const float x2 = (erase && d < dk) ? m2[d] : 0.f;
-        w = fmaf(kv, x3, w);
-        const float dbb = fmaf(lam, x3, db[i][j]);
-        sb = fmaf(dbb, kv, sb);
+        wv[i] = fmaf(kv, x3, wv[i]);
+        const float dbb = fmaf(lam, x3, db[bb][i]);
+        dbv[i] = fmaf(dbb, kv, dbv[i]);
         const float dkr = -g * x2;
-        sr = fmaf(dkr, kv, sr);
-        if (t < n && d < dk) a.dk_out[(tok + t) * dk + d] = fmaf(b, dbb, dkk[i][j] + dkr);
+        kr[i] = fmaf(dkr, kv, kr[i]);
+        if (t < n && d < dk) a.dk_out[(tok + t) * dk + d] = fmaf(b, dbb, dkk[bb][i] + dkr);
       }
-      wv[i] = lam * b * w;
-      dbv[i] = sb;
-      kr[i] = sr;
-      float s = 0.f;
+      wv[i] *= lam * b;
       if (plain && t < n) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = 8 * tn + j;
-          if (col < dv) s = fmaf(a.dR[(row0 + t) * dv + col], a.v[(tok + t) * dv + col], s);
+        for (int bb = 0; bb < 8; ++bb) {
+          const int col = 16 * bb + r;
+          if (col < dv) vv[i] = fmaf(a.dR[(row0 + t) * dv + col], a.v[(tok + t) * dv + col], vv[i]);
         }
       }
-      vv[i] = s;
     }
   }
 #pragma unroll
@@ -747,8 +721,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     wv[i] = sum16(wv[i]);
     dbv[i] = sum16(dbv[i]);
     vv[i] = sum16(vv[i]);
-    if (tn == 0) {
-      const int t = 4 * tm + i;
+    if (r == 0) {
+      const int t = 16 * w + 4 * q + i;
       sRow[t] = pq[i];
       sRow[C + t] = kr[i];
       sRow[2 * C + t] = wv[i];
@@ -759,14 +733,12 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
   __syncthreads();
   if (tid < C) {
     const int t = tid;
-    float rs = 0.f, cs = 0.f;
-    for (int s = 0; s < C; ++s) {
-      rs += sW[t * LC + s];
-      cs += sW[s * LC + t];
-    }
-    const float w = sRow[2 * C + t];
-    float dl = (rs - cs) + sRow[t] + sRow[C + t] - w;
-    float wsum = w;
+    float cs = 0.f;
+#pragma unroll
+    for (int p = 0; p < NT / 64; ++p) cs += sCs[p * C + t];
+    const float w_t = sRow[2 * C + t];
+    float dl = (sRow[5 * C + t] - cs) + sRow[t] + sRow[C + t] - w_t;
+    float wsum = w_t;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off, 64);
     if (t == n - 1) dl += expf(lgC) * a.gs0[(size_t)bh * nch + c] + wsum;
@@ -841,7 +813,7 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
   const size_t f = sizeof(float);
   hipError_t e;
   e = launch_lds(bwd_prep_kernel, dim3(a.BH, nch), NT,
-                 (2 * DP * LT + 2 * C * LC + 32 * 33 + 3 * C) * f, a, s);
+                 (2 * C * (DP + 2) + 2 * C * LC + 32 * 33 + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
   e = launch_lds(bwd_fwd_kernel, dim3(a.BH, ntw), NTC,
                  (C * LKC + C * LCC + DP * LOC + 2 * C * LOC + 3 * C) * f, a, s);
@@ -850,10 +822,11 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
                  (2 * C * LKC + 2 * C * LCC + DP * LOC + 3 * C * LOC + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
   e = launch_lds(bwd_contract_kernel, dim3(a.BH, nch, 3), NT,
-                 (C * (TW + 1) + 64 + TW * LK + TW * LT + NT / 64) * f, a, s);
+                 (2 * C * (TW + 2) + DP * (TW + 2) + NT / 64) * f, a, s);
   if (e != hipSuccess) return e;
   return launch_lds(bwd_grad_kernel, dim3(a.BH, nch), NT,
-                    (2 * C * LK + 5 * C * LC + 3 * C + 5 * C) * f, a, s);
+                    (2 * C * (DP + 16) + 2 * C * (C + 18) + 3 * C + 6 * C + (NT / 64) * C) * f,
+                    a, s);
 }
 
 }  // namespace kdn
