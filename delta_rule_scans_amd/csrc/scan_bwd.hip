@@ -83,22 +83,22 @@ __device__ __forceinline__ void put_cc(const Frag<C * C / NTH>& f, float* dst) {
     dst[(idx >> 6) * LD + (idx & 63)] = f.x[u];
   }
 }
-// columns j0 .. j0 + TW - 1 of [C][dv] rows (n valid), zero padded
-template <int NTH>
-__device__ __forceinline__ void fetch_tile(Frag<C * TW / NTH>& f, const float* src, int n, int dv,
+// columns j0 .. j0 + W - 1 of [C][dv] rows (n valid), zero padded
+template <int NTH, int W = TW>
+__device__ __forceinline__ void fetch_tile(Frag<C * W / NTH>& f, const float* src, int n, int dv,
                                            int j0) {
 #pragma unroll
-  for (int u = 0; u < C * TW / NTH; ++u) {
-    const int idx = threadIdx.x + u * NTH, t = idx >> 5, j = idx & 31;
+  for (int u = 0; u < C * W / NTH; ++u) {
+    const int idx = threadIdx.x + u * NTH, t = idx / W, j = idx % W;
     f.x[u] = (t < n && j0 + j < dv) ? src[(size_t)t * dv + j0 + j] : 0.f;
   }
 }
 // rows scaled by rs[t] when given
-template <int NTH, int LD>
-__device__ __forceinline__ void put_tile(const Frag<C * TW / NTH>& f, float* dst, const float* rs) {
+template <int NTH, int LD, int W = TW>
+__device__ __forceinline__ void put_tile(const Frag<C * W / NTH>& f, float* dst, const float* rs) {
 #pragma unroll
-  for (int u = 0; u < C * TW / NTH; ++u) {
-    const int idx = threadIdx.x + u * NTH, t = idx >> 5, j = idx & 31;
+  for (int u = 0; u < C * W / NTH; ++u) {
+    const int idx = threadIdx.x + u * NTH, t = idx / W, j = idx % W;
     dst[t * LD + j] = rs ? f.x[u] * rs[t] : f.x[u];
   }
 }
@@ -137,52 +137,56 @@ __device__ void put_scalars(const BwdArgs& a, Scal f, float* sLg, float* sB, flo
 
 // ---------------------------------------------------------------------------
 // Every product runs on the fp32 matrix cores in 16 x 16 blocks of
-// v_mfma_f32_16x16x4f32: lane l holds A(m0 + l % 16, k + l / 16) and
-// B(k + l / 16, n0 + l % 16); the block's element (4 (l / 16) + i, l % 16) is
-// accumulator i. LDS row strides are chosen per access pattern so that the 32
-// lanes of a read fall on distinct banks (2 mod 32 words for rows read along
-// the contraction, 16 for rows read across it, 18 for both).
+// v_mfma_f32_16x16x4f32: lane l holds A(m0 + l % 16, k) and B(k, n0 + l % 16)
+// and the block's element (4 (l / 16) + i, l % 16) is accumulator i. The
+// contraction runs in passes of 64; in step s of a pass, lane group l / 16
+// takes k = 16 (l / 16) + s, so with LDS row strides of 1 mod 32 words the 32
+// lanes of a read fall on distinct banks whether an operand is read along its
+// rows or across them.
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int NTC = 512;      // threads of a chain workgroup
-constexpr int LKC = DP + 2;   // [C][d_k] rows
-constexpr int LCC = C + 2;    // [C][C] rows
-constexpr int LOC = TW + 2;   // [C][TW] and [DP][TW] rows
-
 // acc += sum_{k < K} A(m0 + i, k) B(k, n0 + j), A(m, k) = pa[m am + k ak],
-// B(k, n) = pb[k bk + n bn]; K a multiple of 4
+// B(k, n) = pb[k bk + n bn]; K a multiple of 64
 __device__ __forceinline__ void mfma16(floatx4& acc, const float* pa, int am, int ak,
                                        const float* pb, int bk, int bn, int m0, int n0, int K) {
   const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
-  const float* A = pa + (m0 + r) * am + q * ak;
-  const float* B = pb + q * bk + (n0 + r) * bn;
-#pragma unroll 4
-  for (int k = 0; k < K; k += 4)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[k * ak], B[k * bk], acc, 0, 0, 0);
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const float* A = pa + (m0 + r) * am + (k0 + 16 * q) * ak;
+    const float* B = pb + (k0 + 16 * q) * bk + (n0 + r) * bn;
+#pragma unroll 8
+    for (int s = 0; s < 16; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s * ak], B[s * bk], acc, 0, 0, 0);
+  }
 }
 
 // A row of blocks (m0, 16 b), b < NB, sharing the A operand: acc[b] +=
 // sum_{k < K} A(m0 + i, k) B(k, 16 b + j), A(m, k) = pa[m am + k ak] (times
-// as[k] when given), B(k, n) = pb[k bk + n bn].
+// as[k] when given), B(k, n) = pb[k bk + n bn]; K a multiple of 64
 template <int NB>
 __device__ __forceinline__ void mfma_row(floatx4 (&acc)[NB], const float* pa, int am, int ak,
                                          const float* as, const float* pb, int bk, int bn, int m0,
                                          int K) {
   const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
-  const float* A = pa + (m0 + r) * am + q * ak;
-  const float* B = pb + q * bk + r * bn;
-#pragma unroll 2
-  for (int k = 0; k < K; k += 4) {
-    float av = A[k * ak];
-    if (as) av *= as[k + q];
+  for (int k0 = 0; k0 < K; k0 += 64) {
+    const float* A = pa + (m0 + r) * am + (k0 + 16 * q) * ak;
+    const float* B = pb + (k0 + 16 * q) * bk + r * bn;
+#pragma unroll 4
+    for (int s = 0; s < 16; ++s) {
+      float av = A[s * ak];
+      if (as) av *= as[k0 + 16 * q + s];
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-      acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, B[k * bk + 16 * b * bn], acc[b], 0, 0, 0);
+      for (int b = 0; b < NB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, B[s * bk + 16 * b * bn], acc[b], 0, 0, 0);
+    }
   }
 }
 
 // Chain kernels: eight wavefronts; the 128 x 32 state (or state-gradient) tile
 // stays in registers, two blocks per wavefront, mirrored into LDS as an operand.
+constexpr int NTC = 512;      // threads of a chain workgroup
+constexpr int LKC = DP + 1;   // [C][d_k] rows
+constexpr int LCC = C + 1;    // [C][C] rows
+constexpr int LOC = TW + 1;   // [C][TW] and [DP][TW] rows
 
 __device__ __forceinline__ size_t cc_off(int bh, int nch, int c) {
   return ((size_t)bh * nch + c) * C * C;
@@ -192,7 +196,7 @@ __device__ __forceinline__ size_t cc_off(int bh, int nch, int c) {
 // prep: A, Pm, T of one chunk
 __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float lds[];
-  constexpr int LP = DP + 2;
+  constexpr int LP = DP + 1;
   float* sK = lds;                // [C][LP]
   float* sQ = sK + C * LP;        // [C][LP]
   float* sA = sQ + C * LP;        // [C][LC]
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   float* sB = sLg + C;
   float* sAl = sB + C;
   const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, nch = gridDim.y;
-  const int n = min(C, a.L - c * C), dk = a.dk, dk4 = (dk + 3) & ~3;
+  const int n = min(C, a.L - c * C), dk = a.dk, dk64 = dk <= 64 ? 64 : DP;
   const size_t tok = (size_t)bh * a.L + (size_t)c * C;
   const bool erase = a.resid != 2;
   {
@@ -218,8 +222,8 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   __syncthreads();
   const int w = tid >> 6, r = tid & 15, q = (tid & 63) >> 4;
   floatx4 kk[4] = {}, qk[4] = {};
-  mfma_row<4>(kk, sK, LP, 1, nullptr, sK, 1, LP, 16 * w, dk4);
-  mfma_row<4>(qk, sQ, LP, 1, nullptr, sK, 1, LP, 16 * w, dk4);
+  mfma_row<4>(kk, sK, LP, 1, nullptr, sK, 1, LP, 16 * w, dk64);
+  mfma_row<4>(qk, sQ, LP, 1, nullptr, sK, 1, LP, 16 * w, dk64);
   float* Ag = a.Am + cc_off(bh, nch, c);
   float* Pg = a.Pm + cc_off(bh, nch, c);
 #pragma unroll
@@ -308,7 +312,7 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
   float* sB = sLg + C;
   float* sAl = sB + C;
   const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
-  const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C, dk4 = (dk + 3) & ~3;
+  const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C, dk64 = dk <= 64 ? 64 : DP;
   const bool erase = a.resid != 2;
   const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
   const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);  // this wavefront's [C][TW] block
@@ -360,7 +364,7 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
     floatx4 e = {0.f, 0.f, 0.f, 0.f};
     if (erase) {
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
-      mfma16(x, sK, LKC, 1, sS, LOC, 1, m0, n0, dk4);
+      mfma16(x, sK, LKC, 1, sS, LOC, 1, m0, n0, dk64);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = m0 + 4 * q + i;
@@ -407,7 +411,7 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
   float* sB = sLg + C;
   float* sAl = sB + C;
   const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
-  const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C, dk4 = (dk + 3) & ~3;
+  const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C, dk64 = dk <= 64 ? 64 : DP;
   const bool erase = a.resid != 2;
   const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
   const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
     {
       floatx4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
       mfma16(x, sP, 1, LCC, sO, LOC, 1, m0, n0, C);
-      mfma16(y, sK, LKC, 1, sG, LOC, 1, m0, n0, dk4);
+      mfma16(y, sK, LKC, 1, sG, LOC, 1, m0, n0, dk64);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = m0 + 4 * q + i;
@@ -515,53 +519,56 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// contractions over the value columns; part 0: dO S0^T, dO E^T; part 1:
-// dR S0^T, dR E^T; part 2: E G^T, <G, S0>. Wavefront w takes rows 16 w ..
-// 16 w + 15 of both products; the value columns stream through LDS 32 at a time.
+// contractions over the value columns. STATE = false (grid z = part 0, 1):
+// part 0: dO S0^T, dO E^T; part 1: dR S0^T, dR E^T. STATE = true: E G^T and
+// <G, S0>. Wavefront w takes rows 16 w .. 16 w + 15 of the products; the value
+// columns stream through LDS 64 at a time.
+constexpr int VW = 64;  // value columns per pass
+
+template <bool STATE>
 __global__ __launch_bounds__(NT) void bwd_contract_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float lds[];
-  constexpr int LJ = TW + 2;
+  constexpr int LJ = VW + 1;
   float* sL = lds;               // [C][LJ] left operand block
   float* sR = sL + C * LJ;       // [DP][LJ] S0 or G block
   float* sE = sR + DP * LJ;      // [C][LJ] E block
   float* sRed = sE + C * LJ;     // [NT / 64]
-  const int bh = blockIdx.x, c = blockIdx.y, part = blockIdx.z, tid = threadIdx.x;
+  const int bh = blockIdx.x, c = blockIdx.y, part = STATE ? 2 : blockIdx.z, tid = threadIdx.x;
   const int nch = gridDim.y, L = a.L, dk = a.dk, dv = a.dv;
   const int n = min(C, L - c * C);
   const size_t row0 = (size_t)bh * nch * C + (size_t)c * C;  // padded-row arrays
   const float* left = part == 0 ? a.d_o + ((size_t)bh * L + (size_t)c * C) * dv
                                 : (part == 1 ? a.dR : a.E) + row0 * dv;
   const float* S0c = a.S0s + ((size_t)bh * nch + c) * dk * dv;
-  const float* right = part == 2 ? a.Gs + ((size_t)bh * nch + c) * dk * dv : S0c;
+  const float* right = STATE ? a.Gs + ((size_t)bh * nch + c) * dk * dv : S0c;
   const float* Ec = a.E + row0 * dv;
   const int w = tid >> 6, r = tid & 15, q = (tid & 63) >> 4;
   floatx4 m[8] = {}, p[4] = {};
   float gs = 0.f;
-  for (int jb = 0; jb < dv; jb += TW) {
-    Frag<C * TW / NT> fl, fe;
-    Frag<DP * TW / NT> fr, fs0;
-    fetch_tile<NT>(fl, left, n, dv, jb);
-    if (part < 2) fetch_tile<NT>(fe, Ec, n, dv, jb);
+  for (int jb = 0; jb < dv; jb += VW) {
+    Frag<C * VW / NT> fl, fe;
+    Frag<DP * VW / NT> fr, fs0;
+    fetch_tile<NT, VW>(fl, left, n, dv, jb);
+    if (!STATE) fetch_tile<NT, VW>(fe, Ec, n, dv, jb);
 #pragma unroll
-    for (int u = 0; u < DP * TW / NT; ++u) {
-      const int idx = tid + u * NT, d = idx >> 5, j = idx & 31;
+    for (int u = 0; u < DP * VW / NT; ++u) {
+      const int idx = tid + u * NT, d = idx / VW, j = idx % VW;
       const bool ok = d < dk && jb + j < dv;
       fr.x[u] = ok ? right[(size_t)d * dv + jb + j] : 0.f;
-      fs0.x[u] = (ok && part == 2) ? S0c[(size_t)d * dv + jb + j] : 0.f;
+      if (STATE) fs0.x[u] = ok ? S0c[(size_t)d * dv + jb + j] : 0.f;
     }
     __syncthreads();
-    put_tile<NT, LJ>(fl, sL, nullptr);
-    if (part < 2) put_tile<NT, LJ>(fe, sE, nullptr);
+    put_tile<NT, LJ, VW>(fl, sL, nullptr);
+    if (!STATE) put_tile<NT, LJ, VW>(fe, sE, nullptr);
 #pragma unroll
-    for (int u = 0; u < DP * TW / NT; ++u) {
-      const int idx = tid + u * NT, d = idx >> 5, j = idx & 31;
+    for (int u = 0; u < DP * VW / NT; ++u) {
+      const int idx = tid + u * NT, d = idx / VW, j = idx % VW;
       sR[d * LJ + j] = fr.x[u];
-      gs = fmaf(fr.x[u], fs0.x[u], gs);
+      if (STATE) gs = fmaf(fr.x[u], fs0.x[u], gs);
     }
     __syncthreads();
-    const int K4 = (min(TW, dv - jb) + 3) & ~3;
-    mfma_row<8>(m, sL, LJ, 1, nullptr, sR, 1, LJ, 16 * w, K4);
-    if (part < 2) mfma_row<4>(p, sL, LJ, 1, nullptr, sE, 1, LJ, 16 * w, K4);
+    mfma_row<8>(m, sL, LJ, 1, nullptr, sR, 1, LJ, 16 * w, VW);
+    if (!STATE) mfma_row<4>(p, sL, LJ, 1, nullptr, sE, 1, LJ, 16 * w, VW);
   }
   float* M = (part == 0 ? a.M1 : part == 1 ? a.M2 : a.M3) + row0 * dk;
 #pragma unroll
@@ -571,7 +578,7 @@ __global__ __launch_bounds__(NT) void bwd_contract_kernel(BwdArgs a) {
       const int d = 16 * b + r;
       if (d < dk) M[(size_t)(16 * w + 4 * q + i) * dk + d] = m[b][i];
     }
-  if (part < 2) {
+  if (!STATE) {
     float* P = (part == 0 ? a.dPm : a.dA) + cc_off(bh, nch, c);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
@@ -599,8 +606,8 @@ __device__ __forceinline__ float sum16(float x) {
 // of the [C][d_k] products
 __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float lds[];
-  constexpr int LQ = DP + 16;  // read across rows only
-  constexpr int LX = C + 18;   // read along and across rows
+  constexpr int LQ = DP + 1;
+  constexpr int LX = C + 1;
   float* sQ = lds;               // [C][LQ]
   float* sK = sQ + C * LQ;       // [C][LQ]
   float* sXp = sK + C * LQ;      // [C][LX] lower_incl(dO E^T) * D
@@ -633,6 +640,20 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     fetch_cc<NT>(fA, a.Am + o);
     fetch_cc<NT>(fdA, a.dA + o);
   }
+  // this lane's elements of dO S0^T, dR S0^T and E G^T (tokens 16 w + 4 q + i,
+  // columns 16 b + r), in flight during the elementwise pass
+  const int w = tid >> 6, r = tid & 15, q = (tid & 63) >> 4;
+  float m1v[4][8], m2v[4][8], m3v[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int d = 16 * b + r;
+      const size_t e = (row0 + 16 * w + 4 * q + i) * dk + d;
+      m1v[i][b] = d < dk ? a.M1[e] : 0.f;
+      m2v[i][b] = (erase && d < dk) ? a.M2[e] : 0.f;
+      m3v[i][b] = d < dk ? a.M3[e] : 0.f;
+    }
   __syncthreads();
   // Xp, Xa, and the row and column sums of W = dPm * Pm + dA * A (lane = s)
   {
@@ -657,7 +678,6 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     sCs[(tid >> 6) * C + s] = cs;
   }
   __syncthreads();
-  const int w = tid >> 6, r = tid & 15, q = (tid & 63) >> 4;
   const float lgC = sLg[C - 1];
   float pq[4] = {}, kr[4] = {}, wv[4] = {}, dbv[4] = {}, vv[4] = {};
   {  // dQ = diag(g) dO S0^T + Xp diag(b) K
@@ -667,11 +687,10 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * w + 4 * q + i;
       const float g = expf(sLg[t]);
-      const float* m1 = a.M1 + (row0 + t) * dk;
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
         const int d = 16 * b + r;
-        const float x = d < dk ? m1[d] : 0.f;
+        const float x = m1v[i][b];
         pq[i] = fmaf(x, sQ[t * LQ + d], pq[i]);
         if (t < n && d < dk) a.dq[(tok + t) * dk + d] = fmaf(g, x, acc[b][i]);
       }
@@ -689,14 +708,12 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * w + 4 * q + i;
       const float lam = expf(lgC - sLg[t]), g = expf(sLg[t]), b = sB[t];
-      const float* m3 = a.M3 + (row0 + t) * dk;
-      const float* m2 = a.M2 + (row0 + t) * dk;
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
         const int d = 16 * bb + r;
         const float kv = sK[t * LQ + d];
-        const float x3 = d < dk ? m3[d] : 0.f;
-        const float x2 = (erase && d < dk) ? m2[d] : 0.f;
+        const float x3 = m3v[i][bb];
+        const float x2 = m2v[i][bb];
         wv[i] = fmaf(kv, x3, wv[i]);
         const float dbb = fmaf(lam, x3, db[bb][i]);
         dbv[i] = fmaf(dbb, kv, dbv[i]);
@@ -813,7 +830,7 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
   const size_t f = sizeof(float);
   hipError_t e;
   e = launch_lds(bwd_prep_kernel, dim3(a.BH, nch), NT,
-                 (2 * C * (DP + 2) + 2 * C * LC + 32 * 33 + 3 * C) * f, a, s);
+                 (2 * C * (DP + 1) + 2 * C * LC + 32 * 33 + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
   e = launch_lds(bwd_fwd_kernel, dim3(a.BH, ntw), NTC,
                  (C * LKC + C * LCC + DP * LOC + 2 * C * LOC + 3 * C) * f, a, s);
@@ -821,11 +838,13 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
   e = launch_lds(bwd_rev_kernel, dim3(a.BH, ntw), NTC,
                  (2 * C * LKC + 2 * C * LCC + DP * LOC + 3 * C * LOC + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
-  e = launch_lds(bwd_contract_kernel, dim3(a.BH, nch, 3), NT,
-                 (2 * C * (TW + 2) + DP * (TW + 2) + NT / 64) * f, a, s);
+  const size_t lds_c = (2 * C * (VW + 1) + DP * (VW + 1) + NT / 64) * f;
+  e = launch_lds(bwd_contract_kernel<false>, dim3(a.BH, nch, 2), NT, lds_c, a, s);
+  if (e != hipSuccess) return e;
+  e = launch_lds(bwd_contract_kernel<true>, dim3(a.BH, nch), NT, lds_c, a, s);
   if (e != hipSuccess) return e;
   return launch_lds(bwd_grad_kernel, dim3(a.BH, nch), NT,
-                    (2 * C * (DP + 16) + 2 * C * (C + 18) + 3 * C + 6 * C + (NT / 64) * C) * f,
+                    (2 * C * (DP + 1) + 2 * C * (C + 1) + 3 * C + 6 * C + (NT / 64) * C) * f,
                     a, s);
 }
 
