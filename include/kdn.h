@@ -244,14 +244,20 @@ int hola_cache_update(const float *q, const float *k, const float *v, const floa
 /*
  * Gradients of the delta-write scan (reverse mode) for a loss L with given
  * dL/do (d_o) and dL/dS_L (dstate_out). The pages give no backward pass; the
- * library uses the adjoint of the token recurrence (c = alpha for the gated
+ * gradient is the adjoint of the token recurrence (c = alpha for the gated
  * residual, 1 for the plain one, 0 without erase):
  *   S_t = (alpha_t I - c_t beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,  o_t = S_t^T q_t,
  *   G_t = dL/dS_t:  G_t += q_t do_t^T,  dq_t = S_t do_t,  y_t = G_t^T k_t,
  *   dv_t = beta_t y_t,  dbeta_t = y_t . e_t,  dk_t = beta_t G_t e_t - c_t beta_t S_{t-1} y_t,
  *   dalpha_t = <G_t, S_{t-1}> - [gated] beta_t y_t . (S_{t-1}^T k_t),
  *   G_{t-1} = alpha_t G_t - c_t beta_t k_t y_t^T,  dS_0 = G_0.
- * Float32 inputs and outputs, layouts as kdn_scan_fwd; the delta write only.
+ * The library evaluates it in chunk form (64-token chunks; the same gradient up
+ * to rounding order): a forward chain for the chunk-start states, a reverse
+ * chain for the state gradients at chunk ends, everything else chunk-parallel
+ * on the fp32 matrix cores. Float32 inputs and outputs, layouts as
+ * kdn_scan_fwd; the delta write only. The decay gradient is formed as
+ * d(log alpha) / alpha, so alpha must be positive (alpha = 0 gives non-finite
+ * dalpha).
  *
  *  q, k [B,H,L,d_k], v [B,H,L,d_v], alpha (NULL = 1), beta [B,H,L], state_in
  *            (NULL = 0): the forward call's inputs.
@@ -260,11 +266,13 @@ int hola_cache_update(const float *q, const float *k, const float *v, const floa
  *            (required when alpha is given, else ignored);  dbeta [B,H,L] out;
  *            dstate_in [B,H,d_k,d_v] out or NULL.
  *  resid     KDN_RESID_GATED, _PLAIN or _NOERASE.
- *  workspace kdn_scan_bwd_workspace_size(...) bytes, 16-byte aligned: the
- *            states at every 64-token chunk start, one chunk's recomputed
- *            states per (head, 32 value columns), and per-tile partial sums.
- * Sizes: B, H >= 1; L >= 0; 1 <= d_k, d_v <= 128. The kernel walks the
- * tokens one by one (a reference-quality path, not a tuned one).
+ *  workspace kdn_scan_bwd_workspace_size(...) bytes, 16-byte aligned, device
+ *            memory owned by the caller: the state at every chunk start and
+ *            the state gradient at every chunk end (B*H*chunks*d_k*d_v floats
+ *            each), per-token residuals and their gradients, per-chunk 64 x 64
+ *            matrices and [64, d_k] contractions (about 1.2 GB at B=4, H=16,
+ *            L=4096, d=128). Its contents need no initialisation.
+ * Sizes: B, H >= 1; L >= 0; 1 <= d_k, d_v <= 128; ceil(L / 64) <= 65535.
  */
 size_t kdn_scan_bwd_workspace_size(int B, int H, int L, int d_k, int d_v);
 
