@@ -16,9 +16,10 @@
 //    merges the block's top list in.
 //  * read: one workgroup per (head, block, 64 queries), every block in
 //    parallel: streaming softmax over 32-key tiles of (cache members, causal
-//    block tokens) in float32, register-tiled.
-//  * commit: one workgroup per head gathers the final members' keys and values
-//    (from the old cache or the prompt), then writes the cache in rank order.
+//    block tokens), float32 on the matrix cores.
+//  * commit: one workgroup per (head, member) gathers the final members' keys
+//    and values (from the old cache or the prompt) into staging rows, then a
+//    second launch writes the cache in rank order.
 #include <math.h>
 
 #include "kdn_internal.h"
@@ -190,19 +191,60 @@ __global__ __launch_bounds__(NT) void merge_kernel(PrefillArgs a) {
   if (tid == 0) a.final_count[bh] = n;
 }
 
-// Read: 64 queries per workgroup against 32-key tiles, register-tiled so that
-// every LDS read feeds several FMAs. Thread (qg, j) = (tid / 16, tid % 16)
-// owns queries 4 qg .. 4 qg + 3; in the logits it takes keys 2 j, 2 j + 1 of
-// the tile, in the weighted sum value columns 8 j .. 8 j + 7. Queries and
-// keys are stored transposed ([d][query], [d][key]) and scaled by their RMS
-// norm (the queries also by 1/sqrt(d_k)), so a logit is a plain dot product.
+// Read: 64 queries per workgroup against 32-key tiles on the fp32 matrix cores
+// (v_mfma_f32_16x16x4f32: lane l holds A(m0 + l % 16, k) and B(k, n0 + l % 16);
+// the block's element (4 (l / 16) + i, l % 16) is accumulator i). Wavefront w
+// owns queries 16 w .. 16 w + 15: its logits for a tile are two 16 x 16 blocks,
+// the online softmax runs on them in registers (a row's 16 columns sit in 16
+// lanes), the weights go through LDS into operand order, and the outputs are
+// eight 16 x 16 blocks that stay in registers. Each lane keeps its query
+// operands in registers and the keys sit in LDS, both RMS-normalised (the
+// queries also times 1/sqrt(d_k)). In step s of a contraction pass of length
+// PL, lane group l / 16 takes k = (PL / 4)(l / 16) + s; with row strides of 1
+// mod 32 words the key reads are conflict-free. The next key tile is fetched
+// into registers while the current one is used.
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int LDR = MAXD + 1;  // [row][d] strides of the query, key and value tiles
+constexpr int LDP = KT + 1;    // [query][key] weights
+
+// Four consecutive elements (the index a multiple of 4, rows 16-byte aligned
+// for float32 and 8-byte aligned for bf16).
+__device__ __forceinline__ float4 ld4(const float* p, size_t i) {
+  return *reinterpret_cast<const float4*>(p + i);
+}
+__device__ __forceinline__ float4 ld4(const uint16_t* p, size_t i) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p + i);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+__device__ __forceinline__ bool aligned_rows(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
+}
+
+template <int NB, int PL>
+__device__ __forceinline__ void mfma_row(floatx4 (&acc)[NB], const float* pa, int am, int ak,
+                                         const float* pb, int bk, int bn, int m0, int K) {
+  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+  for (int k0 = 0; k0 < K; k0 += PL) {
+    const float* A = pa + (m0 + r) * am + (k0 + (PL / 4) * q) * ak;
+    const float* B = pb + (k0 + (PL / 4) * q) * bk + r * bn;
+#pragma unroll
+    for (int s = 0; s < PL / 4; ++s) {
+      const float av = A[s * ak];
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, B[s * bk + 16 * b * bn], acc[b], 0, 0, 0);
+    }
+  }
+}
+
 template <typename Tin>
 __global__ __launch_bounds__(NT) void read_kernel(PrefillArgs a) {
-  __shared__ float sQt[MAXD][QT + 4];
-  __shared__ float sKt[MAXD][KT + 4];
-  __shared__ float sV[KT][MAXD + 4];
-  __shared__ float sPt[KT][QT + 4];
-  __shared__ int sSrc[KT];
+  extern __shared__ __align__(16) float lds[];
+  float* sK = lds;               // [KT][LDR]
+  float* sV = sK + KT * LDR;     // [KT][LDR]
+  float* sP = sV + KT * LDR;     // [QT][LDP]
   const int bh = blockIdx.x, j = blockIdx.y, qt = blockIdx.z, tid = threadIdx.x;
   const int dk = a.dk, dv = a.dv;
   const int nblk = (a.L + a.block - 1) / a.block;
@@ -219,97 +261,135 @@ __global__ __launch_bounds__(NT) void read_kernel(PrefillArgs a) {
   const int ncache = a.member_count[(size_t)bh * nblk + j];
   // keys: the cache members, then the block's tokens up to the last query here
   const int nkeys = ncache + q0 + nq;
-  const float inv_sqrt_d = 1.f / sqrtf((float)dk);
+  const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
 
-  {  // queries: 4 lanes per row, RMS-normalised, times 1/sqrt(d_k), transposed
-    const int r = tid >> 2, part = tid & 3;
-    float x[MAXD / 4];
+  // This lane's query operands: row 16 w + r, columns 64 p + 16 q + s,
+  // RMS-normalised and times 1/sqrt(d_k) (the row's four lane groups meet by
+  // shuffles).
+  float qa[2][16];
+  {
+    const int row = 16 * w + r;
     float ss = 0.f;
 #pragma unroll
-    for (int u = 0; u < MAXD / 4; ++u) {
-      const int c = part + 4 * u;
-      x[u] = (r < nq && c < dk) ? Elem<Tin>::load(qh, (size_t)(j0 + q0 + r) * dk + c) : 0.f;
-      ss = fmaf(x[u], x[u], ss);
-    }
-    ss += __shfl_xor(ss, 1, 4);
-    ss += __shfl_xor(ss, 2, 4);
-    const float sc = inv_sqrt_d / sqrtf(ss / dk + a.rms_eps);
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-    for (int u = 0; u < MAXD / 4; ++u) sQt[part + 4 * u][r] = x[u] * sc;
+      for (int u = 0; u < 16; ++u) {
+        const int c = 64 * p + 16 * q + u;
+        const float x =
+            (row < nq && c < dk) ? Elem<Tin>::load(qh, (size_t)(j0 + q0 + row) * dk + c) : 0.f;
+        qa[p][u] = x;
+        ss = fmaf(x, x, ss);
+      }
+    ss += __shfl_xor(ss, 16, 64);
+    ss += __shfl_xor(ss, 32, 64);
+    const float sc = (1.f / sqrtf((float)dk)) / sqrtf(ss / dk + a.rms_eps);
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int u = 0; u < 16; ++u) qa[p][u] *= sc;
   }
-  const int qg = tid >> 4, jj = tid & 15;
-  float M[4], Z[4], acc[4][8];
+  // key tiles: 8 lanes per key; lane kp takes columns 32 g + 4 kp + v (g, v <
+  // 4), four consecutive ones per load, which also puts the 32 lanes of an LDS
+  // write on distinct banks. The source of the tile after next is looked up
+  // while the next tile's rows are in flight.
+  const int kr = tid >> 3, kp = tid & 7;
+  auto src_of = [&](int e) { return e < nkeys ? (e < ncache ? mem[e] : j0 + e - ncache) : 0; };
+  const bool vec = ((dk | dv) & 3) == 0 && aligned_rows(a.k) && aligned_rows(a.v) &&
+                   aligned_rows(a.cache_k) && aligned_rows(a.cache_v);
+  float kx[MAXD / 8], vx[MAXD / 8];
+  auto fetch = [&](int e, int src) {
+    const bool ok = e < nkeys;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 32 * g + 4 * kp;
+      float4 xk = make_float4(0.f, 0.f, 0.f, 0.f), xv = xk;
+      if (vec) {
+        if (ok && c < dk)
+          xk = src >= 0 ? ld4(kh, (size_t)src * dk + c) : ld4(ck, (size_t)(-1 - src) * dk + c);
+        if (ok && c < dv)
+          xv = src >= 0 ? ld4(vh, (size_t)src * dv + c) : ld4(cv, (size_t)(-1 - src) * dv + c);
+      } else {
+        float tk[4], tv[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int cc = c + v;
+          tk[v] = (ok && cc < dk) ? (src >= 0 ? Elem<Tin>::load(kh, (size_t)src * dk + cc)
+                                               : ck[(size_t)(-1 - src) * dk + cc])
+                                   : 0.f;
+          tv[v] = (ok && cc < dv) ? (src >= 0 ? Elem<Tin>::load(vh, (size_t)src * dv + cc)
+                                               : cv[(size_t)(-1 - src) * dv + cc])
+                                   : 0.f;
+        }
+        xk = make_float4(tk[0], tk[1], tk[2], tk[3]);
+        xv = make_float4(tv[0], tv[1], tv[2], tv[3]);
+      }
+      kx[4 * g] = xk.x;
+      kx[4 * g + 1] = xk.y;
+      kx[4 * g + 2] = xk.z;
+      kx[4 * g + 3] = xk.w;
+      vx[4 * g] = xv.x;
+      vx[4 * g + 1] = xv.y;
+      vx[4 * g + 2] = xv.z;
+      vx[4 * g + 3] = xv.w;
+    }
+  };
+  float M[4], Z[4];
+  floatx4 acc[MAXD / 16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     M[i] = a.sink_logit ? a.sink_logit[bh % a.H] : -INFINITY;
     Z[i] = a.sink_logit ? 1.f : 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) acc[i][c] = 0.f;
   }
-
+#pragma unroll
+  for (int cb = 0; cb < MAXD / 16; ++cb) acc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  fetch(kr, src_of(kr));
+  int src_next = src_of(KT + kr);
   for (int e0 = 0; e0 < nkeys; e0 += KT) {
     __syncthreads();
-    if (tid < KT) {
-      const int e = e0 + tid;
-      sSrc[tid] = e < nkeys ? (e < ncache ? mem[e] : j0 + e - ncache) : 0x7fffffff;
-    }
-    __syncthreads();
-    {  // keys: 8 lanes per key, RMS-normalised, transposed
-      const int kr = tid >> 3, part = tid & 7;
-      const int src = sSrc[kr];
-      float x[MAXD / 8];
+    {
       float ss = 0.f;
 #pragma unroll
-      for (int u = 0; u < MAXD / 8; ++u) {
-        const int c = part + 8 * u;
-        float v = 0.f;
-        if (src != 0x7fffffff && c < dk)
-          v = src >= 0 ? Elem<Tin>::load(kh, (size_t)src * dk + c) : ck[(size_t)(-1 - src) * dk + c];
-        x[u] = v;
-        ss = fmaf(v, v, ss);
-      }
+      for (int u = 0; u < MAXD / 8; ++u) ss = fmaf(kx[u], kx[u], ss);
       ss += __shfl_xor(ss, 1, 8);
       ss += __shfl_xor(ss, 2, 8);
       ss += __shfl_xor(ss, 4, 8);
       const float sc = 1.f / sqrtf(ss / dk + a.rms_eps);
 #pragma unroll
-      for (int u = 0; u < MAXD / 8; ++u) sKt[part + 8 * u][kr] = x[u] * sc;
-    }
-    for (int idx = tid; idx < KT * dv; idx += NT) {
-      const int r = idx / dv, c = idx - r * dv;
-      const int src = sSrc[r];
-      float x = 0.f;
-      if (src != 0x7fffffff)
-        x = src >= 0 ? Elem<Tin>::load(vh, (size_t)src * dv + c) : cv[(size_t)(-1 - src) * dv + c];
-      sV[r][c] = x;
-    }
-    __syncthreads();
-    // logits: 4 queries x 2 keys per thread
-    float l[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) l[i][0] = l[i][1] = 0.f;
-    for (int d = 0; d < dk; ++d) {
-      const float4 qv = *reinterpret_cast<const float4*>(&sQt[d][4 * qg]);
-      const float2 kv = *reinterpret_cast<const float2*>(&sKt[d][2 * jj]);
-      const float qa[4] = {qv.x, qv.y, qv.z, qv.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        l[i][0] = fmaf(qa[i], kv.x, l[i][0]);
-        l[i][1] = fmaf(qa[i], kv.y, l[i][1]);
+      for (int u = 0; u < MAXD / 8; ++u) {
+        const int c = 32 * (u >> 2) + 4 * kp + (u & 3);
+        sK[kr * LDR + c] = kx[u] * sc;
+        sV[kr * LDR + c] = vx[u];
       }
     }
-    float p[4][2];
+    if (e0 + KT < nkeys) {
+      fetch(e0 + KT + kr, src_next);
+      src_next = src_of(e0 + 2 * KT + kr);
+    }
+    __syncthreads();
+    floatx4 lg[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      if (p == 1 && dk <= 64) break;
+      const float* B = sK + 64 * p + 16 * q + r * LDR;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        lg[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[p][u], B[u], lg[0], 0, 0, 0);
+        lg[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[p][u], B[u + 16 * LDR], lg[1], 0, 0, 0);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int qtok = q0 + 4 * qg + i;  // relative to the block
+      const int qi = 16 * w + 4 * q + i;  // query within the tile
+      const int qtok = q0 + qi;           // relative to the block
+      float lv[2];
       float tmax = -INFINITY;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int e = e0 + 2 * jj + h;
+      for (int b = 0; b < 2; ++b) {
+        const int e = e0 + 16 * b + r;
         // cache members are always visible; block tokens up to the query itself
-        const bool vis = 4 * qg + i < nq && e < nkeys && (e < ncache || e - ncache <= qtok);
-        l[i][h] = vis ? l[i][h] : -INFINITY;
-        tmax = fmaxf(tmax, l[i][h]);
+        const bool vis = qi < nq && e < nkeys && (e < ncache || e - ncache <= qtok);
+        lv[b] = vis ? lg[b][i] : -INFINITY;
+        tmax = fmaxf(tmax, lv[b]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 16));
@@ -320,9 +400,10 @@ __global__ __launch_bounds__(NT) void read_kernel(PrefillArgs a) {
       const float scale = Mn == -INFINITY ? 1.f : __expf(M[i] - Mn);
       float ps = 0.f;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        p[i][h] = l[i][h] == -INFINITY ? 0.f : __expf(l[i][h] - Mn);
-        ps += p[i][h];
+      for (int b = 0; b < 2; ++b) {
+        const float p = lv[b] == -INFINITY ? 0.f : __expf(lv[b] - Mn);
+        sP[qi * LDP + 16 * b + r] = p;
+        ps += p;
       }
       ps += __shfl_xor(ps, 1, 16);
       ps += __shfl_xor(ps, 2, 16);
@@ -331,72 +412,65 @@ __global__ __launch_bounds__(NT) void read_kernel(PrefillArgs a) {
       Z[i] = fmaf(Z[i], scale, ps);
       M[i] = Mn;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[i][c] *= scale;
+      for (int cb = 0; cb < MAXD / 16; ++cb) acc[cb][i] *= scale;
     }
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      *reinterpret_cast<float4*>(&sPt[2 * jj + h][4 * qg]) = make_float4(p[0][h], p[1][h], p[2][h], p[3][h]);
     __syncthreads();
-    // weighted values: 4 queries x 8 value columns per thread
-    for (int e = 0; e < KT; ++e) {
-      const float4 pv = *reinterpret_cast<const float4*>(&sPt[e][4 * qg]);
-      const float4 v0 = *reinterpret_cast<const float4*>(&sV[e][8 * jj]);
-      const float4 v1 = *reinterpret_cast<const float4*>(&sV[e][8 * jj + 4]);
-      const float pa[4] = {pv.x, pv.y, pv.z, pv.w};
-      const float va[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[i][c] = fmaf(pa[i], va[c], acc[i][c]);
-    }
+    mfma_row<MAXD / 16, KT>(acc, sP, LDP, 1, sV, LDR, 1, 16 * w, KT);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int qi = 4 * qg + i;
+    const int qi = 16 * w + 4 * q + i;
     if (qi < nq) {
       float* o = a.o_cache + ((size_t)bh * a.L + j0 + q0 + qi) * dv;
       const float inv = 1.f / Z[i];
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        if (8 * jj + c < dv) o[8 * jj + c] = acc[i][c] * inv;
+      for (int cb = 0; cb < MAXD / 16; ++cb)
+        if (16 * cb + r < dv) o[16 * cb + r] = acc[cb][i] * inv;
     }
   }
 }
 
+// Commit, in two launches so that every (head, member) row has its own
+// workgroup: gather the final members' keys and values (from the prompt or an
+// old slot) into the staging rows, then write the cache in rank order. The
+// gather finishes before any slot is overwritten.
 template <typename Tin>
-__global__ __launch_bounds__(NT) void commit_kernel(PrefillArgs a) {
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int n = a.final_count[bh];
-  const int* fin = a.final_src + (size_t)bh * a.w;
+__global__ __launch_bounds__(64) void commit_gather_kernel(PrefillArgs a) {
+  const int bh = blockIdx.x, e = blockIdx.y, tid = threadIdx.x;
+  if (e >= a.final_count[bh]) return;
+  const int src = a.final_src[(size_t)bh * a.w + e];
   const int row = a.dk + a.dv;
-  float* stage = a.stage + (size_t)bh * a.w * row;
+  float* st = a.stage + ((size_t)bh * a.w + e) * row;
   const Tin* kh = static_cast<const Tin*>(a.k) + (size_t)bh * a.L * a.dk;
   const Tin* vh = static_cast<const Tin*>(a.v) + (size_t)bh * a.L * a.dv;
-  float* ck = a.cache_k + (size_t)bh * a.w * a.dk;
-  float* cv = a.cache_v + (size_t)bh * a.w * a.dv;
-  // gather first: a member may come from an old slot that is rewritten below
-  for (int idx = tid; idx < n * row; idx += NT) {
-    const int e = idx / row, c = idx - e * row;
-    const int src = fin[e];
+  const float* ck = a.cache_k + (size_t)bh * a.w * a.dk;
+  const float* cv = a.cache_v + (size_t)bh * a.w * a.dv;
+  for (int c = tid; c < row; c += 64) {
     float x;
     if (c < a.dk)
       x = src >= 0 ? Elem<Tin>::load(kh, (size_t)src * a.dk + c) : ck[(size_t)(-1 - src) * a.dk + c];
     else
       x = src >= 0 ? Elem<Tin>::load(vh, (size_t)src * a.dv + c - a.dk)
                    : cv[(size_t)(-1 - src) * a.dv + c - a.dk];
-    stage[idx] = x;
+    st[c] = x;
   }
-  __syncthreads();
-  for (int idx = tid; idx < n * row; idx += NT) {
-    const int e = idx / row, c = idx - e * row;
-    if (c < a.dk) ck[(size_t)e * a.dk + c] = stage[idx];
-    else cv[(size_t)e * a.dv + c - a.dk] = stage[idx];
+}
+
+__global__ __launch_bounds__(64) void commit_scatter_kernel(PrefillArgs a) {
+  const int bh = blockIdx.x, e = blockIdx.y, tid = threadIdx.x;
+  const int n = a.final_count[bh];
+  if (e == 0 && tid == 0) a.cache_count[bh] = n;
+  if (e >= n) return;
+  const int row = a.dk + a.dv;
+  const float* st = a.stage + ((size_t)bh * a.w + e) * row;
+  for (int c = tid; c < row; c += 64) {
+    if (c < a.dk) a.cache_k[((size_t)bh * a.w + e) * a.dk + c] = st[c];
+    else a.cache_v[((size_t)bh * a.w + e) * a.dv + c - a.dk] = st[c];
   }
-  for (int e = tid; e < n; e += NT) {
+  if (tid == 0) {
     a.cache_m[(size_t)bh * a.w + e] = a.final_m[(size_t)bh * a.w + e];
     a.cache_pos[(size_t)bh * a.w + e] = a.final_pos[(size_t)bh * a.w + e];
   }
-  if (tid == 0) a.cache_count[bh] = n;
 }
 
 template <typename Tin>
@@ -409,11 +483,18 @@ hipError_t prefill_typed(const PrefillArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(merge_kernel, dim3(a.BH), dim3(NT), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(read_kernel<Tin>, dim3(a.BH, nblk, (a.block + QT - 1) / QT), dim3(NT), 0, s,
-                     a);
+  const size_t read_lds = (size_t)(2 * KT * LDR + QT * LDP) * sizeof(float);
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(read_kernel<Tin>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)read_lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(read_kernel<Tin>, dim3(a.BH, nblk, (a.block + QT - 1) / QT), dim3(NT),
+                     read_lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(commit_kernel<Tin>, dim3(a.BH), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(commit_gather_kernel<Tin>, dim3(a.BH, a.w), dim3(64), 0, s, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(commit_scatter_kernel, dim3(a.BH, a.w), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
