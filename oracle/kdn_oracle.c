@@ -558,7 +558,8 @@ int oracle_scan_bwd(int B, int H, int L, int dk, int dv,
         double *ckpt = (double *)malloc(sizeof(double) * SS * (size_t)(nck + 1));
         double *hist = (double *)malloc(sizeof(double) * SS * (size_t)(CK + 1));
         double *G = (double *)malloc(sizeof(double) * SS);
-        double *y = (double *)malloc(sizeof(double) * (size_t)(dv + dv + dk));
+        /* y = G^T k, e = v - c S^T k and p = S^T k are d_v-vectors */
+        double *y = (double *)malloc(sizeof(double) * (size_t)(3 * dv));
         if (!ckpt || !hist || !G || !y) {
 #pragma omp atomic write
             bad = 1;

@@ -55,3 +55,22 @@ def test_backward_full_size(kdn, orc):
     on sampled heads."""
     log("backward full size")
     _case(kdn, orc, 4, 16, 4096, 128, 128, "gated", seed=403, heads=[(0, 0), (3, 15)])
+
+
+def test_backward_defaults(kdn, orc):
+    """No decay array (alpha = 1), no initial state and no final-state gradient;
+    one token, and one full chunk plus one token, with d_k != d_v."""
+    import torch
+    for L, dk, dv in ((1, 128, 64), (65, 64, 128)):
+        log(f"backward defaults L {L} dk {dk} dv {dv}")
+        inp = workloads.scan_inputs(1, 2, L, dk, dv, seed=404, dtype="f32")
+        rng = np.random.Generator(np.random.PCG64([404, L]))
+        d_o = rng.standard_normal((1, 2, L, dv)).astype(np.float32)
+        g = kdn.kdn_scan_bwd(dev_tensor(inp["q"]), dev_tensor(inp["k"]), dev_tensor(inp["v"]), None,
+                             dev_tensor(inp["beta"]), dev_tensor(d_o))
+        torch.cuda.synchronize()
+        assert g["dalpha"] is None
+        ref = orc.scan_bwd(inp["q"], inp["k"], inp["v"], alpha=None, beta=inp["beta"], d_o=d_o)
+        for n in ("dq", "dk", "dv", "dbeta"):
+            assert_close(host(g[n]), ref[n], TOL_F32, f"defaults {n}")
+        assert_close(host(g["dstate_in"]), ref["dS0"], TOL_F32, "defaults dS0")

@@ -112,6 +112,22 @@ def test_prefill_odd_shapes(kdn, orc):
     _prefill_case(kdn, orc, q, k, v, m, 0, 9, w, "f32", rng.standard_normal(H).astype(np.float32))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prefill_unaligned_rows(kdn, orc, dtype):
+    """Key and value widths that are not multiples of 4 (the element-wise
+    gather), and d_k > 64 (two contraction passes for the logits)."""
+    rng = np.random.Generator(np.random.PCG64(305))
+    B, H, L, dk, dv, w = 1, 2, 150, 66, 18, 7
+    q = rng.standard_normal((B, H, L, dk)).astype(np.float32)
+    k = rng.standard_normal((B, H, L, dk)).astype(np.float32)
+    v = rng.standard_normal((B, H, L, dv)).astype(np.float32)
+    m = rng.uniform(0, 1, (B, H, L)).astype(np.float32)
+    for block, init in ((32, None), (100, 4)):
+        _prefill_case(kdn, orc, q, k, v, m, 3, block, w, dtype,
+                      rng.standard_normal(H).astype(np.float32),
+                      init=None if init is None else (init, rng))
+
+
 def test_scan_scores_then_prefill(kdn, orc):
     """The scan's scores feed the cache: gated delta scan with scores, then the
     prompt cache, both checked against the oracle (scores to the bf16 bar,

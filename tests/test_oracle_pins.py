@@ -840,16 +840,18 @@ def _fd_loss(orc, inp, S0, d_o, dS, resid):
     return float(np.sum(r["o"] * d_o) + np.sum(r["S"] * dS))
 
 
-@pytest.mark.parametrize("resid,L", [("gated", 9), ("plain", 9), ("noerase", 9), ("gated", 150)])
-def test_backward_matches_finite_differences(orc, resid, L):
+@pytest.mark.parametrize("resid,L,dk,dv", [("gated", 9, 4, 3), ("plain", 9, 4, 3),
+                                           ("noerase", 9, 4, 3), ("gated", 150, 4, 3),
+                                           ("gated", 9, 3, 5)])
+def test_backward_matches_finite_differences(orc, resid, L, dk, dv):
     """The gradients of the scan (the pages give none; the adjoint recurrence is
     derived for this library) against central finite differences of the forward
     oracle, for every input including the initial state, on a loss
     sum(d_o * o) + sum(dS * S_L). Inputs are float32, so the steps are powers
     of two that keep the perturbed inputs exact; L = 150 crosses the backward's
-    64-token recomputation checkpoints (sampled elements)."""
+    64-token recomputation checkpoints (sampled elements); d_v > d_k once."""
     rng = _rng(60 + L)
-    B, H, dk, dv = 1, 2, 4, 3
+    B, H = 1, 2
     inp = workloads.scan_inputs(B, H, L, dk, dv, seed=61, dtype="f32")
     S0 = rng.standard_normal((B, H, dk, dv)) * 0.5
     d_o = rng.standard_normal((B, H, L, dv))
