@@ -303,6 +303,30 @@ def cpu_baseline(name="gated", seconds_target=15.0):
                        f"tokens/s = token-heads/s / H")
 
 
+def _extra_scan(name, mode):
+    def run(kdn, torch, args):
+        r = bench_scan(kdn, torch, name, max(2, args.steps // 4), 1, mode=mode, per_phase=True)
+        nb = scan_bytes(r["B"], r["H"], r["L"], r["dk"], r["dv"],
+                        extra_per_token=4 if mode in ("diag", "iso") else 0)
+        return dict(ms_per_step=round(r["ms_per_step"], 5), tokens_per_s=round(r["tokens_per_s"], 1),
+                    prepare_ms=round(r["prepare_ms"], 5), state_ms=round(r["state_ms"], 5),
+                    hbm_frac_step=round(nb / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    return run
+
+
+# the extra workloads, in the order the full run reports them
+EXTRAS = {
+    "decode": lambda kdn, torch, args: bench_decode(kdn, torch, steps=max(8, args.steps),
+                                                    warmup=args.warmup),
+    "prompt_cache": lambda kdn, torch, args: bench_prefill(kdn, torch,
+                                                           steps=max(2, args.steps // 4), warmup=1),
+    "backward": lambda kdn, torch, args: bench_backward(kdn, torch, steps=2, warmup=1),
+    "kdn_diag": _extra_scan("kdn_diag", "diag"),
+    "kdn_iso": _extra_scan("kdn_diag", "iso"),
+    "long": _extra_scan("long", "delta"),
+}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +336,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (counter calibration)")
+    ap.add_argument("--only", choices=list(EXTRAS), default=None,
+                    help="run one of the extra workloads alone and print its result "
+                         "(for profiling; not the benchmark line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -331,6 +358,11 @@ def main():
         y.copy_(x)
         torch.cuda.synchronize()
         del x, y
+
+    if args.only:
+        res = EXTRAS[args.only](kdn, torch, args)
+        print(json.dumps({"only": args.only, args.only: res}), flush=True)
+        return
 
     main_res = bench_scan(kdn, torch, "gated", args.steps, args.warmup)
     B, H, L, dk, dv, C = (main_res[k] for k in ("B", "H", "L", "dk", "dv", "C"))
@@ -371,22 +403,8 @@ def main():
     }
     if not args.quick:
         extra = {}
-        extra["decode"] = bench_decode(kdn, torch, steps=max(8, args.steps), warmup=args.warmup)
-        extra["prompt_cache"] = bench_prefill(kdn, torch, steps=max(2, args.steps // 4), warmup=1)
-        torch.cuda.empty_cache()
-        extra["backward"] = bench_backward(kdn, torch, steps=2, warmup=1)
-        torch.cuda.empty_cache()
-        for key, name, mode in (("kdn_diag", "kdn_diag", "diag"), ("kdn_iso", "kdn_diag", "iso"),
-                                ("long", "long", "delta")):
-            r = bench_scan(kdn, torch, name, max(2, args.steps // 4), 1, mode=mode, per_phase=True)
-            nb = scan_bytes(r["B"], r["H"], r["L"], r["dk"], r["dv"],
-                            extra_per_token=4 if mode in ("diag", "iso") else 0)
-            extra[key] = dict(ms_per_step=round(r["ms_per_step"], 5),
-                               tokens_per_s=round(r["tokens_per_s"], 1),
-                               prepare_ms=round(r["prepare_ms"], 5),
-                               state_ms=round(r["state_ms"], 5),
-                               hbm_frac_step=round(nb / (r["ms_per_step"] * 1e-3) / 1e9
-                                                   / HBM_PEAK_GBS, 4))
+        for key, fn in EXTRAS.items():
+            extra[key] = fn(kdn, torch, args)
             torch.cuda.empty_cache()
         line["extra"] = extra
     if not args.no_cpu_baseline:
