@@ -146,17 +146,22 @@ __device__ void put_scalars(const BwdArgs& a, Scal f, float* sLg, float* sB, flo
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // acc += sum_{k < K} A(m0 + i, k) B(k, n0 + j), A(m, k) = pa[m am + k ak],
-// B(k, n) = pb[k bk + n bn]; K a multiple of 64
+// B(k, n) = pb[k bk + n bn]; K a multiple of 64. Even and odd steps go to two
+// accumulators, so that two independent product chains are in flight.
 __device__ __forceinline__ void mfma16(floatx4& acc, const float* pa, int am, int ak,
                                        const float* pb, int bk, int bn, int m0, int n0, int K) {
   const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+  floatx4 acc2 = {0.f, 0.f, 0.f, 0.f};
   for (int k0 = 0; k0 < K; k0 += 64) {
     const float* A = pa + (m0 + r) * am + (k0 + 16 * q) * ak;
     const float* B = pb + (k0 + 16 * q) * bk + (n0 + r) * bn;
-#pragma unroll 8
-    for (int s = 0; s < 16; ++s)
+#pragma unroll 4
+    for (int s = 0; s < 16; s += 2) {
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[s * ak], B[s * bk], acc, 0, 0, 0);
+      acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(A[(s + 1) * ak], B[(s + 1) * bk], acc2, 0, 0, 0);
+    }
   }
+  acc += acc2;
 }
 
 // A row of blocks (m0, 16 b), b < NB, sharing the A operand: acc[b] +=
@@ -385,13 +390,13 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
     }
     __syncthreads();
     const float gC = expf(lgC);
+    floatx4 acc[2] = {S[0] * gC, S[1] * gC};
+    mfma_row<2>(acc, sK, 1, LKC, nullptr, sE, LOC, 1, 16 * w, C);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      floatx4 acc = S[h] * gC;
-      mfma16(acc, sK, 1, LKC, sE, LOC, 1, 16 * w, 16 * h, C);
-      S[h] = acc;
+      S[h] = acc[h];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * q + i) * LOC + 16 * h + r] = acc[i];
+      for (int i = 0; i < 4; ++i) sS[(16 * w + 4 * q + i) * LOC + 16 * h + r] = acc[h][i];
     }
   }
 }
@@ -497,14 +502,14 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
     __syncthreads();
     // G <- g_C G + Q^T diag(g) dO - K^T diag(g) dR
     const float gC = expf(lgC);
+    floatx4 acc[2] = {G[0] * gC, G[1] * gC};
+    mfma_row<2>(acc, sQ, 1, LKC, nullptr, sO, LOC, 1, 16 * w, C);
+    if (erase) mfma_row<2>(acc, sK, 1, LKC, nullptr, sX, LOC, 1, 16 * w, C);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      floatx4 acc = G[h] * gC;
-      mfma16(acc, sQ, 1, LKC, sO, LOC, 1, 16 * w, 16 * h, C);
-      if (erase) mfma16(acc, sK, 1, LKC, sX, LOC, 1, 16 * w, 16 * h, C);
-      G[h] = acc;
+      G[h] = acc[h];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sG[(16 * w + 4 * q + i) * LOC + 16 * h + r] = acc[i];
+      for (int i = 0; i < 4; ++i) sG[(16 * w + 4 * q + i) * LOC + 16 * h + r] = acc[h][i];
     }
   }
   if (a.dstate_in) {
