@@ -64,16 +64,43 @@ def code_digest(path):
     return hashlib.sha256(re.sub(r"\s+", "", code).encode()).hexdigest()
 
 
-def measured_traffic(kernel_ms):
-    """HBM bytes per launch of the state kernel from the committed counter runs
-    (profiles/*_traffic.json), or None when the kernel code changed since."""
+def counter_record():
+    """The state kernel's committed counter record (profiles/*_traffic.json:
+    HBM bytes per launch, executed matrix-core flops, matrix-core busy
+    fraction), or None when the kernel code changed since it was taken."""
     path = os.path.join(ROOT, "profiles", "scan_gated_B4H16L4096_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if code_digest(os.path.join(ROOT, rec["source"])) != rec["code_sha256"]:
         return None
-    return rec["hbm_read_bytes"] + rec["hbm_write_bytes"]
+    return rec
+
+
+def measured_traffic(kernel_ms):
+    """HBM bytes per launch of the state kernel from the committed counter runs,
+    or None when the kernel code changed since."""
+    rec = counter_record()
+    return None if rec is None else rec["hbm_read_bytes"] + rec["hbm_write_bytes"]
+
+
+def copy_bandwidth(torch, mib=1024, reps=10):
+    """On-box attainable HBM rate: a device-to-device copy of `mib` MiB, bytes
+    read plus bytes written over the time."""
+    x = torch.empty(mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    e0, e1 = _events(torch, 2)
+    e0.record()
+    for _ in range(reps):
+        y.copy_(x)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2 * x.numel() * 4 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del x, y
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
 
 
 # The GPU runs at its idle clock until it has been busy for a few tens of
@@ -98,7 +125,7 @@ def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True):
+def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True, cold=False):
     import workloads
     cfg = workloads.WORKLOADS[name]
     B, H, L, dk, dv, C = cfg["B"], cfg["H"], cfg["L"], cfg["dk"], cfg["dv"], cfg["chunk"]
@@ -135,6 +162,20 @@ def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     res = dict(ms_per_step=ms, tokens_per_s=B * L / (ms * 1e-3), B=B, H=H, L=L, dk=dk, dv=dv, C=C)
+    if cold:
+        # a 512 MiB write between steps evicts the 256 MB last-level cache, so
+        # every step reads its inputs from HBM; only the scan is timed
+        flush = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+        ev = _events(torch, 2 * steps)
+        for i in range(steps):
+            flush.fill_(float(i))
+            ev[2 * i].record()
+            step()
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        cms = sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)) / steps
+        res["cold_ms_per_step"] = cms
+        del flush
     if per_phase:
         ev = _events(torch, 3 * steps)
         for i in range(steps):
@@ -254,21 +295,43 @@ def bench_decode(kdn, torch, steps, warmup):
         kdn.kdn_step_decode(x["q"], x["k"], x["v"], x["alpha"], x["beta"], state, o=o, m=m)
         kdn.hola_cache_update(x["q"], x["k"], x["v"], m, i, cache, o_cache=oc)
 
+    def timed(fn):
+        e0, e1 = _events(torch, 2)
+        e0.record()
+        for i in range(warmup, total):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+    ms = timed(step)
+    gbs = B * H * DECODE_BYTES_PER_HEAD / (ms * 1e-3) / 1e9
+    # the same steps captured once into a HIP graph and replayed (the state and
+    # the cache keep evolving, so every replay does a full step's work)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(warmup, total):
+            step(i)
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = 3
     e0, e1 = _events(torch, 2)
     e0.record()
-    for i in range(warmup, total):
-        step(i)
+    for _ in range(reps):
+        graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    gbs = B * H * DECODE_BYTES_PER_HEAD / (ms * 1e-3) / 1e9
+    gms = e0.elapsed_time(e1) / (reps * steps)
+    frac = lambda t: round(B * H * DECODE_BYTES_PER_HEAD / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)  # noqa: E731
     return dict(ms_per_step=round(ms, 5), tokens_per_s=round(B / (ms * 1e-3), 1),
                 bytes_per_step=B * H * DECODE_BYTES_PER_HEAD, achieved_gbs=round(gbs, 1),
-                hbm_frac=round(gbs / HBM_PEAK_GBS, 4), steps=steps, warmup=warmup,
-                config="decode + HOLA cache, B=256 H=32 d=128 fp32, w=64, cache full")
+                hbm_frac=frac(ms), steps=steps, warmup=warmup,
+                graph_ms_per_step=round(gms, 5), graph_hbm_frac=frac(gms),
+                config="decode + HOLA cache, B=256 H=32 d=128 fp32, w=64, cache full; "
+                       "kdn_step_decode + hola_cache_update per step")
 
 
 def cpu_baseline(name="gated", seconds_target=15.0):
@@ -364,12 +427,13 @@ def main():
         print(json.dumps({"only": args.only, args.only: res}), flush=True)
         return
 
-    main_res = bench_scan(kdn, torch, "gated", args.steps, args.warmup)
+    main_res = bench_scan(kdn, torch, "gated", args.steps, args.warmup, cold=not args.quick)
     B, H, L, dk, dv, C = (main_res[k] for k in ("B", "H", "L", "dk", "dv", "C"))
     nbytes = scan_bytes(B, H, L, dk, dv)
     flops = B * H * L * scan_flops_per_token_head(C, dk, dv)
     state_s = main_res["state_ms"] * 1e-3
     achieved = nbytes / state_s / 1e9
+    rec = counter_record()
     line = {
         "metric": METRIC,
         "value": round(main_res["tokens_per_s"], 1),
@@ -397,11 +461,22 @@ def main():
                  "frac_of_peak_step": round(flops / (main_res["ms_per_step"] * 1e-3) / 1e12
                                             / MFMA_F16_PEAK_TFLOPS, 4),
                  "frac_of_peak_state_kernel": round(flops / state_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
-                 "peak_tflops": MFMA_F16_PEAK_TFLOPS},
+                 "peak_tflops": MFMA_F16_PEAK_TFLOPS,
+                 # from the committed counter run (null once the kernel changed):
+                 # executed matrix-core flops of the state kernel over its time
+                 # here, and its matrix-core busy fraction under the profiler
+                 "executed_frac_state_kernel": (
+                     None if rec is None else
+                     round(rec["mfma_executed_flops"] / state_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)),
+                 "busy_frac_state_kernel": None if rec is None else rec["mfma_busy_frac"]},
         "phases_ms": {"prepare": round(main_res["prepare_ms"], 5),
                       "state": round(main_res["state_ms"], 5)},
     }
     if not args.quick:
+        line["cold"] = {"ms_per_step": round(main_res["cold_ms_per_step"], 5),
+                        "tokens_per_s": round(B * L / (main_res["cold_ms_per_step"] * 1e-3), 1),
+                        "note": "256 MB last-level cache flushed by a 512 MiB write before each step"}
+        line["roofline"]["attainable_copy_gbs"] = copy_bandwidth(torch)
         extra = {}
         for key, fn in EXTRAS.items():
             extra[key] = fn(kdn, torch, args)

@@ -230,3 +230,43 @@ def test_recency_cache(kdn, orc):
     for b in range(B):
         for h in range(H):
             assert sorted(host(cache.pos)[b, h].astype(int).tolist()) == list(range(T - w, T))
+
+
+def test_decode_graph_replays(kdn):
+    """Three decode + cache steps captured in one HIP graph: every replay, with
+    eager work and synchronisation between replays, matches the same steps run
+    eagerly on a copy of the state and cache (bit for bit: same kernels, same
+    inputs)."""
+    import torch
+    B, H, d, w = 2, 3, 128, 4
+    steps = [workloads.decode_step_inputs(s, B, H, d, d) for s in range(3)]
+    x = [{n: dev_tensor(a) for n, a in st.items()} for st in steps]
+
+    def new_state():
+        return torch.zeros((B, H, d, d), device="cuda"), kdn.HolaCache(B, H, d, d, w)
+
+    def run(state, cache, o, m, oc, base):
+        for i, xi in enumerate(x):
+            kdn.kdn_step_decode(xi["q"], xi["k"], xi["v"], xi["alpha"], xi["beta"], state, o=o, m=m)
+            kdn.hola_cache_update(xi["q"], xi["k"], xi["v"], m, base + i, cache, o_cache=oc)
+
+    outs = lambda: (torch.empty((B, H, d), device="cuda"), torch.empty((B, H), device="cuda"),
+                    torch.empty((B, H, d), device="cuda"))
+    se, ce = new_state()
+    oe, me, oce = outs()
+    sg, cg = new_state()
+    og, mg, ocg = outs()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(sg, cg, og, mg, ocg, 0)
+    for rep in range(3):
+        log(f"graph replay {rep}")
+        run(se, ce, oe, me, oce, 0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b, name in ((sg, se, "state"), (og, oe, "o"), (mg, me, "m"), (ocg, oce, "o_cache"),
+                           (cg.k, ce.k, "cache k"), (cg.v, ce.v, "cache v"), (cg.m, ce.m, "cache m"),
+                           (cg.pos, ce.pos, "cache pos"), (cg.count, ce.count, "cache count")):
+            assert torch.equal(a, b), f"replay {rep}: {name}"
+
