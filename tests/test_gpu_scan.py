@@ -104,6 +104,20 @@ def test_plain_residual(kdn, orc, dtype):
     assert_close(got["S"], ref["S"], tol, "plain S")
 
 
+def test_short_sequences(kdn, orc):
+    """Lengths of one token, a partial chunk, exactly one and two chunks and one
+    past them, on the matrix-core path with B*H = 8 (the XCD-aware block order),
+    with and without a final state."""
+    for L in (1, 5, 63, 64, 65, 128, 129):
+        log(f"short L {L}")
+        inp = workloads.scan_inputs(2, 4, L, 128, 128, seed=110 + L, dtype="bf16")
+        ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"])
+        got = _scan_gpu(kdn, inp, "bf16", 64, want_state=L % 2 == 1)
+        assert_close(got["o"], ref["o"], TOL_BF16, f"o L {L}")
+        if got["S"] is not None:
+            assert_close(got["S"], ref["S"], TOL_BF16, f"S L {L}")
+
+
 def test_split_sequence_resume(kdn, orc):
     """Scanning [0, L) equals scanning [0, L1) and resuming [L1, L) from the
     returned state."""
