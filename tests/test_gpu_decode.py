@@ -180,6 +180,21 @@ def test_diag_with_covariance_reset_is_delta(kdn):
     assert_close(host(S2), host(S1), 1e-5, "reset S")
 
 
+@pytest.mark.parametrize("B,H,dk,dv,w,steps,sink", [
+    (48, 32, 128, 128, 12, 30, True),   # many heads, with a sink
+    (2, 3, 64, 64, 80, 100, False),     # w > 64: more slots than a wavefront, evicting
+    (2, 3, 30, 18, 6, 20, True),        # rows that are not whole 16-byte quads (scalar loads)
+])
+def test_cache_kernel_forms(kdn, orc, B, H, dk, dv, w, steps, sink):
+    """The cache kernel against the oracle on the shapes its code paths split
+    on: 16-byte rows or not, and capacities above one slot per lane of the
+    wavefront that chooses the eviction."""
+    log(f"cache kernel B={B} H={H} dk={dk} dv={dv} w={w} steps={steps} sink={sink}")
+    sample = None if B * H <= 16 else [(0, 0), (5, 7), (23, 31), (47, 30), (47, 31)]
+    got, ref = _run_decode(kdn, orc, B, H, dk, dv, w, steps, seed=207, sink=sink, sample=sample)
+    _compare(got, ref, w, f"cache kernel w={w} dk={dk}")
+
+
 def test_full_size_decode_hola(kdn, orc):
     """The decode workload at full size (B=256, H=32, d=128, 512 steps, w=64),
     checked on sampled heads over every step."""
