@@ -11,7 +11,9 @@
 //   S = g_n S0 + (diag(w) B)^T U,  w_l = (g_n / g_l) beta_l  (1 in place of beta for a gain)
 //
 // Two kernels:
-//  * prep_kernel: one workgroup per (head, chunk), every chunk in parallel.
+//  * prep_kernel: every chunk independent of the others; a workgroup takes a
+//    few consecutive chunks of one head and loads the next chunk's inputs
+//    while it computes the current one.
 //    Everything that does not depend on the state: the per-token decay
 //    scalars g_t, w_t; the Grams K B^T and Q B^T on the matrix cores; and
 //    T = (I + A)^-1 by blocks of 16: the four diagonal blocks are inverted in
@@ -39,6 +41,7 @@
 // (16-byte LDS reads); its result gives each lane 4 consecutive rows of one
 // column, which is written either as [n][m] (one 8-byte write) or [m][n]
 // (four 2-byte writes). Every buffer below is laid out for its reader.
+#include <algorithm>
 #include <utility>
 
 #include "kdn_internal.h"
@@ -97,6 +100,7 @@ __device__ __forceinline__ void st4(_Float16* p, floatx4 x) {
 }
 
 typedef float float2v __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 // Two floats -> two fp16 in one dword (one v_cvt_pk_f16_f32).
@@ -164,6 +168,7 @@ struct PrepArgs {
   const float* beta;      // [BH, L]
   unsigned char* rec;     // [BH, nchunks] records of rec_bytes(gain)
   int L, nchunks, plain;
+  int cpw;                // consecutive chunks per workgroup
 };
 
 constexpr int kAdP = 17;  // fp32 pitch of the diagonal blocks of A
@@ -176,9 +181,47 @@ size_t prep_lds_bytes(bool gain) {
          (size_t)2 * C * 4;
 }
 
+// One chunk's inputs in registers: this thread's four 16-byte pieces of K
+// (and of Q and the gains), and token `lane`'s alpha and beta.
+template <bool GAIN>
+struct PrepIn {
+  uint4 k[4], q[GAIN ? 4 : 1], g[GAIN ? 4 : 1];
+  float al, be;
+};
+
+// Loads chunk cc of head bh through buffer descriptors over the head's rows:
+// rows past the sequence read as zero, and so does every load when `has` is
+// false (descriptor range 0, no memory access). No load sits behind a branch,
+// which keeps the compiler's wait counts exact.
+template <bool GAIN>
+__device__ __forceinline__ void prep_load(const PrepArgs& a, int bh, int cc, bool has, int tid, int lane,
+                                          PrepIn<GAIN>& x) {
+  const size_t head_tok = (size_t)bh * a.L;
+  const size_t rows = has ? (size_t)a.L * DK * 2 : 0;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(a.k + head_tok * DK, rows);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int seg = tid + NT * i, row = seg >> 4, c8 = seg & 15;
+    const int off = ((cc * C + row) * DK + c8 * 8) * 2;
+    x.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+    if (GAIN) {
+      const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + head_tok * DK, rows);
+      const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gain + head_tok * DK, rows);
+      x.q[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
+      x.g[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+    }
+  }
+  const int toff = (cc * C + lane) * 4;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.alpha + (a.alpha ? head_tok : 0), has && a.alpha ? (size_t)a.L * 4 : 0);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.beta + (a.beta ? head_tok : 0), has && a.beta ? (size_t)a.L * 4 : 0);
+  x.al = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, toff, 0, 0));
+  x.be = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, toff, 0, 0));
+}
+
+template <bool GAIN>
 __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
-  const bool gain = a.gain != nullptr;
+  constexpr bool gain = GAIN;
   unsigned char* p = lds_raw;
   _Float16* sQ = reinterpret_cast<_Float16*>(p);   // [C][KP] (phases 1-2)
   _Float16* sT = reinterpret_cast<_Float16*>(p);   // [C][CP] (phases 3-5, reuses sQ)
@@ -202,211 +245,242 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   float* sLg = reinterpret_cast<float*>(p);        // [C] log2 of g
   float* sBs = sLg + C;                            // [C] write scale
 
-  const int bh = blockIdx.x, c = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int r16 = lane & 15, kq = lane >> 4, k8 = kq * 8;
-  const int c0 = c * C, n = min(C, a.L - c0);
-  const size_t tok = (size_t)bh * a.L + c0;
-  unsigned char* rec = a.rec + ((size_t)bh * a.nchunks + c) * rec_bytes(gain);
+  const int bh = blockIdx.x;
+  const int cbeg = blockIdx.y * a.cpw, cend = min(cbeg + a.cpw, a.nchunks);
 
-  // phase 1: stage K (and for the Kalman writes Q and the gains) as fp16;
-  // per-token scalars
+  PrepIn<GAIN> in;
+  prep_load<GAIN>(a, bh, cbeg, true, threadIdx.x, threadIdx.x & 63, in);
+  // As many stores as a chunk issues after its next chunk's loads (3 scalar
+  // pieces, 2 rounds of T and P pieces), all dropped (range 0): the wait for a
+  // chunk's inputs is then the same on entry as around the loop, and the
+  // compiler does not fall back to waiting for every store in flight.
+  {
+    const __amdgpu_buffer_rsrc_t none = make_rsrc(a.rec, 0);
+    const v4u32 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int seg = tid + NT * i, row = seg >> 4, c8 = seg & 15;
-    uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, gv = qv;
-    if (row < n) {
-      const size_t off = (tok + row) * DK + c8 * 8;
-      kv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.k + off));
-      if (gain) {
-        qv = bf16x8_to_f16x8(*reinterpret_cast<const uint4*>(a.q + off));
-        gv = *reinterpret_cast<const uint4*>(a.gain + off);
+    for (int i = 0; i < 3 + 2 * (GAIN ? 2 : 1); ++i) __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
+  }
+  for (int c = cbeg; c < cend; ++c) {
+    // The lane index passes through an empty asm statement each chunk: the
+    // compiler then forms the many LDS addresses that derive from it where they
+    // are used, instead of hoisting them out of the loop and holding them all
+    // in registers (which would cost occupancy or spill).
+    int lane_opaque = threadIdx.x & 63;
+    asm volatile("" : "+v"(lane_opaque));
+    const int lane = lane_opaque, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int tid = wave * 64 + lane;
+    const int r16 = lane & 15, kq = lane >> 4, k8 = kq * 8;
+    const int c0 = c * C, n = min(C, a.L - c0);
+    unsigned char* rec = a.rec + ((size_t)bh * a.nchunks + c) * rec_bytes(gain);
+
+    // phase 1: stage K (and for the Kalman writes Q and the gains) as fp16 from
+    // the registers, start loading the next chunk, per-token scalars
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int seg = tid + NT * i, row = seg >> 4, c8 = seg & 15;
+      *reinterpret_cast<uint4*>(sK + row * KP + c8 * 8) = bf16x8_to_f16x8(in.k[i]);
+      if (GAIN) {
+        *reinterpret_cast<uint4*>(sQ + row * KP + c8 * 8) = bf16x8_to_f16x8(in.q[GAIN ? i : 0]);
+        *reinterpret_cast<uint4*>(sB + row * KP + c8 * 8) = in.g[GAIN ? i : 0];
       }
     }
-    *reinterpret_cast<uint4*>(sK + row * KP + c8 * 8) = kv;
-    if (gain) {
-      *reinterpret_cast<uint4*>(sQ + row * KP + c8 * 8) = qv;
-      *reinterpret_cast<uint4*>(sB + row * KP + c8 * 8) = gv;
-    }
-  }
-  if (wave == 0) {
-    float la = 0.f, bs = 0.f, vs = 1.f;
-    if (lane < n) {
-      const float al = a.alpha ? a.alpha[tok + lane] : 1.f;
-      la = log2f(al);
-      bs = gain ? 1.f : a.beta[tok + lane];
-      if (a.plain) {  // plain residual = gated form with (beta / alpha, alpha v)
-        bs /= al;
-        vs = al;
+    const float al_in = in.al, be_in = in.be;
+    prep_load<GAIN>(a, bh, c + 1, c + 1 < cend, tid, lane, in);
+    // Every wavefront forms the scalars (token = lane); wavefront 0 keeps them
+    // in LDS and stores them. The record is written through buffer stores
+    // that every wavefront issues, the others at an offset past the record
+    // (dropped), so the number of stores in flight is the same on every path
+    // and the wait for the next chunk's loads does not include them.
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, rec_bytes(gain));
+    constexpr int kDrop = 1 << 30;  // past any record
+    {
+      float la = 0.f, bs = 0.f, vs = 1.f;
+      if (lane < n) {
+        const float al = a.alpha ? al_in : 1.f;
+        la = log2f(al);
+        bs = gain ? 1.f : be_in;
+        if (a.plain) {  // plain residual = gated form with (beta / alpha, alpha v)
+          bs /= al;
+          vs = al;
+        }
       }
+      const float lg = wave_prefix(la, lane);
+      const float lgn = __shfl(lg, n - 1, 64);
+      const float lg31 = __shfl(lg, 31, 64);
+      const float lgr = __shfl(lg, (lane & 32) + 15, 64);   // reference of this half
+      if (wave == 0) {
+        sLg[lane] = lg;
+        sBs[lane] = bs;
+      }
+      const float w = lane < n ? exp2f(lgn - lg) * bs : 0.f;
+      // exponents of R and Cf stay in [-100, 100] unless the decay is extreme
+      const float span = fabsf(lgr - lg);
+      const bool extreme = __ballot(span > 100.f) != 0;
+      // default (write-back) stores: the state kernel reads the records soon after
+      const int so = wave == 0 ? (int)rec_s_off(gain) + 48 * lane : kDrop;
+      const float4 s0 = make_float4(exp2f(lg), w, lg, bs);
+      const float4 s1 = make_float4(extreme ? 0.f : bs * exp2f(lgr - lg), extreme ? 0.f : exp2f(lg - lgr),
+                                    lane < 32 ? bs * exp2f(lg31 - lg) : 0.f,
+                                    lane >= 32 ? exp2f(lg - lg31) : 0.f);
+      const float4 s2 = make_float4(vs, extreme ? 1.f : 0.f, 0.f, 0.f);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s0), rr, so, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s1), rr, so + 16, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s2), rr, so + 32, 0, 0);
     }
-    const float lg = wave_prefix(la, lane);
-    const float lgn = __shfl(lg, n - 1, 64);
-    const float lg31 = __shfl(lg, 31, 64);
-    const float lgr = __shfl(lg, (lane & 32) + 15, 64);   // reference of this half
-    sLg[lane] = lg;
-    sBs[lane] = bs;
-    const float w = lane < n ? exp2f(lgn - lg) * bs : 0.f;
-    // exponents of R and Cf stay in [-100, 100] unless the decay is extreme
-    const float span = fabsf(lgr - lg);
-    const bool extreme = __ballot(span > 100.f) != 0;
-    // default (write-back) stores: the state kernel reads the records soon after
-    float4* sc = reinterpret_cast<float4*>(rec + rec_s_off(gain));
-    sc[3 * lane] = make_float4(exp2f(lg), w, lg, bs);
-    sc[3 * lane + 1] = make_float4(extreme ? 0.f : bs * exp2f(lgr - lg), extreme ? 0.f : exp2f(lg - lgr),
-                                   lane < 32 ? bs * exp2f(lg31 - lg) : 0.f,
-                                   lane >= 32 ? exp2f(lg - lg31) : 0.f);
-    sc[3 * lane + 2] = make_float4(vs, extreme ? 1.f : 0.f, 0.f, 0.f);
-  }
-  __syncthreads();
+    __syncthreads();
 
-  // phase 2: 20 lower Gram tiles, A (tiles 0-9) from K and P (tiles 10-19) from Q;
-  // wavefront w takes tiles w, w + 4, ..., w + 16.
-  floatx4 pacc[3];
-  int pti[3], ptj[3];
+    // phase 2: 20 lower Gram tiles, A (tiles 0-9) from K and P (tiles 10-19) from Q;
+    // wavefront w takes tiles w, w + 4, ..., w + 16.
+    floatx4 pacc[3];
+    int pti[3], ptj[3];
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    pacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
-    pti[j] = ptj[j] = -1;
-  }
-  int np = 0;
-#pragma unroll
-  for (int j = 0; j < 5; ++j) {
-    const int tl = wave + 4 * j;
-    const bool isP = tl >= 10;
-    if (isP && !gain) continue;
-    int ti, tj;
-    tile_ij(isP ? tl - 10 : tl, ti, tj);
-    const _Float16* srcA = isP ? sQ : sK;
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < DK / 32; ++ks)
-      acc = mfma(ld8(srcA + (16 * ti + r16) * KP + 32 * ks + k8),
-                 ld8(sB + (16 * tj + r16) * KP + 32 * ks + k8), acc);
-    const int col = 16 * tj + r16;
-    const float lgc = sLg[col], bsc = sBs[col];
-    const float4 lgr = *reinterpret_cast<const float4*>(sLg + 16 * ti + kq * 4);
-    const float lgrv[4] = {lgr.x, lgr.y, lgr.z, lgr.w};
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int row = 16 * ti + kq * 4 + jj;
-      const float e = __builtin_amdgcn_exp2f(fminf(lgrv[jj] - lgc, 0.f)) * bsc;
-      const bool keep = isP ? row >= col : row > col;
-      acc[jj] = keep ? acc[jj] * e : 0.f;
+    for (int j = 0; j < 3; ++j) {
+      pacc[j] = floatx4{0.f, 0.f, 0.f, 0.f};
+      pti[j] = ptj[j] = -1;
     }
-    if (isP) {
-      // wave-uniform slot index: tiles 10-19 of this wavefront in order
-      if (np == 0) { pacc[0] = acc; pti[0] = ti; ptj[0] = tj; }
-      else if (np == 1) { pacc[1] = acc; pti[1] = ti; ptj[1] = tj; }
-      else { pacc[2] = acc; pti[2] = ti; ptj[2] = tj; }
-      ++np;
-    } else {
+    int np = 0;
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+      const int tl = wave + 4 * j;
+      const bool isP = tl >= 10;
+      if (isP && !gain) continue;
+      int ti, tj;
+      tile_ij(isP ? tl - 10 : tl, ti, tj);
+      const _Float16* srcA = isP ? sQ : sK;
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < DK / 32; ++ks)
+        acc = mfma(ld8(srcA + (16 * ti + r16) * KP + 32 * ks + k8),
+                   ld8(sB + (16 * tj + r16) * KP + 32 * ks + k8), acc);
+      const int col = 16 * tj + r16;
+      const float lgc = sLg[col], bsc = sBs[col];
+      const float4 lgr = *reinterpret_cast<const float4*>(sLg + 16 * ti + kq * 4);
+      const float lgrv[4] = {lgr.x, lgr.y, lgr.z, lgr.w};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int row = 16 * ti + kq * 4 + jj;
-        sAh[row * CP + col] = (_Float16)acc[jj];
-        if (ti == tj) sAd[(ti * 16 + (row & 15)) * kAdP + (col & 15)] = acc[jj];
+        const float e = __builtin_amdgcn_exp2f(fminf(lgrv[jj] - lgc, 0.f)) * bsc;
+        const bool keep = isP ? row >= col : row > col;
+        acc[jj] = keep ? acc[jj] * e : 0.f;
       }
-    }
-  }
-  __syncthreads();
-  // P tiles into LDS (sK is free now)
+      if (isP) {
+        // wave-uniform slot index: tiles 10-19 of this wavefront in order
+        if (np == 0) { pacc[0] = acc; pti[0] = ti; ptj[0] = tj; }
+        else if (np == 1) { pacc[1] = acc; pti[1] = ti; ptj[1] = tj; }
+        else { pacc[2] = acc; pti[2] = ti; ptj[2] = tj; }
+        ++np;
+      } else {
 #pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    if (pti[j] >= 0) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
-        sP[(16 * pti[j] + kq * 4 + jj) * CP + 16 * ptj[j] + r16] = (_Float16)pacc[j][jj];
-    }
-  }
-
-  // phase 3: diagonal blocks D_b = (I + A_bb)^-1 in float32.
-  // Lane (j = lane / 4, q = lane % 4) owns rows 4q..4q+3 of column j.
-  {
-    const int b = wave, j = lane >> 2, q = lane & 3;
-    float am[16][4];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) am[i][m] = sAd[(b * 16 + i) * kAdP + 4 * q + m];
-    float x[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) x[m] = (4 * q + m == j) ? 1.f : 0.f;
-#pragma unroll
-    for (int i = 1; i < 16; ++i) {
-      float s = am[i][0] * x[0];
-      s = fmaf(am[i][1], x[1], s);
-      s = fmaf(am[i][2], x[2], s);
-      s = fmaf(am[i][3], x[3], s);
-      s += dpp_xor1(s);
-      s += dpp_xor2(s);
-      const float t = (i == j ? 1.f : 0.f) - s;
-      if ((i >> 2) == q) x[i & 3] = t;
-    }
-    const int r0 = 16 * b + 4 * q, cc = 16 * b + j;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) sT[(r0 + m) * CP + cc] = (_Float16)x[m];
-    floatx4 xv = {x[0], x[1], x[2], x[3]};
-    st4(sTt + cc * CP + r0, xv);
-  }
-  __syncthreads();
-
-  // phase 4: off-diagonal blocks, one diagonal at a time.
-  {
-    _Float16* myM = sM + wave * 16 * 24;
-    const half8 zero8 = {};
-    for (int d = 1; d < 4; ++d) {
-      const int i = wave + d, j = wave;
-      const bool active = wave < 4 - d;
-      if (active) {
-        // M = sum_{k=j}^{i-1} A_ik T_kj  (contraction over columns [16j, 16i))
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int kb = 16 * j; kb < 16 * i; kb += 32) {
-          const int kk = kb + k8;
-          const bool ok = kk < 16 * i;
-          const half8 av = ok ? ld8(sAh + (16 * i + r16) * CP + kk) : zero8;
-          const half8 bv = ok ? ld8(sTt + (16 * j + r16) * CP + kk) : zero8;
-          acc = mfma(av, bv, acc);
+        for (int jj = 0; jj < 4; ++jj) {
+          const int row = 16 * ti + kq * 4 + jj;
+          sAh[row * CP + col] = (_Float16)acc[jj];
+          if (ti == tj) sAd[(ti * 16 + (row & 15)) * kAdP + (col & 15)] = acc[jj];
         }
-        st4(myM + r16 * 24 + kq * 4, acc);  // M^T[col][rows]
       }
-      __syncthreads();
-      if (active) {
-        // T_ij = -D_i M
-        const bool ok = kq < 2;
-        const half8 av = ok ? ld8(sT + (16 * i + r16) * CP + 16 * i + k8) : zero8;
-        const half8 bv = ok ? ld8(myM + r16 * 24 + k8) : zero8;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = mfma(av, bv, acc);
-        acc = -acc;
-        const int row0 = 16 * i + kq * 4, col = 16 * j + r16;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) sT[(row0 + jj) * CP + col] = (_Float16)acc[jj];
-        st4(sTt + col * CP + row0, acc);
-      }
-      __syncthreads();
     }
-  }
+    __syncthreads();
+    // P tiles into LDS (sK is free now)
+#pragma unroll
+    for (int j = 0; j < 3; ++j) {
+      if (pti[j] >= 0) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          sP[(16 * pti[j] + kq * 4 + jj) * CP + 16 * ptj[j] + r16] = (_Float16)pacc[j][jj];
+      }
+    }
 
-  // phase 5: T (and P) to the record in three-block form
-  _Float16* tdst = reinterpret_cast<_Float16*>(rec + kRecT);
-  _Float16* pdst = reinterpret_cast<_Float16*>(rec + rec_p_off(gain));
-  {
-    // each block is 32 rows x 64 bytes = 128 pieces of 16 bytes; 3 blocks = 384 pieces
-    for (int seg = tid; seg < 384; seg += NT) {
-      const int blk = seg >> 7, brow = (seg >> 2) & 31, piece = seg & 3;
+    // phase 3: diagonal blocks D_b = (I + A_bb)^-1 in float32.
+    // Lane (j = lane / 4, q = lane % 4) owns rows 4q..4q+3 of column j.
+    {
+      const int b = wave, j = lane >> 2, q = lane & 3;
+      float am[16][4];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) am[i][m] = sAd[(b * 16 + i) * kAdP + 4 * q + m];
+      float x[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) x[m] = (4 * q + m == j) ? 1.f : 0.f;
+#pragma unroll
+      for (int i = 1; i < 16; ++i) {
+        float s = am[i][0] * x[0];
+        s = fmaf(am[i][1], x[1], s);
+        s = fmaf(am[i][2], x[2], s);
+        s = fmaf(am[i][3], x[3], s);
+        s += dpp_xor1(s);
+        s += dpp_xor2(s);
+        const float t = (i == j ? 1.f : 0.f) - s;
+        if ((i >> 2) == q) x[i & 3] = t;
+      }
+      const int r0 = 16 * b + 4 * q, cc = 16 * b + j;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) sT[(r0 + m) * CP + cc] = (_Float16)x[m];
+      floatx4 xv = {x[0], x[1], x[2], x[3]};
+      st4(sTt + cc * CP + r0, xv);
+    }
+    __syncthreads();
+
+    // phase 4: off-diagonal blocks, one diagonal at a time.
+    {
+      _Float16* myM = sM + wave * 16 * 24;
+      const half8 zero8 = {};
+      for (int d = 1; d < 4; ++d) {
+        const int i = wave + d, j = wave;
+        const bool active = wave < 4 - d;
+        if (active) {
+          // M = sum_{k=j}^{i-1} A_ik T_kj  (contraction over columns [16j, 16i))
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int kb = 16 * j; kb < 16 * i; kb += 32) {
+            const int kk = kb + k8;
+            const bool ok = kk < 16 * i;
+            const half8 av = ok ? ld8(sAh + (16 * i + r16) * CP + kk) : zero8;
+            const half8 bv = ok ? ld8(sTt + (16 * j + r16) * CP + kk) : zero8;
+            acc = mfma(av, bv, acc);
+          }
+          st4(myM + r16 * 24 + kq * 4, acc);  // M^T[col][rows]
+        }
+        __syncthreads();
+        if (active) {
+          // T_ij = -D_i M
+          const bool ok = kq < 2;
+          const half8 av = ok ? ld8(sT + (16 * i + r16) * CP + 16 * i + k8) : zero8;
+          const half8 bv = ok ? ld8(myM + r16 * 24 + k8) : zero8;
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc = mfma(av, bv, acc);
+          acc = -acc;
+          const int row0 = 16 * i + kq * 4, col = 16 * j + r16;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) sT[(row0 + jj) * CP + col] = (_Float16)acc[jj];
+          st4(sTt + col * CP + row0, acc);
+        }
+        __syncthreads();
+      }
+    }
+
+    // phase 5: T (and P) to the record in three-block form. Each block is 32
+    // rows x 64 bytes = 128 pieces of 16 bytes, 384 pieces in all: two rounds
+    // over the workgroup, the second one's pieces past 384 dropped.
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+      const int seg = tid + NT * round;
+      const bool ok = seg < 384;
+      const int sg = ok ? seg : seg - NT;  // a piece to read; its store is dropped
+      const int blk = sg >> 7, brow = (sg >> 2) & 31, piece = sg & 3;
       const int row = (blk == 0 ? 0 : 32) + brow, col = (blk == 2 ? 32 : 0) + 8 * piece;
+      const int off = ok ? 2 * (blk * 1024 + brow * 32 + 8 * piece) : kDrop;
       // 16 x 16 blocks above the diagonal were never written: zeros
       const bool lower = (col >> 4) <= (row >> 4);
       uint4 tv = *reinterpret_cast<const uint4*>(sT + row * CP + col);
       if (!lower) tv = make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4*>(tdst + blk * 1024 + brow * 32 + 8 * piece) = tv;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, tv), rr, (int)kRecT + off, 0, 0);
       if (gain) {
         uint4 pv = *reinterpret_cast<const uint4*>(sP + row * CP + col);
         if (!lower) pv = make_uint4(0, 0, 0, 0);
-        *reinterpret_cast<uint4*>(pdst + blk * 1024 + brow * 32 + 8 * piece) = pv;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, pv), rr,
+                                               ok ? (int)rec_p_off(gain) + off : kDrop, 0, 0);
       }
     }
+    __syncthreads();  // the next chunk's staging overwrites sT, sP and the scalars
   }
 }
 
@@ -462,7 +536,6 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef uint32_t v2u32 __attribute__((ext_vector_type(2)));
-typedef uint32_t v4u32 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
 __device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
@@ -1162,6 +1235,14 @@ size_t scan_mfma_workspace_bytes(int BH, int L, bool gain) {
   return (size_t)BH * nchunks * rec_bytes(gain);
 }
 
+// Chunks per prepare workgroup: about one chunk per workgroup that fits on the
+// chip at once (256 CUs x 4) per pass, so the next chunk's loads overlap the
+// current chunk's work, at most 8.
+int prep_chunks_per_workgroup(int BH, int nchunks) {
+  const long long units = (long long)BH * nchunks;
+  return (int)std::min<long long>(8, std::max<long long>(1, units / 1024));
+}
+
 hipError_t launch_tinv_mfma(const ScanArgs& s, void* tbuf, hipStream_t st) {
   const int nchunks = (s.L + C - 1) / C;
   const bool gain = s.gain != nullptr;
@@ -1175,11 +1256,13 @@ hipError_t launch_tinv_mfma(const ScanArgs& s, void* tbuf, hipStream_t st) {
   pa.L = s.L;
   pa.nchunks = nchunks;
   pa.plain = s.plain;
+  pa.cpw = prep_chunks_per_workgroup(s.BH, nchunks);
   const size_t lds = prep_lds_bytes(gain);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel),
+  auto kern = gain ? prep_kernel<true> : prep_kernel<false>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prep_kernel, dim3(s.BH, nchunks), dim3(NT), lds, st, pa);
+  hipLaunchKernelGGL(kern, dim3(s.BH, (nchunks + pa.cpw - 1) / pa.cpw), dim3(NT), lds, st, pa);
   return hipGetLastError();
 }
 

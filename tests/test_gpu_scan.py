@@ -118,6 +118,30 @@ def test_short_sequences(kdn, orc):
             assert_close(got["S"], ref["S"], TOL_BF16, f"S L {L}")
 
 
+@pytest.mark.parametrize("mode", ["delta", "diag"])
+def test_grouped_prepare(kdn, orc, mode):
+    """Enough (head, chunk) pairs that the prepare step hands each workgroup
+    several consecutive chunks (here 4), with a chunk count the group size does
+    not divide and a ragged last chunk: B=2, H=32, L=4100 is 65 chunks, the
+    last of 4 tokens. The delta write and the diagonal Kalman write (which also
+    stages Q and the gains); the oracle on sampled heads."""
+    B, H, L, d = 2, 32, 4100, 128
+    diag = mode == "diag"
+    inp = workloads.scan_inputs(B, H, L, d, d, seed=111, dtype="bf16", with_r=diag)
+    cov0 = np.ones((B, H, d), np.float32) if diag else None
+    got = _scan_gpu(kdn, inp, "bf16", 64, mode=mode, cov0=cov0, qvar=1.0 if diag else 0.0)
+    for (b, h) in [(0, 0), (1, 17), (1, 31)]:
+        log(f"grouped prepare {mode}: oracle on head ({b}, {h})")
+        sub = {n: (x[b:b + 1, h:h + 1] if x is not None else None) for n, x in inp.items()}
+        ref = orc.scan(sub["q"], sub["k"], sub["v"], alpha=sub["alpha"], beta=sub["beta"],
+                       r=sub["r"], cov0=None if cov0 is None else cov0[b:b + 1, h:h + 1],
+                       q_noise_var=1.0 if diag else 0.0, mode=mode, want_m=False)
+        assert_close(got["o"][b:b + 1, h:h + 1], ref["o"], TOL_BF16, f"{mode} o head {(b, h)}")
+        assert_close(got["S"][b:b + 1, h:h + 1], ref["S"], TOL_BF16, f"{mode} S head {(b, h)}")
+        if diag:
+            assert_close(got["cov"][b:b + 1, h:h + 1], ref["cov"], TOL_F32, f"p head {(b, h)}")
+
+
 def test_split_sequence_resume(kdn, orc):
     """Scanning [0, L) equals scanning [0, L1) and resuming [L1, L) from the
     returned state."""
