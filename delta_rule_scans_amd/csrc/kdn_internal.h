@@ -14,11 +14,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 }
 
 // Round to nearest, ties to even; NaN stays a quiet NaN.
+// Two floats -> two bf16 (lo in the low half), round to nearest even, in one
+// v_cvt_pk_bf16_f32.
+typedef float kdn_float2v __attribute__((ext_vector_type(2)));
+typedef __bf16 kdn_bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(kdn_float2v{lo, hi}, kdn_bf16x2v));
+}
+// One float -> bf16 bits, round to nearest even.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end read 0,

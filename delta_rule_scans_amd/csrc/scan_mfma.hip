@@ -1037,25 +1037,39 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         if constexpr (GAIN) q_load(rq, b, min(cc + 2, last), lane);
         // o[tb] registers 4 q .. 4 q + 3: token 32 tb + c32, columns 8 q + 4 h .. + 4
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int tb = 0; tb < 2; ++tb) {
+          const int tok = cc * C + 32 * tb + c32;
+          if constexpr (OBF16) {
+            // Lanes l and l ^ 32 hold the two 8-byte halves of each 16-byte
+            // piece of bf16 columns. One lane swap per dword gives lane h the
+            // whole pieces of column groups pr + 2 h (pr = 0, 1): streaming
+            // stores stay 16 bytes (8-byte ones reach HBM as partial writes).
+            uint2 pk[4];
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int tok = cc * C + 32 * tb + c32;
-            const int off = (tok * a.dv + 8 * q4 + 4 * h) * esz;
-            if constexpr (OBF16) {
-              const uint32_t lo = (uint32_t)f32_to_bf16(o[tb][4 * q4]) |
-                                  ((uint32_t)f32_to_bf16(o[tb][4 * q4 + 1]) << 16);
-              const uint32_t hi = (uint32_t)f32_to_bf16(o[tb][4 * q4 + 2]) |
-                                  ((uint32_t)f32_to_bf16(o[tb][4 * q4 + 3]) << 16);
-              __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(v2u32, make_uint2(lo, hi)), ro, off, 0,
-                                                    kStreamStore);
-            } else {
+            for (int q4 = 0; q4 < 4; ++q4)
+              pk[q4] = make_uint2(pk_bf16(o[tb][4 * q4], o[tb][4 * q4 + 1]),
+                                  pk_bf16(o[tb][4 * q4 + 2], o[tb][4 * q4 + 3]));
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+              // lane h = 0 keeps its group pr and receives lane + 32's half of it;
+              // lane h = 1 receives lane - 32's half of group pr + 2 and keeps its own
+              const auto lo = __builtin_amdgcn_permlane32_swap(pk[pr].x, pk[pr + 2].x, false, false);
+              const auto hi = __builtin_amdgcn_permlane32_swap(pk[pr].y, pk[pr + 2].y, false, false);
+              const uint4 w4 = make_uint4(lo[0], hi[0], lo[1], hi[1]);
+              const int off = (tok * a.dv + 8 * (pr + 2 * h)) * esz;
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w4), ro, off, 0, kStreamStore);
+            }
+          } else {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              const int off = (tok * a.dv + 8 * q4 + 4 * h) * esz;
               const uint4 w4 = make_uint4(__float_as_uint(o[tb][4 * q4]), __float_as_uint(o[tb][4 * q4 + 1]),
                                           __float_as_uint(o[tb][4 * q4 + 2]), __float_as_uint(o[tb][4 * q4 + 3]));
               __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w4), ro, off, 0,
                                                      kStreamStore);
             }
           }
+        }
       }
       cs_prev = cs_prev + 1 == NCH ? 0 : cs_prev + 1;
       __syncthreads();

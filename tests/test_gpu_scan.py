@@ -211,6 +211,11 @@ def test_diag_kalman_small(kdn, orc, dtype):
         assert_close(got["o"], ref["o"], tol, "diag o")
         assert_close(got["S"], ref["S"], tol, "diag S")
         assert_close(got["cov"], ref["cov"], TOL_F32, "diag p")
+    # bf16 output (the Kalman form of the output stores): exactly the float32
+    # result rounded to nearest even
+    f32 = _scan_gpu(kdn, inp, dtype, 64, mode="diag", cov0=p0, qvar=1.0, out_dtype="f32", want_state=False)
+    b16 = _scan_gpu(kdn, inp, dtype, 64, mode="diag", cov0=p0, qvar=1.0, out_dtype="bf16", want_state=False)
+    np.testing.assert_array_equal(b16["o"], workloads.bf16_round(f32["o"].astype(np.float32)))
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
