@@ -774,20 +774,32 @@ __device__ __forceinline__ void prod_stage(const ProdCtx& x, const ProdBuf<GAIN>
 
 // ---- wavefront 1 (Kalman writes): Q rows of one chunk straight from global
 // memory, in operand k order.
+// Q rows of one chunk as the output wavefront's operands, loaded from global
+// memory two steps ahead (Kalman writes: no LDS is left for a Q stage). Lane
+// (h, m) loads the 16 bytes of columns 16 s + 8 h .. + 8 of token 32 tb + m;
+// q_operand swaps 8-byte halves with lane ^ 32 into the operand k order
+// (columns 16 s + 4 h .. + 4 and 16 s + 8 + 4 h .. + 4). Sixteen loads per
+// chunk instead of 32 eight-byte ones keep two chunks of loads plus the
+// stores between them under the 63 memory operations a wavefront can have in
+// flight.
 struct QBuf {
-  uint2 q[2][8][2];  // [token block][k step][low/high quad]
+  uint4 q[2][8];  // [token block][k step]
 };
 __device__ __forceinline__ void q_load(__amdgpu_buffer_rsrc_t rq, QBuf& b, int c, int lane) {
-  const int m = lane & 31, h4 = (lane >> 5) * 4;
+  const int m = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int tb = 0; tb < 2; ++tb) {
-    const int off = (c * C + 32 * tb + m) * (DK * 2) + h4 * 2;
+    const int off = (c * C + 32 * tb + m) * (DK * 2) + 16 * h;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      b.q[tb][s][0] = bload8(rq, off + 32 * s);
-      b.q[tb][s][1] = bload8(rq, off + 32 * s + 16);
-    }
+    for (int s = 0; s < 8; ++s) b.q[tb][s] = bload16(rq, off + 32 * s);
   }
+}
+__device__ __forceinline__ half8 q_operand(uint4 raw) {
+  // lane h = 0 keeps columns 0-3 and receives 8-11 from lane + 32; lane h = 1
+  // receives 4-7 from lane - 32 and keeps 12-15 (all relative to 16 s)
+  const auto d0 = __builtin_amdgcn_permlane32_swap(raw.x, raw.z, false, false);
+  const auto d1 = __builtin_amdgcn_permlane32_swap(raw.y, raw.w, false, false);
+  return cat(bf16x4_to_f16x4(make_uint2(d0[0], d1[0])), bf16x4_to_f16x4(make_uint2(d0[1], d1[1])));
 }
 
 template <bool GAIN, bool OBF16>
@@ -868,10 +880,27 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         make_rsrc(static_cast<unsigned char*>(a.o) + (head_tok * a.dv + j0) * esz,
                   ((size_t)a.L * a.dv - j0) * esz);
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + head_tok * DK, (size_t)a.L * DK * 2);
+    // residuals for the write scores: this (head, slice)'s chunks, or range 0
+    const __amdgpu_buffer_rsrc_t ru =
+        make_rsrc(a.ubuf + (a.ubuf ? (size_t)(bh * a.ntiles + tile) * a.nchunks * 256 : 0),
+                  a.ubuf ? (size_t)a.nchunks * 256 * 16 : 0);
     QBuf b0, b1;
+    // Kalman writes: every step runs the same memory operations (Q loads of
+    // chunk c + 1, 8 output stores (4 for bf16 outputs), 4 residual stores).
+    // On the steps without a chunk (the first, and the last when the chunk
+    // count is even) the outputs are formed from stale LDS data and their
+    // stores fall outside the buffers (dropped). With no branch around them,
+    // and the operations before the loop issued in the loop's order (Q of
+    // chunk 0, then dropped stores), the compiler's wait for a chunk's Q does
+    // not take in the loads issued one step later: measured, the state kernel
+    // of the diagonal Kalman write 191 -> 167 us. The delta write loads
+    // nothing here and skips the steps without a chunk.
     if constexpr (GAIN) {
       q_load(rq, b0, 0, lane);
-      q_load(rq, b1, min(1, last), lane);
+      const __amdgpu_buffer_rsrc_t none = make_rsrc(a.o, 0);
+      const v4u32 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < (OBF16 ? 4 : 8) + 4; ++i) __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
     }
     __syncthreads();
     int cs_prev = NCH - 1;  // chain stage of chunk c - 1
@@ -879,7 +908,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
     auto body = [&](int c, QBuf& b) {
       __builtin_amdgcn_sched_barrier(0);
       const int cc = c - 1;
-      if (cc >= 0 && cc <= last) {
+      if (GAIN || (cc >= 0 && cc <= last)) {
         const half8* ex = exch_at<GAIN>(lds_raw, cc & 1);
         const OutStage os = out_stage<GAIN>(lds_raw, cc & 1);
         const ChainStage cs = chain_stage<GAIN>(lds_raw, cs_prev);
@@ -887,7 +916,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         auto q_op = [&](int i) -> half8 {
           const int tb = i >> 3, s = i & 7;
           if constexpr (GAIN)
-            return cat(bf16x4_to_f16x4(b.q[tb][s][0]), bf16x4_to_f16x4(b.q[tb][s][1]));
+            return q_operand(b.q[tb][s]);
           else
             return ld_op(os.q + (32 * tb + c32) * KP + 16 * s, h);
         };
@@ -1028,11 +1057,13 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         o[1] = mfma32(uv[2], pa[4], o[1]);
         o[1] = mfma32(uv[3], pa[5], o[1]);
         __builtin_amdgcn_sched_barrier(0);
-        if (a.ubuf) {
-          // residuals U of this chunk and d_v slice, in wavefront-0 register order
-          half8* ub = a.ubuf + ((size_t)(bh * a.ntiles + tile) * a.nchunks + cc) * 256;
+        // residuals U of this chunk and d_v slice, in wavefront-0 register
+        // order (Kalman writes: issued, and dropped, without them too)
+        if (GAIN || a.ubuf) {
 #pragma unroll
-          for (int s = 0; s < 4; ++s) ub[s * 64 + lane] = uv[s];
+          for (int s = 0; s < 4; ++s)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, uv[s]), ru,
+                                                   (cc * 256 + s * 64 + lane) * 16, 0, 0);
         }
         if constexpr (GAIN) q_load(rq, b, min(cc + 2, last), lane);
         // o[tb] registers 4 q .. 4 q + 3: token 32 tb + c32, columns 8 q + 4 h .. + 4
