@@ -202,12 +202,15 @@ __device__ __forceinline__ size_t cc_off(int bh, int nch, int c) {
 __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float lds[];
   constexpr int LP = DP + 1;
-  float* sK = lds;                // [C][LP]
-  float* sQ = sK + C * LP;        // [C][LP]
-  float* sA = sQ + C * LP;        // [C][LC]
+  // A, T and the block scratch reuse the K and Q tiles once both Grams are in
+  // registers: 67 KB of LDS, two workgroups per CU
+  static_assert(2 * C * LC + 32 * 33 <= 2 * C * LP, "A, T, Y fit over K and Q");
+  float* sK = lds;                // [C][LP] (Grams)
+  float* sQ = sK + C * LP;        // [C][LP] (Grams)
+  float* sA = lds;                // [C][LC] (after the Grams)
   float* sT = sA + C * LC;        // [C][LC]
   float* sY = sT + C * LC;        // [32][33]
-  float* sLg = sY + 32 * 33;
+  float* sLg = lds + 2 * C * LP;
   float* sB = sLg + C;
   float* sAl = sB + C;
   const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, nch = gridDim.y;
@@ -219,7 +222,6 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
     fetch_rows<NT>(fk, a.k + tok * dk, n, dk);
     fetch_rows<NT>(fq, a.q + tok * dk, n, dk);
     const Scal sc = fetch_scalars(a, tok, n);
-    for (int idx = tid; idx < C * LC; idx += NT) sT[idx] = 0.f;
     put_rows<NT, LP>(fk, sK);
     put_rows<NT, LP>(fq, sQ);
     put_scalars(a, sc, sLg, sB, sAl);
@@ -229,6 +231,8 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   floatx4 kk[4] = {}, qk[4] = {};
   mfma_row<4>(kk, sK, LP, 1, nullptr, sK, 1, LP, 16 * w, dk64);
   mfma_row<4>(qk, sQ, LP, 1, nullptr, sK, 1, LP, 16 * w, dk64);
+  __syncthreads();  // every wavefront is done with K and Q
+  for (int idx = tid; idx < C * LC; idx += NT) sT[idx] = 0.f;
   float* Ag = a.Am + cc_off(bh, nch, c);
   float* Pg = a.Pm + cc_off(bh, nch, c);
 #pragma unroll
@@ -834,8 +838,7 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
   const int nch = (a.L + C - 1) / C, ntw = (a.dv + TW - 1) / TW;
   const size_t f = sizeof(float);
   hipError_t e;
-  e = launch_lds(bwd_prep_kernel, dim3(a.BH, nch), NT,
-                 (2 * C * (DP + 1) + 2 * C * LC + 32 * 33 + 3 * C) * f, a, s);
+  e = launch_lds(bwd_prep_kernel, dim3(a.BH, nch), NT, (2 * C * (DP + 1) + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
   e = launch_lds(bwd_fwd_kernel, dim3(a.BH, ntw), NTC,
                  (C * LKC + C * LCC + DP * LOC + 2 * C * LOC + 3 * C) * f, a, s);
