@@ -142,6 +142,35 @@ def test_grouped_prepare(kdn, orc, mode):
             assert_close(got["cov"][b:b + 1, h:h + 1], ref["cov"], TOL_F32, f"p head {(b, h)}")
 
 
+def test_misaligned_buffers(kdn, orc):
+    """bf16 q, k, v and the output as views at a one-element offset (2 bytes:
+    not 16-byte aligned): the matrix-core kernels need 16-byte rows, so these
+    run on the general float32 kernel. Same oracle bar, and the output agrees
+    with the aligned run to the bf16 tolerance."""
+    import torch
+    B, H, L, d = 1, 2, 130, 128
+    inp = workloads.scan_inputs(B, H, L, d, d, seed=112, dtype="bf16")
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"])
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        view = buf[1:].view(t.shape)
+        view.copy_(t)
+        return view
+
+    q, k, v = (shifted(dev_tensor(inp[n], "bf16")) for n in ("q", "k", "v"))
+    o = shifted(torch.zeros((B, H, L, d), dtype=torch.float32, device="cuda"))
+    assert all(t.data_ptr() % 16 != 0 for t in (q, k, v, o))
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device="cuda")
+    kdn.kdn_scan_fwd(q, k, v, alpha=dev_tensor(inp["alpha"]), beta=dev_tensor(inp["beta"]),
+                     state_out=S, o=o)
+    torch.cuda.synchronize()
+    assert_close(host(o), ref["o"], TOL_BF16, "misaligned o")
+    assert_close(host(S), ref["S"], TOL_BF16, "misaligned S")
+    aligned = _scan_gpu(kdn, inp, "bf16", 64)
+    assert_close(host(o), aligned["o"], TOL_BF16, "misaligned vs aligned o")
+
+
 def test_split_sequence_resume(kdn, orc):
     """Scanning [0, L) equals scanning [0, L1) and resuming [L1, L) from the
     returned state."""
