@@ -404,7 +404,7 @@ def main():
                          "(for profiling; not the benchmark line)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
               "the scan shards over heads with no communication, see the design notes",
               file=sys.stderr)
         sys.exit(2)

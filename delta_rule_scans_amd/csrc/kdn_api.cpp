@@ -82,7 +82,7 @@ KDN_EXPORT const char* kdn_status_string(int status) {
     case KDN_ERR_BAD_CHUNK: return "chunk must be 16, 32 or 64";
     case KDN_ERR_BAD_MODE: return "unknown write mode or residual form, or plain residual with a Kalman gain";
     case KDN_ERR_BAD_DTYPE: return "unknown element type";
-    case KDN_ERR_UNSUPPORTED: return "valid arguments that this build does not implement (e.g. full covariance with d_k > 64)";
+    case KDN_ERR_UNSUPPORTED: return "valid arguments that this library does not implement (e.g. full covariance with d_k > 64)";
     case KDN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than kdn_scan_workspace_size";
     case KDN_ERR_BAD_CAPACITY: return "cache capacity w must be in [1, 256]";
     case KDN_ERR_BAD_ALIGNMENT: return "a pointer is not 16-byte aligned";

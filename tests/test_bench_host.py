@@ -48,10 +48,8 @@ def test_decode_bytes_per_head():
     its scores and positions read (512 B), the token's q, k, v, alpha, beta
     (1544 B), o and o_cache written with the score written and read back
     (1032 B), and the insert: key and value rows, score and position, the
-    fill count read and written (1040 B): 200736 B, 12 B per head above the
-    survey's byte model (200724 B)."""
+    fill count read and written (1040 B): 200736 B."""
     assert bench.DECODE_BYTES_PER_HEAD == 131072 + 65536 + 512 + 1544 + 1032 + 1040 == 200_736
-    assert bench.DECODE_BYTES_PER_HEAD == pytest.approx(200_724, rel=1e-4)
 
 
 def test_code_digest_ignores_comments_and_whitespace(tmp_path):
