@@ -24,6 +24,8 @@
 namespace kdn {
 namespace {
 
+constexpr int kGainBatch = 16;  // tokens whose inputs are loaded together
+
 // Map of one token on (p, 1), projectively: p_new = (m00 p + m01) / (m10 p + m11).
 // From p- = a^2 p + Q and p_new = r p- / (k^2 p- + r). All entries are >= 0,
 // so products never cancel.
@@ -53,18 +55,30 @@ __global__ __launch_bounds__(128) void diag_maps_kernel(const Tk* k, const float
   __syncthreads();
   if (i >= dk) return;
   float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f;
-  for (int t = 0; t < n; ++t) {
-    const size_t g = (size_t)bh * L + t0 + t;
-    float t00, t01, t10, t11;
-    token_map(sa[t], qvar, sr[t], Elem<Tk>::load(k, g * dk + i), t00, t01, t10, t11);
-    const float n00 = fmaf(t00, m00, t01 * m10), n01 = fmaf(t00, m01, t01 * m11);
-    const float n10 = fmaf(t10, m00, t11 * m10), n11 = fmaf(t10, m01, t11 * m11);
-    // projective scale: any positive factor will do, so an approximate reciprocal
-    const float sc = __builtin_amdgcn_rcpf(fmaxf(fmaxf(n00, n01), fmaxf(n10, n11)));
-    m00 = n00 * sc;
-    m01 = n01 * sc;
-    m10 = n10 * sc;
-    m11 = n11 * sc;
+  // k of a batch of tokens loaded together (tokens past the chunk read token
+  // n - 1 and are not used): one memory latency per batch
+  for (int tb = 0; tb < n; tb += kGainBatch) {
+    float kv[kGainBatch];
+#pragma unroll
+    for (int u = 0; u < kGainBatch; ++u)
+      kv[u] = Elem<Tk>::load(k, ((size_t)bh * L + t0 + min(tb + u, n - 1)) * dk + i);
+#pragma unroll
+    for (int u = 0; u < kGainBatch; ++u) {
+      // every token of the batch is formed (t < 64 stays inside sa, sr); only
+      // those inside the chunk are applied, so the loads stay ahead of all uses
+      const int t = tb + u;
+      const bool in = t < n;
+      float t00, t01, t10, t11;
+      token_map(sa[t], qvar, sr[t], kv[u], t00, t01, t10, t11);
+      const float n00 = fmaf(t00, m00, t01 * m10), n01 = fmaf(t00, m01, t01 * m11);
+      const float n10 = fmaf(t10, m00, t11 * m10), n11 = fmaf(t10, m01, t11 * m11);
+      // projective scale: any positive factor will do, so an approximate reciprocal
+      const float sc = __builtin_amdgcn_rcpf(fmaxf(fmaxf(n00, n01), fmaxf(n10, n11)));
+      m00 = in ? n00 * sc : m00;
+      m01 = in ? n01 * sc : m01;
+      m10 = in ? n10 * sc : m10;
+      m11 = in ? n11 * sc : m11;
+    }
   }
   maps[((size_t)bh * nchunks + c) * dk + i] = make_float4(m00, m01, m10, m11);
 }
@@ -97,9 +111,19 @@ __global__ __launch_bounds__(128) void diag_prefix_kernel(const float* cov_in, f
 // s_t = r_t + sum_i p-_i k_i^2 is a wavefront reduction, so the gains of token
 // t are written as soon as it is done. No LDS and no barriers, so many
 // wavefronts per SIMD hide the memory latency.
+// Sum over the 64 lanes, every lane gets it (all 64 lanes must be active):
+// quad steps by DPP, 4-16 by swizzles within each half, the halves by one
+// lane swap.
 __device__ __forceinline__ float wave_sum64(float x) {
-  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));  // ^1
+  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));  // ^2
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (4 << 10)));
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (8 << 10)));
+  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (16 << 10)));
+  // after the swap, lanes 0-31 find the upper half's value in the second
+  // result and lanes 32-63 the lower half's in the first
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return x + __uint_as_float(__lane_id() < 32 ? sw[1] : sw[0]);
 }
 
 template <typename Tk, typename Tg>
@@ -125,11 +149,13 @@ __global__ __launch_bounds__(256) void diag_gains_kernel(const Tk* k, const floa
     const float k1 = ok1 ? Elem<Tk>::load(k, g * dk + i1) : 0.f;
     const float pm0 = fmaf(a2, p0, Q), pm1 = fmaf(a2, p1, Q);
     const float pk0 = pm0 * k0, pk1 = pm1 * k1;
-    const float inv = 1.f / (rt + wave_sum64(fmaf(pk0, k0, pk1 * k1)));
+    // reciprocals by v_rcp_f32 (1 ulp): the kernel is bound by its
+    // instruction count, and exact divisions are ten instructions each
+    const float inv = __builtin_amdgcn_rcpf(rt + wave_sum64(fmaf(pk0, k0, pk1 * k1)));
     if (ok0) Elem<Tg>::store(gains, g * dk + i0, pk0 * inv);
     if (ok1) Elem<Tg>::store(gains, g * dk + i1, pk1 * inv);
-    p0 = pm0 * rt / fmaf(pk0, k0, rt);
-    p1 = pm1 * rt / fmaf(pk1, k1, rt);
+    p0 = pm0 * rt * __builtin_amdgcn_rcpf(fmaf(pk0, k0, rt));
+    p1 = pm1 * rt * __builtin_amdgcn_rcpf(fmaf(pk1, k1, rt));
   }
   if (c == nchunks - 1 && cov_out) {
     if (ok0) cov_out[(size_t)bh * dk + i0] = p0;
