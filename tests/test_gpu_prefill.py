@@ -90,6 +90,20 @@ def test_prefill_small(kdn, orc, dtype):
                       None if init is None else (init, rng))
 
 
+def test_prefill_max_capacity(kdn, orc):
+    """The largest capacity the library takes (w = 256): a cache partly full
+    (200) and a full one, blocks of 128 and 300, with exact score ties."""
+    rng = np.random.Generator(np.random.PCG64(304))
+    B, H, L, d, w = 1, 2, 600, 64, 256
+    q = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    k = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    v = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    m = (np.round(rng.uniform(0, 3, (B, H, L)) * 8) / 8).astype(np.float32)
+    for block, init in ((128, 200), (300, 256)):
+        log(f"prefill w {w} block {block} init {init}")
+        _prefill_case(kdn, orc, q, k, v, m, 7, block, w, "f32", None, (init, rng))
+
+
 def test_prefill_recency(kdn, orc):
     """The recency control (A Hippocampus for Linear Attention, sec. 4.5) over a prompt."""
     rng = np.random.Generator(np.random.PCG64(304))
