@@ -183,6 +183,7 @@ def test_diag_with_covariance_reset_is_delta(kdn):
 @pytest.mark.parametrize("B,H,dk,dv,w,steps,sink", [
     (48, 32, 128, 128, 12, 30, True),   # many heads, with a sink
     (2, 3, 64, 64, 80, 100, False),     # w > 64: more slots than a wavefront, evicting
+    (1, 2, 64, 64, 256, 300, True),     # the largest capacity: four slots per lane
     (2, 3, 30, 18, 6, 20, True),        # rows that are not whole 16-byte quads (scalar loads)
 ])
 def test_cache_kernel_forms(kdn, orc, B, H, dk, dv, w, steps, sink):
