@@ -142,6 +142,17 @@ def test_grouped_prepare(kdn, orc, mode):
             assert_close(got["cov"][b:b + 1, h:h + 1], ref["cov"], TOL_F32, f"p head {(b, h)}")
 
 
+@pytest.mark.parametrize("dv", [32, 96])
+def test_value_slices(kdn, orc, dv):
+    """d_v of one and of three 32-column slices on the matrix-core path, with
+    B*H = 16 (the XCD-aware block order with a slice count other than 4)."""
+    inp = workloads.scan_inputs(2, 8, 200, 128, dv, seed=113 + dv, dtype="bf16")
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"])
+    got = _scan_gpu(kdn, inp, "bf16", 64)
+    assert_close(got["o"], ref["o"], TOL_BF16, f"o d_v {dv}")
+    assert_close(got["S"], ref["S"], TOL_BF16, f"S d_v {dv}")
+
+
 def test_misaligned_buffers(kdn, orc):
     """bf16 q, k, v and the output as views at a one-element offset (2 bytes:
     not 16-byte aligned): the matrix-core kernels need 16-byte rows, so these
