@@ -474,6 +474,42 @@ def test_delta_exact_recall_unit_beta(orc):
         np.testing.assert_allclose(res["o"][0, 0], v[0, 0], rtol=1e-15, atol=0)
 
 
+@pytest.mark.parametrize("mode,resid", [("delta", "gated"), ("delta", "plain"), ("diag", "gated"),
+                                        ("iso", "gated"), ("full", "gated")])
+def test_split_scan_resumes_exactly(orc, mode, resid):
+    """The write is a first-order recursion in the memory S (and, for the
+    Kalman forms, its covariance): each token's update uses only the state
+    left by the token before (A Hippocampus for Linear Attention, eq. (5);
+    Kalman Delta Networks, abstract: a linear-Gaussian state-space model
+    filtered token by token). So a scan over
+    [0, L) equals a scan over [0, L1) followed by one over [L1, L) started from
+    the state and covariance the first returns, exactly: a returned state or
+    covariance taken before the last token's update fails this."""
+    B, H, L, L1, dk, dv = 1, 2, 23, 9, 6, 5
+    kal = mode != "delta"
+    inp = workloads.scan_inputs(B, H, L, dk, dv, seed=31, dtype="f32", with_r=kal)
+    rng = _rng(31)
+    cov0 = {"diag": rng.uniform(0.5, 2.0, (B, H, dk)),
+            "iso": rng.uniform(0.5, 2.0, (B, H)),
+            "full": np.eye(dk)[None, None] * rng.uniform(0.5, 2.0, (B, H, 1, 1))}.get(mode)
+    S0 = rng.standard_normal((B, H, dk, dv))
+    kw = dict(mode=mode, resid=resid, q_noise_var=0.3 if kal else 0.0)
+
+    def part(a, b, S, cov):
+        sl = {n: (x[:, :, a:b] if x is not None else None) for n, x in inp.items()}
+        return orc.scan(sl["q"], sl["k"], sl["v"], alpha=sl["alpha"],
+                        beta=None if kal else sl["beta"], r=sl["r"], cov0=cov, S0=S, **kw)
+
+    whole = part(0, L, S0, cov0)
+    first = part(0, L1, S0, cov0)
+    second = part(L1, L, first["S"], first["cov"])
+    np.testing.assert_array_equal(np.concatenate([first["o"], second["o"]], 2), whole["o"])
+    np.testing.assert_array_equal(second["S"], whole["S"])
+    np.testing.assert_array_equal(np.concatenate([first["m"], second["m"]], 2), whole["m"])
+    if kal:
+        np.testing.assert_array_equal(second["cov"], whole["cov"])
+
+
 def test_delta_noop_write(orc):
     """alpha = 1, beta = 0: the write Delta_t = beta k e^T (A Hippocampus for
     Linear Attention, eq. (5)) vanishes, S stays S_0 and o_t = S_0^T q_t."""
