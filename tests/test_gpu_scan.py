@@ -182,6 +182,25 @@ def test_misaligned_buffers(kdn, orc):
     assert_close(host(o), aligned["o"], TOL_BF16, "misaligned vs aligned o")
 
 
+@pytest.mark.parametrize("mode", ["diag", "iso"])
+def test_split_sequence_resume_kalman(kdn, orc, mode):
+    """The Kalman writes resumed from the returned state and covariance: [0, L)
+    against [0, L1) then [L1, L), both split points inside a chunk."""
+    B, H, L, L1, d = 1, 2, 333, 130, 128
+    inp = workloads.scan_inputs(B, H, L, d, d, seed=105, dtype="bf16", with_r=True)
+    cov0 = np.ones((B, H, d) if mode == "diag" else (B, H), np.float32)
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"], cov0=cov0,
+                   q_noise_var=1.0, mode=mode)
+    first = {n: (x[:, :, :L1] if x is not None else None) for n, x in inp.items()}
+    second = {n: (x[:, :, L1:] if x is not None else None) for n, x in inp.items()}
+    a = _scan_gpu(kdn, first, "bf16", 64, mode=mode, cov0=cov0, qvar=1.0)
+    b = _scan_gpu(kdn, second, "bf16", 64, mode=mode, cov0=a["cov"].astype(np.float32), qvar=1.0,
+                  S0=a["S"].astype(np.float32))
+    assert_close(np.concatenate([a["o"], b["o"]], 2), ref["o"], TOL_BF16, f"{mode} resumed o")
+    assert_close(b["S"], ref["S"], TOL_BF16, f"{mode} resumed S")
+    assert_close(b["cov"], ref["cov"], TOL_F32, f"{mode} resumed p")
+
+
 def test_split_sequence_resume(kdn, orc):
     """Scanning [0, L) equals scanning [0, L1) and resuming [L1, L) from the
     returned state."""
