@@ -310,6 +310,21 @@ def test_full_kalman_small(kdn, orc):
     assert_close(got["cov"], ref["cov"], TOL_F32, "full P")
 
 
+def test_full_kalman_largest_dk(kdn, orc):
+    """Full covariance at the largest d_k it takes (64), bf16 inputs, chunk 64,
+    a random positive-definite initial covariance."""
+    inp = workloads.scan_inputs(1, 2, 130, 64, 64, seed=109, dtype="bf16", with_r=True)
+    rng = np.random.Generator(np.random.PCG64(109))
+    A = rng.standard_normal((1, 2, 64, 64))
+    P0 = (np.einsum("bhij,bhkj->bhik", A, A) / 64 + np.eye(64)).astype(np.float32)
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"], cov0=P0,
+                   q_noise_var=0.5, mode="full")
+    got = _scan_gpu(kdn, inp, "bf16", 64, mode="full", cov0=P0, qvar=0.5)
+    assert_close(got["o"], ref["o"], TOL_BF16, "full o")
+    assert_close(got["S"], ref["S"], TOL_BF16, "full S")
+    assert_close(got["cov"], ref["cov"], TOL_F32, "full P")
+
+
 @pytest.mark.parametrize("mode,resid,dtype,dk", [("delta", "gated", "bf16", 128),
                                                  ("delta", "gated", "f32", 128),
                                                  ("delta", "plain", "bf16", 128),
