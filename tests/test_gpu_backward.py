@@ -48,6 +48,8 @@ def test_backward_small(kdn, orc, resid):
 
 def test_backward_odd_shapes(kdn, orc):
     _case(kdn, orc, 2, 1, 70, 40, 24, "gated", seed=402)
+    # several value tiles, the last one partial (100 = 3 x 32 + 4), full d_k
+    _case(kdn, orc, 1, 1, 200, 128, 100, "plain", seed=405)
 
 
 def test_backward_full_size(kdn, orc):
