@@ -244,6 +244,9 @@ def test_backward_rejections(kdn):
     assert _bwd(kdn, resid=3) == c["KDN_ERR_BAD_MODE"]
     assert _bwd(kdn, dk_=129) == c["KDN_ERR_BAD_SHAPE"]
     assert _bwd(kdn, L=-1) == c["KDN_ERR_BAD_SHAPE"]
+    # one workgroup row per 64-token chunk: at most 65535 chunks
+    assert _bwd(kdn, L=65536 * 64) == c["KDN_ERR_BAD_SHAPE"]
+    assert _bwd(kdn, L=65535 * 64) == c["KDN_ERR_WORKSPACE"]  # passes the shape checks
     assert _bwd(kdn, do=None) == c["KDN_ERR_NULL_POINTER"]
     assert _bwd(kdn, da=None) == c["KDN_ERR_NULL_POINTER"]
     assert _bwd(kdn) == c["KDN_ERR_WORKSPACE"]
