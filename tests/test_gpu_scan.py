@@ -201,6 +201,48 @@ def test_split_sequence_resume_kalman(kdn, orc, mode):
     assert_close(b["cov"], ref["cov"], TOL_F32, f"{mode} resumed p")
 
 
+@pytest.mark.parametrize("mode", ["delta", "diag"])
+def test_phases_on_two_streams(kdn, mode):
+    """kdn_scan_fwd_phase: the state-independent part enqueued on a second
+    stream, the state scan on the first after an event, one caller workspace:
+    the same outputs, state and covariance as one kdn_scan_fwd call, bit for bit."""
+    import torch
+    B, H, L, d = 2, 4, 300, 128
+    diag = mode == "diag"
+    inp = workloads.scan_inputs(B, H, L, d, d, seed=114, dtype="bf16", with_r=diag)
+    q, k, v = (dev_tensor(inp[n], "bf16") for n in ("q", "k", "v"))
+    alpha, beta = dev_tensor(inp["alpha"]), dev_tensor(inp["beta"])
+    r = dev_tensor(inp["r"]) if diag else None
+    kw = dict(alpha=alpha, beta=beta, r=r, mode=mode, q_noise_var=1.0 if diag else 0.0)
+    cov0 = torch.ones((B, H, d), device="cuda") if diag else None
+
+    def fresh():
+        return (torch.empty((B, H, d, d), device="cuda"),
+                torch.empty_like(cov0) if diag else None)
+
+    S1, c1 = fresh()
+    o1 = kdn.kdn_scan_fwd(q, k, v, state_out=S1, cov_in=cov0, cov_out=c1, **kw)
+    need = kdn.kdn_scan_workspace_size(B, H, L, d, d, 64, mode=mode)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    S2, c2 = fresh()
+    o2 = torch.empty_like(o1)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    done = torch.cuda.Event()
+    with torch.cuda.stream(side):
+        kdn.kdn_scan_fwd(q, k, v, state_out=S2, cov_in=cov0, cov_out=c2, o=o2, workspace=ws,
+                         phase="prepare", stream=side, **kw)
+        done.record(side)
+    torch.cuda.current_stream().wait_event(done)
+    kdn.kdn_scan_fwd(q, k, v, state_out=S2, cov_in=cov0, cov_out=c2, o=o2, workspace=ws,
+                     phase="state", **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(S1, S2)
+    if diag:
+        assert torch.equal(c1, c2)
+
+
 def test_split_sequence_resume(kdn, orc):
     """Scanning [0, L) equals scanning [0, L1) and resuming [L1, L) from the
     returned state."""
