@@ -12,8 +12,9 @@
 // covariances by keeping the diagonal of the precision (mean-field):
 //   p-_i = alpha^2 p_i + Q,  g_i = p-_i k_i / (sum_j p-_j k_j^2 + r),  p_i = p-_i r / (r + p-_i k_i^2).
 // Each coordinate's map p -> p_new is a linear-fractional (Moebius) map, so a
-// run of tokens composes into one 2x2 matrix (the abstract's "uncertainty
-// recurrences are Mobius maps"). The DIAG path uses that: one pass composes the
+// run of tokens composes into one 2x2 matrix ("Kalman Delta Networks:
+// Uncertainty-aware Associative Memory", abstract, where the variance
+// recursions are identified as Moebius maps). The DIAG path uses that: one pass composes the
 // maps of every chunk in parallel, a short sequential pass over chunks applies
 // them to get every chunk's starting variances, and a third pass recomputes the
 // per-token values of every chunk in parallel.

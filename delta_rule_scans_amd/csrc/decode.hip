@@ -3,6 +3,7 @@
 // "A Hippocampus for Linear Attention", sec. 3.3 eqs. (5)-(6) and sec. 3.5:
 //   e = v - alpha S^T k,  S <- alpha S + b e^T,  o = S^T q (after the write),
 //   m = ||b e^T||_F  (= beta ||e|| for the delta write with unit keys).
+// The plain residual is e = v - S^T k with the same update.
 // b = beta k (delta), the diagonal Kalman gain or the isotropic one ("Kalman
 // Delta Networks", abstract; the isotropic gain is p- k / (p- ||k||^2 + r) with
 // one variance per head, 1/p = 1/p- + ||k||^2 / (d_k r)). The read-out is
@@ -55,19 +56,13 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
   const bool diag = gmode == 1, iso = gmode == 2;
   const bool plain = resid == 1, noerase = resid == 2;
   const float a = alpha ? alpha[bh] : 1.f;
-  float bscale = 1.f, vscale = 1.f;
-  if (gmode == 0) {
-    bscale = beta[bh];
-    if (plain) {  // plain residual = gated form with (beta / alpha, alpha v)
-      bscale /= a;
-      vscale = a;
-    }
-  }
+  float bscale = gmode == 0 ? beta[bh] : 1.f;
+  const float pscale = plain ? 1.f : a;  // decay of the prediction in the residual
   if (tid < dk) {
     sk[tid] = k[(size_t)bh * dk + tid];
     sq[tid] = q[(size_t)bh * dk + tid];
   }
-  if (tid < dv) sv[tid] = v[(size_t)bh * dv + tid] * vscale;
+  if (tid < dv) sv[tid] = v[(size_t)bh * dv + tid];
   __syncthreads();
 
   // write vector
@@ -148,7 +143,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
       pred += red1[g][tid];
       qp += red2[g][tid];
     }
-    e = noerase ? sv[tid] : sv[tid] - a * pred;
+    e = noerase ? sv[tid] : sv[tid] - pscale * pred;
     oq = a * qp;
     se[tid] = e;
   }
@@ -158,10 +153,8 @@ __global__ __launch_bounds__(NT) void decode_kernel(const float* __restrict__ q,
   const float vv = score_kind == 2 ? block_sum(tid < dv ? sv[tid] * sv[tid] : 0.f, scratch) : 0.f;
   if (tid < dv) o[(size_t)bh * dv + tid] = fmaf(bq, e, oq);
   if (m && tid == 0) {
-    // the plain form runs as the gated one with (beta / alpha, alpha v): its
-    // residual and value are alpha times the plain ones, its beta 1 / alpha times
     const float ws = gmode ? sqrtf(bb) : bscale;
-    m[bh] = score_kind == 1 ? sqrtf(ee) / vscale : (score_kind == 2 ? ws * sqrtf(vv) : ws * sqrtf(ee));
+    m[bh] = score_kind == 1 ? sqrtf(ee) : (score_kind == 2 ? ws * sqrtf(vv) : ws * sqrtf(ee));
   }
 
   // S <- alpha S + b e^T

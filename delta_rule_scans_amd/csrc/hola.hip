@@ -13,8 +13,10 @@
 // per pass), 16-byte loads. Weighted value sum: lane (rg, cg) accumulates
 // columns of group cg over rows rg, rg + 8, ...; partial sums meet in LDS.
 // Eviction: one wavefront takes the lexicographic minimum of (m, -pos) with
-// shuffles, so the choice is deterministic and uses no atomics. The recency
-// control of sec. 4.5 evicts the smallest position instead.
+// shuffles, so the choice is deterministic and uses no atomics. A NaN score
+// ranks below every other score (ranked as -infinity, stored unchanged), as in
+// the prompt cache. The recency control of sec. 4.5 evicts the smallest
+// position instead.
 #include "kdn_internal.h"
 
 namespace kdn {
@@ -22,6 +24,9 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int WMAX = 256;
+
+// ranking key of a score: NaN ranks below every other score
+__device__ __forceinline__ float rank_key(float m) { return m == m ? m : -INFINITY; }
 
 __device__ __forceinline__ float sum32(float x) {
   for (int off = 16; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -141,7 +146,7 @@ __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
   }
   // eviction choice (wavefront 0) while the partial sums settle
   if (tid < 64) {
-    const float mt = m[bh];
+    const float mt = rank_key(m[bh]);
     int slot = -1;
     if (n < w) {
       slot = n;
@@ -150,7 +155,7 @@ __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
       int bp = -1, bs = -1;
       for (int j = lane; j < w; j += 64) {
         // recency: rank by position alone
-        const float mj = recency ? 0.f : cache_m[(size_t)bh * w + j];
+        const float mj = recency ? 0.f : rank_key(cache_m[(size_t)bh * w + j]);
         const int pj = recency ? -cache_pos[(size_t)bh * w + j] : cache_pos[(size_t)bh * w + j];
         if (bs < 0 || mj < bm || (mj == bm && pj > bp)) {
           bm = mj;

@@ -223,8 +223,6 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
     sc.ubuf = a.ubuf;
     sc.ntiles = mfma_ok ? d_v / 32 : (d_v + cols - 1) / cols;
     sc.beta = a.beta;
-    sc.alpha = alpha;
-    sc.plain = a.plain;
     sc.iso_beta = iso_beta;
     sc.iso_kk = iso_beta ? iso_beta + (size_t)BH * L : nullptr;
     sc.gains = gains;

@@ -86,7 +86,7 @@ struct ScanArgs {
   float* state_out;       // [BH, dk, dv] or null
   void* o;                // [BH, L, dv]
   int BH, L, dk, dv, chunk;
-  int plain;  // 1: plain residual (delta only): b = (beta/alpha) k, v' = alpha v
+  int plain;  // 1: plain residual e = v - S^T k (delta only): exclusive decay in A and K S0
   int noerase = 0;  // 1: e = v (no prediction subtracted; float32 path only)
   // Residuals for the write scores, or null: the float32 path writes per-tile
   // sums of e_t^2 to esq [BH, d_v tiles, L]; the matrix-core path writes the
@@ -122,8 +122,7 @@ size_t scan_mfma_ubuf_bytes(int BH, int L, int dv);
 // Write scores m_t = s_t ||e_t|| ("A Hippocampus for Linear Attention", sec.
 // 3.3 eq. (6)) from the residuals a scan left in esq (float32 path, `ntiles`
 // d_v tiles) or ubuf (matrix-core path, dv / 32 tiles). The write scale s_t is
-// beta_t (divided by alpha_t for the plain residual) for the delta write,
-// beta_t ||k_t|| for the isotropic gain (iso_beta, iso_kk = ||k||^2), and
+// beta_t for the delta write, beta_t ||k_t|| for the isotropic gain (iso_beta, iso_kk = ||k||^2), and
 // ||g_t|| for the diagonal / full gains (gains [BH, L, dk], fp16 or f32).
 struct ScoreArgs {
   int kind;  // 0: s ||e||, 1: ||e||, 2: s ||v|| (s: the write scale below)
@@ -133,8 +132,6 @@ struct ScoreArgs {
   const void* ubuf;
   int ntiles;
   const float* beta;
-  const float* alpha;
-  int plain;
   const float* iso_beta;
   const float* iso_kk;
   const void* gains;

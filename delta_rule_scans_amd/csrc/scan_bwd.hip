@@ -32,7 +32,7 @@
 //  * contractions over d_v (head, chunk, part): dO S0^T and dO E^T; dR S0^T and
 //    dR E^T; E G^T and <G, S0>.
 //  * gradients (head, chunk): dQ, dK, dbeta, dalpha.
-// Products run on register tiles of each thread over LDS operands.
+// Products run on the fp32 matrix cores (v_mfma_f32_16x16x4f32) with operands read from LDS.
 #include "kdn_internal.h"
 
 namespace kdn {

@@ -11,7 +11,9 @@
 //   A = strict_lower((K B^T) * G), G_il = g_i / g_l;   (I + A) U = V - diag(g) K S0
 //   O = diag(g) Q S0 + lower_incl((Q B^T) * G) U;      S = g_n S0 + (diag(g_n / g) B)^T U
 // U are exactly the per-token residuals e_t. Without the erase term (e_t = v_t)
-// A = 0 and the K S0 term drops: U = V.
+// A = 0 and the K S0 term drops: U = V. The plain residual e_t = v_t -
+// S_{t-1}^T k_t unrolls to the same form with the exclusive decay g_{t-1} =
+// g_t / alpha_t in the rows of A and in the K S0 term (every ratio <= 1).
 //
 // One workgroup per (head, d_v tile): grid (heads, d_v tiles). The state tile lives in LDS; the loop
 // over chunks is sequential inside the workgroup.
@@ -61,9 +63,9 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
   float* sP = sA + C * CP;      // [C][CP]
   float* sS = sP + C * CP;      // [dk][dvt] state tile
   float* sLg = sS + dk * dvt;   // [C] chunk-local log-decay prefix
-  float* sBs = sLg + C;         // [C] write scale (beta, beta/alpha or 1)
-  float* sVs = sBs + C;         // [C] value scale (alpha for the plain residual)
-  float* sW = sVs + C;          // [C] state-update weights (g_n / g_l) * scale_l
+  float* sBs = sLg + C;         // [C] write scale (beta, or 1 for a gain)
+  float* sLa = sBs + C;         // [C] log alpha_t when the residual decay is exclusive, else 0
+  float* sW = sLa + C;          // [C] state-update weights (g_n / g_l) * scale_l
   float* sRed = sW + C;         // [NT]
 
   const Tin* qp = static_cast<const Tin*>(a.q);
@@ -97,26 +99,22 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
       sB[t * KP + i] = bv;
     }
     if (tid < C) {
-      float la = 0.f, bs = 0.f, vs = 1.f;
+      float la = 0.f, bs = 0.f;
       if (tid < n) {
         const size_t g = tok0 + c0 + tid;
         const float al = a.alpha ? a.alpha[g] : 1.f;
         la = logf(al);
         bs = gp ? 1.f : a.beta[g];
-        if (a.plain) {
-          bs = bs / al;
-          vs = al;
-        }
       }
       sLg[tid] = la;
       sBs[tid] = bs;
-      sVs[tid] = vs;
+      sLa[tid] = a.plain ? la : 0.f;
     }
     __syncthreads();
     for (int idx = tid; idx < C * dvt; idx += NT) {
       const int t = idx / dvt, j = idx - t * dvt;
       float x = 0.f;
-      if (t < n && j < nj) x = Elem<Tin>::load(vp, (tok0 + c0 + t) * dv + j0 + j) * sVs[t];
+      if (t < n && j < nj) x = Elem<Tin>::load(vp, (tok0 + c0 + t) * dv + j0 + j);
       sX[idx] = x;
     }
     if (tid == 0) {
@@ -140,7 +138,7 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
           dqb = fmaf(sQ[i * KP + r], b, dqb);
         }
         const float f = expf(sLg[i] - sLg[l]) * sBs[l];
-        av = (l < i) ? dkb * f : 0.f;
+        av = (l < i) ? dkb * expf(sLg[i] - sLa[i] - sLg[l]) * sBs[l] : 0.f;
         pv = dqb * f;
       }
       sA[i * CP + l] = av;
@@ -155,9 +153,8 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
         ks = fmaf(sK[i * KP + r], s, ks);
         qs = fmaf(sQ[i * KP + r], s, qs);
       }
-      const float g = expf(sLg[i]);
-      if (!a.noerase) sX[idx] -= g * ks;
-      sO[idx] = g * qs;
+      if (!a.noerase) sX[idx] -= expf(sLg[i] - sLa[i]) * ks;
+      sO[idx] = expf(sLg[i]) * qs;
     }
     __syncthreads();
     // Forward substitution (I + A) U = X; each column is split over NT/dvt lanes.

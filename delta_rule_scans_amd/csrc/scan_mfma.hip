@@ -9,6 +9,10 @@
 //   X = V - (diag(g) K) S0,  U = T X  (U are the residuals e_t)
 //   O = (diag(g) Q) S0 + P U
 //   S = g_n S0 + (diag(w) B)^T U,  w_l = (g_n / g_l) beta_l  (1 in place of beta for a gain)
+// The plain residual e_t = v_t - S_{t-1}^T k_t (same update) unrolls to the
+// same form with the exclusive decay g_{t-1} = g_t / alpha_t in the rows of A
+// and in X: A_tl = (k_t . b_l) g_{t-1} / g_l, X = V - diag(g_{t-1}) K S0;
+// every decay ratio stays <= 1, so no factor grows when alpha_t is small.
 //
 // Two kernels:
 //  * prep_kernel: every chunk independent of the others; a workgroup takes a
@@ -64,8 +68,9 @@ constexpr int CP = C + 8;      // fp16 pitch of [.][token] tiles (144 B)
 //   T  = (I + A)^-1 as its three nonzero 32 x 32 blocks (rows/cols 0-31,
 //        rows 32-63 x cols 0-31, rows/cols 32-63), fp16, row-major per block;
 //   P  (Kalman writes only) in the same three-block form;
-//   scalars, three float4 per token: (g, w, log2 g, write scale),
-//        (R, Cf, f0, f1), (value scale, extreme, 0, 0). They factor the decay
+//   scalars, three float4 per token: (g_x, w, log2 g, write scale),
+//        (R, Cf, f0, f1), (value scale, extreme, g, 0), where g_x is the decay
+//        the residual sees (g_{t-1} for the plain residual, else g). They factor the decay
 //        ratio of the masked query-key product bs_l g_i / g_l (l <= i):
 //        across the two 32-token halves as f0_l f1_i with
 //        f0_l = bs_l g_31 / g_l (l < 32), f1_i = g_i / g_31 (i >= 32), both
@@ -178,7 +183,7 @@ constexpr int kPrepR1 = (C * KP > 2 * C * CP ? C * KP : 2 * C * CP) * 2;  // sQ,
 size_t prep_lds_bytes(bool gain) {
   return (size_t)kPrepR1 + (gain ? (size_t)2 * C * KP * 2 : 0) +
          (size_t)C * CP * 2 + (size_t)4 * 16 * kAdP * 4 + (size_t)4 * 16 * 24 * 2 +
-         (size_t)2 * C * 4;
+         (size_t)3 * C * 4;
 }
 
 // One chunk's inputs in registers: this thread's four 16-byte pieces of K
@@ -244,6 +249,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   p += 4 * 16 * 24 * 2;
   float* sLg = reinterpret_cast<float*>(p);        // [C] log2 of g
   float* sBs = sLg + C;                            // [C] write scale
+  float* sLgx = sBs + C;                           // [C] log2 of g_x (rows of A)
 
   const int bh = blockIdx.x;
   const int cbeg = blockIdx.y * a.cpw, cend = min(cbeg + a.cpw, a.nchunks);
@@ -294,23 +300,22 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec, rec_bytes(gain));
     constexpr int kDrop = 1 << 30;  // past any record
     {
-      float la = 0.f, bs = 0.f, vs = 1.f;
+      float la = 0.f, bs = 0.f;
+      const float vs = 1.f;
       if (lane < n) {
         const float al = a.alpha ? al_in : 1.f;
         la = log2f(al);
         bs = gain ? 1.f : be_in;
-        if (a.plain) {  // plain residual = gated form with (beta / alpha, alpha v)
-          bs /= al;
-          vs = al;
-        }
       }
       const float lg = wave_prefix(la, lane);
+      const float lgx = a.plain ? lg - la : lg;   // the residual's decay: exclusive for plain
       const float lgn = __shfl(lg, n - 1, 64);
       const float lg31 = __shfl(lg, 31, 64);
       const float lgr = __shfl(lg, (lane & 32) + 15, 64);   // reference of this half
       if (wave == 0) {
         sLg[lane] = lg;
         sBs[lane] = bs;
+        sLgx[lane] = lgx;
       }
       const float w = lane < n ? exp2f(lgn - lg) * bs : 0.f;
       // exponents of R and Cf stay in [-100, 100] unless the decay is extreme
@@ -318,11 +323,11 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
       const bool extreme = __ballot(span > 100.f) != 0;
       // default (write-back) stores: the state kernel reads the records soon after
       const int so = wave == 0 ? (int)rec_s_off(gain) + 48 * lane : kDrop;
-      const float4 s0 = make_float4(exp2f(lg), w, lg, bs);
+      const float4 s0 = make_float4(exp2f(lgx), w, lg, bs);
       const float4 s1 = make_float4(extreme ? 0.f : bs * exp2f(lgr - lg), extreme ? 0.f : exp2f(lg - lgr),
                                     lane < 32 ? bs * exp2f(lg31 - lg) : 0.f,
                                     lane >= 32 ? exp2f(lg - lg31) : 0.f);
-      const float4 s2 = make_float4(vs, extreme ? 1.f : 0.f, 0.f, 0.f);
+      const float4 s2 = make_float4(vs, extreme ? 1.f : 0.f, exp2f(lg), 0.f);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s0), rr, so, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s1), rr, so + 16, 0, 0);
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s2), rr, so + 32, 0, 0);
@@ -354,7 +359,8 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
                    ld8(sB + (16 * tj + r16) * KP + 32 * ks + k8), acc);
       const int col = 16 * tj + r16;
       const float lgc = sLg[col], bsc = sBs[col];
-      const float4 lgr = *reinterpret_cast<const float4*>(sLg + 16 * ti + kq * 4);
+      // rows of A take the residual's decay, rows of P the read-out's
+      const float4 lgr = *reinterpret_cast<const float4*>((isP ? sLg : sLgx) + 16 * ti + kq * 4);
       const float lgrv[4] = {lgr.x, lgr.y, lgr.z, lgr.w};
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -599,15 +605,15 @@ constexpr int VP = DV + 8;  // fp16 pitch of the staged V rows
 
 // LDS, per chain stage (3 for the delta write, 2 for the Kalman writes):
 //   K [C][KP]; gains [C][KP] (Kalman); T [C][CP] (lower blocks only);
-//   V times the value scale [C][VP]; eight token scalars [8][C] (g, w, log2 g,
-//   write scale, R, Cf, f0, f1) and the chunk's extreme-decay flag;
+//   V times the value scale [C][VP]; nine token scalars [9][C] (g_x, w, log2 g,
+//   write scale, R, Cf, f0, f1, g) and the chunk's extreme-decay flag;
 // per output stage (2): Q [C][KP] (delta) or P [C][CP] and g [C] (Kalman);
 // per exchange buffer (2): S (8 k steps) and U (4 k steps), 16 bytes per lane
 // and k step in wavefront-0 register order.
 constexpr size_t kStK = (size_t)C * KP * 2;
 constexpr size_t kStT = (size_t)C * CP * 2;
 constexpr size_t kStV = (size_t)C * VP * 2;
-constexpr size_t kStSc = (size_t)8 * C * 4 + 16;
+constexpr size_t kStSc = (size_t)9 * C * 4 + 16;
 constexpr size_t kExBytes = (size_t)12 * 64 * 16;
 __host__ __device__ constexpr int n_chain_stages(bool gain) { return gain ? 2 : 3; }
 __host__ __device__ constexpr size_t chain_stage_bytes(bool gain) {
@@ -625,7 +631,7 @@ struct ChainStage {
   _Float16* b;   // write vectors: K (delta) or the gains
   _Float16* t;
   _Float16* v;
-  float* g;      // token scalars
+  float* g;      // token scalars: g_x (the residual's decay)
   float* w;
   float* lg;
   float* bs;
@@ -633,6 +639,7 @@ struct ChainStage {
   float* f1;
   float* rr;
   float* cf;
+  float* go;     // g (the read-out's decay)
   float* extreme;
 };
 struct OutStage {
@@ -651,7 +658,7 @@ __device__ __forceinline__ ChainStage chain_stage(unsigned char* lds, int buf) {
   s.v = reinterpret_cast<_Float16*>(p); p += kStV;
   float* f = reinterpret_cast<float*>(p);
   s.g = f; s.w = f + C; s.lg = f + 2 * C; s.bs = f + 3 * C; s.f0 = f + 4 * C; s.f1 = f + 5 * C;
-  s.rr = f + 6 * C; s.cf = f + 7 * C; s.extreme = f + 8 * C;
+  s.rr = f + 6 * C; s.cf = f + 7 * C; s.go = f + 8 * C; s.extreme = f + 9 * C;
   return s;
 }
 template <bool GAIN>
@@ -688,7 +695,7 @@ struct ProdBuf : ProdX<GAIN> {
   uint4 v[2];    // V slice: rows 32 pw + 16 i + l / 4, piece l % 4
   float4 sc0;    // scalars of token l (chain chunk): g, w, log2 g, write scale
   float4 sc1;    //   R, Cf, f0, f1
-  float2 sc2;    //   value scale, extreme
+  float4 sc2;    //   value scale, extreme, g, 0
 };
 
 struct ProdCtx {
@@ -728,7 +735,7 @@ __device__ __forceinline__ void prod_load(const ProdCtx& x, ProdBuf<GAIN>& b, in
   const float4* sc = reinterpret_cast<const float4*>(rc + rec_s_off(GAIN));
   b.sc0 = sc[3 * l];
   b.sc1 = sc[3 * l + 1];
-  b.sc2 = *reinterpret_cast<const float2*>(sc + 3 * l + 2);
+  b.sc2 = sc[3 * l + 2];
   if constexpr (GAIN) b.go = reinterpret_cast<const float4*>(ro + rec_s_off(true))[3 * l].x;
 }
 
@@ -768,6 +775,7 @@ __device__ __forceinline__ void prod_stage(const ProdCtx& x, const ProdBuf<GAIN>
     cs.cf[l] = b.sc1.y;
     cs.f0[l] = b.sc1.z;
     cs.f1[l] = b.sc1.w;
+    cs.go[l] = b.sc2.z;
     if constexpr (GAIN) os.g[l] = b.go;
   }
 }
@@ -1044,7 +1052,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         // registers are the same, A and B swap), so that each lane ends with 4
         // consecutive value columns of one token: 16-byte stores. Columns of
         // O^T are tokens: O^T = (S^T Q^T) diag(g) + U^T P^T.
-        const float* gsrc = GAIN ? os.g : cs.g;
+        const float* gsrc = GAIN ? os.g : cs.go;
         const float gt[2] = {gsrc[c32], gsrc[32 + c32]};
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
@@ -1189,7 +1197,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) ka[i] = k_op(i);
       s_to_f16(0);
-      const float gn = st.g[n - 1];
+      const float gn = st.go[n - 1];   // the state carries the inclusive decay g_n
       __builtin_amdgcn_sched_barrier(0);
       static_for<38>([&](auto slot_c) {
         constexpr int slot = decltype(slot_c)::value;

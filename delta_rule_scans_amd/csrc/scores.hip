@@ -49,10 +49,8 @@ __global__ __launch_bounds__(64) void scores_kernel(ScoreArgs a) {
   } else {
     for (int tile = 0; tile < a.ntiles; ++tile) ss += a.esq[((size_t)bh * a.ntiles + tile) * a.L + tok];
   }
-  if (a.kind == 1) {  // ||e||; the plain form's residual is alpha e, see ScanArgs
-    float e = sqrtf(ss);
-    if (a.plain && a.alpha) e /= a.alpha[g];
-    a.m[g] = e;
+  if (a.kind == 1) {  // ||e||
+    a.m[g] = sqrtf(ss);
     return;
   }
   float scale;
@@ -68,7 +66,6 @@ __global__ __launch_bounds__(64) void scores_kernel(ScoreArgs a) {
     scale = a.iso_beta[g] * sqrtf(a.iso_kk[g]);
   } else {
     scale = a.beta[g];
-    if (a.plain && a.kind == 0) scale /= a.alpha ? a.alpha[g] : 1.f;
   }
   if (a.kind == 2) {  // write strength times ||v|| of the input value
     float vv = 0.f;

@@ -307,7 +307,8 @@ int kdn_scan_bwd(const float *q, const float *k, const float *v, const float *al
  *            aligned.
  * Sizes: B, H >= 1; L >= 0 (L = 0 leaves the cache as it is); 1 <= d_k, d_v
  * <= 128; 1 <= w <= 256; 1 <= block <= 1024; t0 + L <= 2^31 - 1; rms_eps >= 0.
- * The read runs in float32 on the vector units.
+ * The read runs in float32: logits and weighted values on the fp32 matrix
+ * cores, the softmax on the vector units.
  */
 size_t hola_prefill_workspace_size(int B, int H, int L, int d_k, int d_v, int w, int block);
 

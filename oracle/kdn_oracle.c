@@ -186,6 +186,14 @@ static void scan_one(int L, int dk, int dv,
             for (int i = 0; i < dk; ++i)
                 for (int j = 0; j < dk; ++j)
                     cov[i * dk + j] = Pm[i * dk + j] - u[i] * u[j] / s;
+            /* P is a covariance: symmetric in exact arithmetic. Averaging it with
+             * its transpose keeps it so under rounding, whatever the prior. */
+            for (int i = 0; i < dk; ++i)
+                for (int j = i + 1; j < dk; ++j) {
+                    const double avg = 0.5 * (cov[i * dk + j] + cov[j * dk + i]);
+                    cov[i * dk + j] = avg;
+                    cov[j * dk + i] = avg;
+                }
         }
 
         /* read-out */
@@ -263,6 +271,14 @@ int oracle_scan(int B, int H, int L, int dk, int dv,
     }
     return bad ? -2 : 0;
 }
+
+/*
+ * Ranking key of a write score. The pages never meet a NaN score; the reading
+ * taken here is that a NaN score ranks below every other score (it is ranked
+ * as -infinity and stored unchanged), the same rule for one token at a time
+ * and for a whole prompt.
+ */
+static float orc_rank_key(float m) { return m == m ? m : -INFINITY; }
 
 /*
  * HOLA exact cache, one decode token for every (batch, head)
@@ -354,9 +370,10 @@ int oracle_hola_step(int B, int H, int dk, int dv, int w,
         } else {
             int worst = 0;
             for (int j = 1; j < w; ++j) {
-                if (cm[j] < cm[worst] || (cm[j] == cm[worst] && cp[j] > cp[worst])) worst = j;
+                const float kj = orc_rank_key(cm[j]), kw = orc_rank_key(cm[worst]);
+                if (kj < kw || (kj == kw && cp[j] > cp[worst])) worst = j;
             }
-            if (mt > cm[worst]) slot = worst;
+            if (orc_rank_key(mt) > orc_rank_key(cm[worst])) slot = worst;
         }
         if (slot >= 0) {
             memcpy(ck + (size_t)slot * dk, kt, sizeof(float) * (size_t)dk);
@@ -402,7 +419,8 @@ typedef struct { float m; int32_t pos; int src; } orc_entry; /* src >= 0: token,
 static int orc_entry_before(const orc_entry *a, const orc_entry *b, int policy)
 {
     if (policy == ORC_EVICT_RECENCY) return a->pos > b->pos;
-    return a->m > b->m || (a->m == b->m && a->pos < b->pos);
+    const float ka = orc_rank_key(a->m), kb = orc_rank_key(b->m);
+    return ka > kb || (ka == kb && a->pos < b->pos);
 }
 
 int oracle_hola_prefill(int B, int H, int L, int dk, int dv, int w, int block,

@@ -38,7 +38,10 @@ def rel_err(got, ref):
 
 
 def assert_close(got, ref, tol, what=""):
-    e = rel_err(got, ref)
+    """err = max|got - ref| / RMS(ref) <= tol; the measured ratio is printed
+    (with -s, or in the captured output of a failing test) so margins show."""
     assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    e = rel_err(got, ref)
+    log(f"  {what}: max|diff|/RMS = {e:.3e} (tol {tol:.0e}, margin {tol / max(e, 1e-300):.1f}x)")
     assert e <= tol, f"{what}: max|diff| / RMS = {e:.3e} > {tol:.1e}"
     return e

@@ -54,9 +54,10 @@ def test_backward_odd_shapes(kdn, orc):
 
 def test_backward_full_size(kdn, orc):
     """The gated workload's shape (B=4, H=16, L=4096, d=128) in float32, checked
-    on sampled heads."""
+    on 16 heads spread over the batch and the heads."""
     log("backward full size")
-    _case(kdn, orc, 4, 16, 4096, 128, 128, "gated", seed=403, heads=[(0, 0), (3, 15)])
+    heads = [(b, h) for b in range(4) for h in (0, 5, 10, 15)]
+    _case(kdn, orc, 4, 16, 4096, 128, 128, "gated", seed=403, heads=heads)
 
 
 def test_backward_defaults(kdn, orc):

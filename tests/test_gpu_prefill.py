@@ -160,7 +160,8 @@ def test_scan_scores_then_prefill(kdn, orc):
 
 def test_full_size_gated_prefill(kdn, orc):
     """The gated workload (B=4, H=16, L=4096, d=128, bf16): scan with scores, then
-    the prompt cache with blocks of 256 and w = 64, checked on sampled heads."""
+    the prompt cache with blocks of 256 and w = 64; the scores checked on every
+    head, the cache (membership, order, contents, o_cache) on every head."""
     import torch
     cfg = workloads.WORKLOADS["gated"]
     inp = workloads.named_scan_inputs("gated")
@@ -169,13 +170,11 @@ def test_full_size_gated_prefill(kdn, orc):
     o, m = kdn.kdn_scan_fwd(q, k, v, alpha=dev_tensor(inp["alpha"]), beta=dev_tensor(inp["beta"]),
                             m=True)
     torch.cuda.synchronize()
-    heads = [(0, 0), (2, 9), (3, 15)]
     m_host = host(m)
-    for (b, h) in heads[:2]:
-        log(f"gated: oracle scores head ({b}, {h})")
-        sub = {n: x[b:b + 1, h:h + 1] for n, x in inp.items() if x is not None}
-        ref = orc.scan(sub["q"], sub["k"], sub["v"], alpha=sub["alpha"], beta=sub["beta"])
-        assert_close(m_host[b:b + 1, h:h + 1], ref["m"], TOL_BF16, f"m head {(b, h)}")
-    log("gated: prompt cache")
+    log("gated: oracle scores on every head")
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"])
+    assert_close(m_host, ref["m"], TOL_BF16, "m (all heads)")
+    del ref
+    log("gated: prompt cache, every head")
     _prefill_case(kdn, orc, inp["q"], inp["k"], inp["v"], m_host.astype(np.float32), 0, 256, 64,
-                  "bf16", heads=heads)
+                  "bf16")

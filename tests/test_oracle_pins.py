@@ -157,6 +157,26 @@ def test_kalman_with_process_noise_batch_conditioning(orc):
     np.testing.assert_allclose(res["cov"][0, 0], cov, atol=1e-10)
 
 
+def test_full_covariance_is_symmetrised(orc):
+    """The full covariance is a covariance matrix (Kalman Delta Networks,
+    abstract): symmetric. A prior with a last-bit asymmetry comes out exactly
+    symmetric, and close to the run from the symmetrised prior."""
+    rng = _rng(23)
+    dk, L = 6, 12
+    inp = workloads.scan_inputs(1, 1, L, dk, 3, seed=23, dtype="f32", with_r=True)
+    A = rng.standard_normal((dk, dk))
+    P0 = A @ A.T / dk + np.eye(dk)
+    P0a = P0.copy()
+    P0a[0, 1] = np.nextafter(P0a[0, 1], np.inf)
+    out = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"],
+                   cov0=P0a[None, None], q_noise_var=0.3, mode="full")
+    P = out["cov"][0, 0]
+    np.testing.assert_array_equal(P, P.T)
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"],
+                   cov0=P0[None, None], q_noise_var=0.3, mode="full")
+    np.testing.assert_allclose(P, ref["cov"][0, 0], rtol=1e-12, atol=1e-14)
+
+
 def test_rls_capacity_recall(orc):
     """DeltaNet-PC, summary (empirical results): sequences are recalled with
     perfect accuracy when L <= D. For generic keys with L <= d_k and a vanishing
@@ -523,12 +543,16 @@ def test_delta_noop_write(orc):
     np.testing.assert_array_equal(res["m"], 0.0)
 
 
-def test_plain_residual_is_reparameterised_gated(orc):
+@pytest.mark.parametrize("drop", [None, 1e-6, 1e-8])
+def test_plain_residual_is_reparameterised_gated(orc, drop):
     """The plain residual e = v - S^T k with decay alpha equals the gated form of
     sec. 3.5 (A Hippocampus for Linear Attention) under (beta, v) -> (beta/alpha,
-    alpha v): the rank-1 write, hence the score, is unchanged."""
+    alpha v): the rank-1 write, hence the score, is unchanged. Also with single
+    tokens whose decay drops to 1e-6 or 1e-8 (alpha in (0, 1], sec. 3.5)."""
     inp = workloads.scan_inputs(1, 2, 40, 8, 6, seed=22, dtype="f32")
     a = inp["alpha"]
+    if drop is not None:
+        a[:, :, [3, 17, 18, 31]] = drop
     plain = orc.scan(inp["q"], inp["k"], inp["v"], alpha=a, beta=inp["beta"], resid="plain")
     gated = orc.scan(inp["q"], inp["k"], (inp["v"].astype(np.float64) * a[..., None]),
                      alpha=a, beta=(inp["beta"].astype(np.float64) / a), resid="gated")
@@ -601,6 +625,36 @@ def test_cache_membership_equals_sorted_topw(orc):
                 n = cache.count[b, h]
                 assert n == min(t + 1, w)
                 assert sorted(cache.pos[b, h, :n].tolist()) == sorted(order)
+
+
+def test_cache_membership_nan_scores_rank_last(orc):
+    """The pages never meet a NaN score; the reading taken is that a NaN score
+    ranks below every other score (as -infinity). With it the online cache
+    still equals the top-w of the whole history, one token at a time and a
+    whole prompt in blocks. Brute force: sort with NaN mapped to -infinity."""
+    rng = _rng(26)
+    B, H, dk, dv, w, T = 1, 3, 4, 3, 6, 50
+    q = rng.standard_normal((B, H, T, dk)).astype(np.float32)
+    k = rng.standard_normal((B, H, T, dk)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, dv)).astype(np.float32)
+    m = np.round(rng.uniform(0, 3, (B, H, T)) * 2) / 2
+    m[rng.uniform(size=(B, H, T)) < 0.3] = np.nan
+    m[0, 0, :4] = np.nan          # NaN slots in a cache that then fills up
+    key = lambda s, j: (-(s[j] if s[j] == s[j] else -np.inf), j)  # noqa: E731
+    cache = orc.HolaCache(B, H, dk, dv, w)
+    for t in range(T):
+        cache.step(q[:, :, t], k[:, :, t], v[:, :, t], m[:, :, t], t)
+        for h in range(H):
+            s = m[0, h, :t + 1].astype(np.float32)
+            order = sorted(range(t + 1), key=lambda j: key(s, j))[:w]
+            assert sorted(cache.pos[0, h, :cache.count[0, h]].tolist()) == sorted(order)
+    for block in (1, 7, 64):
+        c = orc.HolaCache(B, H, dk, dv, w)
+        c.prefill(q, k, v, m, 0, block)
+        for h in range(H):
+            s = m[0, h].astype(np.float32)
+            order = sorted(range(T), key=lambda j: key(s, j))[:w]
+            np.testing.assert_array_equal(c.pos[0, h], np.array(order))
 
 
 def _rmsnorm(x, eps):
