@@ -22,8 +22,10 @@ __all__ = [
     "lib", "KdnError", "kdn_scan_fwd", "kdn_step_decode", "hola_cache_update",
     "kdn_scan_workspace_size", "kdn_status_string", "HolaCache", "LIB_PATH",
     "hola_prefill", "hola_prefill_workspace_size", "kdn_scan_bwd",
-    "F32", "BF16", "MODES", "RESIDS", "PHASES",
+    "F32", "BF16", "MODES", "RESIDS", "PHASES", "kdn_scan_fwd_static", "STATIC_SCRATCH_BYTES",
 ]
+
+STATIC_SCRATCH_BYTES = 64 << 20  # KDN_STATIC_SCRATCH_BYTES in include/kdn.h
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkdn.so")
 
@@ -59,6 +61,8 @@ def _load():
     L.kdn_scan_fwd.restype = I
     L.kdn_scan_fwd_phase.argtypes = [I] + L.kdn_scan_fwd.argtypes
     L.kdn_scan_fwd_phase.restype = I
+    L.kdn_scan_fwd_static.argtypes = L.kdn_scan_fwd.argtypes[:-3] + [P]
+    L.kdn_scan_fwd_static.restype = I
     L.kdn_step_decode.argtypes = [P, P, P, P, P, P, P, F, P, P, P, I, I, I, I, I, I, I, P]
     L.kdn_step_decode.restype = I
     L.hola_cache_update.argtypes = [P, P, P, P, ctypes.c_int32, P, P, P, P, P, P, P, F,
@@ -189,6 +193,41 @@ def kdn_scan_fwd(q, k, v, alpha=None, beta=None, r=None, cov_in=None, cov_out=No
     if st != 0:
         raise KdnError(st, "kdn_scan_fwd")
     return (o, m) if want_m else o
+
+
+def kdn_scan_fwd_static(q, k, v, o, alpha=None, beta=None, r=None, cov_in=None, cov_out=None,
+                        q_noise_var: float = 0.0, state_in=None, state_out=None, m=None,
+                        chunk: int = 64, mode: str = "delta", resid: str = "gated", stream=None,
+                        score: str = "write"):
+    """kdn_scan_fwd on the library's static scratch (no workspace, nothing
+    allocated here or in the library): every output, ``o`` and optionally
+    ``m`` ([B,H,L] float32), ``state_out`` and ``cov_out``, is the caller's
+    tensor. Same shapes and meaning as kdn_scan_fwd; calls on one GPU must not
+    overlap (they share its scratch)."""
+    torch = _torch()
+    _check(q, "q", (torch.bfloat16, torch.float32))
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", q.dtype, (B, H, L, dk), dev)
+    _check(v, "v", q.dtype, (B, H, L, dv), dev)
+    for name, t in (("alpha", alpha), ("beta", beta), ("r", r)):
+        _check(t, name, torch.float32, (B, H, L), dev)
+    cshape = {"diag": (B, H, dk), "iso": (B, H)}.get(mode, (B, H, dk, dk))
+    _check(cov_in, "cov_in", torch.float32, cshape, dev)
+    _check(cov_out, "cov_out", torch.float32, cshape, dev)
+    _check(state_in, "state_in", torch.float32, (B, H, dk, dv), dev)
+    _check(state_out, "state_out", torch.float32, (B, H, dk, dv), dev)
+    _check(o, "o", (torch.bfloat16, torch.float32), (B, H, L, dv), dev)
+    _check(m, "m", torch.float32, (B, H, L), dev)
+    st = lib.kdn_scan_fwd_static(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q.dtype), _ptr(alpha),
+                                 _ptr(beta), _ptr(r), _ptr(cov_in), _ptr(cov_out),
+                                 float(q_noise_var), _ptr(state_in), _ptr(state_out), _ptr(o),
+                                 _dtype_code(o.dtype), _ptr(m), SCORES[score], B, H, L, dk, dv,
+                                 int(chunk), MODES[mode], RESIDS[resid], _stream(stream))
+    if st != 0:
+        raise KdnError(st, "kdn_scan_fwd_static")
+    return o
 
 
 # ----------------------------------------------------------------- decode

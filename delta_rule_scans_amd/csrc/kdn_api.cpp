@@ -86,6 +86,9 @@ KDN_EXPORT const char* kdn_status_string(int status) {
     case KDN_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than kdn_scan_workspace_size";
     case KDN_ERR_BAD_CAPACITY: return "cache capacity w must be in [1, 256]";
     case KDN_ERR_BAD_ALIGNMENT: return "a pointer is not 16-byte aligned";
+    case KDN_ERR_SCRATCH_LIMIT:
+      return "the call needs more scratch than the library's static scratch array holds "
+             "(KDN_STATIC_SCRATCH_BYTES per GPU); use kdn_scan_fwd with a workspace";
     default: break;
   }
   if (status > 0) return hipGetErrorString(static_cast<hipError_t>(status));
@@ -100,16 +103,16 @@ KDN_EXPORT size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v,
   return ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype, with_scores != 0).total;
 }
 
-KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const void* v,
-                                  int in_dtype, const float* alpha, const float* beta,
-                                  const float* r, const float* cov_in, float* cov_out,
-                                  float q_noise_var, const float* state_in, float* state_out,
-                                  void* o, int out_dtype, float* m, int score_kind, int B, int H,
-                                  int L, int d_k, int d_v, int chunk, int mode, int resid,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+namespace kdn {
+
+// Every check of kdn_scan_fwd_phase that does not involve the workspace; host
+// only, no HIP call.
+int scan_args_status(int phase, const void* q, const void* k, const void* v, int in_dtype,
+                     const float* beta, const float* cov_in, float q_noise_var, void* o,
+                     int out_dtype, const float* m, int score_kind, int B, int H, int L, int d_k,
+                     int d_v, int chunk, int mode, int resid) {
   if (phase != KDN_PHASE_ALL && phase != KDN_PHASE_PREPARE && phase != KDN_PHASE_STATE)
     return KDN_ERR_BAD_MODE;
-  const bool do_prep = phase != KDN_PHASE_STATE, do_state = phase != KDN_PHASE_PREPARE;
   if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_ERR_BAD_DTYPE;
   if (out_dtype != KDN_F32 && out_dtype != KDN_BF16) return KDN_ERR_BAD_DTYPE;
   if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_FULL &&
@@ -131,12 +134,29 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
     if (!q || !k || !v || !o) return KDN_ERR_NULL_POINTER;
     if (mode == KDN_GAIN_DELTA && beta == nullptr) return KDN_ERR_NULL_POINTER;
   }
-  const WsLayout ws = ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype, m != nullptr);
-  if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total || !aligned16(workspace)))
-    return KDN_ERR_WORKSPACE;
   if (kdn::scan_f32_lds_bytes(d_k, chunk) == 0 &&
       !(in_dtype == KDN_BF16 && kdn::scan_mfma_supported(d_k, d_v, chunk)))
     return KDN_ERR_UNSUPPORTED;
+  return KDN_OK;
+}
+
+}  // namespace kdn
+
+KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const void* v,
+                                  int in_dtype, const float* alpha, const float* beta,
+                                  const float* r, const float* cov_in, float* cov_out,
+                                  float q_noise_var, const float* state_in, float* state_out,
+                                  void* o, int out_dtype, float* m, int score_kind, int B, int H,
+                                  int L, int d_k, int d_v, int chunk, int mode, int resid,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = kdn::scan_args_status(phase, q, k, v, in_dtype, beta, cov_in, q_noise_var, o,
+                                       out_dtype, m, score_kind, B, H, L, d_k, d_v, chunk, mode,
+                                       resid);
+  if (st != KDN_OK) return st;
+  const bool do_prep = phase != KDN_PHASE_STATE, do_state = phase != KDN_PHASE_PREPARE;
+  const WsLayout ws = ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype, m != nullptr);
+  if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total || !aligned16(workspace)))
+    return KDN_ERR_WORKSPACE;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int BH = B * H;

@@ -95,6 +95,13 @@ struct ScanArgs {
   void* ubuf = nullptr;
 };
 
+// Status of kdn_scan_fwd_phase's argument checks other than the workspace
+// (KDN_OK or a negative KDN_ERR_*); host only, makes no HIP call.
+int scan_args_status(int phase, const void* q, const void* k, const void* v, int in_dtype,
+                     const float* beta, const float* cov_in, float q_noise_var, void* o,
+                     int out_dtype, const float* m, int score_kind, int B, int H, int L, int d_k,
+                     int d_v, int chunk, int mode, int resid);
+
 // ------------------------------------------------------------------ launchers
 // Each returns a hipError_t (hipSuccess when the launch was enqueued).
 

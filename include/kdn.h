@@ -90,6 +90,7 @@ extern "C" {
 #define KDN_ERR_WORKSPACE (-7)     /* workspace missing or smaller than required   */
 #define KDN_ERR_BAD_CAPACITY (-8)  /* cache capacity w not in [1, 256]              */
 #define KDN_ERR_BAD_ALIGNMENT (-9) /* a pointer is not 16-byte aligned              */
+#define KDN_ERR_SCRATCH_LIMIT (-10) /* needs more than the static scratch array holds */
 
 /* Static, human-readable message for a status code (never NULL). */
 const char *kdn_status_string(int status);
@@ -188,6 +189,36 @@ int kdn_scan_fwd_phase(int phase, const void *q, const void *k, const void *v, i
                        void *o, int out_dtype, float *m, int score_kind,
                        int B, int H, int L, int d_k, int d_v, int chunk, int mode, int resid,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kdn_scan_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation. The
+ * arguments are those of kdn_scan_fwd without the workspace; the library uses
+ * its own scratch instead: a static device array of KDN_STATIC_SCRATCH_BYTES
+ * on every GPU it runs on, held until the process ends. Its device address is
+ * looked up once per GPU, on the first call with that GPU current. The call
+ * allocates nothing and never synchronises.
+ *
+ * Limit: a call whose kdn_scan_workspace_size(...) (with_scores = m != NULL)
+ * exceeds KDN_STATIC_SCRATCH_BYTES returns KDN_ERR_SCRATCH_LIMIT before
+ * anything is enqueued (64 MiB holds, e.g., the delta write at B*H = 64,
+ * L = 4096, d = 128 on the matrix-core path). Argument errors are those of
+ * kdn_scan_fwd, returned before any HIP call.
+ *
+ * Sharing: every call on one GPU uses that GPU's one array, which keeps the
+ * previous call's contents (no part of a scan needs it cleared). Calls that
+ * overlap on one GPU (other streams, other host threads) race on it and give
+ * wrong results: order them, e.g. on one stream.
+ */
+#define KDN_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int kdn_scan_fwd_static(const void *q, const void *k, const void *v, int in_dtype,
+                        const float *alpha, const float *beta, const float *r,
+                        const float *cov_in, float *cov_out, float q_noise_var,
+                        const float *state_in, float *state_out,
+                        void *o, int out_dtype, float *m, int score_kind,
+                        int B, int H, int L, int d_k, int d_v, int chunk, int mode, int resid,
+                        void *stream);
 
 /*
  * One decode step: the same write and read as kdn_scan_fwd for a single token

@@ -37,7 +37,7 @@ def test_exports_match_header(kdn):
     declared = _header_functions()
     assert declared == sorted(["hola_cache_update", "hola_prefill", "hola_prefill_workspace_size",
                                "kdn_scan_bwd", "kdn_scan_bwd_workspace_size", "kdn_scan_fwd",
-                               "kdn_scan_fwd_phase", "kdn_scan_workspace_size",
+                               "kdn_scan_fwd_phase", "kdn_scan_fwd_static", "kdn_scan_workspace_size",
                                "kdn_status_string", "kdn_step_decode", "kdn_version"])
     out = subprocess.run(["nm", "-D", "--defined-only", kdn.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -251,3 +251,31 @@ def test_backward_rejections(kdn):
     assert _bwd(kdn, da=None) == c["KDN_ERR_NULL_POINTER"]
     assert _bwd(kdn) == c["KDN_ERR_WORKSPACE"]
     assert _bwd(kdn, ws=P, wsb=need - 1) == c["KDN_ERR_WORKSPACE"]
+
+
+def test_static_scratch_entry_rejects_before_any_hip_call(kdn):
+    """kdn_scan_fwd_static (the allocation-free scan) checks its arguments and
+    its scratch limit before any HIP call, so on a machine without a GPU it
+    returns the documented codes: a null pointer, a bad chunk, and a call that
+    needs more workspace than KDN_STATIC_SCRATCH_BYTES."""
+    c = _header_constants()
+    assert kdn.STATIC_SCRATCH_BYTES == 64 << 20
+    fake = ctypes.c_void_p(1 << 40)      # never dereferenced: every call is rejected first
+    lib = kdn.lib
+
+    def call(q, B, H, L, chunk=64, mode=0, m=None, beta=fake):
+        return lib.kdn_scan_fwd_static(q, fake, fake, kdn.BF16, None, beta, None, fake, None,
+                                       0.0, None, None, fake, kdn.F32, m, 0, B, H, L, 128, 128,
+                                       chunk, mode, 0, None)
+
+    assert call(None, 1, 1, 64) == c["KDN_ERR_NULL_POINTER"]
+    assert call(fake, 1, 1, 64, chunk=48) == c["KDN_ERR_BAD_CHUNK"]
+    assert call(fake, 1, 1, 64, beta=None) == c["KDN_ERR_NULL_POINTER"]
+    # B*H = 64, L = 4096 (the gated workload): the delta write fits, with scores or as
+    # the diagonal Kalman write it does not
+    fits = kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 64, "delta", kdn.BF16)
+    assert 0 < fits <= kdn.STATIC_SCRATCH_BYTES
+    assert kdn.kdn_scan_workspace_size(4, 16, 4096, 128, 128, 64, "diag", kdn.BF16) > kdn.STATIC_SCRATCH_BYTES
+    assert call(fake, 4, 16, 4096, mode=1) == c["KDN_ERR_SCRATCH_LIMIT"]
+    assert call(fake, 4, 16, 4096, m=fake) == c["KDN_ERR_SCRATCH_LIMIT"]
+    assert call(fake, 8, 16, 4096) == c["KDN_ERR_SCRATCH_LIMIT"]
