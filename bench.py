@@ -8,11 +8,14 @@ position of one batch row, all H heads). One step = one kdn_scan_fwd call:
 the parallel (I + A)^-1 kernel plus the sequential state kernel. Inputs are
 resident in HBM before timing starts.
 
-Extra fields: the roofline of the dominant (state) kernel, timed on its own
-stream with events around its phase; the fp64 oracle timed on a bounded
-sample on the host cores; and (unless --quick) the decode + HOLA cache step,
-the HOLA prompt cache after a scan with write scores, the backward pass, the
-diagonal and isotropic Kalman scans and the long-context scan.
+Extra fields: the roofline of the dominant (state) kernel, its average
+duration timed with HIP events (created without the system-scope fence) around
+its phase inside the step sequence, on the stream it runs on; the same step with the last-level cache flushed (cold);
+the tiny float32 workload's latency; the fp64 oracle timed on a bounded sample
+on the host cores, which also gives each workload's max|o - o_oracle| / RMS;
+and (unless --quick) the decode + HOLA cache step, the HOLA prompt cache after
+a scan with write scores, the backward pass, the diagonal and isotropic Kalman
+scans and the long-context scan.
 """
 from __future__ import annotations
 
@@ -38,9 +41,12 @@ def scan_flops_per_token_head(C, dk, dv):
     return C * (3 * dk + 2 * dv) + C * C / 3 + 6 * dk * dv
 
 
-def scan_bytes(B, H, L, dk, dv, in_bytes=2, out_bytes=4, extra_per_token=0, state_out=True):
+def scan_bytes(B, H, L, dk, dv, in_bytes=2, out_bytes=2, extra_per_token=0, state_out=True):
     """Algorithmic HBM bytes of one scan: q, k, v read once, alpha/beta (+extra)
-    read once, o written once, the final state written once."""
+    read once, o written once, the final state written once. The default is the
+    survey's unit for the roofline: bf16 q, k, v and o, float32 alpha and beta,
+    1032 B per token and head at d = 128; out_bytes=4 gives the float32 output
+    the library writes by default (1288 B)."""
     per_tok = (2 * dk + dv) * in_bytes + 8 + extra_per_token + dv * out_bytes
     return B * H * L * per_tok + (B * H * dk * dv * 4 if state_out else 0)
 
@@ -125,7 +131,53 @@ def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True, cold=False):
+class HipTimer:
+    """HIP events created with hipEventDisableSystemFence, recorded on a given
+    stream: timing-only events that skip the system-scope cache writeback and
+    invalidate of a default event, which would otherwise land between the two
+    kernels of a step and cool the caches the second one reads. Uses the HIP
+    runtime already loaded in this process (torch's, which libkdn.so binds to)."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, torch):
+        import ctypes
+        self.ct = ctypes
+        torch.cuda.init()
+        paths = [ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln]
+        if not paths:
+            raise RuntimeError("no HIP runtime loaded in this process")
+        self.hip = ctypes.CDLL(paths[0])
+        self.events = []
+
+    def event(self):
+        e = self.ct.c_void_p()
+        rc = self.hip.hipEventCreateWithFlags(self.ct.byref(e), self.ct.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags: {rc}")
+        self.events.append(e)
+        return e
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(e, self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord: {rc}")
+
+    def ms(self, a, b):
+        out = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(out), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime: {rc}")
+        return out.value
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
+def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True, cold=False,
+               keep=False):
     import workloads
     cfg = workloads.WORKLOADS[name]
     B, H, L, dk, dv, C = cfg["B"], cfg["H"], cfg["L"], cfg["dk"], cfg["dv"], cfg["chunk"]
@@ -177,16 +229,31 @@ def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True, co
         res["cold_ms_per_step"] = cms
         del flush
     if per_phase:
-        ev = _events(torch, 3 * steps)
+        # the step as above, split into its two phases with a fence-less event
+        # before, between and after them on the stream the kernels run on: the
+        # state kernel is timed in its own context (right after the prepare
+        # kernel that writes what it reads), and the events do not flush the
+        # caches between the two
+        tm = HipTimer(torch)
+        stream = torch.cuda.current_stream()
+        ev = [tm.event() for _ in range(3 * steps)]
         for i in range(steps):
-            ev[3 * i].record()
+            tm.record(ev[3 * i], stream)
             step("prepare")
-            ev[3 * i + 1].record()
+            tm.record(ev[3 * i + 1], stream)
             step("state")
-            ev[3 * i + 2].record()
+            tm.record(ev[3 * i + 2], stream)
         torch.cuda.synchronize()
-        res["prepare_ms"] = sum(ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(steps)) / steps
-        res["state_ms"] = sum(ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(steps)) / steps
+        res["prepare_ms"] = sum(tm.ms(ev[3 * i], ev[3 * i + 1]) for i in range(steps)) / steps
+        res["state_ms"] = sum(tm.ms(ev[3 * i + 1], ev[3 * i + 2]) for i in range(steps)) / steps
+        tm.close()
+    if keep:
+        step()
+        torch.cuda.synchronize()
+        res["o"] = o.cpu().numpy()
+        res["S"] = s_out.cpu().numpy()
+        if cov_out is not None:
+            res["cov"] = cov_out.cpu().numpy()
     return res
 
 
@@ -272,7 +339,11 @@ def bench_backward(kdn, torch, steps, warmup):
                        "chunked (64 tokens)")
 
 
-def bench_decode(kdn, torch, steps, warmup):
+# heads of the decode workload whose outputs the oracle leg re-derives
+DECODE_PARITY_HEADS = [(b, h) for b in (0, 37, 128, 255) for h in (0, 9, 20, 31)]
+
+
+def bench_decode(kdn, torch, steps, warmup, keep=None):
     """Decode + HOLA cache at B=256, H=32, d=128, w=64, timed after the cache is full."""
     import workloads
     cfg = workloads.WORKLOADS["decode"]
@@ -309,6 +380,12 @@ def bench_decode(kdn, torch, steps, warmup):
     torch.cuda.synchronize()
     ms = timed(step)
     gbs = B * H * DECODE_BYTES_PER_HEAD / (ms * 1e-3) / 1e9
+    if keep is not None:
+        # after all `total` steps once: the state, and the last step's outputs, of a few heads
+        bs = [b for b, _ in DECODE_PARITY_HEADS]
+        hs = [h for _, h in DECODE_PARITY_HEADS]
+        keep["decode"] = dict(steps=total, S=state[bs, hs].cpu().numpy(), o=o[bs, hs].cpu().numpy(),
+                              o_cache=oc[bs, hs].cpu().numpy(), m=m[bs, hs].cpu().numpy())
     # the same steps captured once into a HIP graph and replayed (the state and
     # the cache keep evolving, so every replay does a full step's work)
     graph = torch.cuda.CUDAGraph()
@@ -334,10 +411,86 @@ def bench_decode(kdn, torch, steps, warmup):
                        "kdn_step_decode + hola_cache_update per step")
 
 
-def cpu_baseline(name="gated", seconds_target=15.0):
-    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
-    all (batch, head) sequences at full length, repeated until about
-    `seconds_target` seconds of host time, on all host threads."""
+def bench_tiny(kdn, torch, reps=200, keep=None):
+    """The tiny float32 workload (1 head, d = 16, L = 64, alpha = 1): the delta
+    write (chunk 16) and recursive least squares (full covariance, eps = 1e-2).
+    Latency per call: GPU time from events around `reps` back-to-back calls,
+    and host wall time of one call followed by a synchronisation."""
+    import numpy as np
+    import workloads
+    inp = workloads.named_scan_inputs("tiny")
+    dev = torch.device("cuda:0")
+    t = {n: torch.from_numpy(inp[n]).to(dev) for n in ("q", "k", "v", "alpha", "beta")}
+    d, eps = 16, 1e-2
+    P0 = torch.from_numpy((np.eye(d) / eps).astype(np.float32))[None, None].to(dev)
+    S = torch.empty((1, 1, d, d), device=dev)
+    P = torch.empty_like(P0)
+    o = torch.empty((1, 1, 64, d), device=dev)
+    calls = {
+        "delta": lambda: kdn.kdn_scan_fwd(t["q"], t["k"], t["v"], alpha=t["alpha"],
+                                          beta=t["beta"], state_out=S, o=o, chunk=16),
+        "rls": lambda: kdn.kdn_scan_fwd(t["q"], t["k"], t["v"], cov_in=P0, cov_out=P,
+                                        state_out=S, o=o, chunk=16, mode="full"),
+    }
+    out = {}
+    for name, fn in calls.items():
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = _events(torch, 2)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        gpu_us = e0.elapsed_time(e1) * 1e3 / reps
+        walls = []
+        for _ in range(50):
+            w0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            walls.append(time.perf_counter() - w0)
+        walls.sort()
+        out[name] = dict(gpu_us_per_call=round(gpu_us, 2),
+                         host_us_per_synchronous_call=round(walls[len(walls) // 2] * 1e6, 1))
+        if keep is not None:
+            fn()
+            torch.cuda.synchronize()
+            keep[f"tiny/{name}"] = dict(o=o.cpu().numpy(), S=S.cpu().numpy(),
+                                        cov=P.cpu().numpy() if name == "rls" else None)
+    out["config"] = "1 head, d_k = d_v = 16, L = 64, float32, alpha = 1; delta write (chunk 16), " \
+                    "RLS (full covariance, eps = 1e-2)"
+    return out
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _rel(got, ref):
+    import numpy as np
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return float(np.max(np.abs(got - ref)) / rms) if rms > 0 else float(np.max(np.abs(got - ref)))
+
+
+def oracle_leg(kept, name="gated", seconds_target=15.0):
+    """The CPU baseline and the parity of the benchmark's own outputs, both from
+    the fp64 oracle as it stands. Baseline: the whole gated workload (every
+    (batch, head) sequence at full length), repeated until about
+    `seconds_target` seconds of host time, on all host threads. Parity: each
+    workload the benchmark ran is recomputed by the oracle from the same seeded
+    inputs and compared with the output the GPU produced in this run:
+    max|x - x_oracle| / RMS(x_oracle) for o, the final state and the final
+    covariance (decode: a sample of heads after all its steps)."""
+    import numpy as np
     import oracle
     import workloads
     cfg = workloads.WORKLOADS[name]
@@ -348,10 +501,10 @@ def cpu_baseline(name="gated", seconds_target=15.0):
     threads = oracle.num_threads()
 
     def run():
-        oracle.scan(q, k, v, alpha=a, beta=b, want_m=False)
+        return oracle.scan(q, k, v, alpha=a, beta=b, want_m=False)
 
     t0 = time.perf_counter()
-    run()
+    first = run()
     t1 = time.perf_counter() - t0
     reps = max(1, int(round(seconds_target / max(t1, 1e-3))) - 1)
     t0 = time.perf_counter()
@@ -359,31 +512,95 @@ def cpu_baseline(name="gated", seconds_target=15.0):
         run()
     dt = time.perf_counter() - t0 + t1
     token_heads_per_s = (reps + 1) * B * H * L / dt
-    return dict(value=round(token_heads_per_s / H, 1), unit="tokens/s", cores=threads,
-                kind="oracle",
-                sample=f"the whole gated workload ({B * H} (batch, head) sequences of length {L}) "
-                       f"{reps + 1} times, fp64 sequential recurrence, {dt:.1f} s; "
-                       f"tokens/s = token-heads/s / H")
+    baseline = dict(value=round(token_heads_per_s / H, 1), unit="tokens/s", cores=threads,
+                    cpu_model=_cpu_model(), kind="oracle",
+                    sample=f"the whole gated workload ({B * H} (batch, head) sequences of length "
+                           f"{L}) {reps + 1} times, fp64 sequential recurrence, {dt:.1f} s; "
+                           f"tokens/s = token-heads/s / H")
+    parity = {}
+    g = kept.get("gated/delta")
+    if g is not None:
+        parity["gated"] = dict(o=_rel(g["o"].reshape(first["o"].shape), first["o"]),
+                               S=_rel(g["S"].reshape(first["S"].shape), first["S"]), tol=2e-2)
+    del first
+    for key, (wl, mode) in {"kdn_diag/diag": ("kdn_diag", "diag"), "kdn_diag/iso": ("kdn_diag", "iso"),
+                            "long/delta": ("long", "delta")}.items():
+        got = kept.get(key)
+        if got is None:
+            continue
+        c = workloads.WORKLOADS[wl]
+        x = workloads.named_scan_inputs(wl)
+        cshape = {"diag": (c["B"], c["H"], c["dk"]), "iso": (c["B"], c["H"])}.get(mode)
+        cov0 = np.full(cshape, c.get("cov_init", 1.0), np.float32) if cshape else None
+        ref = oracle.scan(x["q"], x["k"], x["v"], alpha=x["alpha"], beta=x["beta"], r=x["r"],
+                          cov0=cov0, q_noise_var=c.get("q_noise_var", 0.0), mode=mode, want_m=False)
+        del x
+        e = dict(o=_rel(got["o"], ref["o"]), S=_rel(got["S"], ref["S"]), tol=2e-2)
+        if cov0 is not None:
+            e["cov"] = _rel(got["cov"], ref["cov"])
+            e["cov_tol"] = 1e-4
+        parity[key.replace("kdn_diag/", "kdn_")] = e
+        del ref
+    tiny = workloads.named_scan_inputs("tiny")
+    for nm in ("delta", "rls"):
+        got = kept.get(f"tiny/{nm}")
+        if got is None:
+            continue
+        if nm == "delta":
+            ref = oracle.scan(tiny["q"], tiny["k"], tiny["v"], alpha=tiny["alpha"], beta=tiny["beta"])
+        else:
+            P0 = (np.eye(16) / 1e-2)[None, None]
+            ref = oracle.scan(tiny["q"], tiny["k"], tiny["v"], cov0=P0, mode="full")
+        e = dict(o=_rel(got["o"], ref["o"]), S=_rel(got["S"], ref["S"]), tol=1e-4)
+        if got["cov"] is not None:
+            e["cov"] = _rel(got["cov"], ref["cov"])
+        parity[f"tiny_{nm}"] = e
+    dec = kept.get("decode")
+    if dec is not None:
+        c = workloads.WORKLOADS["decode"]
+        bs = np.array([x for x, _ in DECODE_PARITY_HEADS])
+        hs = np.array([x for _, x in DECODE_PARITY_HEADS])
+        steps = []
+        for i in range(dec["steps"]):
+            st = workloads.decode_step_inputs(i, c["B"], c["H"], c["dk"], c["dv"])
+            steps.append({n: np.ascontiguousarray(x[bs, hs][None]) for n, x in st.items()})
+        o_ref, oc_ref, m_ref, S_ref, _, _ = oracle.decode_run(steps, 1, len(bs), c["dk"], c["dv"], c["w"])
+        parity["decode"] = dict(o=_rel(dec["o"], o_ref[-1][0]), o_cache=_rel(dec["o_cache"], oc_ref[-1][0]),
+                                m=_rel(dec["m"], m_ref[-1][0]), S=_rel(dec["S"], S_ref[0]), tol=1e-4,
+                                heads=len(bs), steps=dec["steps"])
+    for v_ in parity.values():
+        for kk in list(v_):
+            if isinstance(v_[kk], float) and kk not in ("tol", "cov_tol"):
+                v_[kk] = float(f"{v_[kk]:.3e}")
+    return baseline, parity
 
 
 def _extra_scan(name, mode):
-    def run(kdn, torch, args):
-        r = bench_scan(kdn, torch, name, max(2, args.steps // 4), 1, mode=mode, per_phase=True)
+    def run(kdn, torch, args, keep=None):
+        r = bench_scan(kdn, torch, name, max(2, args.steps // 4), 1, mode=mode, per_phase=True,
+                       keep=keep is not None)
         nb = scan_bytes(r["B"], r["H"], r["L"], r["dk"], r["dv"],
                         extra_per_token=4 if mode in ("diag", "iso") else 0)
+        if keep is not None:
+            keep[f"{name}/{mode}"] = {k: r[k] for k in ("o", "S", "cov") if k in r}
+        flops = r["B"] * r["H"] * r["L"] * scan_flops_per_token_head(r["C"], r["dk"], r["dv"])
         return dict(ms_per_step=round(r["ms_per_step"], 5), tokens_per_s=round(r["tokens_per_s"], 1),
                     prepare_ms=round(r["prepare_ms"], 5), state_ms=round(r["state_ms"], 5),
-                    hbm_frac_step=round(nb / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+                    algorithmic_bytes=nb,
+                    hbm_frac_step=round(nb / (r["ms_per_step"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    hbm_frac_state_kernel=round(nb / (r["state_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    mfma_frac_step=round(flops / (r["ms_per_step"] * 1e-3) / 1e12
+                                         / MFMA_F16_PEAK_TFLOPS, 4))
     return run
 
 
 # the extra workloads, in the order the full run reports them
 EXTRAS = {
-    "decode": lambda kdn, torch, args: bench_decode(kdn, torch, steps=max(8, args.steps),
-                                                    warmup=args.warmup),
-    "prompt_cache": lambda kdn, torch, args: bench_prefill(kdn, torch,
-                                                           steps=max(2, args.steps // 4), warmup=1),
-    "backward": lambda kdn, torch, args: bench_backward(kdn, torch, steps=2, warmup=1),
+    "decode": lambda kdn, torch, args, keep=None: bench_decode(kdn, torch, steps=max(8, args.steps),
+                                                               warmup=args.warmup, keep=keep),
+    "prompt_cache": lambda kdn, torch, args, keep=None: bench_prefill(
+        kdn, torch, steps=max(2, args.steps // 4), warmup=1),
+    "backward": lambda kdn, torch, args, keep=None: bench_backward(kdn, torch, steps=2, warmup=1),
     "kdn_diag": _extra_scan("kdn_diag", "diag"),
     "kdn_iso": _extra_scan("kdn_diag", "iso"),
     "long": _extra_scan("long", "delta"),
@@ -427,10 +644,17 @@ def main():
         print(json.dumps({"only": args.only, args.only: res}), flush=True)
         return
 
-    main_res = bench_scan(kdn, torch, "gated", args.steps, args.warmup, cold=not args.quick)
+    want_parity = not args.no_cpu_baseline
+    kept = {}
+    main_res = bench_scan(kdn, torch, "gated", args.steps, args.warmup, cold=not args.quick,
+                          keep=want_parity)
+    if want_parity:
+        kept["gated/delta"] = {k: main_res.pop(k) for k in ("o", "S")}
     B, H, L, dk, dv, C = (main_res[k] for k in ("B", "H", "L", "dk", "dv", "C"))
-    nbytes = scan_bytes(B, H, L, dk, dv)
-    flops = B * H * L * scan_flops_per_token_head(C, dk, dv)
+    token_heads = B * H * L
+    nbytes = scan_bytes(B, H, L, dk, dv)            # bf16 o: the survey's 1032 B per token-head
+    nbytes_f32o = scan_bytes(B, H, L, dk, dv, out_bytes=4)
+    flops = token_heads * scan_flops_per_token_head(C, dk, dv)
     state_s = main_res["state_ms"] * 1e-3
     achieved = nbytes / state_s / 1e9
     rec = counter_record()
@@ -456,7 +680,16 @@ def main():
                      "traffic": measured_traffic(main_res["state_ms"]),
                      "kernel": "state_kernel (sequential chunk-state scan)",
                      "kernel_ms": round(main_res["state_ms"], 5),
-                     "algorithmic_bytes": nbytes},
+                     "algorithmic_bytes": nbytes,
+                     "bytes_per_token_head": scan_bytes(B, H, L, dk, dv, state_out=False) // token_heads,
+                     "algorithmic_bytes_note": "1032 B per token-head (bf16 q, k, v, o; float32 "
+                                               "alpha, beta) x 262144 token-heads + the float32 "
+                                               "final state (65536 B per head)",
+                     # the library writes float32 o by default: 256 B more per token-head
+                     "algorithmic_bytes_f32_output": nbytes_f32o,
+                     "frac_f32_output": round(nbytes_f32o / state_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "step_frac": round(nbytes / (main_res["ms_per_step"] * 1e-3) / 1e9
+                                        / HBM_PEAK_GBS, 4)},
         "mfma": {"algorithmic_tflops_per_step": round(flops / 1e12, 3),
                  "frac_of_peak_step": round(flops / (main_res["ms_per_step"] * 1e-3) / 1e12
                                             / MFMA_F16_PEAK_TFLOPS, 4),
@@ -470,20 +703,27 @@ def main():
                      round(rec["mfma_executed_flops"] / state_s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)),
                  "busy_frac_state_kernel": None if rec is None else rec["mfma_busy_frac"]},
         "phases_ms": {"prepare": round(main_res["prepare_ms"], 5),
-                      "state": round(main_res["state_ms"], 5)},
+                      "state": round(main_res["state_ms"], 5),
+                      "note": "each phase bracketed by fence-less HIP events inside the step "
+                              "sequence, on the stream the kernels run on"},
     }
+    line["tiny"] = bench_tiny(kdn, torch, keep=kept if want_parity else None)
     if not args.quick:
-        line["cold"] = {"ms_per_step": round(main_res["cold_ms_per_step"], 5),
-                        "tokens_per_s": round(B * L / (main_res["cold_ms_per_step"] * 1e-3), 1),
-                        "note": "256 MB last-level cache flushed by a 512 MiB write before each step"}
+        cms = main_res["cold_ms_per_step"]
+        line["cold"] = {"ms_per_step": round(cms, 5),
+                        "tokens_per_s": round(B * L / (cms * 1e-3), 1),
+                        "roofline_frac_step": round(nbytes / (cms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "mfma_frac_step": round(flops / (cms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4),
+                        "note": "256 MB last-level cache flushed by a 512 MiB write before each "
+                                "step; fractions over the whole step (both kernels)"}
         line["roofline"]["attainable_copy_gbs"] = copy_bandwidth(torch)
         extra = {}
         for key, fn in EXTRAS.items():
-            extra[key] = fn(kdn, torch, args)
+            extra[key] = fn(kdn, torch, args, keep=kept if want_parity else None)
             torch.cuda.empty_cache()
         line["extra"] = extra
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
+    if want_parity:
+        line["cpu_baseline"], line["parity"] = oracle_leg(kept)
     print(json.dumps(line), flush=True)
 
 

@@ -14,16 +14,17 @@ import bench  # noqa: E402
 
 
 def test_scan_bytes_headline():
-    """Gated workload B=4 H=16 L=4096 d=128: bf16 q, k, v read once (768 B per
-    token and head), float32 alpha and beta (8 B), float32 o written once
-    (512 B), and the float32 final state of every head."""
+    """Gated workload B=4 H=16 L=4096 d=128, the roofline's unit: bf16 q, k, v
+    read once (768 B per token and head), float32 alpha and beta (8 B), bf16 o
+    written once (256 B): 1032 B, plus the float32 final state of every head;
+    with the float32 output the library writes by default, 1288 B."""
     B, H, L, d = 4, 16, 4096, 128
     tokens = B * H * L
-    expect = tokens * (3 * d * 2 + 8 + d * 4) + B * H * d * d * 4
-    assert bench.scan_bytes(B, H, L, d, d) == expect == 341_835_776
-    # without the final state, and with bf16 outputs
-    assert bench.scan_bytes(B, H, L, d, d, state_out=False) == tokens * 1288
-    assert bench.scan_bytes(B, H, L, d, d, out_bytes=2, state_out=False) == tokens * 1032
+    expect = tokens * (3 * d * 2 + 8 + d * 2) + B * H * d * d * 4
+    assert bench.scan_bytes(B, H, L, d, d) == expect == 274_726_912
+    assert bench.scan_bytes(B, H, L, d, d, state_out=False) == tokens * 1032
+    assert bench.scan_bytes(B, H, L, d, d, out_bytes=4) == 341_835_776
+    assert bench.scan_bytes(B, H, L, d, d, out_bytes=4, state_out=False) == tokens * 1288
 
 
 def test_scan_flops_per_token_head():
