@@ -64,6 +64,9 @@ def _load():
         lib.oracle_hola_prefill.restype = i
         lib.oracle_scan_bwd.argtypes = [i, i, i, i, i, P, P, P, P, P, P, P, P, i, P, P, P, P, P, P]
         lib.oracle_scan_bwd.restype = i
+        lib.oracle_scan_bwd_kalman.argtypes = [i, i, i, i, i, P, P, P, P, P, P, d, P, P, P, P, i,
+                                               P, P, P, P, P, P, P]
+        lib.oracle_scan_bwd_kalman.restype = i
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = i
         _lib = lib
@@ -134,6 +137,37 @@ def scan_bwd(q, k, v, alpha=None, beta=None, S0=None, d_o=None, dS=None,
                                  _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dS0"]))
     if rc != 0:
         raise ValueError(f"oracle_scan_bwd rejected the arguments (status {rc})")
+    return out
+
+
+def scan_bwd_kalman(q, k, v, alpha=None, r=None, cov0=None, q_noise_var: float = 0.0, S0=None,
+                    d_o=None, dS=None, dcov=None, mode: str = "diag") -> dict:
+    """Gradients of the Kalman writes (mode "diag": cov [B,H,dk]; "iso": cov [B,H];
+    gated residual) for the loss sum(d_o * o) + sum(dS * S_L) + sum(dcov * cov_L)
+    (fp64 adjoint, see kdn_oracle.c). Returns dict(dq, dk, dv, dalpha, dr, dcov0, dS0)."""
+    q, k, v = _f32(q), _f32(k), _f32(v)
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    alpha, r = _f32(alpha), _f32(r)
+    cshape = (B, H, dk) if mode == "diag" else (B, H)
+    cov0 = np.ascontiguousarray(np.broadcast_to(cov0, cshape), dtype=np.float64)
+    S0 = None if S0 is None else np.ascontiguousarray(S0, dtype=np.float64)
+    d_o = np.ascontiguousarray(d_o, dtype=np.float64)
+    assert d_o.shape == (B, H, L, dv)
+    dS = None if dS is None else np.ascontiguousarray(dS, dtype=np.float64)
+    dcov = None if dcov is None else np.ascontiguousarray(np.broadcast_to(dcov, cshape),
+                                                          dtype=np.float64)
+    out = dict(dq=np.zeros((B, H, L, dk)), dk=np.zeros((B, H, L, dk)), dv=np.zeros((B, H, L, dv)),
+               dalpha=np.zeros((B, H, L)), dr=np.zeros((B, H, L)), dcov0=np.zeros(cshape),
+               dS0=np.zeros((B, H, dk, dv)))
+    rc = _load().oracle_scan_bwd_kalman(B, H, L, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                        _ptr(r), _ptr(cov0), float(q_noise_var), _ptr(S0),
+                                        _ptr(d_o), _ptr(dS), _ptr(dcov), MODES[mode],
+                                        _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                        _ptr(out["dalpha"]), _ptr(out["dr"]), _ptr(out["dcov0"]),
+                                        _ptr(out["dS0"]))
+    if rc != 0:
+        raise ValueError(f"oracle_scan_bwd_kalman rejected the arguments (status {rc})")
     return out
 
 

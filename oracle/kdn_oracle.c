@@ -385,6 +385,255 @@ int oracle_hola_step(int B, int H, int dk, int dv, int w,
     return 0;
 }
 
+/*
+ * Gradients of the Kalman writes, modes DIAG and ISO (gated residual), one
+ * (batch, head) at a time: the adjoint of the per-token recursion of
+ * scan_one, derived by hand and pinned in the tests by finite differences of
+ * oracle_scan. Forward, per token (pm = p-, Q = (1 - a^2) sigma^2):
+ *   DIAG: pm_i = a^2 p_i + Q,  s = sum_i pm_i k_i^2 + r,  b_i = pm_i k_i / s,
+ *         p'_i = pm_i r / D_i,  D_i = r + pm_i k_i^2
+ *   ISO : pm = a^2 p + Q,  kk = |k|^2,  s = pm kk + r,  b = (pm / s) k,
+ *         p' = pm d r / D,  D = d r + pm kk   (d = d_k)
+ *   e = v - a S^T k,  S' = a S + b e^T,  o = S'^T q.
+ * Backward, with G = dL/dS' (after adding q do^T) and dp = dL/dp':
+ *   dq = S' do,  y = G^T b,  dv = y,  db = G e,
+ *   dk = -a S y + (gain terms),  da = <G, S> - y . (S^T k) + (covariance terms),
+ *   G <- a G - a k y^T.
+ * The gain and covariance terms follow from the chain rule through b and p':
+ *   DIAG: ds = -(db . b) / s;  dpm_i = db_i k_i / s + ds k_i^2 + dp_i r^2 / D_i^2;
+ *         dk_i += db_i pm_i / s + 2 ds pm_i k_i - 2 dp_i pm_i^2 r k_i / D_i^2;
+ *         dr = ds + sum_i dp_i pm_i^2 k_i^2 / D_i^2
+ *   ISO : dbeta = db . k;  dk_i += (pm / s) db_i;
+ *         dpm = dbeta r / s^2 + dp (d r)^2 / D^2;
+ *         dkk = -dbeta pm^2 / s^2 - dp pm^2 d r / D^2;  dk_i += 2 dkk k_i;
+ *         dr = -dbeta pm / s^2 + dp pm^2 d kk / D^2
+ *   both: dp <- a^2 dpm;  da += 2 a sum dpm (p - sigma^2).
+ * At the start dp = dL/dp_L (dcovL, or 0) and G = dL/dS_L (dSL, or 0); at the
+ * end dcov0 = dp and dS0 = G. States are recomputed from checkpoints every 64
+ * tokens; the covariance before every token is kept.
+ *
+ *   mode ORC_DIAG (cov [B,H,dk]) or ORC_ISO (cov [B,H]); cov0, dcovL float64;
+ *   other inputs as oracle_scan_bwd (r may be NULL = 1; alpha NULL = 1).
+ *   outputs float64: dq, dk [B,H,L,dk]; dv [B,H,L,dv]; dalpha, dr [B,H,L];
+ *   dcov0 like cov0; dS0 [B,H,dk,dv] (dcov0 and dS0 may be NULL).
+ */
+int oracle_scan_bwd_kalman(int B, int H, int L, int dk, int dv,
+                           const float *q, const float *k, const float *v,
+                           const float *alpha, const float *r, const double *cov0,
+                           double qvar, const double *S0, const double *d_o,
+                           const double *dSL, const double *dcovL, int mode,
+                           double *dq, double *dkk, double *dvv, double *dalpha, double *dr,
+                           double *dcov0, double *dS0)
+{
+    if (mode != ORC_DIAG && mode != ORC_ISO) return -1;
+    const int CK = 64;
+    const int nck = (L + CK - 1) / CK;
+    const int BH = B * H;
+    const size_t SS = (size_t)dk * dv;
+    const int np = mode == ORC_DIAG ? dk : 1;   /* covariance entries per head */
+    int bad = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < BH; ++bh) {
+        double *ckpt = (double *)malloc(sizeof(double) * SS * (size_t)(nck + 1));
+        double *hist = (double *)malloc(sizeof(double) * SS * (size_t)(CK + 1));
+        double *G = (double *)malloc(sizeof(double) * SS);
+        double *ph = (double *)malloc(sizeof(double) * (size_t)np * (size_t)(L + 1));
+        double *vec = (double *)malloc(sizeof(double) * (size_t)(3 * dv + 5 * dk));
+        if (!ckpt || !hist || !G || !ph || !vec) {
+#pragma omp atomic write
+            bad = 1;
+            free(ckpt); free(hist); free(G); free(ph); free(vec);
+            continue;
+        }
+        double *y = vec, *e = y + dv, *pr = e + dv;          /* dv each */
+        double *b = pr + dv, *pm = b + dk, *db = pm + dk;    /* dk each */
+        double *dpm = db + dk, *dp = dpm + dk;               /* dk each */
+        const float *qh = q + (size_t)bh * L * dk, *kh = k + (size_t)bh * L * dk;
+        const float *vh = v + (size_t)bh * L * dv;
+        const float *ah = alpha ? alpha + (size_t)bh * L : NULL;
+        const float *rh = r ? r + (size_t)bh * L : NULL;
+        const double *doh = d_o + (size_t)bh * L * dv;
+
+        /* covariance before every token: ph[t * np ..] = p_{t-1} (ph[0] = p_0) */
+        for (int i = 0; i < np; ++i) ph[i] = cov0[(size_t)bh * np + i];
+        for (int t = 0; t < L; ++t) {
+            const double a = ah ? (double)ah[t] : 1.0, rt = rh ? (double)rh[t] : 1.0;
+            const double Qt = (1.0 - a * a) * qvar;
+            const float *kt = kh + (size_t)t * dk;
+            const double *pp = ph + (size_t)t * np;
+            double *pn = ph + (size_t)(t + 1) * np;
+            if (mode == ORC_DIAG) {
+                for (int i = 0; i < dk; ++i) {
+                    const double m_ = a * a * pp[i] + Qt, k2 = (double)kt[i] * kt[i];
+                    pn[i] = m_ * rt / (rt + m_ * k2);
+                }
+            } else {
+                double kk = 0.0;
+                for (int i = 0; i < dk; ++i) kk += (double)kt[i] * kt[i];
+                const double m_ = a * a * pp[0] + Qt;
+                pn[0] = m_ * dk * rt / (dk * rt + m_ * kk);
+            }
+        }
+        /* the write vector b of token t (and pm, s) from p_{t-1} */
+        #define ORC_GAIN(t_, s_out)                                                  \
+            do {                                                                     \
+                const double a_ = ah ? (double)ah[t_] : 1.0;                         \
+                const double r_ = rh ? (double)rh[t_] : 1.0;                         \
+                const double Q_ = (1.0 - a_ * a_) * qvar;                            \
+                const float *k_ = kh + (size_t)(t_) * dk;                            \
+                const double *p_ = ph + (size_t)(t_) * np;                           \
+                double s_ = r_;                                                      \
+                if (mode == ORC_DIAG) {                                              \
+                    for (int i = 0; i < dk; ++i) {                                   \
+                        pm[i] = a_ * a_ * p_[i] + Q_;                                \
+                        s_ += pm[i] * (double)k_[i] * (double)k_[i];                 \
+                    }                                                                \
+                    for (int i = 0; i < dk; ++i) b[i] = pm[i] * (double)k_[i] / s_;  \
+                } else {                                                             \
+                    double kk_ = 0.0;                                                \
+                    for (int i = 0; i < dk; ++i) kk_ += (double)k_[i] * k_[i];       \
+                    pm[0] = a_ * a_ * p_[0] + Q_;                                    \
+                    s_ = pm[0] * kk_ + r_;                                           \
+                    for (int i = 0; i < dk; ++i) b[i] = pm[0] * (double)k_[i] / s_;  \
+                }                                                                    \
+                s_out = s_;                                                          \
+            } while (0)
+
+        /* forward: state checkpoints at t = 0, 64, ... (the state before token t) */
+        double *S = hist;
+        for (size_t i = 0; i < SS; ++i) S[i] = S0 ? S0[(size_t)bh * SS + i] : 0.0;
+        for (int t = 0; t < L; ++t) {
+            if (t % CK == 0) memcpy(ckpt + SS * (size_t)(t / CK), S, sizeof(double) * SS);
+            double s;
+            ORC_GAIN(t, s);
+            (void)s;
+            const double a = ah ? (double)ah[t] : 1.0;
+            const float *kt = kh + (size_t)t * dk, *vt = vh + (size_t)t * dv;
+            for (int j = 0; j < dv; ++j) {
+                double p_ = 0.0;
+                for (int i = 0; i < dk; ++i) p_ += S[(size_t)i * dv + j] * (double)kt[i];
+                e[j] = (double)vt[j] - a * p_;
+            }
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j)
+                    S[(size_t)i * dv + j] = a * S[(size_t)i * dv + j] + b[i] * e[j];
+        }
+        for (size_t i = 0; i < SS; ++i) G[i] = dSL ? dSL[(size_t)bh * SS + i] : 0.0;
+        for (int i = 0; i < np; ++i) dp[i] = dcovL ? dcovL[(size_t)bh * np + i] : 0.0;
+
+        for (int ck = nck - 1; ck >= 0; --ck) {
+            const int t0 = ck * CK, t1 = (t0 + CK < L) ? t0 + CK : L;
+            memcpy(hist, ckpt + SS * (size_t)ck, sizeof(double) * SS);
+            for (int t = t0; t < t1; ++t) {
+                const double *Sp = hist + SS * (size_t)(t - t0);
+                double *Sn = hist + SS * (size_t)(t - t0 + 1);
+                double s;
+                ORC_GAIN(t, s);
+                (void)s;
+                const double a = ah ? (double)ah[t] : 1.0;
+                const float *kt = kh + (size_t)t * dk, *vt = vh + (size_t)t * dv;
+                for (int j = 0; j < dv; ++j) {
+                    double p_ = 0.0;
+                    for (int i = 0; i < dk; ++i) p_ += Sp[(size_t)i * dv + j] * (double)kt[i];
+                    e[j] = (double)vt[j] - a * p_;
+                }
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j)
+                        Sn[(size_t)i * dv + j] = a * Sp[(size_t)i * dv + j] + b[i] * e[j];
+            }
+            for (int t = t1 - 1; t >= t0; --t) {
+                const double *Sp = hist + SS * (size_t)(t - t0);      /* S_{t-1} */
+                const double *Sn = hist + SS * (size_t)(t - t0 + 1);  /* S_t */
+                double s;
+                ORC_GAIN(t, s);
+                const double a = ah ? (double)ah[t] : 1.0, rt = rh ? (double)rh[t] : 1.0;
+                const float *kt = kh + (size_t)t * dk, *vt = vh + (size_t)t * dv;
+                const float *qt = qh + (size_t)t * dk;
+                const double *dot = doh + (size_t)t * dv;
+                const double *pprev = ph + (size_t)t * np;            /* p_{t-1} */
+                const size_t tok = (size_t)bh * L + t;
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j) G[(size_t)i * dv + j] += (double)qt[i] * dot[j];
+                for (int i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j) acc += Sn[(size_t)i * dv + j] * dot[j];
+                    dq[tok * dk + i] = acc;
+                }
+                for (int j = 0; j < dv; ++j) {
+                    double yy = 0.0, p_ = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        yy += G[(size_t)i * dv + j] * b[i];
+                        p_ += Sp[(size_t)i * dv + j] * (double)kt[i];
+                    }
+                    y[j] = yy;
+                    pr[j] = p_;
+                    e[j] = (double)vt[j] - a * p_;
+                }
+                double yp = 0.0, gs = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    dvv[tok * dv + j] = y[j];
+                    yp += y[j] * pr[j];
+                }
+                for (size_t i = 0; i < SS; ++i) gs += G[i] * Sp[i];
+                double da = gs - yp;
+                for (int i = 0; i < dk; ++i) {
+                    double ge = 0.0, sy = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        ge += G[(size_t)i * dv + j] * e[j];
+                        sy += Sp[(size_t)i * dv + j] * y[j];
+                    }
+                    db[i] = ge;
+                    dkk[tok * dk + i] = -a * sy;
+                }
+                /* gain and covariance */
+                double drt = 0.0;
+                if (mode == ORC_DIAG) {
+                    double dbb = 0.0;
+                    for (int i = 0; i < dk; ++i) dbb += db[i] * b[i];
+                    const double ds = -dbb / s;
+                    drt = ds;
+                    for (int i = 0; i < dk; ++i) {
+                        const double ki = (double)kt[i], k2 = ki * ki;
+                        const double D = rt + pm[i] * k2, D2 = D * D;
+                        dpm[i] = db[i] * ki / s + ds * k2 + dp[i] * rt * rt / D2;
+                        dkk[tok * dk + i] += db[i] * pm[i] / s + 2.0 * ds * pm[i] * ki
+                                             - 2.0 * dp[i] * pm[i] * pm[i] * rt * ki / D2;
+                        drt += dp[i] * pm[i] * pm[i] * k2 / D2;
+                    }
+                    for (int i = 0; i < dk; ++i) {
+                        da += 2.0 * a * dpm[i] * (pprev[i] - qvar);
+                        dp[i] = a * a * dpm[i];
+                    }
+                } else {
+                    double kk = 0.0, dbeta = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        kk += (double)kt[i] * kt[i];
+                        dbeta += db[i] * (double)kt[i];
+                    }
+                    const double m_ = pm[0], beta_ = m_ / s, D = dk * rt + m_ * kk, D2 = D * D;
+                    const double dpm0 = dbeta * rt / (s * s) + dp[0] * (dk * rt) * (dk * rt) / D2;
+                    const double dkk2 = -dbeta * m_ * m_ / (s * s) - dp[0] * m_ * m_ * dk * rt / D2;
+                    drt = -dbeta * m_ / (s * s) + dp[0] * m_ * m_ * dk * kk / D2;
+                    for (int i = 0; i < dk; ++i)
+                        dkk[tok * dk + i] += beta_ * db[i] + 2.0 * dkk2 * (double)kt[i];
+                    da += 2.0 * a * dpm0 * (pprev[0] - qvar);
+                    dp[0] = a * a * dpm0;
+                }
+                dalpha[tok] = da;
+                dr[tok] = drt;
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j)
+                        G[(size_t)i * dv + j] = a * G[(size_t)i * dv + j] - a * (double)kt[i] * y[j];
+            }
+        }
+        #undef ORC_GAIN
+        if (dS0) memcpy(dS0 + (size_t)bh * SS, G, sizeof(double) * SS);
+        if (dcov0) memcpy(dcov0 + (size_t)bh * np, dp, sizeof(double) * (size_t)np);
+        free(ckpt); free(hist); free(G); free(ph); free(vec);
+    }
+    return bad ? -2 : 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -968,3 +968,62 @@ def test_backward_matches_finite_differences(orc, resid, L, dk, dv):
         sm[ix] -= h
         fd = (_fd_loss(orc, inp, sp, d_o, dS, resid) - _fd_loss(orc, inp, sm, d_o, dS, resid)) / (2 * h)
         assert abs(fd - g["dS0"][ix]) <= 1e-6 * (1 + abs(fd)), ("S0", ix, fd, g["dS0"][ix])
+
+
+def _fd_loss_kalman(orc, inp, cov0, S0, d_o, dS, dcov, mode, qvar):
+    out = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"], cov0=cov0,
+                   q_noise_var=qvar, S0=S0, mode=mode, want_m=False)
+    return float(np.sum(d_o * out["o"]) + np.sum(dS * out["S"]) + np.sum(dcov * out["cov"]))
+
+
+@pytest.mark.parametrize("mode,L,dk,dv,qvar", [("diag", 9, 4, 3, 0.7), ("iso", 9, 4, 3, 0.7),
+                                               ("diag", 150, 4, 3, 1.0), ("iso", 150, 3, 5, 0.0),
+                                               ("diag", 9, 3, 5, 0.0)])
+def test_kalman_backward_matches_finite_differences(orc, mode, L, dk, dv, qvar):
+    """The gradients of the Kalman writes (Kalman Delta Networks, abstract: the
+    diagonal and isotropic covariance forms; the pages give no backward pass)
+    against central finite differences of the forward oracle, for q, k, v,
+    alpha, r, the prior covariance and the initial state, on a loss
+    sum(d_o * o) + sum(dS * S_L) + sum(dcov * cov_L), with and without process
+    noise. Keys of varying norm; L = 150 crosses the 64-token checkpoints
+    (sampled elements)."""
+    rng = _rng(70 + L + dk)
+    B, H = 1, 2
+    inp = workloads.scan_inputs(B, H, L, dk, dv, seed=71, dtype="f32", with_r=True)
+    inp["k"] = (inp["k"] * rng.uniform(0.5, 1.5, (B, H, L, 1))).astype(np.float32)
+    cshape = (B, H, dk) if mode == "diag" else (B, H)
+    cov0 = rng.uniform(0.5, 2.0, cshape)
+    S0 = rng.standard_normal((B, H, dk, dv)) * 0.5
+    d_o = rng.standard_normal((B, H, L, dv))
+    dS = rng.standard_normal((B, H, dk, dv))
+    dcov = rng.standard_normal(cshape)
+    g = orc.scan_bwd_kalman(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"],
+                            cov0=cov0, q_noise_var=qvar, S0=S0, d_o=d_o, dS=dS, dcov=dcov, mode=mode)
+    loss = lambda x, c0, s0: _fd_loss_kalman(orc, x, c0, s0, d_o, dS, dcov, mode, qvar)  # noqa: E731
+    h = 2.0 ** -12
+    names = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "r": "dr"}
+    for name, gname in names.items():
+        x = inp[name]
+        idx = list(np.ndindex(x.shape))
+        if L > 20:
+            idx = [idx[i] for i in rng.choice(len(idx), 25, replace=False)]
+        for ix in idx:
+            xp = {**inp, name: x.copy()}
+            xm = {**inp, name: x.copy()}
+            xp[name][ix] += np.float32(h)
+            xm[name][ix] -= np.float32(h)
+            fd = (loss(xp, cov0, S0) - loss(xm, cov0, S0)) / (2 * h)
+            assert abs(fd - g[gname][ix]) <= 1e-6 * (1 + abs(fd)), (name, ix, fd, g[gname][ix])
+    for ix in np.ndindex(cov0.shape):
+        cp, cm = cov0.copy(), cov0.copy()
+        cp[ix] += h
+        cm[ix] -= h
+        fd = (loss(inp, cp, S0) - loss(inp, cm, S0)) / (2 * h)
+        assert abs(fd - g["dcov0"][ix]) <= 1e-6 * (1 + abs(fd)), ("cov0", ix, fd, g["dcov0"][ix])
+    sidx = list(np.ndindex(S0.shape))
+    for ix in [sidx[i] for i in rng.choice(len(sidx), min(len(sidx), 12), replace=False)]:
+        sp, sm = S0.copy(), S0.copy()
+        sp[ix] += h
+        sm[ix] -= h
+        fd = (loss(inp, cov0, sp) - loss(inp, cov0, sm)) / (2 * h)
+        assert abs(fd - g["dS0"][ix]) <= 1e-6 * (1 + abs(fd)), ("S0", ix, fd, g["dS0"][ix])
