@@ -23,6 +23,7 @@ __all__ = [
     "kdn_scan_workspace_size", "kdn_status_string", "HolaCache", "LIB_PATH",
     "hola_prefill", "hola_prefill_workspace_size", "kdn_scan_bwd",
     "F32", "BF16", "MODES", "RESIDS", "PHASES", "kdn_scan_fwd_static", "STATIC_SCRATCH_BYTES",
+    "kdn_scan_bwd_ex",
 ]
 
 STATIC_SCRATCH_BYTES = 64 << 20  # KDN_STATIC_SCRATCH_BYTES in include/kdn.h
@@ -72,6 +73,10 @@ def _load():
     L.kdn_scan_bwd_workspace_size.restype = SZ
     L.kdn_scan_bwd.argtypes = [P] * 14 + [I] * 6 + [P, SZ, P]
     L.kdn_scan_bwd.restype = I
+    L.kdn_scan_bwd_ex_workspace_size.argtypes = [I, I, I, I, I, I, I]
+    L.kdn_scan_bwd_ex_workspace_size.restype = SZ
+    L.kdn_scan_bwd_ex.argtypes = [P, P, P, P, I, P, P, P, P, F] + [P] * 11 + [I] * 7 + [P, SZ, P]
+    L.kdn_scan_bwd_ex.restype = I
     L.hola_prefill_workspace_size.argtypes = [I, I, I, I, I, I, I]
     L.hola_prefill_workspace_size.restype = SZ
     L.hola_prefill.argtypes = [P, P, P, I, P, ctypes.c_int32, I, P, P, P, P, P, P, P, F,
@@ -379,4 +384,55 @@ def kdn_scan_bwd(q, k, v, alpha, beta, d_o, state_in=None, dstate_out=None, resi
                           _stream(stream))
     if st != 0:
         raise KdnError(st, "kdn_scan_bwd")
+    return out
+
+
+def kdn_scan_bwd_ex(q, k, v, d_o, alpha=None, beta=None, r=None, cov_in=None,
+                    q_noise_var: float = 0.0, state_in=None, dstate_out=None, dcov_out=None,
+                    mode: str = "delta", resid: str = "gated", workspace=None, stream=None,
+                    want_dstate: bool = True, want_dcov: bool = True) -> dict:
+    """Gradients of the scan for every write mode but the full covariance
+    (kdn_scan_bwd_ex): q, k, v, d_o float32 or bf16 (one dtype), the forward
+    call's alpha, beta (delta), r, cov_in (Kalman) and state_in, and the
+    gradients of the loss w.r.t. o (d_o), the final state and the final
+    covariance. Returns float32 dict(dq, dk, dv, dalpha, dbeta, dr, dcov_in,
+    dstate_in) (None where the mode has no such input)."""
+    torch = _torch()
+    f = torch.float32
+    _check(q, "q", (torch.bfloat16, f))
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    _check(k, "k", q.dtype, (B, H, L, dk), dev)
+    _check(v, "v", q.dtype, (B, H, L, dv), dev)
+    _check(d_o, "d_o", q.dtype, (B, H, L, dv), dev)
+    for name, t in (("alpha", alpha), ("beta", beta), ("r", r)):
+        _check(t, name, f, (B, H, L), dev)
+    kalman = mode in ("diag", "iso")
+    cshape = {"diag": (B, H, dk), "iso": (B, H)}.get(mode)
+    if kalman:
+        _check(cov_in, "cov_in", f, cshape, dev)
+        _check(dcov_out, "dcov_out", f, cshape, dev)
+    _check(state_in, "state_in", f, (B, H, dk, dv), dev)
+    _check(dstate_out, "dstate_out", f, (B, H, dk, dv), dev)
+    e = lambda shape: torch.empty(shape, dtype=f, device=dev)  # noqa: E731
+    out = dict(dq=e((B, H, L, dk)), dk=e((B, H, L, dk)), dv=e((B, H, L, dv)),
+               dalpha=e((B, H, L)) if alpha is not None else None,
+               dbeta=e((B, H, L)) if mode == "delta" else None,
+               dr=e((B, H, L)) if kalman and r is not None else None,
+               dcov_in=e(cshape) if kalman and want_dcov else None,
+               dstate_in=e((B, H, dk, dv)) if want_dstate else None)
+    code = _dtype_code(q.dtype)
+    need = int(lib.kdn_scan_bwd_ex_workspace_size(B, H, max(L, 1), dk, dv, MODES[mode], code))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.kdn_scan_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(d_o), code, _ptr(alpha), _ptr(beta),
+                             _ptr(r), _ptr(cov_in), float(q_noise_var), _ptr(state_in),
+                             _ptr(dstate_out), _ptr(dcov_out), _ptr(out["dq"]), _ptr(out["dk"]),
+                             _ptr(out["dv"]), _ptr(out["dalpha"]), _ptr(out["dbeta"]),
+                             _ptr(out["dr"]), _ptr(out["dcov_in"]), _ptr(out["dstate_in"]),
+                             B, H, L, dk, dv, MODES[mode], RESIDS[resid], _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != 0:
+        raise KdnError(st, "kdn_scan_bwd_ex")
     return out

@@ -132,7 +132,8 @@ __global__ __launch_bounds__(256) void diag_gains_kernel(const Tk* k, const floa
                                                          const float* r, float* cov_out,
                                                          float qvar, const float4* maps,
                                                          Tg* gains, int BH, int L, int dk,
-                                                         int C, int nchunks) {
+                                                         int C, int nchunks, float* pprev,
+                                                         float* sden) {
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wave >= BH * nchunks) return;
   const int bh = wave / nchunks, c = wave - bh * nchunks;
@@ -150,9 +151,15 @@ __global__ __launch_bounds__(256) void diag_gains_kernel(const Tk* k, const floa
     const float k1 = ok1 ? Elem<Tk>::load(k, g * dk + i1) : 0.f;
     const float pm0 = fmaf(a2, p0, Q), pm1 = fmaf(a2, p1, Q);
     const float pk0 = pm0 * k0, pk1 = pm1 * k1;
+    if (pprev) {  // for the backward: the variance before the token
+      if (ok0) pprev[g * dk + i0] = p0;
+      if (ok1) pprev[g * dk + i1] = p1;
+    }
     // reciprocals by v_rcp_f32 (1 ulp): the kernel is bound by its
     // instruction count, and exact divisions are ten instructions each
-    const float inv = __builtin_amdgcn_rcpf(rt + wave_sum64(fmaf(pk0, k0, pk1 * k1)));
+    const float sd = rt + wave_sum64(fmaf(pk0, k0, pk1 * k1));
+    if (sden && lane == 0) sden[g] = sd;
+    const float inv = __builtin_amdgcn_rcpf(sd);
     if (ok0) Elem<Tg>::store(gains, g * dk + i0, pk0 * inv);
     if (ok1) Elem<Tg>::store(gains, g * dk + i1, pk1 * inv);
     p0 = pm0 * rt * __builtin_amdgcn_rcpf(fmaf(pk0, k0, rt));
@@ -346,7 +353,8 @@ __global__ __launch_bounds__(64) void iso_prefix_kernel(const float* cov_in, flo
 __global__ __launch_bounds__(256) void iso_beta_kernel(const float* alpha, const float* r,
                                                        const float* kk, float* cov_out, float qvar,
                                                        const float4* maps, float* beta, int BH,
-                                                       int L, int dk, int C, int nchunks) {
+                                                       int L, int dk, int C, int nchunks,
+                                                       float* pprev) {
   const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wave >= BH * nchunks) return;
   const int bh = wave / nchunks, c = wave - bh * nchunks;
@@ -365,14 +373,222 @@ __global__ __launch_bounds__(256) void iso_beta_kernel(const float* alpha, const
   const float p = fmaf(e.a, p0, e.b) / fmaf(e.c, p0, e.d);   // variance after token t - 1
   const float pm = fmaf(al * al, p, (1.f - al) * (1.f + al) * qvar);
   if (lane < n) beta[g] = pm / fmaf(pm, kt, rt);
+  if (pprev && lane < n) pprev[g] = p;
   if (c == nchunks - 1 && cov_out && lane == n - 1)
     cov_out[bh] = pm * (dk * rt) / fmaf(pm, kt, dk * rt);
+}
+
+// ======================================================= covariance adjoints
+// Gradients through the Kalman gains and the covariance recursion (the
+// backward of the diagonal and isotropic writes). Given dL/db_t for the gain
+// rows (DIAG) or dL/dbeta_t (ISO) from the state backward, and dL/dp_L, the
+// reverse recursion over tokens carries dp = dL/dp_t per coordinate:
+//   DIAG: ds = -(db . b) / s,  dpm_i = db_i k_i / s + ds k_i^2 + dp_i r^2 / D_i^2,
+//         D_i = r + pm_i k_i^2,  dp_{t-1,i} = a^2 dpm_i,
+//         dk_i += db_i pm_i / s + 2 ds pm_i k_i - 2 dp_i pm_i^2 r k_i / D_i^2,
+//         dr = ds + sum_i dp_i pm_i^2 k_i^2 / D_i^2,  dalpha += 2 a sum_i dpm_i (p_i - sigma^2)
+//   ISO:  dpm = dbeta r / s^2 + dp (d r)^2 / D^2,  D = d r + pm kk,  dp_{t-1} = a^2 dpm,
+//         dkk = -dbeta pm^2 / s^2 - dp pm^2 d r / D^2 (dk += 2 dkk k),
+//         dr = -dbeta pm / s^2 + dp pm^2 d kk / D^2,  dalpha += 2 a dpm (p - sigma^2)
+// (pm = a^2 p + Q with p the variance before the token, s the gain's
+// denominator). dp_{t-1} is affine in dp_t with coefficients that do not
+// depend on dp, so, as in the forward, each chunk's tokens compose into one
+// affine map (in parallel), a short pass over chunks carries dp to every chunk
+// end, and a last pass runs each chunk's tokens in reverse from its carry.
+
+constexpr int kAdjC = 64;  // tokens per adjoint chunk
+
+// DIAG, one wavefront per (head, chunk), lane l: coordinates l and l + 64.
+// Per token: the affine map dp_t -> dp_{t-1}; per chunk their composition.
+__global__ __launch_bounds__(256) void diag_adj_maps_kernel(
+    const float* k, const float* alpha, const float* r, float qvar, const float* pprev,
+    const float* sden, const float* gains, const float* dgain, float2* amap, int BH, int L,
+    int dk, int nchunks) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave >= BH * nchunks) return;
+  const int bh = wave / nchunks, c = wave - bh * nchunks;
+  const int t0 = c * kAdjC, n = min(kAdjC, L - t0);
+  const int i0 = lane, i1 = lane + 64;
+  const bool ok0 = i0 < dk, ok1 = i1 < dk;
+  float A0 = 1.f, C0 = 0.f, A1 = 1.f, C1 = 0.f;  // composed map, dp at chunk end -> start
+  for (int t = 0; t < n; ++t) {
+    const size_t g = (size_t)bh * L + t0 + t;
+    const float a = alpha ? alpha[g] : 1.f, rt = r ? r[g] : 1.f, s = sden[g];
+    const float a2 = a * a, Q = (1.f - a) * (1.f + a) * qvar;
+    const float k0 = ok0 ? k[g * dk + i0] : 0.f, k1 = ok1 ? k[g * dk + i1] : 0.f;
+    const float b0 = ok0 ? gains[g * dk + i0] : 0.f, b1 = ok1 ? gains[g * dk + i1] : 0.f;
+    const float d0 = ok0 ? dgain[g * dk + i0] : 0.f, d1 = ok1 ? dgain[g * dk + i1] : 0.f;
+    const float pm0 = fmaf(a2, ok0 ? pprev[g * dk + i0] : 0.f, Q);
+    const float pm1 = fmaf(a2, ok1 ? pprev[g * dk + i1] : 0.f, Q);
+    const float ds = -wave_sum64(fmaf(d0, b0, d1 * b1)) / s;
+    const float D0 = fmaf(pm0 * k0, k0, rt), D1 = fmaf(pm1 * k1, k1, rt);
+    const float c0 = a2 * fmaf(ds * k0, k0, d0 * k0 / s), c1 = a2 * fmaf(ds * k1, k1, d1 * k1 / s);
+    const float e0 = a2 * (rt / D0) * (rt / D0), e1 = a2 * (rt / D1) * (rt / D1);
+    // F <- F o f: x -> A (e x + c) + C
+    C0 = fmaf(A0, c0, C0);
+    A0 *= e0;
+    C1 = fmaf(A1, c1, C1);
+    A1 *= e1;
+  }
+  float2* m = amap + ((size_t)bh * nchunks + c) * dk;
+  if (ok0) m[i0] = make_float2(A0, C0);
+  if (ok1) m[i1] = make_float2(A1, C1);
+}
+
+// One thread per (head, coordinate) (np coordinates per head): dp at every
+// chunk end, from the last chunk back; dp at the start is dL/dp_0.
+__global__ __launch_bounds__(128) void adj_carry_kernel(const float* dcov_out, const float2* amap,
+                                                        float* carry, float* dcov_in, int BH,
+                                                        int np, int nchunks) {
+  const int idx = blockIdx.x * 128 + threadIdx.x;
+  if (idx >= BH * np) return;
+  const int bh = idx / np, i = idx - bh * np;
+  float dp = dcov_out ? dcov_out[idx] : 0.f;
+  for (int c = nchunks - 1; c >= 0; --c) {
+    const size_t o = ((size_t)bh * nchunks + c) * np + i;
+    carry[o] = dp;
+    const float2 m = amap[o];
+    dp = fmaf(m.x, dp, m.y);
+  }
+  if (dcov_in) dcov_in[idx] = dp;
+}
+
+// DIAG, one wavefront per (head, chunk): the chunk's tokens in reverse from the
+// carried dp; adds the gain and covariance terms to dk and dalpha, writes dr.
+__global__ __launch_bounds__(256) void diag_adj_out_kernel(
+    const float* k, const float* alpha, const float* r, float qvar, const float* pprev,
+    const float* sden, const float* gains, const float* dgain, const float* carry, float* dk_out,
+    float* dalpha, float* dr, int BH, int L, int dk, int nchunks) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave >= BH * nchunks) return;
+  const int bh = wave / nchunks, c = wave - bh * nchunks;
+  const int t0 = c * kAdjC, n = min(kAdjC, L - t0);
+  const int i0 = lane, i1 = lane + 64;
+  const bool ok0 = i0 < dk, ok1 = i1 < dk;
+  const float* cr = carry + ((size_t)bh * nchunks + c) * dk;
+  float dp0 = ok0 ? cr[i0] : 0.f, dp1 = ok1 ? cr[i1] : 0.f;
+  for (int t = n - 1; t >= 0; --t) {
+    const size_t g = (size_t)bh * L + t0 + t;
+    const float a = alpha ? alpha[g] : 1.f, rt = r ? r[g] : 1.f, s = sden[g];
+    const float a2 = a * a, Q = (1.f - a) * (1.f + a) * qvar;
+    const float k0 = ok0 ? k[g * dk + i0] : 0.f, k1 = ok1 ? k[g * dk + i1] : 0.f;
+    const float b0 = ok0 ? gains[g * dk + i0] : 0.f, b1 = ok1 ? gains[g * dk + i1] : 0.f;
+    const float d0 = ok0 ? dgain[g * dk + i0] : 0.f, d1 = ok1 ? dgain[g * dk + i1] : 0.f;
+    const float p0 = ok0 ? pprev[g * dk + i0] : 0.f, p1 = ok1 ? pprev[g * dk + i1] : 0.f;
+    const float pm0 = fmaf(a2, p0, Q), pm1 = fmaf(a2, p1, Q);
+    const float ds = -wave_sum64(fmaf(d0, b0, d1 * b1)) / s;
+    const float D0 = fmaf(pm0 * k0, k0, rt), D1 = fmaf(pm1 * k1, k1, rt);
+    const float q0 = pm0 / D0, q1 = pm1 / D1;   // pm / D
+    const float dpm0 = d0 * k0 / s + ds * k0 * k0 + dp0 * (rt / D0) * (rt / D0);
+    const float dpm1 = d1 * k1 / s + ds * k1 * k1 + dp1 * (rt / D1) * (rt / D1);
+    if (ok0) dk_out[g * dk + i0] += d0 * pm0 / s + 2.f * ds * pm0 * k0 - 2.f * dp0 * q0 * q0 * rt * k0;
+    if (ok1) dk_out[g * dk + i1] += d1 * pm1 / s + 2.f * ds * pm1 * k1 - 2.f * dp1 * q1 * q1 * rt * k1;
+    const float drs = wave_sum64(fmaf(dp0 * q0 * q0 * k0, k0, dp1 * q1 * q1 * k1 * k1));
+    const float das = wave_sum64(fmaf(dpm0, p0 - qvar, ok1 ? dpm1 * (p1 - qvar) : 0.f));
+    if (lane == 0) {
+      if (dr) dr[g] = ds + drs;
+      if (dalpha) dalpha[g] += 2.f * a * (ok0 ? das : 0.f);
+    }
+    dp0 = a2 * dpm0;
+    dp1 = a2 * dpm1;
+  }
+}
+
+// ISO: one wavefront per (head, chunk), lane t = token t. Per token the affine
+// map (e, c): dp_t -> dp_{t-1} = e dp_t + c, and the suffix compositions
+// R_t = f_t o f_{t+1} o ... by a wavefront scan toward lane 0.
+struct Aff {
+  float e, c;
+};
+__device__ __forceinline__ Aff aff_after(Aff f, Aff g) {  // f o g
+  return Aff{f.e * g.e, fmaf(f.e, g.c, f.c)};
+}
+__device__ __forceinline__ Aff aff_suffix(Aff m, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    Aff y{__shfl_down(m.e, off, 64), __shfl_down(m.c, off, 64)};
+    if (lane + off >= 64) y = Aff{1.f, 0.f};
+    m = aff_after(m, y);
+  }
+  return m;
+}
+struct IsoTok {
+  float a, rt, p, pm, s, D, kk, db;
+};
+__device__ __forceinline__ IsoTok iso_tok(const float* alpha, const float* r, const float* kk,
+                                          const float* pprev, const float* dbeta, float qvar,
+                                          int dk, size_t g, bool in) {
+  IsoTok x{1.f, 1.f, 0.f, 0.f, 1.f, 1.f, 0.f, 0.f};
+  if (in) {
+    x.a = alpha ? alpha[g] : 1.f;
+    x.rt = r ? r[g] : 1.f;
+    x.p = pprev[g];
+    x.kk = kk[g];
+    x.db = dbeta[g];
+    x.pm = fmaf(x.a * x.a, x.p, (1.f - x.a) * (1.f + x.a) * qvar);
+    x.s = fmaf(x.pm, x.kk, x.rt);
+    x.D = fmaf(x.pm, x.kk, dk * x.rt);
+  }
+  return x;
+}
+__device__ __forceinline__ Aff iso_aff(const IsoTok& x, int dk, bool in) {
+  if (!in) return Aff{1.f, 0.f};
+  const float a2 = x.a * x.a, u = dk * x.rt / x.D;
+  return Aff{a2 * u * u, a2 * x.db * x.rt / (x.s * x.s)};
+}
+
+__global__ __launch_bounds__(256) void iso_adj_maps_kernel(const float* alpha, const float* r,
+                                                           float qvar, const float* kk,
+                                                           const float* pprev, const float* dbeta,
+                                                           float2* amap, int BH, int L, int dk,
+                                                           int nchunks) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave >= BH * nchunks) return;
+  const int bh = wave / nchunks, c = wave - bh * nchunks;
+  const int t0 = c * kAdjC, n = min(kAdjC, L - t0);
+  const bool in = lane < n;
+  const IsoTok x = iso_tok(alpha, r, kk, pprev, dbeta, qvar, dk, (size_t)bh * L + t0 + lane, in);
+  const Aff m = aff_suffix(iso_aff(x, dk, in), lane);
+  if (lane == 0) amap[(size_t)bh * nchunks + c] = make_float2(m.e, m.c);
+}
+
+__global__ __launch_bounds__(256) void iso_adj_out_kernel(const float* k, const float* alpha,
+                                                          const float* r, float qvar,
+                                                          const float* kk, const float* pprev,
+                                                          const float* dbeta, const float* carry,
+                                                          float* dk_out, float* dalpha, float* dr,
+                                                          int BH, int L, int dk, int nchunks) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave >= BH * nchunks) return;
+  const int bh = wave / nchunks, c = wave - bh * nchunks;
+  const int t0 = c * kAdjC, n = min(kAdjC, L - t0);
+  const bool in = lane < n;
+  const size_t g = (size_t)bh * L + t0 + lane;
+  const IsoTok x = iso_tok(alpha, r, kk, pprev, dbeta, qvar, dk, g, in);
+  const Aff incl = aff_suffix(iso_aff(x, dk, in), lane);       // f_t o ... o f_last
+  Aff after{__shfl_down(incl.e, 1, 64), __shfl_down(incl.c, 1, 64)};  // f_{t+1} o ...
+  if (lane == 63) after = Aff{1.f, 0.f};
+  const float dpe = carry[(size_t)bh * nchunks + c];           // dp at the chunk end
+  const float dp = fmaf(after.e, dpe, after.c);                 // dL/dp_t
+  const float s2 = x.s * x.s, D2 = x.D * x.D, pm2 = x.pm * x.pm;
+  const float dpm = x.db * x.rt / s2 + dp * (dk * x.rt) * (dk * x.rt) / D2;
+  const float dkk = -x.db * pm2 / s2 - dp * pm2 * dk * x.rt / D2;
+  if (in) {
+    if (dr) dr[g] = -x.db * x.pm / s2 + dp * pm2 * dk * x.kk / D2;
+    if (dalpha) dalpha[g] += 2.f * x.a * dpm * (x.p - qvar);
+  }
+  // dk += 2 dkk k, token by token, the wavefront over its coordinates
+  const size_t row0 = (size_t)bh * L + t0;
+  for (int t = 0; t < n; ++t) {
+    const float f = 2.f * __shfl(dkk, t, 64);
+    for (int i = lane; i < dk; i += 64) dk_out[(row0 + t) * dk + i] += f * k[(row0 + t) * dk + i];
+  }
 }
 
 template <typename Tk, typename Tg>
 hipError_t diag_typed(const void* k, const float* alpha, const float* r, const float* cov_in,
                       float* cov_out, float qvar, void* gains, float* maps, int BH, int L, int dk,
-                      int C, hipStream_t s) {
+                      int C, hipStream_t s, float* pprev, float* sden) {
   const int nchunks = (L + C - 1) / C;
   hipLaunchKernelGGL(diag_maps_kernel<Tk>, dim3(BH, nchunks), dim3(128), 0, s,
                      static_cast<const Tk*>(k), alpha, r, qvar, reinterpret_cast<float4*>(maps), L,
@@ -387,7 +603,7 @@ hipError_t diag_typed(const void* k, const float* alpha, const float* r, const f
   hipLaunchKernelGGL((diag_gains_kernel<Tk, Tg>), dim3((waves + 3) / 4), dim3(256), 0, s,
                      static_cast<const Tk*>(k), alpha, r, cov_out, qvar,
                      reinterpret_cast<const float4*>(maps), static_cast<Tg*>(gains), BH, L, dk, C,
-                     nchunks);
+                     nchunks, pprev, sden);
   return hipGetLastError();
 }
 
@@ -406,22 +622,22 @@ hipError_t full_typed(const void* k, const float* alpha, const float* r, const f
 hipError_t launch_diag_gains(const void* k, bool k_bf16, const float* alpha, const float* r,
                              const float* cov_in, float* cov_out, float q_noise_var, void* gains,
                              bool gains_f16, float* maps, int BH, int L, int dk, int chunk,
-                             hipStream_t s) {
+                             hipStream_t s, float* pprev, float* sden) {
   if (k_bf16)
     return gains_f16 ? diag_typed<uint16_t, _Float16>(k, alpha, r, cov_in, cov_out, q_noise_var,
-                                                       gains, maps, BH, L, dk, chunk, s)
+                                                       gains, maps, BH, L, dk, chunk, s, pprev, sden)
                       : diag_typed<uint16_t, float>(k, alpha, r, cov_in, cov_out, q_noise_var,
-                                                    gains, maps, BH, L, dk, chunk, s);
+                                                    gains, maps, BH, L, dk, chunk, s, pprev, sden);
   return gains_f16 ? diag_typed<float, _Float16>(k, alpha, r, cov_in, cov_out, q_noise_var, gains,
-                                                  maps, BH, L, dk, chunk, s)
+                                                  maps, BH, L, dk, chunk, s, pprev, sden)
                     : diag_typed<float, float>(k, alpha, r, cov_in, cov_out, q_noise_var, gains,
-                                               maps, BH, L, dk, chunk, s);
+                                               maps, BH, L, dk, chunk, s, pprev, sden);
 }
 
 hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const float* r,
                           const float* cov_in, float* cov_out, float q_noise_var, float* beta,
                           float* kk, float* maps, int BH, int L, int dk, int chunk,
-                          hipStream_t s) {
+                          hipStream_t s, float* pprev) {
   const int nchunks = (L + chunk - 1) / chunk;
   const int blocks = (BH * nchunks + 3) / 4;  // four wavefronts per workgroup
   if (k_bf16)
@@ -440,7 +656,40 @@ hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(iso_beta_kernel, dim3(blocks), dim3(256), 0, s, alpha, r, kk, cov_out,
                      q_noise_var, reinterpret_cast<const float4*>(maps), beta, BH, L, dk, chunk,
-                     nchunks);
+                     nchunks, pprev);
+  return hipGetLastError();
+}
+
+size_t cov_adj_scratch_floats(int BH, int L, int dk, bool diag) {
+  const size_t nch = ((size_t)L + kAdjC - 1) / kAdjC, np = diag ? (size_t)dk : 1;
+  return (size_t)BH * nch * np * 3;  // affine maps (2) and carries (1)
+}
+
+hipError_t launch_cov_adjoint(const CovAdjArgs& a, float* scratch, hipStream_t s) {
+  const int nch = (a.L + kAdjC - 1) / kAdjC, np = a.diag ? a.dk : 1;
+  float2* amap = reinterpret_cast<float2*>(scratch);
+  float* carry = scratch + (size_t)a.BH * nch * np * 2;
+  const int blocks = (a.BH * nch + 3) / 4;
+  if (a.diag)
+    hipLaunchKernelGGL(diag_adj_maps_kernel, dim3(blocks), dim3(256), 0, s, a.k, a.alpha, a.r,
+                       a.qvar, a.pprev, a.sden, a.gains, a.dgain, amap, a.BH, a.L, a.dk, nch);
+  else
+    hipLaunchKernelGGL(iso_adj_maps_kernel, dim3(blocks), dim3(256), 0, s, a.alpha, a.r, a.qvar,
+                       a.kk, a.pprev, a.dbeta, amap, a.BH, a.L, a.dk, nch);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(adj_carry_kernel, dim3((a.BH * np + 127) / 128), dim3(128), 0, s, a.dcov_out,
+                     amap, carry, a.dcov_in, a.BH, np, nch);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.diag)
+    hipLaunchKernelGGL(diag_adj_out_kernel, dim3(blocks), dim3(256), 0, s, a.k, a.alpha, a.r,
+                       a.qvar, a.pprev, a.sden, a.gains, a.dgain, carry, a.dk_out, a.dalpha, a.dr,
+                       a.BH, a.L, a.dk, nch);
+  else
+    hipLaunchKernelGGL(iso_adj_out_kernel, dim3(blocks), dim3(256), 0, s, a.k, a.alpha, a.r,
+                       a.qvar, a.kk, a.pprev, a.dbeta, carry, a.dk_out, a.dalpha, a.dr, a.BH, a.L,
+                       a.dk, nch);
   return hipGetLastError();
 }
 

@@ -434,3 +434,178 @@ KDN_EXPORT int kdn_scan_bwd(const float* q, const float* k, const float* v, cons
   a.resid = resid;
   return map_hip(kdn::launch_scan_bwd(a, workspace, static_cast<hipStream_t>(stream)));
 }
+
+
+// ------------------------------------------------------------ kdn_scan_bwd_ex
+namespace {
+
+// Workspace of kdn_scan_bwd_ex, 256-byte aligned parts:
+//   [float32 copies of bf16 q, k, v, d_o | Kalman forward recompute: gains or
+//    write strengths, variance before each token, s_t or ||k||^2, chunk maps |
+//    dL/d(gain rows) or dL/dbeta | covariance-adjoint scratch | the state
+//    backward's workspace]
+struct BwdExLayout {
+  size_t cvt_q, cvt_k, cvt_v, cvt_o, gain, pprev, sden, maps, dgain, adj, bwd, total;
+};
+
+BwdExLayout bwd_ex_layout(int B, int H, int L, int dk, int dv, int mode, int in_dtype) {
+  BwdExLayout w{};
+  const size_t BH = (size_t)B * H, T = BH * (size_t)L, nch = ((size_t)L + 63) / 64;
+  const bool bf = in_dtype == KDN_BF16, diag = mode == KDN_GAIN_DIAG, iso = mode == KDN_GAIN_ISO;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes, 256);
+    return at;
+  };
+  w.cvt_q = take(bf ? T * dk * 4 : 0);
+  w.cvt_k = take(bf ? T * dk * 4 : 0);
+  w.cvt_v = take(bf ? T * dv * 4 : 0);
+  w.cvt_o = take(bf ? T * dv * 4 : 0);
+  w.gain = take(diag ? T * dk * 4 : iso ? 2 * T * 4 : 0);        // gains / (beta, ||k||^2)
+  w.pprev = take(diag ? T * dk * 4 : iso ? T * 4 : 0);
+  w.sden = take(diag ? T * 4 : 0);
+  w.maps = take(diag ? BH * nch * dk * 16 : iso ? BH * nch * 16 : 0);
+  w.dgain = take(diag ? T * dk * 4 : iso ? T * 4 : 0);           // dL/dgain / dL/dbeta
+  w.adj = take((diag || iso) ? kdn::cov_adj_scratch_floats((int)BH, L, dk, diag) * 4 : 0);
+  w.bwd = take(kdn::scan_bwd_workspace_bytes((int)BH, L, dk, dv));
+  w.total = o;
+  return w;
+}
+
+}  // namespace
+
+KDN_EXPORT size_t kdn_scan_bwd_ex_workspace_size(int B, int H, int L, int d_k, int d_v, int mode,
+                                                 int in_dtype) {
+  if (B < 1 || H < 1 || L < 1 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim) return 0;
+  if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_ISO) return 0;
+  if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return 0;
+  return bwd_ex_layout(B, H, L, d_k, d_v, mode, in_dtype).total;
+}
+
+KDN_EXPORT int kdn_scan_bwd_ex(const void* q, const void* k, const void* v, const void* d_o,
+                               int in_dtype, const float* alpha, const float* beta, const float* r,
+                               const float* cov_in, float q_noise_var, const float* state_in,
+                               const float* dstate_out, const float* dcov_out, float* dq, float* dk,
+                               float* dv, float* dalpha, float* dbeta, float* dr, float* dcov_in,
+                               float* dstate_in, int B, int H, int L, int d_k, int d_v, int mode,
+                               int resid, void* workspace, size_t workspace_bytes, void* stream) {
+  if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_ERR_BAD_DTYPE;
+  if (mode == KDN_GAIN_FULL) return KDN_ERR_UNSUPPORTED;
+  if (mode != KDN_GAIN_DELTA && mode != KDN_GAIN_DIAG && mode != KDN_GAIN_ISO)
+    return KDN_ERR_BAD_MODE;
+  if (resid != KDN_RESID_GATED && resid != KDN_RESID_PLAIN && resid != KDN_RESID_NOERASE)
+    return KDN_ERR_BAD_MODE;
+  if (resid != KDN_RESID_GATED && mode != KDN_GAIN_DELTA) return KDN_ERR_BAD_MODE;
+  if (B < 1 || H < 1 || L < 0 || d_k < 1 || d_v < 1 || d_k > kMaxDim || d_v > kMaxDim)
+    return KDN_ERR_BAD_SHAPE;
+  if ((long long)B * H > (1LL << 24) || (long long)(d_v + 31) / 32 > kMaxGridYZ ||
+      ((long long)L + 63) / 64 > kMaxGridYZ)
+    return KDN_ERR_BAD_SHAPE;
+  if (!std::isfinite(q_noise_var) || q_noise_var < 0.f) return KDN_ERR_BAD_SHAPE;
+  const bool kalman = mode != KDN_GAIN_DELTA;
+  if (kalman && cov_in == nullptr) return KDN_ERR_NULL_POINTER;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int BH = B * H;
+  const size_t np = mode == KDN_GAIN_DIAG ? (size_t)d_k : 1;
+  if (L == 0) {
+    // no tokens: the initial state's and covariance's gradients are the final ones'
+    hipError_t e = hipSuccess;
+    if (dstate_in) e = kdn::launch_copy_f32(dstate_out, dstate_in, (size_t)BH * d_k * d_v, s);
+    if (e == hipSuccess && kalman && dcov_in) e = kdn::launch_copy_f32(dcov_out, dcov_in, BH * np, s);
+    return map_hip(e);
+  }
+  if (!q || !k || !v || !d_o || !dq || !dk || !dv) return KDN_ERR_NULL_POINTER;
+  if (!kalman && (!beta || !dbeta)) return KDN_ERR_NULL_POINTER;
+  if (alpha && !dalpha) return KDN_ERR_NULL_POINTER;
+  if (kalman && r && !dr) return KDN_ERR_NULL_POINTER;
+  const BwdExLayout w = bwd_ex_layout(B, H, L, d_k, d_v, mode, in_dtype);
+  if (workspace == nullptr || workspace_bytes < w.total || !aligned16(workspace))
+    return KDN_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  const size_t T = (size_t)BH * L;
+  hipError_t e = hipSuccess;
+  const float *qf = static_cast<const float*>(q), *kf = static_cast<const float*>(k);
+  const float *vf = static_cast<const float*>(v), *of = static_cast<const float*>(d_o);
+  if (in_dtype == KDN_BF16) {
+    float* cq = reinterpret_cast<float*>(ws + w.cvt_q);
+    float* ck = reinterpret_cast<float*>(ws + w.cvt_k);
+    float* cv = reinterpret_cast<float*>(ws + w.cvt_v);
+    float* co = reinterpret_cast<float*>(ws + w.cvt_o);
+    e = kdn::launch_bf16_to_f32(static_cast<const uint16_t*>(q), cq, T * d_k, s);
+    if (e == hipSuccess) e = kdn::launch_bf16_to_f32(static_cast<const uint16_t*>(k), ck, T * d_k, s);
+    if (e == hipSuccess) e = kdn::launch_bf16_to_f32(static_cast<const uint16_t*>(v), cv, T * d_v, s);
+    if (e == hipSuccess) e = kdn::launch_bf16_to_f32(static_cast<const uint16_t*>(d_o), co, T * d_v, s);
+    if (e != hipSuccess) return map_hip(e);
+    qf = cq;
+    kf = ck;
+    vf = cv;
+    of = co;
+  }
+  kdn::BwdArgs a{};
+  a.q = qf;
+  a.k = kf;
+  a.v = vf;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.state_in = state_in;
+  a.d_o = of;
+  a.dstate_out = dstate_out;
+  a.dq = dq;
+  a.dk_out = dk;
+  a.dv_out = dv;
+  a.dalpha = alpha ? dalpha : nullptr;
+  a.dbeta = dbeta;
+  a.dstate_in = dstate_in;
+  a.BH = BH;
+  a.L = L;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.resid = resid;
+  kdn::CovAdjArgs c{};
+  float* gain = reinterpret_cast<float*>(ws + w.gain);
+  float* pprev = reinterpret_cast<float*>(ws + w.pprev);
+  float* dgain = reinterpret_cast<float*>(ws + w.dgain);
+  if (mode == KDN_GAIN_DIAG) {
+    // forward: the gains, the variance before each token and s_t
+    float* sden = reinterpret_cast<float*>(ws + w.sden);
+    e = kdn::launch_diag_gains(kf, false, alpha, r, cov_in, nullptr, q_noise_var, gain, false,
+                               reinterpret_cast<float*>(ws + w.maps), BH, L, d_k, 64, s, pprev,
+                               sden);
+    if (e != hipSuccess) return map_hip(e);
+    a.beta = nullptr;
+    a.dbeta = nullptr;
+    a.gain = gain;
+    a.dgain = dgain;
+    c.sden = sden;
+    c.gains = gain;
+    c.dgain = dgain;
+  } else if (mode == KDN_GAIN_ISO) {
+    // forward: the write strengths beta_t (the delta write), ||k||^2, variances
+    float* kk = gain + T;
+    e = kdn::launch_iso_beta(kf, false, alpha, r, cov_in, nullptr, q_noise_var, gain, kk,
+                             reinterpret_cast<float*>(ws + w.maps), BH, L, d_k, 64, s, pprev);
+    if (e != hipSuccess) return map_hip(e);
+    a.beta = gain;
+    a.dbeta = dgain;
+    c.kk = kk;
+    c.dbeta = dgain;
+  }
+  e = kdn::launch_scan_bwd(a, ws + w.bwd, s);
+  if (e != hipSuccess || !kalman) return map_hip(e);
+  c.diag = mode == KDN_GAIN_DIAG;
+  c.k = kf;
+  c.alpha = alpha;
+  c.r = r;
+  c.qvar = q_noise_var;
+  c.pprev = pprev;
+  c.dcov_out = dcov_out;
+  c.dk_out = dk;
+  c.dalpha = alpha ? dalpha : nullptr;
+  c.dr = r ? dr : nullptr;
+  c.dcov_in = dcov_in;
+  c.BH = BH;
+  c.L = L;
+  c.dk = d_k;
+  return map_hip(kdn::launch_cov_adjoint(c, reinterpret_cast<float*>(ws + w.adj), s));
+}

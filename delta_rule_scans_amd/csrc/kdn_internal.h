@@ -150,18 +150,51 @@ hipError_t launch_scores(const ScoreArgs& a, hipStream_t s);
 
 // Diagonal-covariance Kalman gains: writes gains [BH, L, dk] (fp16 or f32) and
 // the final covariance. `maps` is scratch of BH * nchunks * dk * 4 floats.
+// pprev (optional, [BH, L, dk] float32): the variance before every token; sden
+// (optional, [BH, L]): s_t = r_t + sum_i p-_i k_i^2 (the backward reads both).
 hipError_t launch_diag_gains(const void* k, bool k_bf16, const float* alpha, const float* r,
                              const float* cov_in, float* cov_out, float q_noise_var,
                              void* gains, bool gains_f16, float* maps, int BH, int L, int dk,
-                             int chunk, hipStream_t s);
+                             int chunk, hipStream_t s, float* pprev = nullptr,
+                             float* sden = nullptr);
 
 // Isotropic Kalman write: the per-token write strengths beta [BH, L] (the gain
 // is beta_t k_t) and the final variance [BH]. `kk` is scratch of BH * L floats,
 // `maps` of BH * nchunks * 4 floats (16-byte aligned). chunk <= 64.
+// pprev (optional, [BH, L]): the variance before every token.
 hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const float* r,
                           const float* cov_in, float* cov_out, float q_noise_var, float* beta,
                           float* kk, float* maps, int BH, int L, int dk, int chunk,
-                          hipStream_t s);
+                          hipStream_t s, float* pprev = nullptr);
+
+// Backward through the Kalman gains and the covariance recursion (see cov.hip):
+// adds the gain and covariance terms to dk_out and dalpha, writes dr and
+// dcov_in. DIAG reads the gains and dL/d(gain rows), ISO reads ||k||^2 and
+// dL/dbeta. All arrays float32; k [BH, L, dk].
+struct CovAdjArgs {
+  bool diag;
+  const float* k;
+  const float* alpha;    // [BH, L] or null
+  const float* r;        // [BH, L] or null
+  float qvar;
+  const float* pprev;    // [BH, L, dk] (DIAG) / [BH, L] (ISO): variance before each token
+  const float* sden;     // [BH, L] (DIAG): the gain's denominator s_t
+  const float* gains;    // [BH, L, dk] (DIAG)
+  const float* dgain;    // [BH, L, dk] (DIAG)
+  const float* kk;       // [BH, L] (ISO): ||k_t||^2
+  const float* dbeta;    // [BH, L] (ISO): dL/dbeta_t of the equivalent delta write
+  const float* dcov_out; // [BH, dk] / [BH] or null
+  float* dk_out;         // [BH, L, dk], added to
+  float* dalpha;         // [BH, L] or null, added to
+  float* dr;             // [BH, L] or null
+  float* dcov_in;        // [BH, dk] / [BH] or null
+  int BH, L, dk;
+};
+size_t cov_adj_scratch_floats(int BH, int L, int dk, bool diag);
+hipError_t launch_cov_adjoint(const CovAdjArgs& a, float* scratch, hipStream_t s);
+
+// bf16 -> float32, n elements (the backward takes float32 operands).
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, size_t n, hipStream_t s);
 
 // Full-covariance Kalman gains (dk <= 64): gains [BH, L, dk] and the final covariance.
 hipError_t launch_full_gains(const void* k, bool k_bf16, const float* alpha, const float* r,
@@ -203,6 +236,9 @@ struct BwdArgs {
   float* dstate_in;         // [BH, dk, dv] or null
   int BH, L, dk, dv;
   int resid;                // 0 gated, 1 plain, 2 no erase
+  // gain mode (Kalman writes): write vectors given as rows, beta unused
+  const float* gain = nullptr;  // [BH, L, dk] or null (delta write)
+  float* dgain = nullptr;       // [BH, L, dk] out: dL/d(gain rows) (gain mode)
   // workspace parts (set by launch_scan_bwd)
   float* S0s = nullptr;  // [BH, chunks, dk, dv] state at each chunk start
   float* Gs = nullptr;   // [BH, chunks, dk, dv] state gradient at each chunk end

@@ -33,6 +33,14 @@
 //    dR E^T; E G^T and <G, S0>.
 //  * gradients (head, chunk): dQ, dK, dbeta, dalpha.
 // Products run on the fp32 matrix cores (v_mfma_f32_16x16x4f32) with operands read from LDS.
+//
+// Gain mode (a.gain set: the Kalman writes, "Kalman Delta Networks", abstract):
+// the write vectors B are given rows g_t (the gains) instead of beta_t k_t, the
+// residual is gated (c_t = alpha_t). The same formulas hold with diag(b) K
+// replaced by the gain rows; dB is written out (a.dgain) for the covariance
+// adjoint, dK keeps only the terms through the prediction K S0 and the Gram
+// K B^T (Xa B - diag(g) dR S0^T), and the state terms of the decay use
+// Lambda_t g_t . (G e_t). There is no dbeta.
 #include "kdn_internal.h"
 
 namespace kdn {
@@ -114,7 +122,7 @@ __device__ __forceinline__ Scal fetch_scalars(const BwdArgs& a, size_t tok, int 
   Scal r{1.f, 0.f};
   if (t < n && t < C) {
     r.al = a.alpha ? a.alpha[tok + t] : 1.f;
-    r.be = a.beta[tok + t];
+    r.be = a.beta ? a.beta[tok + t] : 1.f;  // no beta in gain mode: the gain rows are B
   }
   return r;
 }
@@ -213,24 +221,28 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   float* sLg = lds + 2 * C * LP;
   float* sB = sLg + C;
   float* sAl = sB + C;
+  float* sGn = sAl + C;           // [C][LP] gain rows (gain mode)
   const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, nch = gridDim.y;
   const int n = min(C, a.L - c * C), dk = a.dk, dk64 = dk <= 64 ? 64 : DP;
   const size_t tok = (size_t)bh * a.L + (size_t)c * C;
-  const bool erase = a.resid != 2;
+  const bool erase = a.resid != 2, gain = a.gain != nullptr;
   {
-    Frag<C * DP / NT> fk, fq;
+    Frag<C * DP / NT> fk, fq, fg;
     fetch_rows<NT>(fk, a.k + tok * dk, n, dk);
     fetch_rows<NT>(fq, a.q + tok * dk, n, dk);
+    if (gain) fetch_rows<NT>(fg, a.gain + tok * dk, n, dk);
     const Scal sc = fetch_scalars(a, tok, n);
     put_rows<NT, LP>(fk, sK);
     put_rows<NT, LP>(fq, sQ);
+    if (gain) put_rows<NT, LP>(fg, sGn);
     put_scalars(a, sc, sLg, sB, sAl);
   }
   __syncthreads();
   const int w = tid >> 6, r = tid & 15, q = (tid & 63) >> 4;
   floatx4 kk[4] = {}, qk[4] = {};
-  mfma_row<4>(kk, sK, LP, 1, nullptr, sK, 1, LP, 16 * w, dk64);
-  mfma_row<4>(qk, sQ, LP, 1, nullptr, sK, 1, LP, 16 * w, dk64);
+  const float* sW = gain ? sGn : sK;  // the write vectors' direction: K B^T, Q B^T
+  mfma_row<4>(kk, sK, LP, 1, nullptr, sW, 1, LP, 16 * w, dk64);
+  mfma_row<4>(qk, sQ, LP, 1, nullptr, sW, 1, LP, 16 * w, dk64);
   __syncthreads();  // every wavefront is done with K and Q
   for (int idx = tid; idx < C * LC; idx += NT) sT[idx] = 0.f;
   float* Ag = a.Am + cc_off(bh, nch, c);
@@ -320,9 +332,10 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
   float* sLg = sE + C * LOC;
   float* sB = sLg + C;
   float* sAl = sB + C;
+  float* sGn = sAl + C;         // [C][LKC] gain rows (gain mode)
   const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
   const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C, dk64 = dk <= 64 ? 64 : DP;
-  const bool erase = a.resid != 2;
+  const bool erase = a.resid != 2, gain = a.gain != nullptr;
   const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
   const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);  // this wavefront's [C][TW] block
   // state rows 16 w + 4 q + i, columns 16 h + r (h = 0, 1)
@@ -337,7 +350,7 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
                     : 0.f;
       sS[d * LOC + j] = S[h][i];
     }
-  Frag<C * DP / NTC> fk;
+  Frag<C * DP / NTC> fk, fg;
   Frag<C * C / NTC> ft;
   Frag<C * TW / NTC> fv;
   Scal fs;
@@ -345,6 +358,7 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
     const int n = min(C, L - c * C);
     const size_t tok = (size_t)bh * L + (size_t)c * C;
     fetch_rows<NTC>(fk, a.k + tok * dk, n, dk);
+    if (gain) fetch_rows<NTC>(fg, a.gain + tok * dk, n, dk);
     if (erase) fetch_cc<NTC>(ft, a.Tm + cc_off(bh, nch, c));
     fetch_tile<NTC>(fv, a.v + tok * dv, n, dv, j0);
     fs = fetch_scalars(a, tok, n);
@@ -354,6 +368,7 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
     const int n = min(C, L - c * C);
     __syncthreads();
     put_rows<NTC, LKC>(fk, sK);
+    if (gain) put_rows<NTC, LKC>(fg, sGn);
     if (erase) put_cc<NTC, LCC>(ft, sT);
     put_scalars(a, fs, sLg, sB, sAl);
     {
@@ -395,7 +410,7 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
     __syncthreads();
     const float gC = expf(lgC);
     floatx4 acc[2] = {S[0] * gC, S[1] * gC};
-    mfma_row<2>(acc, sK, 1, LKC, nullptr, sE, LOC, 1, 16 * w, C);
+    mfma_row<2>(acc, gain ? sGn : sK, 1, LKC, nullptr, sE, LOC, 1, 16 * w, C);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       S[h] = acc[h];
@@ -421,7 +436,7 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
   float* sAl = sB + C;
   const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
   const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C, dk64 = dk <= 64 ? 64 : DP;
-  const bool erase = a.resid != 2;
+  const bool erase = a.resid != 2, gain = a.gain != nullptr;
   const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
   const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
   floatx4 G[2];
@@ -435,27 +450,36 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
                     : 0.f;
       sG[d * LOC + j] = G[h][i];
     }
-  Frag<C * DP / NTC> fk, fq;
+  // gain mode: the gain rows take the Q tile while dE is formed (no room for a
+  // third [C][d_k] tile), and Q, loaded after that, replaces them before the
+  // state-gradient update
+  Frag<C * DP / NTC> fk, fq, fg;
   Frag<C * C / NTC> fp, ft;
   Frag<C * TW / NTC> fo;
   Scal fs;
+  auto fetch_q = [&](int c) {
+    const int n = min(C, L - c * C);
+    fetch_rows<NTC>(fq, a.q + ((size_t)bh * L + (size_t)c * C) * dk, n, dk);
+  };
   auto fetch = [&](int c) {
     const int n = min(C, L - c * C);
     const size_t tok = (size_t)bh * L + (size_t)c * C;
     fetch_rows<NTC>(fk, a.k + tok * dk, n, dk);
-    fetch_rows<NTC>(fq, a.q + tok * dk, n, dk);
+    if (gain) fetch_rows<NTC>(fg, a.gain + tok * dk, n, dk);
+    else fetch_q(c);
     fetch_cc<NTC>(fp, a.Pm + cc_off(bh, nch, c));
     if (erase) fetch_cc<NTC>(ft, a.Tm + cc_off(bh, nch, c));
     fetch_tile<NTC>(fo, a.d_o + tok * dv, n, dv, j0);
     fs = fetch_scalars(a, tok, n);
   };
   fetch(nch - 1);
+  if (gain) fetch_q(nch - 1);
   for (int c = nch - 1; c >= 0; --c) {
     const int n = min(C, L - c * C);
     const size_t tok = (size_t)bh * L + (size_t)c * C;
     __syncthreads();
     put_rows<NTC, LKC>(fk, sK);
-    put_rows<NTC, LKC>(fq, sQ);
+    put_rows<NTC, LKC>(gain ? fg : fq, sQ);
     put_cc<NTC, LCC>(fp, sP);
     if (erase) put_cc<NTC, LCC>(ft, sT);
     put_tile<NTC, LOC>(fo, sO, nullptr);
@@ -478,7 +502,7 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
     {
       floatx4 x = {0.f, 0.f, 0.f, 0.f}, y = {0.f, 0.f, 0.f, 0.f};
       mfma16(x, sP, 1, LCC, sO, LOC, 1, m0, n0, C);
-      mfma16(y, sK, LKC, 1, sG, LOC, 1, m0, n0, dk64);
+      mfma16(y, gain ? sQ : sK, LKC, 1, sG, LOC, 1, m0, n0, dk64);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = m0 + 4 * q + i;
@@ -487,6 +511,10 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
+    if (gain) {  // every wavefront is done with the gain rows: Q takes the tile
+      put_rows<NTC, LKC>(fq, sQ);
+      if (c > 0) fetch_q(c - 1);
+    }
     floatx4 dr = de;
     if (erase) {
       dr = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -626,19 +654,22 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
   float* sAl = sB + C;
   float* sRow = sAl + C;         // [6][C] per-token sums
   float* sCs = sRow + 6 * C;     // [NT / 64][C] partial column sums
+  float* sGn = sCs + (NT / 64) * C;  // [C][LQ] gain rows (gain mode)
   const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, nch = gridDim.y;
   const int L = a.L, dk = a.dk, dv = a.dv;
   const int n = min(C, L - c * C);
   const size_t tok = (size_t)bh * L + (size_t)c * C;
   const size_t row0 = (size_t)bh * nch * C + (size_t)c * C;
-  const bool erase = a.resid != 2, plain = a.resid == 1;
+  const bool erase = a.resid != 2, plain = a.resid == 1, gain = a.gain != nullptr;
   {
-    Frag<C * DP / NT> fq, fk;
+    Frag<C * DP / NT> fq, fk, fg;
     fetch_rows<NT>(fq, a.q + tok * dk, n, dk);
     fetch_rows<NT>(fk, a.k + tok * dk, n, dk);
+    if (gain) fetch_rows<NT>(fg, a.gain + tok * dk, n, dk);
     const Scal sc = fetch_scalars(a, tok, n);
     put_rows<NT, LQ>(fq, sQ);
     put_rows<NT, LQ>(fk, sK);
+    if (gain) put_rows<NT, LQ>(fg, sGn);
     put_scalars(a, sc, sLg, sB, sAl);
   }
   const size_t o = cc_off(bh, nch, c);
@@ -689,9 +720,12 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
   __syncthreads();
   const float lgC = sLg[C - 1];
   float pq[4] = {}, kr[4] = {}, wv[4] = {}, dbv[4] = {}, vv[4] = {};
+  // the write vectors: rows b_t k_t (sB scaling sK), or the gain rows
+  const float* sW = gain ? sGn : sK;
+  const float* sWs = gain ? nullptr : sB;
   {  // dQ = diag(g) dO S0^T + Xp diag(b) K
     floatx4 acc[8] = {};
-    mfma_row<8>(acc, sXp, LX, 1, sB, sK, LQ, 1, 16 * w, C);
+    mfma_row<8>(acc, sXp, LX, 1, sWs, sW, LQ, 1, 16 * w, C);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * w + 4 * q + i;
@@ -711,7 +745,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     mfma_row<8>(db, sXp, 1, LX, nullptr, sQ, LQ, 1, 16 * w, C);
     if (erase) {
       mfma_row<8>(db, sXa, 1, LX, nullptr, sK, LQ, 1, 16 * w, C);
-      mfma_row<8>(dkk, sXa, LX, 1, sB, sK, LQ, 1, 16 * w, C);
+      mfma_row<8>(dkk, sXa, LX, 1, sWs, sW, LQ, 1, 16 * w, C);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -723,12 +757,19 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
         const float kv = sK[t * LQ + d];
         const float x3 = m3v[i][bb];
         const float x2 = m2v[i][bb];
-        wv[i] = fmaf(kv, x3, wv[i]);
+        wv[i] = fmaf(sW[t * LQ + d], x3, wv[i]);
         const float dbb = fmaf(lam, x3, db[bb][i]);
         dbv[i] = fmaf(dbb, kv, dbv[i]);
         const float dkr = -g * x2;
         kr[i] = fmaf(dkr, kv, kr[i]);
-        if (t < n && d < dk) a.dk_out[(tok + t) * dk + d] = fmaf(b, dbb, dkk[bb][i] + dkr);
+        if (t < n && d < dk) {
+          if (gain) {
+            a.dgain[(tok + t) * dk + d] = dbb;
+            a.dk_out[(tok + t) * dk + d] = dkk[bb][i] + dkr;
+          } else {
+            a.dk_out[(tok + t) * dk + d] = fmaf(b, dbb, dkk[bb][i] + dkr);
+          }
+        }
       }
       wv[i] *= lam * b;
       if (plain && t < n) {
@@ -782,7 +823,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
         dbe = dbp / al;
       }
       if (a.dalpha) a.dalpha[tok + t] = dal;
-      a.dbeta[tok + t] = dbe;
+      if (a.dbeta) a.dbeta[tok + t] = dbe;
     }
   }
 }
@@ -838,10 +879,11 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
   const int nch = (a.L + C - 1) / C, ntw = (a.dv + TW - 1) / TW;
   const size_t f = sizeof(float);
   hipError_t e;
-  e = launch_lds(bwd_prep_kernel, dim3(a.BH, nch), NT, (2 * C * (DP + 1) + 3 * C) * f, a, s);
+  const int ng = a.gain ? 1 : 0;  // gain mode: one more [C][d_k] tile per kernel
+  e = launch_lds(bwd_prep_kernel, dim3(a.BH, nch), NT, ((2 + ng) * C * (DP + 1) + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
   e = launch_lds(bwd_fwd_kernel, dim3(a.BH, ntw), NTC,
-                 (C * LKC + C * LCC + DP * LOC + 2 * C * LOC + 3 * C) * f, a, s);
+                 ((1 + ng) * C * LKC + C * LCC + DP * LOC + 2 * C * LOC + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
   e = launch_lds(bwd_rev_kernel, dim3(a.BH, ntw), NTC,
                  (2 * C * LKC + 2 * C * LCC + DP * LOC + 3 * C * LOC + 3 * C) * f, a, s);
@@ -852,7 +894,7 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
   e = launch_lds(bwd_contract_kernel<true>, dim3(a.BH, nch), NT, lds_c, a, s);
   if (e != hipSuccess) return e;
   return launch_lds(bwd_grad_kernel, dim3(a.BH, nch), NT,
-                    (2 * C * (DP + 1) + 2 * C * (C + 1) + 3 * C + 6 * C + (NT / 64) * C) * f,
+                    ((2 + ng) * C * (DP + 1) + 2 * C * (C + 1) + 3 * C + 6 * C + (NT / 64) * C) * f,
                     a, s);
 }
 

@@ -224,6 +224,12 @@ hipError_t launch_gain_typed(const ScanArgs& a, bool gain_f16, hipStream_t s) {
   return gain_f16 ? launch_typed<Tin, Tout, _Float16>(a, s) : launch_typed<Tin, Tout, float>(a, s);
 }
 
+__global__ void bf16_to_f32_kernel(const uint16_t* src, float* dst, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    dst[i] = bf16_to_f32(src[i]);
+}
+
 __global__ void copy_f32_kernel(const float* src, float* dst, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n;
        i += (size_t)gridDim.x * blockDim.x)
@@ -242,6 +248,14 @@ hipError_t launch_scan_f32(const ScanArgs& a, bool in_bf16, bool out_bf16, bool 
                     : launch_gain_typed<uint16_t, float>(a, gain_f16, s);
   return out_bf16 ? launch_gain_typed<float, uint16_t>(a, gain_f16, s)
                   : launch_gain_typed<float, float>(a, gain_f16, s);
+}
+
+hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(bf16_to_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s) {

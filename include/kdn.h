@@ -314,6 +314,48 @@ int kdn_scan_bwd(const float *q, const float *k, const float *v, const float *al
                  int resid, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Gradients of every write mode's scan except the full covariance, for float32
+ * or bf16 inputs: kdn_scan_bwd extended to the Kalman writes ("Kalman Delta
+ * Networks: Uncertainty-aware Associative Memory", abstract: the diagonal and
+ * isotropic covariance forms) with the gradients of the observation noise r
+ * and of the prior covariance. The loss L has the given dL/do (d_o), dL/dS_L
+ * (dstate_out) and, for the Kalman writes, dL/dcov_L (dcov_out).
+ *
+ * Mode DELTA: as kdn_scan_bwd (resid GATED, PLAIN or NOERASE; beta and dbeta
+ * required). Modes DIAG and ISO (resid GATED): the adjoint of the write of
+ * kdn_scan_fwd, evaluated as (1) the gains (DIAG) or write strengths (ISO) and
+ * the variance before every token, recomputed from cov_in; (2) the chunk-form
+ * state backward with those write vectors, which gives dL/d(write vector);
+ * (3) the reverse recursion through the gain and covariance maps per token
+ * (dp_{t-1} = alpha_t^2 (c_t + e_t dp_t), chunk maps composed in parallel),
+ * which adds the gain terms to dk and dalpha and gives dr and dcov_in.
+ *
+ *  q, k      [B,H,L,d_k] in_dtype (KDN_F32 or KDN_BF16);  v, d_o [B,H,L,d_v] in_dtype
+ *            (bf16 operands are converted to float32 inside the library).
+ *  alpha, beta, r, cov_in, q_noise_var, state_in: the forward call's inputs
+ *            (beta: DELTA only; r (NULL = 1) and cov_in (required): Kalman only).
+ *  dstate_out [B,H,d_k,d_v] or NULL (= 0);  dcov_out like cov_in or NULL (= 0).
+ *  dq, dk    [B,H,L,d_k] out;  dv [B,H,L,d_v] out;  dalpha [B,H,L] out (required
+ *            when alpha is given);  dbeta [B,H,L] out (DELTA);  dr [B,H,L] out
+ *            (Kalman, required when r is given);  dcov_in like cov_in, out or NULL;
+ *            dstate_in [B,H,d_k,d_v] out or NULL. All outputs float32.
+ *  workspace kdn_scan_bwd_ex_workspace_size(B, H, L, d_k, d_v, mode, in_dtype)
+ *            bytes, 16-byte aligned; no initialisation needed.
+ * Sizes as kdn_scan_bwd. Mode FULL returns KDN_ERR_UNSUPPORTED; alpha must be
+ * positive where given (dalpha is formed through log alpha).
+ */
+size_t kdn_scan_bwd_ex_workspace_size(int B, int H, int L, int d_k, int d_v, int mode,
+                                      int in_dtype);
+
+int kdn_scan_bwd_ex(const void *q, const void *k, const void *v, const void *d_o, int in_dtype,
+                    const float *alpha, const float *beta, const float *r, const float *cov_in,
+                    float q_noise_var, const float *state_in, const float *dstate_out,
+                    const float *dcov_out, float *dq, float *dk, float *dv, float *dalpha,
+                    float *dbeta, float *dr, float *dcov_in, float *dstate_in, int B, int H,
+                    int L, int d_k, int d_v, int mode, int resid, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
  * The HOLA cache over a whole prompt ("A Hippocampus for Linear Attention",
  * sec. 3.3 (top-w cache by write score), sec. 3.4 eq. (7) (visible set: the
  * cache, the causal tokens of the current block and an optional null sink),

@@ -36,7 +36,8 @@ def kdn():
 def test_exports_match_header(kdn):
     declared = _header_functions()
     assert declared == sorted(["hola_cache_update", "hola_prefill", "hola_prefill_workspace_size",
-                               "kdn_scan_bwd", "kdn_scan_bwd_workspace_size", "kdn_scan_fwd",
+                               "kdn_scan_bwd", "kdn_scan_bwd_workspace_size", "kdn_scan_bwd_ex",
+                               "kdn_scan_bwd_ex_workspace_size", "kdn_scan_fwd",
                                "kdn_scan_fwd_phase", "kdn_scan_fwd_static", "kdn_scan_workspace_size",
                                "kdn_status_string", "kdn_step_decode", "kdn_version"])
     out = subprocess.run(["nm", "-D", "--defined-only", kdn.LIB_PATH], capture_output=True,

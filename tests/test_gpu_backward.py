@@ -77,3 +77,81 @@ def test_backward_defaults(kdn, orc):
         for n in ("dq", "dk", "dv", "dbeta"):
             assert_close(host(g[n]), ref[n], TOL_F32, f"defaults {n}")
         assert_close(host(g["dstate_in"]), ref["dS0"], TOL_F32, "defaults dS0")
+
+
+def _kalman_case(kdn, orc, B, H, L, dk, dv, mode, dtype, seed, heads=None, qvar=0.7):
+    """kdn_scan_bwd_ex for a Kalman write against the oracle's adjoint: every
+    gradient (q, k, v, alpha, r, the prior covariance, the initial state) for a
+    loss with dL/do, dL/dS_L and dL/dcov_L all given."""
+    import torch
+    inp = workloads.scan_inputs(B, H, L, dk, dv, seed=seed, dtype=dtype, with_r=True)
+    rng = np.random.Generator(np.random.PCG64([seed, 8]))
+    inp["k"] = inp["k"] * rng.uniform(0.5, 1.5, (B, H, L, 1)).astype(np.float32)
+    d_o = rng.standard_normal((B, H, L, dv)).astype(np.float32)
+    if dtype == "bf16":
+        inp["k"] = workloads.bf16_round(inp["k"])
+        d_o = workloads.bf16_round(d_o)
+    cshape = (B, H, dk) if mode == "diag" else (B, H)
+    cov0 = rng.uniform(0.5, 2.0, cshape).astype(np.float32)
+    S0 = (rng.standard_normal((B, H, dk, dv)) * 0.1).astype(np.float32)
+    dS = rng.standard_normal((B, H, dk, dv)).astype(np.float32)
+    dcov = rng.standard_normal(cshape).astype(np.float32)
+    g = kdn.kdn_scan_bwd_ex(*(dev_tensor(inp[n], dtype) for n in ("q", "k", "v")),
+                            dev_tensor(d_o, dtype), alpha=dev_tensor(inp["alpha"]),
+                            r=dev_tensor(inp["r"]), cov_in=dev_tensor(cov0), q_noise_var=qvar,
+                            state_in=dev_tensor(S0), dstate_out=dev_tensor(dS),
+                            dcov_out=dev_tensor(dcov), mode=mode)
+    torch.cuda.synchronize()
+    got = {n: host(x) for n, x in g.items() if x is not None}
+    sel = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    bs = np.array([s[0] for s in sel])
+    hs = np.array([s[1] for s in sel])
+    sub = lambda x: np.ascontiguousarray(x[bs, hs][None])  # noqa: E731
+    ref = orc.scan_bwd_kalman(sub(inp["q"]), sub(inp["k"]), sub(inp["v"]), alpha=sub(inp["alpha"]),
+                              r=sub(inp["r"]), cov0=sub(cov0), q_noise_var=qvar, S0=sub(S0),
+                              d_o=sub(d_o), dS=sub(dS), dcov=sub(dcov), mode=mode)
+    for n in ("dq", "dk", "dv", "dalpha", "dr", "dS0", "dcov0"):
+        gn = {"dS0": "dstate_in", "dcov0": "dcov_in"}.get(n, n)
+        assert_close(got[gn][bs, hs], ref[n][0], TOL_F32, f"{mode} {dtype} {n}")
+
+
+@pytest.mark.parametrize("mode", ["diag", "iso"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_kalman_backward_small(kdn, orc, mode, dtype):
+    log(f"kalman backward {mode} {dtype}")
+    _kalman_case(kdn, orc, 1, 2, 150, 64, 64, mode, dtype, seed=406)
+
+
+def test_kalman_backward_shapes(kdn, orc):
+    """d_k = 128 (two coordinates per lane in the covariance adjoint), d_v not
+    a multiple of 32, no process noise, a ragged last chunk."""
+    _kalman_case(kdn, orc, 2, 1, 77, 128, 40, "diag", "f32", seed=407, qvar=0.0)
+    _kalman_case(kdn, orc, 1, 3, 130, 40, 24, "iso", "f32", seed=408)
+
+
+def test_delta_backward_bf16_inputs(kdn, orc):
+    """The delta write's gradients from bf16 inputs through kdn_scan_bwd_ex: the
+    oracle on the same bf16 values, float32 bar (the backward runs in float32)."""
+    import torch
+    B, H, L, d = 1, 2, 150, 128
+    inp = workloads.scan_inputs(B, H, L, d, d, seed=409, dtype="bf16")
+    rng = np.random.Generator(np.random.PCG64(409))
+    d_o = workloads.bf16_round(rng.standard_normal((B, H, L, d)).astype(np.float32))
+    dS = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    g = kdn.kdn_scan_bwd_ex(*(dev_tensor(inp[n], "bf16") for n in ("q", "k", "v")),
+                            dev_tensor(d_o, "bf16"), alpha=dev_tensor(inp["alpha"]),
+                            beta=dev_tensor(inp["beta"]), dstate_out=dev_tensor(dS), mode="delta")
+    torch.cuda.synchronize()
+    ref = orc.scan_bwd(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"], d_o=d_o,
+                       dS=dS)
+    for n in ("dq", "dk", "dv", "dalpha", "dbeta"):
+        assert_close(host(g[n]), ref[n], TOL_F32, f"bf16 delta {n}")
+    assert_close(host(g["dstate_in"]), ref["dS0"], TOL_F32, "bf16 delta dS0")
+
+
+def test_kalman_backward_full_size(kdn, orc):
+    """The diagonal Kalman workload's shape (B=4, H=16, L=4096, d=128, bf16
+    inputs), checked on 16 heads spread over the batch and the heads."""
+    log("kalman backward full size")
+    heads = [(b, h) for b in range(4) for h in (0, 5, 10, 15)]
+    _kalman_case(kdn, orc, 4, 16, 4096, 128, 128, "diag", "bf16", seed=410, heads=heads, qvar=1.0)
