@@ -22,7 +22,12 @@ constexpr int kMaxPrefillBlock = 1024;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+bool valid_chunk(int c) { return c == 16 || c == 32 || c == 64 || c == 128; }
+
+// The chunk the kernels run. 128 runs as 64-token chunks: the chunk form gives
+// the same result for any chunk length up to rounding, and the matrix-core
+// kernels are built for 64 while the float32 kernel's LDS grows with C^2.
+int run_chunk(int c) { return c == 128 ? 64 : c; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -79,7 +84,7 @@ KDN_EXPORT const char* kdn_status_string(int status) {
     case KDN_OK: return "ok";
     case KDN_ERR_NULL_POINTER: return "a required pointer is NULL";
     case KDN_ERR_BAD_SHAPE: return "a size argument is out of range";
-    case KDN_ERR_BAD_CHUNK: return "chunk must be 16, 32 or 64";
+    case KDN_ERR_BAD_CHUNK: return "chunk must be 16, 32, 64 or 128";
     case KDN_ERR_BAD_MODE: return "unknown write mode or residual form, or plain residual with a Kalman gain";
     case KDN_ERR_BAD_DTYPE: return "unknown element type";
     case KDN_ERR_UNSUPPORTED: return "valid arguments that this library does not implement (e.g. full covariance with d_k > 64)";
@@ -100,7 +105,7 @@ KDN_EXPORT int kdn_version(void) { return 100; }
 KDN_EXPORT size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
                                           int mode, int in_dtype, int with_scores) {
   if (B < 1 || H < 1 || L < 0 || d_k < 1 || d_v < 1 || !valid_chunk(chunk)) return 0;
-  return ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype, with_scores != 0).total;
+  return ws_layout(B, H, L, d_k, d_v, run_chunk(chunk), mode, in_dtype, with_scores != 0).total;
 }
 
 namespace kdn {
@@ -126,6 +131,7 @@ int scan_args_status(int phase, const void* q, const void* k, const void* v, int
     return KDN_ERR_BAD_SHAPE;
   if ((long long)B * H > (1LL << 24)) return KDN_ERR_BAD_SHAPE;
   if (!valid_chunk(chunk)) return KDN_ERR_BAD_CHUNK;
+  chunk = run_chunk(chunk);
   if ((long long)(L + chunk - 1) / chunk > kMaxGridYZ) return KDN_ERR_BAD_SHAPE;
   if (mode == KDN_GAIN_FULL && d_k > kMaxFullDk) return KDN_ERR_UNSUPPORTED;
   if (mode != KDN_GAIN_DELTA && cov_in == nullptr) return KDN_ERR_NULL_POINTER;
@@ -153,6 +159,7 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
                                        out_dtype, m, score_kind, B, H, L, d_k, d_v, chunk, mode,
                                        resid);
   if (st != KDN_OK) return st;
+  chunk = run_chunk(chunk);
   const bool do_prep = phase != KDN_PHASE_STATE, do_state = phase != KDN_PHASE_PREPARE;
   const WsLayout ws = ws_layout(B, H, L, d_k, d_v, chunk, mode, in_dtype, m != nullptr);
   if (ws.total > 0 && (workspace == nullptr || workspace_bytes < ws.total || !aligned16(workspace)))
@@ -241,6 +248,7 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
     sc.v_bf16 = in_bf16 ? 1 : 0;
     sc.esq = a.esq;
     sc.ubuf = a.ubuf;
+    sc.uexp = a.ubuf ? kdn::scan_mfma_ubuf_exps(a.ubuf, BH, L, d_v) : nullptr;
     sc.ntiles = mfma_ok ? d_v / 32 : (d_v + cols - 1) / cols;
     sc.beta = a.beta;
     sc.iso_beta = iso_beta;

@@ -125,6 +125,9 @@ size_t scan_mfma_workspace_bytes(int BH, int L, bool gain);
 // Bytes of the residual buffer of the matrix-core path (fp16 residuals of
 // every token and value column).
 size_t scan_mfma_ubuf_bytes(int BH, int L, int dv);
+// The residuals there are times 2^e_S, one int exponent per (head, 32-column
+// slice, chunk), stored after them: their address.
+const int* scan_mfma_ubuf_exps(const void* ubuf, int BH, int L, int dv);
 
 // Write scores m_t = s_t ||e_t|| ("A Hippocampus for Linear Attention", sec.
 // 3.3 eq. (6)) from the residuals a scan left in esq (float32 path, `ntiles`
@@ -137,6 +140,7 @@ struct ScoreArgs {
   int v_bf16;
   const float* esq;
   const void* ubuf;
+  const int* uexp;  // exponents of the residuals in ubuf (see scan_mfma_ubuf_exps)
   int ntiles;
   const float* beta;
   const float* iso_beta;

@@ -41,6 +41,21 @@
 // operands the output error at the gated-delta workload is ~3.7e-2 RMS(o),
 // with fp16 ~5e-3.
 //
+// Range: fp16 operands overflow above 65504. The state, the values and the
+// residuals are therefore carried scaled by powers of two, which is exact:
+// the producers stage a chunk's values times 2^e_p when its largest finite
+// |v| reaches 2^12 (e_p = 11 - floor(log2 max), else 0), and the chain keeps
+// S * 2^e_S in its accumulators. It checks max |S * 2^e_S| while a chunk's
+// K S products run; at the next chunk start, if that reached 2^11 (or stayed
+// below 2^5 with e_S < 0), e_S is recomputed from the state so that its
+// largest finite entry lies in [2^9, 2^10) (e_S = 0 if the state is below
+// 2^11). Then e_S is lowered to the chunk's value exponents if they are
+// lower, and value rows staged at a higher exponent are scaled down in
+// place, so one exponent holds for the whole chunk. The recurrence is linear
+// in (V, S, U, O), so the residuals and outputs come out scaled and are
+// unscaled when stored. With values and states below 2^11 nothing is scaled;
+// the step itself never branches on the range.
+//
 // Operand layouts: an MFMA reads A as [m][k] and B as [n][k] with k contiguous
 // (16-byte LDS reads); its result gives each lane 4 consecutive rows of one
 // column, which is written either as [n][m] (one 8-byte write) or [m][n]
@@ -588,6 +603,7 @@ __device__ __forceinline__ half4 bf16x4_to_f16x4(uint2 u) {
 }
 
 struct StateArgs {
+  int* uexp;             // e_S of every (head, slice, chunk) for the write scores, or null
   const uint16_t* q;     // bf16 [BH, L, DK]
   const uint16_t* k;     // bf16 [BH, L, DK]
   const uint16_t* v;     // bf16 [BH, L, dv]
@@ -605,8 +621,9 @@ constexpr int VP = DV + 8;  // fp16 pitch of the staged V rows
 
 // LDS, per chain stage (3 for the delta write, 2 for the Kalman writes):
 //   K [C][KP]; gains [C][KP] (Kalman); T [C][CP] (lower blocks only);
-//   V times the value scale [C][VP]; nine token scalars [9][C] (g_x, w, log2 g,
-//   write scale, R, Cf, f0, f1, g) and the chunk's extreme-decay flag;
+//   V times 2^e_p [C][VP]; nine token scalars [9][C] (g_x, w, log2 g, write
+//   scale, R, Cf, f0, f1, g), the chunk's extreme-decay flag and the two
+//   producers' value exponents (floor log2 of their rows' largest finite |v|);
 // per output stage (2): Q [C][KP] (delta) or P [C][CP] and g [C] (Kalman);
 // per exchange buffer (2): S (8 k steps) and U (4 k steps), 16 bytes per lane
 // and k step in wavefront-0 register order.
@@ -614,7 +631,7 @@ constexpr size_t kStK = (size_t)C * KP * 2;
 constexpr size_t kStT = (size_t)C * CP * 2;
 constexpr size_t kStV = (size_t)C * VP * 2;
 constexpr size_t kStSc = (size_t)9 * C * 4 + 16;
-constexpr size_t kExBytes = (size_t)12 * 64 * 16;
+constexpr size_t kExBytes = (size_t)12 * 64 * 16 + 16;  // S, U, then their exponent
 __host__ __device__ constexpr int n_chain_stages(bool gain) { return gain ? 2 : 3; }
 __host__ __device__ constexpr size_t chain_stage_bytes(bool gain) {
   return kStK * (gain ? 2 : 1) + kStT + kStV + kStSc;
@@ -641,6 +658,7 @@ struct ChainStage {
   float* cf;
   float* go;     // g (the read-out's decay)
   float* extreme;
+  int* vexp;     // [2] exponents of the largest finite |v| of rows 0-31, 32-63 (< 12: all below 2^12)
 };
 struct OutStage {
   _Float16* q;   // delta write
@@ -659,6 +677,7 @@ __device__ __forceinline__ ChainStage chain_stage(unsigned char* lds, int buf) {
   float* f = reinterpret_cast<float*>(p);
   s.g = f; s.w = f + C; s.lg = f + 2 * C; s.bs = f + 3 * C; s.f0 = f + 4 * C; s.f1 = f + 5 * C;
   s.rr = f + 6 * C; s.cf = f + 7 * C; s.go = f + 8 * C; s.extreme = f + 9 * C;
+  s.vexp = reinterpret_cast<int*>(f + 9 * C + 1);
   return s;
 }
 template <bool GAIN>
@@ -739,6 +758,47 @@ __device__ __forceinline__ void prod_load(const ProdCtx& x, ProdBuf<GAIN>& b, in
   if constexpr (GAIN) b.go = reinterpret_cast<const float4*>(ro + rec_s_off(true))[3 * l].x;
 }
 
+// Maximum over the 64 lanes (every lane gets it; all lanes active).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, true));  // ^1
+  x = max(x, (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, true));  // ^2
+  x = max(x, (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (4 << 10)));
+  x = max(x, (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (8 << 10)));
+  x = max(x, (uint32_t)__builtin_amdgcn_ds_swizzle((int)x, 0x1F | (16 << 10)));
+  const auto sw = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return max(x, __lane_id() < 32 ? sw[1] : sw[0]);
+}
+// 2^e as a float, -126 <= e <= 127
+__device__ __forceinline__ float pow2i(int e) { return __int_as_float((127 + e) << 23); }
+// Largest of three, a NaN propagating (one v_maximum3_f32, abs folded into
+// its operands; no quieting of the inputs as the number-preferring maximum needs)
+__device__ __forceinline__ float max3_nan(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+// Exponent floor(log2 |v|) of the largest finite |v| among the bf16 values in
+// `n` dwords of every lane, when it is at least 12; any smaller result (-127
+// here) means that every finite |v| is below 2^12. A ballot on the lanes'
+// packed maxima decides whether some |v| reaches 4096 or is not finite; only
+// then are the non-finite ones masked and the maximum taken over the wave.
+template <int N>
+__device__ __forceinline__ int bf16_max_exponent(const uint32_t (&w)[N]) {
+  typedef unsigned short ushort2v __attribute__((ext_vector_type(2)));
+  ushort2v m = {0, 0};
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    m = __builtin_elementwise_max(m, __builtin_bit_cast(ushort2v, w[i] & 0x7fff7fffu));
+  if (__ballot(max((uint32_t)m[0], (uint32_t)m[1]) >= 0x4580u) == 0) return -127;
+  uint32_t f = 0;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const uint32_t lo = w[i] & 0x7fffu, hi = (w[i] >> 16) & 0x7fffu;
+    f = max(f, max(lo < 0x7f80u ? lo : 0u, hi < 0x7f80u ? hi : 0u));
+  }
+  return (int)(__builtin_amdgcn_readfirstlane(wave_max_u32(f)) >> 7) - 127;
+}
+// The staging exponent for values whose largest |v| has exponent E.
+__device__ __forceinline__ int value_shift(int E) { return E >= 12 ? max(11 - E, -120) : 0; }
+
 template <bool GAIN>
 __device__ __forceinline__ void prod_stage(const ProdCtx& x, const ProdBuf<GAIN>& b,
                                            const ChainStage& cs, const OutStage& os) {
@@ -757,12 +817,24 @@ __device__ __forceinline__ void prod_stage(const ProdCtx& x, const ProdBuf<GAIN>
     *reinterpret_cast<uint4*>(cs.t + row * CP + col) = b.t[i];
     if constexpr (GAIN) *reinterpret_cast<uint4*>(os.p + row * CP + col) = b.p[i];
   }
-  // V times the value scale of its row (lane t holds token t's scalars)
+  // V times 2^e_p, e_p from the largest finite |v| of this producer's rows
+  {
+    const uint32_t vw[8] = {b.v[0].x, b.v[0].y, b.v[0].z, b.v[0].w,
+                            b.v[1].x, b.v[1].y, b.v[1].z, b.v[1].w};
+    const int E = bf16_max_exponent(vw);
+    uint4 vh[2];
+    if (E >= 12) {
+      const float vsc = pow2i(value_shift(E));
+      vh[0] = bf16x8_to_f16x8(b.v[0], vsc);
+      vh[1] = bf16x8_to_f16x8(b.v[1], vsc);
+    } else {
+      vh[0] = bf16x8_to_f16x8(b.v[0]);
+      vh[1] = bf16x8_to_f16x8(b.v[1]);
+    }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const float vsr = __shfl(b.sc2.x, r0 + 16 * i + (l >> 2), 64);
-    *reinterpret_cast<uint4*>(cs.v + (r0 + 16 * i + (l >> 2)) * VP + (l & 3) * 8) =
-        bf16x8_to_f16x8(b.v[i], vsr);
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint4*>(cs.v + (r0 + 16 * i + (l >> 2)) * VP + (l & 3) * 8) = vh[i];
+    if (l == 0) cs.vexp[x.pw] = E;
   }
   if (x.pw == 0) {
     cs.g[l] = b.sc0.x;
@@ -892,6 +964,10 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
     const __amdgpu_buffer_rsrc_t ru =
         make_rsrc(a.ubuf + (a.ubuf ? (size_t)(bh * a.ntiles + tile) * a.nchunks * 256 : 0),
                   a.ubuf ? (size_t)a.nchunks * 256 * 16 : 0);
+    // the chunk's state exponent e_S beside the residuals (scaled by 2^e_S)
+    const __amdgpu_buffer_rsrc_t rue =
+        make_rsrc(a.uexp + (a.uexp ? (size_t)(bh * a.ntiles + tile) * a.nchunks : 0),
+                  a.uexp ? (size_t)a.nchunks * 4 : 0);
     QBuf b0, b1;
     // Kalman writes: every step runs the same memory operations (Q loads of
     // chunk c + 1, 8 output stores (4 for bf16 outputs), 4 residual stores).
@@ -909,6 +985,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
       const v4u32 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < (OBF16 ? 4 : 8) + 4; ++i) __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
     }
     __syncthreads();
     int cs_prev = NCH - 1;  // chain stage of chunk c - 1
@@ -1053,6 +1130,8 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         // consecutive value columns of one token: 16-byte stores. Columns of
         // O^T are tokens: O^T = (S^T Q^T) diag(g) + U^T P^T.
         const float* gsrc = GAIN ? os.g : cs.go;
+        // S and U came times 2^eo
+        const int eo = __builtin_amdgcn_readfirstlane(reinterpret_cast<const int*>(ex + 12 * 64)[0]);
         const float gt[2] = {gsrc[c32], gsrc[32 + c32]};
 #pragma unroll
         for (int tb = 0; tb < 2; ++tb)
@@ -1065,6 +1144,16 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         o[1] = mfma32(uv[2], pa[4], o[1]);
         o[1] = mfma32(uv[3], pa[5], o[1]);
         __builtin_amdgcn_sched_barrier(0);
+        // U came times 2^eo, and so did o
+        if (eo != 0) {
+          const float f = pow2i(-eo);
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[tb][e] *= f;
+        }
+        if (GAIN || a.uexp)
+          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)eo, rue, lane == 0 ? cc * 4 : 1 << 30, 0, 0);
         // residuals U of this chunk and d_v slice, in wavefront-0 register
         // order (Kalman writes: issued, and dropped, without them too)
         if (GAIN || a.ubuf) {
@@ -1130,6 +1219,42 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
       const int d = 32 * b + 8 * (j >> 2) + 4 * h + (j & 3);
       S[b][j] = a.state_in ? a.state_in[((size_t)bh * DK + d) * a.dv + j0 + c32] : 0.f;
     }
+  // The state is carried as S * 2^eS (see "Range" at the top). The state
+  // entering each chunk is checked while the chunk runs (largest |S 2^eS|, a
+  // NaN propagating: its column is NaN from then on); at the next chunk start
+  // a check that reached 2^11, or one below 2^5 with eS < 0, has the exponent
+  // recomputed from the state at hand.
+  auto absmax16 = [](const floatx16& x) {
+    float m = max3_nan(fabsf(x[0]), fabsf(x[1]), fabsf(x[2]));
+#pragma unroll
+    for (int j = 3; j < 15; j += 2) m = max3_nan(m, fabsf(x[j]), fabsf(x[j + 1]));
+    return __builtin_elementwise_maximum(m, fabsf(x[15]));
+  };
+  int eS = 0;
+  // eS that brings the largest finite |S| into [2^9, 2^10), or 0 if it is below 2^11
+  auto rescale_state = [&]() {
+    float f = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) f = fabsf(S[b][j]) < INFINITY ? fmaxf(f, fabsf(S[b][j])) : f;
+    const uint32_t mb = __builtin_amdgcn_readfirstlane(wave_max_u32(__float_as_uint(f)));
+    const int Et = (int)(mb >> 23) - 127 - eS;  // exponent of the largest true |S|
+    const int e = Et >= 11 ? max(9 - Et, -120) : 0;
+    if (e != eS) {
+      const float sc = pow2i(e - eS);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) S[b] = S[b] * sc;
+      eS = e;
+    }
+  };
+  bool s_chk = false;  // the last check asks for a recomputed exponent
+  {
+    float smax = 0.f;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) smax = fmaxf(smax, absmax16(S[b]));
+    s_chk = __ballot(smax >= 2048.f) != 0;
+  }
   __syncthreads();
 
   // One step is 38 products issued back to back, one per "slot"; the
@@ -1167,7 +1292,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         ex[(2 * b) * 64 + lane] = s16[2 * b];
         ex[(2 * b + 1) * 64 + lane] = s16[2 * b + 1];
       };
-      // X = V' - g K S for token block blk, column quads g4 (k = token operand)
+      // X = V - g K S for token block blk, column quads g4 (k = token operand)
       auto x_quad = [&](int blk, int g4) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
@@ -1193,10 +1318,46 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         btr[q] = ld_tr(st.b + (16 * s + 8 * hi + tr_row) * KP + 32 * b + tr_col);
       };
       const int tr_[6] = {0, 0, 32, 32, 32, 32}, tk_[6] = {0, 16, 0, 16, 32, 48};
+      float smax = 0.f;  // largest |S 2^eS| entering this chunk
 
+      // the chunk's exponent: the state's, recomputed if the last check asked,
+      // and no higher than the staging exponents of the chunk's values, so
+      // that |V 2^eS| < 2^12; rows staged at a higher exponent are scaled down
+      const int vE0 = st.vexp[0], vE1 = st.vexp[1];
+      if (s_chk) rescale_state();
 #pragma unroll
       for (int i = 0; i < 4; ++i) ka[i] = k_op(i);
       s_to_f16(0);
+      {
+        const int p0 = value_shift(__builtin_amdgcn_readfirstlane(vE0));
+        const int p1 = value_shift(__builtin_amdgcn_readfirstlane(vE1));
+        const int e = min(eS, min(p0, p1));
+        if (e != eS || p0 != e || p1 != e) {
+          if (e != eS) {
+            const float sc = pow2i(e - eS);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) S[b] = S[b] * sc;
+            eS = e;
+            s_to_f16(0);
+          }
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk) {
+            const int p = blk ? p1 : p0;
+            if (p != e) {
+              const float sc = pow2i(e - p);
+#pragma unroll
+              for (int i = 0; i < 2; ++i) {
+                half8* vp = reinterpret_cast<half8*>(st.v + (32 * blk + 16 * i + (lane >> 2)) * VP + (lane & 3) * 8);
+                half8 v = *vp;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) v[j] = (_Float16)((float)v[j] * sc);
+                *vp = v;
+              }
+            }
+          }
+        }
+        if (lane == 0) reinterpret_cast<int*>(ex + 12 * 64)[0] = eS;
+      }
       const float gn = st.go[n - 1];   // the state carries the inclusive decay g_n
       __builtin_amdgcn_sched_barrier(0);
       static_for<38>([&](auto slot_c) {
@@ -1222,6 +1383,14 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
           const int q = slot - 1, blk = q >> 2, g4 = q & 3;
           vv[blk][g4] = ld_tr(st.v + (32 * blk + 8 * g4 + tr_row) * VP + tr_col);
           gg[blk][g4] = *reinterpret_cast<const float4*>(st.g + 32 * blk + 8 * g4 + 4 * h);
+        }
+        // the state entering the chunk: checked block by block once converted
+        if constexpr (slot == 1) smax = absmax16(S[0]);
+        if constexpr (slot == 3 || slot == 5) smax = __builtin_elementwise_maximum(smax, absmax16(S[(slot - 1) / 2]));
+        if constexpr (slot == 7) {
+          smax = __builtin_elementwise_maximum(smax, absmax16(S[3]));
+          const bool hi = __ballot(smax >= 2048.f) != 0, lo = __ballot(smax >= 32.f) == 0;
+          s_chk = hi | (lo & (eS < 0));
         }
         if constexpr (slot >= 8 && slot <= 11) S[slot - 8] = S[slot - 8] * gn;
         if constexpr (slot >= 9 && slot <= 12) {
@@ -1262,12 +1431,13 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
   }
 
   if (a.state_out) {
+    const float f = pow2i(-eS);
 #pragma unroll
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int d = 32 * b + 8 * (j >> 2) + 4 * h + (j & 3);
-        a.state_out[((size_t)bh * DK + d) * a.dv + j0 + c32] = S[b][j];
+        a.state_out[((size_t)bh * DK + d) * a.dv + j0 + c32] = S[b][j] * f;
       }
   }
 }
@@ -1278,9 +1448,17 @@ bool scan_mfma_supported(int dk, int dv, int chunk) {
   return dk == DK && chunk == C && dv % DV == 0 && dv >= DV;
 }
 
-size_t scan_mfma_ubuf_bytes(int BH, int L, int dv) {
+// residuals, then the int exponent e_S of every (head, slice, chunk)
+static size_t ubuf_core_bytes(int BH, int L, int dv) {
   const size_t nchunks = ((size_t)L + C - 1) / C;
   return (size_t)BH * (dv / DV) * nchunks * 256 * sizeof(half8);
+}
+size_t scan_mfma_ubuf_bytes(int BH, int L, int dv) {
+  const size_t nchunks = ((size_t)L + C - 1) / C;
+  return ubuf_core_bytes(BH, L, dv) + (size_t)BH * (dv / DV) * nchunks * sizeof(int);
+}
+const int* scan_mfma_ubuf_exps(const void* ubuf, int BH, int L, int dv) {
+  return reinterpret_cast<const int*>(static_cast<const char*>(ubuf) + ubuf_core_bytes(BH, L, dv));
 }
 
 size_t scan_mfma_workspace_bytes(int BH, int L, bool gain) {
@@ -1346,6 +1524,7 @@ hipError_t launch_state_mfma(const ScanArgs& s, bool out_bf16, const void* tbuf,
   sa.nchunks = (s.L + C - 1) / C;
   sa.ntiles = s.dv / DV;
   sa.ubuf = static_cast<half8*>(s.ubuf);
+  sa.uexp = s.ubuf ? const_cast<int*>(scan_mfma_ubuf_exps(s.ubuf, s.BH, s.L, s.dv)) : nullptr;
   if (s.gain)
     return out_bf16 ? launch_state_typed<true, true>(sa, st) : launch_state_typed<true, false>(sa, st);
   return out_bf16 ? launch_state_typed<false, true>(sa, st) : launch_state_typed<false, false>(sa, st);

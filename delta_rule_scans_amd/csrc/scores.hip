@@ -23,16 +23,22 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 // state kernel's register order. Token t = 32 b + 8 g + 4 h + r sits in block
 // 2 b + g / 2, element 4 (g % 2) + r, of the 32 lanes 32 h .. 32 h + 31 (one
 // value column each).
-__device__ float ubuf_sq(const half8* ub, int bh, int ntiles, int nchunks, int cc, int t) {
+// The residuals of a (head, tile, chunk) are stored times 2^e_S (uexp).
+__device__ float ubuf_sq(const half8* ub, const int* uexp, int bh, int ntiles, int nchunks, int cc,
+                         int t) {
   const int b = t >> 5, g = (t >> 3) & 3, h = (t >> 2) & 1, r = t & 3;
   const int blk = 2 * b + (g >> 1), e = 4 * (g & 1) + r;
   float ss = 0.f;
   for (int tile = 0; tile < ntiles; ++tile) {
-    const half8* p = ub + ((size_t)(bh * ntiles + tile) * nchunks + cc) * 256 + blk * 64 + 32 * h;
+    const size_t rec = (size_t)(bh * ntiles + tile) * nchunks + cc;
+    const half8* p = ub + rec * 256 + blk * 64 + 32 * h;
+    float st = 0.f;
     for (int c = 0; c < 32; ++c) {
       const float x = (float)p[c][e];
-      ss = fmaf(x, x, ss);
+      st = fmaf(x, x, st);
     }
+    const float f = __int_as_float((127 - uexp[rec]) << 23);  // 2^-e_S
+    ss = fmaf(st * f, f, ss);
   }
   return ss;
 }
@@ -45,7 +51,7 @@ __global__ __launch_bounds__(64) void scores_kernel(ScoreArgs a) {
   float ss = 0.f;
   if (a.ubuf) {
     const int nchunks = (a.L + 63) / 64;
-    ss = ubuf_sq(static_cast<const half8*>(a.ubuf), bh, a.dv / 32, nchunks, cc, t);
+    ss = ubuf_sq(static_cast<const half8*>(a.ubuf), a.uexp, bh, a.dv / 32, nchunks, cc, t);
   } else {
     for (int tile = 0; tile < a.ntiles; ++tile) ss += a.esq[((size_t)bh * a.ntiles + tile) * a.L + tok];
   }

@@ -82,7 +82,7 @@ extern "C" {
 #define KDN_OK 0
 #define KDN_ERR_NULL_POINTER (-1)  /* a required pointer is NULL                   */
 #define KDN_ERR_BAD_SHAPE (-2)     /* a size is < 1 (L may be 0) or out of range   */
-#define KDN_ERR_BAD_CHUNK (-3)     /* chunk not in {16, 32, 64}                     */
+#define KDN_ERR_BAD_CHUNK (-3)     /* chunk not in {16, 32, 64, 128}                */
 #define KDN_ERR_BAD_MODE (-4)      /* unknown mode / residual / score / policy, or a
                                       residual form the write mode does not take   */
 #define KDN_ERR_BAD_DTYPE (-5)     /* unknown element type                          */
@@ -144,19 +144,25 @@ size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
  *            matrix-core path e_t is taken from its fp16 copy (relative error
  *            ~2^-11). Needs the workspace sized with with_scores = 1.
  *  score_kind KDN_SCORE_* (ignored when m is NULL).
- *  chunk     chunk length in tokens: 16, 32 or 64. The result does not depend on
- *            it beyond rounding; L need not be a multiple of it.
+ *  chunk     chunk length in tokens: 16, 32, 64 or 128. The result does not
+ *            depend on it beyond rounding; L need not be a multiple of it. 128
+ *            runs as 64-token chunks (the kernels' largest).
  *  mode      KDN_GAIN_*;  resid  KDN_RESID_* (PLAIN and NOERASE only with
  *            DELTA; NOERASE runs on the float32 path).
  *  workspace device scratch of at least kdn_scan_workspace_size(...) bytes,
  *            16-byte aligned (may be NULL when that size is 0).
  * Sizes: B, H >= 1; L >= 0 (L = 0 copies state_in to state_out and cov_in to
  * cov_out); 1 <= d_k, d_v <= 128; FULL mode needs d_k <= 64.
- * Paths: bf16 inputs with d_k = 128, d_v a multiple of 32, chunk = 64 and
- * 16-byte-aligned q, k, v, o run on the matrix cores: products in fp16 with
- * float32 accumulation, float32 state; bf16 inputs are converted to fp16, so
- * their magnitudes must stay below 65504 (values below 2^-14 lose precision as
- * fp16 subnormals). Every other combination runs the float32 vector path.
+ * Paths: bf16 inputs with d_k = 128, d_v a multiple of 32, chunk = 64 (or
+ * 128) and 16-byte-aligned q, k, v, o run on the matrix cores: products in
+ * fp16 with float32 accumulation, float32 state. The values, the state and the
+ * residuals are carried scaled by exact powers of two: a chunk's values once
+ * one reaches 2^12, the state once its largest entry reaches 2^11 (checked
+ * once per chunk, so it may grow up to 32-fold within one chunk), so they may
+ * take any finite magnitude; q and k are staged as fp16 unscaled, so their
+ * entries must stay below 65504 (unit keys always do; entries below 2^-14
+ * become fp16 subnormals, an absolute error below 2^-24). Every other
+ * combination runs the float32 vector path.
  */
 int kdn_scan_fwd(const void *q, const void *k, const void *v, int in_dtype,
                  const float *alpha, const float *beta, const float *r,

@@ -115,8 +115,13 @@ def test_scan_rejections(kdn):
         assert _scan(kdn, **bad) == c["KDN_ERR_BAD_SHAPE"], bad
     assert _scan(kdn, qvar=-1.0) == c["KDN_ERR_BAD_SHAPE"]
     assert _scan(kdn, qvar=float("nan")) == c["KDN_ERR_BAD_SHAPE"]
-    for ch in (0, 8, 17, 128, 256):
+    for ch in (0, 8, 17, 96, 256):
         assert _scan(kdn, chunk=ch) == c["KDN_ERR_BAD_CHUNK"], ch
+    # chunk 128 is taken, and runs as 64-token chunks: the same workspace
+    for mode in ("delta", "diag", "iso"):
+        for dt in (kdn.F32, kdn.BF16):
+            assert kdn.kdn_scan_workspace_size(2, 3, 1000, 128, 128, 128, mode, dt, True) == \
+                kdn.kdn_scan_workspace_size(2, 3, 1000, 128, 128, 64, mode, dt, True)
     assert _scan(kdn, mode=2, cov_in=P, dk=128) == c["KDN_ERR_UNSUPPORTED"]
     assert _scan(kdn, mode=2, cov_in=P, dk=64) == c["KDN_ERR_WORKSPACE"]
     # an unknown phase is rejected like an unknown mode

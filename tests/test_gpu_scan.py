@@ -74,7 +74,7 @@ def test_gated_delta_small(kdn, orc, dtype):
     S0 = np.random.Generator(np.random.PCG64(101)).standard_normal((2, 3, 128, 128)).astype(np.float32) * 0.1
     ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"], S0=S0)
     tol = TOL_BF16 if dtype == "bf16" else TOL_F32
-    for chunk in (16, 32, 64):
+    for chunk in (16, 32, 64, 128):
         log(f"gated {dtype} chunk {chunk}")
         got = _scan_gpu(kdn, inp, dtype, chunk, S0=S0)
         assert_close(got["o"], ref["o"], tol, f"o chunk {chunk}")
@@ -541,6 +541,77 @@ def test_nonfinite_inputs_propagate(kdn, orc, dtype):
         keep = np.arange(d) != col
         assert_close(got["o"][0, h][:, keep], ref["o"][0, h][:, keep], tol, f"head {h} untouched columns")
         assert np.all(~np.isfinite(got["o"][0, h, (70 if h == 3 else 100):, col]))
+
+
+@pytest.mark.parametrize("mode", ["delta", "diag"])
+def test_fp16_range_large_values(kdn, orc, mode):
+    """Values far beyond the fp16 range of the matrix-core operands (bf16 allows
+    them): the state, values and residuals are carried scaled by exact powers
+    of two. Head 0: |v| up to ~1e5 in chunks 1 and 2, ordinary values around
+    them (the scale must come back); head 1: values ~5000 (the state grows
+    past 2^12 and is rescaled on its own); head 2: an initial state of ~1e5
+    with ordinary values. o, S (and p) against the oracle at the bf16 bar."""
+    B, H, L, d = 1, 3, 330, 128
+    diag = mode == "diag"
+    inp = workloads.scan_inputs(B, H, L, d, d, seed=124, dtype="bf16", with_r=diag)
+    v = inp["v"].copy()
+    v[0, 0, 64:192] *= 4.0e4
+    v[0, 1] *= 2.5e3
+    inp["v"] = workloads.bf16_round(v)
+    rng = np.random.Generator(np.random.PCG64(124))
+    S0 = (rng.standard_normal((B, H, d, d)) * 0.1).astype(np.float32)
+    S0[0, 2] *= 1.0e6
+    inp["alpha"][0, 2] = 1.0   # the large initial state lasts to the final state
+    cov0 = np.ones((B, H, d), np.float32) if diag else None
+    qvar = 1.0 if diag else 0.0
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"], r=inp["r"],
+                   cov0=cov0, q_noise_var=qvar, S0=S0, mode=mode)
+    assert np.abs(ref["o"][0, :2]).max() > 65504 and np.abs(ref["S"][0, 2]).max() > 65504
+    got = _scan_gpu(kdn, inp, "bf16", 64, mode=mode, cov0=cov0, qvar=qvar, S0=S0)
+    for h in range(H):
+        assert_close(got["o"][0, h], ref["o"][0, h], TOL_BF16, f"range {mode} o head {h}")
+        assert_close(got["S"][0, h], ref["S"][0, h], TOL_BF16, f"range {mode} S head {h}")
+    # the ordinary chunks after the large ones, on their own scale
+    assert_close(got["o"][0, 0, 192:], ref["o"][0, 0, 192:], TOL_BF16, f"range {mode} o after")
+    if diag:
+        assert_close(got["cov"], ref["cov"], TOL_F32, "range diag p")
+
+
+def test_fp16_range_scores(kdn, orc):
+    """Write scores from the matrix-core path's fp16 residual copies when those
+    residuals are carried scaled (values ~5000)."""
+    import torch
+    inp = workloads.scan_inputs(1, 2, 200, 128, 128, seed=125, dtype="bf16")
+    inp["v"] = workloads.bf16_round(inp["v"] * 5.0e3)
+    q, k, v = (dev_tensor(inp[n], "bf16") for n in ("q", "k", "v"))
+    o, m = kdn.kdn_scan_fwd(q, k, v, alpha=dev_tensor(inp["alpha"]), beta=dev_tensor(inp["beta"]),
+                            m=True)
+    torch.cuda.synchronize()
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"])
+    assert_close(host(m), ref["m"], TOL_BF16, "range scores m")
+    assert_close(host(o), ref["o"], TOL_BF16, "range scores o")
+
+
+def test_fp16_range_tiny_components(kdn, orc):
+    """Key and query components below 2^-14 (fp16 subnormals once staged):
+    keys whose mass sits on a few coordinates with the rest ~1e-6, queries
+    with small entries; the bar relative to RMS(o) holds."""
+    B, H, L, d = 1, 2, 200, 128
+    inp = workloads.scan_inputs(B, H, L, d, d, seed=126, dtype="f32")
+    rng = np.random.Generator(np.random.PCG64(126))
+    k = inp["k"].copy()
+    small = rng.uniform(size=k.shape) < 0.8
+    k[small] *= 1.0e-5
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q = inp["q"].copy()
+    q[rng.uniform(size=q.shape) < 0.5] *= 3.0e-5
+    inp["k"], inp["q"] = workloads.bf16_round(k), workloads.bf16_round(q)
+    inp["v"] = workloads.bf16_round(inp["v"])
+    assert np.sum((np.abs(inp["k"]) < 2.0 ** -14) & (inp["k"] != 0)) > 1000
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"])
+    got = _scan_gpu(kdn, inp, "bf16", 64)
+    assert_close(got["o"], ref["o"], TOL_BF16, "tiny components o")
+    assert_close(got["S"], ref["S"], TOL_BF16, "tiny components S")
 
 
 # --------------------------------------------------------------- full-size workloads
