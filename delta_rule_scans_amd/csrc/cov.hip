@@ -107,25 +107,29 @@ __global__ __launch_bounds__(128) void diag_prefix_kernel(const float* cov_in, f
   }
 }
 
+// Sum over the 64 lanes, every lane gets it (all 64 lanes must be active).
+// DPP only, no trip through the LDS crossbar: the quad, half-row and row sums
+// by lane permutations within each row of 16; then row 1 and row 3 add lane 15
+// of the row before them, rows 2 and 3 add lane 31, and lane 63 holds the total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+  x += dpp_perm<0xB1>(x);   // quad_perm 1,0,3,2
+  x += dpp_perm<0x4E>(x);   // quad_perm 2,3,0,1
+  x += dpp_perm<0x141>(x);  // row_half_mirror
+  x += dpp_perm<0x140>(x);  // row_mirror
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x142, 0xA, 0xF, false));  // row_bcast:15
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
 // One wavefront per (head, chunk): lane l carries coordinates l and l + 64
 // through the chunk's tokens in order; the sum over coordinates in
 // s_t = r_t + sum_i p-_i k_i^2 is a wavefront reduction, so the gains of token
-// t are written as soon as it is done. No LDS and no barriers, so many
-// wavefronts per SIMD hide the memory latency.
-// Sum over the 64 lanes, every lane gets it (all 64 lanes must be active):
-// quad steps by DPP, 4-16 by swizzles within each half, the halves by one
-// lane swap.
-__device__ __forceinline__ float wave_sum64(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));  // ^1
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));  // ^2
-  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (4 << 10)));
-  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (8 << 10)));
-  x += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), 0x1F | (16 << 10)));
-  // after the swap, lanes 0-31 find the upper half's value in the second
-  // result and lanes 32-63 the lower half's in the first
-  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return x + __uint_as_float(__lane_id() < 32 ? sw[1] : sw[0]);
-}
+// t are written as soon as it is done. No LDS and no barriers. (Any d_k and
+// input type; the matrix-core path's shape uses diag_gains_rows_kernel.)
 
 template <typename Tk, typename Tg>
 __global__ __launch_bounds__(256) void diag_gains_kernel(const Tk* k, const float* alpha,
@@ -155,8 +159,8 @@ __global__ __launch_bounds__(256) void diag_gains_kernel(const Tk* k, const floa
       if (ok0) pprev[g * dk + i0] = p0;
       if (ok1) pprev[g * dk + i1] = p1;
     }
-    // reciprocals by v_rcp_f32 (1 ulp): the kernel is bound by its
-    // instruction count, and exact divisions are ten instructions each
+    // reciprocals by v_rcp_f32 (1 ulp): exact divisions are ten instructions
+    // each and sit on the chain from token to token
     const float sd = rt + wave_sum64(fmaf(pk0, k0, pk1 * k1));
     if (sden && lane == 0) sden[g] = sd;
     const float inv = __builtin_amdgcn_rcpf(sd);
@@ -168,6 +172,101 @@ __global__ __launch_bounds__(256) void diag_gains_kernel(const Tk* k, const floa
   if (c == nchunks - 1 && cov_out) {
     if (ok0) cov_out[(size_t)bh * dk + i0] = p0;
     if (ok1) cov_out[(size_t)bh * dk + i1] = p1;
+  }
+}
+
+// The same for bf16 keys, fp16 gains and d_k = 128: four chunks per
+// wavefront, one per row of 16 lanes; lane j of a row carries coordinates
+// 8 j .. 8 j + 7 of its chunk, so keys are read and gains written as 16-byte
+// pieces (a row covers a token's 256-byte key row), and the sum over
+// coordinates is a row reduction. The inputs of 8 tokens are loaded ahead.
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp_perm<0xB1>(x);   // quad_perm 1,0,3,2
+  x += dpp_perm<0x4E>(x);   // quad_perm 2,3,0,1
+  x += dpp_perm<0x141>(x);  // row_half_mirror
+  return x + dpp_perm<0x140>(x);  // row_mirror
+}
+__global__ __launch_bounds__(256) void diag_gains_rows_kernel(const uint16_t* k, const float* alpha,
+                                                              const float* r, float* cov_out,
+                                                              float qvar, const float4* maps,
+                                                              _Float16* gains, int BH, int L,
+                                                              int C, int nchunks, float* pprev,
+                                                              float* sden) {
+  constexpr int DK = 128, NB = 8;
+  const int lane = threadIdx.x & 63, cg = lane & 15;
+  const int nitems = BH * nchunks;
+  const int item0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  const bool live = item0 < nitems;  // rows past the last chunk repeat it and store nothing
+  const int item = live ? item0 : nitems - 1;
+  const int bh = item / nchunks, c = item - bh * nchunks;
+  const int t0 = c * C, n = min(C, L - t0);
+  const size_t tok = (size_t)bh * L + t0;
+  float p[8];  // variances of coordinates 8 cg .. + 8, from the chunk start
+  {
+    const float4* mp = maps + (size_t)item * DK + 8 * cg;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) p[e] = mp[e].x;
+  }
+  for (int tb = 0; tb < C; tb += NB) {
+    // tokens past the chunk read token n - 1 and are not applied
+    uint4 kv[NB];
+    float av[NB], rv[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const size_t g = tok + min(tb + u, n - 1);
+      kv[u] = *reinterpret_cast<const uint4*>(k + g * DK + 8 * cg);
+      av[u] = alpha ? alpha[g] : 1.f;
+      rv[u] = r ? r[g] : 1.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int t = tb + u;
+      const bool in = live && t < n;
+      const size_t g = tok + t;
+      const uint32_t w[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+      float kf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[2 * e] = __uint_as_float(w[e] << 16);
+        kf[2 * e + 1] = __uint_as_float(w[e] & 0xffff0000u);
+      }
+      const float a = av[u], rt = rv[u];
+      const float a2 = a * a, Q = (1.f - a) * (1.f + a) * qvar;
+      float pm[8], pk[8], part = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        pm[e] = fmaf(a2, p[e], Q);
+        pk[e] = pm[e] * kf[e];
+        part = fmaf(pk[e], kf[e], part);
+      }
+      // reciprocals by v_rcp_f32 (1 ulp), as in diag_gains_kernel
+      const float sd = rt + row_sum16(part);
+      const float inv = __builtin_amdgcn_rcpf(sd);
+      if (in) {
+        if (pprev) {  // for the backward: the variances before the token
+          float4* pp = reinterpret_cast<float4*>(pprev + g * DK + 8 * cg);
+          pp[0] = make_float4(p[0], p[1], p[2], p[3]);
+          pp[1] = make_float4(p[4], p[5], p[6], p[7]);
+        }
+        if (sden && cg == 0) sden[g] = sd;
+        uint32_t gh[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          gh[e] = __builtin_bit_cast(
+              uint32_t, __builtin_convertvector(f2v{pk[2 * e] * inv, pk[2 * e + 1] * inv}, h2v));
+        *reinterpret_cast<uint4*>(gains + g * DK + 8 * cg) = make_uint4(gh[0], gh[1], gh[2], gh[3]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        p[e] = in ? pm[e] * rt * __builtin_amdgcn_rcpf(fmaf(pk[e], kf[e], rt)) : p[e];
+    }
+  }
+  if (live && c == nchunks - 1 && cov_out) {
+    float4* co = reinterpret_cast<float4*>(cov_out + (size_t)bh * DK + 8 * cg);
+    co[0] = make_float4(p[0], p[1], p[2], p[3]);
+    co[1] = make_float4(p[4], p[5], p[6], p[7]);
   }
 }
 
@@ -599,6 +698,16 @@ hipError_t diag_typed(const void* k, const float* alpha, const float* r, const f
                      reinterpret_cast<float4*>(maps), BH, dk, nchunks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if constexpr (std::is_same<Tk, uint16_t>::value && std::is_same<Tg, _Float16>::value) {
+    if (dk == 128) {
+      const int waves = (BH * nchunks + 3) / 4;  // four chunks per wavefront
+      hipLaunchKernelGGL(diag_gains_rows_kernel, dim3((waves + 3) / 4), dim3(256), 0, s,
+                         static_cast<const uint16_t*>(k), alpha, r, cov_out, qvar,
+                         reinterpret_cast<const float4*>(maps), static_cast<_Float16*>(gains), BH,
+                         L, C, nchunks, pprev, sden);
+      return hipGetLastError();
+    }
+  }
   const int waves = BH * nchunks;
   hipLaunchKernelGGL((diag_gains_kernel<Tk, Tg>), dim3((waves + 3) / 4), dim3(256), 0, s,
                      static_cast<const Tk*>(k), alpha, r, cov_out, qvar,
