@@ -177,7 +177,7 @@ class HipTimer:
 
 
 def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True, cold=False,
-               keep=False):
+               keep=False, resid="gated"):
     import workloads
     cfg = workloads.WORKLOADS[name]
     B, H, L, dk, dv, C = cfg["B"], cfg["H"], cfg["L"], cfg["dk"], cfg["dv"], cfg["chunk"]
@@ -203,7 +203,7 @@ def bench_scan(kdn, torch, name, steps, warmup, mode="delta", per_phase=True, co
     def step(phase="all"):
         kdn.kdn_scan_fwd(t["q"], t["k"], t["v"], alpha=alpha, beta=beta, r=r, cov_in=cov_in,
                          cov_out=cov_out, q_noise_var=qvar, state_out=s_out, o=o, chunk=C,
-                         mode=mode, workspace=ws, phase=phase)
+                         mode=mode, resid=resid, workspace=ws, phase=phase)
 
     _warm(torch, step, warmup)
     e0, e1 = _events(torch, 2)
@@ -523,8 +523,10 @@ def oracle_leg(kept, name="gated", seconds_target=15.0):
         parity["gated"] = dict(o=_rel(g["o"].reshape(first["o"].shape), first["o"]),
                                S=_rel(g["S"].reshape(first["S"].shape), first["S"]), tol=2e-2)
     del first
-    for key, (wl, mode) in {"kdn_diag/diag": ("kdn_diag", "diag"), "kdn_diag/iso": ("kdn_diag", "iso"),
-                            "long/delta": ("long", "delta")}.items():
+    for key, (wl, mode, resid) in {"kdn_diag/diag": ("kdn_diag", "diag", "gated"),
+                                   "kdn_diag/iso": ("kdn_diag", "iso", "gated"),
+                                   "long/delta": ("long", "delta", "gated"),
+                                   "gated/noerase": ("gated", "delta", "noerase")}.items():
         got = kept.get(key)
         if got is None:
             continue
@@ -533,7 +535,8 @@ def oracle_leg(kept, name="gated", seconds_target=15.0):
         cshape = {"diag": (c["B"], c["H"], c["dk"]), "iso": (c["B"], c["H"])}.get(mode)
         cov0 = np.full(cshape, c.get("cov_init", 1.0), np.float32) if cshape else None
         ref = oracle.scan(x["q"], x["k"], x["v"], alpha=x["alpha"], beta=x["beta"], r=x["r"],
-                          cov0=cov0, q_noise_var=c.get("q_noise_var", 0.0), mode=mode, want_m=False)
+                          cov0=cov0, q_noise_var=c.get("q_noise_var", 0.0), mode=mode,
+                          resid=resid, want_m=False)
         del x
         e = dict(o=_rel(got["o"], ref["o"]), S=_rel(got["S"], ref["S"]), tol=2e-2)
         if cov0 is not None:
@@ -575,14 +578,15 @@ def oracle_leg(kept, name="gated", seconds_target=15.0):
     return baseline, parity
 
 
-def _extra_scan(name, mode):
+def _extra_scan(name, mode, resid="gated"):
     def run(kdn, torch, args, keep=None):
         r = bench_scan(kdn, torch, name, max(2, args.steps // 4), 1, mode=mode, per_phase=True,
-                       keep=keep is not None)
+                       keep=keep is not None, resid=resid)
         nb = scan_bytes(r["B"], r["H"], r["L"], r["dk"], r["dv"],
                         extra_per_token=4 if mode in ("diag", "iso") else 0)
         if keep is not None:
-            keep[f"{name}/{mode}"] = {k: r[k] for k in ("o", "S", "cov") if k in r}
+            keep[f"{name}/{mode if resid == 'gated' else resid}"] = {
+                k: r[k] for k in ("o", "S", "cov") if k in r}
         flops = r["B"] * r["H"] * r["L"] * scan_flops_per_token_head(r["C"], r["dk"], r["dv"])
         return dict(ms_per_step=round(r["ms_per_step"], 5), tokens_per_s=round(r["tokens_per_s"], 1),
                     prepare_ms=round(r["prepare_ms"], 5), state_ms=round(r["state_ms"], 5),
@@ -604,6 +608,8 @@ EXTRAS = {
     "kdn_diag": _extra_scan("kdn_diag", "diag"),
     "kdn_iso": _extra_scan("kdn_diag", "iso"),
     "long": _extra_scan("long", "delta"),
+    # the gated workload's inputs, write without its erase term (decayed linear attention)
+    "noerase": _extra_scan("gated", "delta", resid="noerase"),
 }
 
 

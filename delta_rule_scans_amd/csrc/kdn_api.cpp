@@ -232,9 +232,7 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   a.noerase = resid == KDN_RESID_NOERASE ? 1 : 0;
 
   const bool out_bf16 = out_dtype == KDN_BF16;
-  // the matrix-core kernels carry the erase term; the no-erase write runs on the
-  // float32 path
-  const bool mfma_ok = use_mfma_path(in_dtype, d_k, d_v, chunk) && !a.noerase && aligned16(q) &&
+  const bool mfma_ok = use_mfma_path(in_dtype, d_k, d_v, chunk) && aligned16(q) &&
                        aligned16(k) && aligned16(v) && aligned16(o) &&
                        (gains == nullptr || aligned16(gains));
   kdn::ScoreArgs sc{};

@@ -87,7 +87,7 @@ struct ScanArgs {
   void* o;                // [BH, L, dv]
   int BH, L, dk, dv, chunk;
   int plain;  // 1: plain residual e = v - S^T k (delta only): exclusive decay in A and K S0
-  int noerase = 0;  // 1: e = v (no prediction subtracted; float32 path only)
+  int noerase = 0;  // 1: e = v (no prediction subtracted, delta only)
   // Residuals for the write scores, or null: the float32 path writes per-tile
   // sums of e_t^2 to esq [BH, d_v tiles, L]; the matrix-core path writes the
   // residuals themselves (fp16) to ubuf, see scan_mfma_ubuf_bytes.

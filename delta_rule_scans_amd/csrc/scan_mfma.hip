@@ -13,6 +13,8 @@
 // same form with the exclusive decay g_{t-1} = g_t / alpha_t in the rows of A
 // and in X: A_tl = (k_t . b_l) g_{t-1} / g_l, X = V - diag(g_{t-1}) K S0;
 // every decay ratio stays <= 1, so no factor grows when alpha_t is small.
+// The write without its erase term (e_t = v_t, decayed linear attention) is
+// the same form with no decay at all in the residual: A = 0, T = I, X = V.
 //
 // Two kernels:
 //  * prep_kernel: every chunk independent of the others; a workgroup takes a
@@ -187,7 +189,7 @@ struct PrepArgs {
   const float* alpha;     // [BH, L] or null
   const float* beta;      // [BH, L]
   unsigned char* rec;     // [BH, nchunks] records of rec_bytes(gain)
-  int L, nchunks, plain;
+  int L, nchunks, plain, noerase;
   int cpw;                // consecutive chunks per workgroup
 };
 
@@ -323,7 +325,9 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
         bs = gain ? 1.f : be_in;
       }
       const float lg = wave_prefix(la, lane);
-      const float lgx = a.plain ? lg - la : lg;   // the residual's decay: exclusive for plain
+      // the residual's decay: exclusive for plain, none (g_x = 0: A = 0,
+      // T = I and X = V) for the write without its erase term
+      const float lgx = a.noerase ? -INFINITY : a.plain ? lg - la : lg;
       const float lgn = __shfl(lg, n - 1, 64);
       const float lg31 = __shfl(lg, 31, 64);
       const float lgr = __shfl(lg, (lane & 32) + 15, 64);   // reference of this half
@@ -1487,6 +1491,7 @@ hipError_t launch_tinv_mfma(const ScanArgs& s, void* tbuf, hipStream_t st) {
   pa.L = s.L;
   pa.nchunks = nchunks;
   pa.plain = s.plain;
+  pa.noerase = s.noerase;
   pa.cpw = prep_chunks_per_workgroup(s.BH, nchunks);
   const size_t lds = prep_lds_bytes(gain);
   auto kern = gain ? prep_kernel<true> : prep_kernel<false>;

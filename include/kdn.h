@@ -148,7 +148,7 @@ size_t kdn_scan_workspace_size(int B, int H, int L, int d_k, int d_v, int chunk,
  *            depend on it beyond rounding; L need not be a multiple of it. 128
  *            runs as 64-token chunks (the kernels' largest).
  *  mode      KDN_GAIN_*;  resid  KDN_RESID_* (PLAIN and NOERASE only with
- *            DELTA; NOERASE runs on the float32 path).
+ *            DELTA).
  *  workspace device scratch of at least kdn_scan_workspace_size(...) bytes,
  *            16-byte aligned (may be NULL when that size is 0).
  * Sizes: B, H >= 1; L >= 0 (L = 0 copies state_in to state_out and cov_in to

@@ -616,21 +616,21 @@ def test_fp16_range_tiny_components(kdn, orc):
 
 # --------------------------------------------------------------- full-size workloads
 
-def _full_check(kdn, orc, name, mode="delta"):
+def _full_check(kdn, orc, name, mode="delta", resid="gated"):
     """The named workload at full size, launched as the benchmark launches it,
     against the oracle on every head: o, the final state and (Kalman) the final
     covariance, each to its bar over all heads at once and per head."""
     cfg = workloads.WORKLOADS[name]
     inp = workloads.named_scan_inputs(name)
-    log(f"{name}/{mode}: full-size GPU run")
+    log(f"{name}/{mode}/{resid}: full-size GPU run")
     cshape = {"diag": (cfg["B"], cfg["H"], cfg["dk"]), "iso": (cfg["B"], cfg["H"])}.get(mode)
     cov0 = np.full(cshape, cfg.get("cov_init", 1.0), np.float32) if cshape else None
     got = _scan_gpu(kdn, inp, cfg["dtype"], cfg["chunk"], mode=mode, cov0=cov0,
-                    qvar=cfg.get("q_noise_var", 0.0))
-    log(f"{name}/{mode}: oracle on all {cfg['B'] * cfg['H']} heads")
+                    qvar=cfg.get("q_noise_var", 0.0), resid=resid)
+    log(f"{name}/{mode}/{resid}: oracle on all {cfg['B'] * cfg['H']} heads")
     ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], beta=inp["beta"],
                    r=inp["r"], cov0=cov0, q_noise_var=cfg.get("q_noise_var", 0.0), mode=mode,
-                   want_m=False)
+                   resid=resid, want_m=False)
     assert_close(got["o"], ref["o"], TOL_BF16, f"{name} o (all heads)")
     assert_close(got["S"], ref["S"], TOL_BF16, f"{name} S (all heads)")
     if cov0 is not None:
@@ -643,6 +643,12 @@ def _full_check(kdn, orc, name, mode="delta"):
 
 def test_full_size_gated(kdn, orc):
     _full_check(kdn, orc, "gated")
+
+
+def test_full_size_noerase(kdn, orc):
+    """The gated workload's inputs with the write's erase term dropped (decayed
+    linear attention) on the matrix cores: the same chunk form with A = 0."""
+    _full_check(kdn, orc, "gated", resid="noerase")
 
 
 def test_full_size_kdn_diag(kdn, orc):
