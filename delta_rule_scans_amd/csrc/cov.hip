@@ -15,9 +15,9 @@
 // run of tokens composes into one 2x2 matrix ("Kalman Delta Networks:
 // Uncertainty-aware Associative Memory", abstract, where the variance
 // recursions are identified as Moebius maps). The DIAG path uses that: one pass composes the
-// maps of every chunk in parallel, a short sequential pass over chunks applies
-// them to get every chunk's starting variances, and a third pass recomputes the
-// per-token values of every chunk in parallel.
+// maps of every chunk in parallel, an associative scan over chunks (log depth)
+// turns them into every chunk's starting variances, and a third pass
+// recomputes the per-token values of every chunk in parallel.
 #include <type_traits>
 
 #include "kdn_internal.h"
@@ -82,29 +82,6 @@ __global__ __launch_bounds__(128) void diag_maps_kernel(const Tk* k, const float
     }
   }
   maps[((size_t)bh * nchunks + c) * dk + i] = make_float4(m00, m01, m10, m11);
-}
-
-// One thread per (head, coordinate): the variance at every chunk start, by
-// applying the chunk maps in order; stored over the map's first entry.
-__global__ __launch_bounds__(128) void diag_prefix_kernel(const float* cov_in, float4* maps,
-                                                          int BH, int dk, int nchunks) {
-  const int idx = blockIdx.x * 128 + threadIdx.x;
-  if (idx >= BH * dk) return;
-  const int bh = idx / dk, i = idx - bh * dk;
-  float p = cov_in[idx];
-  float4* m = maps + (size_t)bh * nchunks * dk + i;
-  for (int c0 = 0; c0 < nchunks; c0 += 8) {  // eight maps in flight at a time
-    float4 M[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (c0 + j < nchunks) M[j] = m[(size_t)(c0 + j) * dk];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (c0 + j < nchunks) {
-        m[(size_t)(c0 + j) * dk].x = p;
-        p = fmaf(M[j].x, p, M[j].y) / fmaf(M[j].z, p, M[j].w);
-      }
-  }
 }
 
 // Sum over the 64 lanes, every lane gets it (all 64 lanes must be active).
@@ -424,30 +401,46 @@ have_norms:
   if (lane == 0) maps[(size_t)bh * nchunks + c] = make_float4(tot.a, tot.b, tot.c, tot.d);
 }
 
-// One thread per head: the variance at every chunk start (over the map's
-// first entry).
-__global__ __launch_bounds__(64) void iso_prefix_kernel(const float* cov_in, float4* maps, int BH,
-                                                        int nchunks) {
-  const int bh = blockIdx.x * 64 + threadIdx.x;
-  if (bh >= BH) return;
-  float p = cov_in[bh];
-  float4* m = maps + (size_t)bh * nchunks;
-  for (int c0 = 0; c0 < nchunks; c0 += 8) {  // eight maps in flight at a time
-    float4 M[8];
+// The variance at every chunk start, by an associative scan over chunks: the
+// chunk maps are Moebius maps, which compose associatively ("Kalman Delta
+// Networks: Uncertainty-aware Associative Memory", abstract). One wavefront
+// per sequence -- (head, coordinate) for the diagonal write, head for the
+// isotropic one (dk = 1) -- with lanes as chunks, 64 at a time: an inclusive
+// scan of the maps over the lanes in six doubling steps; each lane's
+// exclusive composite takes the variance carried in from the chunks before to
+// its chunk start, and the last lane's inclusive composite carries it on.
+// Depth: six map products per 64 chunks, against 64 map applications one
+// after the other. The result goes over each map's first entry.
+__global__ __launch_bounds__(256) void prefix_scan_kernel(const float* cov_in, float4* maps,
+                                                          int nseq, int dk, int nchunks) {
+  const int seq = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (seq >= nseq) return;  // whole wavefronts
+  const int bh = seq / dk, i = seq - bh * dk;
+  float p = cov_in[seq];
+  float4* m = maps + (size_t)bh * nchunks * dk + i;
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {
+    const int c = c0 + lane;
+    const bool ok = c < nchunks;
+    Mob M{1.f, 0.f, 0.f, 1.f};  // lanes past the last chunk: the identity
+    if (ok) {
+      const float4 v = m[(size_t)c * dk];
+      M = Mob{v.x, v.y, v.z, v.w};
+    }
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (c0 + j < nchunks) M[j] = m[c0 + j];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (c0 + j < nchunks) {
-        m[c0 + j].x = p;
-        p = fmaf(M[j].x, p, M[j].y) / fmaf(M[j].z, p, M[j].w);
-      }
+    for (int d = 1; d < 64; d <<= 1) M = mob_mul(M, mob_shfl_up(M, d, lane));
+    const Mob X = mob_shfl_up(M, 1, lane);  // maps of the chunks before this one
+    if (ok) m[(size_t)c * dk].x = fmaf(X.a, p, X.b) / fmaf(X.c, p, X.d);
+    const int last = min(63, nchunks - 1 - c0);
+    const float ta = __builtin_amdgcn_readlane(__float_as_int(M.a), last);
+    const float tb = __builtin_amdgcn_readlane(__float_as_int(M.b), last);
+    const float tc = __builtin_amdgcn_readlane(__float_as_int(M.c), last);
+    const float td = __builtin_amdgcn_readlane(__float_as_int(M.d), last);
+    p = fmaf(__int_as_float(ta), p, __int_as_float(tb)) / fmaf(__int_as_float(tc), p, __int_as_float(td));
   }
 }
 
 // One wavefront per (head, chunk), lane t = token t: the variance before the
-// token from the chunk's starting p (iso_prefix_kernel) and an exclusive scan
+// token from the chunk's starting p (prefix_scan_kernel) and an exclusive scan
 // of the token maps, then the write strength beta_t.
 __global__ __launch_bounds__(256) void iso_beta_kernel(const float* alpha, const float* r,
                                                        const float* kk, float* cov_out, float qvar,
@@ -492,7 +485,7 @@ __global__ __launch_bounds__(256) void iso_beta_kernel(const float* alpha, const
 // (pm = a^2 p + Q with p the variance before the token, s the gain's
 // denominator). dp_{t-1} is affine in dp_t with coefficients that do not
 // depend on dp, so, as in the forward, each chunk's tokens compose into one
-// affine map (in parallel), a short pass over chunks carries dp to every chunk
+// affine map (in parallel), a suffix scan over chunks carries dp to every chunk
 // end, and a last pass runs each chunk's tokens in reverse from its carry.
 
 constexpr int kAdjC = 64;  // tokens per adjoint chunk
@@ -532,24 +525,6 @@ __global__ __launch_bounds__(256) void diag_adj_maps_kernel(
   float2* m = amap + ((size_t)bh * nchunks + c) * dk;
   if (ok0) m[i0] = make_float2(A0, C0);
   if (ok1) m[i1] = make_float2(A1, C1);
-}
-
-// One thread per (head, coordinate) (np coordinates per head): dp at every
-// chunk end, from the last chunk back; dp at the start is dL/dp_0.
-__global__ __launch_bounds__(128) void adj_carry_kernel(const float* dcov_out, const float2* amap,
-                                                        float* carry, float* dcov_in, int BH,
-                                                        int np, int nchunks) {
-  const int idx = blockIdx.x * 128 + threadIdx.x;
-  if (idx >= BH * np) return;
-  const int bh = idx / np, i = idx - bh * np;
-  float dp = dcov_out ? dcov_out[idx] : 0.f;
-  for (int c = nchunks - 1; c >= 0; --c) {
-    const size_t o = ((size_t)bh * nchunks + c) * np + i;
-    carry[o] = dp;
-    const float2 m = amap[o];
-    dp = fmaf(m.x, dp, m.y);
-  }
-  if (dcov_in) dcov_in[idx] = dp;
 }
 
 // DIAG, one wavefront per (head, chunk): the chunk's tokens in reverse from the
@@ -611,6 +586,38 @@ __device__ __forceinline__ Aff aff_suffix(Aff m, int lane) {
   }
   return m;
 }
+// dp at every chunk end, from the last chunk back (dp at the start is
+// dL/dp_0), by a suffix scan of the chunks' affine maps: one wavefront per
+// (head, coordinate) (np coordinates per head), lanes as chunks, 64 at a time
+// from the end; each lane applies the composite of the chunks after it to
+// the dp carried in, and lane 0's composite carries it on.
+__global__ __launch_bounds__(256) void adj_carry_kernel(const float* dcov_out, const float2* amap,
+                                                        float* carry, float* dcov_in, int nseq,
+                                                        int np, int nchunks) {
+  const int seq = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (seq >= nseq) return;  // whole wavefronts
+  const int bh = seq / np, i = seq - bh * np;
+  float dp = dcov_out ? dcov_out[seq] : 0.f;
+  for (int hi = nchunks - 1; hi >= 0; hi -= 64) {
+    const int c = hi - 63 + lane;
+    const bool ok = c >= 0;  // lanes before the first chunk: the identity
+    const size_t o = ((size_t)bh * nchunks + (ok ? c : 0)) * np + i;
+    Aff m{1.f, 0.f};
+    if (ok) {
+      const float2 v = amap[o];
+      m = Aff{v.x, v.y};
+    }
+    m = aff_suffix(m, lane);  // this chunk's map after those of the later chunks
+    Aff x{__shfl_down(m.e, 1, 64), __shfl_down(m.c, 1, 64)};
+    if (lane == 63) x = Aff{1.f, 0.f};
+    if (ok) carry[o] = fmaf(x.e, dp, x.c);
+    const float e0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m.e), 0));
+    const float c0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m.c), 0));
+    dp = fmaf(e0, dp, c0);
+  }
+  if (dcov_in) dcov_in[seq] = dp;
+}
+
 struct IsoTok {
   float a, rt, p, pm, s, D, kk, db;
 };
@@ -694,8 +701,8 @@ hipError_t diag_typed(const void* k, const float* alpha, const float* r, const f
                      dk, C, nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(diag_prefix_kernel, dim3((BH * dk + 127) / 128), dim3(128), 0, s, cov_in,
-                     reinterpret_cast<float4*>(maps), BH, dk, nchunks);
+  hipLaunchKernelGGL(prefix_scan_kernel, dim3((BH * dk + 3) / 4), dim3(256), 0, s, cov_in,
+                     reinterpret_cast<float4*>(maps), BH * dk, dk, nchunks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (std::is_same<Tk, uint16_t>::value && std::is_same<Tg, _Float16>::value) {
@@ -759,8 +766,8 @@ hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const
                        reinterpret_cast<float4*>(maps), BH, L, dk, chunk, nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(iso_prefix_kernel, dim3((BH + 63) / 64), dim3(64), 0, s, cov_in,
-                     reinterpret_cast<float4*>(maps), BH, nchunks);
+  hipLaunchKernelGGL(prefix_scan_kernel, dim3((BH + 3) / 4), dim3(256), 0, s, cov_in,
+                     reinterpret_cast<float4*>(maps), BH, 1, nchunks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(iso_beta_kernel, dim3(blocks), dim3(256), 0, s, alpha, r, kk, cov_out,
@@ -787,8 +794,8 @@ hipError_t launch_cov_adjoint(const CovAdjArgs& a, float* scratch, hipStream_t s
                        a.kk, a.pprev, a.dbeta, amap, a.BH, a.L, a.dk, nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(adj_carry_kernel, dim3((a.BH * np + 127) / 128), dim3(128), 0, s, a.dcov_out,
-                     amap, carry, a.dcov_in, a.BH, np, nch);
+  hipLaunchKernelGGL(adj_carry_kernel, dim3((a.BH * np + 3) / 4), dim3(256), 0, s, a.dcov_out,
+                     amap, carry, a.dcov_in, a.BH * np, np, nch);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.diag)

@@ -129,6 +129,13 @@ def test_kalman_backward_shapes(kdn, orc):
     _kalman_case(kdn, orc, 1, 3, 130, 40, 24, "iso", "f32", seed=408)
 
 
+def test_kalman_backward_many_chunks(kdn, orc):
+    """131 adjoint chunks of 64 tokens: the carry of dp over chunks takes them
+    64 at a time from the end, the first block ragged."""
+    _kalman_case(kdn, orc, 1, 1, 64 * 130 + 17, 64, 32, "diag", "f32", seed=410)
+    _kalman_case(kdn, orc, 1, 1, 64 * 130 + 17, 64, 32, "iso", "f32", seed=411)
+
+
 def test_delta_backward_bf16_inputs(kdn, orc):
     """The delta write's gradients from bf16 inputs through kdn_scan_bwd_ex: the
     oracle on the same bf16 values, float32 bar (the backward runs in float32)."""

@@ -339,6 +339,25 @@ def test_iso_kalman_small(kdn, orc, dtype):
         assert_close(got["cov"], ref["cov"], TOL_F32, "iso p")
 
 
+@pytest.mark.parametrize("mode", ["diag", "iso"])
+def test_kalman_prefix_many_chunks(kdn, orc, mode):
+    """More chunks than the prefix scan takes at once (64): 151 chunks of 64 on
+    the matrix cores and 603 of 16 on the float32 path, the last block and the
+    last chunk ragged; o, S and the final variance against the oracle."""
+    B, H, L, d = 1, 2, 9637, 128
+    inp = workloads.scan_inputs(B, H, L, d, d, seed=131, dtype="bf16", with_r=True)
+    p0 = (np.full((B, H, d), 1.0, np.float32) if mode == "diag"
+          else np.array([[0.7, 1.3]], np.float32))
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"], cov0=p0,
+                   q_noise_var=1.0, mode=mode, want_m=False)
+    for chunk in (64, 16):
+        log(f"{mode} prefix scan, L {L} chunk {chunk}")
+        got = _scan_gpu(kdn, inp, "bf16", chunk, mode=mode, cov0=p0, qvar=1.0)
+        assert_close(got["o"], ref["o"], TOL_BF16, f"{mode} o chunk {chunk}")
+        assert_close(got["S"], ref["S"], TOL_BF16, f"{mode} S chunk {chunk}")
+        assert_close(got["cov"], ref["cov"], TOL_F32, f"{mode} p chunk {chunk}")
+
+
 def test_full_kalman_small(kdn, orc):
     inp = workloads.scan_inputs(1, 2, 150, 32, 48, seed=108, dtype="f32", with_r=True)
     rng = np.random.Generator(np.random.PCG64(108))
