@@ -696,19 +696,19 @@ hipError_t diag_typed(const void* k, const float* alpha, const float* r, const f
                       float* cov_out, float qvar, void* gains, float* maps, int BH, int L, int dk,
                       int C, hipStream_t s, float* pprev, float* sden) {
   const int nchunks = (L + C - 1) / C;
-  hipLaunchKernelGGL(diag_maps_kernel<Tk>, dim3(BH, nchunks), dim3(128), 0, s,
+  KDN_LAUNCH(diag_maps_kernel<Tk>, dim3(BH, nchunks), dim3(128), 0, s,
                      static_cast<const Tk*>(k), alpha, r, qvar, reinterpret_cast<float4*>(maps), L,
                      dk, C, nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefix_scan_kernel, dim3((BH * dk + 3) / 4), dim3(256), 0, s, cov_in,
+  KDN_LAUNCH(prefix_scan_kernel, dim3((BH * dk + 3) / 4), dim3(256), 0, s, cov_in,
                      reinterpret_cast<float4*>(maps), BH * dk, dk, nchunks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if constexpr (std::is_same<Tk, uint16_t>::value && std::is_same<Tg, _Float16>::value) {
     if (dk == 128) {
       const int waves = (BH * nchunks + 3) / 4;  // four chunks per wavefront
-      hipLaunchKernelGGL(diag_gains_rows_kernel, dim3((waves + 3) / 4), dim3(256), 0, s,
+      KDN_LAUNCH(diag_gains_rows_kernel, dim3((waves + 3) / 4), dim3(256), 0, s,
                          static_cast<const uint16_t*>(k), alpha, r, cov_out, qvar,
                          reinterpret_cast<const float4*>(maps), static_cast<_Float16*>(gains), BH,
                          L, C, nchunks, pprev, sden);
@@ -716,7 +716,7 @@ hipError_t diag_typed(const void* k, const float* alpha, const float* r, const f
     }
   }
   const int waves = BH * nchunks;
-  hipLaunchKernelGGL((diag_gains_kernel<Tk, Tg>), dim3((waves + 3) / 4), dim3(256), 0, s,
+  KDN_LAUNCH((diag_gains_kernel<Tk, Tg>), dim3((waves + 3) / 4), dim3(256), 0, s,
                      static_cast<const Tk*>(k), alpha, r, cov_out, qvar,
                      reinterpret_cast<const float4*>(maps), static_cast<Tg*>(gains), BH, L, dk, C,
                      nchunks, pprev, sden);
@@ -727,7 +727,7 @@ template <typename Tk, typename Tg>
 hipError_t full_typed(const void* k, const float* alpha, const float* r, const float* cov_in,
                       float* cov_out, float qvar, void* gains, int BH, int L, int dk,
                       hipStream_t s) {
-  hipLaunchKernelGGL((full_gains_kernel<Tk, Tg>), dim3(BH), dim3(256), 0, s,
+  KDN_LAUNCH((full_gains_kernel<Tk, Tg>), dim3(BH), dim3(256), 0, s,
                      static_cast<const Tk*>(k), alpha, r, cov_in, cov_out, qvar,
                      static_cast<Tg*>(gains), L, dk);
   return hipGetLastError();
@@ -757,20 +757,20 @@ hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const
   const int nchunks = (L + chunk - 1) / chunk;
   const int blocks = (BH * nchunks + 3) / 4;  // four wavefronts per workgroup
   if (k_bf16)
-    hipLaunchKernelGGL(iso_maps_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s,
+    KDN_LAUNCH(iso_maps_kernel<uint16_t>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const uint16_t*>(k), alpha, r, q_noise_var, kk,
                        reinterpret_cast<float4*>(maps), BH, L, dk, chunk, nchunks);
   else
-    hipLaunchKernelGGL(iso_maps_kernel<float>, dim3(blocks), dim3(256), 0, s,
+    KDN_LAUNCH(iso_maps_kernel<float>, dim3(blocks), dim3(256), 0, s,
                        static_cast<const float*>(k), alpha, r, q_noise_var, kk,
                        reinterpret_cast<float4*>(maps), BH, L, dk, chunk, nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefix_scan_kernel, dim3((BH + 3) / 4), dim3(256), 0, s, cov_in,
+  KDN_LAUNCH(prefix_scan_kernel, dim3((BH + 3) / 4), dim3(256), 0, s, cov_in,
                      reinterpret_cast<float4*>(maps), BH, 1, nchunks);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(iso_beta_kernel, dim3(blocks), dim3(256), 0, s, alpha, r, kk, cov_out,
+  KDN_LAUNCH(iso_beta_kernel, dim3(blocks), dim3(256), 0, s, alpha, r, kk, cov_out,
                      q_noise_var, reinterpret_cast<const float4*>(maps), beta, BH, L, dk, chunk,
                      nchunks, pprev);
   return hipGetLastError();
@@ -787,23 +787,23 @@ hipError_t launch_cov_adjoint(const CovAdjArgs& a, float* scratch, hipStream_t s
   float* carry = scratch + (size_t)a.BH * nch * np * 2;
   const int blocks = (a.BH * nch + 3) / 4;
   if (a.diag)
-    hipLaunchKernelGGL(diag_adj_maps_kernel, dim3(blocks), dim3(256), 0, s, a.k, a.alpha, a.r,
+    KDN_LAUNCH(diag_adj_maps_kernel, dim3(blocks), dim3(256), 0, s, a.k, a.alpha, a.r,
                        a.qvar, a.pprev, a.sden, a.gains, a.dgain, amap, a.BH, a.L, a.dk, nch);
   else
-    hipLaunchKernelGGL(iso_adj_maps_kernel, dim3(blocks), dim3(256), 0, s, a.alpha, a.r, a.qvar,
+    KDN_LAUNCH(iso_adj_maps_kernel, dim3(blocks), dim3(256), 0, s, a.alpha, a.r, a.qvar,
                        a.kk, a.pprev, a.dbeta, amap, a.BH, a.L, a.dk, nch);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(adj_carry_kernel, dim3((a.BH * np + 3) / 4), dim3(256), 0, s, a.dcov_out,
+  KDN_LAUNCH(adj_carry_kernel, dim3((a.BH * np + 3) / 4), dim3(256), 0, s, a.dcov_out,
                      amap, carry, a.dcov_in, a.BH * np, np, nch);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.diag)
-    hipLaunchKernelGGL(diag_adj_out_kernel, dim3(blocks), dim3(256), 0, s, a.k, a.alpha, a.r,
+    KDN_LAUNCH(diag_adj_out_kernel, dim3(blocks), dim3(256), 0, s, a.k, a.alpha, a.r,
                        a.qvar, a.pprev, a.sden, a.gains, a.dgain, carry, a.dk_out, a.dalpha, a.dr,
                        a.BH, a.L, a.dk, nch);
   else
-    hipLaunchKernelGGL(iso_adj_out_kernel, dim3(blocks), dim3(256), 0, s, a.k, a.alpha, a.r,
+    KDN_LAUNCH(iso_adj_out_kernel, dim3(blocks), dim3(256), 0, s, a.k, a.alpha, a.r,
                        a.qvar, a.kk, a.pprev, a.dbeta, carry, a.dk_out, a.dalpha, a.dr, a.BH, a.L,
                        a.dk, nch);
   return hipGetLastError();

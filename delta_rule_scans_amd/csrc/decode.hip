@@ -191,10 +191,10 @@ hipError_t launch_decode(const float* q, const float* k, const float* v, const f
                          int resid, int score_kind, hipStream_t s) {
   const bool vec = (dv % 4 == 0) && ((reinterpret_cast<uintptr_t>(state) & 15) == 0);
   if (vec)
-    hipLaunchKernelGGL(decode_kernel<true>, dim3(BH), dim3(NT), 0, s, q, k, v, alpha, beta, r, cov,
+    KDN_LAUNCH(decode_kernel<true>, dim3(BH), dim3(NT), 0, s, q, k, v, alpha, beta, r, cov,
                        q_noise_var, state, o, m, dk, dv, gmode, resid, score_kind);
   else
-    hipLaunchKernelGGL(decode_kernel<false>, dim3(BH), dim3(NT), 0, s, q, k, v, alpha, beta, r,
+    KDN_LAUNCH(decode_kernel<false>, dim3(BH), dim3(NT), 0, s, q, k, v, alpha, beta, r,
                        cov, q_noise_var, state, o, m, dk, dv, gmode, resid, score_kind);
   return hipGetLastError();
 }

@@ -206,11 +206,11 @@ hipError_t launch_hola(const float* q, const float* k, const float* v, const flo
                    ((reinterpret_cast<uintptr_t>(cache_k) | reinterpret_cast<uintptr_t>(cache_v)) &
                     15) == 0;
   if (vec)
-    hipLaunchKernelGGL(hola_kernel<true>, dim3(B * H), dim3(NT), 0, s, q, k, v, m, t, cache_k,
+    KDN_LAUNCH(hola_kernel<true>, dim3(B * H), dim3(NT), 0, s, q, k, v, m, t, cache_k,
                        cache_v, cache_m, cache_pos, cache_count, sink_logit, o_cache, rms_eps, H, dk,
                        dv, w, policy);
   else
-    hipLaunchKernelGGL(hola_kernel<false>, dim3(B * H), dim3(NT), 0, s, q, k, v, m, t, cache_k,
+    KDN_LAUNCH(hola_kernel<false>, dim3(B * H), dim3(NT), 0, s, q, k, v, m, t, cache_k,
                        cache_v, cache_m, cache_pos, cache_count, sink_logit, o_cache, rms_eps, H,
                        dk, dv, w, policy);
   return hipGetLastError();

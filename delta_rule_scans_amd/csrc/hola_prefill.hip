@@ -480,24 +480,24 @@ template <typename Tin>
 hipError_t prefill_typed(const PrefillArgs& a, hipStream_t s) {
   const int nblk = (a.L + a.block - 1) / a.block;
   if (a.w > kMaxW || a.block > kMaxBlock || a.w > NT) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(block_top_kernel, dim3(a.BH, nblk), dim3(NT), 0, s, a);
+  KDN_LAUNCH(block_top_kernel, dim3(a.BH, nblk), dim3(NT), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.BH), dim3(NT), 0, s, a);
+  KDN_LAUNCH(merge_kernel, dim3(a.BH), dim3(NT), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const size_t read_lds = (size_t)(2 * KT * LDR + QT * LDP) * sizeof(float);
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(read_kernel<Tin>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)read_lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(read_kernel<Tin>, dim3(a.BH, nblk, (a.block + QT - 1) / QT), dim3(NT),
+  KDN_LAUNCH(read_kernel<Tin>, dim3(a.BH, nblk, (a.block + QT - 1) / QT), dim3(NT),
                      read_lds, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(commit_gather_kernel<Tin>, dim3(a.BH, a.w), dim3(64), 0, s, a);
+  KDN_LAUNCH(commit_gather_kernel<Tin>, dim3(a.BH, a.w), dim3(64), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(commit_scatter_kernel, dim3(a.BH, a.w), dim3(64), 0, s, a);
+  KDN_LAUNCH(commit_scatter_kernel, dim3(a.BH, a.w), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

@@ -6,11 +6,43 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdarg>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "kdn_internal.h"
 
 #define KDN_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace kdn {
+
+bool trace_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("KDN_TRACE");
+    return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+  }();
+  return on;
+}
+
+void trace_launch(const char* kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s) {
+  std::fprintf(stderr, "kdn: launch %s grid (%u,%u,%u) block (%u,%u,%u) lds %zu stream %p\n",
+               kernel, grid.x, grid.y, grid.z, block.x, block.y, block.z, lds,
+               static_cast<void*>(s));
+}
+
+void trace_call(const char* fmt, ...) {
+  if (!trace_enabled()) return;
+  std::va_list ap;
+  va_start(ap, fmt);
+  std::fputs("kdn: ", stderr);
+  std::vfprintf(stderr, fmt, ap);
+  std::fputc('\n', stderr);
+  va_end(ap);
+}
+
+}  // namespace kdn
 
 namespace {
 
@@ -235,6 +267,9 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   const bool mfma_ok = use_mfma_path(in_dtype, d_k, d_v, chunk) && aligned16(q) &&
                        aligned16(k) && aligned16(v) && aligned16(o) &&
                        (gains == nullptr || aligned16(gains));
+  kdn::trace_call("kdn_scan_fwd phase %d B %d H %d L %d d_k %d d_v %d chunk %d mode %d resid %d "
+                  "in %s -> %s path", phase, B, H, L, d_k, d_v, chunk, mode, resid,
+                  in_bf16 ? "bf16" : "f32", mfma_ok ? "matrix-core" : "float32");
   kdn::ScoreArgs sc{};
   if (m) {
     void* sbuf = static_cast<char*>(workspace) + ws.s_off;

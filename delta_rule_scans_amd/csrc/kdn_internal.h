@@ -8,6 +8,20 @@
 
 namespace kdn {
 
+// Launch tracing: with KDN_TRACE=1 in the environment every kernel launch is
+// written to stderr (kernel, grid, workgroup, LDS bytes, stream) as it is
+// enqueued; otherwise the cost is one test of a cached flag.
+bool trace_enabled();
+void trace_launch(const char* kernel, dim3 grid, dim3 block, size_t lds, hipStream_t s);
+void trace_call(const char* fmt, ...);
+#define KDN_LAUNCH_NAMED(name, kernel, grid, block, lds, stream, ...)                          \
+  do {                                                                                        \
+    if (::kdn::trace_enabled()) ::kdn::trace_launch(name, dim3(grid), dim3(block), (lds), (stream)); \
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, __VA_ARGS__);                        \
+  } while (0)
+#define KDN_LAUNCH(kernel, grid, block, lds, stream, ...) \
+  KDN_LAUNCH_NAMED(#kernel, kernel, grid, block, lds, stream, __VA_ARGS__)
+
 // ---------------------------------------------------------------- bf16 helpers
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);

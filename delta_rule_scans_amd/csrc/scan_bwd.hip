@@ -855,11 +855,12 @@ BwdPlan plan_bwd(int BH, int L, int dk, int dv) {
 }
 
 template <typename K>
-hipError_t launch_lds(K kern, dim3 grid, int threads, size_t lds, const BwdArgs& a, hipStream_t s) {
+hipError_t launch_lds(const char* name, K kern, dim3 grid, int threads, size_t lds, const BwdArgs& a,
+                      hipStream_t s) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(threads), lds, s, a);
+  KDN_LAUNCH_NAMED(name, kern, grid, dim3(threads), lds, s, a);
   return hipGetLastError();
 }
 
@@ -880,20 +881,23 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
   const size_t f = sizeof(float);
   hipError_t e;
   const int ng = a.gain ? 1 : 0;  // gain mode: one more [C][d_k] tile per kernel
-  e = launch_lds(bwd_prep_kernel, dim3(a.BH, nch), NT, ((2 + ng) * C * (DP + 1) + 3 * C) * f, a, s);
+  e = launch_lds("bwd_prep_kernel", bwd_prep_kernel, dim3(a.BH, nch), NT,
+                 ((2 + ng) * C * (DP + 1) + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
-  e = launch_lds(bwd_fwd_kernel, dim3(a.BH, ntw), NTC,
+  e = launch_lds("bwd_fwd_kernel", bwd_fwd_kernel, dim3(a.BH, ntw), NTC,
                  ((1 + ng) * C * LKC + C * LCC + DP * LOC + 2 * C * LOC + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
-  e = launch_lds(bwd_rev_kernel, dim3(a.BH, ntw), NTC,
+  e = launch_lds("bwd_rev_kernel", bwd_rev_kernel, dim3(a.BH, ntw), NTC,
                  (2 * C * LKC + 2 * C * LCC + DP * LOC + 3 * C * LOC + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
   const size_t lds_c = (2 * C * (VW + 1) + DP * (VW + 1) + NT / 64) * f;
-  e = launch_lds(bwd_contract_kernel<false>, dim3(a.BH, nch, 2), NT, lds_c, a, s);
+  e = launch_lds("bwd_contract_kernel<false>", bwd_contract_kernel<false>, dim3(a.BH, nch, 2), NT,
+                 lds_c, a, s);
   if (e != hipSuccess) return e;
-  e = launch_lds(bwd_contract_kernel<true>, dim3(a.BH, nch), NT, lds_c, a, s);
+  e = launch_lds("bwd_contract_kernel<true>", bwd_contract_kernel<true>, dim3(a.BH, nch), NT, lds_c,
+                 a, s);
   if (e != hipSuccess) return e;
-  return launch_lds(bwd_grad_kernel, dim3(a.BH, nch), NT,
+  return launch_lds("bwd_grad_kernel", bwd_grad_kernel, dim3(a.BH, nch), NT,
                     ((2 + ng) * C * (DP + 1) + 2 * C * (C + 1) + 3 * C + 6 * C + (NT / 64) * C) * f,
                     a, s);
 }

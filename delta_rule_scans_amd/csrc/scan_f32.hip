@@ -215,7 +215,7 @@ hipError_t launch_typed(const ScanArgs& a, hipStream_t s) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)p.lds);
   if (e != hipSuccess) return e;
   dim3 grid(a.BH, (a.dv + p.dvt - 1) / p.dvt);
-  hipLaunchKernelGGL(kern, grid, dim3(NT), p.lds, s, a, p.dvt);
+  KDN_LAUNCH_NAMED("scan_f32_kernel", kern, grid, dim3(NT), p.lds, s, a, p.dvt);
   return hipGetLastError();
 }
 
@@ -254,7 +254,7 @@ hipError_t launch_bf16_to_f32(const uint16_t* src, float* dst, size_t n, hipStre
   if (n == 0) return hipSuccess;
   size_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(bf16_to_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+  KDN_LAUNCH(bf16_to_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
   return hipGetLastError();
 }
 
@@ -262,7 +262,7 @@ hipError_t launch_copy_f32(const float* src, float* dst, size_t n, hipStream_t s
   if (n == 0 || dst == nullptr) return hipSuccess;
   size_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
-  hipLaunchKernelGGL(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+  KDN_LAUNCH(copy_f32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
   return hipGetLastError();
 }
 

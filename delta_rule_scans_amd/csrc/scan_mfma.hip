@@ -1498,7 +1498,8 @@ hipError_t launch_tinv_mfma(const ScanArgs& s, void* tbuf, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(s.BH, (nchunks + pa.cpw - 1) / pa.cpw), dim3(NT), lds, st, pa);
+  KDN_LAUNCH_NAMED(gain ? "prep_kernel<true>" : "prep_kernel<false>", kern,
+                   dim3(s.BH, (nchunks + pa.cpw - 1) / pa.cpw), dim3(NT), lds, st, pa);
   return hipGetLastError();
 }
 
@@ -1509,7 +1510,9 @@ hipError_t launch_state_typed(const StateArgs& sa, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(sa.BH * sa.ntiles), dim3(NT_STATE), lds, st, sa);
+  KDN_LAUNCH_NAMED(GAIN ? (OBF16 ? "state_kernel<true, true>" : "state_kernel<true, false>")
+                        : (OBF16 ? "state_kernel<false, true>" : "state_kernel<false, false>"),
+                   kern, dim3(sa.BH * sa.ntiles), dim3(NT_STATE), lds, st, sa);
   return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ __global__ __launch_bounds__(64) void scores_kernel(ScoreArgs a) {
 
 hipError_t launch_scores(const ScoreArgs& a, hipStream_t s) {
   const int nblk = (a.L + 63) / 64;
-  hipLaunchKernelGGL(scores_kernel, dim3(a.BH, nblk), dim3(64), 0, s, a);
+  KDN_LAUNCH(scores_kernel, dim3(a.BH, nblk), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 
