@@ -63,6 +63,8 @@
 // column, which is written either as [n][m] (one 8-byte write) or [m][n]
 // (four 2-byte writes). Every buffer below is laid out for its reader.
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 #include <utility>
 
 #include "kdn_internal.h"
@@ -886,7 +888,7 @@ __device__ __forceinline__ half8 q_operand(uint4 raw) {
   return cat(bf16x4_to_f16x4(make_uint2(d0[0], d1[0])), bf16x4_to_f16x4(make_uint2(d0[1], d1[1])));
 }
 
-template <bool GAIN, bool OBF16>
+template <bool GAIN, bool OBF16, bool NARROW>
 __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   constexpr int NCH = n_chain_stages(GAIN);
@@ -908,9 +910,15 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
       tile = id % a.ntiles;
     }
   }
-  const int j0 = tile * DV;
+  const int j0 = tile * (NARROW ? 16 : DV);
   const int last = a.nchunks - 1;
   const int nsteps = (a.nchunks + 2) & ~1;  // chunks + 1 (output lag), even
+  if constexpr (NARROW) {
+    // the exchange's columns 16-31 and its second exponent are never written
+    // by the narrow chain: zero them once (the roles' first barrier orders it)
+    uint4* ex0 = reinterpret_cast<uint4*>(exch_at<GAIN>(lds_raw, 0));
+    for (int i = tid; i < (int)(2 * kExBytes / 16); i += NT_STATE) ex0[i] = make_uint4(0, 0, 0, 0);
+  }
   const unsigned char* rec_head = a.rec + (size_t)bh * a.nchunks * rec_bytes(GAIN);
   const size_t head_tok = (size_t)bh * a.L;
 
@@ -1189,11 +1197,13 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
               const auto hi = __builtin_amdgcn_permlane32_swap(pk[pr].y, pk[pr + 2].y, false, false);
               const uint4 w4 = make_uint4(lo[0], hi[0], lo[1], hi[1]);
               const int off = (tok * a.dv + 8 * (pr + 2 * h)) * esz;
-              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w4), ro, off, 0, kStreamStore);
+              // (a narrow slice holds columns 0-15 only: lanes h = 1 store nothing)
+              if (!NARROW || h == 0)
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w4), ro, off, 0, kStreamStore);
             }
           } else {
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
+            for (int q4 = 0; q4 < (NARROW ? 2 : 4); ++q4) {
               const int off = (tok * a.dv + 8 * q4 + 4 * h) * esz;
               const uint4 w4 = make_uint4(__float_as_uint(o[tb][4 * q4]), __float_as_uint(o[tb][4 * q4 + 1]),
                                           __float_as_uint(o[tb][4 * q4 + 2]), __float_as_uint(o[tb][4 * q4 + 3]));
@@ -1214,6 +1224,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
     return;
   }
 
+  if constexpr (!NARROW) {
   // -------------------------------------------------------------- chain
   floatx16 S[4];  // S[b] register j: d_k row 32 b + 8 (j / 4) + 4 h + j % 4, column c32
 #pragma unroll
@@ -1444,6 +1455,227 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
         a.state_out[((size_t)bh * DK + d) * a.dv + j0 + c32] = S[b][j] * f;
       }
   }
+  } else {
+  // ------------------------------------------------- chain, 16 columns
+  // The narrow slice (16 columns j0 .. j0 + 16) on 16 x 16 x 32 products. A lane holds column n16 and rows
+  // 4 q4 .. + 4 of every 16-row result tile; an operand gives it row (or
+  // column) n16 and k positions 8 q4 .. + 8. Over a 32-wide k block, k
+  // position 8 q + j stands for row 4 q + j (j < 4) or 16 + 4 q + j - 4
+  // (j >= 4) of the block, so that the two result tiles of a block, side by
+  // side, are the operand as they are; the other operand reads its rows in
+  // the same order (two 8-byte reads, or two transposed reads).
+  constexpr int ci = 0;
+  const int n16 = lane & 15, q4 = lane >> 4;
+  const int col = j0 + 16 * ci + n16;
+  floatx4 S[8];  // S[i][r]: d_k row 16 i + 4 q4 + r, column col
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S[i][r] = a.state_in ? a.state_in[((size_t)bh * DK + 16 * i + 4 * q4 + r) * a.dv + col] : 0.f;
+  auto cvt4 = [](const floatx4& x) -> half4 {
+    return __builtin_bit_cast(half4, make_uint2(pk_f16(x[0], x[1]), pk_f16(x[2], x[3])));
+  };
+  // The state is carried as S * 2^eS (see "Range" at the top). The state
+  // entering each chunk is checked while the chunk runs (largest |S 2^eS|, a
+  // NaN propagating: its column is NaN from then on); at the next chunk start
+  // a check that reached 2^11, or one below 2^5 with eS < 0, has the exponent
+  // recomputed from the state at hand.
+  auto absmax8 = [&](float m, int i) {   // m and the 8 entries of tiles i, i + 1
+    m = max3_nan(m, fabsf(S[i][0]), fabsf(S[i][1]));
+    m = max3_nan(m, fabsf(S[i][2]), fabsf(S[i][3]));
+    m = max3_nan(m, fabsf(S[i + 1][0]), fabsf(S[i + 1][1]));
+    return max3_nan(m, fabsf(S[i + 1][2]), fabsf(S[i + 1][3]));
+  };
+  int eS = 0;
+  // eS that brings the largest finite |S| into [2^9, 2^10), or 0 if it is below 2^11
+  auto rescale_state = [&]() {
+    float f = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) f = fabsf(S[i][r]) < INFINITY ? fmaxf(f, fabsf(S[i][r])) : f;
+    const uint32_t mb = __builtin_amdgcn_readfirstlane(wave_max_u32(__float_as_uint(f)));
+    const int Et = (int)(mb >> 23) - 127 - eS;  // exponent of the largest true |S|
+    const int e = Et >= 11 ? max(9 - Et, -120) : 0;
+    if (e != eS) {
+      const float sc = pow2i(e - eS);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) S[i] = S[i] * sc;
+      eS = e;
+    }
+  };
+  bool s_chk;  // the last check asks for a recomputed exponent
+  {
+    float smax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) smax = absmax8(smax, i);
+    s_chk = __ballot(smax >= 2048.f) != 0;
+  }
+  __syncthreads();
+
+  // One step is 38 products issued back to back, one per "slot"; the
+  // conversions between them and the LDS reads are placed under earlier
+  // products:
+  //   slots  0-15  K S, token tile slot / 4, k block slot % 4
+  //   slots 16-21  U = T X (tiles 0, 1 from X block 0; 2, 3 from blocks 0, 1)
+  //   slots 22-37  S += B^T w U, state tile (slot - 22) % 8, token block (slot - 22) / 8
+  constexpr int KA = 6;   // K operands read this many products ahead
+  constexpr int BA = 6;   // transposed write vectors likewise
+  int cs_cur = 0;  // chain stage of chunk c
+  for (int c = 0; c < nsteps; ++c) {
+    __builtin_amdgcn_sched_barrier(0);
+    if (c <= last) {
+      const ChainStage st = chain_stage<GAIN>(lds_raw, cs_cur);
+      half8* ex = exch_at<GAIN>(lds_raw, c & 1);
+      const int n = min(C, a.L - c * C);
+      half8 s16[4], ka[16], x16[2], uw16[2], ta[6], bt[16];
+      half4 vv[4], xt[4], uwt[4];
+      float4 gg[4], ww[4];
+      floatx4 ks[4] = {floatx4{}, floatx4{}, floatx4{}, floatx4{}};
+      floatx4 u[4] = {floatx4{}, floatx4{}, floatx4{}, floatx4{}};
+      // product i of K S: token tile i / 4, k block i % 4
+      auto k_op = [&](int i) -> half8 {
+        const _Float16* p = st.k + (16 * (i >> 2) + n16) * KP + 32 * (i & 3) + 4 * q4;
+        return cat(ld4(p), ld4(p + 16));
+      };
+      // The output wavefront reads S and U as 32 x 32 operands: k step s,
+      // lane c32 + 32 h, elements 4 p + r for row 16 s + 8 p + 4 h + r. Tile s
+      // of this wavefront goes there as 8-byte pieces.
+      auto ex_put = [&](int s, half4 v) {
+        reinterpret_cast<half4*>(ex + s * 64 + 16 * ci + n16 + 32 * (q4 & 1))[q4 >> 1] = v;
+      };
+      auto s_to_f16 = [&](int kb) {
+        const half4 h0 = cvt4(S[2 * kb]), h1 = cvt4(S[2 * kb + 1]);
+        s16[kb] = cat(h0, h1);
+        ex_put(2 * kb, h0);
+        ex_put(2 * kb + 1, h1);
+      };
+      // X = V - g K S of token tile t
+      auto x_tile = [&](int t) {
+        const float gv[4] = {gg[t].x, gg[t].y, gg[t].z, gg[t].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) xt[t][r] = (_Float16)fmaf(-gv[r], ks[t][r], (float)vv[t][r]);
+      };
+      // U of token tile t: to the exchange, and w U as the update's operand
+      auto u_tile = [&](int t) {
+        ex_put(8 + t, cvt4(u[t]));
+        const float wv[4] = {ww[t].x, ww[t].y, ww[t].z, ww[t].w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) uwt[t][r] = (_Float16)(u[t][r] * wv[r]);
+      };
+      // T operand of U tile t, token block kb
+      auto t_op = [&](int t, int kb) -> half8 {
+        const _Float16* p = st.t + (16 * t + n16) * CP + 32 * kb + 4 * q4;
+        return cat(ld4(p), ld4(p + 16));
+      };
+      // transposed write vectors for product q of the update: state tile
+      // q % 8, token block q / 8
+      auto bt_read = [&](int q) {
+        const int i = q & 7, kb = q >> 3;
+        const _Float16* p = st.b + (32 * kb + 4 * q4 + (n16 >> 2)) * KP + 16 * i + 4 * (n16 & 3);
+        bt[q] = cat(ld_tr(p), ld_tr(p + 16 * KP));
+      };
+      constexpr int tt_[6] = {0, 1, 2, 3, 2, 3}, tk_[6] = {0, 0, 0, 0, 1, 1};
+      float smax = 0.f;  // largest |S 2^eS| entering this chunk
+
+      // the chunk's exponent: the state's, recomputed if the last check asked,
+      // and no higher than the staging exponents of the chunk's values, so
+      // that |V 2^eS| < 2^12; this wavefront's columns of rows staged at a
+      // higher exponent are scaled down in place
+      const int vE0 = st.vexp[0], vE1 = st.vexp[1];
+      if (s_chk) rescale_state();
+#pragma unroll
+      for (int i = 0; i < KA; ++i) ka[i] = k_op(i);
+      s_to_f16(0);
+      s_to_f16(1);
+      {
+        const int p0 = value_shift(__builtin_amdgcn_readfirstlane(vE0));
+        const int p1 = value_shift(__builtin_amdgcn_readfirstlane(vE1));
+        const int e = min(eS, min(p0, p1));
+        if (e != eS || p0 != e || p1 != e) {
+          if (e != eS) {
+            const float sc = pow2i(e - eS);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) S[i] = S[i] * sc;
+            eS = e;
+            s_to_f16(0);
+            s_to_f16(1);
+          }
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk) {
+            const int p = blk ? p1 : p0;
+            if (p != e) {
+              const float sc = pow2i(e - p);
+              half8* vp = reinterpret_cast<half8*>(st.v + (32 * blk + (lane >> 1)) * VP + 16 * ci + 8 * (lane & 1));
+              half8 v = *vp;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) v[j] = (_Float16)((float)v[j] * sc);
+              *vp = v;
+            }
+          }
+        }
+        if (lane == 0) reinterpret_cast<int*>(ex + 12 * 64)[ci] = eS;
+      }
+      const float gn = st.go[n - 1];   // the state carries the inclusive decay g_n
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<38>([&](auto slot_c) {
+        constexpr int slot = decltype(slot_c)::value;
+        // ---- the product
+        if constexpr (slot < 16) {
+          ks[slot >> 2] = mfma(ka[slot], s16[slot & 3], ks[slot >> 2]);
+        } else if constexpr (slot < 22) {
+          constexpr int j = slot - 16;
+          u[tt_[j]] = mfma(ta[j], x16[tk_[j]], u[tt_[j]]);
+        } else {
+          constexpr int q = slot - 22, i = q & 7, kb = q >> 3;
+          S[i] = mfma(bt[q], uw16[kb], S[i]);
+        }
+        // ---- work placed under it
+        if constexpr (slot + KA < 16) ka[slot + KA] = k_op(slot + KA);
+        if constexpr (slot == 0) s_to_f16(2);
+        if constexpr (slot == 1) s_to_f16(3);
+        if constexpr (slot >= 1 && slot <= 4) {
+          constexpr int t = slot - 1;
+          vv[t] = ld_tr(st.v + (16 * t + 4 * q4 + (n16 >> 2)) * VP + 16 * ci + 4 * (n16 & 3));
+          gg[t] = *reinterpret_cast<const float4*>(st.g + 16 * t + 4 * q4);
+        }
+        // the state entering the chunk, checked once converted
+        if constexpr (slot >= 3 && slot <= 6) smax = absmax8(smax, 2 * (slot - 3));
+        if constexpr (slot == 6) {
+          const bool hi = __ballot(smax >= 2048.f) != 0, lo = __ballot(smax >= 32.f) == 0;
+          s_chk = hi | (lo & (eS < 0));
+        }
+        if constexpr (slot >= 7 && slot <= 14) S[slot - 7] = S[slot - 7] * gn;
+        if constexpr (slot == 5 || slot == 9 || slot == 13 || slot == 17) x_tile((slot - 5) / 4);
+        if constexpr (slot == 9) x16[0] = cat(xt[0], xt[1]);
+        if constexpr (slot == 17) x16[1] = cat(xt[2], xt[3]);
+        if constexpr (slot >= 8 && slot <= 13) ta[slot - 8] = t_op(tt_[slot - 8], tk_[slot - 8]);
+        if constexpr (slot >= 12 && slot <= 15) {
+          constexpr int t = slot - 12;
+          ww[t] = *reinterpret_cast<const float4*>(st.w + 16 * t + 4 * q4);
+        }
+        if constexpr (slot >= 22 - BA && slot - (22 - BA) < 16) bt_read(slot - (22 - BA));
+        if constexpr (slot == 18) u_tile(0);
+        if constexpr (slot == 19) { u_tile(1); uw16[0] = cat(uwt[0], uwt[1]); }
+        if constexpr (slot == 23) u_tile(2);
+        if constexpr (slot == 24) { u_tile(3); uw16[1] = cat(uwt[2], uwt[3]); }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    }
+    cs_cur = cs_cur + 1 == NCH ? 0 : cs_cur + 1;
+    __syncthreads();
+  }
+
+  if (a.state_out) {
+    const float f = pow2i(-eS);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        a.state_out[((size_t)bh * DK + 16 * i + 4 * q4 + r) * a.dv + col] = S[i][r] * f;
+  }
+  }
 }
 
 }  // namespace
@@ -1503,17 +1735,33 @@ hipError_t launch_tinv_mfma(const ScanArgs& s, void* tbuf, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool GAIN, bool OBF16>
+template <bool GAIN, bool OBF16, bool NARROW>
 hipError_t launch_state_typed(const StateArgs& sa, hipStream_t st) {
   const size_t lds = state_lds_bytes(GAIN);
-  auto kern = state_kernel<GAIN, OBF16>;
+  auto kern = state_kernel<GAIN, OBF16, NARROW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   KDN_LAUNCH_NAMED(GAIN ? (OBF16 ? "state_kernel<true, true>" : "state_kernel<true, false>")
-                        : (OBF16 ? "state_kernel<false, true>" : "state_kernel<false, false>"),
+                   : NARROW ? (OBF16 ? "state_kernel<false, true> (16 columns)"
+                                     : "state_kernel<false, false> (16 columns)")
+                            : (OBF16 ? "state_kernel<false, true>" : "state_kernel<false, false>"),
                    kern, dim3(sa.BH * sa.ntiles), dim3(NT_STATE), lds, st, sa);
   return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device index).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
 }
 
 hipError_t launch_state_mfma(const ScanArgs& s, bool out_bf16, const void* tbuf, hipStream_t st) {
@@ -1530,12 +1778,29 @@ hipError_t launch_state_mfma(const ScanArgs& s, bool out_bf16, const void* tbuf,
   sa.L = s.L;
   sa.dv = s.dv;
   sa.nchunks = (s.L + C - 1) / C;
-  sa.ntiles = s.dv / DV;
   sa.ubuf = static_cast<half8*>(s.ubuf);
   sa.uexp = s.ubuf ? const_cast<int*>(scan_mfma_ubuf_exps(s.ubuf, s.BH, s.L, s.dv)) : nullptr;
-  if (s.gain)
-    return out_bf16 ? launch_state_typed<true, true>(sa, st) : launch_state_typed<true, false>(sa, st);
-  return out_bf16 ? launch_state_typed<false, true>(sa, st) : launch_state_typed<false, false>(sa, st);
+  if (s.gain) {
+    sa.ntiles = s.dv / DV;
+    return out_bf16 ? launch_state_typed<true, true, false>(sa, st)
+                    : launch_state_typed<true, false, false>(sa, st);
+  }
+  // One workgroup fills a compute unit. When 32-column slices would leave
+  // half of them idle, the delta write takes 16-column slices: twice the
+  // workgroups, each with half the chain (its residuals are not kept for
+  // the write scores, which take the 32-column slices).
+  // KDN_STATE_COLS=16 or 32 in the environment forces either.
+  bool narrow = s.ubuf == nullptr && (long long)s.BH * (s.dv / DV) * 2 <= device_cus();
+  if (const char* f = std::getenv("KDN_STATE_COLS")) {
+    if (std::strcmp(f, "16") == 0) narrow = s.ubuf == nullptr;
+    else if (std::strcmp(f, "32") == 0) narrow = false;
+  }
+  sa.ntiles = s.dv / (narrow ? 16 : DV);
+  if (narrow)
+    return out_bf16 ? launch_state_typed<false, true, true>(sa, st)
+                    : launch_state_typed<false, false, true>(sa, st);
+  return out_bf16 ? launch_state_typed<false, true, false>(sa, st)
+                  : launch_state_typed<false, false, false>(sa, st);
 }
 
 }  // namespace kdn

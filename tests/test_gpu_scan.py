@@ -681,3 +681,21 @@ def test_full_size_kdn_iso(kdn, orc):
 
 def test_full_size_long(kdn, orc):
     _full_check(kdn, orc, "long")
+
+
+@pytest.mark.parametrize("cols", ["16", "32"])
+def test_state_tilings(kdn, orc, cols, monkeypatch):
+    """The delta write's two state-kernel tilings -- 32-column slices, and the
+    16-column slices taken when the heads are too few to fill the device --
+    each forced in turn through KDN_STATE_COLS, on the cases that reach every
+    branch of the chain (initial state, bf16 output, plain and no-erase
+    residuals, short and ragged lengths, extreme decay, the fp16 range)."""
+    monkeypatch.setenv("KDN_STATE_COLS", cols)
+    log(f"state tiling: {cols}-column slices")
+    test_gated_delta_small(kdn, orc, "bf16")
+    test_plain_residual(kdn, orc, "bf16")
+    test_noerase_write(kdn, orc, "bf16")
+    test_short_sequences(kdn, orc)
+    test_extreme_decay(kdn, orc, "delta", "gated", "bf16")
+    test_fp16_range_large_values(kdn, orc, "delta")
+    test_fp16_range_tiny_components(kdn, orc)
