@@ -420,7 +420,10 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
   }
 }
 
-// reverse chain: state gradients at chunk ends, dR (= dV), dS0
+// reverse chain: state gradients at chunk ends, dR (= dV), dS0. GAIN is a
+// template switch: a gain tile held in registers by every instantiation would
+// push the delta-write chain past its register budget into scratch.
+template <bool GAIN>
 __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float lds[];
   float* sK = lds;              // [C][LKC]
@@ -436,7 +439,8 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
   float* sAl = sB + C;
   const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
   const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C, dk64 = dk <= 64 ? 64 : DP;
-  const bool erase = a.resid != 2, gain = a.gain != nullptr;
+  const bool erase = a.resid != 2;
+  constexpr bool gain = GAIN;
   const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
   const int m0 = 16 * (w >> 1), n0 = 16 * (w & 1);
   floatx4 G[2];
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
     const int n = min(C, L - c * C);
     const size_t tok = (size_t)bh * L + (size_t)c * C;
     fetch_rows<NTC>(fk, a.k + tok * dk, n, dk);
-    if (gain) fetch_rows<NTC>(fg, a.gain + tok * dk, n, dk);
+    if constexpr (GAIN) fetch_rows<NTC>(fg, a.gain + tok * dk, n, dk);
     else fetch_q(c);
     fetch_cc<NTC>(fp, a.Pm + cc_off(bh, nch, c));
     if (erase) fetch_cc<NTC>(ft, a.Tm + cc_off(bh, nch, c));
@@ -473,13 +477,14 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
     fs = fetch_scalars(a, tok, n);
   };
   fetch(nch - 1);
-  if (gain) fetch_q(nch - 1);
+  if constexpr (GAIN) fetch_q(nch - 1);
   for (int c = nch - 1; c >= 0; --c) {
     const int n = min(C, L - c * C);
     const size_t tok = (size_t)bh * L + (size_t)c * C;
     __syncthreads();
     put_rows<NTC, LKC>(fk, sK);
-    put_rows<NTC, LKC>(gain ? fg : fq, sQ);
+    if constexpr (GAIN) put_rows<NTC, LKC>(fg, sQ);
+    else put_rows<NTC, LKC>(fq, sQ);
     put_cc<NTC, LCC>(fp, sP);
     if (erase) put_cc<NTC, LCC>(ft, sT);
     put_tile<NTC, LOC>(fo, sO, nullptr);
@@ -511,7 +516,7 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
       }
     }
     __syncthreads();
-    if (gain) {  // every wavefront is done with the gain rows: Q takes the tile
+    if constexpr (GAIN) {  // every wavefront is done with the gain rows: Q takes the tile
       put_rows<NTC, LKC>(fq, sQ);
       if (c > 0) fetch_q(c - 1);
     }
@@ -887,8 +892,11 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
   e = launch_lds("bwd_fwd_kernel", bwd_fwd_kernel, dim3(a.BH, ntw), NTC,
                  ((1 + ng) * C * LKC + C * LCC + DP * LOC + 2 * C * LOC + 3 * C) * f, a, s);
   if (e != hipSuccess) return e;
-  e = launch_lds("bwd_rev_kernel", bwd_rev_kernel, dim3(a.BH, ntw), NTC,
-                 (2 * C * LKC + 2 * C * LCC + DP * LOC + 3 * C * LOC + 3 * C) * f, a, s);
+  const size_t lds_rev = (2 * C * LKC + 2 * C * LCC + DP * LOC + 3 * C * LOC + 3 * C) * f;
+  e = a.gain ? launch_lds("bwd_rev_kernel<true>", bwd_rev_kernel<true>, dim3(a.BH, ntw), NTC,
+                          lds_rev, a, s)
+             : launch_lds("bwd_rev_kernel<false>", bwd_rev_kernel<false>, dim3(a.BH, ntw), NTC,
+                          lds_rev, a, s);
   if (e != hipSuccess) return e;
   const size_t lds_c = (2 * C * (VW + 1) + DP * (VW + 1) + NT / 64) * f;
   e = launch_lds("bwd_contract_kernel<false>", bwd_contract_kernel<false>, dim3(a.BH, nch, 2), NT,
