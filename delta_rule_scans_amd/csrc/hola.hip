@@ -12,6 +12,9 @@
 // One workgroup (256 lanes) per head. Logits: 32 lanes per cached row (8 rows
 // per pass), 16-byte loads. Weighted value sum: lane (rg, cg) accumulates
 // columns of group cg over rows rg, rg + 8, ...; partial sums meet in LDS.
+// With 16-byte rows and at most 64 slots, every key and value row a lane
+// needs (8 of each) is loaded into registers before anything else, so the
+// value reads are in flight while the logits and the softmax are formed.
 // Eviction: one wavefront takes the lexicographic minimum of (m, -pos) with
 // shuffles, so the choice is deterministic and uses no atomics. A NaN score
 // ranks below every other score (ranked as -infinity, stored unchanged), as in
@@ -24,6 +27,7 @@ namespace {
 
 constexpr int NT = 256;
 constexpr int WMAX = 256;
+constexpr int PF = 8;  // rows per lane held in registers (capacities up to 8 * PF)
 
 // ranking key of a score: NaN ranks below every other score
 __device__ __forceinline__ float rank_key(float m) { return m == m ? m : -INFINITY; }
@@ -53,7 +57,7 @@ __device__ __forceinline__ void dot_row(const float* row, const float* sq, int d
   }
 }
 
-template <bool VEC>
+template <bool VEC, bool REGS>
 __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
                                                   const float* __restrict__ k,
                                                   const float* __restrict__ v,
@@ -66,7 +70,8 @@ __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
                                                   const float* __restrict__ sink_logit,
                                                   float* __restrict__ o_cache, float rms_eps,
                                                   int H, int dk, int dv, int w, int recency) {
-  __shared__ float sq[128], sk[128], sv[128];
+  // one entry per lane: every lane stores its element (0 past d_k, d_v)
+  __shared__ __align__(16) float sq[NT], sk[NT], sv[NT];
   __shared__ float sl[WMAX + 2];
   __shared__ float red[8][128];
   __shared__ float sscal[4];
@@ -77,11 +82,31 @@ __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
   const float* ck = cache_k + (size_t)bh * w * dk;
   const float* cv = cache_v + (size_t)bh * w * dv;
 
-  if (tid < dk) {
-    sq[tid] = q[(size_t)bh * dk + tid];
-    sk[tid] = k[(size_t)bh * dk + tid];
+  // the token's own rows, then (REGS: capacity at most 8 PF, 16-byte rows)
+  // rows rg + 8 i of the cache, all without branches (buffer reads past the
+  // n filled rows, or past the token's rows, return 0; columns past d_k or
+  // d_v are never used), so that the first wait takes in only the token's rows
+  const float xq = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(q + (size_t)bh * dk, dk * sizeof(float)), tid * 4, 0, 0));
+  const float xk = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(k + (size_t)bh * dk, dk * sizeof(float)), tid * 4, 0, 0));
+  const float xv = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(v + (size_t)bh * dv, dv * sizeof(float)), tid * 4, 0, 0));
+  constexpr bool regs = REGS;
+  float4 kr[PF], vr[PF];
+  if constexpr (REGS) {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(ck, (size_t)n * dk * sizeof(float));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(cv, (size_t)n * dv * sizeof(float));
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int j = rg + 8 * i;
+      kr[i] = stream_load16(rk, (j * dk + 4 * cg) * (int)sizeof(float));
+      vr[i] = stream_load16(rv, (j * dv + 4 * cg) * (int)sizeof(float));
+    }
   }
-  if (tid < dv) sv[tid] = v[(size_t)bh * dv + tid];
+  sq[tid] = xq;
+  sk[tid] = xk;
+  sv[tid] = xv;
   __syncthreads();
   if (tid < 64) {  // one wavefront: |q|^2
     float x = 0.f;
@@ -93,12 +118,31 @@ __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
   const float qscale = sscal[0];
 
   // logits of the cached rows and of the current token (index n)
-  for (int j = rg; j <= n; j += 8) {
-    float qk, kk;
-    dot_row<VEC>(j < n ? ck + (size_t)j * dk : sk, sq, dk, cg, qk, kk);
-    qk = sum32(qk);
-    kk = sum32(kk);
-    if (cg == 0) sl[j] = qk * qscale / sqrtf(kk / dk + rms_eps);
+  if (regs) {
+    auto logit = [&](int j, float4 x, bool cur) {
+      float qk = 0.f, kk = 0.f;
+      if (4 * cg < dk) {
+        if (cur) x = *reinterpret_cast<const float4*>(sk + 4 * cg);
+        const float4 y = *reinterpret_cast<const float4*>(sq + 4 * cg);
+        qk = x.x * y.x + x.y * y.y + x.z * y.z + x.w * y.w;
+        kk = x.x * x.x + x.y * x.y + x.z * x.z + x.w * x.w;
+      }
+      qk = sum32(qk);
+      kk = sum32(kk);
+      if (cg == 0) sl[j] = qk * qscale / sqrtf(kk / dk + rms_eps);
+    };
+#pragma unroll
+    for (int i = 0; i < PF; ++i)
+      if (rg + 8 * i < n) logit(rg + 8 * i, kr[i], false);
+    if (rg == (n & 7)) logit(n, kr[0], true);
+  } else {
+    for (int j = rg; j <= n; j += 8) {
+      float qk, kk;
+      dot_row<VEC>(j < n ? ck + (size_t)j * dk : sk, sq, dk, cg, qk, kk);
+      qk = sum32(qk);
+      kk = sum32(kk);
+      if (cg == 0) sl[j] = qk * qscale / sqrtf(kk / dk + rms_eps);
+    }
   }
   const int nl = n + 1 + (sink_logit ? 1 : 0);
   if (sink_logit && tid == 0) sl[n + 1] = sink_logit[bh % H];
@@ -122,7 +166,28 @@ __global__ __launch_bounds__(NT) void hola_kernel(const float* __restrict__ q,
 
   // weighted value sum (the sink's value is 0)
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int j = rg; j <= n; j += 8) {
+  if (regs) {
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+      const int j = rg + 8 * i;
+      if (j < n) {
+        const float p = sl[j];
+        acc[0] = fmaf(p, vr[i].x, acc[0]);
+        acc[1] = fmaf(p, vr[i].y, acc[1]);
+        acc[2] = fmaf(p, vr[i].z, acc[2]);
+        acc[3] = fmaf(p, vr[i].w, acc[3]);
+      }
+    }
+    if (rg == (n & 7) && 4 * cg < dv) {
+      const float p = sl[n];
+      const float4 x = *reinterpret_cast<const float4*>(sv + 4 * cg);
+      acc[0] = fmaf(p, x.x, acc[0]);
+      acc[1] = fmaf(p, x.y, acc[1]);
+      acc[2] = fmaf(p, x.z, acc[2]);
+      acc[3] = fmaf(p, x.w, acc[3]);
+    }
+  }
+  for (int j = regs ? n + 1 : rg; j <= n; j += 8) {
     const float p = sl[j];
     const float* row = j < n ? cv + (size_t)j * dv : sv;
     if (VEC) {
@@ -205,14 +270,20 @@ hipError_t launch_hola(const float* q, const float* k, const float* v, const flo
   const bool vec = dk % 4 == 0 && dv % 4 == 0 &&
                    ((reinterpret_cast<uintptr_t>(cache_k) | reinterpret_cast<uintptr_t>(cache_v)) &
                     15) == 0;
-  if (vec)
-    KDN_LAUNCH(hola_kernel<true>, dim3(B * H), dim3(NT), 0, s, q, k, v, m, t, cache_k,
-                       cache_v, cache_m, cache_pos, cache_count, sink_logit, o_cache, rms_eps, H, dk,
-                       dv, w, policy);
-  else
-    KDN_LAUNCH(hola_kernel<false>, dim3(B * H), dim3(NT), 0, s, q, k, v, m, t, cache_k,
-                       cache_v, cache_m, cache_pos, cache_count, sink_logit, o_cache, rms_eps, H,
-                       dk, dv, w, policy);
+  const int nb = B * H;
+  if (vec && w <= 8 * PF) {
+    KDN_LAUNCH_NAMED("hola_kernel<true, true>", (hola_kernel<true, true>), dim3(nb), dim3(NT), 0,
+                     s, q, k, v, m, t, cache_k, cache_v, cache_m, cache_pos, cache_count,
+                     sink_logit, o_cache, rms_eps, H, dk, dv, w, policy);
+  } else if (vec) {
+    KDN_LAUNCH_NAMED("hola_kernel<true, false>", (hola_kernel<true, false>), dim3(nb), dim3(NT),
+                     0, s, q, k, v, m, t, cache_k, cache_v, cache_m, cache_pos, cache_count,
+                     sink_logit, o_cache, rms_eps, H, dk, dv, w, policy);
+  } else {
+    KDN_LAUNCH_NAMED("hola_kernel<false, false>", (hola_kernel<false, false>), dim3(nb), dim3(NT),
+                     0, s, q, k, v, m, t, cache_k, cache_v, cache_m, cache_pos, cache_count,
+                     sink_logit, o_cache, rms_eps, H, dk, dv, w, policy);
+  }
   return hipGetLastError();
 }
 
