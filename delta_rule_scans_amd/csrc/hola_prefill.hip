@@ -204,9 +204,13 @@ __global__ __launch_bounds__(NT) void merge_kernel(PrefillArgs a) {
 // mod 32 words the key reads are conflict-free. The next key tile is fetched
 // into registers while the current one is used.
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 
-constexpr int LDR = MAXD + 1;  // [row][d] strides of the query, key and value tiles
-constexpr int LDP = KT + 1;    // [query][key] weights
+constexpr int KHP = MAXD + 8;  // fp16 pitch of the key tiles [key][d]
+constexpr int VTP = KT + 8;    // fp16 pitch of the value tiles, transposed [d][key]
+constexpr int PHP = KT + 8;    // fp16 pitch of the weight tiles [query][key]
+constexpr size_t kReadLds = (size_t)(2 * KT * KHP + 2 * MAXD * VTP + 2 * QT * PHP) * 2 + 16;
 
 // Four consecutive elements (the index a multiple of 4, rows 16-byte aligned
 // for float32 and 8-byte aligned for bf16).
@@ -222,32 +226,71 @@ __device__ __forceinline__ bool aligned_rows(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15) == 0;
 }
 
-template <int NB, int PL>
-__device__ __forceinline__ void mfma_row(floatx4 (&acc)[NB], const float* pa, int am, int ak,
-                                         const float* pb, int bk, int bn, int m0, int K) {
-  const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
-  for (int k0 = 0; k0 < K; k0 += PL) {
-    const float* A = pa + (m0 + r) * am + (k0 + (PL / 4) * q) * ak;
-    const float* B = pb + (k0 + (PL / 4) * q) * bk + r * bn;
-#pragma unroll
-    for (int s = 0; s < PL / 4; ++s) {
-      const float av = A[s * ak];
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, B[s * bk + 16 * b * bn], acc[b], 0, 0, 0);
-    }
-  }
+// x as two fp16 parts: x_h = fp16(x), x_l = fp16(x - x_h). The matrix cores
+// take subnormal fp16 inputs as zero, so callers scale x by a power of two
+// that keeps x_l normal wherever it matters.
+struct Split16 {
+  _Float16 h, l;
+};
+// The high part is converted once and held opaque, so that the operand and
+// the residual use the same bits: the compiler would otherwise convert x again
+// where it builds the operand, and its two conversions can round a tie (x
+// halfway between two fp16 values) in different directions.
+__device__ __forceinline__ Split16 split16(float x) {
+  uint32_t hb = __builtin_bit_cast(uint16_t, (_Float16)x);
+  asm volatile("" : "+v"(hb));
+  const _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)hb);
+  return {h, (_Float16)(x - (float)h)};
 }
+// c + a b, a and b each given as two fp16 parts (the product of the two low
+// parts, below 2^-22 of the product, is left out). The matrix cores align the
+// products of one instruction to the largest of them and of the incoming
+// accumulator, keeping float32 precision only relative to that (measured: a
+// 2^20 accumulator costs products near 2^5 their low bits), so the high and
+// the low products each start from zero and meet c in vector adds.
+__device__ __forceinline__ floatx4 mfma_split(half8 ah, half8 al, half8 bh, half8 bl, floatx4 c) {
+  const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+  const floatx4 hh = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, z, 0, 0, 0);
+  floatx4 lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, z, 0, 0, 0);
+  lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, lo, 0, 0, 0);
+  return c + (hh + lo);
+}
+// 2^e as a float, -126 <= e <= 127
+__device__ __forceinline__ float pow2f(int e) { return __int_as_float((127 + e) << 23); }
 
-// Three workgroups per CU (as many as its 41.5 KB of LDS allows): the bound
-// keeps the registers (vector and accumulation together) within a third of
-// the file, with no spills; at two per CU the cache phase took 15% longer.
+// Read: 64 queries per workgroup against 32-key tiles on the fp16 matrix cores
+// (v_mfma_f32_16x16x32_f16: lane l holds A(m0 + l % 16, k0 + 8 (l / 16) .. + 8)
+// and B(k0 + 8 (l / 16) .. + 8, n0 + l % 16); the block's element
+// (4 (l / 16) + i, l % 16) is accumulator i). Every float32 operand goes in as
+// two fp16 parts and each product as three (high x high, high x low, low x
+// high): about 22 significant bits, float32-level results at a fifth of the
+// float32 products' matrix-core time. The parts are formed from exact
+// power-of-two multiples that keep the high parts below 2^15 and the low parts
+// normal (the matrix cores take fp16 subnormals as zero): RMS-normalised
+// queries and keys (no component above sqrt(d_k)) times 2^8 each; weights
+// (at most 1) times 2^14; the values of key tile t times 2^-E_t, E_t the
+// exponent that brings its largest finite |v| into [2^14, 2^15), with its
+// weights times a further 2^(E_t - E_run), E_run the largest E_t so far (the
+// accumulated outputs are rescaled when it grows). The logits and outputs are
+// scaled back. Wavefront w owns queries 16 w .. 16 w + 15: its logits for a
+// tile are two 16 x 16 blocks, the online softmax runs on them in registers (a
+// row's 16 columns sit in 16 lanes), its weights go through its own rows of
+// LDS into operand order, and its outputs are eight 16 x 16 blocks in
+// registers. Values are staged transposed ([d][key]) so that every operand is
+// one 16-byte read. The next key tile is fetched into registers while the
+// current one is used.
+//
+// Three workgroups per CU (as many as its 47 KB of LDS allows).
 template <typename Tin>
 __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
-  extern __shared__ __align__(16) float lds[];
-  float* sK = lds;               // [KT][LDR]
-  float* sV = sK + KT * LDR;     // [KT][LDR]
-  float* sP = sV + KT * LDR;     // [QT][LDP]
+  extern __shared__ __align__(16) _Float16 ldsh[];
+  _Float16* sKh = ldsh;                   // [KT][KHP] keys, high parts
+  _Float16* sKl = sKh + KT * KHP;         //           low parts
+  _Float16* sVh = sKl + KT * KHP;         // [MAXD][VTP] values transposed, high parts
+  _Float16* sVl = sVh + MAXD * VTP;       //             low parts
+  _Float16* sPh = sVl + MAXD * VTP;       // [QT][PHP] weights, high parts
+  _Float16* sPl = sPh + QT * PHP;         //           low parts
+  uint32_t* sE = reinterpret_cast<uint32_t*>(sPl + QT * PHP);  // [4] per-wavefront max |v| bits
   const int bh = blockIdx.x, j = blockIdx.y, qt = blockIdx.z, tid = threadIdx.x;
   const int dk = a.dk, dv = a.dv;
   const int nblk = (a.L + a.block - 1) / a.block;
@@ -266,35 +309,37 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
   const int nkeys = ncache + q0 + nq;
   const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
 
-  // This lane's query operands: row 16 w + r, columns 64 p + 16 q + s,
-  // RMS-normalised and times 1/sqrt(d_k) (the row's four lane groups meet by
-  // shuffles).
-  float qa[2][16];
+  // This lane's query operands: row 16 w + r, columns 32 s + 8 q .. + 8,
+  // RMS-normalised (the row's four lane groups meet by shuffles), in two parts.
+  half8 qoh[4], qol[4];
   {
     const int row = 16 * w + r;
+    float x[4][8];
     float ss = 0.f;
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int c = 64 * p + 16 * q + u;
-        const float x =
-            (row < nq && c < dk) ? Elem<Tin>::load(qh, (size_t)(j0 + q0 + row) * dk + c) : 0.f;
-        qa[p][u] = x;
-        ss = fmaf(x, x, ss);
+      for (int u = 0; u < 8; ++u) {
+        const int c = 32 * s + 8 * q + u;
+        x[s][u] = (row < nq && c < dk) ? Elem<Tin>::load(qh, (size_t)(j0 + q0 + row) * dk + c) : 0.f;
+        ss = fmaf(x[s][u], x[s][u], ss);
       }
     ss += __shfl_xor(ss, 16, 64);
     ss += __shfl_xor(ss, 32, 64);
-    const float sc = (1.f / sqrtf((float)dk)) / sqrtf(ss / dk + a.rms_eps);
+    const float sc = 256.f / sqrtf(ss / dk + a.rms_eps);  // times 2^8
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) qa[p][u] *= sc;
+      for (int u = 0; u < 8; ++u) {
+        const Split16 t = split16(x[s][u] * sc);
+        qoh[s][u] = t.h;
+        qol[s][u] = t.l;
+      }
   }
+  const float lscale = (1.f / 65536.f) / sqrtf((float)dk);  // logit scale, less the 2^16
   // key tiles: 8 lanes per key; lane kp takes columns 32 g + 4 kp + v (g, v <
-  // 4), four consecutive ones per load, which also puts the 32 lanes of an LDS
-  // write on distinct banks. The source of the tile after next is looked up
-  // while the next tile's rows are in flight.
+  // 4), four consecutive ones per load. The source of the tile after next is
+  // looked up while the next tile's rows are in flight.
   const int kr = tid >> 3, kp = tid & 7;
   auto src_of = [&](int e) { return e < nkeys ? (e < ncache ? mem[e] : j0 + e - ncache) : 0; };
   const bool vec = ((dk | dv) & 3) == 0 && aligned_rows(a.k) && aligned_rows(a.v) &&
@@ -345,23 +390,59 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
   }
 #pragma unroll
   for (int cb = 0; cb < MAXD / 16; ++cb) acc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  constexpr int kNoE = -1000;  // E_run before the first tile
+  int erun = kNoE;            // E_run
   fetch(kr, src_of(kr));
   int src_next = src_of(KT + kr);
   for (int e0 = 0; e0 < nkeys; e0 += KT) {
+    {  // the largest finite |v| of this tile, per wavefront
+      uint32_t mv = 0;
+#pragma unroll
+      for (int u = 0; u < MAXD / 8; ++u) {
+        const uint32_t b = __float_as_uint(fabsf(vx[u]));
+        mv = b < 0x7f800000u ? max(mv, b) : mv;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) mv = max(mv, (uint32_t)__shfl_xor((int)mv, off, 64));
+      if (l == 0) sE[w] = mv;
+    }
     __syncthreads();
-    {
+    // E_t, and the running exponent
+    const uint32_t mall = max(max(sE[0], sE[1]), max(sE[2], sE[3]));
+    const int ex = (int)(mall >> 23) - 127;  // floor(log2) of the largest finite |v|
+    const int et = max(ex - 14, -100);        // E_t
+    if (et > erun) {
+      if (erun != kNoE) {
+        const float f = pow2f(max(erun - et, -126));
+#pragma unroll
+        for (int cb = 0; cb < MAXD / 16; ++cb) acc[cb] = acc[cb] * f;
+      }
+      erun = et;
+    }
+    {  // stage: keys RMS-normalised, values times 2^-E_t, both in two parts
       float ss = 0.f;
 #pragma unroll
       for (int u = 0; u < MAXD / 8; ++u) ss = fmaf(kx[u], kx[u], ss);
       ss += __shfl_xor(ss, 1, 8);
       ss += __shfl_xor(ss, 2, 8);
       ss += __shfl_xor(ss, 4, 8);
-      const float sc = 1.f / sqrtf(ss / dk + a.rms_eps);
+      const float sc = 256.f / sqrtf(ss / dk + a.rms_eps);  // times 2^8
+      const float vsc = pow2f(-et);
 #pragma unroll
-      for (int u = 0; u < MAXD / 8; ++u) {
-        const int c = 32 * (u >> 2) + 4 * kp + (u & 3);
-        sK[kr * LDR + c] = kx[u] * sc;
-        sV[kr * LDR + c] = vx[u];
+      for (int g = 0; g < 4; ++g) {
+        const int c = 32 * g + 4 * kp;
+        half4 hk, lk;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const Split16 tk = split16(kx[4 * g + v] * sc);
+          hk[v] = tk.h;
+          lk[v] = tk.l;
+          const Split16 tv = split16(vx[4 * g + v] * vsc);
+          sVh[(c + v) * VTP + kr] = tv.h;
+          sVl[(c + v) * VTP + kr] = tv.l;
+        }
+        *reinterpret_cast<half4*>(sKh + kr * KHP + c) = hk;
+        *reinterpret_cast<half4*>(sKl + kr * KHP + c) = lk;
       }
     }
     if (e0 + KT < nkeys) {
@@ -371,15 +452,16 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
     __syncthreads();
     floatx4 lg[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      if (p == 1 && dk <= 64) break;
-      const float* B = sK + 64 * p + 16 * q + r * LDR;
+    for (int s = 0; s < 4; ++s) {
+      if (32 * s >= dk) break;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        lg[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[p][u], B[u], lg[0], 0, 0, 0);
-        lg[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[p][u], B[u + 16 * LDR], lg[1], 0, 0, 0);
+      for (int b = 0; b < 2; ++b) {
+        const int off = (16 * b + r) * KHP + 32 * s + 8 * q;
+        lg[b] = mfma_split(qoh[s], qol[s], *reinterpret_cast<const half8*>(sKh + off),
+                           *reinterpret_cast<const half8*>(sKl + off), lg[b]);
       }
     }
+    const float pw = pow2f(max(14 + et - erun, -126));  // weights times 2^(14 + E_t - E_run)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int qi = 16 * w + 4 * q + i;  // query within the tile
@@ -391,7 +473,7 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
         const int e = e0 + 16 * b + r;
         // cache members are always visible; block tokens up to the query itself
         const bool vis = qi < nq && e < nkeys && (e < ncache || e - ncache <= qtok);
-        lv[b] = vis ? lg[b][i] : -INFINITY;
+        lv[b] = vis ? lg[b][i] * lscale : -INFINITY;
         tmax = fmaxf(tmax, lv[b]);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 16));
@@ -405,7 +487,9 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const float p = lv[b] == -INFINITY ? 0.f : __expf(lv[b] - Mn);
-        sP[qi * LDP + 16 * b + r] = p;
+        const Split16 tp = split16(p * pw);
+        sPh[qi * PHP + 16 * b + r] = tp.h;
+        sPl[qi * PHP + 16 * b + r] = tp.l;
         ps += p;
       }
       ps += __shfl_xor(ps, 1, 16);
@@ -417,15 +501,26 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
 #pragma unroll
       for (int cb = 0; cb < MAXD / 16; ++cb) acc[cb][i] *= scale;
     }
-    __syncthreads();
-    mfma_row<MAXD / 16, KT>(acc, sP, LDP, 1, sV, LDR, 1, 16 * w, KT);
+    // the weight rows just written are this wavefront's own: in-order LDS
+    // access within the wavefront needs no barrier
+    const int poff = (16 * w + r) * PHP + 8 * q;
+    const half8 ph = *reinterpret_cast<const half8*>(sPh + poff);
+    const half8 pl = *reinterpret_cast<const half8*>(sPl + poff);
+#pragma unroll
+    for (int cb = 0; cb < MAXD / 16; ++cb) {
+      if (16 * cb >= dv) break;
+      const int voff = (16 * cb + r) * VTP + 8 * q;
+      acc[cb] = mfma_split(ph, pl, *reinterpret_cast<const half8*>(sVh + voff),
+                           *reinterpret_cast<const half8*>(sVl + voff), acc[cb]);
+    }
   }
+  const float fo = pow2f(erun - 14);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int qi = 16 * w + 4 * q + i;
     if (qi < nq) {
       float* o = a.o_cache + ((size_t)bh * a.L + j0 + q0 + qi) * dv;
-      const float inv = 1.f / Z[i];
+      const float inv = fo / Z[i];
 #pragma unroll
       for (int cb = 0; cb < MAXD / 16; ++cb)
         if (16 * cb + r < dv) o[16 * cb + r] = acc[cb][i] * inv;
@@ -486,7 +581,7 @@ hipError_t prefill_typed(const PrefillArgs& a, hipStream_t s) {
   KDN_LAUNCH(merge_kernel, dim3(a.BH), dim3(NT), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t read_lds = (size_t)(2 * KT * LDR + QT * LDP) * sizeof(float);
+  const size_t read_lds = kReadLds;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(read_kernel<Tin>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)read_lds);
   if (e != hipSuccess) return e;

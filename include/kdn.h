@@ -386,8 +386,11 @@ int kdn_scan_bwd_ex(const void *q, const void *k, const void *v, const void *d_o
  *            aligned.
  * Sizes: B, H >= 1; L >= 0 (L = 0 leaves the cache as it is); 1 <= d_k, d_v
  * <= 128; 1 <= w <= 256; 1 <= block <= 1024; t0 + L <= 2^31 - 1; rms_eps >= 0.
- * The read runs in float32: logits and weighted values on the fp32 matrix
- * cores, the softmax on the vector units.
+ * The read keeps float32 accuracy: logits and weighted values run on the fp16
+ * matrix cores with every float32 operand split into two fp16 parts (three
+ * products per float32 product, about 22 significant bits, each part formed
+ * from an exact power-of-two multiple of the operand), the softmax on the
+ * vector units.
  */
 size_t hola_prefill_workspace_size(int B, int H, int L, int d_k, int d_v, int w, int block);
 
