@@ -210,7 +210,7 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 constexpr int KHP = MAXD + 8;  // fp16 pitch of the key tiles [key][d]
 constexpr int VTP = KT + 8;    // fp16 pitch of the value tiles, transposed [d][key]
 constexpr int PHP = KT + 8;    // fp16 pitch of the weight tiles [query][key]
-constexpr size_t kReadLds = (size_t)(2 * KT * KHP + 2 * MAXD * VTP + 2 * QT * PHP) * 2 + 16;
+constexpr size_t kReadLds = (size_t)(2 * KT * KHP + 2 * MAXD * VTP + 2 * QT * PHP) * 2 + KT * 4;
 
 // Four consecutive elements (the index a multiple of 4, rows 16-byte aligned
 // for float32 and 8-byte aligned for bf16).
@@ -268,11 +268,12 @@ __device__ __forceinline__ float pow2f(int e) { return __int_as_float((127 + e) 
 // power-of-two multiples that keep the high parts below 2^15 and the low parts
 // normal (the matrix cores take fp16 subnormals as zero): RMS-normalised
 // queries and keys (no component above sqrt(d_k)) times 2^8 each; weights
-// (at most 1) times 2^14; the values of key tile t times 2^-E_t, E_t the
-// exponent that brings its largest finite |v| into [2^14, 2^15), with its
-// weights times a further 2^(E_t - E_run), E_run the largest E_t so far (the
-// accumulated outputs are rescaled when it grows). The logits and outputs are
-// scaled back. Wavefront w owns queries 16 w .. 16 w + 15: its logits for a
+// (at most 1) times 2^14; the values of key j times 2^-E_j, E_j the exponent
+// that brings the row's largest finite |v| into [2^14, 2^15), with the weight
+// of key j for query i times a further 2^(E_j - F_i), F_i the largest E_j
+// among the keys query i has seen (its accumulated outputs are rescaled
+// with the online softmax when F_i grows). The logits and outputs are scaled
+// back. Wavefront w owns queries 16 w .. 16 w + 15: its logits for a
 // tile are two 16 x 16 blocks, the online softmax runs on them in registers (a
 // row's 16 columns sit in 16 lanes), its weights go through its own rows of
 // LDS into operand order, and its outputs are eight 16 x 16 blocks in
@@ -290,7 +291,7 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
   _Float16* sVl = sVh + MAXD * VTP;       //             low parts
   _Float16* sPh = sVl + MAXD * VTP;       // [QT][PHP] weights, high parts
   _Float16* sPl = sPh + QT * PHP;         //           low parts
-  uint32_t* sE = reinterpret_cast<uint32_t*>(sPl + QT * PHP);  // [4] per-wavefront max |v| bits
+  int* sEk = reinterpret_cast<int*>(sPl + QT * PHP);  // [KT] value exponents E_j of the tile's keys
   const int bh = blockIdx.x, j = blockIdx.y, qt = blockIdx.z, tid = threadIdx.x;
   const int dk = a.dk, dv = a.dv;
   const int nblk = (a.L + a.block - 1) / a.block;
@@ -390,44 +391,31 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
   }
 #pragma unroll
   for (int cb = 0; cb < MAXD / 16; ++cb) acc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  constexpr int kNoE = -1000;  // E_run before the first tile
-  int erun = kNoE;            // E_run
+  constexpr int kNoE = -1000;  // F_i before the first visible key
+  int F[4] = {kNoE, kNoE, kNoE, kNoE};
   fetch(kr, src_of(kr));
   int src_next = src_of(KT + kr);
   for (int e0 = 0; e0 < nkeys; e0 += KT) {
-    {  // the largest finite |v| of this tile, per wavefront
-      uint32_t mv = 0;
+    __syncthreads();
+    {  // stage: keys RMS-normalised, values times 2^-E_j, both in two parts
+      float ss = 0.f;
+      uint32_t mv = 0;  // bits of the row's largest finite |v|
 #pragma unroll
       for (int u = 0; u < MAXD / 8; ++u) {
+        ss = fmaf(kx[u], kx[u], ss);
         const uint32_t b = __float_as_uint(fabsf(vx[u]));
         mv = b < 0x7f800000u ? max(mv, b) : mv;
       }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) mv = max(mv, (uint32_t)__shfl_xor((int)mv, off, 64));
-      if (l == 0) sE[w] = mv;
-    }
-    __syncthreads();
-    // E_t, and the running exponent
-    const uint32_t mall = max(max(sE[0], sE[1]), max(sE[2], sE[3]));
-    const int ex = (int)(mall >> 23) - 127;  // floor(log2) of the largest finite |v|
-    const int et = max(ex - 14, -100);        // E_t
-    if (et > erun) {
-      if (erun != kNoE) {
-        const float f = pow2f(max(erun - et, -126));
-#pragma unroll
-        for (int cb = 0; cb < MAXD / 16; ++cb) acc[cb] = acc[cb] * f;
-      }
-      erun = et;
-    }
-    {  // stage: keys RMS-normalised, values times 2^-E_t, both in two parts
-      float ss = 0.f;
-#pragma unroll
-      for (int u = 0; u < MAXD / 8; ++u) ss = fmaf(kx[u], kx[u], ss);
       ss += __shfl_xor(ss, 1, 8);
       ss += __shfl_xor(ss, 2, 8);
       ss += __shfl_xor(ss, 4, 8);
+      mv = max(mv, (uint32_t)__shfl_xor((int)mv, 1, 8));
+      mv = max(mv, (uint32_t)__shfl_xor((int)mv, 2, 8));
+      mv = max(mv, (uint32_t)__shfl_xor((int)mv, 4, 8));
+      const int ej = max((int)(mv >> 23) - 127 - 14, -100);  // E_j
+      if (kp == 0) sEk[kr] = ej;
       const float sc = 256.f / sqrtf(ss / dk + a.rms_eps);  // times 2^8
-      const float vsc = pow2f(-et);
+      const float vsc = pow2f(-ej);
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = 32 * g + 4 * kp;
@@ -461,13 +449,14 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
                            *reinterpret_cast<const half8*>(sKl + off), lg[b]);
       }
     }
-    const float pw = pow2f(max(14 + et - erun, -126));  // weights times 2^(14 + E_t - E_run)
+    const int ek[2] = {sEk[r], sEk[16 + r]};  // E_j of this lane's two keys
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int qi = 16 * w + 4 * q + i;  // query within the tile
       const int qtok = q0 + qi;           // relative to the block
       float lv[2];
       float tmax = -INFINITY;
+      int emax = kNoE;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int e = e0 + 16 * b + r;
@@ -475,19 +464,29 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
         const bool vis = qi < nq && e < nkeys && (e < ncache || e - ncache <= qtok);
         lv[b] = vis ? lg[b][i] * lscale : -INFINITY;
         tmax = fmaxf(tmax, lv[b]);
+        emax = vis ? max(emax, ek[b]) : emax;
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 1, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 2, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 4, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 8, 16));
+      emax = max(emax, __shfl_xor(emax, 1, 16));
+      emax = max(emax, __shfl_xor(emax, 2, 16));
+      emax = max(emax, __shfl_xor(emax, 4, 16));
+      emax = max(emax, __shfl_xor(emax, 8, 16));
       const float Mn = fmaxf(M[i], tmax);
-      // rows with nothing visible yet keep M = -inf; their weights stay 0
-      const float scale = Mn == -INFINITY ? 1.f : __expf(M[i] - Mn);
+      const int Fn = max(F[i], emax);
+      // rows with nothing visible yet keep M = -inf; their weights stay 0;
+      // the outputs so far move to the scale of F_i's new value
+      const float ms = Mn == -INFINITY ? 1.f : __expf(M[i] - Mn);  // the softmax's rescale
+      const float scale = ms * pow2f(max(F[i] - Fn, -126));          // and the outputs'
       float ps = 0.f;
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const float p = lv[b] == -INFINITY ? 0.f : __expf(lv[b] - Mn);
-        const Split16 tp = split16(p * pw);
+        // (a key not visible to this query may have E_j above F_i: its weight
+        // is 0 and its factor is held finite)
+        const Split16 tp = split16(p * pow2f(min(max(14 + ek[b] - Fn, -126), 14)));
         sPh[qi * PHP + 16 * b + r] = tp.h;
         sPl[qi * PHP + 16 * b + r] = tp.l;
         ps += p;
@@ -496,8 +495,9 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
       ps += __shfl_xor(ps, 2, 16);
       ps += __shfl_xor(ps, 4, 16);
       ps += __shfl_xor(ps, 8, 16);
-      Z[i] = fmaf(Z[i], scale, ps);
+      Z[i] = fmaf(Z[i], ms, ps);
       M[i] = Mn;
+      F[i] = Fn;
 #pragma unroll
       for (int cb = 0; cb < MAXD / 16; ++cb) acc[cb][i] *= scale;
     }
@@ -514,13 +514,12 @@ __global__ __launch_bounds__(NT, 3) void read_kernel(PrefillArgs a) {
                            *reinterpret_cast<const half8*>(sVl + voff), acc[cb]);
     }
   }
-  const float fo = pow2f(erun - 14);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int qi = 16 * w + 4 * q + i;
     if (qi < nq) {
       float* o = a.o_cache + ((size_t)bh * a.L + j0 + q0 + qi) * dv;
-      const float inv = fo / Z[i];
+      const float inv = pow2f(min(max(F[i] - 14, -126), 127)) / Z[i];
 #pragma unroll
       for (int cb = 0; cb < MAXD / 16; ++cb)
         if (16 * cb + r < dv) o[16 * cb + r] = acc[cb][i] * inv;

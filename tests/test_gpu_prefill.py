@@ -142,6 +142,32 @@ def test_prefill_unaligned_rows(kdn, orc, dtype):
                       init=None if init is None else (init, rng))
 
 
+def test_prefill_value_range(kdn, orc):
+    """Value rows from 1e-20 to 1e30 (far outside fp16 range, where the read's
+    split products scale each key tile by a power of two) and one whole block
+    of tiny values: every query's output against the oracle, relative to that
+    query's own output size."""
+    import torch
+    rng = np.random.Generator(np.random.PCG64(306))
+    B, H, L, d, w = 1, 2, 260, 64, 12
+    q = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    k = rng.standard_normal((B, H, L, d)).astype(np.float32)
+    mag = 10.0 ** rng.uniform(-20, 30, (B, H, L, 1))
+    mag[:, :, 64:128] = 1e-25  # the second block: tiny values only
+    v = (rng.standard_normal((B, H, L, d)) * mag).astype(np.float32)
+    m = rng.uniform(0, 1, (B, H, L)).astype(np.float32)
+    cache = kdn.HolaCache(B, H, d, d, w)
+    oc = kdn.hola_prefill(dev_tensor(q), dev_tensor(k), dev_tensor(v), dev_tensor(m), 0, cache, block=64)
+    torch.cuda.synchronize()
+    got = host(oc).astype(np.float64)
+    ref = orc.HolaCache(B, H, d, d, w).prefill(q, k, v, m.astype(np.float64), 0, 64, None)
+    assert np.all(np.isfinite(got))
+    scale = np.sqrt(np.mean(ref ** 2, axis=-1, keepdims=True))
+    err = np.max(np.abs(got - ref) / scale)
+    log(f"  value range 1e-20..1e30: worst per-query max|diff|/RMS = {err:.3e} (tol {TOL_F32:.0e})")
+    assert err <= TOL_F32
+
+
 def test_scan_scores_then_prefill(kdn, orc):
     """The scan's scores feed the cache: gated delta scan with scores, then the
     prompt cache, both checked against the oracle (scores to the bf16 bar,
