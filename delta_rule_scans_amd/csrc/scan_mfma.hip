@@ -466,7 +466,9 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
           }
           st4(myM + r16 * 24 + kq * 4, acc);  // M^T[col][rows]
         }
-        __syncthreads();
+        // no barrier: M is this wavefront's own scratch (LDS accesses of one
+        // wavefront stay in order), D_i was written before the last barrier,
+        // and no wavefront reads a block of this diagonal during it
         if (active) {
           // T_ij = -D_i M
           const bool ok = kq < 2;
