@@ -27,37 +27,34 @@ namespace {
 
 constexpr int kGainBatch = 16;  // tokens whose inputs are loaded together
 
-// Map of one token on (p, 1), projectively: p_new = (m00 p + m01) / (m10 p + m11).
-// From p- = a^2 p + Q and p_new = r p- / (k^2 p- + r). All entries are >= 0,
-// so products never cancel.
-__device__ __forceinline__ void token_map(float a, float qvar, float r, float kv, float& t00,
-                                          float& t01, float& t10, float& t11) {
-  const float a2 = a * a;
-  const float Q = (1.f - a) * (1.f + a) * qvar;
-  const float k2 = kv * kv;
-  t00 = r * a2;
-  t01 = r * Q;
-  t10 = k2 * a2;
-  t11 = fmaf(k2, Q, r);
-}
-
+// One workgroup per (head, chunk), thread i = coordinate i: the composite of
+// the chunk's token maps. The map of one token on (p, 1), projectively, is
+// p_new = (m00 p + m01) / (m10 p + m11) with, from p- = a^2 p + Q and
+// p_new = r p- / (k^2 p- + r): m00 = r a^2, m01 = r Q, m10 = k^2 a^2,
+// m11 = k^2 Q + r. All entries are >= 0, so products never cancel.
 template <typename Tk>
 __global__ __launch_bounds__(128) void diag_maps_kernel(const Tk* k, const float* alpha,
                                                         const float* r, float qvar, float4* maps,
                                                         int L, int dk, int C, int nchunks) {
-  __shared__ float sa[64], sr[64];
+  // per token: r a^2, r Q, a^2, Q and r (what of the map does not depend on
+  // the key); tokens past the sequence get the identity map
+  __shared__ float4 sp[64];
+  __shared__ float sr[64];
   const int bh = blockIdx.x, c = blockIdx.y, i = threadIdx.x;
   const int t0 = c * C, n = min(C, L - t0);
-  if (i < n) {
-    const size_t g = (size_t)bh * L + t0 + i;
-    sa[i] = alpha ? alpha[g] : 1.f;
-    sr[i] = r ? r[g] : 1.f;
+  if (i < 64) {
+    const bool in = i < n;
+    const size_t g = (size_t)bh * L + t0 + min(i, n - 1);
+    const float a = in && alpha ? alpha[g] : 1.f, rt = in && r ? r[g] : 1.f;
+    const float a2 = a * a, Q = (1.f - a) * (1.f + a) * qvar;
+    sp[i] = in ? make_float4(rt * a2, rt * Q, a2, Q) : make_float4(1.f, 0.f, 0.f, 0.f);
+    sr[i] = rt;
   }
   __syncthreads();
   if (i >= dk) return;
   float m00 = 1.f, m01 = 0.f, m10 = 0.f, m11 = 1.f;
   // k of a batch of tokens loaded together (tokens past the chunk read token
-  // n - 1 and are not used): one memory latency per batch
+  // n - 1 and then count as zero: with their identity map they change nothing)
   for (int tb = 0; tb < n; tb += kGainBatch) {
     float kv[kGainBatch];
 #pragma unroll
@@ -65,20 +62,18 @@ __global__ __launch_bounds__(128) void diag_maps_kernel(const Tk* k, const float
       kv[u] = Elem<Tk>::load(k, ((size_t)bh * L + t0 + min(tb + u, n - 1)) * dk + i);
 #pragma unroll
     for (int u = 0; u < kGainBatch; ++u) {
-      // every token of the batch is formed (t < 64 stays inside sa, sr); only
-      // those inside the chunk are applied, so the loads stay ahead of all uses
-      const int t = tb + u;
-      const bool in = t < n;
-      float t00, t01, t10, t11;
-      token_map(sa[t], qvar, sr[t], kv[u], t00, t01, t10, t11);
-      const float n00 = fmaf(t00, m00, t01 * m10), n01 = fmaf(t00, m01, t01 * m11);
+      const int t = tb + u;  // < 64: inside sp, sr
+      const float4 tp = sp[t];
+      const float k2 = t < n ? kv[u] * kv[u] : 0.f;
+      const float t10 = k2 * tp.z, t11 = fmaf(k2, tp.w, sr[t]);
+      const float n00 = fmaf(tp.x, m00, tp.y * m10), n01 = fmaf(tp.x, m01, tp.y * m11);
       const float n10 = fmaf(t10, m00, t11 * m10), n11 = fmaf(t10, m01, t11 * m11);
       // projective scale: any positive factor will do, so an approximate reciprocal
       const float sc = __builtin_amdgcn_rcpf(fmaxf(fmaxf(n00, n01), fmaxf(n10, n11)));
-      m00 = in ? n00 * sc : m00;
-      m01 = in ? n01 * sc : m01;
-      m10 = in ? n10 * sc : m10;
-      m11 = in ? n11 * sc : m11;
+      m00 = n00 * sc;
+      m01 = n01 * sc;
+      m10 = n10 * sc;
+      m11 = n11 * sc;
     }
   }
   maps[((size_t)bh * nchunks + c) * dk + i] = make_float4(m00, m01, m10, m11);
@@ -439,6 +434,64 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(const float* cov_in, f
   }
 }
 
+// The same scan for the diagonal write with d_k a multiple of 64, laid out for
+// coalesced rows: one workgroup of kPfxWaves wavefronts per (head, 64
+// coordinates), lane = coordinate, so each chunk's maps are one contiguous row
+// of 64 float4. The chunks go in passes of kPfxWaves x kPfxRun: wavefront g
+// composes the maps of its kPfxRun chunks, the composites meet in LDS, the
+// wavefront carries the variance to its first chunk through the composites of
+// the wavefronts before it and then through its own chunks, writing each
+// chunk's starting variance over the map's first entry; the variance after
+// the pass goes through all composites.
+constexpr int kPfxWaves = 8, kPfxRun = 16;
+__device__ __forceinline__ float mob_apply(Mob x, float p) {
+  return fmaf(x.a, p, x.b) / fmaf(x.c, p, x.d);
+}
+__global__ __launch_bounds__(64 * kPfxWaves) void prefix_rows_kernel(const float* cov_in, float4* maps,
+                                                                    int dk, int nchunks) {
+  __shared__ Mob sAcc[kPfxWaves][64];
+  const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int groups = dk / 64;
+  const int bh = blockIdx.x / groups, i = (blockIdx.x - bh * groups) * 64 + lane;
+  float p = cov_in[(size_t)bh * dk + i];
+  float4* m = maps + (size_t)bh * nchunks * dk + i;
+  for (int c0 = 0; c0 < nchunks; c0 += kPfxWaves * kPfxRun) {
+    const int cb = c0 + g * kPfxRun;
+    Mob run[kPfxRun];
+#pragma unroll
+    for (int j = 0; j < kPfxRun; ++j) {
+      const float4 v = cb + j < nchunks ? m[(size_t)(cb + j) * dk] : make_float4(1.f, 0.f, 0.f, 1.f);
+      run[j] = Mob{v.x, v.y, v.z, v.w};
+    }
+    Mob acc = run[0];
+#pragma unroll
+    for (int j = 1; j < kPfxRun; ++j) acc = mob_mul(run[j], acc);
+    sAcc[g][lane] = acc;
+    __syncthreads();
+    float pg = p;
+    for (int h = 0; h < g; ++h) pg = mob_apply(sAcc[h][lane], pg);
+#pragma unroll
+    for (int j = 0; j < kPfxRun; ++j) {
+      if (cb + j < nchunks) m[(size_t)(cb + j) * dk].x = pg;
+      pg = mob_apply(run[j], pg);
+    }
+#pragma unroll
+    for (int h = 0; h < kPfxWaves; ++h) p = mob_apply(sAcc[h][lane], p);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_prefix_diag(const float* cov_in, float* maps, int BH, int dk, int nchunks,
+                              hipStream_t s) {
+  if (dk % 64 == 0)
+    KDN_LAUNCH(prefix_rows_kernel, dim3(BH * (dk / 64)), dim3(64 * kPfxWaves), 0, s, cov_in,
+               reinterpret_cast<float4*>(maps), dk, nchunks);
+  else
+    KDN_LAUNCH(prefix_scan_kernel, dim3((BH * dk + 3) / 4), dim3(256), 0, s, cov_in,
+               reinterpret_cast<float4*>(maps), BH * dk, dk, nchunks);
+  return hipGetLastError();
+}
+
 // One wavefront per (head, chunk), lane t = token t: the variance before the
 // token from the chunk's starting p (prefix_scan_kernel) and an exclusive scan
 // of the token maps, then the write strength beta_t.
@@ -701,9 +754,7 @@ hipError_t diag_typed(const void* k, const float* alpha, const float* r, const f
                      dk, C, nchunks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  KDN_LAUNCH(prefix_scan_kernel, dim3((BH * dk + 3) / 4), dim3(256), 0, s, cov_in,
-                     reinterpret_cast<float4*>(maps), BH * dk, dk, nchunks);
-  e = hipGetLastError();
+  e = launch_prefix_diag(cov_in, maps, BH, dk, nchunks, s);
   if (e != hipSuccess) return e;
   if constexpr (std::is_same<Tk, uint16_t>::value && std::is_same<Tg, _Float16>::value) {
     if (dk == 128) {
@@ -748,6 +799,23 @@ hipError_t launch_diag_gains(const void* k, bool k_bf16, const float* alpha, con
                                                   maps, BH, L, dk, chunk, s, pprev, sden)
                     : diag_typed<float, float>(k, alpha, r, cov_in, cov_out, q_noise_var, gains,
                                                maps, BH, L, dk, chunk, s, pprev, sden);
+}
+
+hipError_t launch_diag_starts(const void* k, bool k_bf16, const float* alpha, const float* r,
+                              const float* cov_in, float q_noise_var, float* maps, int BH, int L,
+                              int dk, int chunk, hipStream_t s) {
+  const int nchunks = (L + chunk - 1) / chunk;
+  if (k_bf16)
+    KDN_LAUNCH(diag_maps_kernel<uint16_t>, dim3(BH, nchunks), dim3(128), 0, s,
+               static_cast<const uint16_t*>(k), alpha, r, q_noise_var,
+               reinterpret_cast<float4*>(maps), L, dk, chunk, nchunks);
+  else
+    KDN_LAUNCH(diag_maps_kernel<float>, dim3(BH, nchunks), dim3(128), 0, s,
+               static_cast<const float*>(k), alpha, r, q_noise_var, reinterpret_cast<float4*>(maps),
+               L, dk, chunk, nchunks);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_prefix_diag(cov_in, maps, BH, dk, nchunks, s);
 }
 
 hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const float* r,

@@ -83,7 +83,10 @@ WsLayout ws_layout(int B, int H, int L, int dk, int dv, int chunk, int mode, int
   if (L <= 0) return w;
   const size_t BH = (size_t)B * H;
   const size_t nchunks = ((size_t)L + chunk - 1) / chunk;
-  if (mode == KDN_GAIN_DIAG) w.maps_bytes = BH * nchunks * dk * 4 * sizeof(float);
+  // the diagonal write on the matrix-core path scans half chunks
+  const size_t nmaps = use_mfma_path(in_dtype, dk, dv, chunk) ? ((size_t)L + chunk / 2 - 1) / (chunk / 2)
+                                                               : nchunks;
+  if (mode == KDN_GAIN_DIAG) w.maps_bytes = BH * nmaps * dk * 4 * sizeof(float);
   if (mode == KDN_GAIN_ISO) w.maps_bytes = BH * nchunks * 4 * sizeof(float);
   if (mode == KDN_GAIN_DIAG || mode == KDN_GAIN_FULL)
     w.gains_bytes = BH * (size_t)L * dk * (in_dtype == KDN_BF16 ? 2 : 4);
@@ -231,7 +234,20 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
         reinterpret_cast<float*>(base + ws.maps_off), BH, L, d_k, chunk, s);
     if (e != hipSuccess) return map_hip(e);
   }
-  if (do_prep && has_gain) {
+  const bool mfma_ok = use_mfma_path(in_dtype, d_k, d_v, chunk) && aligned16(q) &&
+                       aligned16(k) && aligned16(v) && aligned16(o) &&
+                       (gains == nullptr || aligned16(gains));
+  // the diagonal write on the matrix-core path: the covariance scan over half
+  // chunks gives their starting variances and the prepare kernel forms the
+  // gains from them
+  const bool diag_fused = mode == KDN_GAIN_DIAG && mfma_ok;
+  if (do_prep && diag_fused) {
+    const hipError_t e = kdn::launch_diag_starts(
+        k, in_bf16, alpha, r, cov_in, q_noise_var,
+        reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.maps_off), BH, L, d_k,
+        chunk / 2, s);
+    if (e != hipSuccess) return map_hip(e);
+  } else if (do_prep && has_gain) {
     char* base = static_cast<char*>(workspace);
     void* g = base + ws.gains_off;
     hipError_t e;
@@ -263,10 +279,14 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   a.plain = resid == KDN_RESID_PLAIN ? 1 : 0;
   a.noerase = resid == KDN_RESID_NOERASE ? 1 : 0;
 
+  if (diag_fused) {
+    a.dmaps = reinterpret_cast<const float*>(static_cast<char*>(workspace) + ws.maps_off);
+    a.r = r;
+    a.qvar = q_noise_var;
+    a.cov_out = cov_out;
+  }
+
   const bool out_bf16 = out_dtype == KDN_BF16;
-  const bool mfma_ok = use_mfma_path(in_dtype, d_k, d_v, chunk) && aligned16(q) &&
-                       aligned16(k) && aligned16(v) && aligned16(o) &&
-                       (gains == nullptr || aligned16(gains));
   kdn::trace_call("kdn_scan_fwd phase %d B %d H %d L %d d_k %d d_v %d chunk %d mode %d resid %d "
                   "in %s -> %s path", phase, B, H, L, d_k, d_v, chunk, mode, resid,
                   in_bf16 ? "bf16" : "f32", mfma_ok ? "matrix-core" : "float32");

@@ -193,31 +193,48 @@ struct PrepArgs {
   unsigned char* rec;     // [BH, nchunks] records of rec_bytes(gain)
   int L, nchunks, plain, noerase;
   int cpw;                // consecutive chunks per workgroup
+  // diagonal Kalman write with its gains formed here (else null): the starting
+  // variances (.x) of every half chunk [BH, nsub, DK], observation noise
+  // [BH, L] (null: 1), process noise variance, the fp16 gains written out
+  // [BH, L, DK], and the variances after the last token [BH, DK] (or null)
+  int nsub = 0;
+  const float4* dmaps = nullptr;
+  const float* r = nullptr;
+  float qvar = 0.f;
+  _Float16* gain_out = nullptr;
+  float* cov_out = nullptr;
 };
 
 constexpr int kAdP = 17;  // fp32 pitch of the diagonal blocks of A
 constexpr int kPrepR1 = (C * KP > 2 * C * CP ? C * KP : 2 * C * CP) * 2;  // sQ, later sT + sTt
 
 // The delta write stages only K, which then shares the first region with T.
-size_t prep_lds_bytes(bool gain) {
+// The diagonal Kalman write with its gains formed here adds a token array.
+size_t prep_lds_bytes(bool gain, bool diagf = false) {
   return (size_t)kPrepR1 + (gain ? (size_t)2 * C * KP * 2 : 0) +
          (size_t)C * CP * 2 + (size_t)4 * 16 * kAdP * 4 + (size_t)4 * 16 * 24 * 2 +
-         (size_t)3 * C * 4;
+         (size_t)3 * C * 4 + (diagf ? (size_t)C * 4 : 0);
 }
+// fp32 pitch of the per-(token, coordinate) terms p-_i k_i^2 summed for the
+// gain denominators (they borrow the region from the gains tile to the end of
+// the per-wavefront scratch)
+constexpr int kKuP = DK + 1;
 
 // One chunk's inputs in registers: this thread's four 16-byte pieces of K
-// (and of Q and the gains), and token `lane`'s alpha and beta.
+// (and of Q and the gains), token `lane`'s alpha and beta (and r), and with
+// the gains formed here the variance of coordinate tid mod d_k at the start of
+// half tid / d_k of the chunk.
 template <bool GAIN>
 struct PrepIn {
   uint4 k[4], q[GAIN ? 4 : 1], g[GAIN ? 4 : 1];
-  float al, be;
+  float al, be, rn, pv;
 };
 
 // Loads chunk cc of head bh through buffer descriptors over the head's rows:
 // rows past the sequence read as zero, and so does every load when `has` is
 // false (descriptor range 0, no memory access). No load sits behind a branch,
 // which keeps the compiler's wait counts exact.
-template <bool GAIN>
+template <bool GAIN, bool DIAGF>
 __device__ __forceinline__ void prep_load(const PrepArgs& a, int bh, int cc, bool has, int tid, int lane,
                                           PrepIn<GAIN>& x) {
   const size_t head_tok = (size_t)bh * a.L;
@@ -230,9 +247,11 @@ __device__ __forceinline__ void prep_load(const PrepArgs& a, int bh, int cc, boo
     x.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
     if (GAIN) {
       const __amdgpu_buffer_rsrc_t rq = make_rsrc(a.q + head_tok * DK, rows);
-      const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gain + head_tok * DK, rows);
       x.q[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0));
-      x.g[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+      if (!DIAGF) {
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gain + head_tok * DK, rows);
+        x.g[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rg, off, 0, 0));
+      }
     }
   }
   const int toff = (cc * C + lane) * 4;
@@ -240,12 +259,24 @@ __device__ __forceinline__ void prep_load(const PrepArgs& a, int bh, int cc, boo
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.beta + (a.beta ? head_tok : 0), has && a.beta ? (size_t)a.L * 4 : 0);
   x.al = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(ra, toff, 0, 0));
   x.be = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rb, toff, 0, 0));
+  if (DIAGF) {
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(a.r + (a.r ? head_tok : 0), has && a.r ? (size_t)a.L * 4 : 0);
+    x.rn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, toff, 0, 0));
+    // a half past the sequence reads zero (its tokens are all padding)
+    const __amdgpu_buffer_rsrc_t rm =
+        make_rsrc(a.dmaps + (size_t)bh * a.nsub * DK, has ? (size_t)a.nsub * DK * 16 : 0);
+    x.pv = __builtin_bit_cast(
+        float, __builtin_amdgcn_raw_buffer_load_b32(rm, ((2 * cc + (tid >> 7)) * DK + (tid & (DK - 1))) * 16, 0, 0));
+  } else {
+    x.rn = x.pv = 0.f;
+  }
 }
 
-template <bool GAIN>
+template <bool GAIN, bool DIAGF>
 __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   extern __shared__ __align__(16) unsigned char lds_raw[];
   constexpr bool gain = GAIN;
+  static_assert(GAIN || !DIAGF, "the gains are formed here only for the diagonal Kalman write");
   unsigned char* p = lds_raw;
   _Float16* sQ = reinterpret_cast<_Float16*>(p);   // [C][KP] (phases 1-2)
   _Float16* sT = reinterpret_cast<_Float16*>(p);   // [C][CP] (phases 3-5, reuses sQ)
@@ -269,21 +300,30 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   float* sLg = reinterpret_cast<float*>(p);        // [C] log2 of g
   float* sBs = sLg + C;                            // [C] write scale
   float* sLgx = sBs + C;                           // [C] log2 of g_x (rows of A)
+  // diagonal Kalman write, gains formed here: per token sum_i p-_i k_i^2, and
+  // the terms of those sums (they borrow the gains tile and what follows it)
+  float* sSd = sLgx + C;                           // [C]
+  float* sKu = reinterpret_cast<float*>(sB);       // [C][kKuP] p-_i k_i^2 (before the Grams)
+  static_assert(C * kKuP * 4 <= C * KP * 2 + C * CP * 2 + 4 * 16 * kAdP * 4 + 4 * 16 * 24 * 2,
+                "the terms of the gain denominators fit from the gains tile to the token arrays");
 
   const int bh = blockIdx.x;
   const int cbeg = blockIdx.y * a.cpw, cend = min(cbeg + a.cpw, a.nchunks);
 
   PrepIn<GAIN> in;
-  prep_load<GAIN>(a, bh, cbeg, true, threadIdx.x, threadIdx.x & 63, in);
+  prep_load<GAIN, DIAGF>(a, bh, cbeg, true, threadIdx.x, threadIdx.x & 63, in);
   // As many stores as a chunk issues after its next chunk's loads (3 scalar
-  // pieces, 2 rounds of T and P pieces), all dropped (range 0): the wait for a
+  // pieces, 2 rounds of T and P pieces; with the gains formed here 4 pieces of
+  // gains and a variance), all dropped (range 0): the wait for a
   // chunk's inputs is then the same on entry as around the loop, and the
   // compiler does not fall back to waiting for every store in flight.
   {
     const __amdgpu_buffer_rsrc_t none = make_rsrc(a.rec, 0);
     const v4u32 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 3 + 2 * (GAIN ? 2 : 1); ++i) __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
+    for (int i = 0; i < 3 + 2 * (GAIN ? 2 : 1) + (DIAGF ? 4 : 0); ++i)
+      __builtin_amdgcn_raw_buffer_store_b128(z, none, 0, 0, 0);
+    if (DIAGF) __builtin_amdgcn_raw_buffer_store_b32(0u, none, 0, 0, 0);
   }
   for (int c = cbeg; c < cend; ++c) {
     // The lane index passes through an empty asm statement each chunk: the
@@ -306,11 +346,11 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
       *reinterpret_cast<uint4*>(sK + row * KP + c8 * 8) = bf16x8_to_f16x8(in.k[i]);
       if (GAIN) {
         *reinterpret_cast<uint4*>(sQ + row * KP + c8 * 8) = bf16x8_to_f16x8(in.q[GAIN ? i : 0]);
-        *reinterpret_cast<uint4*>(sB + row * KP + c8 * 8) = in.g[GAIN ? i : 0];
+        if (!DIAGF) *reinterpret_cast<uint4*>(sB + row * KP + c8 * 8) = in.g[GAIN ? i : 0];
       }
     }
-    const float al_in = in.al, be_in = in.be;
-    prep_load<GAIN>(a, bh, c + 1, c + 1 < cend, tid, lane, in);
+    const float al_in = in.al, be_in = in.be, rn_in = in.rn, pv_in = in.pv;
+    prep_load<GAIN, DIAGF>(a, bh, c + 1, c + 1 < cend, tid, lane, in);
     // Every wavefront forms the scalars (token = lane); wavefront 0 keeps them
     // in LDS and stores them. The record is written through buffer stores
     // that every wavefront issues, the others at an offset past the record
@@ -354,6 +394,76 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
       __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s2), rr, so + 32, 0, 0);
     }
     __syncthreads();
+
+    if constexpr (DIAGF) {
+      // The diagonal Kalman gains of this chunk ("Kalman Delta Networks",
+      // abstract: the mean-field diagonal covariance), as the separate gains
+      // kernel forms them. Lane i of wavefronts 0 and 1 carries coordinate i's
+      // variance through the first half of the chunk's tokens, wavefronts 2
+      // and 3 through the second half, each from the variance the covariance
+      // scan gives at the start of its half (p- = a^2 p + Q, u = p- k,
+      // p = p- r / (r + p- k^2)). The denominators s_t = r_t + sum_i p-_i k_i^2
+      // are summed through LDS; the gains u_t / s_t go to the write-vector tile
+      // and to the gains buffer. The per-token scalars are read across lanes
+      // (token = lane in every wavefront), the keys from the staged tile.
+      constexpr int TH = C / 2;
+      const int ci = 64 * (wave & 1) + lane, t0h = TH * (wave >> 1);
+      // tokens past the sequence: alpha = r = 1 and no process noise (their
+      // zero keys then leave p alone)
+      const float al = lane < n && a.alpha ? al_in : 1.f;
+      const float a2l = al * al, qnl = (1.f - al) * (1.f + al) * a.qvar;
+      const float rl = lane < n && a.r ? rn_in : 1.f;
+      float kf[TH], u[TH];
+#pragma unroll
+      for (int t = 0; t < TH; ++t) kf[t] = (float)sK[(t0h + t) * KP + ci];
+      float pv = pv_in;
+#pragma unroll
+      for (int t = 0; t < TH; ++t) {
+        const float a2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a2l), t0h + t));
+        const float qn = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, qnl), t0h + t));
+        const float rt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rl), t0h + t));
+        const float pm = fmaf(a2, pv, qn);
+        u[t] = pm * kf[t];
+        pv = pm * rt * __builtin_amdgcn_rcpf(fmaf(u[t], kf[t], rt));
+      }
+#pragma unroll
+      for (int t = 0; t < TH; ++t) sKu[(t0h + t) * kKuP + ci] = u[t] * kf[t];
+      {  // the variances after the sequence's last token: from the half that holds it
+        const bool last = c == a.nchunks - 1 && (wave >> 1) == (n - 1) / TH;
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(a.cov_out + (a.cov_out ? (size_t)bh * DK : 0), a.cov_out ? (size_t)DK * 4 : 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(pv), rc, last ? ci * 4 : kDrop, 0, 0);
+      }
+      __syncthreads();
+      {  // sum_i p-_i k_i^2: four lanes per token
+        const int t = tid >> 2, part = tid & 3;
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < DK / 4; ++j) sum += sKu[t * kKuP + part + 4 * j];
+        sum += __shfl_xor(sum, 1, 64);
+        sum += __shfl_xor(sum, 2, 64);
+        if (part == 0) sSd[t] = sum;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < TH; ++t) {
+        const float rt = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rl), t0h + t));
+        // reciprocal by v_rcp_f32 (1 ulp), as in the gains kernel
+        sB[(t0h + t) * KP + ci] = (_Float16)(u[t] * __builtin_amdgcn_rcpf(rt + sSd[t0h + t]));
+      }
+      __syncthreads();
+      {  // gains rows to the buffer the state kernel reads (rows past the sequence dropped)
+        const size_t head_tok = (size_t)bh * a.L;
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(a.gain_out + head_tok * DK, (size_t)a.L * DK * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int seg = tid + NT * i, row = seg >> 4, c8 = seg & 15;
+          const uint4 gv = *reinterpret_cast<const uint4*>(sB + row * KP + c8 * 8);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, gv), rg,
+                                                 ((c * C + row) * DK + c8 * 8) * 2, 0, 0);
+        }
+      }
+    }
 
     // phase 2: 20 lower Gram tiles, A (tiles 0-9) from K and P (tiles 10-19) from Q;
     // wavefront w takes tiles w, w + 4, ..., w + 16.
@@ -1728,13 +1838,22 @@ hipError_t launch_tinv_mfma(const ScanArgs& s, void* tbuf, hipStream_t st) {
   pa.plain = s.plain;
   pa.noerase = s.noerase;
   pa.cpw = prep_chunks_per_workgroup(s.BH, nchunks);
-  const size_t lds = prep_lds_bytes(gain);
-  auto kern = gain ? prep_kernel<true> : prep_kernel<false>;
+  const bool diagf = s.dmaps != nullptr;
+  if (diagf) {
+    pa.nsub = (s.L + C / 2 - 1) / (C / 2);
+    pa.dmaps = reinterpret_cast<const float4*>(s.dmaps);
+    pa.r = s.r;
+    pa.qvar = s.qvar;
+    pa.gain_out = static_cast<_Float16*>(const_cast<void*>(s.gain));
+    pa.cov_out = s.cov_out;
+  }
+  const size_t lds = prep_lds_bytes(gain, diagf);
+  auto kern = diagf ? prep_kernel<true, true> : gain ? prep_kernel<true, false> : prep_kernel<false, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  KDN_LAUNCH_NAMED(gain ? "prep_kernel<true>" : "prep_kernel<false>", kern,
-                   dim3(s.BH, (nchunks + pa.cpw - 1) / pa.cpw), dim3(NT), lds, st, pa);
+  KDN_LAUNCH_NAMED(diagf ? "prep_kernel<true> (diagonal gains)" : gain ? "prep_kernel<true>" : "prep_kernel<false>",
+                   kern, dim3(s.BH, (nchunks + pa.cpw - 1) / pa.cpw), dim3(NT), lds, st, pa);
   return hipGetLastError();
 }
 

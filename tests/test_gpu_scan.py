@@ -27,9 +27,8 @@ def _scan_gpu(kdn, inp, dtype, chunk, mode="delta", resid="gated", cov0=None, qv
     q, k, v = (dev_tensor(inp[n], dtype) for n in ("q", "k", "v"))
     B, H, L, dk = inp["q"].shape
     dv = inp["v"].shape[-1]
-    alpha = dev_tensor(inp["alpha"])
-    beta = dev_tensor(inp["beta"])
-    r = dev_tensor(inp["r"]) if inp.get("r") is not None else None
+    alpha, beta, r = (dev_tensor(inp[n]) if inp.get(n) is not None else None
+                      for n in ("alpha", "beta", "r"))
     cov_in = dev_tensor(cov0) if cov0 is not None else None
     cov_out = torch.empty_like(cov_in) if cov0 is not None else None
     s_in = dev_tensor(S0) if S0 is not None else None
@@ -317,6 +316,29 @@ def test_diag_kalman_small(kdn, orc, dtype):
     f32 = _scan_gpu(kdn, inp, dtype, 64, mode="diag", cov0=p0, qvar=1.0, out_dtype="f32", want_state=False)
     b16 = _scan_gpu(kdn, inp, dtype, 64, mode="diag", cov0=p0, qvar=1.0, out_dtype="bf16", want_state=False)
     np.testing.assert_array_equal(b16["o"], workloads.bf16_round(f32["o"].astype(np.float32)))
+
+
+@pytest.mark.parametrize("given", [False, True])
+def test_diag_kalman_spread_variances(kdn, orc, given):
+    """Diagonal Kalman write on the matrix-core path from starting variances
+    that differ per coordinate (0.05 .. 20, log-uniform), so that a coordinate
+    taken for another where the chunk-start variances reach the gains would
+    show; alpha and r left out (alpha = 1, r = 1: no process noise) or given.
+    B=1 H=3 L=200: four chunks, the last ragged; o, S and the final variances
+    against the oracle."""
+    B, H, L, d = 1, 3, 200, 128
+    inp = workloads.scan_inputs(B, H, L, d, d, seed=131, dtype="bf16", with_r=True)
+    if not given:
+        inp["alpha"] = None
+        inp["r"] = None
+    rng = np.random.Generator(np.random.PCG64(131))
+    p0 = np.exp(rng.uniform(np.log(0.05), np.log(20.0), (B, H, d))).astype(np.float32)
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"], cov0=p0,
+                   q_noise_var=0.5, mode="diag")
+    got = _scan_gpu(kdn, inp, "bf16", 64, mode="diag", cov0=p0, qvar=0.5)
+    assert_close(got["o"], ref["o"], TOL_BF16, "diag o")
+    assert_close(got["S"], ref["S"], TOL_BF16, "diag S")
+    assert_close(got["cov"], ref["cov"], TOL_F32, "diag p")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
