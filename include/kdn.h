@@ -100,7 +100,8 @@ int kdn_version(void);
 
 /*
  * Bytes of device workspace kdn_scan_fwd needs for these arguments: the
- * per-token Kalman gains and per-chunk covariance maps (Kalman modes), on the
+ * per-token Kalman gains and covariance maps per chunk (per half chunk for the
+ * diagonal write on the matrix-core path) (Kalman modes), on the
  * matrix-core path the per-chunk records of the chunk form ((I + A)^-1 and
  * token scalars), and with with_scores != 0 room for the residuals the write
  * scores are formed from (needed when kdn_scan_fwd is given an `m` output).
