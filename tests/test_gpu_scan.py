@@ -318,15 +318,16 @@ def test_diag_kalman_small(kdn, orc, dtype):
     np.testing.assert_array_equal(b16["o"], workloads.bf16_round(f32["o"].astype(np.float32)))
 
 
-@pytest.mark.parametrize("given", [False, True])
-def test_diag_kalman_spread_variances(kdn, orc, given):
+@pytest.mark.parametrize("given,L", [(False, 200), (True, 230), (True, 192)])
+def test_diag_kalman_spread_variances(kdn, orc, given, L):
     """Diagonal Kalman write on the matrix-core path from starting variances
     that differ per coordinate (0.05 .. 20, log-uniform), so that a coordinate
     taken for another where the chunk-start variances reach the gains would
     show; alpha and r left out (alpha = 1, r = 1: no process noise) or given.
-    B=1 H=3 L=200: four chunks, the last ragged; o, S and the final variances
-    against the oracle."""
-    B, H, L, d = 1, 3, 200, 128
+    B=1 H=3; the last chunk holds 8 tokens (inside its first 32-token half),
+    38 (inside its second half) or 64; o, S and the final variances against
+    the oracle."""
+    B, H, d = 1, 3, 128
     inp = workloads.scan_inputs(B, H, L, d, d, seed=131, dtype="bf16", with_r=True)
     if not given:
         inp["alpha"] = None
