@@ -342,6 +342,40 @@ def test_diag_kalman_spread_variances(kdn, orc, given, L):
     assert_close(got["cov"], ref["cov"], TOL_F32, "diag p")
 
 
+@pytest.mark.parametrize("dk", [40, 64])
+def test_diag_kalman_other_key_widths(kdn, orc, dk):
+    """Diagonal Kalman write on the float32 path with d_k = 40 (the chunk-start
+    scan with lanes as chunks) and d_k = 64 (the scan with one group of 64
+    coordinates as lanes), L = 300 (five chunks of 64, the last ragged), from
+    starting variances that differ per coordinate."""
+    B, H, L, dv = 1, 2, 300, 48
+    inp = workloads.scan_inputs(B, H, L, dk, dv, seed=140 + dk, dtype="f32", with_r=True)
+    rng = np.random.Generator(np.random.PCG64(140 + dk))
+    p0 = np.exp(rng.uniform(np.log(0.1), np.log(10.0), (B, H, dk))).astype(np.float32)
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"], cov0=p0,
+                   q_noise_var=0.7, mode="diag")
+    got = _scan_gpu(kdn, inp, "f32", 64, mode="diag", cov0=p0, qvar=0.7)
+    assert_close(got["o"], ref["o"], TOL_F32, f"diag o d_k {dk}")
+    assert_close(got["S"], ref["S"], TOL_F32, f"diag S d_k {dk}")
+    assert_close(got["cov"], ref["cov"], TOL_F32, f"diag p d_k {dk}")
+
+
+def test_diag_kalman_without_final_variances(kdn):
+    """The matrix-core diagonal write with no cov_out: the same o and state as
+    the call that asks for the final variances (they are only dropped)."""
+    import torch
+    inp = workloads.scan_inputs(1, 2, 230, 128, 128, seed=141, dtype="bf16", with_r=True)
+    p0 = np.ones((1, 2, 128), np.float32)
+    full = _scan_gpu(kdn, inp, "bf16", 64, mode="diag", cov0=p0, qvar=1.0)
+    q, k, v = (dev_tensor(inp[n], "bf16") for n in ("q", "k", "v"))
+    S = torch.empty((1, 2, 128, 128), dtype=torch.float32, device="cuda")
+    o = kdn.kdn_scan_fwd(q, k, v, alpha=dev_tensor(inp["alpha"]), r=dev_tensor(inp["r"]),
+                         cov_in=dev_tensor(p0), q_noise_var=1.0, state_out=S, mode="diag")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(o), full["o"])
+    np.testing.assert_array_equal(host(S), full["S"])
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_iso_kalman_small(kdn, orc, dtype):
     """Isotropic Kalman write (one variance per head), keys of varying norm."""
