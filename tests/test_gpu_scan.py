@@ -119,17 +119,19 @@ def test_short_sequences(kdn, orc):
 
 @pytest.mark.parametrize("mode", ["delta", "diag"])
 def test_grouped_prepare(kdn, orc, mode):
-    """Enough (head, chunk) pairs that the prepare step hands each workgroup
-    several consecutive chunks (here 4), with a chunk count the group size does
-    not divide and a ragged last chunk: B=2, H=32, L=4100 is 65 chunks, the
-    last of 4 tokens. The delta write and the diagonal Kalman write (which also
-    stages Q and the gains); the oracle on sampled heads."""
-    B, H, L, d = 2, 32, 4100, 128
+    """Enough (head, chunk) pairs (more than 16384) that the prepare step hands
+    each workgroup two consecutive chunks, the second one's inputs loading
+    while the first is computed, with a chunk count the group size does not
+    divide and a ragged last chunk: B=2, H=64, L=8196 is 129 chunks per head,
+    the last of 4 tokens, 16512 in all. The delta write and the diagonal
+    Kalman write (which also stages Q, carries each coordinate's variance
+    through the chunk and writes the gains); the oracle on sampled heads."""
+    B, H, L, d = 2, 64, 8196, 128
     diag = mode == "diag"
     inp = workloads.scan_inputs(B, H, L, d, d, seed=111, dtype="bf16", with_r=diag)
     cov0 = np.ones((B, H, d), np.float32) if diag else None
     got = _scan_gpu(kdn, inp, "bf16", 64, mode=mode, cov0=cov0, qvar=1.0 if diag else 0.0)
-    for (b, h) in [(0, 0), (1, 17), (1, 31)]:
+    for (b, h) in [(0, 0), (1, 17), (1, 63)]:
         log(f"grouped prepare {mode}: oracle on head ({b}, {h})")
         sub = {n: (x[b:b + 1, h:h + 1] if x is not None else None) for n, x in inp.items()}
         ref = orc.scan(sub["q"], sub["k"], sub["v"], alpha=sub["alpha"], beta=sub["beta"],
