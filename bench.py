@@ -46,7 +46,7 @@ def scan_flops_per_token_head(C, dk, dv):
 def scan_bytes(B, H, L, dk, dv, in_bytes=2, out_bytes=2, extra_per_token=0, state_out=True):
     """Algorithmic HBM bytes of one scan: q, k, v read once, alpha/beta (+extra)
     read once, o written once, the final state written once. The default is the
-    survey's unit for the roofline: bf16 q, k, v and o, float32 alpha and beta,
+    roofline's unit: bf16 q, k, v and o, float32 alpha and beta,
     1032 B per token and head at d = 128; out_bytes=4 gives the float32 output
     the library writes by default (1288 B)."""
     per_tok = (2 * dk + dv) * in_bytes + 8 + extra_per_token + dv * out_bytes
@@ -674,7 +674,7 @@ def main():
         kept["gated/delta"] = {k: main_res.pop(k) for k in ("o", "S")}
     B, H, L, dk, dv, C = (main_res[k] for k in ("B", "H", "L", "dk", "dv", "C"))
     token_heads = B * H * L
-    nbytes = scan_bytes(B, H, L, dk, dv)            # bf16 o: the survey's 1032 B per token-head
+    nbytes = scan_bytes(B, H, L, dk, dv)            # bf16 o: 1032 B per token-head
     nbytes_f32o = scan_bytes(B, H, L, dk, dv, out_bytes=4)
     flops = token_heads * scan_flops_per_token_head(C, dk, dv)
     state_s = main_res["state_kernel_ms"] * 1e-3
