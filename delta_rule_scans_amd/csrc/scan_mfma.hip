@@ -701,16 +701,19 @@ __device__ __forceinline__ half4 ld_tr(const _Float16* p) {
   return __builtin_bit_cast(half4, v);
 }
 
-// The delta write's output stores stream (kStreamStore, kdn_internal.h): the
-// outputs are never read back by the kernel, and keeping them out of L2 leaves
-// it to the keys, queries and records that the four d_v slices of a head share
-// (measured: its state kernel 98 against 116 us with default stores). The
-// Kalman writes' state kernel, which also reads the gain rows and the output's
-// Q rows, is faster with default stores (153 against 169 us on the diagonal
-// write at the gated workload's shape). Non-temporal loads are much slower and
-// are not used.
-template <bool GAIN>
-constexpr int out_store_policy() { return GAIN ? 0 : kStreamStore; }
+// The delta write's output stores stream on the 32-column tiling
+// (kStreamStore, kdn_internal.h): the outputs are never read back by the
+// kernel, and keeping them out of L2 leaves it to the keys, queries and
+// records that the four d_v slices of a head share (measured: its state kernel
+// 98 against 116 us with default stores). With default stores the slices'
+// pieces of each output row meet in L2 before they go to HBM instead; that
+// wins for the Kalman writes' state kernel, which also reads the gain rows and
+// the output's Q rows (153 against 169 us on the diagonal write at the gated
+// workload's shape), and for the 16-column tiling, whose eight slices store
+// 64-byte pieces of each row (the long workload's step 1.74 against 1.81 ms).
+// Non-temporal loads are much slower and are not used.
+template <bool GAIN, bool NARROW>
+constexpr int out_store_policy() { return GAIN || NARROW ? 0 : kStreamStore; }
 
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -1316,7 +1319,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
               const int off = (tok * a.dv + 8 * (pr + 2 * h)) * esz;
               // (a narrow slice holds columns 0-15 only: lanes h = 1 store nothing)
               if (!NARROW || h == 0)
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w4), ro, off, 0, out_store_policy<GAIN>());
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w4), ro, off, 0, out_store_policy<GAIN, NARROW>());
             }
           } else {
 #pragma unroll
@@ -1325,7 +1328,7 @@ __global__ __launch_bounds__(NT_STATE) void state_kernel(StateArgs a) {
               const uint4 w4 = make_uint4(__float_as_uint(o[tb][4 * q4]), __float_as_uint(o[tb][4 * q4 + 1]),
                                           __float_as_uint(o[tb][4 * q4 + 2]), __float_as_uint(o[tb][4 * q4 + 3]));
               __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, w4), ro, off, 0,
-                                                     out_store_policy<GAIN>());
+                                                     out_store_policy<GAIN, NARROW>());
             }
           }
         }
