@@ -220,6 +220,13 @@ size_t prep_lds_bytes(bool gain, bool diagf = false) {
 // the per-wavefront scratch)
 constexpr int kKuP = DK + 1;
 
+// Cache policy of the prepare kernel's stores for the Kalman writes: nt
+// (marked for early eviction). Their records and gains, 130 MB at the gated
+// workload's shape, then leave the caches to the state kernel's other reads
+// (diagonal write: 275 -> 264 us per step); the delta write keeps the default
+// policy for its records (its state kernel was 101 against 107 us).
+constexpr int kNtStore = 2;
+
 // One chunk's inputs in registers: this thread's four 16-byte pieces of K
 // (and of Q and the gains), token `lane`'s alpha and beta (and r), and with
 // the gains formed here the variance of coordinate tid mod d_k at the start of
@@ -389,9 +396,10 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
                                     lane < 32 ? bs * exp2f(lg31 - lg) : 0.f,
                                     lane >= 32 ? exp2f(lg - lg31) : 0.f);
       const float4 s2 = make_float4(vs, extreme ? 1.f : 0.f, exp2f(lg), 0.f);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s0), rr, so, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s1), rr, so + 16, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s2), rr, so + 32, 0, 0);
+      constexpr int rpol = GAIN ? kNtStore : 0;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s0), rr, so, 0, rpol);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s1), rr, so + 16, 0, rpol);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, s2), rr, so + 32, 0, rpol);
     }
     __syncthreads();
 
@@ -460,7 +468,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
           const int seg = tid + NT * i, row = seg >> 4, c8 = seg & 15;
           const uint4 gv = *reinterpret_cast<const uint4*>(sB + row * KP + c8 * 8);
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, gv), rg,
-                                                 ((c * C + row) * DK + c8 * 8) * 2, 0, 0);
+                                                 ((c * C + row) * DK + c8 * 8) * 2, 0, kNtStore);
         }
       }
     }
@@ -611,12 +619,13 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
       const bool lower = (col >> 4) <= (row >> 4);
       uint4 tv = *reinterpret_cast<const uint4*>(sT + row * CP + col);
       if (!lower) tv = make_uint4(0, 0, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, tv), rr, (int)kRecT + off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, tv), rr, (int)kRecT + off, 0,
+                                             GAIN ? kNtStore : 0);
       if (gain) {
         uint4 pv = *reinterpret_cast<const uint4*>(sP + row * CP + col);
         if (!lower) pv = make_uint4(0, 0, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32, pv), rr,
-                                               ok ? (int)rec_p_off(gain) + off : kDrop, 0, 0);
+                                               ok ? (int)rec_p_off(gain) + off : kDrop, 0, kNtStore);
       }
     }
     __syncthreads();  // the next chunk's staging overwrites sT, sP and the scalars
