@@ -17,11 +17,15 @@
 // the same form with no decay at all in the residual: A = 0, T = I, X = V.
 //
 // Two kernels:
-//  * prep_kernel: every chunk independent of the others; a workgroup takes a
-//    few consecutive chunks of one head and loads the next chunk's inputs
-//    while it computes the current one.
+//  * prep_kernel: every chunk independent of the others; a workgroup takes
+//    one chunk of one head (two consecutive ones past 16384 chunks, loading
+//    the second one's inputs while it computes the first).
 //    Everything that does not depend on the state: the per-token decay
-//    scalars g_t, w_t; the Grams K B^T and Q B^T on the matrix cores; and
+//    scalars g_t, w_t; for the diagonal Kalman write the gains themselves
+//    (each coordinate's variance carried through the chunk's two 32-token
+//    halves from the starting variances of the covariance scan, the gains
+//    written out for the state kernel); the Grams K B^T and Q B^T on the
+//    matrix cores; and
 //    T = (I + A)^-1 by blocks of 16: the four diagonal blocks are inverted in
 //    float32 registers (one wavefront per block, four lanes per column, quad
 //    reductions through DPP), the six off-diagonal blocks follow by block
