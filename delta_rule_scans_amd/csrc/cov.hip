@@ -15,9 +15,10 @@
 // run of tokens composes into one 2x2 matrix ("Kalman Delta Networks:
 // Uncertainty-aware Associative Memory", abstract, where the variance
 // recursions are identified as Moebius maps). The DIAG path uses that: one pass composes the
-// maps of every chunk in parallel, an associative scan over chunks (log depth)
-// turns them into every chunk's starting variances, and a third pass
-// recomputes the per-token values of every chunk in parallel.
+// maps of every chunk in parallel, an associative scan over chunks turns them
+// into every chunk's starting variances, and a third pass recomputes the
+// per-token values of every chunk in parallel (on the matrix-core path the
+// chunks are 32-token halves and the prepare kernel makes that third pass).
 #include <type_traits>
 
 #include "kdn_internal.h"
