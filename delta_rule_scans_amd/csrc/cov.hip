@@ -443,19 +443,22 @@ __global__ __launch_bounds__(256) void prefix_scan_kernel(const float* cov_in, f
 // wavefront carries the variance to its first chunk through the composites of
 // the wavefronts before it and then through its own chunks, writing each
 // chunk's starting variance over the map's first entry; the variance after
-// the pass goes through all composites.
-constexpr int kPfxWaves = 8, kPfxRun = 16;
+// the pass goes through all composites. With `starts` the starting variances
+// go there instead, [BH, nchunks, dk] floats (coalesced rows, the maps left
+// as they are).
+constexpr int kPfxWaves = 16, kPfxRun = 8;
 __device__ __forceinline__ float mob_apply(Mob x, float p) {
   return fmaf(x.a, p, x.b) / fmaf(x.c, p, x.d);
 }
 __global__ __launch_bounds__(64 * kPfxWaves) void prefix_rows_kernel(const float* cov_in, float4* maps,
-                                                                    int dk, int nchunks) {
+                                                                    float* starts, int dk, int nchunks) {
   __shared__ Mob sAcc[kPfxWaves][64];
   const int lane = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int groups = dk / 64;
   const int bh = blockIdx.x / groups, i = (blockIdx.x - bh * groups) * 64 + lane;
   float p = cov_in[(size_t)bh * dk + i];
   float4* m = maps + (size_t)bh * nchunks * dk + i;
+  float* st = starts ? starts + (size_t)bh * nchunks * dk + i : nullptr;
   for (int c0 = 0; c0 < nchunks; c0 += kPfxWaves * kPfxRun) {
     const int cb = c0 + g * kPfxRun;
     Mob run[kPfxRun];
@@ -473,7 +476,10 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_rows_kernel(const float
     for (int h = 0; h < g; ++h) pg = mob_apply(sAcc[h][lane], pg);
 #pragma unroll
     for (int j = 0; j < kPfxRun; ++j) {
-      if (cb + j < nchunks) m[(size_t)(cb + j) * dk].x = pg;
+      if (cb + j < nchunks) {
+        if (st) st[(size_t)(cb + j) * dk] = pg;
+        else m[(size_t)(cb + j) * dk].x = pg;
+      }
       pg = mob_apply(run[j], pg);
     }
 #pragma unroll
@@ -483,10 +489,10 @@ __global__ __launch_bounds__(64 * kPfxWaves) void prefix_rows_kernel(const float
 }
 
 hipError_t launch_prefix_diag(const float* cov_in, float* maps, int BH, int dk, int nchunks,
-                              hipStream_t s) {
+                              hipStream_t s, float* starts = nullptr) {
   if (dk % 64 == 0)
     KDN_LAUNCH(prefix_rows_kernel, dim3(BH * (dk / 64)), dim3(64 * kPfxWaves), 0, s, cov_in,
-               reinterpret_cast<float4*>(maps), dk, nchunks);
+               reinterpret_cast<float4*>(maps), starts, dk, nchunks);
   else
     KDN_LAUNCH(prefix_scan_kernel, dim3((BH * dk + 3) / 4), dim3(256), 0, s, cov_in,
                reinterpret_cast<float4*>(maps), BH * dk, dk, nchunks);
@@ -803,8 +809,9 @@ hipError_t launch_diag_gains(const void* k, bool k_bf16, const float* alpha, con
 }
 
 hipError_t launch_diag_starts(const void* k, bool k_bf16, const float* alpha, const float* r,
-                              const float* cov_in, float q_noise_var, float* maps, int BH, int L,
-                              int dk, int chunk, hipStream_t s) {
+                              const float* cov_in, float q_noise_var, float* maps, float* starts,
+                              int BH, int L, int dk, int chunk, hipStream_t s) {
+  if (dk % 64 != 0) return hipErrorInvalidValue;  // the compact starts need the row scan
   const int nchunks = (L + chunk - 1) / chunk;
   if (k_bf16)
     KDN_LAUNCH(diag_maps_kernel<uint16_t>, dim3(BH, nchunks), dim3(128), 0, s,
@@ -816,7 +823,7 @@ hipError_t launch_diag_starts(const void* k, bool k_bf16, const float* alpha, co
                L, dk, chunk, nchunks);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_prefix_diag(cov_in, maps, BH, dk, nchunks, s);
+  return launch_prefix_diag(cov_in, maps, BH, dk, nchunks, s, starts);
 }
 
 hipError_t launch_iso_beta(const void* k, bool k_bf16, const float* alpha, const float* r,

@@ -83,10 +83,11 @@ WsLayout ws_layout(int B, int H, int L, int dk, int dv, int chunk, int mode, int
   if (L <= 0) return w;
   const size_t BH = (size_t)B * H;
   const size_t nchunks = ((size_t)L + chunk - 1) / chunk;
-  // the diagonal write on the matrix-core path scans half chunks
-  const size_t nmaps = use_mfma_path(in_dtype, dk, dv, chunk) ? ((size_t)L + chunk / 2 - 1) / (chunk / 2)
-                                                               : nchunks;
-  if (mode == KDN_GAIN_DIAG) w.maps_bytes = BH * nmaps * dk * 4 * sizeof(float);
+  // the diagonal write on the matrix-core path scans half chunks and keeps
+  // their starting variances after the maps
+  const bool half = use_mfma_path(in_dtype, dk, dv, chunk);
+  const size_t nmaps = half ? ((size_t)L + chunk / 2 - 1) / (chunk / 2) : nchunks;
+  if (mode == KDN_GAIN_DIAG) w.maps_bytes = BH * nmaps * dk * (half ? 5 : 4) * sizeof(float);
   if (mode == KDN_GAIN_ISO) w.maps_bytes = BH * nchunks * 4 * sizeof(float);
   if (mode == KDN_GAIN_DIAG || mode == KDN_GAIN_FULL)
     w.gains_bytes = BH * (size_t)L * dk * (in_dtype == KDN_BF16 ? 2 : 4);
@@ -241,11 +242,15 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   // chunks gives their starting variances and the prepare kernel forms the
   // gains from them
   const bool diag_fused = mode == KDN_GAIN_DIAG && mfma_ok;
+  float* diag_maps = nullptr;    // [BH, half chunks, d_k] float4, then
+  float* diag_starts = nullptr;  // [BH, half chunks, d_k] starting variances
+  if (diag_fused) {
+    diag_maps = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.maps_off);
+    diag_starts = diag_maps + (size_t)BH * ((L + chunk / 2 - 1) / (chunk / 2)) * d_k * 4;
+  }
   if (do_prep && diag_fused) {
-    const hipError_t e = kdn::launch_diag_starts(
-        k, in_bf16, alpha, r, cov_in, q_noise_var,
-        reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.maps_off), BH, L, d_k,
-        chunk / 2, s);
+    const hipError_t e = kdn::launch_diag_starts(k, in_bf16, alpha, r, cov_in, q_noise_var,
+                                                 diag_maps, diag_starts, BH, L, d_k, chunk / 2, s);
     if (e != hipSuccess) return map_hip(e);
   } else if (do_prep && has_gain) {
     char* base = static_cast<char*>(workspace);
@@ -280,7 +285,7 @@ KDN_EXPORT int kdn_scan_fwd_phase(int phase, const void* q, const void* k, const
   a.noerase = resid == KDN_RESID_NOERASE ? 1 : 0;
 
   if (diag_fused) {
-    a.dmaps = reinterpret_cast<const float*>(static_cast<char*>(workspace) + ws.maps_off);
+    a.dmaps = diag_starts;
     a.r = r;
     a.qvar = q_noise_var;
     a.cov_out = cov_out;

@@ -109,7 +109,7 @@ struct ScanArgs {
   void* ubuf = nullptr;
   // Diagonal Kalman write on the matrix-core path with the gains formed by the
   // prepare kernel (else null): the variances at the start of every half chunk
-  // (launch_diag_starts with chunk / 2),
+  // ([BH, half chunks, dk] floats from launch_diag_starts with chunk / 2),
   // r [BH, L] (null: 1), the process noise variance and the final variances
   // [BH, dk] (or null); the gains go to `gain`, which the state kernel reads.
   const float* dmaps = nullptr;
@@ -185,11 +185,12 @@ hipError_t launch_diag_gains(const void* k, bool k_bf16, const float* alpha, con
                              int chunk, hipStream_t s, float* pprev = nullptr,
                              float* sden = nullptr);
 // The first two passes of launch_diag_gains only: every chunk's starting
-// variances, in the first entry of each map of `maps` ([BH, nchunks, dk]
-// float4). The matrix-core prepare kernel then forms the gains itself.
+// variances into `starts` ([BH, nchunks, dk] floats); `maps` is scratch of
+// BH * nchunks * dk float4. d_k must be a multiple of 64. The matrix-core
+// prepare kernel then forms the gains itself.
 hipError_t launch_diag_starts(const void* k, bool k_bf16, const float* alpha, const float* r,
-                              const float* cov_in, float q_noise_var, float* maps, int BH, int L,
-                              int dk, int chunk, hipStream_t s);
+                              const float* cov_in, float q_noise_var, float* maps, float* starts,
+                              int BH, int L, int dk, int chunk, hipStream_t s);
 
 // Isotropic Kalman write: the per-token write strengths beta [BH, L] (the gain
 // is beta_t k_t) and the final variance [BH]. `kk` is scratch of BH * L floats,

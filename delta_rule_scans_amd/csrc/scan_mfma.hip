@@ -198,11 +198,11 @@ struct PrepArgs {
   int L, nchunks, plain, noerase;
   int cpw;                // consecutive chunks per workgroup
   // diagonal Kalman write with its gains formed here (else null): the starting
-  // variances (.x) of every half chunk [BH, nsub, DK], observation noise
+  // variances of every half chunk [BH, nsub, DK], observation noise
   // [BH, L] (null: 1), process noise variance, the fp16 gains written out
   // [BH, L, DK], and the variances after the last token [BH, DK] (or null)
   int nsub = 0;
-  const float4* dmaps = nullptr;
+  const float* dmaps = nullptr;
   const float* r = nullptr;
   float qvar = 0.f;
   _Float16* gain_out = nullptr;
@@ -275,9 +275,9 @@ __device__ __forceinline__ void prep_load(const PrepArgs& a, int bh, int cc, boo
     x.rn = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rr, toff, 0, 0));
     // a half past the sequence reads zero (its tokens are all padding)
     const __amdgpu_buffer_rsrc_t rm =
-        make_rsrc(a.dmaps + (size_t)bh * a.nsub * DK, has ? (size_t)a.nsub * DK * 16 : 0);
+        make_rsrc(a.dmaps + (size_t)bh * a.nsub * DK, has ? (size_t)a.nsub * DK * 4 : 0);
     x.pv = __builtin_bit_cast(
-        float, __builtin_amdgcn_raw_buffer_load_b32(rm, ((2 * cc + (tid >> 7)) * DK + (tid & (DK - 1))) * 16, 0, 0));
+        float, __builtin_amdgcn_raw_buffer_load_b32(rm, ((2 * cc + (tid >> 7)) * DK + (tid & (DK - 1))) * 4, 0, 0));
   } else {
     x.rn = x.pv = 0.f;
   }
@@ -1862,7 +1862,7 @@ hipError_t launch_tinv_mfma(const ScanArgs& s, void* tbuf, hipStream_t st) {
   const bool diagf = s.dmaps != nullptr;
   if (diagf) {
     pa.nsub = (s.L + C / 2 - 1) / (C / 2);
-    pa.dmaps = reinterpret_cast<const float4*>(s.dmaps);
+    pa.dmaps = s.dmaps;
     pa.r = s.r;
     pa.qvar = s.qvar;
     pa.gain_out = static_cast<_Float16*>(const_cast<void*>(s.gain));
