@@ -344,6 +344,26 @@ def test_diag_kalman_spread_variances(kdn, orc, given, L):
     assert_close(got["cov"], ref["cov"], TOL_F32, "diag p")
 
 
+def test_diag_kalman_wide_variance_range(kdn, orc):
+    """Diagonal Kalman write on the matrix-core path with starting variances
+    spread over six decades (1e-3 .. 1e3, log-uniform per coordinate) and a
+    small observation noise (r = 0.01): gains that range widely within a
+    token, and variances that fall by orders of magnitude over the sequence
+    (the float32 recursion of the prepare kernel and the chunk-start scan).
+    B=1 H=2 L=300, o, S and the final variances against the oracle."""
+    B, H, L, d = 1, 2, 300, 128
+    inp = workloads.scan_inputs(B, H, L, d, d, seed=142, dtype="bf16", with_r=True)
+    inp["r"] = np.full((B, H, L), 0.01, np.float32)
+    rng = np.random.Generator(np.random.PCG64(142))
+    p0 = np.exp(rng.uniform(np.log(1e-3), np.log(1e3), (B, H, d))).astype(np.float32)
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"], cov0=p0,
+                   q_noise_var=0.2, mode="diag")
+    got = _scan_gpu(kdn, inp, "bf16", 64, mode="diag", cov0=p0, qvar=0.2)
+    assert_close(got["o"], ref["o"], TOL_BF16, "diag o")
+    assert_close(got["S"], ref["S"], TOL_BF16, "diag S")
+    assert_close(got["cov"], ref["cov"], TOL_F32, "diag p")
+
+
 @pytest.mark.parametrize("dk", [40, 64])
 def test_diag_kalman_other_key_widths(kdn, orc, dk):
     """Diagonal Kalman write on the float32 path with d_k = 40 (the chunk-start
