@@ -466,7 +466,23 @@ def bench_tiny(kdn, torch, reps=200, keep=None):
             torch.cuda.synchronize()
             walls.append(time.perf_counter() - w0)
         walls.sort()
+        # the call captured 20 times into one HIP graph and replayed: GPU time
+        # per call without the host's per-call cost (Python, argument checks,
+        # launch), which back-to-back eager calls of this size are bound by
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(20):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = _events(torch, 2)
+        g0.record()
+        for _ in range(10):
+            graph.replay()
+        g1.record()
+        torch.cuda.synchronize()
         out[name] = dict(gpu_us_per_call=round(gpu_us, 2),
+                         graph_gpu_us_per_call=round(g0.elapsed_time(g1) * 1e3 / 200, 2),
                          host_us_per_synchronous_call=round(walls[len(walls) // 2] * 1e6, 1))
         if keep is not None:
             fn()

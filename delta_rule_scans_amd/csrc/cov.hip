@@ -249,42 +249,76 @@ __global__ __launch_bounds__(256) void full_gains_kernel(const Tk* k, const floa
                                                          const float* r, const float* cov_in,
                                                          float* cov_out, float qvar, Tg* gains,
                                                          int L, int dk) {
+  // The token inputs of up to 64 tokens are staged together (keys [t][d_k],
+  // alpha^2, Q, r), so the sequential loop reads only LDS. P holds the
+  // predicted covariance of the token at hand; each token's update also
+  // applies the next token's prediction, P <- a^2 (P - u u^T / s) + Q I, in
+  // the same pass (the last token of a tile leaves the update alone and the
+  // next tile predicts first), the same arithmetic as predicting separately.
+  constexpr int TT = 64;
   __shared__ float sP[64 * 65];
   __shared__ float sU[64];
-  __shared__ float sKv[64];
+  __shared__ float sKt[TT * 64];
+  __shared__ float sA2[TT], sQv[TT], sR[TT];
+  __shared__ float sKu[4];
   const int bh = blockIdx.x, tid = threadIdx.x;
   const int PP = dk + 1;
+  const int ri = tid >> 2, pq = tid & 3;  // row and quarter of P k
   for (int idx = tid; idx < dk * dk; idx += 256) {
     const int i = idx / dk, j = idx - i * dk;
     sP[i * PP + j] = cov_in[(size_t)bh * dk * dk + idx];
   }
-  for (int t = 0; t < L; ++t) {
-    const size_t g = (size_t)bh * L + t;
-    const float a = alpha ? alpha[g] : 1.f;
-    const float rt = r ? r[g] : 1.f;
-    const float Q = (1.f - a) * (1.f + a) * qvar;
-    if (tid < dk) sKv[tid] = Elem<Tk>::load(k, g * dk + tid);
-    __syncthreads();
-    for (int idx = tid; idx < dk * dk; idx += 256) {
-      const int i = idx / dk, j = idx - i * dk;
-      sP[i * PP + j] = fmaf(a * a, sP[i * PP + j], i == j ? Q : 0.f);
+  for (int t0 = 0; t0 < L; t0 += TT) {
+    const int nt = min(TT, L - t0);
+    __syncthreads();  // the previous tile's inputs are no longer read
+    for (int idx = tid; idx < nt * dk; idx += 256)
+      sKt[idx] = Elem<Tk>::load(k, ((size_t)bh * L + t0) * dk + idx);
+    if (tid < nt) {
+      const size_t g = (size_t)bh * L + t0 + tid;
+      const float a = alpha ? alpha[g] : 1.f;
+      sA2[tid] = a * a;
+      sQv[tid] = (1.f - a) * (1.f + a) * qvar;
+      sR[tid] = r ? r[g] : 1.f;
     }
     __syncthreads();
-    if (tid < dk) {
+    // predict the tile's first token
+    for (int idx = tid; idx < dk * dk; idx += 256) {
+      const int i = idx / dk, j = idx - i * dk;
+      sP[i * PP + j] = fmaf(sA2[0], sP[i * PP + j], i == j ? sQv[0] : 0.f);
+    }
+    __syncthreads();
+    for (int tt = 0; tt < nt; ++tt) {
+      const float* kt = sKt + tt * dk;
+      // u = P k: four adjacent lanes per row (two interleaved sums each),
+      // combined by lane shuffles; each wavefront's share of k^T u goes to LDS
       float u = 0.f;
-      for (int j = 0; j < dk; ++j) u = fmaf(sP[tid * PP + j], sKv[j], u);
-      sU[tid] = u;
+      if (ri < dk) {
+        float u0 = 0.f, u1 = 0.f;
+        const float* pr_ = sP + ri * PP;
+        for (int j = pq; j < dk; j += 8) {
+          u0 = fmaf(pr_[j], kt[j], u0);
+          if (j + 4 < dk) u1 = fmaf(pr_[j + 4], kt[j + 4], u1);
+        }
+        u = u0 + u1;
+      }
+      u += __shfl_xor(u, 1, 64);
+      u += __shfl_xor(u, 2, 64);
+      if (pq == 0 && ri < dk) sU[ri] = u;
+      const float ku = wave_sum64(pq == 0 && ri < dk ? kt[ri] * u : 0.f);
+      if ((tid & 63) == 0) sKu[tid >> 6] = ku;
+      __syncthreads();
+      const float s = sR[tt] + ((sKu[0] + sKu[1]) + (sKu[2] + sKu[3]));
+      const float inv = 1.f / s;
+      if (tid < dk) Elem<Tg>::store(gains, ((size_t)bh * L + t0 + tt) * dk + tid, sU[tid] * inv);
+      const bool pred = tt + 1 < nt;
+      const float a2 = pred ? sA2[tt + 1] : 1.f, Q = pred ? sQv[tt + 1] : 0.f;
+      for (int idx = tid; idx < dk * dk; idx += 256) {
+        const int i = idx / dk, j = idx - i * dk;
+        const float p = sP[i * PP + j] - sU[i] * sU[j] * inv;
+        sP[i * PP + j] = pred ? fmaf(a2, p, i == j ? Q : 0.f) : p;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    float s = rt;
-    for (int j = 0; j < dk; ++j) s = fmaf(sKv[j], sU[j], s);
-    const float inv = 1.f / s;
-    if (tid < dk) Elem<Tg>::store(gains, g * dk + tid, sU[tid] * inv);
-    for (int idx = tid; idx < dk * dk; idx += 256) {
-      const int i = idx / dk, j = idx - i * dk;
-      sP[i * PP + j] -= sU[i] * sU[j] * inv;
-    }
-    __syncthreads();
   }
   if (cov_out) {
     for (int idx = tid; idx < dk * dk; idx += 256) {

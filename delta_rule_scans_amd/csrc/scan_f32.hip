@@ -31,7 +31,7 @@ struct F32Plan {
 
 __host__ __device__ inline size_t f32_lds_floats(int dk, int C, int dvt) {
   return (size_t)3 * C * (dk + 1) + (size_t)2 * C * dvt + (size_t)2 * C * (C + 1) +
-         (size_t)dk * dvt + 4 * (size_t)C + NT;
+         (size_t)dk * dvt + 4 * (size_t)C;
 }
 
 constexpr size_t kMaxLds = 160 * 1024;
@@ -66,7 +66,6 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
   float* sBs = sLg + C;         // [C] write scale (beta, or 1 for a gain)
   float* sLa = sBs + C;         // [C] log alpha_t when the residual decay is exclusive, else 0
   float* sW = sLa + C;          // [C] state-update weights (g_n / g_l) * scale_l
-  float* sRed = sW + C;         // [NT]
 
   const Tin* qp = static_cast<const Tin*>(a.q);
   const Tin* kp = static_cast<const Tin*>(a.k);
@@ -85,6 +84,9 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
   for (int c0 = 0; c0 < L; c0 += C) {
     const int n = min(C, L - c0);
     __syncthreads();
+    // every global read of the chunk in one round: keys, queries, write
+    // directions, values, and (wavefront 0, lane t = token t) the decays and
+    // write scales, whose chunk-local prefix of log alpha is a wavefront scan
     for (int idx = tid; idx < C * dk; idx += NT) {
       const int t = idx / dk, i = idx - t * dk;
       float kv = 0.f, qv = 0.f, bv = 0.f;
@@ -98,7 +100,13 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
       sQ[t * KP + i] = qv;
       sB[t * KP + i] = bv;
     }
-    if (tid < C) {
+    for (int idx = tid; idx < C * dvt; idx += NT) {
+      const int t = idx / dvt, j = idx - t * dvt;
+      float x = 0.f;
+      if (t < n && j < nj) x = Elem<Tin>::load(vp, (tok0 + c0 + t) * dv + j0 + j);
+      sX[idx] = x;
+    }
+    if (tid < 64) {  // C <= 64
       float la = 0.f, bs = 0.f;
       if (tid < n) {
         const size_t g = tok0 + c0 + tid;
@@ -106,22 +114,16 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
         la = logf(al);
         bs = gp ? 1.f : a.beta[g];
       }
-      sLg[tid] = la;
-      sBs[tid] = bs;
-      sLa[tid] = a.plain ? la : 0.f;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < C * dvt; idx += NT) {
-      const int t = idx / dvt, j = idx - t * dvt;
-      float x = 0.f;
-      if (t < n && j < nj) x = Elem<Tin>::load(vp, (tok0 + c0 + t) * dv + j0 + j);
-      sX[idx] = x;
-    }
-    if (tid == 0) {
-      float s = 0.f;
-      for (int t = 0; t < n; ++t) {
-        s += sLg[t];
-        sLg[t] = s;
+      float pre = la;  // inclusive prefix over the chunk's tokens (0 past n)
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(pre, off, 64);
+        if (tid >= off) pre += y;
+      }
+      if (tid < C) {
+        sLg[tid] = pre;
+        sBs[tid] = bs;
+        sLa[tid] = a.plain ? la : 0.f;
       }
     }
     __syncthreads();
@@ -132,6 +134,7 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
       float av = 0.f, pv = 0.f;
       if (l <= i) {
         float dkb = 0.f, dqb = 0.f;
+#pragma unroll 4
         for (int r = 0; r < dk; ++r) {
           const float b = sB[l * KP + r];
           dkb = fmaf(sK[i * KP + r], b, dkb);
@@ -148,6 +151,7 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
     for (int idx = tid; idx < n * dvt; idx += NT) {
       const int i = idx / dvt, j = idx - i * dvt;
       float ks = 0.f, qs = 0.f;
+#pragma unroll 4
       for (int r = 0; r < dk; ++r) {
         const float s = sS[r * dvt + j];
         ks = fmaf(sK[i * KP + r], s, ks);
@@ -157,24 +161,25 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
       sO[idx] = expf(sLg[i]) * qs;
     }
     __syncthreads();
-    // Forward substitution (I + A) U = X; each column is split over NT/dvt lanes.
-    {
-      const int j = tid % dvt;
-      const int part = tid / dvt;
-      const int nparts = NT / dvt;
-      for (int i = 1; i < (a.noerase ? 0 : n); ++i) {
-        float acc = 0.f;
-        for (int l = part; l < i; l += nparts) acc = fmaf(sA[i * CP + l], sX[l * dvt + j], acc);
-        sRed[tid] = acc;
-        __syncthreads();
-        if (part == 0) {
-          float s = 0.f;
-          for (int p = 0; p < nparts; ++p) s += sRed[p * dvt + j];
-          sX[i * dvt + j] -= s;
+    // Forward substitution (I + A) U = X: one lane per column, rows in order
+    // (no barrier between rows; row i of A is read by every lane at once)
+    if (!a.noerase && tid < dvt) {
+      const int j = tid;
+      for (int i = 1; i < n; ++i) {
+        const float* ar = sA + i * CP;
+        float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+        int l = 0;
+        for (; l + 4 <= i; l += 4) {
+          s0 = fmaf(ar[l], sX[l * dvt + j], s0);
+          s1 = fmaf(ar[l + 1], sX[(l + 1) * dvt + j], s1);
+          s2 = fmaf(ar[l + 2], sX[(l + 2) * dvt + j], s2);
+          s3 = fmaf(ar[l + 3], sX[(l + 3) * dvt + j], s3);
         }
-        __syncthreads();
+        for (; l < i; ++l) s0 = fmaf(ar[l], sX[l * dvt + j], s0);
+        sX[i * dvt + j] -= (s0 + s1) + (s2 + s3);
       }
     }
+    __syncthreads();
     // per-tile squared residual norms for the write scores
     if (a.esq && tid < n) {
       float ss = 0.f;
@@ -185,6 +190,7 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
     for (int idx = tid; idx < n * dvt; idx += NT) {
       const int i = idx / dvt, j = idx - i * dvt;
       float acc = sO[idx];
+#pragma unroll 4
       for (int l = 0; l <= i; ++l) acc = fmaf(sP[i * CP + l], sX[l * dvt + j], acc);
       if (j < nj) Elem<Tout>::store(op, (tok0 + c0 + i) * dv + j0 + j, acc);
     }
@@ -193,6 +199,7 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
     for (int idx = tid; idx < dk * dvt; idx += NT) {
       const int r = idx / dvt, j = idx - r * dvt;
       float acc = 0.f;
+#pragma unroll 4
       for (int l = 0; l < n; ++l) acc = fmaf(sW[l] * sB[l * KP + r], sX[l * dvt + j], acc);
       sS[idx] = fmaf(gn, sS[idx], acc);
     }

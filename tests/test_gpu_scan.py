@@ -1,8 +1,8 @@
 """GPU parity of kdn_scan_fwd against the fp64 oracle (element by element).
 
 Small cases span several chunks and a ragged tail; the full-size workloads are
-run exactly as the benchmark launches them and checked on sampled heads, each
-of which the oracle recomputes over the whole sequence.
+run exactly as the benchmark launches them and checked on every head, each of
+which the oracle recomputes over the whole sequence.
 """
 import numpy as np
 import pytest
@@ -242,6 +242,64 @@ def test_phases_on_two_streams(kdn, mode):
     assert torch.equal(S1, S2)
     if diag:
         assert torch.equal(c1, c2)
+
+
+@pytest.mark.parametrize("case", ["delta_bf16", "diag_bf16", "tiny_f32", "tiny_rls"])
+def test_graph_replay_matches_eager(kdn, case):
+    """One kdn_scan_fwd call captured into a HIP graph and replayed three times,
+    with eager scans of other inputs and synchronisations between the replays:
+    every replay gives the eager call's outputs, state and covariance bit for
+    bit (the library enqueues kernels only: no allocation, copy or fill)."""
+    import torch
+    if case.startswith("tiny"):
+        inp = workloads.named_scan_inputs("tiny")
+        dtype, chunk, d = "f32", 16, inp["q"].shape[-1]
+        mode = "full" if case == "tiny_rls" else "delta"
+    else:
+        d, dtype, chunk = 128, "bf16", 64
+        mode = "diag" if case == "diag_bf16" else "delta"
+        inp = workloads.scan_inputs(2, 3, 200, d, d, seed=131, dtype="bf16", with_r=mode == "diag")
+    B, H, L, _ = inp["q"].shape
+    q, k, v = (dev_tensor(inp[n], dtype) for n in ("q", "k", "v"))
+    alpha = dev_tensor(inp["alpha"])
+    beta = dev_tensor(inp["beta"]) if mode == "delta" else None
+    r = dev_tensor(inp["r"]) if mode == "diag" else None
+    cov_in = {"diag": lambda: torch.ones((B, H, d), device="cuda"),
+              "full": lambda: (100.0 * torch.eye(d, device="cuda")).expand(B, H, d, d).contiguous(),
+              "delta": lambda: None}[mode]()
+    S0 = dev_tensor(np.random.default_rng(5).standard_normal((B, H, d, d)).astype(np.float32) * 0.1)
+    need = kdn.kdn_scan_workspace_size(B, H, L, d, d, chunk, mode=mode,
+                                       in_dtype=kdn.F32 if dtype == "f32" else kdn.BF16)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, H, L, d), device="cuda")
+    S = torch.empty((B, H, d, d), device="cuda")
+    cov = torch.empty_like(cov_in) if cov_in is not None else None
+    kw = dict(alpha=alpha, beta=beta, r=r, cov_in=cov_in, cov_out=cov, state_in=S0, state_out=S,
+              o=o, chunk=chunk, mode=mode, q_noise_var=1.0 if mode == "diag" else 0.0,
+              workspace=ws)
+    kdn.kdn_scan_fwd(q, k, v, **kw)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in (o, S, cov) if t is not None]
+    # eager work between replays: the same call on reversed inputs
+    other = [x.flip(2).contiguous() for x in (q, k, v)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        kdn.kdn_scan_fwd(q, k, v, **kw)
+    for rep in range(3):
+        for t in (o, S, cov):
+            if t is not None:
+                t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in (o, S, cov) if t is not None]
+        for g, w in zip(got, want):
+            assert torch.equal(g, w), f"{case}: replay {rep} differs from the eager call"
+        kdn.kdn_scan_fwd(*other, **{**kw, "o": torch.empty_like(o), "state_out": torch.empty_like(S),
+                                    "cov_out": torch.empty_like(cov) if cov is not None else None,
+                                    "workspace": None})
+        torch.cuda.synchronize()
+    log(f"graph replay {case}: 3 replays equal to the eager call")
 
 
 def test_split_sequence_resume(kdn, orc):
