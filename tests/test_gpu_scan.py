@@ -508,6 +508,23 @@ def test_full_kalman_small(kdn, orc):
     assert_close(got["cov"], ref["cov"], TOL_F32, "full P")
 
 
+@pytest.mark.parametrize("dk,dv,L", [(13, 7, 70), (1, 5, 65), (61, 17, 129)])
+def test_full_kalman_odd_sizes(kdn, orc, dk, dv, L):
+    """Full covariance with key widths that are not multiples of the four lanes
+    that share a row of P k, one key coordinate, and lengths one past a
+    64-token input tile."""
+    inp = workloads.scan_inputs(2, 1, L, dk, dv, seed=150 + dk, dtype="f32", with_r=True)
+    rng = np.random.Generator(np.random.PCG64(150 + dk))
+    A = rng.standard_normal((2, 1, dk, dk))
+    P0 = (np.einsum("bhij,bhkj->bhik", A, A) / dk + np.eye(dk)).astype(np.float32)
+    ref = orc.scan(inp["q"], inp["k"], inp["v"], alpha=inp["alpha"], r=inp["r"], cov0=P0,
+                   q_noise_var=0.5, mode="full")
+    got = _scan_gpu(kdn, inp, "f32", 16, mode="full", cov0=P0, qvar=0.5)
+    assert_close(got["o"], ref["o"], TOL_F32, f"full d_k {dk} o")
+    assert_close(got["S"], ref["S"], TOL_F32, f"full d_k {dk} S")
+    assert_close(got["cov"], ref["cov"], TOL_F32, f"full d_k {dk} P")
+
+
 def test_full_kalman_largest_dk(kdn, orc):
     """Full covariance at the largest d_k it takes (64), bf16 inputs, chunk 64,
     a random positive-definite initial covariance."""
