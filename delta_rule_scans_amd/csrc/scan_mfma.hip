@@ -210,12 +210,14 @@ struct PrepArgs {
 };
 
 constexpr int kAdP = 17;  // fp32 pitch of the diagonal blocks of A
-constexpr int kPrepR1 = (C * KP > 2 * C * CP ? C * KP : 2 * C * CP) * 2;  // sQ, later sT + sTt
+constexpr int kPrepR1 = (C * KP > 2 * C * CP ? C * KP : 2 * C * CP) * 2;  // a tile, later sT + sTt
 
 // The delta write stages only K, which then shares the first region with T.
-// The diagonal Kalman write with its gains formed here adds a token array.
+// The Kalman writes stage K, then Q, then P in one tile, and the gains in the
+// first region, which then takes T (53.5 KB: three workgroups per CU). The
+// diagonal Kalman write with its gains formed here adds a token array.
 size_t prep_lds_bytes(bool gain, bool diagf = false) {
-  return (size_t)kPrepR1 + (gain ? (size_t)2 * C * KP * 2 : 0) +
+  return (size_t)kPrepR1 + (gain ? (size_t)C * KP * 2 : 0) +
          (size_t)C * CP * 2 + (size_t)4 * 16 * kAdP * 4 + (size_t)4 * 16 * 24 * 2 +
          (size_t)3 * C * 4 + (diagf ? (size_t)C * 4 : 0);
 }
@@ -289,18 +291,16 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   constexpr bool gain = GAIN;
   static_assert(GAIN || !DIAGF, "the gains are formed here only for the diagonal Kalman write");
   unsigned char* p = lds_raw;
-  _Float16* sQ = reinterpret_cast<_Float16*>(p);   // [C][KP] (phases 1-2)
-  _Float16* sT = reinterpret_cast<_Float16*>(p);   // [C][CP] (phases 3-5, reuses sQ)
+  // delta write: K [C][KP] (phases 1-2) in the first region, then T;
+  // Kalman writes: K, then Q (phase 2), then P [C][CP] in one tile, the
+  // gains [C][KP] (phases 1-2) in the first region, then T
+  _Float16* sK = reinterpret_cast<_Float16*>(p);
+  if (gain) p += C * KP * 2;
+  _Float16* sB = reinterpret_cast<_Float16*>(p);   // write vectors (K for the delta write)
+  _Float16* sT = sB;                               // [C][CP] (phases 3-5)
   _Float16* sTt = sT + C * CP;                     // [C][CP] T transposed
   p += kPrepR1;
-  _Float16* sK = sQ;                               // [C][KP] (phases 1-2)
-  _Float16* sB = sK;                               // [C][KP] write vectors
-  if (gain) {
-    sK = reinterpret_cast<_Float16*>(p);
-    p += C * KP * 2;
-    sB = reinterpret_cast<_Float16*>(p);
-    p += C * KP * 2;
-  }
+  _Float16* sQ = sK;                               // [C][KP] (phase 2, Kalman writes)
   _Float16* sP = sK;                               // [C][CP] (phases 3-5, Kalman writes)
   _Float16* sAh = reinterpret_cast<_Float16*>(p);  // [C][CP] A in fp16
   p += C * CP * 2;
@@ -315,7 +315,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
   // the terms of those sums (they borrow the gains tile and what follows it)
   float* sSd = sLgx + C;                           // [C]
   float* sKu = reinterpret_cast<float*>(sB);       // [C][kKuP] p-_i k_i^2 (before the Grams)
-  static_assert(C * kKuP * 4 <= C * KP * 2 + C * CP * 2 + 4 * 16 * kAdP * 4 + 4 * 16 * 24 * 2,
+  static_assert(C * kKuP * 4 <= kPrepR1 + C * CP * 2 + 4 * 16 * kAdP * 4 + 4 * 16 * 24 * 2,
                 "the terms of the gain denominators fit from the gains tile to the token arrays");
 
   const int bh = blockIdx.x;
@@ -351,12 +351,15 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
 
     // phase 1: stage K (and for the Kalman writes Q and the gains) as fp16 from
     // the registers, start loading the next chunk, per-token scalars
+    // (Kalman writes: Q is staged over K once the A Gram is done; its pieces
+    // wait in registers)
+    uint4 q_cur[GAIN ? 4 : 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int seg = tid + NT * i, row = seg >> 4, c8 = seg & 15;
       *reinterpret_cast<uint4*>(sK + row * KP + c8 * 8) = bf16x8_to_f16x8(in.k[i]);
       if (GAIN) {
-        *reinterpret_cast<uint4*>(sQ + row * KP + c8 * 8) = bf16x8_to_f16x8(in.q[GAIN ? i : 0]);
+        q_cur[GAIN ? i : 0] = in.q[GAIN ? i : 0];
         if (!DIAGF) *reinterpret_cast<uint4*>(sB + row * KP + c8 * 8) = in.g[GAIN ? i : 0];
       }
     }
@@ -478,7 +481,8 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
     }
 
     // phase 2: 20 lower Gram tiles, A (tiles 0-9) from K and P (tiles 10-19) from Q;
-    // wavefront w takes tiles w, w + 4, ..., w + 16.
+    // wavefront w takes tiles w, w + 4, ..., w + 16. The Kalman writes stage
+    // Q over K between the A and the P tiles.
     floatx4 pacc[3];
     int pti[3], ptj[3];
 #pragma unroll
@@ -492,6 +496,17 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
       const int tl = wave + 4 * j;
       const bool isP = tl >= 10;
       if (isP && !gain) continue;
+      if (gain && tl == 10 + (wave + 2) % 4) {
+        // the first P tile of this wavefront: every wavefront's A tiles (its
+        // tiles below 10) are done reading K
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int seg = tid + NT * i, row = seg >> 4, c8 = seg & 15;
+          *reinterpret_cast<uint4*>(sQ + row * KP + c8 * 8) = bf16x8_to_f16x8(q_cur[GAIN ? i : 0]);
+        }
+        __syncthreads();
+      }
       int ti, tj;
       tile_ij(isP ? tl - 10 : tl, ti, tj);
       const _Float16* srcA = isP ? sQ : sK;
