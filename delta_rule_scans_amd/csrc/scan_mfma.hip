@@ -349,10 +349,10 @@ __global__ __launch_bounds__(NT) void prep_kernel(PrepArgs a) {
     const int c0 = c * C, n = min(C, a.L - c0);
     unsigned char* rec = a.rec + ((size_t)bh * a.nchunks + c) * rec_bytes(gain);
 
-    // phase 1: stage K (and for the Kalman writes Q and the gains) as fp16 from
-    // the registers, start loading the next chunk, per-token scalars
-    // (Kalman writes: Q is staged over K once the A Gram is done; its pieces
-    // wait in registers)
+    // phase 1: stage K (and the gains when they come from the gains kernel)
+    // as fp16 from the registers, start loading the next chunk, per-token
+    // scalars (Kalman writes: Q is staged over K once the A Gram is done; its
+    // pieces wait in registers)
     uint4 q_cur[GAIN ? 4 : 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
