@@ -31,7 +31,7 @@ struct F32Plan {
 
 __host__ __device__ inline size_t f32_lds_floats(int dk, int C, int dvt) {
   return (size_t)3 * C * (dk + 1) + (size_t)2 * C * dvt + (size_t)2 * C * (C + 1) +
-         (size_t)dk * dvt + 4 * (size_t)C;
+         (size_t)dk * dvt + 5 * (size_t)C;
 }
 
 constexpr size_t kMaxLds = 160 * 1024;
@@ -46,7 +46,7 @@ F32Plan plan_f32(int dk, int C) {
 
 template <typename Tin, typename Tout, typename Tg>
 __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
-  extern __shared__ float lds[];
+  extern __shared__ __align__(16) float lds[];
   const int C = a.chunk, dk = a.dk, dv = a.dv, L = a.L;
   const int KP = dk + 1, CP = C + 1;
   const int bh = blockIdx.x;
@@ -62,8 +62,13 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
   float* sA = sO + C * dvt;     // [C][CP]
   float* sP = sA + C * CP;      // [C][CP]
   float* sS = sP + C * CP;      // [dk][dvt] state tile
-  float* sLg = sS + dk * dvt;   // [C] chunk-local log-decay prefix
-  float* sBs = sLg + C;         // [C] write scale (beta, or 1 for a gain)
+  // [C] chunk-local prefix of log alpha in float64 (8-byte aligned: every
+  // region before it is an even number of floats). Decay ratios come from
+  // differences of these prefixes, which reach about -1000 in a chunk of
+  // tokens with alpha near 1e-8: in float32 they would keep only ~6e-5 of
+  // each ratio.
+  double* sLg = reinterpret_cast<double*>(sS + dk * dvt);
+  float* sBs = reinterpret_cast<float*>(sLg + C);  // [C] write scale (beta, or 1 for a gain)
   float* sLa = sBs + C;         // [C] log alpha_t when the residual decay is exclusive, else 0
   float* sW = sLa + C;          // [C] state-update weights (g_n / g_l) * scale_l
 
@@ -114,10 +119,10 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
         la = logf(al);
         bs = gp ? 1.f : a.beta[g];
       }
-      float pre = la;  // inclusive prefix over the chunk's tokens (0 past n)
+      double pre = la;  // inclusive prefix over the chunk's tokens (0 past n)
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(pre, off, 64);
+        const double y = __shfl_up(pre, off, 64);
         if (tid >= off) pre += y;
       }
       if (tid < C) {
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
       }
     }
     __syncthreads();
-    if (tid < n) sW[tid] = expf(sLg[n - 1] - sLg[tid]) * sBs[tid];
+    if (tid < n) sW[tid] = expf((float)(sLg[n - 1] - sLg[tid])) * sBs[tid];
     // Gram blocks: A strictly lower, P lower including the diagonal.
     for (int idx = tid; idx < n * n; idx += NT) {
       const int i = idx / n, l = idx - i * n;
@@ -140,8 +145,8 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
           dkb = fmaf(sK[i * KP + r], b, dkb);
           dqb = fmaf(sQ[i * KP + r], b, dqb);
         }
-        const float f = expf(sLg[i] - sLg[l]) * sBs[l];
-        av = (l < i) ? dkb * expf(sLg[i] - sLa[i] - sLg[l]) * sBs[l] : 0.f;
+        const float f = expf((float)(sLg[i] - sLg[l])) * sBs[l];
+        av = (l < i) ? dkb * expf((float)((sLg[i] - sLa[i]) - sLg[l])) * sBs[l] : 0.f;
         pv = dqb * f;
       }
       sA[i * CP + l] = av;
@@ -157,8 +162,8 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
         ks = fmaf(sK[i * KP + r], s, ks);
         qs = fmaf(sQ[i * KP + r], s, qs);
       }
-      if (!a.noerase) sX[idx] -= expf(sLg[i] - sLa[i]) * ks;
-      sO[idx] = expf(sLg[i]) * qs;
+      if (!a.noerase) sX[idx] -= expf((float)(sLg[i] - sLa[i])) * ks;
+      sO[idx] = expf((float)sLg[i]) * qs;
     }
     __syncthreads();
     // Forward substitution (I + A) U = X: one lane per column, rows in order
@@ -195,7 +200,7 @@ __global__ __launch_bounds__(NT) void scan_f32_kernel(ScanArgs a, int dvt) {
       if (j < nj) Elem<Tout>::store(op, (tok0 + c0 + i) * dv + j0 + j, acc);
     }
     // S <- g_n S0 + sum_l w_l b_l U_l^T
-    const float gn = expf(sLg[n - 1]);
+    const float gn = expf((float)sLg[n - 1]);
     for (int idx = tid; idx < dk * dvt; idx += NT) {
       const int r = idx / dvt, j = idx - r * dvt;
       float acc = 0.f;

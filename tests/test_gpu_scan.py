@@ -640,8 +640,10 @@ def _extreme_alpha(B, H, L, seed):
 
 
 @pytest.mark.parametrize("mode,resid,dtype", [("delta", "gated", "bf16"), ("delta", "plain", "bf16"),
+                                              ("delta", "noerase", "bf16"),
                                               ("diag", "gated", "bf16"), ("iso", "gated", "bf16"),
-                                              ("delta", "plain", "f32"), ("delta", "gated", "f32")])
+                                              ("delta", "plain", "f32"), ("delta", "gated", "f32"),
+                                              ("delta", "noerase", "f32")])
 def test_extreme_decay(kdn, orc, mode, resid, dtype):
     """Very fast decay, alpha = 1 exactly and abrupt switches (see _extreme_alpha),
     on the matrix-core path (bf16, d_k = 128, chunk 64) and the float32 path,
