@@ -126,14 +126,17 @@ __device__ __forceinline__ Scal fetch_scalars(const BwdArgs& a, size_t tok, int 
   }
   return r;
 }
-__device__ void put_scalars(const BwdArgs& a, Scal f, float* sLg, float* sB, float* sAl) {
+// The chunk-local prefix of log alpha is kept in float64: decay ratios are
+// differences of prefixes, which reach about -1000 in a chunk of tokens with
+// alpha near 1e-8, where float32 would keep only ~6e-5 of each ratio.
+__device__ void put_scalars(const BwdArgs& a, Scal f, double* sLg, float* sB, float* sAl) {
   const int t = threadIdx.x;
   if (t < C) {
     const float b = a.resid == 1 ? f.be / f.al : f.be;
-    float lg = logf(f.al);
+    double lg = logf(f.al);
 #pragma unroll
     for (int off = 1; off < C; off <<= 1) {
-      const float y = __shfl_up(lg, off, C);
+      const double y = __shfl_up(lg, off, C);
       if (t >= off) lg += y;
     }
     sLg[t] = lg;
@@ -218,8 +221,8 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
   float* sA = lds;                // [C][LC] (after the Grams)
   float* sT = sA + C * LC;        // [C][LC]
   float* sY = sT + C * LC;        // [32][33]
-  float* sLg = lds + 2 * C * LP;
-  float* sB = sLg + C;
+  double* sLg = reinterpret_cast<double*>(lds + 2 * C * LP);  // [C] (8-byte aligned)
+  float* sB = reinterpret_cast<float*>(sLg + C);
   float* sAl = sB + C;
   float* sGn = sAl + C;           // [C][LP] gain rows (gain mode)
   const int bh = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, nch = gridDim.y;
@@ -252,7 +255,7 @@ __global__ __launch_bounds__(NT) void bwd_prep_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * w + 4 * q + i, l = 16 * b + r;
-      const float f = l <= t ? sB[l] * expf(sLg[t] - sLg[l]) : 0.f;
+      const float f = l <= t ? sB[l] * expf((float)(sLg[t] - sLg[l])) : 0.f;
       const float av = (erase && l < t) ? kk[b][i] * f : 0.f;
       sA[t * LC + l] = av;
       Ag[t * C + l] = av;
@@ -329,8 +332,8 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
   float* sS = sT + C * LCC;     // [DP][LOC] state tile (operand copy)
   float* sR = sS + DP * LOC;    // [C][LOC] V - diag(g) K S0
   float* sE = sR + C * LOC;     // [C][LOC] diag(Lambda b) E
-  float* sLg = sE + C * LOC;
-  float* sB = sLg + C;
+  double* sLg = reinterpret_cast<double*>(sE + C * LOC);  // [C] (8-byte aligned)
+  float* sB = reinterpret_cast<float*>(sLg + C);
   float* sAl = sB + C;
   float* sGn = sAl + C;         // [C][LKC] gain rows (gain mode)
   const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
@@ -392,7 +395,7 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = m0 + 4 * q + i;
-        sR[t * LOC + n0 + r] -= expf(sLg[t]) * x[i];
+        sR[t * LOC + n0 + r] -= expf((float)sLg[t]) * x[i];
       }
       __syncthreads();
       mfma16(e, sT, LCC, 1, sR, LOC, 1, m0, n0, C);
@@ -400,15 +403,15 @@ __global__ __launch_bounds__(NTC) void bwd_fwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) e[i] = sR[(m0 + 4 * q + i) * LOC + n0 + r];
     }
-    const float lgC = sLg[C - 1];
+    const double lgC = sLg[C - 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = m0 + 4 * q + i, col = j0 + n0 + r;
       if (t < n && col < dv) a.E[((size_t)bh * nch * C + (size_t)c * C + t) * dv + col] = e[i];
-      sE[t * LOC + n0 + r] = e[i] * sB[t] * expf(lgC - sLg[t]);
+      sE[t * LOC + n0 + r] = e[i] * sB[t] * expf((float)(lgC - sLg[t]));
     }
     __syncthreads();
-    const float gC = expf(lgC);
+    const float gC = expf((float)lgC);
     floatx4 acc[2] = {S[0] * gC, S[1] * gC};
     mfma_row<2>(acc, gain ? sGn : sK, 1, LKC, nullptr, sE, LOC, 1, 16 * w, C);
 #pragma unroll
@@ -434,8 +437,8 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
   float* sO = sG + DP * LOC;    // [C][LOC] dO, then diag(g) dO
   float* sD = sO + C * LOC;     // [C][LOC] dE
   float* sX = sD + C * LOC;     // [C][LOC] -diag(g) dR
-  float* sLg = sX + C * LOC;
-  float* sB = sLg + C;
+  double* sLg = reinterpret_cast<double*>(sX + C * LOC);  // [C] (8-byte aligned)
+  float* sB = reinterpret_cast<float*>(sLg + C);
   float* sAl = sB + C;
   const int bh = blockIdx.x, j0 = blockIdx.y * TW, tid = threadIdx.x;
   const int L = a.L, dk = a.dk, dv = a.dv, nch = (L + C - 1) / C, dk64 = dk <= 64 ? 64 : DP;
@@ -501,7 +504,7 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
         }
     }
     __syncthreads();
-    const float lgC = sLg[C - 1];
+    const double lgC = sLg[C - 1];
     // dE = Pm^T dO + diag(Lambda b) K G
     floatx4 de;
     {
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = m0 + 4 * q + i;
-        de[i] = fmaf(sB[t] * expf(lgC - sLg[t]), y[i], x[i]);
+        de[i] = fmaf(sB[t] * expf((float)(lgC - sLg[t])), y[i], x[i]);
         sD[t * LOC + n0 + r] = de[i];
       }
     }
@@ -532,13 +535,13 @@ __global__ __launch_bounds__(NTC) void bwd_rev_kernel(BwdArgs a) {
         a.dR[((size_t)bh * nch * C + (size_t)c * C + t) * dv + col] = dr[i];
         a.dv_out[(tok + t) * dv + col] = a.resid == 1 ? sAl[t] * dr[i] : dr[i];
       }
-      const float g = expf(sLg[t]);
+      const float g = expf((float)sLg[t]);
       sX[t * LOC + n0 + r] = -g * dr[i];
       sO[t * LOC + n0 + r] *= g;
     }
     __syncthreads();
     // G <- g_C G + Q^T diag(g) dO - K^T diag(g) dR
-    const float gC = expf(lgC);
+    const float gC = expf((float)lgC);
     floatx4 acc[2] = {G[0] * gC, G[1] * gC};
     mfma_row<2>(acc, sQ, 1, LKC, nullptr, sO, LOC, 1, 16 * w, C);
     if (erase) mfma_row<2>(acc, sK, 1, LKC, nullptr, sX, LOC, 1, 16 * w, C);
@@ -654,8 +657,8 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
   float* sK = sQ + C * LQ;       // [C][LQ]
   float* sXp = sK + C * LQ;      // [C][LX] lower_incl(dO E^T) * D
   float* sXa = sXp + C * LX;     // [C][LX] dA * D
-  float* sLg = sXa + C * LX;
-  float* sB = sLg + C;
+  double* sLg = reinterpret_cast<double*>(sXa + C * LX);  // [C] (8-byte aligned)
+  float* sB = reinterpret_cast<float*>(sLg + C);
   float* sAl = sB + C;
   float* sRow = sAl + C;         // [6][C] per-token sums
   float* sCs = sRow + 6 * C;     // [NT / 64][C] partial column sums
@@ -708,7 +711,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     for (int u = 0; u < C * C / NT; ++u) {
       const int t = (tid >> 6) + u * (NT / 64);
       const bool lo = s <= t, st = erase && s < t;
-      const float D = lo ? expf(sLg[t] - sLg[s]) : 0.f;
+      const float D = lo ? expf((float)(sLg[t] - sLg[s])) : 0.f;
       const float dp = lo ? fdP.x[u] : 0.f;
       const float da = st ? -fdA.x[u] : 0.f;
       sXp[t * LX + s] = dp * D;
@@ -723,7 +726,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     sCs[(tid >> 6) * C + s] = cs;
   }
   __syncthreads();
-  const float lgC = sLg[C - 1];
+  const double lgC = sLg[C - 1];
   float pq[4] = {}, kr[4] = {}, wv[4] = {}, dbv[4] = {}, vv[4] = {};
   // the write vectors: rows b_t k_t (sB scaling sK), or the gain rows
   const float* sW = gain ? sGn : sK;
@@ -734,7 +737,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * w + 4 * q + i;
-      const float g = expf(sLg[t]);
+      const float g = expf((float)sLg[t]);
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
         const int d = 16 * b + r;
@@ -755,7 +758,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * w + 4 * q + i;
-      const float lam = expf(lgC - sLg[t]), g = expf(sLg[t]), b = sB[t];
+      const float lam = expf((float)(lgC - sLg[t])), g = expf((float)sLg[t]), b = sB[t];
 #pragma unroll
       for (int bb = 0; bb < 8; ++bb) {
         const int d = 16 * bb + r;
@@ -813,7 +816,7 @@ __global__ __launch_bounds__(NT) void bwd_grad_kernel(BwdArgs a) {
     float wsum = w_t;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off, 64);
-    if (t == n - 1) dl += expf(lgC) * a.gs0[(size_t)bh * nch + c] + wsum;
+    if (t == n - 1) dl += expf((float)lgC) * a.gs0[(size_t)bh * nch + c] + wsum;
     float suf = dl;  // sum over t' >= t (tokens past the end hold 0)
 #pragma unroll
     for (int off = 1; off < C; off <<= 1) {
@@ -887,12 +890,12 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
   hipError_t e;
   const int ng = a.gain ? 1 : 0;  // gain mode: one more [C][d_k] tile per kernel
   e = launch_lds("bwd_prep_kernel", bwd_prep_kernel, dim3(a.BH, nch), NT,
-                 ((2 + ng) * C * (DP + 1) + 3 * C) * f, a, s);
+                 ((2 + ng) * C * (DP + 1) + 4 * C) * f, a, s);
   if (e != hipSuccess) return e;
   e = launch_lds("bwd_fwd_kernel", bwd_fwd_kernel, dim3(a.BH, ntw), NTC,
-                 ((1 + ng) * C * LKC + C * LCC + DP * LOC + 2 * C * LOC + 3 * C) * f, a, s);
+                 ((1 + ng) * C * LKC + C * LCC + DP * LOC + 2 * C * LOC + 4 * C) * f, a, s);
   if (e != hipSuccess) return e;
-  const size_t lds_rev = (2 * C * LKC + 2 * C * LCC + DP * LOC + 3 * C * LOC + 3 * C) * f;
+  const size_t lds_rev = (2 * C * LKC + 2 * C * LCC + DP * LOC + 3 * C * LOC + 4 * C) * f;
   e = a.gain ? launch_lds("bwd_rev_kernel<true>", bwd_rev_kernel<true>, dim3(a.BH, ntw), NTC,
                           lds_rev, a, s)
              : launch_lds("bwd_rev_kernel<false>", bwd_rev_kernel<false>, dim3(a.BH, ntw), NTC,
@@ -906,7 +909,7 @@ hipError_t launch_scan_bwd(BwdArgs a, void* ws, hipStream_t s) {
                  a, s);
   if (e != hipSuccess) return e;
   return launch_lds("bwd_grad_kernel", bwd_grad_kernel, dim3(a.BH, nch), NT,
-                    ((2 + ng) * C * (DP + 1) + 2 * C * (C + 1) + 3 * C + 6 * C + (NT / 64) * C) * f,
+                    ((2 + ng) * C * (DP + 1) + 2 * C * (C + 1) + 4 * C + 6 * C + (NT / 64) * C) * f,
                     a, s);
 }
 

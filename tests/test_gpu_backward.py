@@ -17,9 +17,12 @@ def kdn():
     return k
 
 
-def _case(kdn, orc, B, H, L, dk, dv, resid, seed, heads=None, tol=TOL_F32):
+def _case(kdn, orc, B, H, L, dk, dv, resid, seed, heads=None, tol=TOL_F32, alpha=None,
+          dlog_alpha=False):
     import torch
     inp = workloads.scan_inputs(B, H, L, dk, dv, seed=seed, dtype="f32")
+    if alpha is not None:
+        inp["alpha"] = alpha
     rng = np.random.Generator(np.random.PCG64([seed, 7]))
     S0 = (rng.standard_normal((B, H, dk, dv)) * 0.1).astype(np.float32)
     d_o = rng.standard_normal((B, H, L, dv)).astype(np.float32)
@@ -36,7 +39,12 @@ def _case(kdn, orc, B, H, L, dk, dv, resid, seed, heads=None, tol=TOL_F32):
     ref = orc.scan_bwd(sub(inp["q"]), sub(inp["k"]), sub(inp["v"]), alpha=sub(inp["alpha"]),
                        beta=sub(inp["beta"]), S0=sub(S0), d_o=sub(d_o), dS=sub(dS), resid=resid)
     for n in ("dq", "dk", "dv", "dalpha", "dbeta"):
-        assert_close(got[n][bs, hs], ref[n][0], tol, f"{resid} {n}")
+        g_, r_ = got[n][bs, hs], ref[n][0]
+        if n == "dalpha" and dlog_alpha:
+            # the gradient with respect to log alpha: alpha dL/dalpha
+            a_ = inp["alpha"][bs, hs].astype(np.float64)
+            g_, r_, n = g_ * a_, r_ * a_, "alpha dalpha"
+        assert_close(g_, r_, tol, f"{resid} {n}")
     assert_close(got["dstate_in"][bs, hs], ref["dS0"][0], tol, f"{resid} dS0")
 
 
@@ -44,6 +52,21 @@ def _case(kdn, orc, B, H, L, dk, dv, resid, seed, heads=None, tol=TOL_F32):
 def test_backward_small(kdn, orc, resid):
     log(f"backward {resid}")
     _case(kdn, orc, 1, 2, 150, 64, 64, resid, seed=401)
+
+
+@pytest.mark.parametrize("resid", ["gated", "noerase"])
+def test_backward_extreme_decay(kdn, orc, resid):
+    """Decays from exactly 1 down to 1e-8 inside 64-token chunks, with abrupt
+    switches and a ragged tail (the scan tests' extreme-decay pattern): the
+    decay ratios are differences of log-decay prefixes near -1000. The decay's
+    gradient is checked as alpha dL/dalpha, the gradient with respect to log
+    alpha: at alpha = 1e-8, dL/dalpha is that gradient times 1e8, so its
+    float32 rounding, relative to the other tokens' entries, grows by the same
+    factor (measured: 12.6 of RMS(dL/dalpha) against 1e-4)."""
+    from test_gpu_scan import _extreme_alpha
+    log(f"backward extreme decay {resid}")
+    _case(kdn, orc, 1, 2, 357, 64, 64, resid, seed=406, alpha=_extreme_alpha(1, 2, 357, 406),
+          dlog_alpha=True)
 
 
 def test_backward_odd_shapes(kdn, orc):
