@@ -4,7 +4,7 @@ import numpy as np
 import pytest
 
 import workloads
-from _util import TOL_F32, assert_close, dev_tensor, host, log
+from _util import TOL_F32, assert_close, dev_tensor, extreme_alpha, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -63,9 +63,8 @@ def test_backward_extreme_decay(kdn, orc, resid):
     alpha: at alpha = 1e-8, dL/dalpha is that gradient times 1e8, so its
     float32 rounding, relative to the other tokens' entries, grows by the same
     factor (measured: 12.6 of RMS(dL/dalpha) against 1e-4)."""
-    from test_gpu_scan import _extreme_alpha
     log(f"backward extreme decay {resid}")
-    _case(kdn, orc, 1, 2, 357, 64, 64, resid, seed=406, alpha=_extreme_alpha(1, 2, 357, 406),
+    _case(kdn, orc, 1, 2, 357, 64, 64, resid, seed=406, alpha=extreme_alpha(1, 2, 357, 406),
           dlog_alpha=True)
 
 
